@@ -1,0 +1,232 @@
+"""CPU oracle (numpy, float64) for DSA sparse-MLA prefill attention.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  It shares no code
+with the HIP path (no kernels, headers, helpers or tables) and the HIP path
+never calls it.
+
+Every function is the plain definition of what the pages compute, written out
+slowly and obviously; none of the kernels' blocking, tiling, online softmax or
+bitmap tricks appear here.  Pages cited:
+
+* [MASKED] "[2/N][Attention] Enable masked MHA for sparse MLA prefills"
+  (vllm-project/vllm PR #48770) -- Purpose section: below a length threshold a
+  masked MHA simulates DSA (mask = causal AND top-k membership).
+* [NOPE] "[Perf][GLM-5.3-Flash] Dense/masked-MHA sparse prefill for the NoPE
+  (256, 0, 256) layout + skip the NoPE K concat" (vllm-project/vllm PR #55738)
+  -- commit messages (K is k_nope itself when the rope part is empty; K is
+  k_nope concatenated with the broadcast k_pe otherwise) and the Purpose
+  section (per-token top-k MQA kernel over the latent).
+* [GROUPED] "[Perf][DSA] Grouped sparse prefill with the FlashMLA
+  head-group-mask kernel" (JaredforReal/vllm PR #6) -- commit message and the
+  "How" section: 128 // num_heads consecutive tokens form 128 pseudo-heads over
+  the sorted union of their top-k rows; a per-token membership mask restricts
+  each token's heads to its own top-k, which reproduces per-token sparse
+  attention exactly; the union is padded to a multiple of a block; the GLM
+  comment on that page: -1 entries pad a wider (2176-column) top-k buffer.
+
+Readings where the pages are silent (each also listed in the design notes):
+
+* Selection: sel(t) = {x in topk[t, :cols] : 0 <= x < S and x <= q_pos_offset + t}.
+  -1 padding, out-of-range and non-causal entries are ignored in every routing.
+  Entries of a row are distinct (an indexer top-k is a set); the oracle raises
+  on duplicates.
+* Softmax scale multiplies the raw dot products; LSE is the natural log of the
+  sum of exp(scaled logits).  An empty selection gives out = 0 and LSE = -inf.
+* Values: V is the first d_v (= 512) dims of the latent row.
+* Grouping: group g holds tokens gG .. min(T, gG + G) - 1 with G = 128 / H;
+  pseudo-head r = i * H + h for token gG + i and head h.
+* Union list: strictly ascending, -1 padded to union_pad = ceil(G*cols/64)*64.
+* head_group_mask: uint8 [NG, union_pad]; bit i of slot j is set iff token
+  gG + i selects union position j; padding slots are 0.
+
+Pins: see ``tests/test_oracle_pins.py`` (library routines, closed forms,
+brute-force set arithmetic, invariants).  No function here is parity-unpinned.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Iterable, Optional
+
+import numpy as np
+
+UNION_BLOCK = 64
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 bit patterns (uint16) as float64."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def union_pad(G: int, cols: int) -> int:
+    """Padded length of one group's union list: ceil(G * cols / 64) * 64."""
+    return -(-(G * cols) // UNION_BLOCK) * UNION_BLOCK
+
+
+def selected_positions(row: np.ndarray, S: int, pos: int) -> np.ndarray:
+    """sel(t) for one top-k row, in row order (see the module docstring)."""
+    row = np.asarray(row, dtype=np.int64)
+    sel = row[(row >= 0) & (row < S) & (row <= pos)]
+    if np.unique(sel).size != sel.size:
+        raise ValueError("a top-k row holds the same valid position twice")
+    return sel
+
+
+def softmax_attention(qrows: np.ndarray, keys: np.ndarray, values: np.ndarray,
+                      scale: float):
+    """Exact softmax attention of query rows over a key set.
+
+    qrows [R, d], keys [n, d], values [n, dv] (float64).
+    Returns out [R, dv] = softmax(scale * q k^T) v and lse [R] = log sum exp(scale * q k^T).
+    """
+    R = qrows.shape[0]
+    if keys.shape[0] == 0:
+        return np.zeros((R, values.shape[1])), np.full(R, -np.inf)
+    logits = scale * (qrows @ keys.T)
+    m = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - m)
+    total = e.sum(axis=1, keepdims=True)
+    out = (e @ values) / total
+    lse = m[:, 0] + np.log(total[:, 0])
+    return out, lse
+
+
+def _as_scale(scale: float) -> float:
+    # the GPU receives the scale as float32; the oracle uses that same value
+    return float(np.float32(scale))
+
+
+def _tokens(T: int, tokens: Optional[Iterable[int]]) -> np.ndarray:
+    return np.arange(T) if tokens is None else np.asarray(list(tokens), dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# per-token sparse MQA  ([NOPE] Purpose; [GROUPED] commit message)
+# ---------------------------------------------------------------------------
+
+def pertoken_sparse_mqa(q: np.ndarray, kv: np.ndarray, topk: np.ndarray, S: int,
+                        q_pos_offset: int, scale: float, d_v: int = 512,
+                        tokens: Optional[Iterable[int]] = None):
+    """Every token t attends, for all H heads, over the latent rows sel(t).
+
+    q uint16 [T, H, d_qk], kv uint16 [S, d_qk], topk int32 [T, cols].
+    Returns (out float64 [n, H, d_v], lse float64 [n, H]) for the requested tokens.
+    """
+    T, H, _ = q.shape
+    scale = _as_scale(scale)
+    toks = _tokens(T, tokens)
+    kv64 = bf16_to_f64(kv[:S])
+    out = np.zeros((toks.size, H, d_v))
+    lse = np.full((toks.size, H), -np.inf)
+    for n, t in enumerate(toks):
+        sel = selected_positions(topk[t], S, q_pos_offset + int(t))
+        keys = kv64[sel]
+        out[n], lse[n] = softmax_attention(bf16_to_f64(q[t]), keys, keys[:, :d_v], scale)
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# union list + head_group_mask  ([GROUPED] commit message, "How" section)
+# ---------------------------------------------------------------------------
+
+def group_union_mask(topk: np.ndarray, S: int, q_pos_offset: int, G: int,
+                     pad: Optional[int] = None):
+    """Sorted union of each group's selections and the per-token membership mask.
+
+    Returns union_idx int32 [NG, pad] (-1 padded), union_len int32 [NG],
+    mask uint8 [NG, pad].
+    """
+    T, cols = topk.shape
+    pad = union_pad(G, cols) if pad is None else pad
+    NG = -(-T // G)
+    union_idx = np.full((NG, pad), -1, dtype=np.int32)
+    union_len = np.zeros(NG, dtype=np.int32)
+    mask = np.zeros((NG, pad), dtype=np.uint8)
+    for g in range(NG):
+        members = [selected_positions(topk[t], S, q_pos_offset + t)
+                   for t in range(g * G, min(T, g * G + G))]
+        U = np.unique(np.concatenate(members)) if members else np.zeros(0, np.int64)
+        n = U.size
+        union_idx[g, :n] = U
+        union_len[g] = n
+        for i, sel in enumerate(members):
+            mask[g, :n] |= (np.isin(U, sel).astype(np.uint8) << np.uint8(i))
+    return union_idx, union_len, mask
+
+
+# ---------------------------------------------------------------------------
+# grouped sparse MQA over the union  ([GROUPED] commit message, "How")
+# ---------------------------------------------------------------------------
+
+def grouped_sparse_mqa(q: np.ndarray, kv: np.ndarray, union_idx: np.ndarray,
+                       union_len: np.ndarray, mask: np.ndarray, scale: float,
+                       d_v: int = 512, groups: Optional[Iterable[int]] = None):
+    """Pseudo-head r = i*H + h of group g attends over the union slots j whose
+    mask bit i is set.  Returns (out [T, H, d_v], lse [T, H]); tokens of groups
+    not requested stay at out 0 / lse -inf.
+    """
+    T, H, _ = q.shape
+    G = 128 // H
+    scale = _as_scale(scale)
+    S = kv.shape[0]
+    kv64 = bf16_to_f64(kv)
+    out = np.zeros((T, H, d_v))
+    lse = np.full((T, H), -np.inf)
+    gs = range(union_len.size) if groups is None else groups
+    for g in gs:
+        n = int(union_len[g])
+        U = union_idx[g, :n].astype(np.int64)
+        bits = mask[g, :n]
+        if np.any((U < 0) | (U >= S)):
+            raise ValueError("union list holds an out-of-range position")
+        for i in range(G):
+            t = g * G + i
+            if t >= T:
+                break
+            keys = kv64[U[((bits >> i) & 1) == 1]]
+            out[t], lse[t] = softmax_attention(bf16_to_f64(q[t]), keys, keys[:, :d_v], scale)
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# masked dense MHA  ([MASKED] Purpose; [NOPE] commit messages)
+# ---------------------------------------------------------------------------
+
+def masked_mha(q: np.ndarray, k_nope: np.ndarray, k_pe: Optional[np.ndarray],
+               v: np.ndarray, topk: np.ndarray, S: int, q_pos_offset: int, scale: float,
+               tokens: Optional[Iterable[int]] = None):
+    """Dense MHA over all S keys with mask = causal AND top-k membership.
+
+    q uint16 [T, H, dn + dr]; k_nope [S, H, dn]; k_pe [S, dr] or None (dr = 0:
+    K is k_nope itself); v [S, H, dv].  Masked logits are -inf, so a token
+    with no allowed key gets out 0 and LSE -inf.
+    """
+    T, H, _ = q.shape
+    scale = _as_scale(scale)
+    toks = _tokens(T, tokens)
+    kn = bf16_to_f64(k_nope[:S])
+    kp = bf16_to_f64(k_pe[:S]) if k_pe is not None and k_pe.shape[-1] > 0 else None
+    vv = bf16_to_f64(v[:S])
+    dv = v.shape[2]
+    positions = np.arange(S)
+    out = np.zeros((toks.size, H, dv))
+    lse = np.full((toks.size, H), -np.inf)
+    for n, t in enumerate(toks):
+        member = np.zeros(S, dtype=bool)
+        member[selected_positions(topk[t], S, q_pos_offset + int(t))] = True
+        allowed = member & (positions <= q_pos_offset + int(t))
+        if not allowed.any():
+            continue
+        qt = bf16_to_f64(q[t])
+        for h in range(H):
+            K = kn[:, h, :] if kp is None else np.concatenate([kn[:, h, :], kp], axis=1)
+            logits = scale * (K @ qt[h])
+            logits[~allowed] = -np.inf
+            m = logits.max()
+            e = np.exp(logits - m)
+            total = e.sum()
+            out[n, h] = (e @ vv[:, h, :]) / total
+            lse[n, h] = m + math.log(total)
+    return out, lse

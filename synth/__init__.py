@@ -1,0 +1,18 @@
+"""Seeded synthetic inputs for DSA sparse-MLA prefill attention.
+
+This package only draws inputs (bf16 tensors as uint16 bit patterns and int32
+top-k index buffers). It contains none of the attention arithmetic, so both
+the CPU oracle and the HIP path can take their inputs from it without sharing
+any of the method's code.
+"""
+
+from .gen import (  # noqa: F401
+    CONFIGS,
+    Case,
+    Config,
+    bf16_bits_from_f32,
+    bf16_bits_to_f32,
+    make_case,
+    topk_locality,
+    topk_uniform,
+)

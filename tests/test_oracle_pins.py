@@ -1,0 +1,329 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+* library routines: torch scaled_dot_product_attention / logsumexp in float64
+  with a boolean mask built here from the selection rule with torch scatter;
+* the textbook special case: all causal positions selected -> causal attention;
+* closed forms: q = 0, a single selected row, n identical selected rows,
+  empty selection;
+* brute-force set arithmetic (pure Python) for the union list and mask;
+* invariants: row permutation, -1 placement, wider buffers, non-causal and
+  out-of-range entries, perturbing unselected rows, grouped == per-token,
+  masked MHA == per-token MQA when all heads share K = V.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth.gen import normal_bf16, shuffle_rows, topk_locality, topk_uniform, widen
+
+
+def to_t64(bits):
+    """bf16 bits -> torch float64 through torch's own bfloat16 type."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).double()
+
+
+def allowed_mask(topk, S, P0):
+    """[T, S] bool: x appears in row t, 0 <= x < S, x <= P0 + t (built with torch scatter)."""
+    tk = torch.from_numpy(topk.astype(np.int64))
+    T = tk.shape[0]
+    valid = (tk >= 0) & (tk < S)
+    m = torch.zeros(T, S + 1, dtype=torch.bool)
+    m.scatter_(1, torch.where(valid, tk, torch.full_like(tk, S)), True)
+    m = m[:, :S]
+    causal = torch.arange(S)[None, :] <= (P0 + torch.arange(T))[:, None]
+    return m & causal
+
+
+def sdpa_reference(q_bits, kv_bits, topk, S, P0, scale, d_v):
+    q = to_t64(q_bits)                 # [T, H, d]
+    kv = to_t64(kv_bits)[:S]           # [S, d]
+    allow = allowed_mask(topk, S, P0)  # [T, S]
+    T, H, _ = q.shape
+    out = torch.nn.functional.scaled_dot_product_attention(
+        q.transpose(0, 1), kv[None].expand(H, S, -1), kv[None, :, :d_v].expand(H, S, -1),
+        attn_mask=allow[None], scale=scale).transpose(0, 1)
+    logits = torch.einsum("thd,sd->ths", q, kv) * scale
+    logits = logits.masked_fill(~allow[:, None, :], -math.inf)
+    lse = torch.logsumexp(logits, dim=-1)
+    return out.numpy(), lse.numpy(), allow.any(dim=1).numpy()
+
+
+def rand_case(seed, T=40, S=48, H=4, d=24, cols=12, P0=None, extra_junk=True):
+    rng = np.random.default_rng(seed)
+    P0 = S - T if P0 is None else P0
+    q = normal_bf16(rng, (T, H, d))
+    kv = normal_bf16(rng, (S, d))
+    topk = topk_uniform(rng, T, S, cols - 3 if extra_junk else cols, cols, P0)
+    if extra_junk:
+        # sprinkle entries the selection rule must ignore: -7, >= S, non-causal
+        for t in range(T):
+            row = topk[t]
+            free = np.flatnonzero(row < 0)
+            if free.size >= 3:
+                p = P0 + t
+                row[free[0]] = -7
+                row[free[1]] = S + 3
+                row[free[2]] = p + 1 if p + 1 < S else -1
+    return q, kv, topk, P0
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_pertoken_matches_torch_sdpa(seed):
+    S, T, d, dv = 48, 40, 24, 16
+    q, kv, topk, P0 = rand_case(seed, T=T, S=S, d=d)
+    scale = 0.37
+    out, lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, P0, scale, d_v=dv)
+    ref_out, ref_lse, nonempty = sdpa_reference(q, kv, topk, S, P0, float(np.float32(scale)), dv)
+    assert nonempty.all()
+    np.testing.assert_allclose(out, ref_out, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+
+
+def test_all_causal_selected_is_causal_attention():
+    rng = np.random.default_rng(5)
+    T = S = 33
+    H, d, dv = 3, 20, 12
+    q = normal_bf16(rng, (T, H, d))
+    kv = normal_bf16(rng, (S, d))
+    topk = widen(topk_uniform(rng, T, S, S, S), S + 5)   # k >= S: every causal position
+    out, _ = oracle.pertoken_sparse_mqa(q, kv, topk, S, 0, 0.25, d_v=dv)
+    qt, kt = to_t64(q).transpose(0, 1), to_t64(kv)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt[None].expand(H, S, d), kt[None, :, :dv].expand(H, S, dv),
+        is_causal=True, scale=0.25).transpose(0, 1).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_closed_form_zero_query_is_mean_of_selected_values():
+    rng = np.random.default_rng(7)
+    T, S, H, d, dv = 6, 30, 2, 16, 8
+    q = np.zeros((T, H, d), np.uint16)        # +0.0 in bf16
+    kv = normal_bf16(rng, (S, d))
+    topk = topk_uniform(rng, T, S, 5, 9, q_pos_offset=S - T)
+    out, lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, S - T, 0.5, d_v=dv)
+    kvf = to_t64(kv).numpy()
+    for t in range(T):
+        sel = [x for x in topk[t] if x >= 0]
+        np.testing.assert_allclose(out[t], np.tile(kvf[sel, :dv].mean(0), (H, 1)), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse[t], math.log(len(sel)), rtol=0, atol=1e-13)
+
+
+def test_closed_form_single_selected_row():
+    rng = np.random.default_rng(8)
+    T, S, H, d, dv = 5, 20, 3, 24, 16
+    q = normal_bf16(rng, (T, H, d))
+    kv = normal_bf16(rng, (S, d))
+    topk = np.full((T, 4), -1, np.int32)
+    picks = [0, 3, 17, 9, 19]
+    topk[:, 2] = picks
+    out, lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, S - T, 0.125, d_v=dv)
+    qf, kvf = to_t64(q).numpy(), to_t64(kv).numpy()
+    for t, x in enumerate(picks):
+        np.testing.assert_array_equal(out[t], np.tile(kvf[x, :dv], (H, 1)))
+        # the dot product runs over the whole row (all d dims, including the rope part)
+        np.testing.assert_allclose(lse[t], 0.125 * (qf[t] @ kvf[x]), rtol=1e-13, atol=1e-13)
+
+
+def test_closed_form_identical_rows():
+    rng = np.random.default_rng(9)
+    T, S, H, d, dv = 1, 16, 2, 8, 4
+    q = normal_bf16(rng, (T, H, d))
+    kv = normal_bf16(rng, (S, d))
+    kv[[2, 5, 11, 12]] = kv[7]
+    topk = np.array([[5, -1, 2, 12, 7, 11]], np.int32)
+    out, lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, S - 1, 0.3, d_v=dv)
+    qf, kvf = to_t64(q).numpy(), to_t64(kv).numpy()
+    s = float(np.float32(0.3)) * (qf[0] @ kvf[7])
+    np.testing.assert_allclose(lse[0], s + math.log(5), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(out[0], np.tile(kvf[7, :dv], (H, 1)), rtol=1e-13)
+
+
+def test_empty_selection():
+    rng = np.random.default_rng(10)
+    T, S, H, d = 4, 8, 2, 8
+    q = normal_bf16(rng, (T, H, d))
+    kv = normal_bf16(rng, (S, d))
+    topk = np.array([[-1, -1], [9, -3], [3, -1], [2, 5]], np.int32)  # rows 0-2 select nothing valid
+    out, lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, 0, 1.0, d_v=4)
+    for t in range(3):
+        assert np.all(out[t] == 0) and np.all(np.isneginf(lse[t]))
+    assert np.all(np.isfinite(lse[3]))
+
+
+def test_duplicates_are_rejected():
+    with pytest.raises(ValueError):
+        oracle.selected_positions(np.array([3, 1, 3, -1]), 10, 9)
+
+
+def test_invariances():
+    S, T = 48, 40
+    q, kv, topk, P0 = rand_case(11, T=T, S=S)
+    base_out, base_lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, P0, 0.3, d_v=16)
+    for variant in (shuffle_rows(topk, 1), widen(topk, 20), shuffle_rows(widen(topk, 17), 2)):
+        o, l = oracle.pertoken_sparse_mqa(q, kv, variant, S, P0, 0.3, d_v=16)
+        np.testing.assert_allclose(o, base_out, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(l, base_lse, rtol=1e-13, atol=1e-13)
+    # perturbing rows outside sel(t) leaves token t unchanged
+    t = 17
+    sel = set(oracle.selected_positions(topk[t], S, P0 + t).tolist())
+    kv2 = kv.copy()
+    for x in range(S):
+        if x not in sel:
+            kv2[x] = kv2[x] ^ np.uint16(0x1234)
+    o, l = oracle.pertoken_sparse_mqa(q, kv2, topk, S, P0, 0.3, d_v=16, tokens=[t])
+    np.testing.assert_array_equal(o[0], base_out[t])
+    np.testing.assert_array_equal(l[0], base_lse[t])
+
+
+# ---------------------------------------------------------------------------
+# union list + mask: brute force with Python sets and invariants
+# ---------------------------------------------------------------------------
+
+def brute_union(topk, S, P0, G):
+    T, cols = topk.shape
+    pad = ((G * cols + 63) // 64) * 64
+    NG = (T + G - 1) // G
+    ui = [[-1] * pad for _ in range(NG)]
+    ul = [0] * NG
+    mk = [[0] * pad for _ in range(NG)]
+    for g in range(NG):
+        sets = []
+        for t in range(g * G, min(T, g * G + G)):
+            sets.append({int(x) for x in topk[t] if 0 <= x < S and x <= P0 + t})
+        U = sorted(set().union(*sets))
+        ul[g] = len(U)
+        for j, x in enumerate(U):
+            ui[g][j] = x
+            mk[g][j] = sum(1 << i for i, s in enumerate(sets) if x in s)
+    return np.array(ui, np.int32), np.array(ul, np.int32), np.array(mk, np.uint8)
+
+
+@pytest.mark.parametrize("G,T,S,cols,P0,seed", [
+    (8, 37, 45, 9, 8, 0), (4, 21, 21, 7, 0, 1), (2, 9, 30, 12, 21, 2), (1, 13, 13, 5, 0, 3),
+    (8, 8, 64, 16, 56, 4), (3, 10, 10, 4, 0, 5),
+])
+def test_union_matches_brute_force(G, T, S, cols, P0, seed):
+    rng = np.random.default_rng(seed)
+    topk = topk_uniform(rng, T, S, max(1, cols - 2), cols, P0)
+    topk[0, -1] = S + 1     # ignored: out of range
+    topk[-1, -1] = -5       # ignored: negative
+    ui, ul, mk = oracle.group_union_mask(topk, S, P0, G)
+    bi, bl, bm = brute_union(topk, S, P0, G)
+    np.testing.assert_array_equal(ui, bi)
+    np.testing.assert_array_equal(ul, bl)
+    np.testing.assert_array_equal(mk, bm)
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_union_invariants(G):
+    rng = np.random.default_rng(20 + G)
+    T, S, k, cols, P0 = 203, 300, 64, 70, 97
+    topk = shuffle_rows(topk_locality(rng, T, S, k, cols, G, P0), 3)
+    ui, ul, mk = oracle.group_union_mask(topk, S, P0, G)
+    pad = oracle.union_pad(G, cols)
+    assert ui.shape == (-(-T // G), pad)
+    for g in range(ui.shape[0]):
+        n = int(ul[g])
+        U = ui[g, :n]
+        assert np.all(np.diff(U) > 0)                      # strictly ascending
+        assert np.all(ui[g, n:] == -1) and np.all(mk[g, n:] == 0)
+        assert n <= min(G * cols, P0 + g * G + G)
+        for i, t in enumerate(range(g * G, min(T, g * G + G))):
+            sel = oracle.selected_positions(topk[t], S, P0 + t)
+            assert set(sel.tolist()) <= set(U.tolist())      # union covers every member
+            assert int(((mk[g, :n] >> i) & 1).sum()) == sel.size
+        last = min(T, g * G + G) - g * G
+        assert np.all(mk[g, :n] >> last == 0)                # absent tokens have no bits
+        if G == 1:
+            sel = oracle.selected_positions(topk[g], S, P0 + g)
+            np.testing.assert_array_equal(U, np.sort(sel))
+            assert np.all(mk[g, :n] == 1)
+
+
+def test_union_pad_formula():
+    assert oracle.union_pad(8, 2048) == 16384
+    assert oracle.union_pad(8, 2176) == 17408
+    assert oracle.union_pad(1, 2048) == 2048
+    assert oracle.union_pad(8, 32) == 256
+    assert oracle.union_pad(3, 7) == 64
+
+
+# ---------------------------------------------------------------------------
+# grouped == per-token
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("H,T", [(16, 29), (32, 13), (64, 7), (128, 5)])
+def test_grouped_equals_pertoken(H, T):
+    rng = np.random.default_rng(H + T)
+    G = 128 // H
+    S, d, dv, cols = 40, 20, 12, 10
+    P0 = S - T
+    q = normal_bf16(rng, (T, H, d))
+    kv = normal_bf16(rng, (S, d))
+    topk = shuffle_rows(topk_locality(rng, T, S, 8, cols, G, P0), 4)
+    ui, ul, mk = oracle.group_union_mask(topk, S, P0, G)
+    og, lg = oracle.grouped_sparse_mqa(q, kv, ui, ul, mk, 0.2, d_v=dv)
+    op, lp = oracle.pertoken_sparse_mqa(q, kv, topk, S, P0, 0.2, d_v=dv)
+    np.testing.assert_allclose(og, op, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lg, lp, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# masked dense MHA
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dr", [0, 6])
+def test_masked_mha_matches_torch_sdpa(dr):
+    rng = np.random.default_rng(30 + dr)
+    T, S, H, dn, dv, cols = 22, 30, 3, 10, 7, 9
+    P0 = S - T
+    q = normal_bf16(rng, (T, H, dn + dr))
+    kn = normal_bf16(rng, (S, H, dn))
+    kp = normal_bf16(rng, (S, dr)) if dr else None
+    v = normal_bf16(rng, (S, H, dv))
+    topk = topk_uniform(rng, T, S, 6, cols, P0)
+    out, lse = oracle.masked_mha(q, kn, kp, v, topk, S, P0, 0.4, )
+    qt = to_t64(q).transpose(0, 1)                                  # [H, T, d]
+    K = to_t64(kn).transpose(0, 1)                                  # [H, S, dn]
+    if dr:
+        K = torch.cat([K, to_t64(kp)[None].expand(H, S, dr)], dim=-1)
+    V = to_t64(v).transpose(0, 1)
+    allow = allowed_mask(topk, S, P0)
+    sc = float(np.float32(0.4))
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, K, V, attn_mask=allow[None], scale=sc)
+    logits = (qt @ K.transpose(1, 2) * sc).masked_fill(~allow[None], -math.inf)
+    np.testing.assert_allclose(out, ref.transpose(0, 1).numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(lse, torch.logsumexp(logits, -1).transpose(0, 1).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_masked_mha_all_selected_is_causal():
+    rng = np.random.default_rng(41)
+    T = S = 25
+    H, dn, dv = 2, 8, 8
+    q = normal_bf16(rng, (T, H, dn))
+    kn = normal_bf16(rng, (S, H, dn))
+    v = normal_bf16(rng, (S, H, dv))
+    topk = topk_uniform(rng, T, S, S, S)
+    out, _ = oracle.masked_mha(q, kn, None, v, topk, S, 0, 0.5)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        to_t64(q).transpose(0, 1), to_t64(kn).transpose(0, 1), to_t64(v).transpose(0, 1),
+        is_causal=True, scale=0.5).transpose(0, 1).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_masked_mha_equals_pertoken_when_heads_share_kv():
+    rng = np.random.default_rng(42)
+    T, S, H, d, cols = 19, 26, 4, 12, 8
+    P0 = S - T
+    q = normal_bf16(rng, (T, H, d))
+    X = normal_bf16(rng, (S, d))
+    shared = np.repeat(X[:, None, :], H, axis=1)
+    topk = topk_locality(rng, T, S, 6, cols, 8, P0)
+    om, lm = oracle.masked_mha(q, shared, None, shared, topk, S, P0, 0.3)
+    op, lp = oracle.pertoken_sparse_mqa(q, X, topk, S, P0, 0.3, d_v=d)
+    np.testing.assert_allclose(om, op, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lm, lp, rtol=1e-12, atol=1e-13)
