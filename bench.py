@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Throughput of DSA sparse-MLA prefill attention on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+
+  * union + membership-mask build, then grouped attention  (grouped routing)
+  * per-token sparse MQA                                   (per-token routing)
+  * top-k bit scatter, then masked dense MHA               (masked-MHA routing)
+
+Default workload "glm16k": the GLM-style per-GPU share of a 16k-token prefill
+chunk (T = S = 16384, H = 16, top-2048, groups of 8 tokens, 576-wide bf16
+latent, scale 1/16; locality top-k, seed 2) for the two MQA routings, and the
+NoPE masked-MHA layer of the same chunk (qk 256, rope 0, v 256, H = 16, scale
+1/16; locality top-k, seed 3) for the masked routing.  Inputs are resident in
+HBM before the timed region starts.
+
+value = query tokens per second of the whole step (T / step time).  Per-kernel
+times come from HIP events recorded on the launch stream over the timed region.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "query-tokens/s per layer (DSA sparse prefill, k=2048) + % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+
+WORKLOADS = {
+    # name: (MQA config, masked-MHA config or None)
+    "glm16k": ("c3_glm16k", "c4_masked_nope"),
+    "glm16k_uniform": ("c3w_glm16k_uniform", None),
+    "long32k": ("c5_long", None),
+    "dsv32": ("c2_dsv32", None),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="glm16k", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    return ap.parse_args()
+
+
+def algorithmic_work(case, union_len_sum, mha_case):
+    """Bytes / flops each kernel must move or execute (definitions in the design notes)."""
+    cfg, topk = case.cfg, case.topk
+    T, S, H, cols = cfg.T, cfg.S, cfg.H, cfg.cols
+    pos = cfg.q_pos_offset + np.arange(T)[:, None]
+    nsel = int(((topk >= 0) & (topk < S) & (topk <= pos)).sum())
+    NG = cfg.NG
+    pad = -(-(cfg.G * cols) // 64) * 64
+    rows_live = np.minimum(cfg.G, T - np.arange(NG) * cfg.G) * H   # live pseudo-head rows per group
+    w = {
+        "build_union": {"bound": "hbm", "bytes": T * cols * 4 + NG * pad * 5 + NG * 4},
+        "grouped_attn": {"bound": "mfma", "flops": None},   # filled below from the union lengths
+        "pertoken_attn": {"bound": "hbm",
+                          "bytes": nsel * 1152 + T * H * 576 * 2 + T * H * 512 * 2 + T * H * 4 + T * cols * 4},
+    }
+    w["grouped_attn"]["flops"] = float(np.sum(union_len_sum * rows_live)) * 2 * (576 + 512)
+    if mha_case is not None:
+        m = mha_case.cfg
+        words = (m.S + 31) // 32
+        causal_keys = np.minimum(m.S, m.q_pos_offset + np.arange(m.T) + 1).astype(np.float64)
+        w["scatter_topk_bits"] = {"bound": "hbm", "bytes": m.T * m.cols * 4 + m.T * words * 4}
+        w["masked_mha"] = {"bound": "mfma",
+                           "flops": float(causal_keys.sum()) * m.H * 2 * (m.dn + m.dr + m.dv)}
+    return w, nsel
+
+
+def cpu_baseline(case, mha_case, budget_s):
+    """The oracle, as it stands, on whole groups sampled across the sequence."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    cfg = case.cfg
+    G = cfg.G
+    rng = np.random.default_rng(0)
+    order = rng.permutation(cfg.NG)
+    done_tokens, spent = 0, 0.0
+    groups = []
+    for g in order:
+        toks = list(range(g * G, min(cfg.T, g * G + G)))
+        t0 = time.perf_counter()
+        sub = case.topk[g * G:g * G + G]
+        ui, ul, mk = oracle.group_union_mask(sub, cfg.S, cfg.q_pos_offset + g * G, G)
+        oracle.grouped_sparse_mqa(case.q[g * G:g * G + G], case.kv, ui, ul, mk, cfg.scale)
+        oracle.pertoken_sparse_mqa(case.q, case.kv, case.topk, cfg.S, cfg.q_pos_offset, cfg.scale, tokens=toks)
+        if mha_case is not None:
+            m = mha_case.cfg
+            oracle.masked_mha(mha_case.q, mha_case.k_nope, mha_case.k_pe, mha_case.v, mha_case.topk,
+                              m.S, m.q_pos_offset, m.scale, tokens=toks)
+        spent += time.perf_counter() - t0
+        done_tokens += len(toks)
+        groups.append(int(g))
+        if spent >= budget_s:
+            break
+    return {
+        "value": done_tokens / spent,
+        "unit": "query-tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{len(groups)} whole groups ({done_tokens} query tokens) drawn uniformly from the "
+                   f"{cfg.NG} groups of the workload; every routing of the step (union/mask, grouped, "
+                   f"per-token" + (", masked MHA" if mha_case is not None else "") +
+                   f") on numpy float64; {spent:.1f} s"),
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); every GPU box here has one "
+              "GPU and this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mla_prefill_amd import routings
+    from synth import CONFIGS, make_case
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    mqa_name, mha_name = WORKLOADS[a.workload]
+    t_gen = time.perf_counter()
+    case = make_case(CONFIGS[mqa_name])
+    mha_case = make_case(CONFIGS[mha_name]) if mha_name else None
+    cfg = case.cfg
+    print(f"# inputs generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    def dbf(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+
+    q, kv = dbf(case.q), dbf(case.kv)
+    topk = torch.from_numpy(case.topk).cuda()
+    G, H, T = cfg.G, cfg.H, cfg.T
+    bufs = routings.alloc_union(T, G, cfg.cols)
+    out_g, lse_g = routings.alloc_out(T, H, 512)
+    out_p, lse_p = routings.alloc_out(T, H, 512)
+    if mha_case is not None:
+        m = mha_case.cfg
+        mq, mk, mv = dbf(mha_case.q), dbf(mha_case.k_nope), dbf(mha_case.v)
+        mtopk = torch.from_numpy(mha_case.topk).cuda()
+        ws = torch.empty((m.T, (m.S + 31) // 32), dtype=torch.int32, device="cuda")
+        out_m, lse_m = routings.alloc_out(m.T, m.H, m.dv)
+    from mla_prefill_amd import _lib
+    stream = torch.cuda.current_stream()
+
+    names = ["build_union", "grouped_attn", "pertoken_attn"] + (["masked_mha_routing"] if mha_case else [])
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        _lib.dsa_build_group_union(topk, cfg.S, cfg.q_pos_offset, G, bufs.union_idx, bufs.union_len,
+                                   bufs.mask, stream=stream)
+        mark(1)
+        _lib.dsa_sparse_prefill_grouped(q, kv, bufs.union_idx, bufs.union_len, bufs.mask, cfg.scale,
+                                        out_g, lse_g, stream=stream)
+        mark(2)
+        _lib.dsa_sparse_prefill_pertoken(q, kv, topk, cfg.q_pos_offset, cfg.scale, out_p, lse_p,
+                                         stream=stream)
+        mark(3)
+        if mha_case is not None:
+            _lib.dsa_masked_mha_prefill(mq, mk, None, mv, mtopk, m.q_pos_offset, m.scale, ws, out_m,
+                                        lse_m, stream=stream)
+            mark(4)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    nev = len(names) + 1
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(a.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(a.steps)]))
+           for i, n in enumerate(names)}
+    ms_step = wall * 1e3 / a.steps
+    if not (torch.isfinite(out_g.float()).all() and torch.isfinite(out_p.float()).all()):
+        print("non-finite output", file=sys.stderr)
+        sys.exit(3)
+
+    work, nsel = algorithmic_work(case, bufs.union_len.cpu().numpy().astype(np.float64), mha_case)
+    kernels = {}
+    for n in names:
+        key = "masked_mha" if n == "masked_mha_routing" else n
+        wk = work[key]
+        ms = per[n]
+        if wk["bound"] == "hbm":
+            ach = wk["bytes"] / (ms * 1e-3) / 1e9
+            kernels[n] = {"ms": ms, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": ach / HBM_PEAK_GBS, "algorithmic": wk["bytes"]}
+        else:
+            ach = wk["flops"] / (ms * 1e-3) / 1e12
+            kernels[n] = {"ms": ms, "bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFS,
+                          "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFS, "algorithmic": wk["flops"]}
+    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+    d = kernels[dom]
+    roofline = {"kernel": dom, "bound": d["bound"], "achieved": round(d["achieved"], 2), "peak": d["peak"],
+                "unit": d["unit"], "frac": round(d["frac"], 4), "traffic": None}
+    routing_tps = {
+        "grouped (union build + attention)": T / ((per["build_union"] + per["grouped_attn"]) * 1e-3),
+        "per-token": T / (per["pertoken_attn"] * 1e-3),
+    }
+    if mha_case is not None:
+        routing_tps["masked MHA (bit scatter + attention)"] = mha_case.cfg.T / (per["masked_mha_routing"] * 1e-3)
+
+    cpu = None
+    if not a.no_cpu:
+        cpu = cpu_baseline(case, mha_case, a.cpu_seconds)
+
+    config = {"workload": a.workload, "mqa": mqa_name, "T": cfg.T, "S": cfg.S, "H": cfg.H, "k": cfg.k,
+              "cols": cfg.cols, "G": cfg.G, "q_pos_offset": cfg.q_pos_offset,
+              "selected_rows": nsel}
+    if mha_case is not None:
+        config["masked_mha"] = {"config": mha_name, "dn": m.dn, "dr": m.dr, "dv": m.dv, "H": m.H}
+    line = {
+        "metric": METRIC,
+        "value": round(T / (ms_step * 1e-3), 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": config,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+        "routing_query_tokens_per_s": {k: round(v, 1) for k, v in routing_tps.items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

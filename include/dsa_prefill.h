@@ -1,0 +1,157 @@
+/*
+ * dsa_prefill.h -- C ABI of libdsa_prefill.so: DSA sparse-MLA prefill attention
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Every query token attends only over its own indexer-selected top-k KV rows;
+ * the result is per-token sparse softmax attention, out plus LSE.  The pages
+ * describe three routings of this one function, each exposed here:
+ *
+ *   per-token  -- dsa_sparse_prefill_pertoken: each token gathers its own rows
+ *                 of the 576-wide bf16 latent ("[Perf][GLM-5.3-Flash]
+ *                 Dense/masked-MHA sparse prefill for the NoPE (256, 0, 256)
+ *                 layout + skip the NoPE K concat", Purpose section);
+ *   grouped    -- dsa_build_group_union + dsa_sparse_prefill_grouped: 128/H
+ *                 consecutive tokens become 128 pseudo-heads over the sorted
+ *                 union of their top-k sets, with a per-token membership mask
+ *                 ("[Perf][DSA] Grouped sparse prefill with the FlashMLA
+ *                 head-group-mask kernel", commit message and "How" section);
+ *   masked MHA -- dsa_masked_mha_prefill: dense MHA with mask = causal AND
+ *                 top-k membership ("[2/N][Attention] Enable masked MHA for
+ *                 sparse MLA prefills", Purpose section).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - bf16 tensors are passed as uint16_t bit patterns.
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  Tensors are
+ *    contiguous row-major; the top-k buffer alone has a leading dimension `ld`
+ *    (int32 elements between consecutive token rows, ld >= cols).
+ *  - bf16 tensors must be 16-byte aligned; int32 / float tensors 4-byte
+ *    aligned.  Outputs must not alias inputs.
+ *  - The library never allocates, frees or synchronizes.  All work is
+ *    enqueued on `stream` (a hipStream_t; NULL = the default stream) and
+ *    completes asynchronously.
+ *  - Selection rule, identical in every routing: token t (at absolute position
+ *    p_t = q_pos_offset + t) selects entry x of its top-k row iff 0 <= x < S and
+ *    x <= p_t.  -1 padding, out-of-range and non-causal entries are ignored, so
+ *    kernels stay memory-safe for any index contents.  Valid entries of a row
+ *    must be distinct (a top-k is a set); with duplicates the union list and
+ *    masks stay well defined but per-token results are unspecified.
+ *  - A token that selects nothing gets out = 0 and lse = -inf.
+ *  - out is bf16 (round to nearest even) of the fp32 result; lse is fp32, the
+ *    natural log of the sum of exp(scale * q.k) over the token's selection.
+ *  - Arguments are checked on the host before anything is enqueued; a
+ *    rejected call enqueues nothing and returns a negative status.
+ */
+#ifndef DSA_PREFILL_H
+#define DSA_PREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+/* status codes */
+#define DSA_OK 0
+#define DSA_ERR_NULL (-1)        /* a required pointer is NULL */
+#define DSA_ERR_SHAPE (-2)       /* a size or leading dimension is out of range */
+#define DSA_ERR_UNSUPPORTED (-3) /* head count / head dims outside the supported set */
+#define DSA_ERR_ALIGN (-4)       /* a pointer is not aligned as required */
+#define DSA_ERR_LAUNCH (-5)      /* the HIP runtime rejected a kernel launch */
+
+/* Version of this ABI (DSA_ABI_VERSION). */
+int dsa_abi_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* dsa_status_string(int status);
+
+/* Padded length of one group's union list: ceil(G * cols / 64) * 64 (the
+ * pages pad the union to whole blocks; block = 64 here).  Returns
+ * DSA_ERR_SHAPE for G outside 1..8, cols < 0 or an int overflow. */
+int dsa_union_pad(int G, int cols);
+
+/* Bytes of the bit-packed masked-MHA workspace: T * ceil(S / 32) * 4
+ * (0 for negative sizes). */
+size_t dsa_masked_mha_workspace_bytes(int T, int S);
+
+/* Union list and per-token membership mask of every group of G consecutive
+ * tokens ("[Perf][DSA] Grouped sparse prefill ...", "How" section: sorted
+ * union by bitmap and prefix sum, per-token membership mask).
+ *
+ *   topk            int32 [T, ld], first `cols` entries of each row used
+ *   T, cols, S      query tokens, top-k columns used, KV rows (T >= 0, cols >= 0, S >= 1)
+ *   q_pos_offset    position of token 0 (>= 0); token t sits at q_pos_offset + t
+ *   G               tokens per group, 1..8 (128 / H for the grouped routing)
+ *   union_pad       row length of the outputs; a multiple of 64 and >= G * cols
+ *                   (dsa_union_pad(G, cols) is the smallest such value)
+ * Outputs, NG = ceil(T / G) groups, group g = tokens gG .. min(T, gG + G) - 1:
+ *   union_idx       int32 [NG, union_pad]: the strictly ascending union of the
+ *                   members' selections, then -1 up to union_pad
+ *   union_len       int32 [NG]: number of union entries
+ *   head_group_mask uint8 [NG, union_pad]: bit i of slot j is set iff token
+ *                   gG + i selects union_idx[g, j]; 0 in padding slots and for
+ *                   absent members of the last group.
+ * All three outputs are fully overwritten.  Bit-exact and deterministic. */
+int dsa_build_group_union(const int32_t* topk, int64_t ld, int T, int cols, int S,
+                          int64_t q_pos_offset, int G, int union_pad, int32_t* union_idx,
+                          int32_t* union_len, uint8_t* head_group_mask, void* stream);
+
+/* Grouped sparse attention ("[Perf][DSA] Grouped sparse prefill ...", commit
+ * message and "How" section): with G = 128 / H, row r = i * H + h of group g
+ * (token gG + i, head h) attends over the slots j < union_len[g] of
+ * union_idx[g] whose mask bit i is set; this equals per-token attention.
+ *
+ *   q         bf16 [T, H, 576] absorbed MLA queries (free view [NG, 128, 576])
+ *   kv        bf16 [S, 576] latent rows; V = the first 512 dims of a row
+ *   union_idx, union_len, head_group_mask: as written by dsa_build_group_union
+ *             (union_len is clamped to [0, union_pad]; slots holding a
+ *             position outside [0, S) are skipped)
+ *   H         16, 32, 64 or 128 (128 % H == 0 and G = 128 / H <= 8)
+ *   d_qk, d_v must be 576 and 512
+ *   scale     softmax scale applied to q.k
+ *   out       bf16 [T, H, 512];  lse  fp32 [T, H]
+ * Rows of the partial last group beyond T are neither read nor written. */
+int dsa_sparse_prefill_grouped(const uint16_t* q, const uint16_t* kv, const int32_t* union_idx,
+                               const int32_t* union_len, const uint8_t* head_group_mask, int T,
+                               int H, int S, int union_pad, int d_qk, int d_v, float scale,
+                               uint16_t* out, float* lse, void* stream);
+
+/* Per-token sparse MQA ("[Perf][GLM-5.3-Flash] ...", Purpose section): token t
+ * attends, for each head, over the latent rows it selects from its own top-k
+ * row (selection rule above), gathering them itself.
+ *
+ *   q [T, H, 576], kv [S, 576], topk int32 [T, ld] (cols used), H a multiple of
+ *   16 up to 128, d_qk = 576, d_v = 512, q_pos_offset >= 0;
+ *   out bf16 [T, H, 512], lse fp32 [T, H]. */
+int dsa_sparse_prefill_pertoken(const uint16_t* q, const uint16_t* kv, const int32_t* topk,
+                                int64_t ld, int T, int H, int S, int cols, int64_t q_pos_offset,
+                                int d_qk, int d_v, float scale, uint16_t* out, float* lse,
+                                void* stream);
+
+/* Masked dense MHA ("[2/N][Attention] Enable masked MHA for sparse MLA
+ * prefills", Purpose section; "[Perf][GLM-5.3-Flash] ...", commit messages):
+ * token t, head h attends over every key x with x <= q_pos_offset + t and
+ * x in sel(t), using per-head keys and values.  Supported geometry:
+ * dn = 256, dr = 0, dv = 256 (the NoPE layout): the key is k_nope itself,
+ * read in place (no K concat); k_pe is not read (it may be NULL).
+ *
+ *   q       bf16 [T, H, dn + dr];  k_nope bf16 [S, H, dn];  v bf16 [S, H, dv]
+ *   topk    int32 [T, ld] (cols used)
+ *   mask_ws uint32 [T, ceil(S / 32)] caller-owned workspace of
+ *           dsa_masked_mha_workspace_bytes(T, S) bytes; overwritten with the
+ *           bit-packed top-k membership (bit x % 32 of word x / 32 of row t)
+ *   out     bf16 [T, H, dv];  lse fp32 [T, H]
+ * Two kernels are enqueued: the mask scatter, then the attention. */
+int dsa_masked_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_pe,
+                           const uint16_t* v, const int32_t* topk, int64_t ld, int T, int S, int H,
+                           int dn, int dr, int dv, int cols, int64_t q_pos_offset, float scale,
+                           uint32_t* mask_ws, uint16_t* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_PREFILL_H */

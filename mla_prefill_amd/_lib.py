@@ -1,0 +1,151 @@
+"""ctypes binding of libdsa_prefill.so (argument marshalling only).
+
+Each function has the name of the C entry point it calls and takes torch
+tensors that live on the GPU; it passes their data pointers, sizes and the
+current HIP stream to the library and raises ``DsaError`` on a non-zero status.
+Every step of the computation runs in the library's HIP kernels.  There is no
+fallback: if the library is missing, importing this module fails loudly.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa_prefill.so")
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        f"{_LIB_PATH} is missing: build it with `python -m mla_prefill_amd.build` "
+        "(hipcc --offload-arch=gfx950); there is no non-HIP fallback")
+
+lib = ctypes.CDLL(_LIB_PATH)
+
+_i32, _i64, _f32, _vp, _sz = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+_SIGNATURES = {
+    "dsa_abi_version": ([], _i32),
+    "dsa_status_string": ([_i32], ctypes.c_char_p),
+    "dsa_union_pad": ([_i32, _i32], _i32),
+    "dsa_masked_mha_workspace_bytes": ([_i32, _i32], _sz),
+    "dsa_build_group_union": ([_vp, _i64, _i32, _i32, _i32, _i64, _i32, _i32, _vp, _vp, _vp, _vp], _i32),
+    "dsa_sparse_prefill_grouped": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                    _vp, _vp, _vp], _i32),
+    "dsa_sparse_prefill_pertoken": ([_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _f32,
+                                     _vp, _vp, _vp], _i32),
+    "dsa_masked_mha_prefill": ([_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                _i64, _f32, _vp, _vp, _vp, _vp], _i32),
+}
+for _name, (_args, _ret) in _SIGNATURES.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _ret
+
+EXPORTED = tuple(_SIGNATURES)
+
+
+class DsaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: status {status} ({lib.dsa_status_string(status).decode()})")
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise DsaError(fn, status)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if t.numel() and not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if t.numel() and not t.is_contiguous() and t.dim() > 1 and t.stride(-1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _bits(t):
+    """bf16 tensors travel as their 16-bit patterns."""
+    if t is None:
+        return None
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"expected bf16 bits, got {t.dtype}")
+    return t
+
+
+def _topk_ld(topk):
+    if topk.dtype != torch.int32:
+        raise TypeError("topk must be int32")
+    if topk.dim() != 2 or topk.stride(1) != 1:
+        raise ValueError("topk must be [T, ld] with unit column stride")
+    return topk.stride(0) if topk.shape[0] > 1 else max(topk.shape[1], 1)
+
+
+def dsa_abi_version() -> int:
+    return lib.dsa_abi_version()
+
+
+def dsa_status_string(status: int) -> str:
+    return lib.dsa_status_string(status).decode()
+
+
+def dsa_union_pad(G: int, cols: int) -> int:
+    v = lib.dsa_union_pad(G, cols)
+    _check("dsa_union_pad", v if v < 0 else 0)
+    return v
+
+
+def dsa_masked_mha_workspace_bytes(T: int, S: int) -> int:
+    return lib.dsa_masked_mha_workspace_bytes(T, S)
+
+
+def dsa_build_group_union(topk, S, q_pos_offset, G, union_idx, union_len, head_group_mask,
+                          cols=None, stream=None):
+    T = topk.shape[0]
+    cols = topk.shape[1] if cols is None else cols
+    _check("dsa_build_group_union", lib.dsa_build_group_union(
+        _ptr(topk), _topk_ld(topk), T, cols, S, q_pos_offset, G, union_idx.shape[1],
+        _ptr(union_idx), _ptr(union_len), _ptr(head_group_mask), _stream(stream)))
+
+
+def dsa_sparse_prefill_grouped(q, kv, union_idx, union_len, head_group_mask, scale, out, lse,
+                               stream=None):
+    T, H, d_qk = q.shape
+    S = kv.shape[0]
+    _check("dsa_sparse_prefill_grouped", lib.dsa_sparse_prefill_grouped(
+        _ptr(_bits(q)), _ptr(_bits(kv)), _ptr(union_idx), _ptr(union_len), _ptr(head_group_mask),
+        T, H, S, union_idx.shape[1], d_qk, out.shape[2], scale, _ptr(_bits(out)), _ptr(lse),
+        _stream(stream)))
+
+
+def dsa_sparse_prefill_pertoken(q, kv, topk, q_pos_offset, scale, out, lse, cols=None, stream=None):
+    T, H, d_qk = q.shape
+    S = kv.shape[0]
+    cols = topk.shape[1] if cols is None else cols
+    _check("dsa_sparse_prefill_pertoken", lib.dsa_sparse_prefill_pertoken(
+        _ptr(_bits(q)), _ptr(_bits(kv)), _ptr(topk), _topk_ld(topk), T, H, S, cols, q_pos_offset,
+        d_qk, out.shape[2], scale, _ptr(_bits(out)), _ptr(lse), _stream(stream)))
+
+
+def dsa_masked_mha_prefill(q, k_nope, k_pe, v, topk, q_pos_offset, scale, mask_ws, out, lse,
+                           cols=None, stream=None):
+    T, H, dqk = q.shape
+    S, _, dn = k_nope.shape
+    dr = 0 if k_pe is None else k_pe.shape[-1]
+    dv = v.shape[2]
+    cols = topk.shape[1] if cols is None else cols
+    _check("dsa_masked_mha_prefill", lib.dsa_masked_mha_prefill(
+        _ptr(_bits(q)), _ptr(_bits(k_nope)), _ptr(_bits(k_pe)), _ptr(_bits(v)), _ptr(topk),
+        _topk_ld(topk), T, S, H, dn, dr, dv, cols, q_pos_offset, scale, _ptr(mask_ws),
+        _ptr(_bits(out)), _ptr(lse), _stream(stream)))

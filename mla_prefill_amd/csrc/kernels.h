@@ -1,0 +1,42 @@
+// Internal launchers of the HIP kernels (called by the C-ABI layer in api.cpp
+// after it has validated every argument).  Each enqueues on `stream`, never
+// allocates, never synchronizes, and returns hipGetLastError() of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+hipError_t launch_build_union(const int32_t* topk, int64_t ld, int T, int cols, int S,
+                              int64_t q_pos_offset, int G, int union_pad, int32_t* union_idx,
+                              int32_t* union_len, uint8_t* head_group_mask, hipStream_t stream);
+
+hipError_t launch_scatter_topk_bits(const int32_t* topk, int64_t ld, int T, int cols, int S,
+                                    int64_t q_pos_offset, uint32_t* bits, int words,
+                                    hipStream_t stream);
+
+// per-token sparse MQA for H % 16 == 0 (one workgroup per (token, 16-head block))
+hipError_t launch_pertoken_attn(const uint16_t* q, const uint16_t* kv, const int32_t* topk,
+                                int64_t ld, int T, int H, int S, int cols, int64_t q_pos_offset,
+                                float scale, uint16_t* out, float* lse, hipStream_t stream);
+
+// 128-row attention over a per-workgroup key list.  Grouped mode: rows are the
+// 128 pseudo-heads of a group, keys the group's union list, and each row is
+// restricted by its token's bit of head_group_mask.  Per-token mode (H = 128):
+// rows are the token's heads and keys its top-k row.
+hipError_t launch_grouped_attn(const uint16_t* q, const uint16_t* kv, const int32_t* union_idx,
+                               const int32_t* union_len, const uint8_t* head_group_mask, int T,
+                               int H, int S, int union_pad, float scale, uint16_t* out, float* lse,
+                               hipStream_t stream);
+hipError_t launch_pertoken_rows128(const uint16_t* q, const uint16_t* kv, const int32_t* topk,
+                                   int64_t ld, int T, int S, int cols, int64_t q_pos_offset,
+                                   float scale, uint16_t* out, float* lse, hipStream_t stream);
+
+// masked dense MHA, qk 256 (nope 256, rope 0), v 256, mask = causal AND top-k bit
+hipError_t launch_masked_mha(const uint16_t* q, const uint16_t* k_nope, const uint16_t* v,
+                             const uint32_t* bits, int words, int T, int S, int H,
+                             int64_t q_pos_offset, float scale, uint16_t* out, float* lse,
+                             hipStream_t stream);
+
+}  // namespace dsa

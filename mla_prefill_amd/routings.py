@@ -1,0 +1,76 @@
+"""The three routings of DSA sparse prefill, with torch-allocated outputs.
+
+Allocation and argument marshalling only: every step runs in the HIP kernels
+of libdsa_prefill.so through the C ABI (``mla_prefill_amd._lib``).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+
+
+@dataclass
+class UnionBuffers:
+    union_idx: torch.Tensor   # int32 [NG, union_pad]
+    union_len: torch.Tensor   # int32 [NG]
+    mask: torch.Tensor        # uint8 [NG, union_pad]
+
+
+def alloc_union(T: int, G: int, cols: int, device="cuda") -> UnionBuffers:
+    NG = -(-T // G)
+    pad = _lib.dsa_union_pad(G, cols)
+    return UnionBuffers(torch.empty((NG, pad), dtype=torch.int32, device=device),
+                        torch.empty((NG,), dtype=torch.int32, device=device),
+                        torch.empty((NG, pad), dtype=torch.uint8, device=device))
+
+
+def alloc_out(T: int, H: int, dv: int, device="cuda"):
+    return (torch.empty((T, H, dv), dtype=torch.bfloat16, device=device),
+            torch.empty((T, H), dtype=torch.float32, device=device))
+
+
+def build_group_union(topk, S: int, q_pos_offset: int, G: int, bufs: UnionBuffers | None = None,
+                      stream=None) -> UnionBuffers:
+    T, cols = topk.shape
+    bufs = bufs or alloc_union(T, G, cols, topk.device)
+    _lib.dsa_build_group_union(topk, S, q_pos_offset, G, bufs.union_idx, bufs.union_len, bufs.mask,
+                               stream=stream)
+    return bufs
+
+
+def grouped(q, kv, topk, q_pos_offset: int, scale: float, bufs: UnionBuffers | None = None,
+            out=None, lse=None, stream=None):
+    """Union/mask build followed by grouped attention (G = 128 / H)."""
+    T, H, _ = q.shape
+    G = 128 // H
+    bufs = build_group_union(topk, kv.shape[0], q_pos_offset, G, bufs, stream)
+    if out is None:
+        out, lse = alloc_out(T, H, 512, q.device)
+    _lib.dsa_sparse_prefill_grouped(q, kv, bufs.union_idx, bufs.union_len, bufs.mask, scale, out, lse,
+                                    stream=stream)
+    return out, lse, bufs
+
+
+def pertoken(q, kv, topk, q_pos_offset: int, scale: float, out=None, lse=None, stream=None):
+    T, H, _ = q.shape
+    if out is None:
+        out, lse = alloc_out(T, H, 512, q.device)
+    _lib.dsa_sparse_prefill_pertoken(q, kv, topk, q_pos_offset, scale, out, lse, stream=stream)
+    return out, lse
+
+
+def masked_mha(q, k_nope, k_pe, v, topk, q_pos_offset: int, scale: float, mask_ws=None, out=None,
+               lse=None, stream=None):
+    T, H, _ = q.shape
+    S = k_nope.shape[0]
+    if mask_ws is None:
+        mask_ws = torch.empty((T, (S + 31) // 32), dtype=torch.int32, device=q.device)
+    if out is None:
+        out, lse = alloc_out(T, H, v.shape[2], q.device)
+    _lib.dsa_masked_mha_prefill(q, k_nope, k_pe, v, topk, q_pos_offset, scale, mask_ws, out, lse,
+                                stream=stream)
+    return out, lse, mask_ws

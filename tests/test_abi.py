@@ -1,0 +1,148 @@
+"""The C-ABI library: exports and host-side argument checks (CPU only).
+
+Every call below is rejected on the host before any HIP call, so it runs
+without a GPU.  No compute call is made here.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa_prefill.h")
+LIB = os.path.join(ROOT, "mla_prefill_amd", "libdsa_prefill.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libdsa_prefill.so not built")
+
+OK, NULL, SHAPE, UNSUP, ALIGN = 0, -1, -2, -3, -4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from mla_prefill_amd import _lib
+    return _lib.lib
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("dsa_build_group_union", "dsa_sparse_prefill_grouped", "dsa_sparse_prefill_pertoken",
+              "dsa_masked_mha_prefill"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (dsa_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        getattr(lib, name)  # resolvable through the dynamic loader too
+
+
+def test_binding_covers_every_declared_symbol():
+    from mla_prefill_amd import _lib
+    assert set(declared_functions()) == set(_lib.EXPORTED)
+
+
+def test_helpers(lib):
+    from mla_prefill_amd import _lib
+    assert _lib.dsa_abi_version() == 1
+    assert _lib.dsa_union_pad(8, 2048) == 16384
+    assert _lib.dsa_union_pad(8, 2176) == 17408
+    assert _lib.dsa_union_pad(1, 1) == 64
+    assert lib.dsa_union_pad(0, 5) == SHAPE and lib.dsa_union_pad(9, 5) == SHAPE
+    assert lib.dsa_union_pad(8, -1) == SHAPE and lib.dsa_union_pad(8, 2**30) == SHAPE
+    assert _lib.dsa_masked_mha_workspace_bytes(16384, 16384) == 16384 * 512 * 4
+    assert _lib.dsa_masked_mha_workspace_bytes(3, 33) == 3 * 2 * 4
+    for s in (0, -1, -2, -3, -4, -5, 7):
+        assert isinstance(_lib.dsa_status_string(s), str)
+
+
+P = 0x10000  # a non-null, 16-byte aligned fake address: never dereferenced on these paths
+
+
+def union_call(lib, topk=P, ld=32, T=64, cols=32, S=64, P0=0, G=8, pad=256, ui=P, ul=P, mk=P):
+    return lib.dsa_build_group_union(topk, ld, T, cols, S, P0, G, pad, ui, ul, mk, None)
+
+
+def test_union_validation(lib):
+    assert union_call(lib, T=-1) == SHAPE
+    assert union_call(lib, S=0) == SHAPE
+    assert union_call(lib, ld=31) == SHAPE
+    assert union_call(lib, P0=-1) == SHAPE
+    assert union_call(lib, G=0) == SHAPE and union_call(lib, G=9) == SHAPE
+    assert union_call(lib, pad=192) == SHAPE          # < G * cols
+    assert union_call(lib, pad=257) == SHAPE          # not a multiple of 64
+    assert union_call(lib, T=0) == OK                 # nothing to do, nothing enqueued
+    assert union_call(lib, topk=None) == NULL
+    assert union_call(lib, ui=None) == NULL
+    assert union_call(lib, ul=None) == NULL
+    assert union_call(lib, mk=None) == NULL
+    assert union_call(lib, topk=P + 2) == ALIGN
+    assert union_call(lib, ui=P + 1) == ALIGN
+
+
+def grouped_call(lib, q=P, kv=P, ui=P, ul=P, mk=P, T=64, H=16, S=64, pad=256, dqk=576, dv=512,
+                 out=P, lse=P):
+    return lib.dsa_sparse_prefill_grouped(q, kv, ui, ul, mk, T, H, S, pad, dqk, dv, 0.1, out, lse, None)
+
+
+def test_grouped_validation(lib):
+    for H in (8, 24, 48, 256):
+        assert grouped_call(lib, H=H) == UNSUP
+    assert grouped_call(lib, dqk=512) == UNSUP and grouped_call(lib, dv=256) == UNSUP
+    assert grouped_call(lib, T=-3) == SHAPE and grouped_call(lib, S=0) == SHAPE
+    assert grouped_call(lib, T=0) == OK
+    for kw in ("q", "kv", "ui", "ul", "mk", "out", "lse"):
+        assert grouped_call(lib, **{kw: None}) == NULL
+    assert grouped_call(lib, q=P + 8) == ALIGN
+    assert grouped_call(lib, kv=P + 2) == ALIGN
+    assert grouped_call(lib, out=P + 4) == ALIGN
+    assert grouped_call(lib, lse=P + 2) == ALIGN
+
+
+def pertoken_call(lib, q=P, kv=P, tk=P, ld=32, T=64, H=16, S=64, cols=32, P0=0, dqk=576, dv=512,
+                  out=P, lse=P):
+    return lib.dsa_sparse_prefill_pertoken(q, kv, tk, ld, T, H, S, cols, P0, dqk, dv, 0.1, out, lse, None)
+
+
+def test_pertoken_validation(lib):
+    for H in (8, 24, 136, 0):
+        assert pertoken_call(lib, H=H) == UNSUP
+    assert pertoken_call(lib, dqk=192) == UNSUP
+    assert pertoken_call(lib, ld=16) == SHAPE and pertoken_call(lib, cols=-1) == SHAPE
+    assert pertoken_call(lib, P0=-5) == SHAPE
+    assert pertoken_call(lib, T=0) == OK
+    for kw in ("q", "kv", "tk", "out", "lse"):
+        assert pertoken_call(lib, **{kw: None}) == NULL
+    assert pertoken_call(lib, q=P + 2) == ALIGN and pertoken_call(lib, tk=P + 1) == ALIGN
+
+
+def mha_call(lib, q=P, kn=P, kp=None, v=P, tk=P, ld=32, T=64, S=64, H=16, dn=256, dr=0, dv=256,
+             cols=32, P0=0, ws=P, out=P, lse=P):
+    return lib.dsa_masked_mha_prefill(q, kn, kp, v, tk, ld, T, S, H, dn, dr, dv, cols, P0, 0.0625, ws,
+                                      out, lse, None)
+
+
+def test_masked_mha_validation(lib):
+    assert mha_call(lib, dn=192, dr=64) == UNSUP      # rope > 0: not in the first build
+    assert mha_call(lib, dn=128) == UNSUP and mha_call(lib, dv=128) == UNSUP
+    assert mha_call(lib, H=0) == SHAPE and mha_call(lib, ld=8) == SHAPE
+    assert mha_call(lib, T=0) == OK
+    for kw in ("q", "kn", "v", "tk", "ws", "out", "lse"):
+        assert mha_call(lib, **{kw: None}) == NULL
+    assert mha_call(lib, kn=P + 2) == ALIGN and mha_call(lib, ws=P + 2) == ALIGN
+
+
+def test_library_links_only_hip_runtime():
+    out = subprocess.run(["ldd", LIB], capture_output=True, text=True).stdout
+    assert "libamdhip64" in out
+    assert "torch" not in out and "python" not in out

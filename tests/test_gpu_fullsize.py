@@ -1,0 +1,102 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py times.
+
+* union list / length / mask: bit-exact over every group (oracle over all groups);
+* grouped and per-token attention: sampled tokens (head and tail of the
+  sequence, the partial last group, random tokens) against the fp64 oracle;
+* grouped == per-token over every token, checked on the GPU outputs;
+* masked MHA: sampled tokens against the dense-mask oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import CONFIGS, make_case
+from tests.gpu_helpers import OUT_RTOL, check_attention, dev_bf16, dev_i32
+
+pytestmark = pytest.mark.gpu
+
+MQA = ["c2_dsv32", "c3_glm16k", "c3w_glm16k_uniform", "c5_long"]
+
+
+@pytest.fixture(scope="module", params=MQA)
+def full(request):
+    """Inputs and GPU outputs of one configuration (module-scoped: pytest groups tests by it)."""
+    name = request.param
+    print(f"[{name}] generating inputs and running both routings", flush=True)
+    yield name, _run(name)
+    torch.cuda.empty_cache()
+
+
+def _run(name):
+    from mla_prefill_amd import routings
+    c = make_case(CONFIGS[name])
+    cfg = c.cfg
+    q, kv, tk = dev_bf16(c.q), dev_bf16(c.kv), dev_i32(c.topk)
+    og, lg, bufs = routings.grouped(q, kv, tk, cfg.q_pos_offset, cfg.scale)
+    op, lp = routings.pertoken(q, kv, tk, cfg.q_pos_offset, cfg.scale)
+    torch.cuda.synchronize()
+    return c, (og, lg), (op, lp), bufs
+
+
+def sample_tokens(T, G, n_random=24, seed=0):
+    rng = np.random.default_rng(seed)
+    last_group = ((T - 1) // G) * G
+    toks = set(range(0, min(T, 4))) | set(range(max(0, T - 4), T)) | set(range(last_group, T))
+    toks |= set(rng.choice(T, size=min(T, n_random), replace=False).tolist())
+    return sorted(toks)
+
+
+def test_union_full(full):
+    name, (c, _, _, bufs) = full
+    cfg = c.cfg
+    print(f"[{name}] union oracle over {cfg.NG} groups", flush=True)
+    ui, ul, mk = oracle.group_union_mask(c.topk, cfg.S, cfg.q_pos_offset, cfg.G)
+    np.testing.assert_array_equal(bufs.union_len.cpu().numpy(), ul)
+    np.testing.assert_array_equal(bufs.union_idx.cpu().numpy(), ui)
+    np.testing.assert_array_equal(bufs.mask.cpu().numpy(), mk)
+
+
+def test_attention_sampled(full):
+    name, (c, (og, lg), (op, lp), _) = full
+    cfg = c.cfg
+    toks = sample_tokens(cfg.T, cfg.G)
+    print(f"[{name}] oracle on {len(toks)} sampled tokens", flush=True)
+    ref_out, ref_lse = oracle.pertoken_sparse_mqa(c.q, c.kv, c.topk, cfg.S, cfg.q_pos_offset, cfg.scale,
+                                                  tokens=toks)
+    idx = torch.tensor(toks, device="cuda")
+    check_attention(op[idx], lp[idx], ref_out, ref_lse, f"{name} per-token")
+    check_attention(og[idx], lg[idx], ref_out, ref_lse, f"{name} grouped")
+
+
+def test_grouped_equals_pertoken_everywhere(full):
+    name, (_, (og, lg), (op, lp), _) = full
+    a, b = og.float(), op.float()
+    rel = (torch.linalg.vector_norm(a - b) / torch.linalg.vector_norm(b)).item()
+    assert rel <= OUT_RTOL, rel
+    fin = torch.isfinite(lp)
+    assert torch.equal(fin, torch.isfinite(lg))
+    assert (lg[fin] - lp[fin]).abs().max().item() <= 2e-3
+
+
+def test_masked_mha_full():
+    from mla_prefill_amd import routings
+    c = make_case(CONFIGS["c4_masked_nope"])
+    cfg = c.cfg
+    out, lse, ws = routings.masked_mha(dev_bf16(c.q), dev_bf16(c.k_nope), None, dev_bf16(c.v),
+                                       dev_i32(c.topk), cfg.q_pos_offset, cfg.scale)
+    torch.cuda.synchronize()
+    toks = sample_tokens(cfg.T, cfg.G, n_random=16, seed=1)
+    print(f"[c4] dense-mask oracle on {len(toks)} sampled tokens", flush=True)
+    ref_out, ref_lse = oracle.masked_mha(c.q, c.k_nope, None, c.v, c.topk, cfg.S, cfg.q_pos_offset,
+                                         cfg.scale, tokens=toks)
+    idx = torch.tensor(toks, device="cuda")
+    check_attention(out[idx], lse[idx], ref_out, ref_lse, "c4 masked MHA")
+    # bit-packed selection rows of the sampled tokens
+    wsn = ws.cpu().numpy().view(np.uint32)
+    for t in toks[:8]:
+        row = np.zeros(wsn.shape[1], np.uint32)
+        for x in oracle.selected_positions(c.topk[t], cfg.S, cfg.q_pos_offset + t):
+            row[x // 32] |= np.uint32(1) << np.uint32(x % 32)
+        np.testing.assert_array_equal(wsn[t], row)

@@ -1,0 +1,210 @@
+"""GPU parity of every entry point against the CPU oracle, through the C ABI.
+
+Sizes here finish in seconds on the oracle yet span several kernel tiles and
+end on ragged tails (T not a multiple of the group, top-k widths that are not
+multiples of the tile, -1 padding shuffled through the rows, chunked context).
+Full-size configurations are covered by test_gpu_fullsize.py.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import CONFIGS, make_case
+from synth.gen import normal_bf16, shuffle_rows, topk_locality, topk_uniform, widen
+from tests.gpu_helpers import check_attention, dev_bf16, dev_i32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def R():
+    from mla_prefill_amd import routings
+    return routings
+
+
+def small_mqa(seed, T, S, H, k, cols, G, P0, mode="locality", shuffle=False):
+    rng = np.random.default_rng(seed)
+    q = normal_bf16(rng, (T, H, 576))
+    kv = normal_bf16(rng, (S, 576))
+    if mode == "uniform":
+        topk = topk_uniform(rng, T, S, k, cols, P0)
+    else:
+        topk = topk_locality(rng, T, S, k, cols, G, P0)
+    if shuffle:
+        topk = shuffle_rows(topk, seed + 1)
+    return q, kv, topk
+
+
+MQA_CASES = [
+    # (label, seed, T, S, H, k, cols, P0, mode, shuffle)
+    ("h16_ragged", 1, 203, 203, 16, 96, 100, 0, "locality", False),
+    ("h16_ctx_shuffled", 2, 150, 420, 16, 130, 137, 270, "locality", True),
+    ("h16_uniform", 3, 97, 97, 16, 64, 64, 0, "uniform", False),
+    ("h32", 4, 61, 190, 32, 70, 75, 129, "locality", True),
+    ("h64", 5, 37, 160, 64, 90, 90, 123, "uniform", False),
+    ("h128", 6, 19, 300, 128, 100, 110, 281, "locality", True),
+]
+
+
+@pytest.mark.parametrize("case", MQA_CASES, ids=[c[0] for c in MQA_CASES])
+def test_union_bit_exact(R, case):
+    label, seed, T, S, H, k, cols, P0, mode, shuffle = case
+    G = 128 // H
+    _, _, topk = small_mqa(seed, T, S, H, k, cols, G, P0, mode, shuffle)
+    bufs = R.build_group_union(dev_i32(topk), S, P0, G)
+    ui, ul, mk = oracle.group_union_mask(topk, S, P0, G)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bufs.union_len.cpu().numpy(), ul)
+    np.testing.assert_array_equal(bufs.union_idx.cpu().numpy(), ui)
+    np.testing.assert_array_equal(bufs.mask.cpu().numpy(), mk)
+
+
+@pytest.mark.parametrize("case", MQA_CASES, ids=[c[0] for c in MQA_CASES])
+def test_pertoken_parity(R, case):
+    label, seed, T, S, H, k, cols, P0, mode, shuffle = case
+    q, kv, topk = small_mqa(seed, T, S, H, k, cols, 128 // H, P0, mode, shuffle)
+    scale = 1.0 / 16.0
+    out, lse = R.pertoken(dev_bf16(q), dev_bf16(kv), dev_i32(topk), P0, scale)
+    ref_out, ref_lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, P0, scale)
+    check_attention(out, lse, ref_out, ref_lse, label)
+
+
+@pytest.mark.parametrize("case", MQA_CASES, ids=[c[0] for c in MQA_CASES])
+def test_grouped_parity(R, case):
+    label, seed, T, S, H, k, cols, P0, mode, shuffle = case
+    G = 128 // H
+    q, kv, topk = small_mqa(seed, T, S, H, k, cols, G, P0, mode, shuffle)
+    scale = 1.0 / 16.0
+    out, lse, _ = R.grouped(dev_bf16(q), dev_bf16(kv), dev_i32(topk), P0, scale)
+    # grouped must reproduce per-token attention: compare with the per-token oracle
+    ref_out, ref_lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, P0, scale)
+    check_attention(out, lse, ref_out, ref_lse, label)
+
+
+def test_tiny_config_all_mqa_routings(R):
+    c = make_case(CONFIGS["c1_tiny"])
+    cfg = c.cfg
+    q, kv, tk = dev_bf16(c.q), dev_bf16(c.kv), dev_i32(c.topk)
+    ref_out, ref_lse = oracle.pertoken_sparse_mqa(c.q, c.kv, c.topk, cfg.S, 0, cfg.scale)
+    o1, l1 = R.pertoken(q, kv, tk, 0, cfg.scale)
+    check_attention(o1, l1, ref_out, ref_lse, "c1 per-token")
+    o2, l2, bufs = R.grouped(q, kv, tk, 0, cfg.scale)
+    check_attention(o2, l2, ref_out, ref_lse, "c1 grouped")
+    ui, ul, mk = oracle.group_union_mask(c.topk, cfg.S, 0, cfg.G)
+    np.testing.assert_array_equal(bufs.union_idx.cpu().numpy(), ui)
+    np.testing.assert_array_equal(bufs.union_len.cpu().numpy(), ul)
+    np.testing.assert_array_equal(bufs.mask.cpu().numpy(), mk)
+    og, lg = oracle.grouped_sparse_mqa(c.q, c.kv, ui, ul, mk, cfg.scale)
+    check_attention(o2, l2, og, lg, "c1 grouped vs grouped oracle")
+
+
+def test_empty_and_degenerate_rows(R):
+    rng = np.random.default_rng(9)
+    T, S, H = 21, 40, 16
+    q = normal_bf16(rng, (T, H, 576))
+    kv = normal_bf16(rng, (S, 576))
+    topk = np.full((T, 70), -1, np.int32)
+    topk[3, 5] = 2                 # a single selected row
+    topk[4, :3] = [S + 5, -9, 39]  # nothing valid (39 > position 4)
+    topk[7, 10:18] = np.arange(8)  # every causal position of token 7
+    for t in range(12, T):
+        topk[t, 60:60 + 5] = rng.choice(t + 1, 5, replace=False)
+    scale = 0.0625
+    ref_out, ref_lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, 0, scale)
+    qd, kvd, tkd = dev_bf16(q), dev_bf16(kv), dev_i32(topk)
+    out, lse = R.pertoken(qd, kvd, tkd, 0, scale)
+    check_attention(out, lse, ref_out, ref_lse, "per-token degenerate")
+    out, lse, bufs = R.grouped(qd, kvd, tkd, 0, scale)
+    check_attention(out, lse, ref_out, ref_lse, "grouped degenerate")
+    ui, ul, mk = oracle.group_union_mask(topk, S, 0, 8)
+    np.testing.assert_array_equal(bufs.union_idx.cpu().numpy(), ui)
+    np.testing.assert_array_equal(bufs.mask.cpu().numpy(), mk)
+
+
+def test_single_token_and_single_group(R):
+    rng = np.random.default_rng(10)
+    S, H = 300, 16
+    for T in (1, 8):
+        q = normal_bf16(rng, (T, H, 576))
+        kv = normal_bf16(rng, (S, 576))
+        topk = topk_uniform(rng, T, S, 200, 256, S - T)
+        ref_out, ref_lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, S - T, 0.1)
+        out, lse = R.pertoken(dev_bf16(q), dev_bf16(kv), dev_i32(topk), S - T, 0.1)
+        check_attention(out, lse, ref_out, ref_lse, f"T={T} per-token")
+        out, lse, _ = R.grouped(dev_bf16(q), dev_bf16(kv), dev_i32(topk), S - T, 0.1)
+        check_attention(out, lse, ref_out, ref_lse, f"T={T} grouped")
+
+
+def test_strided_topk_and_wider_buffer(R):
+    """topk with a leading dimension larger than the used columns, and -1 widening."""
+    q, kv, topk = small_mqa(11, 40, 120, 16, 50, 60, 8, 80)
+    wide = widen(topk, 100)
+    scale = 0.07
+    ref_out, ref_lse = oracle.pertoken_sparse_mqa(q, kv, topk, 120, 80, scale)
+    tk = dev_i32(wide)[:, :60]                      # ld = 100, cols = 60
+    out, lse = R.pertoken(dev_bf16(q), dev_bf16(kv), tk, 80, scale)
+    check_attention(out, lse, ref_out, ref_lse, "strided topk")
+    out2, lse2, _ = R.grouped(dev_bf16(q), dev_bf16(kv), dev_i32(wide), 80, scale)
+    check_attention(out2, lse2, ref_out, ref_lse, "wider buffer grouped")
+
+
+def test_deterministic(R):
+    q, kv, topk = small_mqa(12, 64, 200, 16, 100, 120, 8, 136)
+    qd, kvd, tkd = dev_bf16(q), dev_bf16(kv), dev_i32(topk)
+    a = R.pertoken(qd, kvd, tkd, 136, 0.1)
+    b = R.pertoken(qd, kvd, tkd, 136, 0.1)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)) and torch.equal(a[1], b[1])
+    c = R.grouped(qd, kvd, tkd, 136, 0.1)
+    d = R.grouped(qd, kvd, tkd, 136, 0.1)
+    assert torch.equal(c[0].view(torch.int16), d[0].view(torch.int16)) and torch.equal(c[1], d[1])
+
+
+# ---------------------------------------------------------------------------
+# masked dense MHA
+# ---------------------------------------------------------------------------
+
+MHA_CASES = [
+    # (label, seed, T, S, H, k, cols, P0, mode)
+    ("causal_ragged", 20, 150, 150, 2, 40, 45, 0, "locality"),
+    ("chunked_ctx", 21, 100, 230, 3, 64, 70, 130, "uniform"),
+    ("all_selected", 22, 70, 70, 1, 70, 80, 0, "uniform"),
+]
+
+
+@pytest.mark.parametrize("case", MHA_CASES, ids=[c[0] for c in MHA_CASES])
+def test_masked_mha_parity(R, case):
+    label, seed, T, S, H, k, cols, P0, mode = case
+    rng = np.random.default_rng(seed)
+    q = normal_bf16(rng, (T, H, 256))
+    kn = normal_bf16(rng, (S, H, 256))
+    v = normal_bf16(rng, (S, H, 256))
+    topk = (topk_uniform(rng, T, S, k, cols, P0) if mode == "uniform"
+            else topk_locality(rng, T, S, k, cols, 8, P0))
+    topk = shuffle_rows(topk, seed)
+    scale = 1.0 / 16.0
+    out, lse, ws = R.masked_mha(dev_bf16(q), dev_bf16(kn), None, dev_bf16(v), dev_i32(topk), P0, scale)
+    ref_out, ref_lse = oracle.masked_mha(q, kn, None, v, topk, S, P0, scale)
+    check_attention(out, lse, ref_out, ref_lse, label)
+    # the workspace holds exactly the bit-packed selection
+    words = (S + 31) // 32
+    bits = np.zeros((T, words), np.uint32)
+    for t in range(T):
+        for x in oracle.selected_positions(topk[t], S, P0 + t):
+            bits[t, x // 32] |= np.uint32(1) << np.uint32(x % 32)
+    np.testing.assert_array_equal(ws.cpu().numpy().view(np.uint32), bits)
+
+
+def test_masked_mha_equals_pertoken_with_shared_heads(R):
+    """Heads sharing K = V = X: masked MHA must equal per-token sparse attention over X."""
+    rng = np.random.default_rng(23)
+    T, S, H = 90, 130, 2
+    X = normal_bf16(rng, (S, 256))
+    shared = np.ascontiguousarray(np.repeat(X[:, None, :], H, axis=1))
+    q = normal_bf16(rng, (T, H, 256))
+    topk = topk_locality(rng, T, S, 50, 55, 8, S - T)
+    out, lse, _ = R.masked_mha(dev_bf16(q), dev_bf16(shared), None, dev_bf16(shared), dev_i32(topk),
+                               S - T, 0.0625)
+    ref_out, ref_lse = oracle.pertoken_sparse_mqa(q, X, topk, S, S - T, 0.0625, d_v=256)
+    check_attention(out, lse, ref_out, ref_lse, "masked == per-token")
