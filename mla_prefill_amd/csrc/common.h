@@ -52,6 +52,73 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// 32x32x16 bf16: A lane l = row l%32, k-chunk 8*(l/32)..+8; B = col l%32, same chunk;
+// C register j = row 8*(j/4) + 4*(l/32) + j%4, col l%32.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Asynchronous global -> LDS copies (gfx950 LDS DMA).
+//
+// One instruction per wave: lane l copies `size` bytes from its own global
+// address to lds_base + l * size, where lds_base is wave-uniform.  The copies
+// count in vmcnt like any vector load; the kernels wait for them with
+// wait_vmcnt<N>() (N = vector-memory operations issued after the ones needed)
+// and then a workgroup barrier before other waves read the data.  They are
+// written as inline asm so that the compiler does not serialize the pipeline
+// with a full vmcnt(0) before every LDS read; the kernels that use them issue
+// no other vector-memory loads inside their pipelined loops, and use no
+// dynamic register indexing (the copies set M0).
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const lds_u8*)p);
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is named as clobbered on purpose
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+
+// Compiler-only fence: keeps the scheduler from hoisting LDS operand reads of
+// later MFMA groups above it (bounds the registers held by in-flight reads).
+__device__ __forceinline__ void sched_fence() { asm volatile("" : : : "memory"); }
+
+// Opaque to the optimizer: a value passed through here is recomputed inside a
+// loop instead of being hoisted (hoisted per-lane offsets otherwise spill).
+template <typename T>
+__device__ __forceinline__ T loop_local(T x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// transposed 64-bit LDS read (gfx950).  Within each group of 16 lanes, output
+// lane i slot j receives slot i%4 of the 4 elements addressed by lane i/4 + 4j
+// of that group.
+__device__ __forceinline__ u16x4 lds_read_tr16(const void* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)((const lds_u8*)p));
+  return __builtin_bit_cast(u16x4, v);
+}
+
 // Blocks are handed to the 8 XCDs round-robin (block b runs on XCD b % 8).
 // Remap so that every XCD receives a contiguous range of logical block ids:
 // neighbouring work items then share that XCD's L2.
