@@ -34,6 +34,20 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
+// A wave-uniform value or pointer, proven so to the compiler: loads through a
+// uniform pointer become scalar loads (counted in lgkmcnt, not vmcnt).
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+// Read-only global data addressed uniformly by a wave: a pointer into the
+// constant address space (the data is never written while a kernel runs), so
+// its loads go through the scalar cache.
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+__device__ __forceinline__ const_i32* uniform_const(const int32_t* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (const_i32*)(((uint64_t)hi << 32) | lo);
+}
+
 // fp32 -> bf16 bits, round to nearest even (inputs here are finite or +-inf)
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
@@ -65,11 +79,14 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 // address to lds_base + l * size, where lds_base is wave-uniform.  The copies
 // count in vmcnt like any vector load; the kernels wait for them with
 // wait_vmcnt<N>() (N = vector-memory operations issued after the ones needed)
-// and then a workgroup barrier before other waves read the data.  They are
-// written as inline asm so that the compiler does not serialize the pipeline
-// with a full vmcnt(0) before every LDS read; the kernels that use them issue
-// no other vector-memory loads inside their pipelined loops, and use no
-// dynamic register indexing (the copies set M0).
+// and then a workgroup barrier before other waves read the data (or, for a
+// wave reading its own copies, wait_vmcnt_dep, which orders the reads by a
+// data dependency).  They are written as inline asm so that the compiler does
+// not serialize the pipeline with a full vmcnt(0) before every LDS read; the
+// kernels that use them issue no other vector-memory loads inside their
+// pipelined loops, and use no dynamic register indexing (the copies set M0).
+// The copies only write LDS, so they carry no "memory" clobber: that keeps
+// loads of read-only global data eligible for the scalar cache.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
@@ -83,14 +100,14 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory", "m0");
+               : "m0");
 }
 
 __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
                :
                : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory", "m0");
+               : "m0");
 }
 
 // Compiler-only fence: keeps the scheduler from hoisting LDS operand reads of
@@ -108,6 +125,14 @@ __device__ __forceinline__ T loop_local(T x) {
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Wait as above and return `x` unchanged; LDS addresses computed from the
+// result cannot be read before the wait.
+template <int N>
+__device__ __forceinline__ int wait_vmcnt_dep(int x) {
+  asm volatile("s_waitcnt vmcnt(%1)" : "+v"(x) : "n"(N));
+  return x;
 }
 
 // transposed 64-bit LDS read (gfx950).  Within each group of 16 lanes, output
