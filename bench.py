@@ -51,7 +51,22 @@ def parse():
     ap.add_argument("--workload", default="glm16k", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (calibrates HBM byte counters)")
     return ap.parse_args()
+
+
+def calibrate_copy(mib: int) -> None:
+    """A plain elementwise copy of known size: reads and writes mib MiB each (counter calibration)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.add(a, 0.0, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes_read": n * 4, "calibration_copy_bytes_written": n * 4,
+                      "kernel": "elementwise add(a, 0) -> b", "dispatches": 3}), flush=True)
 
 
 def algorithmic_work(case, union_len_sum, mha_case):
@@ -78,6 +93,35 @@ def algorithmic_work(case, union_len_sum, mha_case):
         w["masked_mha"] = {"bound": "mfma",
                            "flops": float(causal_keys.sum()) * m.H * 2 * (m.dn + m.dr + m.dv)}
     return w, nsel
+
+
+KERNEL_SYMBOLS = {  # bench kernel name -> (device symbol, sources)
+    "build_union": ("dsa::build_union_kernel", ["union_builder.hip", "common.h"]),
+    "grouped_attn": ("dsa::rows128_attn_kernel<false>", ["grouped_attn.hip", "common.h"]),
+    "pertoken_attn": ("dsa::pertoken_attn_kernel", ["pertoken_attn.hip", "common.h"]),
+    "masked_mha_routing": ("dsa::masked_mha_kernel", ["masked_mha.hip", "common.h"]),
+}
+
+
+def measured_traffic(kernel: str, workload: str):
+    """L2-to-memory bytes per launch from the committed rocprofv3 counter record, or None when
+    there is no record for this workload or the kernel's source has changed since."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", f"hbm_traffic_{workload}.json")
+    if not os.path.exists(path) or kernel not in KERNEL_SYMBOLS:
+        return None
+    rec = json.load(open(path))
+    sym, files = KERNEL_SYMBOLS[kernel]
+    k = rec["kernels"].get(sym)
+    if k is None:
+        return None
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(root, "mla_prefill_amd", "csrc", f), "rb").read())
+    if h.hexdigest()[:16] != k["source_sha256_16"]:
+        return None
+    return (k["fetch_kib"] * rec["fetch_scale"] + k["write_kib"] * rec["write_scale"]) * 1024.0
 
 
 def cpu_baseline(case, mha_case, budget_s):
@@ -136,6 +180,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if a.calibrate_copy_mib:
+        calibrate_copy(a.calibrate_copy_mib)
+        return
 
     mqa_name, mha_name = WORKLOADS[a.workload]
     t_gen = time.perf_counter()
@@ -217,8 +264,10 @@ def main():
                           "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFS, "algorithmic": wk["flops"]}
     dom = max(kernels, key=lambda k: kernels[k]["ms"])
     d = kernels[dom]
+    traffic = measured_traffic(dom, a.workload)
     roofline = {"kernel": dom, "bound": d["bound"], "achieved": round(d["achieved"], 2), "peak": d["peak"],
-                "unit": d["unit"], "frac": round(d["frac"], 4), "traffic": None}
+                "unit": d["unit"], "frac": round(d["frac"], 4),
+                "traffic": None if traffic is None else round(traffic)}
     routing_tps = {
         "grouped (union build + attention)": T / ((per["build_union"] + per["grouped_attn"]) * 1e-3),
         "per-token": T / (per["pertoken_attn"] * 1e-3),

@@ -108,7 +108,9 @@ int dsa_build_group_union(const int32_t* topk, int64_t ld, int T, int cols, int 
  *   kv        bf16 [S, 576] latent rows; V = the first 512 dims of a row
  *   union_idx, union_len, head_group_mask: as written by dsa_build_group_union
  *             (union_len is clamped to [0, union_pad]; slots holding a
- *             position outside [0, S) are skipped)
+ *             position outside [0, S) are skipped); union_pad must be a
+ *             multiple of 32 (dsa_union_pad gives a multiple of 64) and
+ *             head_group_mask 4-byte aligned
  *   H         16, 32, 64 or 128 (128 % H == 0 and G = 128 / H <= 8)
  *   d_qk, d_v must be 576 and 512
  *   scale     softmax scale applied to q.k

@@ -67,12 +67,12 @@ int dsa_sparse_prefill_grouped(const uint16_t* q, const uint16_t* kv, const int3
                                uint16_t* out, float* lse, void* stream) {
   if (H != 16 && H != 32 && H != 64 && H != 128) return DSA_ERR_UNSUPPORTED;
   if (d_qk != kLatentDim || d_v != kValueDim) return DSA_ERR_UNSUPPORTED;
-  if (T < 0 || S < 1 || union_pad < 0) return DSA_ERR_SHAPE;
+  if (T < 0 || S < 1 || union_pad < 0 || union_pad % 32 != 0) return DSA_ERR_SHAPE;
   if (T == 0) return DSA_OK;
   if (!q || !kv || !union_idx || !union_len || !head_group_mask || !out || !lse)
     return DSA_ERR_NULL;
   if (!aligned_to(q, 16) || !aligned_to(kv, 16) || !aligned_to(out, 16) || !aligned_to(lse, 4) ||
-      !aligned_to(union_idx, 4) || !aligned_to(union_len, 4))
+      !aligned_to(union_idx, 4) || !aligned_to(union_len, 4) || !aligned_to(head_group_mask, 4))
     return DSA_ERR_ALIGN;
   return launch_status(dsa::launch_grouped_attn(q, kv, union_idx, union_len, head_group_mask, T,
                                                 H, S, union_pad, scale, out, lse,

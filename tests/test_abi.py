@@ -100,6 +100,7 @@ def test_grouped_validation(lib):
         assert grouped_call(lib, H=H) == UNSUP
     assert grouped_call(lib, dqk=512) == UNSUP and grouped_call(lib, dv=256) == UNSUP
     assert grouped_call(lib, T=-3) == SHAPE and grouped_call(lib, S=0) == SHAPE
+    assert grouped_call(lib, pad=48) == SHAPE          # union rows must hold whole 32-slot tiles
     assert grouped_call(lib, T=0) == OK
     for kw in ("q", "kv", "ui", "ul", "mk", "out", "lse"):
         assert grouped_call(lib, **{kw: None}) == NULL
@@ -107,6 +108,7 @@ def test_grouped_validation(lib):
     assert grouped_call(lib, kv=P + 2) == ALIGN
     assert grouped_call(lib, out=P + 4) == ALIGN
     assert grouped_call(lib, lse=P + 2) == ALIGN
+    assert grouped_call(lib, mk=P + 2) == ALIGN        # membership bytes are read 4 at a time
 
 
 def pertoken_call(lib, q=P, kv=P, tk=P, ld=32, T=64, H=16, S=64, cols=32, P0=0, dqk=576, dv=512,
