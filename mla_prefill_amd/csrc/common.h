@@ -144,6 +144,20 @@ __device__ __forceinline__ u16x4 lds_read_tr16(const void* p) {
   return __builtin_bit_cast(u16x4, v);
 }
 
+// ---------------------------------------------------------------------------
+// LDS tile layout for row-gathered operands ("8-row groups"):
+//   rows are stored in groups of 8; within a group, 16-byte chunk k of row r
+//   lives in 1 KiB block k / 8 at 128 B * (r % 8) + 16 B * pos, with
+//   pos = (k % 8) ^ swz8(r % 8) ^ (r / 8 % 8).
+// One wave copy (64 lanes x 16 B) fills one 1 KiB block of a group: lane l
+// takes row l / 8 of the group, position l % 8.  With this swizzle the 16-byte
+// MFMA operand reads of 16 or 32 consecutive rows at one chunk, and the
+// transposed reads of 4 consecutive rows x 32 B, hit distinct LDS banks.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz8(int r8) {
+  return ((r8 >> 2) & 1) | (r8 & 2) | (((r8 ^ (r8 >> 1) ^ (r8 >> 2)) & 1) << 2);
+}
+
 // Blocks are handed to the 8 XCDs round-robin (block b runs on XCD b % 8).
 // Remap so that every XCD receives a contiguous range of logical block ids:
 // neighbouring work items then share that XCD's L2.

@@ -18,15 +18,18 @@
 //    shape on gfx950);
 //  * 32-key tiles of K and V (512 B per key row of one head) and the matching
 //    mask words stream through a 3-stage LDS ring by asynchronous global->LDS
-//    DMA, two tiles ahead of the compute; one barrier per tile;
-//  * rows are stored with a per-row chunk rotation (mrot below): the 16-byte
-//    K reads (16 rows, one column) and the transposed V reads (4 rows x 32 B)
-//    are both free of bank conflicts, and every copy instruction fills two
-//    whole rows;
-//  * causal test and top-k bit are applied to the S^T accumulators in
-//    registers; fp32 online softmax in base 2; the bf16 probabilities go
-//    straight from the accumulators into the B operand of O^T = V^T P^T (keys
-//    relabelled consistently), V^T comes from ds_read_b64_tr_b16;
+//    DMA, two tiles ahead of the compute; one barrier per tile.  Each wave
+//    copy moves 128 B of 8 consecutive key rows into the swizzled 8-row-group
+//    layout (common.h), so a lane's source address is its row plus an
+//    immediate, and every operand read is a per-lane base plus an immediate
+//    with no LDS bank conflicts;
+//  * the causal test and the top-k bit select scores in registers (bit-field
+//    insert of -inf); the running max is taken on raw scores and the softmax
+//    scale is folded into one fused multiply-add before the base-2
+//    exponential; O and l are rescaled only when a row's max grows by more
+//    than 2^8; the bf16 probabilities go straight from the accumulators into
+//    the B operand of O^T = V^T P^T (keys relabelled consistently), V^T comes
+//    from ds_read_b64_tr_b16;
 //  * key tiles past the causal diagonal of the tile's last query are never
 //    visited; query tiles run longest first.
 #include "common.h"
@@ -40,20 +43,13 @@ constexpr int kMThreads = 64 * kMWaves;
 constexpr int kMQ = 32 * kMWaves;                     // query rows per workgroup
 constexpr int kMKeys = 32;                            // keys per tile
 constexpr int kMStages = 3;
-constexpr int kMRowBytes = kMD * 2;                   // 512 B rows, 32 chunks of 16 B
-constexpr int kMTileBytes = kMKeys * kMRowBytes;      // K (or V) tile
+constexpr int kMGroupBytes = 8 * kMD * 2;             // 8 key rows of 512 B
+constexpr int kMTileBytes = kMKeys * kMD * 2;         // K (or V) tile: 16 KiB
 constexpr int kMStageBytes = 2 * kMTileBytes;
-constexpr int kMDmaTotal = kMStageBytes / 1024;       // 32 wave copies per tile (2 rows each)
-constexpr int kMDmaPerWave = kMDmaTotal / kMWaves;    // 4
-constexpr int kMOpsPerTile = kMDmaPerWave + 1;        // + the mask-word copy
-static_assert(kMDmaTotal % kMWaves == 0, "copies must split evenly over the waves");
-
-// Chunk c of tile row r is stored at chunk position (c - rot(r)) mod 32 of the
-// row.  With rot(r) = 2 r + r / 8, the 16-byte reads of one chunk by 16
-// consecutive rows hit 16 distinct positions, and the transposed reads of two
-// neighbouring chunks by 4 consecutive rows (a 4-aligned group) hit 8 distinct
-// positions: no LDS bank conflicts for either operand.
-__device__ __forceinline__ int mrot(int r) { return (2 * r + (r >> 3)) & 31; }
+constexpr int kMCopiesPerWave = kMStageBytes / 1024 / kMWaves;  // 4
+constexpr int kMOpsPerTile = kMCopiesPerWave + 1;     // + the mask-word copy
+constexpr float kRescaleSlack = 8.f;                  // rescale O only when the max grows by > 2^8
+static_assert(kMStageBytes == 1024 * kMWaves * kMCopiesPerWave, "copies split evenly over waves");
 
 __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -63,8 +59,10 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
   __shared__ __align__(16) uint8_t stage[kMStages][kMStageBytes];
   __shared__ __align__(16) uint32_t maskw[kMStages][kMWaves][64];
 
+  // longest query tiles first; consecutive blocks take consecutive heads, so the
+  // round-robin XCD dispatch keeps each head on one XCD and balances the work
   const int nqt = (T + kMQ - 1) / kMQ;
-  const int lb = xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
+  const int lb = (int)blockIdx.x;
   const int qt = nqt - 1 - lb / H;
   const int h = lb - (lb / H) * H;
   const int q0 = qt * kMQ;
@@ -77,11 +75,19 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
   if (rpos64 > S - 1) rpos64 = S - 1;
   const int rpos = live ? (int)rpos64 : -1;
 
+  // queries; a negative scale is applied as |scale| on negated queries so that the
+  // running max can be taken on raw scores
+  const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
+  const float sc = fabsf(scale_log2);
   bf16x8 qreg[kMD / 16];
   if (live) {
     const uint16_t* qrow = q + ((size_t)row * H + h) * kMD + 8 * hi;
 #pragma unroll
-    for (int s = 0; s < kMD / 16; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
+    for (int s = 0; s < kMD / 16; ++s) {
+      uint4 w = *reinterpret_cast<const uint4*>(qrow + 16 * s);
+      w.x ^= qsign; w.y ^= qsign; w.z ^= qsign; w.w ^= qsign;
+      qreg[s] = __builtin_bit_cast(bf16x8, w);
+    }
   } else {
 #pragma unroll
     for (int s = 0; s < kMD / 16; ++s) qreg[s] = bf16x8{};
@@ -97,32 +103,44 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
   const int ntiles = (kend + kMKeys - 1) / kMKeys;
   const int mrow = min(row, T - 1);
 
+  // copies: wave w fills K (w < 4) or V (w >= 4) rows 8 (w % 4) .. + 7, blocks 0..3;
+  // lane l takes row l / 8 of the group, position l % 8 (chunk 8 c + pos ^ swizzle)
+  const int cgrp = wave & 3;
+  const int crow = 8 * cgrp + (lane >> 3);
+  const int cchunk = (lane & 7) ^ swz8(lane >> 3) ^ cgrp;
+  const uint16_t* cbase = (wave < 4 ? k : v) + (size_t)h * kMD + 8 * cchunk;
+  const size_t key_stride = (size_t)H * kMD;
+  const uint32_t cdst = (wave < 4 ? 0 : kMTileBytes) + cgrp * kMGroupBytes;
+
   auto issue = [&](int t) {
-    const int k0 = t * kMKeys;
-    uint8_t* st = stage[t % kMStages];
-#pragma unroll
-    for (int u = 0; u < kMDmaPerWave; ++u) {
-      const int i = wave + kMWaves * u;          // copy i: rows 2 i, 2 i + 1 of the K|V stage
-      const int which = i >= kMDmaTotal / 2 ? 1 : 0;
-      const int r = 2 * (i - which * (kMDmaTotal / 2)) + hi;
-      const int c = (m + mrot(r)) & 31;          // lane m of the row fills position m
-      int key = k0 + r;
-      key = key < kend ? key : kend - 1;
-      dma16((which ? v : k) + ((size_t)key * H + h) * kMD + c * 8, lds_addr(st + 1024 * i));
-    }
-    dma4(bits + (size_t)mrow * words + (k0 >> 5), lds_addr(&maskw[t % kMStages][wave][0]));
+    int key = t * kMKeys + crow;
+    key = key < kend ? key : kend - 1;
+    const uint16_t* src = cbase + (size_t)key * key_stride;
+    const uint32_t dst = lds_addr(stage[t % kMStages]) + cdst;
+    // (the global address carries the block offset: an instruction offset would also
+    // move the LDS destination of an LDS-DMA load)
+    dma16(src, dst);
+    dma16(src + 64, dst + 1024);
+    dma16(src + 128, dst + 2048);
+    dma16(src + 192, dst + 3072);
+    dma4(bits + (size_t)mrow * words + ((t * kMKeys) >> 5), lds_addr(&maskw[t % kMStages][wave][0]));
   };
 
-  float m_run = kNegInf, l_run = 0.f;
+  float m_run = kNegInf, l_run = 0.f;  // m_run: reference max of the exponents (log2 units)
   f32x16 o[kMD / 32];
 #pragma unroll
   for (int cb = 0; cb < kMD / 32; ++cb) o[cb] = f32x16{};
 
+  // K reads (A of S^T): row m, chunk 2 s + hi -> 4 bases, one per s % 4, plus (s / 4) KiB
+  const int kx = swz8(m & 7) ^ (m >> 3) ^ hi;
+  int kofs[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) kofs[u] = (m >> 3) * kMGroupBytes + (m & 7) * 128 + 16 * ((2 * u) ^ kx);
+  // transposed V reads: row 16 st + 8 uu + 4 hi + s16 / 4, columns 32 cb + 16 (g16 % 2) + 4 (s16 % 4)
   const int g16 = lane >> 4, s16 = lane & 15;
-  const int vrow = 4 * (g16 >> 1) + (s16 >> 2);         // transposed-read row within a 16-key step
-  const int vchunk = 2 * (g16 & 1) + ((s16 & 3) >> 1);  // chunk within a 32-column block
-  const int vhalf = 8 * (s16 & 1);                      // byte offset within the chunk
-  const int krot = hi - mrot(m);                        // K read: position of chunk 2 s + hi
+  const int vr8 = 4 * hi + (s16 >> 2);
+  const int vx = (2 * (g16 & 1) + ((s16 & 3) >> 1)) ^ swz8(vr8);
+  const int vbase = vr8 * 128 + 8 * (s16 & 1);
 
   if (ntiles > 0) issue(0);
   if (ntiles > 1) issue(1);
@@ -134,72 +152,72 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
     __syncthreads();  // tile t visible to all waves; stage (t + 2) % 3 free
     if (t + 2 < ntiles) issue(t + 2);
 
-    const uint8_t* kt = stage[t % kMStages];
+    // one stage offset per iteration (kept opaque so no per-stage address sets are hoisted)
+    const int sofs = loop_local((t % kMStages) * kMStageBytes);
+    const uint8_t* kt = &stage[0][0] + sofs;
     const uint8_t* vt = kt + kMTileBytes;
     const int k0 = t * kMKeys;
 
     f32x16 sacc = {};
-    const uint8_t* kp = kt + m * kMRowBytes;
-    const int kr = loop_local(krot);
 #pragma unroll
-    for (int s0 = 0; s0 < kMD / 16; s0 += 2) {
-      bf16x8 ka[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-        ka[u] = *reinterpret_cast<const bf16x8*>(kp + 16 * ((2 * (s0 + u) + kr) & 31));
-#pragma unroll
-      for (int u = 0; u < 2; ++u) sacc = mfma32x32x16(ka[u], qreg[s0 + u], sacc);
-      sched_fence();
-    }
-    // sacc[j] = score(key k0 + 8 (j / 4) + 4 hi + j % 4, row)
+    for (int s = 0; s < kMD / 16; ++s)
+      sacc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kt + kofs[s & 3] + 1024 * (s >> 2)), qreg[s], sacc);
+    // sacc[j] = raw score(key k0 + 8 (j / 4) + 4 hi + j % 4, row)
 
-    // bits of this lane's 16 keys: key 8 (j / 4) + 4 hi + j % 4 -> bit 8 (j / 4) + j % 4 of mw
-    const uint32_t mw = maskw[t % kMStages][wave][m] >> (4 * hi);
-    const int lim = rpos - k0 - 4 * hi;  // key offset 8 (j / 4) + j % 4 must be <= lim
+    // allowed keys: top-k bit AND key <= position; bit kk <-> key k0 + 4 hi + kk
+    uint32_t allowed = *reinterpret_cast<const uint32_t*>(
+                           reinterpret_cast<const uint8_t*>(&maskw[0][wave][m]) +
+                           loop_local((t % kMStages) * (int)sizeof(maskw[0]))) >> (4 * hi);
+    const int lim = rpos - k0 - 4 * hi;
+    allowed &= lim >= 31 ? 0xffffffffu : (lim < 0 ? 0u : ((2u << lim) - 1u));
     float mt = kNegInf;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int kk = 8 * (j >> 2) + (j & 3);
-      const bool ok = ((mw >> kk) & 1u) != 0u && kk <= lim;
-      const float val = ok ? sacc[j] * scale_log2 : kNegInf;
+      const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)allowed, kk, 1);  // all ones if allowed
+      // (the element goes through a scalar first: a bit cast applied directly to a
+      // vector element reads element 0 with this compiler)
+      const float raw = sacc[j];
+      const float val = __builtin_bit_cast(float, (sel & __builtin_bit_cast(uint32_t, raw)) |
+                                                      (~sel & 0xff800000u));
       sacc[j] = val;
       mt = fmaxf(mt, val);
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const bool any = m_new != kNegInf;
-    const float alpha = any ? fast_exp2(m_run - m_new) : 1.f;
-    uint16_t pb[16];
+    mt = fmaxf(mt, __shfl_xor(mt, 32)) * sc;
+    // lazy rescale: move the reference max only when this tile exceeds it by > 2^8
+    const bool need = mt > m_run + kRescaleSlack;
+    if (ballot(need) != 0) {
+      // rows that keep their max keep alpha = 1 (m_run may still be -inf there)
+      const float alpha = need ? fast_exp2(m_run - mt) : 1.f;  // 0 when m_run = -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < kMD / 32; ++cb) o[cb] *= alpha;
+      m_run = need ? mt : m_run;
+    }
+    const float nm = m_run == kNegInf ? 0.f : -m_run;
     float ls = 0.f;
+    bf16x8 bop[2];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      pb[j] = any ? f32_to_bf16_bits(fast_exp2(sacc[j] - m_new)) : (uint16_t)0;
-      ls += bf16_bits_to_f32(pb[j]);
+      const float pj = fast_exp2(__builtin_fmaf(sacc[j], sc, nm));
+      ls += pj;
+      bop[j >> 3][j & 7] = (__bf16)pj;
     }
-    ls += __shfl_xor(ls, 32);
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
-#pragma unroll
-    for (int cb = 0; cb < kMD / 32; ++cb) o[cb] *= alpha;
+    l_run += ls + __shfl_xor(ls, 32);
 
     // O^T += V^T P^T: step st covers keys 16 st .. 16 st + 15 with k-slot (hi, i) <->
     // key 16 st + 8 (i / 4) + 4 hi + i % 4, i.e. accumulator registers 8 st .. 8 st + 7
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const u16x8 pv = {pb[8 * st + 0], pb[8 * st + 1], pb[8 * st + 2], pb[8 * st + 3],
-                        pb[8 * st + 4], pb[8 * st + 5], pb[8 * st + 6], pb[8 * st + 7]};
-      const bf16x8 bop = __builtin_bit_cast(bf16x8, pv);
-      const int r0 = 16 * st + vrow, r1 = r0 + 8;
-      const uint8_t* v0 = vt + r0 * kMRowBytes + vhalf;
-      const uint8_t* v1 = vt + r1 * kMRowBytes + vhalf;
-      const int p0 = loop_local(vchunk - mrot(r0)), p1 = loop_local(vchunk - mrot(r1));
 #pragma unroll
       for (int cb = 0; cb < kMD / 32; ++cb) {
-        const u16x4 lo = lds_read_tr16(v0 + 16 * ((4 * cb + p0) & 31));
-        const u16x4 up = lds_read_tr16(v1 + 16 * ((4 * cb + p1) & 31));
-        const u16x8 a = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
-        o[cb] = mfma32x32x16(__builtin_bit_cast(bf16x8, a), bop, o[cb]);
-        if (cb & 1) sched_fence();
+        // rows 16 st + 8 uu + vr8 are in group 2 st + uu; chunk 4 cb + c2 is in block cb / 2
+        const int p0 = loop_local(16 * (vx ^ (4 * (cb & 1)) ^ (2 * st)));
+        const int p1 = loop_local(16 * (vx ^ (4 * (cb & 1)) ^ (2 * st + 1)));
+        const u16x4 lo = lds_read_tr16(vt + (2 * st) * kMGroupBytes + 1024 * (cb >> 1) + vbase + p0);
+        const u16x4 up = lds_read_tr16(vt + (2 * st + 1) * kMGroupBytes + 1024 * (cb >> 1) + vbase + p1);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, u16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
+        o[cb] = mfma32x32x16(a, bop[st], o[cb]);
       }
     }
   }
@@ -212,9 +230,9 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
   for (int cb = 0; cb < kMD / 32; ++cb)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const u16x4 w = {f32_to_bf16_bits(o[cb][4 * jj + 0] * inv), f32_to_bf16_bits(o[cb][4 * jj + 1] * inv),
-                       f32_to_bf16_bits(o[cb][4 * jj + 2] * inv), f32_to_bf16_bits(o[cb][4 * jj + 3] * inv)};
-      *reinterpret_cast<u16x4*>(orow + 32 * cb + 8 * jj) = w;
+      const bf16x4 w = {(__bf16)(o[cb][4 * jj + 0] * inv), (__bf16)(o[cb][4 * jj + 1] * inv),
+                        (__bf16)(o[cb][4 * jj + 2] * inv), (__bf16)(o[cb][4 * jj + 3] * inv)};
+      *reinterpret_cast<bf16x4*>(orow + 32 * cb + 8 * jj) = w;
     }
   if (hi == 0)
     lse[(size_t)row * H + h] = l_run > 0.f ? (m_run + fast_log2(l_run)) * kLn2 : kNegInf;
