@@ -39,6 +39,8 @@
  *  - A token that selects nothing gets out = 0 and lse = -inf.
  *  - out is bf16 (round to nearest even) of the fp32 result; lse is fp32, the
  *    natural log of the sum of exp(scale * q.k) over the token's selection.
+ *  - scale must be finite and nonzero (either sign); other values are
+ *    rejected with DSA_ERR_UNSUPPORTED.
  *  - Arguments are checked on the host before anything is enqueued; a
  *    rejected call enqueues nothing and returns a negative status.
  */
@@ -58,7 +60,7 @@ extern "C" {
 #define DSA_OK 0
 #define DSA_ERR_NULL (-1)        /* a required pointer is NULL */
 #define DSA_ERR_SHAPE (-2)       /* a size or leading dimension is out of range */
-#define DSA_ERR_UNSUPPORTED (-3) /* head count / head dims outside the supported set */
+#define DSA_ERR_UNSUPPORTED (-3) /* head count / head dims / scale outside the supported set */
 #define DSA_ERR_ALIGN (-4)       /* a pointer is not aligned as required */
 #define DSA_ERR_LAUNCH (-5)      /* the HIP runtime rejected a kernel launch */
 

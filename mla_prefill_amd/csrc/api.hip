@@ -12,6 +12,9 @@ inline bool aligned_to(const void* p, uintptr_t a) { return (reinterpret_cast<ui
 
 inline int launch_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH; }
 
+// the kernels fold the scale into exponent FMAs on raw scores: it must be finite and nonzero
+inline bool scale_ok(float s) { return s == s && s != 0.f && s - s == 0.f; }
+
 constexpr int kLatentDim = 576;
 constexpr int kValueDim = 512;
 
@@ -26,7 +29,7 @@ const char* dsa_status_string(int status) {
     case DSA_OK: return "ok";
     case DSA_ERR_NULL: return "a required pointer is NULL";
     case DSA_ERR_SHAPE: return "a size or leading dimension is out of range";
-    case DSA_ERR_UNSUPPORTED: return "unsupported head count or head dimensions";
+    case DSA_ERR_UNSUPPORTED: return "unsupported head count, head dimensions or scale";
     case DSA_ERR_ALIGN: return "a pointer is not aligned as required";
     case DSA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
     default: return "unknown status";
@@ -66,7 +69,7 @@ int dsa_sparse_prefill_grouped(const uint16_t* q, const uint16_t* kv, const int3
                                int H, int S, int union_pad, int d_qk, int d_v, float scale,
                                uint16_t* out, float* lse, void* stream) {
   if (H != 16 && H != 32 && H != 64 && H != 128) return DSA_ERR_UNSUPPORTED;
-  if (d_qk != kLatentDim || d_v != kValueDim) return DSA_ERR_UNSUPPORTED;
+  if (d_qk != kLatentDim || d_v != kValueDim || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
   if (T < 0 || S < 1 || union_pad < 0 || union_pad % 32 != 0) return DSA_ERR_SHAPE;
   if (T == 0) return DSA_OK;
   if (!q || !kv || !union_idx || !union_len || !head_group_mask || !out || !lse)
@@ -84,7 +87,7 @@ int dsa_sparse_prefill_pertoken(const uint16_t* q, const uint16_t* kv, const int
                                 int d_qk, int d_v, float scale, uint16_t* out, float* lse,
                                 void* stream) {
   if (H < 16 || H > 128 || H % 16 != 0) return DSA_ERR_UNSUPPORTED;
-  if (d_qk != kLatentDim || d_v != kValueDim) return DSA_ERR_UNSUPPORTED;
+  if (d_qk != kLatentDim || d_v != kValueDim || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
   if (T < 0 || S < 1 || cols < 0 || ld < cols || q_pos_offset < 0) return DSA_ERR_SHAPE;
   if (T == 0) return DSA_OK;
   if (!q || !kv || (cols > 0 && !topk) || !out || !lse) return DSA_ERR_NULL;
@@ -106,7 +109,7 @@ int dsa_masked_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint
                            int dn, int dr, int dv, int cols, int64_t q_pos_offset, float scale,
                            uint32_t* mask_ws, uint16_t* out, float* lse, void* stream) {
   (void)k_pe;  // dr == 0: the key is k_nope itself
-  if (dn != 256 || dr != 0 || dv != 256) return DSA_ERR_UNSUPPORTED;
+  if (dn != 256 || dr != 0 || dv != 256 || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
   if (H < 1 || T < 0 || S < 1 || cols < 0 || ld < cols || q_pos_offset < 0) return DSA_ERR_SHAPE;
   if (T == 0) return DSA_OK;
   if (!q || !k_nope || !v || (cols > 0 && !topk) || !mask_ws || !out || !lse) return DSA_ERR_NULL;

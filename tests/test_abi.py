@@ -91,8 +91,8 @@ def test_union_validation(lib):
 
 
 def grouped_call(lib, q=P, kv=P, ui=P, ul=P, mk=P, T=64, H=16, S=64, pad=256, dqk=576, dv=512,
-                 out=P, lse=P):
-    return lib.dsa_sparse_prefill_grouped(q, kv, ui, ul, mk, T, H, S, pad, dqk, dv, 0.1, out, lse, None)
+                 out=P, lse=P, scale=0.1):
+    return lib.dsa_sparse_prefill_grouped(q, kv, ui, ul, mk, T, H, S, pad, dqk, dv, scale, out, lse, None)
 
 
 def test_grouped_validation(lib):
@@ -112,8 +112,8 @@ def test_grouped_validation(lib):
 
 
 def pertoken_call(lib, q=P, kv=P, tk=P, ld=32, T=64, H=16, S=64, cols=32, P0=0, dqk=576, dv=512,
-                  out=P, lse=P):
-    return lib.dsa_sparse_prefill_pertoken(q, kv, tk, ld, T, H, S, cols, P0, dqk, dv, 0.1, out, lse, None)
+                  out=P, lse=P, scale=0.1):
+    return lib.dsa_sparse_prefill_pertoken(q, kv, tk, ld, T, H, S, cols, P0, dqk, dv, scale, out, lse, None)
 
 
 def test_pertoken_validation(lib):
@@ -129,8 +129,8 @@ def test_pertoken_validation(lib):
 
 
 def mha_call(lib, q=P, kn=P, kp=None, v=P, tk=P, ld=32, T=64, S=64, H=16, dn=256, dr=0, dv=256,
-             cols=32, P0=0, ws=P, out=P, lse=P):
-    return lib.dsa_masked_mha_prefill(q, kn, kp, v, tk, ld, T, S, H, dn, dr, dv, cols, P0, 0.0625, ws,
+             cols=32, P0=0, ws=P, out=P, lse=P, scale=0.0625):
+    return lib.dsa_masked_mha_prefill(q, kn, kp, v, tk, ld, T, S, H, dn, dr, dv, cols, P0, scale, ws,
                                       out, lse, None)
 
 
@@ -142,6 +142,17 @@ def test_masked_mha_validation(lib):
     for kw in ("q", "kn", "v", "tk", "ws", "out", "lse"):
         assert mha_call(lib, **{kw: None}) == NULL
     assert mha_call(lib, kn=P + 2) == ALIGN and mha_call(lib, ws=P + 2) == ALIGN
+
+
+def test_scale_must_be_finite_and_nonzero(lib):
+    for bad in (0.0, -0.0, float("inf"), float("-inf"), float("nan")):
+        assert grouped_call(lib, scale=bad) == UNSUP
+        assert pertoken_call(lib, scale=bad) == UNSUP
+        assert mha_call(lib, scale=bad) == UNSUP
+    for good in (1e-30, -0.1, 3.0e30):
+        assert grouped_call(lib, scale=good, T=0) == OK
+        assert pertoken_call(lib, scale=good, T=0) == OK
+        assert mha_call(lib, scale=good, T=0) == OK
 
 
 def test_library_links_only_hip_runtime():

@@ -161,6 +161,29 @@ def test_deterministic(R):
     assert torch.equal(c[0].view(torch.int16), d[0].view(torch.int16)) and torch.equal(c[1], d[1])
 
 
+def test_large_score_jump_and_negative_scale(R):
+    """Scores that jump far above everything earlier in the row (one key per affected token
+    scores ~900 raw units on head 0, ~80 in base-2 softmax units, placed late in the row),
+    and a negative softmax scale on the same inputs."""
+    rng = np.random.default_rng(13)
+    T, S, H, P0 = 24, 200, 16, 176
+    q = normal_bf16(rng, (T, H, 576))
+    kv = normal_bf16(rng, (S, 576))
+    topk = topk_uniform(rng, T, S, 120, 128, P0)
+    for t in range(0, T, 3):
+        r = t                                          # a distinct, causally valid row per token
+        kv[r] = np.where(q[t, 0] & 0x8000, 0xC000, 0x4000).astype(np.uint16)  # bf16 -2 / +2
+        topk[t][topk[t] == r] = -1
+        topk[t, 120] = r
+    for scale in (0.0625, -0.0625):
+        ref_out, ref_lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, P0, scale)
+        qd, kvd, tkd = dev_bf16(q), dev_bf16(kv), dev_i32(topk)
+        out, lse = R.pertoken(qd, kvd, tkd, P0, scale)
+        check_attention(out, lse, ref_out, ref_lse, f"per-token score jump, scale {scale}")
+        out, lse, _ = R.grouped(qd, kvd, tkd, P0, scale)
+        check_attention(out, lse, ref_out, ref_lse, f"grouped score jump, scale {scale}")
+
+
 # ---------------------------------------------------------------------------
 # masked dense MHA
 # ---------------------------------------------------------------------------
