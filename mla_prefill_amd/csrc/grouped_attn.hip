@@ -13,76 +13,91 @@
 // token's 128 heads and the key list is its top-k row, filtered by the
 // selection rule (0 <= x < S, x <= position) instead of a membership byte.
 //
-// MI355X design (one workgroup of 8 waves per group, 2 waves per SIMD):
-//  * 32-slot tiles of latent rows (72 x 16 B chunks each, LDS rows padded to
-//    1168 B) stream through a 3-stage LDS ring by asynchronous global->LDS
-//    DMA, issued two tiles ahead; slot indices and membership bytes are
-//    wave-uniform and come through scalar loads;
-//  * QK^T is split by rows: wave w owns rows 16 w .. 16 w + 15 (for H = 16, one
-//    token), keeps their queries in registers and computes S^T = K Q^T with
-//    v_mfma_f32_16x16x32_bf16; membership masking and the fp32 online softmax
-//    (lazy rescaling: only when a row's max grows by more than 2^8) stay in
-//    registers; the bf16 probabilities and per-row rescale factors go to LDS;
-//  * PV is split by value columns: wave w owns columns 64 w .. 64 w + 63 of all
-//    128 rows and computes O^T = V^T P^T with v_mfma_f32_32x32x16_bf16 (the
-//    full-rate shape), V^T from ds_read_b64_tr_b16, P^T from 16-byte reads;
+// MI355X design (one workgroup of 4 waves per group, one wave per SIMD):
+//  * wave w owns rows 32 w .. 32 w + 31 for the whole attention: their
+//    576-dim queries sit in registers as the B operand of S^T = K Q^T, and
+//    O^T (512 columns x 32 rows) accumulates in registers, so no
+//    probabilities or rescale factors cross waves;
+//  * 32-slot tiles of latent rows stream through a 3-stage LDS ring by
+//    asynchronous global->LDS DMA, two tiles ahead of the compute, one
+//    barrier per tile.  Each wave copies one 8-row group of a tile (nine
+//    128-byte blocks per row) into the XOR-swizzled 8-row-group layout
+//    (common.h), so the 16-byte K reads and the transposed V reads are free of
+//    bank conflicts.  The slot indices and membership bytes of a tile arrive
+//    by their own DMA one tile earlier; per-token membership masks then come
+//    from ballots;
+//  * S^T = K Q^T and O^T = V^T P^T both run on v_mfma_f32_32x32x16_bf16 (the
+//    full-rate shape); V^T comes from ds_read_b64_tr_b16, and the bf16
+//    probabilities go straight from the score accumulators into the B
+//    operand (keys relabelled consistently);
+//  * softmax in base 2 on raw scores (the scale folded into the exponent's
+//    FMA; a negative scale negates the queries) against a per-row reference
+//    fixed at the row's first valid scores, so O is written only by MFMAs.
+//    Probabilities may exceed 1 by up to 2^64 (safe for bf16 P and fp32 O and
+//    l); a group with a score beyond that is marked and recomputed by the
+//    exact kernel (rows128_exact.hip), which ordinary inputs never reach;
 //  * longest groups (most union slots) are launched first.
 #include "common.h"
 #include "kernels.h"
 
 namespace dsa {
 
-constexpr int kGDqk = 576;
-constexpr int kGDv = 512;
-constexpr int kGWaves = 8;
-constexpr int kGThreads = 64 * kGWaves;
-constexpr int kGKeys = 32;                            // slots per tile
-constexpr int kGRowBytes = kGDqk * 2 + 16;            // 1168: 72 data chunks + 1 pad chunk
-constexpr int kGSlots = kGRowBytes / 16;              // 73
-constexpr int kGDma = (kGKeys * kGSlots + 63) / 64;   // 37 wave copies per tile
-constexpr int kGDmaPerWave = (kGDma + kGWaves - 1) / kGWaves;  // 5 (3 go to a dummy area)
-constexpr int kGStageBytes = kGDma * 1024;
-constexpr int kGStages = 3;
-constexpr int kGPStride = 40;                         // halves per probability row (32 + 8 pad)
-constexpr float kGSlack = 8.f;                        // lazy-rescale threshold (log2 units)
+constexpr int kRDqk = 576;
+constexpr int kRDv = 512;
+constexpr int kRWaves = 4;
+constexpr int kRThreads = 64 * kRWaves;
+constexpr int kRKeys = 32;                          // slots per tile
+constexpr int kRStages = 3;
+constexpr int kRIdxBufs = 4;                        // index/membership buffers (one tile further ahead)
+constexpr int kRGroupBytes = 8 * kRDqk * 2;         // 9216: one 8-row group
+constexpr int kRStageBytes = 4 * kRGroupBytes;      // one 32-slot tile
+constexpr int kRCopies = kRGroupBytes / 1024;       // 9 row copies per wave per tile
+constexpr float kRSlack = 64.f;                     // log2 of the largest probability allowed
 
 template <bool kPerToken>
-__global__ __launch_bounds__(kGThreads) void rows128_attn_kernel(
+__global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ keys, int64_t keys_ld, const int32_t* __restrict__ union_len,
     const uint8_t* __restrict__ hgmask, int T, int H, int S, int ncols, int64_t q_pos_offset,
     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  __shared__ __align__(16) uint8_t stage[kGStages][kGStageBytes];
-  __shared__ __align__(16) uint16_t pbuf[128 * kGPStride];
-  __shared__ float alpha_s[128];
-  __shared__ float linv_s[128];
-  __shared__ __align__(16) uint8_t dummy[1024];
+  __shared__ __align__(16) uint8_t stage[kRStages][kRStageBytes];
+  // per tile and wave: lanes 0..7 = slot indices 8 w .. 8 w + 7, lanes 8, 9 = their membership bytes
+  __shared__ __align__(16) uint32_t idxw[kRIdxBufs][kRWaves][64];
+  __shared__ int over_any;
 
   const int G = 128 / H;
   const int NG = (T + G - 1) / G;
   const int grp = NG - 1 - xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, n = lane & 15;
+  const int hi = lane >> 5, m = lane & 31;
   const int t0 = grp * G;
+  const int r = 32 * wave + m;  // this lane's row
+  const int ri = r / H;
+  const int rh = r - ri * H;
+  const int tok = t0 + ri;
+  const bool live = tok < T;
+  if (tid == 0) over_any = 0;  // ordered before any use by the loop's (or the final) barrier
 
-  // the row this lane's wave owns for QK^T / softmax
-  const int r_own = 16 * wave + n;
-  const int i_own = r_own / H;
-  const int h_own = r_own - i_own * H;
-  const int tok_own = t0 + i_own;
-  const bool row_live = tok_own < T;
-
-  bf16x8 qreg[kGDqk / 32];
-  if (row_live) {
-    const uint16_t* qrow = q + ((size_t)tok_own * H + h_own) * kGDqk + 8 * g;
+  // queries: row r, dims 16 s + 8 hi .. + 8; a negative scale is applied as |scale| on
+  // negated queries so that the reference can be taken on raw scores
+  const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
+  const float sc = fabsf(scale_log2);
+  bf16x8 qreg[kRDqk / 16];
+  if (live) {
+    const uint16_t* qrow = q + ((size_t)tok * H + rh) * kRDqk + 8 * hi;
 #pragma unroll
-    for (int s = 0; s < kGDqk / 32; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
+    for (int s = 0; s < kRDqk / 16; ++s) {
+      uint4 w = *reinterpret_cast<const uint4*>(qrow + 16 * s);
+      w.x ^= qsign; w.y ^= qsign; w.z ^= qsign; w.w ^= qsign;
+      qreg[s] = __builtin_bit_cast(bf16x8, w);
+    }
   } else {
 #pragma unroll
-    for (int s = 0; s < kGDqk / 32; ++s) qreg[s] = bf16x8{};
+    for (int s = 0; s < kRDqk / 16; ++s) qreg[s] = bf16x8{};
   }
+  // complete the query loads now, before any asynchronous copy is in flight
 #pragma unroll
-  for (int s = 0; s < kGDqk / 32; ++s) asm volatile("" : : "v"(qreg[s]));  // loads done before any copy
+  for (int s = 0; s < kRDqk / 16; ++s) asm volatile("" : : "v"(qreg[s]));
 
   int nkeys;
   if (kPerToken) {
@@ -97,221 +112,176 @@ __global__ __launch_bounds__(kGThreads) void rows128_attn_kernel(
   int64_t pos64 = q_pos_offset + t0;  // per-token mode: the token's position
   if (pos64 > S - 1) pos64 = S - 1;
   const int pos = uniform((int)pos64);
-  const int ntiles = (nkeys + kGKeys - 1) / kGKeys;
-
-  // validity of slot j0 + r as a latent-row index (grouped: a union entry inside [0, S);
-  // per-token: the selection rule) -- wave-uniform, scalar loads
+  const int ntiles = (nkeys + kRKeys - 1) / kRKeys;
+  // validity of slot j holding latent row x (grouped: a union entry inside [0, S);
+  // per-token: the selection rule)
   auto slot_ok = [&](int32_t x, int j) -> bool {
     return j < nkeys && x >= 0 && (kPerToken ? x <= pos : x < S);  // pos <= S - 1
   };
 
-  // this wave's copies of a tile are 5 w .. 5 w + 4: slots 320 w .. 320 w + 319, i.e. at
-  // most 6 consecutive slot rows starting at r_lo
-  const int r_lo = uniform((64 * kGDmaPerWave * wave) / kGSlots);
-  auto issue = [&](int t) {
-    const int j0 = t * kGKeys;
-    int32_t x[6];
-    const_i32* ip = uniform_const(klist + j0 + r_lo);
-    const int avail = min(kGKeys - r_lo, nkeys - j0 - r_lo);  // rows of this tile past r_lo
-    if (avail >= 6) {
+  // the tokens of this wave's rows: 32 w / H and (32 w + 31) / H (two only for H = 16)
+  const int ti0 = (32 * wave) / H, ti1 = (32 * wave + 31) / H;
+  const bool second = ri != ti0;
+
+  // DMA.  Index copy of tile t: lane l < 8 takes slot 8 w + l, lanes 8 and 9 the four
+  // membership bytes of slots 8 w .. + 3 and 8 w + 4 .. + 7 (the others repeat slot 8 w + l % 8;
+  // in per-token mode the list is the top-k row, read no further than its last column).
+  // Row copies of tile t: wave w fills tile rows 8 w .. 8 w + 7 (8-row group w), blocks
+  // 0..8; lane l takes row l / 8, position l % 8.
+  const int crow = lane >> 3;
+  const int cchunk = (lane & 7) ^ swz8(crow) ^ wave;
+  const uint16_t* cbase = kv + 8 * cchunk;
+  const uint32_t cdst = wave * kRGroupBytes;
+  auto issue_idx = [&](int t) {
+    const int j0 = t * kRKeys + 8 * wave;
+    const int32_t* src;
+    if (!kPerToken && lane >= 8 && lane < 10)
+      src = reinterpret_cast<const int32_t*>(mlist + j0) + (lane - 8);
+    else
+      src = klist + min(j0 + (lane & 7), ncols - 1);
+    dma4(src, lds_addr(&idxw[t % kRIdxBufs][wave][0]));
+  };
+  auto issue_rows = [&](int t) {
+    const int32_t x = (int32_t)idxw[t % kRIdxBufs][wave][crow];  // landed (own copy, waited for)
+    const bool ok = slot_ok(x, t * kRKeys + 8 * wave + crow);
+    const uint16_t* src = cbase + (size_t)(ok ? x : 0) * kRDqk;  // invalid slots copy row 0 (masked)
+    const uint32_t dst = lds_addr(stage[t % kRStages]) + cdst;
+    // (the global address carries the block offset: an instruction offset would also
+    // move the LDS destination of an LDS-DMA load)
 #pragma unroll
-      for (int e = 0; e < 6; ++e) x[e] = ip[e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 6; ++e) x[e] = e < avail ? ip[e] : -1;
-    }
-#pragma unroll
-    for (int e = 0; e < 6; ++e) x[e] = slot_ok(x[e], j0 + r_lo + e) ? x[e] : 0;
-    uint8_t* st = stage[t % kGStages];
-#pragma unroll
-    for (int u = 0; u < kGDmaPerWave; ++u) {
-      const int i = kGDmaPerWave * wave + u;
-      if (i < kGDma) {
-        const int r0 = (64 * i) / kGSlots;
-        const int thr = kGSlots * (r0 + 1) - 64 * i;
-        const bool up = lane >= thr;
-        const int r = up ? r0 + 1 : r0;
-        const int c = 64 * i + lane - kGSlots * r;
-        const int e0 = r0 - r_lo;  // 0..4, wave-uniform
-        int32_t x0 = x[0], x1 = x[1];
-#pragma unroll
-        for (int e = 1; e < 5; ++e) {
-          x0 = e == e0 ? x[e] : x0;
-          x1 = e == e0 ? x[e + 1] : x1;
-        }
-        int32_t xr = up ? x1 : x0;
-        if (r >= kGKeys) xr = 0;
-        dma16(kv + (size_t)xr * kGDqk + (c < 72 ? c : 0) * 8, lds_addr(st + 1024 * i));
-      } else {
-        dma16(kv, lds_addr(dummy));  // keeps every wave's copy count per tile equal
-      }
-    }
+    for (int c = 0; c < kRCopies; ++c) dma16(src + 64 * c, dst + 1024 * c);
   };
 
-  // for the row this lane owns: bit 4 kb + jj <-> slot 16 kb + 4 g + jj of tile t is allowed
-  auto allowed_bits = [&](int t) -> uint32_t {
-    const int j0 = t * kGKeys;
-    uint32_t bits = 0;
+  // K reads (A of S^T): key m, dims 16 s + 8 hi -> chunk 2 s + hi: 4 bases (s % 4) + (s / 4) KiB
+  const int kx = swz8(m & 7) ^ (m >> 3) ^ hi;
+  int kofs[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int jb = j0 + 16 * kb;
-      const_i32* ip = uniform_const(klist + jb);
-      int32_t e[16];
-      if (!kPerToken || nkeys - jb >= 16) {  // union lists are padded to whole tiles
-#pragma unroll
-        for (int r = 0; r < 16; ++r) e[r] = ip[r];
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) e[r] = r < nkeys - jb ? ip[r] : -1;
-      }
-      uint32_t vbits = 0;  // validity of the 16 slots
-#pragma unroll
-      for (int r = 0; r < 16; ++r) vbits |= slot_ok(e[r], jb + r) ? (1u << r) : 0u;
-      const uint32_t vb = (vbits >> (4 * g)) & 0xfu;
-      if (kPerToken) {
-        bits |= vb << (4 * kb);
-      } else {
-        // membership bytes of slots 16 kb + 4 g .. + 3
-        const_i32* mp = uniform_const(reinterpret_cast<const int32_t*>(mlist + jb));
-        const uint32_t w0 = (uint32_t)mp[0], w1 = (uint32_t)mp[1], w2 = (uint32_t)mp[2], w3 = (uint32_t)mp[3];
-        const uint32_t w = g == 0 ? w0 : g == 1 ? w1 : g == 2 ? w2 : w3;
-        uint32_t mbits = 0;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) mbits |= ((w >> (8 * jj + i_own)) & 1u) << jj;
-        bits |= (vb & mbits) << (4 * kb);
-      }
-    }
-    return bits;
-  };
+  for (int u = 0; u < 4; ++u) kofs[u] = (m >> 3) * kRGroupBytes + (m & 7) * 128 + 16 * ((2 * u) ^ kx);
+  // transposed V reads: key 16 st + 8 uu + 4 hi + s16 / 4, cols 32 cb + 16 (g16 % 2) + 4 (s16 % 4)
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int vr8 = 4 * hi + (s16 >> 2);
+  const int vx = (2 * (g16 & 1) + ((s16 & 3) >> 1)) ^ swz8(vr8);
+  const int vbase = vr8 * 128 + 8 * (s16 & 1);
 
-  float m_run = kNegInf, l_run = 0.f;  // row r_own (replicated over the 4 lane groups)
-  f32x16 o[2][4];                      // [col block][row block]
+  float m_ref = kNegInf;  // row r's reference (log2 units), equal in both halves
+  float l_run = 0.f;      // this lane's partial sum (its 16 keys of every tile)
+  bool over = false;
+  f32x16 o[kRDv / 32];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) o[cb][rb] = f32x16{};
+  for (int cb = 0; cb < kRDv / 32; ++cb) o[cb] = f32x16{};
 
-  const int hi = lane >> 5, m = lane & 31;
-  const int koff = n * kGRowBytes + 16 * g;  // K read: row n of a 16-slot block, chunk 4 s + g
-  // transposed V reads: row 8 hi + s16 / 4 (+4), columns 64 w + 32 cb + 16 (g16 % 2) + 4 (s16 % 4)
-  const int voff = (8 * hi + ((lane & 15) >> 2)) * kGRowBytes +
-                   2 * (64 * wave + 16 * (g & 1) + 4 * (lane & 3));
-  const int poff = m * kGPStride + 8 * hi;   // P^T read: row 32 rb + m, slots 16 ks + 8 hi .. + 8
-
-  if (ntiles > 0) issue(0);
-  if (ntiles > 1) issue(1);
-
+  if (ntiles > 0) {
+    issue_idx(0);
+    if (ntiles > 1) issue_idx(1);
+    wait_vmcnt<0>();
+    issue_rows(0);
+    if (ntiles > 2) issue_idx(2);
+    if (ntiles > 1) issue_rows(1);
+  }
   for (int t = 0; t < ntiles; ++t) {
+    // tile t and the indices of tile t + 2 (copied before tile t + 1's rows) have landed
     if (t + 1 < ntiles)
-      wait_vmcnt<kGDmaPerWave>();
+      wait_vmcnt<kRCopies>();
     else
       wait_vmcnt<0>();
-    __syncthreads();  // tile t visible; every wave is done with tile t - 1 (stage and P)
-    if (t + 2 < ntiles) issue(t + 2);
-    const uint32_t abits = allowed_bits(t);
+    __syncthreads();  // tile t visible to all waves; stage (t + 2) % 3 and index buffer (t + 3) % 4 free
+    if (t + 3 < ntiles) issue_idx(t + 3);
+    if (t + 2 < ntiles) issue_rows(t + 2);
 
-    const uint8_t* tile = stage[t % kGStages];
-    // ---- scores of this wave's 16 rows over the 32 slots
-    f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int s = 0; s < kGDqk / 32; ++s)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        sacc[kb] = mfma16x16x32(*reinterpret_cast<const bf16x8*>(tile + koff + kb * 16 * kGRowBytes + 64 * s),
-                                qreg[s], sacc[kb]);
-    // sacc[kb][jj] = score(slot 16 kb + 4 g + jj, row r_own)
+    // membership masks of this tile for the wave's two tokens (bit j <-> slot j)
+    uint32_t mk0, mk1;
+    {
+      const int sl = lane & 31;
+      const uint32_t* iw = &idxw[t % kRIdxBufs][sl >> 3][0];
+      const bool ok = slot_ok((int32_t)iw[sl & 7], t * kRKeys + sl);
+      if (kPerToken) {
+        mk0 = mk1 = (uint32_t)ballot(ok);
+      } else {
+        const uint32_t byte = iw[8 + ((sl & 7) >> 2)] >> (8 * (sl & 3));
+        mk0 = (uint32_t)ballot(ok && ((byte >> ti0) & 1u));
+        mk1 = (uint32_t)ballot(ok && ((byte >> ti1) & 1u));
+      }
+    }
+    // bit kk <-> slot 4 hi + kk
+    const uint32_t allowed = (second ? mk1 : mk0) >> (4 * hi);
 
-    float mt = kNegInf;
+    // one stage offset per iteration (kept opaque so no per-stage address sets are hoisted)
+    const int sofs = loop_local((t % kRStages) * kRStageBytes);
+    const uint8_t* kt = &stage[0][0] + sofs;
+    f32x16 sa = {}, sb = {};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const bool ok = ((abits >> (4 * kb + jj)) & 1u) != 0u;
-        const float val = ok ? sacc[kb][jj] * scale_log2 : kNegInf;
-        sacc[kb][jj] = val;
-        mt = fmaxf(mt, val);
-      }
+    for (int s = 0; s < kRDqk / 16; s += 2) {
+      sa = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kt + kofs[s & 3] + 1024 * (s >> 2)), qreg[s], sa);
+      sb = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kt + kofs[(s + 1) & 3] + 1024 * ((s + 1) >> 2)),
+                        qreg[s + 1], sb);
     }
-    mt = max_over_rowgroups(mt);
-    float alpha = 1.f;
-    const bool need = mt > m_run + kGSlack;
-    if (ballot(need) != 0) {
-      const float m_new = need ? mt : m_run;
-      alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf
-      l_run *= alpha;
-      m_run = m_new;
-    }
-    const float msafe = m_run == kNegInf ? 0.f : m_run;
-    float ls = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      bf16x4 pw;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float p = fast_exp2(sacc[kb][jj] - msafe);
-        ls += p;
-        pw[jj] = (__bf16)p;
-      }
-      *reinterpret_cast<bf16x4*>(pbuf + r_own * kGPStride + 16 * kb + 4 * g) = pw;
-    }
-    l_run += sum_over_rowgroups(ls);
-    if (g == 0) alpha_s[r_own] = alpha;
-    __syncthreads();  // P and alpha of all 128 rows visible
+    f32x16 sacc = sa + sb;  // sacc[j] = raw score(slot 8 (j / 4) + 4 hi + j % 4, row r)
 
-    // ---- O^T[64 w .. 64 w + 63][all rows] += V^T P^T over the 32 slots
+    float ml = kNegInf;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const float al = alpha_s[32 * rb + m];
-      if (ballot(al != 1.f) != 0) {
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) o[cb][rb] *= al;
-      }
+    for (int j = 0; j < 16; ++j) {
+      const int kk = 8 * (j >> 2) + (j & 3);
+      const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)allowed, kk, 1);  // all ones if allowed
+      const float raw = sacc[j];  // (a scalar copy: bit casts of vector elements misread)
+      const float val = __builtin_bit_cast(float, (sel & __builtin_bit_cast(uint32_t, raw)) | (~sel & 0xff800000u));
+      sacc[j] = val;
+      ml = fmaxf(ml, val);
     }
+    ml *= sc;
+    // a row's first valid scores set its reference (its O and l are still zero)
+    if (ballot(m_ref == kNegInf && ml != kNegInf) != 0) {
+      const float mr = fmaxf(ml, __shfl_xor(ml, 32));
+      m_ref = m_ref == kNegInf ? mr : m_ref;
+    }
+    over |= ballot(ml > m_ref + kRSlack) != 0;
+    const float nm = m_ref == kNegInf ? 0.f : -m_ref;
+    bf16x8 bop[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 va[2];
+    for (int j = 0; j < 16; ++j) {
+      const float p = fast_exp2(__builtin_fmaf(sacc[j], sc, nm));
+      l_run += p;
+      bop[j >> 3][j & 7] = (__bf16)p;
+    }
+
+    // O^T += V^T P^T: step st covers slots 16 st .. 16 st + 15 with k-slot (hi, i) <->
+    // slot 16 st + 8 (i / 4) + 4 hi + i % 4, i.e. score registers 8 st .. 8 st + 7
+    const uint8_t* vt = kt;  // V = the first 512 dims of the same rows
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const uint8_t* vp = tile + voff + 16 * ks * kGRowBytes + 64 * cb;
-        const u16x4 lo = lds_read_tr16(vp);
-        const u16x4 up = lds_read_tr16(vp + 4 * kGRowBytes);
-        va[cb] = __builtin_bit_cast(bf16x8, u16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
-      }
+    for (int st = 0; st < 2; ++st) {
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const bf16x8 pb = *reinterpret_cast<const bf16x8*>(pbuf + 32 * rb * kGPStride + poff + 16 * ks);
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) o[cb][rb] = mfma32x32x16(va[cb], pb, o[cb][rb]);
+      for (int cb = 0; cb < kRDv / 32; ++cb) {
+        // rows 16 st + 8 uu + vr8 are in group 2 st + uu; chunk 4 cb + c2 is in block cb / 2
+        const int p0 = 16 * (vx ^ (4 * (cb & 1)) ^ (2 * st));
+        const int p1 = 16 * (vx ^ (4 * (cb & 1)) ^ (2 * st + 1));
+        const u16x4 lo = lds_read_tr16(vt + (2 * st) * kRGroupBytes + 1024 * (cb >> 1) + vbase + p0);
+        const u16x4 up = lds_read_tr16(vt + (2 * st + 1) * kRGroupBytes + 1024 * (cb >> 1) + vbase + p1);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, u16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
+        o[cb] = mfma32x32x16(a, bop[st], o[cb]);
       }
     }
   }
 
-  if (g == 0) {
-    linv_s[r_own] = l_run > 0.f ? 1.f / l_run : 0.f;
-    if (row_live)
-      lse[(size_t)tok_own * H + h_own] = l_run > 0.f ? (m_run + fast_log2(l_run)) * kLn2 : kNegInf;
-  }
+  if (over && lane == 0) over_any = 1;
   __syncthreads();
-
-  // o[cb][rb][j] = O^T[col 64 w + 32 cb + 8 (j / 4) + 4 hi + j % 4][row 32 rb + m]
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const int row = 32 * rb + m;
-    const int i = row / H;
-    const int h = row - i * H;
-    const int tok = t0 + i;
-    if (tok >= T) continue;
-    const float inv = linv_s[row];
-    uint16_t* orow = out + ((size_t)tok * H + h) * kGDv + 64 * wave + 4 * hi;
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const bf16x4 w = {(__bf16)(o[cb][rb][4 * jj + 0] * inv), (__bf16)(o[cb][rb][4 * jj + 1] * inv),
-                          (__bf16)(o[cb][rb][4 * jj + 2] * inv), (__bf16)(o[cb][rb][4 * jj + 3] * inv)};
-        *reinterpret_cast<bf16x4*>(orow + 32 * cb + 8 * jj) = w;
-      }
+  const bool marked = over_any != 0;
+  const float l = l_run + __shfl_xor(l_run, 32);
+  if (!live) return;
+  if (marked) {  // recomputed by the exact kernel
+    if (hi == 0) lse[(size_t)tok * H + rh] = __uint_as_float(kOverflowMark);
+    return;
   }
+  // o[cb][j] = O^T[col 32 cb + 8 (j / 4) + 4 hi + j % 4][row r]
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  uint16_t* orow = out + ((size_t)tok * H + rh) * kRDv + 4 * hi;
+#pragma unroll
+  for (int cb = 0; cb < kRDv / 32; ++cb)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const bf16x4 w = {(__bf16)(o[cb][4 * jj + 0] * inv), (__bf16)(o[cb][4 * jj + 1] * inv),
+                        (__bf16)(o[cb][4 * jj + 2] * inv), (__bf16)(o[cb][4 * jj + 3] * inv)};
+      *reinterpret_cast<bf16x4*>(orow + 32 * cb + 8 * jj) = w;
+    }
+  if (hi == 0) lse[(size_t)tok * H + rh] = l > 0.f ? (m_ref + fast_log2(l)) * kLn2 : kNegInf;
 }
 
 hipError_t launch_grouped_attn(const uint16_t* q, const uint16_t* kv, const int32_t* union_idx,
@@ -321,20 +291,26 @@ hipError_t launch_grouped_attn(const uint16_t* q, const uint16_t* kv, const int3
   const int G = 128 / H;
   const int NG = (T + G - 1) / G;
   if (NG == 0) return hipSuccess;
-  hipLaunchKernelGGL(rows128_attn_kernel<false>, dim3(NG), dim3(kGThreads), 0, stream, q, kv,
+  hipLaunchKernelGGL(rows128_attn_kernel<false>, dim3(NG), dim3(kRThreads), 0, stream, q, kv,
                      union_idx, (int64_t)union_pad, union_len, head_group_mask, T, H, S, union_pad,
                      (int64_t)0, scale * kLog2e, out, lse);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_rows128_exact(q, kv, union_idx, (int64_t)union_pad, union_len, head_group_mask, T, H,
+                              S, union_pad, 0, scale, out, lse, stream);
 }
 
 hipError_t launch_pertoken_rows128(const uint16_t* q, const uint16_t* kv, const int32_t* topk,
                                    int64_t ld, int T, int S, int cols, int64_t q_pos_offset,
                                    float scale, uint16_t* out, float* lse, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(rows128_attn_kernel<true>, dim3(T), dim3(kGThreads), 0, stream, q, kv, topk,
+  hipLaunchKernelGGL(rows128_attn_kernel<true>, dim3(T), dim3(kRThreads), 0, stream, q, kv, topk,
                      ld, (const int32_t*)nullptr, (const uint8_t*)nullptr, T, 128, S, cols,
                      q_pos_offset, scale * kLog2e, out, lse);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_rows128_exact(q, kv, topk, ld, nullptr, nullptr, T, 128, S, cols, q_pos_offset, scale,
+                              out, lse, stream);
 }
 
 }  // namespace dsa

@@ -33,6 +33,17 @@ hipError_t launch_pertoken_rows128(const uint16_t* q, const uint16_t* kv, const 
                                    int64_t ld, int T, int S, int cols, int64_t q_pos_offset,
                                    float scale, uint16_t* out, float* lse, hipStream_t stream);
 
+// The fast 128-row kernel fixes each row's softmax reference at the row's first valid
+// scores.  A group in which a later score exceeds that reference by more than 2^64 gets
+// this NaN bit pattern in the LSE of all its rows; launch_rows128_exact then recomputes
+// exactly those groups with a running-max softmax (other workgroups return at once).
+// hgmask == nullptr selects the per-token mode.
+constexpr uint32_t kOverflowMark = 0x7fa5a5a5u;
+hipError_t launch_rows128_exact(const uint16_t* q, const uint16_t* kv, const int32_t* keys,
+                                int64_t keys_ld, const int32_t* union_len, const uint8_t* hgmask,
+                                int T, int H, int S, int ncols, int64_t q_pos_offset, float scale,
+                                uint16_t* out, float* lse, hipStream_t stream);
+
 // masked dense MHA, qk 256 (nope 256, rope 0), v 256, mask = causal AND top-k bit
 hipError_t launch_masked_mha(const uint16_t* q, const uint16_t* k_nope, const uint16_t* v,
                              const uint32_t* bits, int words, int T, int S, int H,

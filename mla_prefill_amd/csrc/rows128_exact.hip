@@ -1,0 +1,332 @@
+// Exact path of the 128-row attention (grouped routing, and per-token at
+// H = 128): recomputes the groups that rows128_attn_kernel marked because a
+// score overflowed its fixed softmax reference.  Every other workgroup returns
+// at once.
+//
+// Definition: as rows128_attn_kernel ("[Perf][DSA] Grouped sparse prefill
+// with the FlashMLA head-group-mask kernel", commit message and "How"
+// section).  This kernel is an online softmax with a running max: when a
+// row's max grows by more than 2^8, its O and l are rescaled.  Probabilities
+// never exceed 2^8, so no input overflows it.
+//
+// Design (one workgroup of 8 waves per group, 2 waves per SIMD):
+//  * 32-slot tiles of latent rows (72 x 16 B chunks each, LDS rows padded to
+//    1168 B) stream through a 3-stage LDS ring by asynchronous global->LDS
+//    DMA, issued two tiles ahead; slot indices and membership bytes are
+//    wave-uniform and come through scalar loads;
+//  * QK^T is split by rows: wave w owns rows 16 w .. 16 w + 15, keeps their
+//    queries in registers and computes S^T = K Q^T with
+//    v_mfma_f32_16x16x32_bf16; masking and the online softmax stay in
+//    registers; the bf16 probabilities and per-row rescale factors go to LDS;
+//  * PV is split by value columns: wave w owns columns 64 w .. 64 w + 63 of all
+//    128 rows and computes O^T = V^T P^T with v_mfma_f32_32x32x16_bf16, V^T
+//    from ds_read_b64_tr_b16, P^T from 16-byte reads.
+#include "common.h"
+#include "kernels.h"
+
+namespace dsa {
+
+constexpr int kGDqk = 576;
+constexpr int kGDv = 512;
+constexpr int kGWaves = 8;
+constexpr int kGThreads = 64 * kGWaves;
+constexpr int kGKeys = 32;                            // slots per tile
+constexpr int kGRowBytes = kGDqk * 2 + 16;            // 1168: 72 data chunks + 1 pad chunk
+constexpr int kGSlots = kGRowBytes / 16;              // 73
+constexpr int kGDma = (kGKeys * kGSlots + 63) / 64;   // 37 wave copies per tile
+constexpr int kGDmaPerWave = (kGDma + kGWaves - 1) / kGWaves;  // 5 (3 go to a dummy area)
+constexpr int kGStageBytes = kGDma * 1024;
+constexpr int kGStages = 3;
+constexpr int kGPStride = 40;                         // halves per probability row (32 + 8 pad)
+constexpr float kGSlack = 8.f;                        // lazy-rescale threshold (log2 units)
+
+template <bool kPerToken>
+__global__ __launch_bounds__(kGThreads) void rows128_exact_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+    const int32_t* __restrict__ keys, int64_t keys_ld, const int32_t* __restrict__ union_len,
+    const uint8_t* __restrict__ hgmask, int T, int H, int S, int ncols, int64_t q_pos_offset,
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  __shared__ __align__(16) uint8_t stage[kGStages][kGStageBytes];
+  __shared__ __align__(16) uint16_t pbuf[128 * kGPStride];
+  __shared__ float alpha_s[128];
+  __shared__ float linv_s[128];
+  __shared__ __align__(16) uint8_t dummy[1024];
+
+  const int G = 128 / H;
+  const int NG = (T + G - 1) / G;
+  const int grp = NG - 1 - xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, n = lane & 15;
+  const int t0 = grp * G;
+  // only groups the fast kernel marked are recomputed (the mark sits in the LSE of the
+  // group's first row, which always exists)
+  if (__float_as_uint(lse[(size_t)t0 * H]) != kOverflowMark) return;
+
+  // the row this lane's wave owns for QK^T / softmax
+  const int r_own = 16 * wave + n;
+  const int i_own = r_own / H;
+  const int h_own = r_own - i_own * H;
+  const int tok_own = t0 + i_own;
+  const bool row_live = tok_own < T;
+
+  bf16x8 qreg[kGDqk / 32];
+  if (row_live) {
+    const uint16_t* qrow = q + ((size_t)tok_own * H + h_own) * kGDqk + 8 * g;
+#pragma unroll
+    for (int s = 0; s < kGDqk / 32; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
+  } else {
+#pragma unroll
+    for (int s = 0; s < kGDqk / 32; ++s) qreg[s] = bf16x8{};
+  }
+#pragma unroll
+  for (int s = 0; s < kGDqk / 32; ++s) asm volatile("" : : "v"(qreg[s]));  // loads done before any copy
+
+  int nkeys;
+  if (kPerToken) {
+    nkeys = ncols;
+  } else {
+    nkeys = union_len[grp];
+    nkeys = nkeys < 0 ? 0 : (nkeys > ncols ? ncols : nkeys);
+  }
+  nkeys = uniform(nkeys);
+  const int32_t* klist = keys + (size_t)grp * keys_ld;
+  const uint8_t* mlist = kPerToken ? nullptr : hgmask + (size_t)grp * keys_ld;
+  int64_t pos64 = q_pos_offset + t0;  // per-token mode: the token's position
+  if (pos64 > S - 1) pos64 = S - 1;
+  const int pos = uniform((int)pos64);
+  const int ntiles = (nkeys + kGKeys - 1) / kGKeys;
+
+  // validity of slot j0 + r as a latent-row index (grouped: a union entry inside [0, S);
+  // per-token: the selection rule) -- wave-uniform, scalar loads
+  auto slot_ok = [&](int32_t x, int j) -> bool {
+    return j < nkeys && x >= 0 && (kPerToken ? x <= pos : x < S);  // pos <= S - 1
+  };
+
+  // this wave's copies of a tile are 5 w .. 5 w + 4: slots 320 w .. 320 w + 319, i.e. at
+  // most 6 consecutive slot rows starting at r_lo
+  const int r_lo = uniform((64 * kGDmaPerWave * wave) / kGSlots);
+  auto issue = [&](int t) {
+    const int j0 = t * kGKeys;
+    int32_t x[6];
+    const_i32* ip = uniform_const(klist + j0 + r_lo);
+    const int avail = min(kGKeys - r_lo, nkeys - j0 - r_lo);  // rows of this tile past r_lo
+    if (avail >= 6) {
+#pragma unroll
+      for (int e = 0; e < 6; ++e) x[e] = ip[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 6; ++e) x[e] = e < avail ? ip[e] : -1;
+    }
+#pragma unroll
+    for (int e = 0; e < 6; ++e) x[e] = slot_ok(x[e], j0 + r_lo + e) ? x[e] : 0;
+    uint8_t* st = stage[t % kGStages];
+#pragma unroll
+    for (int u = 0; u < kGDmaPerWave; ++u) {
+      const int i = kGDmaPerWave * wave + u;
+      if (i < kGDma) {
+        const int r0 = (64 * i) / kGSlots;
+        const int thr = kGSlots * (r0 + 1) - 64 * i;
+        const bool up = lane >= thr;
+        const int r = up ? r0 + 1 : r0;
+        const int c = 64 * i + lane - kGSlots * r;
+        const int e0 = r0 - r_lo;  // 0..4, wave-uniform
+        int32_t x0 = x[0], x1 = x[1];
+#pragma unroll
+        for (int e = 1; e < 5; ++e) {
+          x0 = e == e0 ? x[e] : x0;
+          x1 = e == e0 ? x[e + 1] : x1;
+        }
+        int32_t xr = up ? x1 : x0;
+        if (r >= kGKeys) xr = 0;
+        dma16(kv + (size_t)xr * kGDqk + (c < 72 ? c : 0) * 8, lds_addr(st + 1024 * i));
+      } else {
+        dma16(kv, lds_addr(dummy));  // keeps every wave's copy count per tile equal
+      }
+    }
+  };
+
+  // for the row this lane owns: bit 4 kb + jj <-> slot 16 kb + 4 g + jj of tile t is allowed
+  auto allowed_bits = [&](int t) -> uint32_t {
+    const int j0 = t * kGKeys;
+    uint32_t bits = 0;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int jb = j0 + 16 * kb;
+      const_i32* ip = uniform_const(klist + jb);
+      int32_t e[16];
+      if (!kPerToken || nkeys - jb >= 16) {  // union lists are padded to whole tiles
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] = ip[r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] = r < nkeys - jb ? ip[r] : -1;
+      }
+      uint32_t vbits = 0;  // validity of the 16 slots
+#pragma unroll
+      for (int r = 0; r < 16; ++r) vbits |= slot_ok(e[r], jb + r) ? (1u << r) : 0u;
+      const uint32_t vb = (vbits >> (4 * g)) & 0xfu;
+      if (kPerToken) {
+        bits |= vb << (4 * kb);
+      } else {
+        // membership bytes of slots 16 kb + 4 g .. + 3
+        const_i32* mp = uniform_const(reinterpret_cast<const int32_t*>(mlist + jb));
+        const uint32_t w0 = (uint32_t)mp[0], w1 = (uint32_t)mp[1], w2 = (uint32_t)mp[2], w3 = (uint32_t)mp[3];
+        const uint32_t w = g == 0 ? w0 : g == 1 ? w1 : g == 2 ? w2 : w3;
+        uint32_t mbits = 0;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) mbits |= ((w >> (8 * jj + i_own)) & 1u) << jj;
+        bits |= (vb & mbits) << (4 * kb);
+      }
+    }
+    return bits;
+  };
+
+  float m_run = kNegInf, l_run = 0.f;  // row r_own (replicated over the 4 lane groups)
+  f32x16 o[2][4];                      // [col block][row block]
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) o[cb][rb] = f32x16{};
+
+  const int hi = lane >> 5, m = lane & 31;
+  const int koff = n * kGRowBytes + 16 * g;  // K read: row n of a 16-slot block, chunk 4 s + g
+  // transposed V reads: row 8 hi + s16 / 4 (+4), columns 64 w + 32 cb + 16 (g16 % 2) + 4 (s16 % 4)
+  const int voff = (8 * hi + ((lane & 15) >> 2)) * kGRowBytes +
+                   2 * (64 * wave + 16 * (g & 1) + 4 * (lane & 3));
+  const int poff = m * kGPStride + 8 * hi;   // P^T read: row 32 rb + m, slots 16 ks + 8 hi .. + 8
+
+  if (ntiles > 0) issue(0);
+  if (ntiles > 1) issue(1);
+
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles)
+      wait_vmcnt<kGDmaPerWave>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();  // tile t visible; every wave is done with tile t - 1 (stage and P)
+    if (t + 2 < ntiles) issue(t + 2);
+    const uint32_t abits = allowed_bits(t);
+
+    const uint8_t* tile = stage[t % kGStages];
+    // ---- scores of this wave's 16 rows over the 32 slots
+    f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int s = 0; s < kGDqk / 32; ++s)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        sacc[kb] = mfma16x16x32(*reinterpret_cast<const bf16x8*>(tile + koff + kb * 16 * kGRowBytes + 64 * s),
+                                qreg[s], sacc[kb]);
+    // sacc[kb][jj] = score(slot 16 kb + 4 g + jj, row r_own)
+
+    float mt = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const bool ok = ((abits >> (4 * kb + jj)) & 1u) != 0u;
+        const float val = ok ? sacc[kb][jj] * scale_log2 : kNegInf;
+        sacc[kb][jj] = val;
+        mt = fmaxf(mt, val);
+      }
+    }
+    mt = max_over_rowgroups(mt);
+    float alpha = 1.f;
+    const bool need = mt > m_run + kGSlack;
+    if (ballot(need) != 0) {
+      const float m_new = need ? mt : m_run;
+      alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float msafe = m_run == kNegInf ? 0.f : m_run;
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      bf16x4 pw;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float p = fast_exp2(sacc[kb][jj] - msafe);
+        ls += p;
+        pw[jj] = (__bf16)p;
+      }
+      *reinterpret_cast<bf16x4*>(pbuf + r_own * kGPStride + 16 * kb + 4 * g) = pw;
+    }
+    l_run += sum_over_rowgroups(ls);
+    if (g == 0) alpha_s[r_own] = alpha;
+    __syncthreads();  // P and alpha of all 128 rows visible
+
+    // ---- O^T[64 w .. 64 w + 63][all rows] += V^T P^T over the 32 slots
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const float al = alpha_s[32 * rb + m];
+      if (ballot(al != 1.f) != 0) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) o[cb][rb] *= al;
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 va[2];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const uint8_t* vp = tile + voff + 16 * ks * kGRowBytes + 64 * cb;
+        const u16x4 lo = lds_read_tr16(vp);
+        const u16x4 up = lds_read_tr16(vp + 4 * kGRowBytes);
+        va[cb] = __builtin_bit_cast(bf16x8, u16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
+      }
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const bf16x8 pb = *reinterpret_cast<const bf16x8*>(pbuf + 32 * rb * kGPStride + poff + 16 * ks);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) o[cb][rb] = mfma32x32x16(va[cb], pb, o[cb][rb]);
+      }
+    }
+  }
+
+  if (g == 0) {
+    linv_s[r_own] = l_run > 0.f ? 1.f / l_run : 0.f;
+    if (row_live)
+      lse[(size_t)tok_own * H + h_own] = l_run > 0.f ? (m_run + fast_log2(l_run)) * kLn2 : kNegInf;
+  }
+  __syncthreads();
+
+  // o[cb][rb][j] = O^T[col 64 w + 32 cb + 8 (j / 4) + 4 hi + j % 4][row 32 rb + m]
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int row = 32 * rb + m;
+    const int i = row / H;
+    const int h = row - i * H;
+    const int tok = t0 + i;
+    if (tok >= T) continue;
+    const float inv = linv_s[row];
+    uint16_t* orow = out + ((size_t)tok * H + h) * kGDv + 64 * wave + 4 * hi;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const bf16x4 w = {(__bf16)(o[cb][rb][4 * jj + 0] * inv), (__bf16)(o[cb][rb][4 * jj + 1] * inv),
+                          (__bf16)(o[cb][rb][4 * jj + 2] * inv), (__bf16)(o[cb][rb][4 * jj + 3] * inv)};
+        *reinterpret_cast<bf16x4*>(orow + 32 * cb + 8 * jj) = w;
+      }
+  }
+}
+
+hipError_t launch_rows128_exact(const uint16_t* q, const uint16_t* kv, const int32_t* keys,
+                                int64_t keys_ld, const int32_t* union_len, const uint8_t* hgmask,
+                                int T, int H, int S, int ncols, int64_t q_pos_offset, float scale,
+                                uint16_t* out, float* lse, hipStream_t stream) {
+  const int G = 128 / H;
+  const int NG = (T + G - 1) / G;
+  if (NG == 0) return hipSuccess;
+  if (hgmask != nullptr)
+    hipLaunchKernelGGL(rows128_exact_kernel<false>, dim3(NG), dim3(kGThreads), 0, stream, q, kv, keys,
+                       keys_ld, union_len, hgmask, T, H, S, ncols, q_pos_offset, scale * kLog2e, out,
+                       lse);
+  else
+    hipLaunchKernelGGL(rows128_exact_kernel<true>, dim3(NG), dim3(kGThreads), 0, stream, q, kv, keys,
+                       keys_ld, union_len, hgmask, T, H, S, ncols, q_pos_offset, scale * kLog2e, out,
+                       lse);
+  return hipGetLastError();
+}
+
+}  // namespace dsa
