@@ -53,6 +53,8 @@ constexpr int kRGroupBytes = 8 * kRDqk * 2;         // 9216: one 8-row group
 constexpr int kRStageBytes = 4 * kRGroupBytes;      // one 32-slot tile
 constexpr int kRCopies = kRGroupBytes / 1024;       // 9 row copies per wave per tile
 constexpr float kRSlack = 64.f;                     // log2 of the largest probability allowed
+constexpr int kRQRegSteps = 28;                     // query k-steps kept in registers (of 36)
+constexpr int kRQLdsSteps = kRDqk / 16 - kRQRegSteps;  // the rest sit in LDS (lane-private)
 
 template <bool kPerToken>
 __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
@@ -63,6 +65,7 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   __shared__ __align__(16) uint8_t stage[kRStages][kRStageBytes];
   // per tile and wave: lanes 0..7 = slot indices 8 w .. 8 w + 7, lanes 8, 9 = their membership bytes
   __shared__ __align__(16) uint32_t idxw[kRIdxBufs][kRWaves][64];
+  __shared__ __align__(16) uint4 qlds[kRWaves][kRQLdsSteps][64];
   __shared__ int over_any;
 
   const int G = 128 / H;
@@ -82,22 +85,25 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   // negated queries so that the reference can be taken on raw scores
   const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
   const float sc = fabsf(scale_log2);
-  bf16x8 qreg[kRDqk / 16];
-  if (live) {
+  // (steps kRQRegSteps.. go to a lane-private LDS area: the registers are needed to keep
+  // operand reads in flight)
+  bf16x8 qreg[kRQRegSteps];
+  {
     const uint16_t* qrow = q + ((size_t)tok * H + rh) * kRDqk + 8 * hi;
 #pragma unroll
     for (int s = 0; s < kRDqk / 16; ++s) {
-      uint4 w = *reinterpret_cast<const uint4*>(qrow + 16 * s);
+      uint4 w = {0u, 0u, 0u, 0u};
+      if (live) w = *reinterpret_cast<const uint4*>(qrow + 16 * s);
       w.x ^= qsign; w.y ^= qsign; w.z ^= qsign; w.w ^= qsign;
-      qreg[s] = __builtin_bit_cast(bf16x8, w);
+      if (s < kRQRegSteps)
+        qreg[s] = __builtin_bit_cast(bf16x8, w);
+      else
+        qlds[wave][s - kRQRegSteps][lane] = w;
     }
-  } else {
-#pragma unroll
-    for (int s = 0; s < kRDqk / 16; ++s) qreg[s] = bf16x8{};
   }
   // complete the query loads now, before any asynchronous copy is in flight
 #pragma unroll
-  for (int s = 0; s < kRDqk / 16; ++s) asm volatile("" : : "v"(qreg[s]));
+  for (int s = 0; s < kRQRegSteps; ++s) asm volatile("" : : "v"(qreg[s]));
 
   int nkeys;
   if (kPerToken) {
@@ -208,14 +214,35 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
     // one stage offset per iteration (kept opaque so no per-stage address sets are hoisted)
     const int sofs = loop_local((t % kRStages) * kRStageBytes);
     const uint8_t* kt = &stage[0][0] + sofs;
-    f32x16 sa = {}, sb = {};
+    // (the LDS query address is made opaque per tile, so that its reads are not hoisted)
+    const uint8_t* qb = reinterpret_cast<const uint8_t*>(&qlds[wave][0][0]) + loop_local(16 * lane);
+    // K operand reads run kRAhead steps ahead of the MFMAs (the order is pinned: left to
+    // itself the scheduler puts every read right before its MFMA and waits out its latency)
+    auto kread = [&](int s) -> bf16x8 {
+      return *reinterpret_cast<const bf16x8*>(kt + kofs[s & 3] + 1024 * (s >> 2));
+    };
+    auto qread = [&](int s) -> bf16x8 {
+      return s < kRQRegSteps ? qreg[s < kRQRegSteps ? s : 0]
+                             : *reinterpret_cast<const bf16x8*>(qb + 1024 * (s - kRQRegSteps));
+    };
+    constexpr int kRAhead = 4;
+    bf16x8 kw[kRAhead], qw[kRAhead];
 #pragma unroll
-    for (int s = 0; s < kRDqk / 16; s += 2) {
-      sa = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kt + kofs[s & 3] + 1024 * (s >> 2)), qreg[s], sa);
-      sb = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kt + kofs[(s + 1) & 3] + 1024 * ((s + 1) >> 2)),
-                        qreg[s + 1], sb);
+    for (int s = 0; s < kRAhead; ++s) {
+      kw[s] = kread(s);
+      qw[s] = qread(s);
     }
-    f32x16 sacc = sa + sb;  // sacc[j] = raw score(slot 8 (j / 4) + 4 hi + j % 4, row r)
+    f32x16 sacc = {};  // sacc[j] = raw score(slot 8 (j / 4) + 4 hi + j % 4, row r)
+#pragma unroll
+    for (int s = 0; s < kRDqk / 16; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
+      sacc = mfma32x32x16(kw[s % kRAhead], qw[s % kRAhead], sacc);
+      if (s + kRAhead < kRDqk / 16) {
+        kw[s % kRAhead] = kread(s + kRAhead);
+        qw[s % kRAhead] = qread(s + kRAhead);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
     float ml = kNegInf;
 #pragma unroll
@@ -244,21 +271,30 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
     }
 
     // O^T += V^T P^T: step st covers slots 16 st .. 16 st + 15 with k-slot (hi, i) <->
-    // slot 16 st + 8 (i / 4) + 4 hi + i % 4, i.e. score registers 8 st .. 8 st + 7
+    // slot 16 st + 8 (i / 4) + 4 hi + i % 4, i.e. score registers 8 st .. 8 st + 7.  MFMA i
+    // (0..31) is step i / 16, column block i % 16; its V^T operand is read kRVAhead MFMAs
+    // ahead (order pinned as for QK).
     const uint8_t* vt = kt;  // V = the first 512 dims of the same rows
+    auto vread = [&](int i) -> bf16x8 {
+      const int st = i >> 4, cb = i & 15;
+      // rows 16 st + 8 uu + vr8 are in group 2 st + uu; chunk 4 cb + c2 is in block cb / 2
+      const int p0 = 16 * (vx ^ (4 * (cb & 1)) ^ (2 * st));
+      const int p1 = 16 * (vx ^ (4 * (cb & 1)) ^ (2 * st + 1));
+      const u16x4 lo = lds_read_tr16(vt + (2 * st) * kRGroupBytes + 1024 * (cb >> 1) + vbase + p0);
+      const u16x4 up = lds_read_tr16(vt + (2 * st + 1) * kRGroupBytes + 1024 * (cb >> 1) + vbase + p1);
+      return __builtin_bit_cast(bf16x8, u16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
+    };
+    constexpr int kRVAhead = 3;
+    bf16x8 vw[kRVAhead];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int i = 0; i < kRVAhead; ++i) vw[i] = vread(i);
 #pragma unroll
-      for (int cb = 0; cb < kRDv / 32; ++cb) {
-        // rows 16 st + 8 uu + vr8 are in group 2 st + uu; chunk 4 cb + c2 is in block cb / 2
-        const int p0 = 16 * (vx ^ (4 * (cb & 1)) ^ (2 * st));
-        const int p1 = 16 * (vx ^ (4 * (cb & 1)) ^ (2 * st + 1));
-        const u16x4 lo = lds_read_tr16(vt + (2 * st) * kRGroupBytes + 1024 * (cb >> 1) + vbase + p0);
-        const u16x4 up = lds_read_tr16(vt + (2 * st + 1) * kRGroupBytes + 1024 * (cb >> 1) + vbase + p1);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, u16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
-        o[cb] = mfma32x32x16(a, bop[st], o[cb]);
-      }
+    for (int i = 0; i < 2 * (kRDv / 32); ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      o[i & 15] = mfma32x32x16(vw[i % kRVAhead], bop[i >> 4], o[i & 15]);
+      if (i + kRVAhead < 2 * (kRDv / 32)) vw[i % kRVAhead] = vread(i + kRVAhead);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   if (over && lane == 0) over_any = 1;
