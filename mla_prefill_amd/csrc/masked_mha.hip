@@ -49,6 +49,8 @@ constexpr int kMStageBytes = 2 * kMTileBytes;
 constexpr int kMCopiesPerWave = kMStageBytes / 1024 / kMWaves;  // 4
 constexpr int kMOpsPerTile = kMCopiesPerWave + 1;     // + the mask-word copy
 constexpr float kRescaleSlack = 8.f;                  // rescale O only when the max grows by > 2^8
+constexpr int kMQRegSteps = 12;                       // query k-steps kept in registers (of 16)
+constexpr int kMQLdsSteps = kMD / 16 - kMQRegSteps;   // the rest sit in LDS (lane-private)
 static_assert(kMStageBytes == 1024 * kMWaves * kMCopiesPerWave, "copies split evenly over waves");
 
 __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
@@ -58,6 +60,7 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
     float* __restrict__ lse) {
   __shared__ __align__(16) uint8_t stage[kMStages][kMStageBytes];
   __shared__ __align__(16) uint32_t maskw[kMStages][kMWaves][64];
+  __shared__ __align__(16) uint4 qlds[kMWaves][kMQLdsSteps][64];
 
   // longest query tiles first; consecutive blocks take consecutive heads, so the
   // round-robin XCD dispatch keeps each head on one XCD and balances the work
@@ -79,22 +82,25 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
   // running max can be taken on raw scores
   const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
   const float sc = fabsf(scale_log2);
-  bf16x8 qreg[kMD / 16];
-  if (live) {
+  // (steps kMQRegSteps.. go to a lane-private LDS area: the registers are needed to keep
+  // operand reads in flight)
+  bf16x8 qreg[kMQRegSteps];
+  {
     const uint16_t* qrow = q + ((size_t)row * H + h) * kMD + 8 * hi;
 #pragma unroll
     for (int s = 0; s < kMD / 16; ++s) {
-      uint4 w = *reinterpret_cast<const uint4*>(qrow + 16 * s);
+      uint4 w = {0u, 0u, 0u, 0u};
+      if (live) w = *reinterpret_cast<const uint4*>(qrow + 16 * s);
       w.x ^= qsign; w.y ^= qsign; w.z ^= qsign; w.w ^= qsign;
-      qreg[s] = __builtin_bit_cast(bf16x8, w);
+      if (s < kMQRegSteps)
+        qreg[s] = __builtin_bit_cast(bf16x8, w);
+      else
+        qlds[wave][s - kMQRegSteps][lane] = w;
     }
-  } else {
-#pragma unroll
-    for (int s = 0; s < kMD / 16; ++s) qreg[s] = bf16x8{};
   }
   // complete the query loads now, before any asynchronous copy is in flight
 #pragma unroll
-  for (int s = 0; s < kMD / 16; ++s) asm volatile("" : : "v"(qreg[s]));
+  for (int s = 0; s < kMQRegSteps; ++s) asm volatile("" : : "v"(qreg[s]));
 
   const int last = min(T, q0 + kMQ) - 1;
   int64_t kend64 = q_pos_offset + last + 1;
@@ -158,10 +164,34 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
     const uint8_t* vt = kt + kMTileBytes;
     const int k0 = t * kMKeys;
 
+    // K operand reads run kMAhead steps ahead of the MFMAs (the order is pinned: left to
+    // itself the scheduler puts every read right before its MFMA and waits out its latency)
+    const uint8_t* qb = reinterpret_cast<const uint8_t*>(&qlds[wave][0][0]) + loop_local(16 * lane);
+    auto kread = [&](int s) -> bf16x8 {
+      return *reinterpret_cast<const bf16x8*>(kt + kofs[s & 3] + 1024 * (s >> 2));
+    };
+    auto qread = [&](int s) -> bf16x8 {
+      return s < kMQRegSteps ? qreg[s < kMQRegSteps ? s : 0]
+                             : *reinterpret_cast<const bf16x8*>(qb + 1024 * (s - kMQRegSteps));
+    };
+    constexpr int kMAhead = 4;
+    bf16x8 kw[kMAhead], qw[kMAhead];
+#pragma unroll
+    for (int s = 0; s < kMAhead; ++s) {
+      kw[s] = kread(s);
+      qw[s] = qread(s);
+    }
     f32x16 sacc = {};
 #pragma unroll
-    for (int s = 0; s < kMD / 16; ++s)
-      sacc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kt + kofs[s & 3] + 1024 * (s >> 2)), qreg[s], sacc);
+    for (int s = 0; s < kMD / 16; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
+      sacc = mfma32x32x16(kw[s % kMAhead], qw[s % kMAhead], sacc);
+      if (s + kMAhead < kMD / 16) {
+        kw[s % kMAhead] = kread(s + kMAhead);
+        qw[s % kMAhead] = qread(s + kMAhead);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     // sacc[j] = raw score(key k0 + 8 (j / 4) + 4 hi + j % 4, row)
 
     // allowed keys: top-k bit AND key <= position; bit kk <-> key k0 + 4 hi + kk
@@ -207,19 +237,28 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
 
     // O^T += V^T P^T: step st covers keys 16 st .. 16 st + 15 with k-slot (hi, i) <->
     // key 16 st + 8 (i / 4) + 4 hi + i % 4, i.e. accumulator registers 8 st .. 8 st + 7
+    // MFMA i (0..15) is step i / 8, column block i % 8; its V^T operand is read kMVAhead
+    // MFMAs ahead (order pinned as for QK)
+    auto vread = [&](int i) -> bf16x8 {
+      const int st = i >> 3, cb = i & 7;
+      // rows 16 st + 8 uu + vr8 are in group 2 st + uu; chunk 4 cb + c2 is in block cb / 2
+      const int p0 = 16 * (vx ^ (4 * (cb & 1)) ^ (2 * st));
+      const int p1 = 16 * (vx ^ (4 * (cb & 1)) ^ (2 * st + 1));
+      const u16x4 lo = lds_read_tr16(vt + (2 * st) * kMGroupBytes + 1024 * (cb >> 1) + vbase + p0);
+      const u16x4 up = lds_read_tr16(vt + (2 * st + 1) * kMGroupBytes + 1024 * (cb >> 1) + vbase + p1);
+      return __builtin_bit_cast(bf16x8, u16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
+    };
+    constexpr int kMVAhead = 3;
+    bf16x8 vw[kMVAhead];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int i = 0; i < kMVAhead; ++i) vw[i] = vread(i);
 #pragma unroll
-      for (int cb = 0; cb < kMD / 32; ++cb) {
-        // rows 16 st + 8 uu + vr8 are in group 2 st + uu; chunk 4 cb + c2 is in block cb / 2
-        const int p0 = loop_local(16 * (vx ^ (4 * (cb & 1)) ^ (2 * st)));
-        const int p1 = loop_local(16 * (vx ^ (4 * (cb & 1)) ^ (2 * st + 1)));
-        const u16x4 lo = lds_read_tr16(vt + (2 * st) * kMGroupBytes + 1024 * (cb >> 1) + vbase + p0);
-        const u16x4 up = lds_read_tr16(vt + (2 * st + 1) * kMGroupBytes + 1024 * (cb >> 1) + vbase + p1);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, u16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
-        o[cb] = mfma32x32x16(a, bop[st], o[cb]);
-      }
+    for (int i = 0; i < 2 * (kMD / 32); ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      o[i & 7] = mfma32x32x16(vw[i % kMVAhead], bop[i >> 3], o[i & 7]);
+      if (i + kMVAhead < 2 * (kMD / 32)) vw[i % kMVAhead] = vread(i + kMVAhead);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   if (!live) return;
