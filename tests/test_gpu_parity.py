@@ -161,6 +161,19 @@ def test_deterministic(R):
     assert torch.equal(c[0].view(torch.int16), d[0].view(torch.int16)) and torch.equal(c[1], d[1])
 
 
+def test_pertoken_far_positions_and_wide_rows(R):
+    """Per-token rows with positions beyond 65535 and rows wider than 3072 columns."""
+    rng = np.random.default_rng(14)
+    H = 16
+    for T, S, k, cols, P0 in ((12, 70000, 300, 320, 70000 - 12), (10, 4000, 3000, 3100, 4000 - 10)):
+        q = normal_bf16(rng, (T, H, 576))
+        kv = normal_bf16(rng, (S, 576))
+        topk = topk_uniform(rng, T, S, k, cols, P0)
+        ref_out, ref_lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, P0, 0.0625)
+        out, lse = R.pertoken(dev_bf16(q), dev_bf16(kv), dev_i32(topk), P0, 0.0625)
+        check_attention(out, lse, ref_out, ref_lse, f"per-token S={S} cols={cols}")
+
+
 def test_large_score_jump_and_negative_scale(R):
     """Scores that jump far above everything earlier in the row (one key per affected token
     scores ~900 raw units on head 0, ~80 in base-2 softmax units, placed late in the row),
