@@ -10,24 +10,26 @@
 //
 // MI355X design: one wave per (token, 16-head block), one wave per workgroup
 // (no barriers), one wave per SIMD:
-//  * the token's top-k row is consumed 16 entries at a time; lane (g, n) owns
-//    entry n of a step and loads 16-byte chunks 4 s + g (s = 0..17) of that
-//    latent row straight into registers.  Two register buffers form a ring: a
-//    step's buffer is refilled with the rows two steps ahead as soon as its
-//    QK MFMAs have read it, so up to two steps (36 KiB) are in flight per
-//    wave -- a gather of scattered 1152-byte rows is latency bound, and LDS
-//    capacity no longer limits the bytes in flight.  Invalid entries (-1, past
-//    the row, beyond the token's position) load the token's own row and are
-//    masked;
-//  * S^T = K Q^T takes the rows from registers as the A operand of
-//    v_mfma_f32_16x16x32_bf16, in three independent accumulation chains; the
-//    B operand (the 16 heads' queries) is re-read every step from a
-//    lane-private LDS area, since the register file holds the ring;
-//  * the value part of the rows goes through a 16 KiB LDS tile (XOR-swizzled,
-//    free of bank conflicts for both the 16-byte writes and the transposed
-//    reads) so that ds_read_b64_tr_b16 can hand V^T to O^T = V^T P^T
-//    (v_mfma_f32_16x16x16_bf16); the probabilities leave the accumulators
-//    directly as the B operand;
+//  * the token's top-k row is consumed 16 entries at a time.  Rows are loaded
+//    straight into registers with coalesced loads: each load instruction
+//    covers one 128-byte line of 8 rows (lane l takes row l / 8, 16 bytes
+//    l % 8 of the line), so a quarter-wave touches two cache lines.  (Loading
+//    rows directly in the MFMA operand layout puts 16 rows under every
+//    quarter-wave, and the address path, one cache line at a time, then
+//    bounds the kernel.)  Two register buffers form a ring: a step's buffer is
+//    refilled with the rows two steps ahead as soon as it has been written to
+//    LDS, so about two steps (36 KiB) are in flight per wave.  Invalid entries
+//    (-1, past the row, beyond the token's position) load the token's own row
+//    and are masked;
+//  * each step's 16 rows go to an 18 KiB LDS tile (XOR-swizzled, free of bank
+//    conflicts for the stores, the 16-byte K reads and the transposed V
+//    reads).  S^T = K Q^T runs on v_mfma_f32_16x16x32_bf16 in three
+//    independent accumulation chains, with the B operand (the 16 heads'
+//    queries) re-read from a lane-private LDS area; O^T = V^T P^T runs on
+//    v_mfma_f32_16x16x16_bf16 with V^T from ds_read_b64_tr_b16 and the
+//    probabilities straight from the score accumulators as the B operand.
+//    Operand reads run several MFMAs ahead (the order is pinned: left to
+//    itself the scheduler puts every read right before its MFMA);
 //  * fp32 softmax in base 2 on raw scores (the scale is folded into the
 //    exponent's FMA; a negative scale negates the queries) against a per-head
 //    reference fixed at the head's first valid scores, so O is only ever
@@ -48,65 +50,140 @@ constexpr int kDqk = 576;
 constexpr int kDv = 512;
 constexpr int kPKeys = 16;                  // keys per step
 constexpr int kPLoads = kDqk / 32;          // 16-byte chunks per lane per step (18)
-constexpr int kPVLoads = kDv / 32;          // of which hold value dims (16)
+constexpr int kPLines = kDqk * 2 / 128;     // 128-byte lines per latent row (9)
 constexpr int kPRowBytes = kDqk * 2;        // 1152
-constexpr int kPVRowBytes = kDv * 2;        // 1024: one V row in the LDS tile
 constexpr float kPSlack = 64.f;             // log2 of the largest probability allowed
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+// (a native vector: row chunks loaded into HIP's uint4 struct through a byte pointer
+// become memcpys into a stack array that is never promoted to registers)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma16x16x16(s16x4_t a, s16x4_t b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-// LDS of the (single-wave) workgroup: the V tile of the current step -- chunk c (16 B,
-// 0..63) of row r (0..15) at r * 1024 + 16 (c ^ vswz(r)) -- and the queries, lane-private:
-// lane l's chunk s at pt_q[s][l].
-__shared__ __align__(16) uint8_t pt_vtile[kPKeys * kPVRowBytes];
+// LDS of the (single-wave) workgroup: the rows of the current step -- chunk c (16 B,
+// 0..71) of row r (0..15) at r * 1152 + 16 (c ^ tswz(r)); the XOR stays inside a
+// 128-byte line -- and the queries, lane-private: lane l's chunk s at pt_q[s][l].
+__shared__ __align__(16) uint8_t pt_tile[kPKeys * kPRowBytes];
 __shared__ __align__(16) uint4 pt_q[kPLoads][64];
 
-__device__ __forceinline__ int vswz(int r) { return (2 * r + (r >> 3)) & 15; }
+__device__ __forceinline__ int tswz(int r) { return (2 * (r >> 1) + (r >> 3)) & 7; }
 
 // What one wave needs to walk its token's row.
 struct PtCtx {
   const int32_t* trow;  // the token's top-k row
-  const uint8_t* kvb;   // latent base + 16 g (this lane's chunk column)
+  const uint8_t* kvb;   // latent base + 16 (lane % 8): this lane's 16 bytes of each line
   int cols, pos, lane, g, n;
+  int er;               // the rows this lane loads: er and 8 + er of each step
   float sc;             // |scale| * log2(e)
-  int wofs[4];          // LDS V-tile store offsets (per chunk group s % 4)
-  int rofs[8];          // LDS V-tile transposed-read offsets (per column block cb % 8)
+  int wofs[2];          // tile store offsets (rows er, 8 + er; + 128 per line)
+  int kofs[2];          // K read offsets (row n, chunk 4 s + g: per s % 2; + 128 (s / 2))
+  int rofs[4];          // transposed V read offsets (per column block cb % 4; + 128 (cb / 4))
 };
 
-// this lane's entry of step j (column 16 j + n, clamped into the row)
-__device__ __forceinline__ int32_t pt_entry(const PtCtx& c, int j) {
-  return c.trow[min(kPKeys * j + c.n, c.cols - 1)];
-}
-
-// start the loads of step j's rows into `buf`; returns the validity bits (key r <-> bit r)
-__device__ __forceinline__ uint32_t pt_issue(const PtCtx& c, int32_t e, int j, uint4 (&buf)[kPLoads]) {
-  const bool ok = kPKeys * j + c.n < c.cols && e >= 0 && e <= c.pos;
-  const uint4* src = reinterpret_cast<const uint4*>(c.kvb + (size_t)(ok ? e : c.pos) * kPRowBytes);
+// The per-wave context for token `token` (built in registers; the exact routine rebuilds
+// it from the same scalars rather than taking it by reference, which would put it in
+// scratch memory for the whole kernel).
+__device__ __forceinline__ PtCtx pt_context(const uint16_t* kv, const int32_t* topk, int64_t ld, int S,
+                                            int cols, int64_t q_pos_offset, float scale_log2, int token) {
+  PtCtx c;
+  c.lane = threadIdx.x;
+  c.g = c.lane >> 4;
+  c.n = c.lane & 15;
+  int64_t pos64 = q_pos_offset + token;
+  if (pos64 > S - 1) pos64 = S - 1;  // positions beyond S - 1 cannot be selected
+  c.pos = uniform((int)pos64);
+  c.cols = cols;
+  c.trow = topk + (size_t)token * ld;
+  c.er = c.lane >> 3;
+  c.kvb = reinterpret_cast<const uint8_t*>(kv) + 16 * (c.lane & 7);
+  c.sc = fabsf(scale_log2);
+  // LDS tile offsets.  Stores: lane l writes 16 bytes l % 8 of each line of rows er and
+  // 8 + er.  K reads: lane (g, n) reads row n, chunk 4 s + g.  Transposed reads for O^T
+  // block cb (cols 16 cb .. + 15): lane (g, i) of a 16-lane group addresses row 4 g + i / 4,
+  // cols 16 cb + 4 (i % 4) .. + 3 (chunk 2 cb + (i % 4) / 2, half i % 2), so that output
+  // lane (g, n) receives V[key 4 g + jj][col 16 cb + n], jj = 0..3.
+  {
 #pragma unroll
-  for (int s = 0; s < kPLoads; ++s) buf[s] = src[4 * s];
-  return (uint32_t)ballot(ok) & 0xffffu;
-}
-
-__device__ __forceinline__ void pt_store_v(const PtCtx& c, const uint4 (&buf)[kPLoads]) {
+    for (int h = 0; h < 2; ++h) {
+      const int r = 8 * h + c.er;
+      c.wofs[h] = r * kPRowBytes + 16 * ((c.lane & 7) ^ tswz(r));
+    }
 #pragma unroll
-  for (int s = 0; s < kPVLoads; ++s)
-    *reinterpret_cast<uint4*>(pt_vtile + c.wofs[s & 3] + 256 * (s >> 2)) = buf[s];
+    for (int p = 0; p < 2; ++p) c.kofs[p] = c.n * kPRowBytes + 16 * ((4 * p + c.g) ^ tswz(c.n));
+    const int rr = 4 * c.g + (c.n >> 2);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      c.rofs[u] = rr * kPRowBytes + 8 * (c.n & 1) + 16 * ((2 * u + ((c.n & 3) >> 1)) ^ tswz(rr));
+  }
+
+  return c;
 }
 
-// S^T[key 4 g + jj][head n] (raw) of the rows in `buf`, in three independent chains
-__device__ __forceinline__ f32x4 pt_qk(const PtCtx& c, const uint4 (&buf)[kPLoads]) {
+// this lane's entries of step j: rows er and 8 + er (clamped into the row)
+__device__ __forceinline__ int2 pt_entries(const PtCtx& c, int j) {
+  return int2{c.trow[min(kPKeys * j + c.er, c.cols - 1)], c.trow[min(kPKeys * j + 8 + c.er, c.cols - 1)]};
+}
+
+// start the loads of step j's rows into `buf` (buf[k]: line k of row er, buf[9 + k]: of row
+// 8 + er); returns the validity bits of the step's 16 keys (key r <-> bit r)
+__device__ __forceinline__ uint32_t pt_issue(const PtCtx& c, int2 e, int j, u32x4 (&buf)[kPLoads]) {
+  const bool ok0 = kPKeys * j + c.er < c.cols && e.x >= 0 && e.x <= c.pos;
+  const bool ok1 = kPKeys * j + 8 + c.er < c.cols && e.y >= 0 && e.y <= c.pos;
+  const uint8_t* src0 = c.kvb + (size_t)(ok0 ? e.x : c.pos) * kPRowBytes;
+  const uint8_t* src1 = c.kvb + (size_t)(ok1 ? e.y : c.pos) * kPRowBytes;
+#pragma unroll
+  for (int k = 0; k < kPLines; ++k) {
+    buf[k] = *reinterpret_cast<const u32x4*>(src0 + 128 * k);
+    buf[kPLines + k] = *reinterpret_cast<const u32x4*>(src1 + 128 * k);
+  }
+  // key r's validity is that of lanes 8 (r % 8) .. + 7 (bits 8 (r % 8) of the ballots)
+  const uint64_t b0 = ballot(ok0), b1 = ballot(ok1);
+  uint32_t v = 0;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) v |= (uint32_t)((b0 >> (8 * r)) & 1u) << r | (uint32_t)((b1 >> (8 * r)) & 1u) << (8 + r);
+  return v;
+}
+
+__device__ __forceinline__ void pt_store(const PtCtx& c, const u32x4 (&buf)[kPLoads]) {
+#pragma unroll
+  for (int k = 0; k < kPLines; ++k) {
+    *reinterpret_cast<u32x4*>(pt_tile + c.wofs[0] + 128 * k) = buf[k];
+    *reinterpret_cast<u32x4*>(pt_tile + c.wofs[1] + 128 * k) = buf[kPLines + k];
+  }
+}
+
+// S^T[key 4 g + jj][head n] (raw) of the tile's rows, in three independent chains.  The K
+// and query reads run kPQAhead MFMAs ahead (the order is pinned: left to itself the
+// scheduler puts every read right before its MFMA and waits out its latency).
+constexpr int kPQAhead = 4;
+__device__ __forceinline__ f32x4 pt_qk(const PtCtx& c) {
   // (the query address is made opaque: hoisted out of a loop, the 18 reads would pin 72
   // registers for the whole token)
   const uint8_t* qb = reinterpret_cast<const uint8_t*>(&pt_q[0][0]) + loop_local(16 * c.lane);
+  auto kread = [&](int s) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(pt_tile + c.kofs[s & 1] + 128 * (s >> 1));
+  };
+  auto qread = [&](int s) -> bf16x8 { return *reinterpret_cast<const bf16x8*>(qb + 1024 * s); };
+  bf16x8 kw[kPQAhead], qw[kPQAhead];
+#pragma unroll
+  for (int s = 0; s < kPQAhead; ++s) {
+    kw[s] = kread(s);
+    qw[s] = qread(s);
+  }
   f32x4 acc[3] = {};
 #pragma unroll
-  for (int s = 0; s < kPLoads; ++s)
-    acc[s % 3] = mfma16x16x32(__builtin_bit_cast(bf16x8, buf[s]),
-                              *reinterpret_cast<const bf16x8*>(qb + 1024 * s), acc[s % 3]);
+  for (int s = 0; s < kPLoads; ++s) {
+    __builtin_amdgcn_sched_barrier(0);
+    acc[s % 3] = mfma16x16x32(kw[s % kPQAhead], qw[s % kPQAhead], acc[s % 3]);
+    if (s + kPQAhead < kPLoads) {
+      kw[s % kPQAhead] = kread(s + kPQAhead);
+      qw[s % kPQAhead] = qread(s + kPQAhead);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   return acc[0] + acc[1] + acc[2];
 }
 
@@ -137,13 +214,21 @@ __device__ __forceinline__ s16x4_t pt_probs(const PtCtx& c, const float (&sv)[4]
   return __builtin_bit_cast(s16x4_t, pb);
 }
 
-// O^T[col 16 cb + 4 g + jj][head n] += V^T P^T
+// O^T[col 16 cb + 4 g + jj][head n] += V^T P^T.  The transposed reads run kPVAhead MFMAs
+// ahead (order pinned as in pt_qk).
+constexpr int kPVAhead = 6;
 __device__ __forceinline__ void pt_pv(const PtCtx& c, s16x4_t bop, f32x4 (&o)[kDv / 16]) {
+  auto vread = [&](int cb) -> u16x4 { return lds_read_tr16(pt_tile + c.rofs[cb & 3] + 128 * (cb >> 2)); };
+  u16x4 vw[kPVAhead];
+#pragma unroll
+  for (int i = 0; i < kPVAhead; ++i) vw[i] = vread(i);
 #pragma unroll
   for (int cb = 0; cb < kDv / 16; ++cb) {
-    const u16x4 a = lds_read_tr16(pt_vtile + c.rofs[cb & 7] + 256 * (cb >> 3));
-    o[cb] = mfma16x16x16(__builtin_bit_cast(s16x4_t, a), bop, o[cb]);
+    __builtin_amdgcn_sched_barrier(0);
+    o[cb] = mfma16x16x16(__builtin_bit_cast(s16x4_t, vw[cb % kPVAhead]), bop, o[cb]);
+    if (cb + kPVAhead < kDv / 16) vw[cb % kPVAhead] = vread(cb + kPVAhead);
   }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 __device__ __forceinline__ void pt_write(const PtCtx& c, const f32x4 (&o)[kDv / 16], float l_part, float m,
@@ -162,14 +247,18 @@ __device__ __forceinline__ void pt_write(const PtCtx& c, const f32x4 (&o)[kDv / 
 // Exact two-pass routine: head n's max over the whole row first, then the softmax
 // against it (no probability exceeds 1).  Both passes share pt_qk / pt_mask with the main
 // loop, so their scores are bit-identical.
-__device__ __noinline__ void pt_exact(const PtCtx& c, uint16_t* orow, float* lse_at) {
+__device__ __noinline__ void pt_exact(const uint16_t* kv, const int32_t* topk, int64_t ld, int S, int cols,
+                                     int64_t q_pos_offset, float scale_log2, int token, uint16_t* orow,
+                                     float* lse_at) {
+  const PtCtx c = pt_context(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token);
   const int nsteps = (c.cols + kPKeys - 1) / kPKeys;
   float m = kNegInf;
   for (int j = 0; j < nsteps; ++j) {
-    uint4 buf[kPLoads];
-    const uint32_t vbits = pt_issue(c, pt_entry(c, j), j, buf);
+    u32x4 buf[kPLoads];
+    const uint32_t vbits = pt_issue(c, pt_entries(c, j), j, buf);
+    pt_store(c, buf);
     float sv[4];
-    m = fmaxf(m, pt_mask(c, pt_qk(c, buf), vbits, sv));
+    m = fmaxf(m, pt_mask(c, pt_qk(c), vbits, sv));
   }
   m = max_over_rowgroups(m) * c.sc;
   float l = 0.f;
@@ -177,11 +266,11 @@ __device__ __noinline__ void pt_exact(const PtCtx& c, uint16_t* orow, float* lse
 #pragma unroll
   for (int cb = 0; cb < kDv / 16; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < nsteps; ++j) {
-    uint4 buf[kPLoads];
-    const uint32_t vbits = pt_issue(c, pt_entry(c, j), j, buf);
-    pt_store_v(c, buf);
+    u32x4 buf[kPLoads];
+    const uint32_t vbits = pt_issue(c, pt_entries(c, j), j, buf);
+    pt_store(c, buf);
     float sv[4];
-    pt_mask(c, pt_qk(c, buf), vbits, sv);
+    pt_mask(c, pt_qk(c), vbits, sv);
     pt_pv(c, pt_probs(c, sv, m, l), o);
   }
   pt_write(c, o, l, m, orow, lse_at);
@@ -197,30 +286,7 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
   const int token = T - 1 - tq;
   const int hb = item - tq * nb;
 
-  PtCtx c;
-  c.lane = threadIdx.x;
-  c.g = c.lane >> 4;
-  c.n = c.lane & 15;
-  int64_t pos64 = q_pos_offset + token;
-  if (pos64 > S - 1) pos64 = S - 1;  // positions beyond S - 1 cannot be selected
-  c.pos = uniform((int)pos64);
-  c.cols = cols;
-  c.trow = topk + (size_t)token * ld;
-  c.kvb = reinterpret_cast<const uint8_t*>(kv) + 16 * c.g;
-  c.sc = fabsf(scale_log2);
-  // LDS V tile.  Stores: lane (g, n) writes chunk 4 s + g of row n.  Transposed reads for
-  // O^T block cb (cols 16 cb .. + 15): lane (g, i) of a 16-lane group addresses row
-  // 4 g + i / 4, cols 16 cb + 4 (i % 4) .. + 3 (chunk 2 cb + (i % 4) / 2, half i % 2), so
-  // that output lane (g, n) receives V[key 4 g + jj][col 16 cb + n], jj = 0..3.
-  {
-    const int wx = c.g ^ vswz(c.n);
-    const int rr = 4 * c.g + (c.n >> 2);
-    const int rx = ((c.n >> 1) & 1) ^ vswz(rr);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) c.wofs[u] = c.n * kPVRowBytes + 16 * (wx ^ (4 * u));
-#pragma unroll
-    for (int b = 0; b < 8; ++b) c.rofs[b] = rr * kPVRowBytes + 8 * (c.n & 1) + 16 * (rx ^ (2 * b));
-  }
+  const PtCtx c = pt_context(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token);
 
   // queries of head n, dims 32 s + 8 g .. + 8 (the B operand of S^T = K Q^T); a negative
   // scale is applied as |scale| on negated queries so the max can be taken on raw scores
@@ -244,10 +310,10 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
 
   // The main loop runs an even number of steps (an odd count gets one all-masked step,
   // which adds nothing), so that it has a single exit.  Step j lives in register buffer
-  // j % 2; its QK MFMAs and V stores consume the buffer, which then receives step j + 2's
-  // rows, in flight during step j's softmax and PV and all of step j + 1.  The entry of
-  // step j + 3 is read before step j + 2's loads, so that waiting for an entry never
-  // waits for rows issued after it.
+  // j % 2; once its rows are stored to the LDS tile the buffer receives step j + 2's rows,
+  // in flight during the rest of step j and all of step j + 1.  The entries of step j + 3
+  // are read before step j + 2's loads, so that waiting for an entry never waits for rows
+  // issued after it.
   const int nsteps = (cols + kPKeys - 1) / kPKeys;
   const int nsteps2 = nsteps + (nsteps & 1);
   float m_ref = kNegInf;  // head n's reference (log2 units); equal in the 4 lane groups
@@ -255,17 +321,17 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
   f32x4 o[kDv / 16];
 #pragma unroll
   for (int cb = 0; cb < kDv / 16; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  uint4 ra[kPLoads], rb[kPLoads];
+  u32x4 ra[kPLoads], rb[kPLoads];
   uint32_t va = 0, vb = 0;
-  int32_t e_next = 0;  // entry of the step whose loads start next
-  {  // issue order as in the loop (entry, rows, entry, rows), pinned by scheduling
+  int2 e_next = {0, 0};  // entries of the step whose loads start next
+  {  // issue order as in the loop (entries, rows, entries, rows), pinned by scheduling
      // barriers: the wait counts at the loop head merge this order with the loop's
-    const int32_t e0 = pt_entry(c, 0);
-    const int32_t e1 = pt_entry(c, 1);
+    const int2 e0 = pt_entries(c, 0);
+    const int2 e1 = pt_entries(c, 1);
     __builtin_amdgcn_sched_barrier(0);
     va = pt_issue(c, e0, 0, ra);
     __builtin_amdgcn_sched_barrier(0);
-    e_next = pt_entry(c, 2);
+    e_next = pt_entries(c, 2);
     __builtin_amdgcn_sched_barrier(0);
     vb = pt_issue(c, e1, 1, rb);
     __builtin_amdgcn_sched_barrier(0);
@@ -273,22 +339,21 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
   // one step; `over` becomes true when a score exceeds the reference by more than the
   // slack (the loop still runs to its end, and its result is then discarded)
   bool over = false;
-  auto step = [&](int j, uint4 (&buf)[kPLoads], uint32_t& vbuf) {
-    pt_store_v(c, buf);
-    const f32x4 sacc = pt_qk(c, buf);
+  auto step = [&](int j, u32x4 (&buf)[kPLoads], uint32_t& vbuf) {
+    pt_store(c, buf);
     const uint32_t vbits = vbuf;
-    // the refill must not be scheduled above the reads of the buffer it overwrites
+    // the refill must not be scheduled above the stores that read the buffer
     __builtin_amdgcn_sched_barrier(0);
     {  // (unconditional: past the row the loads are masked dummies, and the wait
        // counts stay exact only on a branch-free path)
-      const int32_t e = e_next;
-      e_next = pt_entry(c, j + 3);
+      const int2 e = e_next;
+      e_next = pt_entries(c, j + 3);
       __builtin_amdgcn_sched_barrier(0);
       vbuf = pt_issue(c, e, j + 2, buf);
     }
     __builtin_amdgcn_sched_barrier(0);
     float sv[4];
-    const float mt = pt_mask(c, sacc, vbits, sv) * c.sc;
+    const float mt = pt_mask(c, pt_qk(c), vbits, sv) * c.sc;
     // a head's first valid scores set its reference (its O and l are still zero)
     if (ballot(m_ref == kNegInf && mt != kNegInf) != 0) {
       const float mh = max_over_rowgroups(mt);
@@ -302,7 +367,7 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
     step(j + 1, rb, vb);
   }
   if (over) {
-    pt_exact(c, orow, lse_at);
+    pt_exact(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token, orow, lse_at);
     return;
   }
   pt_write(c, o, l_run, m_ref, orow, lse_at);
