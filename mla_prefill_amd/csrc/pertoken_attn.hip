@@ -68,6 +68,10 @@ __device__ __forceinline__ f32x4 mfma16x16x16(s16x4_t a, s16x4_t b, f32x4 c) {
 // 128-byte line -- and the queries, lane-private: lane l's chunk s at pt_q[s][l].
 __shared__ __align__(16) uint8_t pt_tile[kPKeys * kPRowBytes];
 __shared__ __align__(16) uint4 pt_q[kPLoads][64];
+// sorted mode (positions < 65536, rows of at most kPSortMax columns): the token's valid
+// entries in ascending order
+constexpr int kPSortMax = 2048;
+__shared__ __align__(16) uint16_t pt_sorted[kPSortMax];
 
 __device__ __forceinline__ int tswz(int r) { return (2 * (r >> 1) + (r >> 3)) & 7; }
 
@@ -122,9 +126,13 @@ __device__ __forceinline__ PtCtx pt_context(const uint16_t* kv, const int32_t* t
   return c;
 }
 
-// this lane's entries of step j: rows er and 8 + er (clamped into the row)
+// this lane's entries of step j: rows er and 8 + er (clamped into the list: the top-k row,
+// or in sorted mode the sorted valid entries, c.cols of them)
+template <bool kSorted>
 __device__ __forceinline__ int2 pt_entries(const PtCtx& c, int j) {
-  return int2{c.trow[min(kPKeys * j + c.er, c.cols - 1)], c.trow[min(kPKeys * j + 8 + c.er, c.cols - 1)]};
+  const int i0 = min(kPKeys * j + c.er, c.cols - 1), i1 = min(kPKeys * j + 8 + c.er, c.cols - 1);
+  if (kSorted) return int2{(int)pt_sorted[i0], (int)pt_sorted[i1]};
+  return int2{c.trow[i0], c.trow[i1]};
 }
 
 // start the loads of step j's rows into `buf` (buf[k]: line k of row er, buf[9 + k]: of row
@@ -247,6 +255,7 @@ __device__ __forceinline__ void pt_write(const PtCtx& c, const f32x4 (&o)[kDv / 
 // Exact two-pass routine: head n's max over the whole row first, then the softmax
 // against it (no probability exceeds 1).  Both passes share pt_qk / pt_mask with the main
 // loop, so their scores are bit-identical.
+template <bool kSorted>
 __device__ __noinline__ void pt_exact(const uint16_t* kv, const int32_t* topk, int64_t ld, int S, int cols,
                                      int64_t q_pos_offset, float scale_log2, int token, uint16_t* orow,
                                      float* lse_at) {
@@ -255,7 +264,7 @@ __device__ __noinline__ void pt_exact(const uint16_t* kv, const int32_t* topk, i
   float m = kNegInf;
   for (int j = 0; j < nsteps; ++j) {
     u32x4 buf[kPLoads];
-    const uint32_t vbits = pt_issue(c, pt_entries(c, j), j, buf);
+    const uint32_t vbits = pt_issue(c, pt_entries<kSorted>(c, j), j, buf);
     pt_store(c, buf);
     float sv[4];
     m = fmaxf(m, pt_mask(c, pt_qk(c), vbits, sv));
@@ -267,7 +276,7 @@ __device__ __noinline__ void pt_exact(const uint16_t* kv, const int32_t* topk, i
   for (int cb = 0; cb < kDv / 16; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < nsteps; ++j) {
     u32x4 buf[kPLoads];
-    const uint32_t vbits = pt_issue(c, pt_entries(c, j), j, buf);
+    const uint32_t vbits = pt_issue(c, pt_entries<kSorted>(c, j), j, buf);
     pt_store(c, buf);
     float sv[4];
     pt_mask(c, pt_qk(c), vbits, sv);
@@ -276,6 +285,7 @@ __device__ __noinline__ void pt_exact(const uint16_t* kv, const int32_t* topk, i
   pt_write(c, o, l, m, orow, lse_at);
 }
 
+template <bool kSorted>
 __global__ __launch_bounds__(64) void pertoken_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ topk, int64_t ld, int T, int H, int S, int cols,
@@ -286,7 +296,7 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
   const int token = T - 1 - tq;
   const int hb = item - tq * nb;
 
-  const PtCtx c = pt_context(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token);
+  PtCtx c = pt_context(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token);
 
   // queries of head n, dims 32 s + 8 g .. + 8 (the B operand of S^T = K Q^T); a negative
   // scale is applied as |scale| on negated queries so the max can be taken on raw scores
@@ -302,7 +312,45 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
   }
   uint16_t* orow = out + ((size_t)token * H + hb * 16 + c.n) * kDv + 4 * c.g;
   float* lse_at = lse + (size_t)token * H + hb * 16 + c.n;
-  if (cols == 0) {  // nothing selected: zero output, LSE -inf
+  if (kSorted && cols > 0) {
+    // The token's valid entries (0 <= x <= position) in ascending order: a bitmap of the
+    // positions (in the LDS tile, unused until the first step), a prefix count over the
+    // lanes, and compaction.  Tokens of a group select nearly the same rows; walking them
+    // in the same order lets the concurrent tokens of a group find each other's rows in
+    // L2.  (Repeated entries collapse to one.)
+    uint32_t* bm = reinterpret_cast<uint32_t*>(pt_tile);
+    const int nw = (c.pos >> 5) + 1;  // words covering positions 0..pos (pos < 65536)
+    for (int w = c.lane; w < nw; w += 64) bm[w] = 0u;
+    __syncthreads();  // (one wave: orders the LDS accesses for the compiler)
+    for (int col = c.lane; col < cols; col += 64) {
+      const int32_t x = c.trow[col];
+      if (x >= 0 && x <= c.pos) atomicOr(&bm[x >> 5], 1u << (x & 31));
+    }
+    __syncthreads();
+    const int wpl = (nw + 63) >> 6;  // lane l owns words l * wpl .. + wpl - 1
+    const int w0 = c.lane * wpl;
+    int cnt = 0;
+    for (int k = 0; k < wpl; ++k)
+      if (w0 + k < nw) cnt += __popc(bm[w0 + k]);
+    int incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d);
+      if (c.lane >= d) incl += v;
+    }
+    int at = incl - cnt;
+    for (int k = 0; k < wpl; ++k) {
+      if (w0 + k >= nw) break;
+      uint32_t bits = bm[w0 + k];
+      while (bits != 0u) {
+        pt_sorted[at++] = (uint16_t)(32 * (w0 + k) + __ffs(bits) - 1);
+        bits &= bits - 1u;
+      }
+    }
+    c.cols = uniform(__shfl(incl, 63));
+    __syncthreads();  // the sorted list is read, and the tile rewritten, from here on
+  }
+  if (c.cols == 0) {  // nothing selected: zero output, LSE -inf
     const f32x4 z[kDv / 16] = {};
     pt_write(c, z, 0.f, kNegInf, orow, lse_at);
     return;
@@ -314,7 +362,7 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
   // in flight during the rest of step j and all of step j + 1.  The entries of step j + 3
   // are read before step j + 2's loads, so that waiting for an entry never waits for rows
   // issued after it.
-  const int nsteps = (cols + kPKeys - 1) / kPKeys;
+  const int nsteps = (c.cols + kPKeys - 1) / kPKeys;
   const int nsteps2 = nsteps + (nsteps & 1);
   float m_ref = kNegInf;  // head n's reference (log2 units); equal in the 4 lane groups
   float l_run = 0.f;      // this lane's partial sum (keys 4 g .. 4 g + 3 of every step)
@@ -326,12 +374,12 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
   int2 e_next = {0, 0};  // entries of the step whose loads start next
   {  // issue order as in the loop (entries, rows, entries, rows), pinned by scheduling
      // barriers: the wait counts at the loop head merge this order with the loop's
-    const int2 e0 = pt_entries(c, 0);
-    const int2 e1 = pt_entries(c, 1);
+    const int2 e0 = pt_entries<kSorted>(c, 0);
+    const int2 e1 = pt_entries<kSorted>(c, 1);
     __builtin_amdgcn_sched_barrier(0);
     va = pt_issue(c, e0, 0, ra);
     __builtin_amdgcn_sched_barrier(0);
-    e_next = pt_entries(c, 2);
+    e_next = pt_entries<kSorted>(c, 2);
     __builtin_amdgcn_sched_barrier(0);
     vb = pt_issue(c, e1, 1, rb);
     __builtin_amdgcn_sched_barrier(0);
@@ -347,7 +395,7 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
     {  // (unconditional: past the row the loads are masked dummies, and the wait
        // counts stay exact only on a branch-free path)
       const int2 e = e_next;
-      e_next = pt_entries(c, j + 3);
+      e_next = pt_entries<kSorted>(c, j + 3);
       __builtin_amdgcn_sched_barrier(0);
       vbuf = pt_issue(c, e, j + 2, buf);
     }
@@ -367,7 +415,7 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
     step(j + 1, rb, vb);
   }
   if (over) {
-    pt_exact(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token, orow, lse_at);
+    pt_exact<kSorted>(kv, topk, ld, S, c.cols, q_pos_offset, scale_log2, token, orow, lse_at);
     return;
   }
   pt_write(c, o, l_run, m_ref, orow, lse_at);
@@ -378,8 +426,12 @@ hipError_t launch_pertoken_attn(const uint16_t* q, const uint16_t* kv, const int
                                 float scale, uint16_t* out, float* lse, hipStream_t stream) {
   const long long items = (long long)T * (H / 16);
   if (items == 0) return hipSuccess;
-  hipLaunchKernelGGL(pertoken_attn_kernel, dim3((unsigned)items), dim3(64), 0, stream, q, kv, topk,
-                     ld, T, H, S, cols, q_pos_offset, scale * kLog2e, out, lse);
+  if (S <= 65536 && cols <= kPSortMax)
+    hipLaunchKernelGGL(pertoken_attn_kernel<true>, dim3((unsigned)items), dim3(64), 0, stream, q, kv,
+                       topk, ld, T, H, S, cols, q_pos_offset, scale * kLog2e, out, lse);
+  else
+    hipLaunchKernelGGL(pertoken_attn_kernel<false>, dim3((unsigned)items), dim3(64), 0, stream, q, kv,
+                       topk, ld, T, H, S, cols, q_pos_offset, scale * kLog2e, out, lse);
   return hipGetLastError();
 }
 
