@@ -9,23 +9,24 @@
 // this kernel bound by the KV gather (2048 rows x 1152 B per token).
 //
 // MI355X design: one wave per (token, 16-head block), one wave per workgroup
-// (no barriers), one wave per SIMD:
-//  * the token's top-k row is consumed 16 entries at a time.  Rows are loaded
-//    straight into registers with coalesced loads: each load instruction
-//    covers one 128-byte line of 8 rows (lane l takes row l / 8, 16 bytes
-//    l % 8 of the line), so a quarter-wave touches two cache lines.  (Loading
-//    rows directly in the MFMA operand layout puts 16 rows under every
-//    quarter-wave, and the address path, one cache line at a time, then
-//    bounds the kernel.)  Two register buffers form a ring: a step's buffer is
-//    refilled with the rows two steps ahead as soon as it has been written to
-//    LDS, so about two steps (36 KiB) are in flight per wave.  Invalid entries
-//    (-1, past the row, beyond the token's position) load the token's own row
-//    and are masked;
-//  * each step's 16 rows go to an 18 KiB LDS tile (XOR-swizzled, free of bank
-//    conflicts for the stores, the 16-byte K reads and the transposed V
-//    reads).  S^T = K Q^T runs on v_mfma_f32_16x16x32_bf16 in three
-//    independent accumulation chains, with the B operand (the 16 heads'
-//    queries) re-read from a lane-private LDS area; O^T = V^T P^T runs on
+// (no barriers), one wave per SIMD.  Two kernels share the arithmetic:
+//  * sorted walk (positions below 65536, rows of at most 2048 columns, which
+//    covers the pages' workloads): the wave first sorts its token's valid
+//    entries in LDS, so that the concurrent tokens of a range, which select
+//    nearly the same rows, walk them in the same order and find them in L2.
+//    Rows then stream 16 at a time into two 18 KiB LDS tiles by asynchronous
+//    global->LDS copies, one step ahead of the compute (each copy instruction
+//    covers one 128-byte line of 8 rows, so a quarter-wave touches two cache
+//    lines); the 16 heads' queries stay in registers;
+//  * register ring (any size): rows are loaded with the same coalesced pattern
+//    into two register buffers, each refilled two steps ahead as soon as it
+//    has been written to an 18 KiB LDS tile; the queries sit in a lane-private
+//    LDS area;
+//  * both: invalid entries (-1, past the row, beyond the token's position)
+//    fetch the token's own row and are masked.  The tiles are XOR-swizzled,
+//    free of bank conflicts for the writes, the 16-byte K reads and the
+//    transposed V reads.  S^T = K Q^T runs on v_mfma_f32_16x16x32_bf16 in
+//    three independent accumulation chains; O^T = V^T P^T runs on
 //    v_mfma_f32_16x16x16_bf16 with V^T from ds_read_b64_tr_b16 and the
 //    probabilities straight from the score accumulators as the B operand.
 //    Operand reads run several MFMAs ahead (the order is pinned: left to
@@ -239,7 +240,7 @@ __device__ __forceinline__ void pt_pv(const PtCtx& c, s16x4_t bop, f32x4 (&o)[kD
   __builtin_amdgcn_sched_barrier(0);
 }
 
-__device__ __forceinline__ void pt_write(const PtCtx& c, const f32x4 (&o)[kDv / 16], float l_part, float m,
+__device__ __forceinline__ void pt_write(int g, const f32x4 (&o)[kDv / 16], float l_part, float m,
                                          uint16_t* orow, float* lse_at) {
   const float l = sum_over_rowgroups(l_part);
   const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -249,7 +250,7 @@ __device__ __forceinline__ void pt_write(const PtCtx& c, const f32x4 (&o)[kDv / 
                       (__bf16)(o[cb][3] * inv)};
     *reinterpret_cast<bf16x4*>(orow + 16 * cb) = w;
   }
-  if (c.g == 0) *lse_at = l > 0.f ? (m + fast_log2(l)) * kLn2 : kNegInf;
+  if (g == 0) *lse_at = l > 0.f ? (m + fast_log2(l)) * kLn2 : kNegInf;
 }
 
 // Exact two-pass routine: head n's max over the whole row first, then the softmax
@@ -282,10 +283,9 @@ __device__ __noinline__ void pt_exact(const uint16_t* kv, const int32_t* topk, i
     pt_mask(c, pt_qk(c), vbits, sv);
     pt_pv(c, pt_probs(c, sv, m, l), o);
   }
-  pt_write(c, o, l, m, orow, lse_at);
+  pt_write(c.g, o, l, m, orow, lse_at);
 }
 
-template <bool kSorted>
 __global__ __launch_bounds__(64) void pertoken_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ topk, int64_t ld, int T, int H, int S, int cols,
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
   const int token = T - 1 - tq;
   const int hb = item - tq * nb;
 
-  PtCtx c = pt_context(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token);
+  const PtCtx c = pt_context(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token);
 
   // queries of head n, dims 32 s + 8 g .. + 8 (the B operand of S^T = K Q^T); a negative
   // scale is applied as |scale| on negated queries so the max can be taken on raw scores
@@ -312,47 +312,9 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
   }
   uint16_t* orow = out + ((size_t)token * H + hb * 16 + c.n) * kDv + 4 * c.g;
   float* lse_at = lse + (size_t)token * H + hb * 16 + c.n;
-  if (kSorted && cols > 0) {
-    // The token's valid entries (0 <= x <= position) in ascending order: a bitmap of the
-    // positions (in the LDS tile, unused until the first step), a prefix count over the
-    // lanes, and compaction.  Tokens of a group select nearly the same rows; walking them
-    // in the same order lets the concurrent tokens of a group find each other's rows in
-    // L2.  (Repeated entries collapse to one.)
-    uint32_t* bm = reinterpret_cast<uint32_t*>(pt_tile);
-    const int nw = (c.pos >> 5) + 1;  // words covering positions 0..pos (pos < 65536)
-    for (int w = c.lane; w < nw; w += 64) bm[w] = 0u;
-    __syncthreads();  // (one wave: orders the LDS accesses for the compiler)
-    for (int col = c.lane; col < cols; col += 64) {
-      const int32_t x = c.trow[col];
-      if (x >= 0 && x <= c.pos) atomicOr(&bm[x >> 5], 1u << (x & 31));
-    }
-    __syncthreads();
-    const int wpl = (nw + 63) >> 6;  // lane l owns words l * wpl .. + wpl - 1
-    const int w0 = c.lane * wpl;
-    int cnt = 0;
-    for (int k = 0; k < wpl; ++k)
-      if (w0 + k < nw) cnt += __popc(bm[w0 + k]);
-    int incl = cnt;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int v = __shfl_up(incl, d);
-      if (c.lane >= d) incl += v;
-    }
-    int at = incl - cnt;
-    for (int k = 0; k < wpl; ++k) {
-      if (w0 + k >= nw) break;
-      uint32_t bits = bm[w0 + k];
-      while (bits != 0u) {
-        pt_sorted[at++] = (uint16_t)(32 * (w0 + k) + __ffs(bits) - 1);
-        bits &= bits - 1u;
-      }
-    }
-    c.cols = uniform(__shfl(incl, 63));
-    __syncthreads();  // the sorted list is read, and the tile rewritten, from here on
-  }
   if (c.cols == 0) {  // nothing selected: zero output, LSE -inf
     const f32x4 z[kDv / 16] = {};
-    pt_write(c, z, 0.f, kNegInf, orow, lse_at);
+    pt_write(c.g, z, 0.f, kNegInf, orow, lse_at);
     return;
   }
 
@@ -374,12 +336,12 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
   int2 e_next = {0, 0};  // entries of the step whose loads start next
   {  // issue order as in the loop (entries, rows, entries, rows), pinned by scheduling
      // barriers: the wait counts at the loop head merge this order with the loop's
-    const int2 e0 = pt_entries<kSorted>(c, 0);
-    const int2 e1 = pt_entries<kSorted>(c, 1);
+    const int2 e0 = pt_entries<false>(c, 0);
+    const int2 e1 = pt_entries<false>(c, 1);
     __builtin_amdgcn_sched_barrier(0);
     va = pt_issue(c, e0, 0, ra);
     __builtin_amdgcn_sched_barrier(0);
-    e_next = pt_entries<kSorted>(c, 2);
+    e_next = pt_entries<false>(c, 2);
     __builtin_amdgcn_sched_barrier(0);
     vb = pt_issue(c, e1, 1, rb);
     __builtin_amdgcn_sched_barrier(0);
@@ -395,7 +357,7 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
     {  // (unconditional: past the row the loads are masked dummies, and the wait
        // counts stay exact only on a branch-free path)
       const int2 e = e_next;
-      e_next = pt_entries<kSorted>(c, j + 3);
+      e_next = pt_entries<false>(c, j + 3);
       __builtin_amdgcn_sched_barrier(0);
       vbuf = pt_issue(c, e, j + 2, buf);
     }
@@ -415,10 +377,271 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
     step(j + 1, rb, vb);
   }
   if (over) {
-    pt_exact<kSorted>(kv, topk, ld, S, c.cols, q_pos_offset, scale_log2, token, orow, lse_at);
+    pt_exact<false>(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token, orow, lse_at);
     return;
   }
-  pt_write(c, o, l_run, m_ref, orow, lse_at);
+  pt_write(c.g, o, l_run, m_ref, orow, lse_at);
+}
+
+// ---------------------------------------------------------------------------
+// Sorted-walk kernel (positions below 65536, rows of at most kPSortMax columns).
+//
+// The wave first sorts its token's valid entries (0 <= x <= position) into pt_sorted:
+// a bitmap of the positions in the LDS tile, a prefix count over the lanes, and
+// compaction.  Tokens of a range select nearly the same rows, so walking them in the
+// same order lets concurrent tokens find each other's rows in L2.  (Repeated entries
+// collapse to one.)  Rows then stream into two 18 KiB LDS tiles by asynchronous
+// global->LDS copies (one step ahead; no register ring and no LDS store instructions),
+// in the 8-row-group layout of common.h: 16-byte chunk k of tile row r at
+// 9216 (r / 8) + 1024 (k / 8) + 128 (r % 8) + 16 ((k % 8) ^ swz8(r % 8) ^ (r / 8)).
+// The queries stay in registers.  The exact fallback reuses the register-ring
+// routines (the second tile is the query area there).
+// ---------------------------------------------------------------------------
+constexpr int kPGroupBytes = 8 * kPRowBytes;  // one 8-row group of a tile (9216)
+
+// returns the number of distinct valid entries of the token's row, sorted into pt_sorted
+__device__ __forceinline__ int pt_sort(const int32_t* trow, int cols, int pos, int lane) {
+  uint32_t* bm = reinterpret_cast<uint32_t*>(pt_tile);
+  const int nw = (pos >> 5) + 1;  // words covering positions 0..pos (pos < 65536)
+  for (int w = lane; w < nw; w += 64) bm[w] = 0u;
+  __syncthreads();  // (one wave: orders the LDS accesses for the compiler)
+  for (int col = lane; col < cols; col += 64) {
+    const int32_t x = trow[col];
+    if (x >= 0 && x <= pos) atomicOr(&bm[x >> 5], 1u << (x & 31));
+  }
+  __syncthreads();
+  const int wpl = (nw + 63) >> 6;  // lane l owns words l * wpl .. + wpl - 1
+  const int w0 = lane * wpl;
+  int cnt = 0;
+  for (int k = 0; k < wpl; ++k)
+    if (w0 + k < nw) cnt += __popc(bm[w0 + k]);
+  int incl = cnt;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d);
+    if (lane >= d) incl += v;
+  }
+  int at = incl - cnt;
+  for (int k = 0; k < wpl; ++k) {
+    if (w0 + k >= nw) break;
+    uint32_t bits = bm[w0 + k];
+    while (bits != 0u) {
+      pt_sorted[at++] = (uint16_t)(32 * (w0 + k) + __ffs(bits) - 1);
+      bits &= bits - 1u;
+    }
+  }
+  const int n = uniform(__shfl(incl, 63));
+  __syncthreads();  // the sorted list is read, and the tile rewritten, from here on
+  return n;
+}
+
+struct PdCtx {
+  int cols, pos, lane, g, n, er;
+  float sc;
+  int dofs[2];  // this lane's 16 bytes of each 128-byte line, for rows er (h = 0) and 8 + er (h = 1)
+  int kofs[2];  // K read offsets (row n, chunk 4 s + g: per s % 2; + 1024 (s / 2))
+  int rofs[4];  // transposed V read offsets (per column block cb % 4; + 1024 (cb / 4))
+};
+
+__device__ __forceinline__ PdCtx pd_context(int pos, int cols, float scale_log2) {
+  PdCtx c;
+  c.lane = threadIdx.x;
+  c.g = c.lane >> 4;
+  c.n = c.lane & 15;
+  c.er = c.lane >> 3;
+  c.pos = pos;
+  c.cols = cols;
+  c.sc = fabsf(scale_log2);
+  // copies: lane l fills position l % 8 of row l / 8 of a group's 1 KiB block, i.e. it
+  // fetches chunk (l % 8) ^ swz8(l / 8) ^ h of the block's 128-byte line
+#pragma unroll
+  for (int h = 0; h < 2; ++h) c.dofs[h] = 16 * ((c.lane & 7) ^ swz8(c.er) ^ h);
+  // K reads: lane (g, n) reads row n, chunk 4 s + g
+  const int kg = c.n >> 3, k8 = c.n & 7;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) c.kofs[p] = kg * kPGroupBytes + 128 * k8 + 16 * ((4 * p + c.g) ^ swz8(k8) ^ kg);
+  // transposed reads for block cb: lane (g, i) addresses row 4 g + i / 4, cols 16 cb + 4 (i % 4)
+  // .. + 3 (chunk 2 cb + (i % 4) / 2, half i % 2): output lane (g, n) receives
+  // V[key 4 g + jj][col 16 cb + n]
+  const int rr = 4 * c.g + (c.n >> 2), rg = rr >> 3, r8 = rr & 7;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    c.rofs[u] = rg * kPGroupBytes + 128 * r8 + 16 * ((2 * u + ((c.n & 3) >> 1)) ^ swz8(r8) ^ rg) + 8 * (c.n & 1);
+  return c;
+}
+
+// start the copies of step j's rows into the tile at LDS address `tile`; returns the
+// validity bits of the step's 16 keys (key r <-> bit r)
+__device__ __forceinline__ uint32_t pd_issue(const PdCtx& c, const uint8_t* kvb, int2 e, int j, uint32_t tile) {
+  const bool ok0 = kPKeys * j + c.er < c.cols && e.x >= 0 && e.x <= c.pos;
+  const bool ok1 = kPKeys * j + 8 + c.er < c.cols && e.y >= 0 && e.y <= c.pos;
+  const uint8_t* src0 = kvb + (size_t)(ok0 ? e.x : c.pos) * kPRowBytes + c.dofs[0];
+  const uint8_t* src1 = kvb + (size_t)(ok1 ? e.y : c.pos) * kPRowBytes + c.dofs[1];
+#pragma unroll
+  for (int k = 0; k < kPLines; ++k) {
+    dma16(src0 + 128 * k, tile + 1024 * k);
+    dma16(src1 + 128 * k, tile + kPGroupBytes + 1024 * k);
+  }
+  const uint64_t b0 = ballot(ok0), b1 = ballot(ok1);
+  uint32_t v = 0;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) v |= (uint32_t)((b0 >> (8 * r)) & 1u) << r | (uint32_t)((b1 >> (8 * r)) & 1u) << (8 + r);
+  return v;
+}
+
+__device__ __forceinline__ int2 pd_entries(const PdCtx& c, int j) {
+  const int i0 = min(kPKeys * j + c.er, c.cols - 1), i1 = min(kPKeys * j + 8 + c.er, c.cols - 1);
+  return int2{(int)pt_sorted[i0], (int)pt_sorted[i1]};
+}
+
+// S^T[key 4 g + jj][head n] (raw), three chains; K reads kPQAhead MFMAs ahead
+__device__ __forceinline__ f32x4 pd_qk(const PdCtx& c, const uint8_t* tile, const bf16x8 (&qreg)[kPLoads]) {
+  auto kread = [&](int s) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(tile + c.kofs[s & 1] + 1024 * (s >> 1));
+  };
+  bf16x8 kw[kPQAhead];
+#pragma unroll
+  for (int s = 0; s < kPQAhead; ++s) kw[s] = kread(s);
+  f32x4 acc[3] = {};
+#pragma unroll
+  for (int s = 0; s < kPLoads; ++s) {
+    __builtin_amdgcn_sched_barrier(0);
+    acc[s % 3] = mfma16x16x32(kw[s % kPQAhead], qreg[s], acc[s % 3]);
+    if (s + kPQAhead < kPLoads) kw[s % kPQAhead] = kread(s + kPQAhead);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  return acc[0] + acc[1] + acc[2];
+}
+
+__device__ __forceinline__ void pd_pv(const PdCtx& c, const uint8_t* tile, s16x4_t bop, f32x4 (&o)[kDv / 16]) {
+  auto vread = [&](int cb) -> u16x4 { return lds_read_tr16(tile + c.rofs[cb & 3] + 1024 * (cb >> 2)); };
+  u16x4 vw[kPVAhead];
+#pragma unroll
+  for (int i = 0; i < kPVAhead; ++i) vw[i] = vread(i);
+#pragma unroll
+  for (int cb = 0; cb < kDv / 16; ++cb) {
+    __builtin_amdgcn_sched_barrier(0);
+    o[cb] = mfma16x16x16(__builtin_bit_cast(s16x4_t, vw[cb % kPVAhead]), bop, o[cb]);
+    if (cb + kPVAhead < kDv / 16) vw[cb % kPVAhead] = vread(cb + kPVAhead);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// invalid keys -> -inf; returns the max of this lane's 4 scores
+__device__ __forceinline__ float pd_mask(int g, const f32x4& sacc, uint32_t vbits, float (&sv)[4]) {
+  const uint32_t mine = vbits >> (4 * g);
+  float mt = kNegInf;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)mine, jj, 1);  // all ones if valid
+    const float raw = sacc[jj];  // (a scalar copy: bit casts of vector elements misread)
+    sv[jj] = __builtin_bit_cast(float, (sel & __builtin_bit_cast(uint32_t, raw)) | (~sel & 0xff800000u));
+    mt = fmaxf(mt, sv[jj]);
+  }
+  return mt;
+}
+
+__device__ __forceinline__ s16x4_t pd_probs(float sc, const float (&sv)[4], float m, float& l) {
+  const float nm = m == kNegInf ? 0.f : -m;
+  bf16x4 pb;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const float p = fast_exp2(__builtin_fmaf(sv[jj], sc, nm));
+    l += p;
+    pb[jj] = (__bf16)p;
+  }
+  return __builtin_bit_cast(s16x4_t, pb);
+}
+
+__global__ __launch_bounds__(64) void pertoken_sorted_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+    const int32_t* __restrict__ topk, int64_t ld, int T, int H, int S, int cols,
+    int64_t q_pos_offset, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  const int nb = H >> 4;
+  const int item = xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
+  const int tq = item / nb;
+  const int token = T - 1 - tq;
+  const int hb = item - tq * nb;
+  const int lane = threadIdx.x, g = lane >> 4, n = lane & 15;
+  int64_t pos64 = q_pos_offset + token;
+  if (pos64 > S - 1) pos64 = S - 1;  // positions beyond S - 1 cannot be selected
+  const int pos = uniform((int)pos64);
+
+  // queries of head n, dims 32 s + 8 g .. + 8 (the B operand of S^T = K Q^T), negated for a
+  // negative scale; completed before any asynchronous copy is in flight
+  bf16x8 qreg[kPLoads];
+  {
+    const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
+    const uint16_t* qrow = q + ((size_t)token * H + hb * 16 + n) * kDqk + 8 * g;
+#pragma unroll
+    for (int s = 0; s < kPLoads; ++s) {
+      u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 32 * s);
+      w ^= qsign;
+      qreg[s] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  uint16_t* orow = out + ((size_t)token * H + hb * 16 + n) * kDv + 4 * g;
+  float* lse_at = lse + (size_t)token * H + hb * 16 + n;
+  const int nsel = pt_sort(topk + (size_t)token * ld, cols, pos, lane);
+#pragma unroll
+  for (int s = 0; s < kPLoads; ++s) asm volatile("" : : "v"(qreg[s]));
+  if (nsel == 0) {  // nothing selected: zero output, LSE -inf
+    const f32x4 z[kDv / 16] = {};
+    pt_write(g, z, 0.f, kNegInf, orow, lse_at);
+    return;
+  }
+  const PdCtx c = pd_context(pos, nsel, scale_log2);
+  const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv);
+  uint8_t* const tile0 = pt_tile;
+  uint8_t* const tile1 = reinterpret_cast<uint8_t*>(&pt_q[0][0]);
+
+  // An even number of steps (an odd count gets one all-masked step, which adds nothing);
+  // step j reads tile j % 2, and once its last operand read has been consumed the tile
+  // receives step j + 2's rows, in flight during step j + 1.  Past the list the copies
+  // fetch the token's own row and are masked.
+  const int nsteps = (nsel + kPKeys - 1) / kPKeys;
+  const int nsteps2 = nsteps + (nsteps & 1);
+  float m_ref = kNegInf;  // head n's reference (log2 units); equal in the 4 lane groups
+  float l_run = 0.f;      // this lane's partial sum (keys 4 g .. 4 g + 3 of every step)
+  f32x4 o[kDv / 16];
+#pragma unroll
+  for (int cb = 0; cb < kDv / 16; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint32_t va = pd_issue(c, kvb, pd_entries(c, 0), 0, lds_addr(tile0));
+  uint32_t vb = pd_issue(c, kvb, pd_entries(c, 1), 1, lds_addr(tile1));
+  int2 e_next = pd_entries(c, 2);
+  bool over = false;
+  auto step = [&](int j, const uint8_t* tile, uint32_t& vbuf) {
+    wait_vmcnt<2 * kPLines>();  // step j's copies have landed (step j + 1's may be in flight)
+    float sv[4];
+    const float mt = pd_mask(g, pd_qk(c, tile, qreg), vbuf, sv) * c.sc;
+    // a head's first valid scores set its reference (its O and l are still zero)
+    if (ballot(m_ref == kNegInf && mt != kNegInf) != 0) {
+      const float mh = max_over_rowgroups(mt);
+      m_ref = m_ref == kNegInf ? mh : m_ref;
+    }
+    over |= ballot(mt > m_ref + kPSlack) != 0;
+    pd_pv(c, tile, pd_probs(c.sc, sv, m_ref, l_run), o);
+    // every operand read of the tile has been consumed; refill it
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    const int2 e = e_next;
+    e_next = pd_entries(c, j + 3);
+    vbuf = pd_issue(c, kvb, e, j + 2, lds_addr(tile));
+  };
+  for (int j = 0; j < nsteps2; j += 2) {
+    step(j, tile0, va);
+    step(j + 1, tile1, vb);
+  }
+  wait_vmcnt<0>();  // the copies issued past the list
+  if (over) {
+    // the exact routine reads the queries from the second tile's area
+#pragma unroll
+    for (int s = 0; s < kPLoads; ++s) pt_q[s][lane] = __builtin_bit_cast(uint4, qreg[s]);
+    __syncthreads();
+    pt_exact<true>(kv, topk, ld, S, nsel, q_pos_offset, scale_log2, token, orow, lse_at);
+    return;
+  }
+  pt_write(g, o, l_run, m_ref, orow, lse_at);
 }
 
 hipError_t launch_pertoken_attn(const uint16_t* q, const uint16_t* kv, const int32_t* topk,
@@ -427,11 +650,11 @@ hipError_t launch_pertoken_attn(const uint16_t* q, const uint16_t* kv, const int
   const long long items = (long long)T * (H / 16);
   if (items == 0) return hipSuccess;
   if (S <= 65536 && cols <= kPSortMax)
-    hipLaunchKernelGGL(pertoken_attn_kernel<true>, dim3((unsigned)items), dim3(64), 0, stream, q, kv,
-                       topk, ld, T, H, S, cols, q_pos_offset, scale * kLog2e, out, lse);
+    hipLaunchKernelGGL(pertoken_sorted_kernel, dim3((unsigned)items), dim3(64), 0, stream, q, kv, topk, ld,
+                       T, H, S, cols, q_pos_offset, scale * kLog2e, out, lse);
   else
-    hipLaunchKernelGGL(pertoken_attn_kernel<false>, dim3((unsigned)items), dim3(64), 0, stream, q, kv,
-                       topk, ld, T, H, S, cols, q_pos_offset, scale * kLog2e, out, lse);
+    hipLaunchKernelGGL(pertoken_attn_kernel, dim3((unsigned)items), dim3(64), 0, stream, q, kv, topk, ld,
+                       T, H, S, cols, q_pos_offset, scale * kLog2e, out, lse);
   return hipGetLastError();
 }
 
