@@ -168,16 +168,29 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nblocks) {
   return start + k;
 }
 
+// The values of lanes l and l ^ 32 (or l ^ 16), as a pair (own half first or second does not
+// matter to the symmetric reductions below).  v_permlane32_swap / v_permlane16_swap are
+// VALU operations: no LDS round trip, unlike a general lane shuffle.
+struct LanePair { float a, b; };
+__device__ __forceinline__ LanePair pair_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ LanePair pair_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float max_xor32(float v) { const LanePair p = pair_xor32(v); return fmaxf(p.a, p.b); }
+__device__ __forceinline__ float sum_xor32(float v) { const LanePair p = pair_xor32(v); return p.a + p.b; }
+
 // max / sum over the 4 lanes l, l^16, l^32, l^48 (the 4 row groups of a 16x16 C tile)
 __device__ __forceinline__ float max_over_rowgroups(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  const LanePair p = pair_xor16(v);
+  return max_xor32(fmaxf(p.a, p.b));
 }
 __device__ __forceinline__ float sum_over_rowgroups(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  const LanePair p = pair_xor16(v);
+  return sum_xor32(p.a + p.b);
 }
 
 }  // namespace dsa

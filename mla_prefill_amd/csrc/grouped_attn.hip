@@ -244,32 +244,6 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    float ml = kNegInf;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int kk = 8 * (j >> 2) + (j & 3);
-      const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)allowed, kk, 1);  // all ones if allowed
-      const float raw = sacc[j];  // (a scalar copy: bit casts of vector elements misread)
-      const float val = __builtin_bit_cast(float, (sel & __builtin_bit_cast(uint32_t, raw)) | (~sel & 0xff800000u));
-      sacc[j] = val;
-      ml = fmaxf(ml, val);
-    }
-    ml *= sc;
-    // a row's first valid scores set its reference (its O and l are still zero)
-    if (ballot(m_ref == kNegInf && ml != kNegInf) != 0) {
-      const float mr = fmaxf(ml, __shfl_xor(ml, 32));
-      m_ref = m_ref == kNegInf ? mr : m_ref;
-    }
-    over |= ballot(ml > m_ref + kRSlack) != 0;
-    const float nm = m_ref == kNegInf ? 0.f : -m_ref;
-    bf16x8 bop[2];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float p = fast_exp2(__builtin_fmaf(sacc[j], sc, nm));
-      l_run += p;
-      bop[j >> 3][j & 7] = (__bf16)p;
-    }
-
     // O^T += V^T P^T: step st covers slots 16 st .. 16 st + 15 with k-slot (hi, i) <->
     // slot 16 st + 8 (i / 4) + 4 hi + i % 4, i.e. score registers 8 st .. 8 st + 7.  MFMA i
     // (0..31) is step i / 16, column block i % 16; its V^T operand is read kRVAhead MFMAs
@@ -285,22 +259,58 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
       return __builtin_bit_cast(bf16x8, u16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
     };
     constexpr int kRVAhead = 3;
+    // (the first V^T reads do not depend on the probabilities: issued before the softmax,
+    // they complete under it)
     bf16x8 vw[kRVAhead];
 #pragma unroll
     for (int i = 0; i < kRVAhead; ++i) vw[i] = vread(i);
+    __builtin_amdgcn_sched_barrier(0);
+
+    float ml = kNegInf;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int kk = 8 * (j >> 2) + (j & 3);
+      const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)allowed, kk, 1);  // all ones if allowed
+      const float raw = sacc[j];  // (a scalar copy: bit casts of vector elements misread)
+      const float val = __builtin_bit_cast(float, (sel & __builtin_bit_cast(uint32_t, raw)) | (~sel & 0xff800000u));
+      sacc[j] = val;
+      ml = fmaxf(ml, val);
+    }
+    ml *= sc;
+    // a row's first valid scores set its reference (its O and l are still zero)
+    if (ballot(m_ref == kNegInf && ml != kNegInf) != 0) {
+      const float mr = max_xor32(ml);
+      m_ref = m_ref == kNegInf ? mr : m_ref;
+    }
+    over |= ballot(ml > m_ref + kRSlack) != 0;
+    const float nm = m_ref == kNegInf ? 0.f : -m_ref;
+    // probabilities of the first 16 slots (step 0); those of step 1 are computed between
+    // step 0's MFMAs, which do not need them
+    bf16x8 bop[2];
+    float l0 = 0.f, l1 = 0.f;
+    auto prob = [&](int j, float& l) {
+      const float p = fast_exp2(__builtin_fmaf(sacc[j], sc, nm));
+      l += p;
+      bop[j >> 3][j & 7] = (__bf16)p;
+    };
+#pragma unroll
+    for (int j = 0; j < 8; ++j) prob(j, l0);
+
 #pragma unroll
     for (int i = 0; i < 2 * (kRDv / 32); ++i) {
       __builtin_amdgcn_sched_barrier(0);
       o[i & 15] = mfma32x32x16(vw[i % kRVAhead], bop[i >> 4], o[i & 15]);
       if (i + kRVAhead < 2 * (kRDv / 32)) vw[i % kRVAhead] = vread(i + kRVAhead);
+      if (i < 8) prob(8 + i, l1);
     }
     __builtin_amdgcn_sched_barrier(0);
+    l_run += l0 + l1;
   }
 
   if (over && lane == 0) over_any = 1;
   __syncthreads();
   const bool marked = over_any != 0;
-  const float l = l_run + __shfl_xor(l_run, 32);
+  const float l = sum_xor32(l_run);
   if (!live) return;
   if (marked) {  // recomputed by the exact kernel
     if (hi == 0) lse[(size_t)tok * H + rh] = __uint_as_float(kOverflowMark);

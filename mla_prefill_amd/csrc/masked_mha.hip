@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
       sacc[j] = val;
       mt = fmaxf(mt, val);
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32)) * sc;
+    mt = max_xor32(mt) * sc;
     // lazy rescale: move the reference max only when this tile exceeds it by > 2^8
     const bool need = mt > m_run + kRescaleSlack;
     if (ballot(need) != 0) {
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
       ls += pj;
       bop[j >> 3][j & 7] = (__bf16)pj;
     }
-    l_run += ls + __shfl_xor(ls, 32);
+    l_run += ls;  // this half's keys; the halves are summed at the end
 
     // O^T += V^T P^T: step st covers keys 16 st .. 16 st + 15 with k-slot (hi, i) <->
     // key 16 st + 8 (i / 4) + 4 hi + i % 4, i.e. accumulator registers 8 st .. 8 st + 7
@@ -261,9 +261,10 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
     __builtin_amdgcn_sched_barrier(0);
   }
 
+  const float l_tot = sum_xor32(l_run);  // (before the exit: every lane takes part)
   if (!live) return;
   // o[cb][j] = O^T[col 32 cb + 8 (j / 4) + 4 hi + j % 4][row]
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   uint16_t* orow = out + ((size_t)row * H + h) * kMD + 4 * hi;
 #pragma unroll
   for (int cb = 0; cb < kMD / 32; ++cb)
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
       *reinterpret_cast<bf16x4*>(orow + 32 * cb + 8 * jj) = w;
     }
   if (hi == 0)
-    lse[(size_t)row * H + h] = l_run > 0.f ? (m_run + fast_log2(l_run)) * kLn2 : kNegInf;
+    lse[(size_t)row * H + h] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
 }
 
 hipError_t launch_masked_mha(const uint16_t* q, const uint16_t* k_nope, const uint16_t* v,
