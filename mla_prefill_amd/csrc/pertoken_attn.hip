@@ -489,6 +489,31 @@ __device__ __forceinline__ uint32_t pd_issue(const PdCtx& c, const uint8_t* kvb,
   return v;
 }
 
+// the sources of step j's copies and the validity bits of its 16 keys (key r <-> bit r)
+struct PdSrc {
+  const uint8_t* src0;  // this lane's 16 bytes of row er's first line
+  const uint8_t* src1;  // ... of row 8 + er
+  uint32_t vbits;
+};
+__device__ __forceinline__ PdSrc pd_prep(const PdCtx& c, const uint8_t* kvb, int2 e, int j) {
+  const bool ok0 = kPKeys * j + c.er < c.cols && e.x >= 0 && e.x <= c.pos;
+  const bool ok1 = kPKeys * j + 8 + c.er < c.cols && e.y >= 0 && e.y <= c.pos;
+  PdSrc p;
+  p.src0 = kvb + (size_t)(ok0 ? e.x : c.pos) * kPRowBytes + c.dofs[0];
+  p.src1 = kvb + (size_t)(ok1 ? e.y : c.pos) * kPRowBytes + c.dofs[1];
+  const uint64_t b0 = ballot(ok0), b1 = ballot(ok1);
+  uint32_t v = 0;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) v |= (uint32_t)((b0 >> (8 * r)) & 1u) << r | (uint32_t)((b1 >> (8 * r)) & 1u) << (8 + r);
+  p.vbits = v;
+  return p;
+}
+// the two copies (row groups 0 and 1) of line k
+__device__ __forceinline__ void pd_copy_line(const PdSrc& p, uint32_t tile, int k) {
+  dma16(p.src0 + 128 * k, tile + 1024 * k);
+  dma16(p.src1 + 128 * k, tile + kPGroupBytes + 1024 * k);
+}
+
 __device__ __forceinline__ int2 pd_entries(const PdCtx& c, int j) {
   const int i0 = min(kPKeys * j + c.er, c.cols - 1), i1 = min(kPKeys * j + 8 + c.er, c.cols - 1);
   return int2{(int)pt_sorted[i0], (int)pt_sorted[i1]};
@@ -513,16 +538,30 @@ __device__ __forceinline__ f32x4 pd_qk(const PdCtx& c, const uint8_t* tile, cons
   return acc[0] + acc[1] + acc[2];
 }
 
-__device__ __forceinline__ void pd_pv(const PdCtx& c, const uint8_t* tile, s16x4_t bop, f32x4 (&o)[kDv / 16]) {
+// O^T += V^T P^T over the tile, which is refilled as it goes with the rows of a later step
+// (`next`): line 8 (dims 512..575, read only by S) first, then line k as soon as the MFMA of
+// column block 4 k + 3 has consumed the last read of that line.  Spread over the MFMAs,
+// the copies do not stall the wave on the CU's address path as a burst of 18 would.
+__device__ __forceinline__ void pd_pv(const PdCtx& c, const uint8_t* tile, s16x4_t bop, f32x4 (&o)[kDv / 16],
+                                      const PdSrc& next) {
+  const uint32_t tl = lds_addr(tile);
   auto vread = [&](int cb) -> u16x4 { return lds_read_tr16(tile + c.rofs[cb & 3] + 1024 * (cb >> 2)); };
   u16x4 vw[kPVAhead];
 #pragma unroll
   for (int i = 0; i < kPVAhead; ++i) vw[i] = vread(i);
+  __builtin_amdgcn_sched_barrier(0);
+  pd_copy_line(next, tl, kPLines - 1);
 #pragma unroll
   for (int cb = 0; cb < kDv / 16; ++cb) {
     __builtin_amdgcn_sched_barrier(0);
     o[cb] = mfma16x16x16(__builtin_bit_cast(s16x4_t, vw[cb % kPVAhead]), bop, o[cb]);
     if (cb + kPVAhead < kDv / 16) vw[cb % kPVAhead] = vread(cb + kPVAhead);
+    if ((cb & 3) == 3) {
+      // (after the MFMA: its wait for the operand read orders the copy behind the line's
+      // last read)
+      __builtin_amdgcn_sched_barrier(0);
+      pd_copy_line(next, tl, cb >> 2);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -620,13 +659,11 @@ __global__ __launch_bounds__(64) void pertoken_sorted_kernel(
       m_ref = m_ref == kNegInf ? mh : m_ref;
     }
     over |= ballot(mt > m_ref + kPSlack) != 0;
-    pd_pv(c, tile, pd_probs(c.sc, sv, m_ref, l_run), o);
-    // every operand read of the tile has been consumed; refill it
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    const int2 e = e_next;
+    // the tile takes step j + 2's rows during its PV
+    const PdSrc next = pd_prep(c, kvb, e_next, j + 2);
     e_next = pd_entries(c, j + 3);
-    vbuf = pd_issue(c, kvb, e, j + 2, lds_addr(tile));
+    pd_pv(c, tile, pd_probs(c.sc, sv, m_ref, l_run), o, next);
+    vbuf = next.vbits;
   };
   for (int j = 0; j < nsteps2; j += 2) {
     step(j, tile0, va);
