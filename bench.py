@@ -37,6 +37,7 @@ MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 WORKLOADS = {
     # name: (MQA config, masked-MHA config or None)
     "glm16k": ("c3_glm16k", "c4_masked_nope"),
+    "glm16k_rope": ("c3_glm16k", "c6_masked_rope"),
     "glm16k_uniform": ("c3w_glm16k_uniform", None),
     "long32k": ("c5_long", None),
     "dsv32": ("c2_dsv32", None),
@@ -99,7 +100,7 @@ KERNEL_SYMBOLS = {  # bench kernel name -> (device symbol, sources)
     "build_union": ("dsa::build_union_kernel", ["union_builder.hip", "common.h"]),
     "grouped_attn": ("dsa::rows128_attn_kernel<false>", ["grouped_attn.hip", "common.h"]),
     "pertoken_attn": ("dsa::pertoken_sorted_kernel", ["pertoken_attn.hip", "common.h"]),
-    "masked_mha_routing": ("dsa::masked_mha_kernel", ["masked_mha.hip", "common.h"]),
+    "masked_mha_routing": ("dsa::masked_mha_kernel<256>", ["masked_mha.hip", "common.h"]),
 }
 
 
@@ -203,6 +204,7 @@ def main():
     if mha_case is not None:
         m = mha_case.cfg
         mq, mk, mv = dbf(mha_case.q), dbf(mha_case.k_nope), dbf(mha_case.v)
+        mkp = None if mha_case.k_pe is None else dbf(mha_case.k_pe)
         mtopk = torch.from_numpy(mha_case.topk).cuda()
         ws = torch.empty((m.T, (m.S + 31) // 32), dtype=torch.int32, device="cuda")
         out_m, lse_m = routings.alloc_out(m.T, m.H, m.dv)
@@ -226,7 +228,7 @@ def main():
                                          stream=stream)
         mark(3)
         if mha_case is not None:
-            _lib.dsa_masked_mha_prefill(mq, mk, None, mv, mtopk, m.q_pos_offset, m.scale, ws, out_m,
+            _lib.dsa_masked_mha_prefill(mq, mk, mkp, mv, mtopk, m.q_pos_offset, m.scale, ws, out_m,
                                         lse_m, stream=stream)
             mark(4)
 

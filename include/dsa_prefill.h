@@ -138,11 +138,19 @@ int dsa_sparse_prefill_pertoken(const uint16_t* q, const uint16_t* kv, const int
 /* Masked dense MHA ("[2/N][Attention] Enable masked MHA for sparse MLA
  * prefills", Purpose section; "[Perf][GLM-5.3-Flash] ...", commit messages):
  * token t, head h attends over every key x with x <= q_pos_offset + t and
- * x in sel(t), using per-head keys and values.  Supported geometry:
- * dn = 256, dr = 0, dv = 256 (the NoPE layout): the key is k_nope itself,
- * read in place (no K concat); k_pe is not read (it may be NULL).
+ * x in sel(t), using per-head keys and values.  Supported geometries (the
+ * qk 256 / v 256 layouts the pages' masked-MHA allow-list shares one kernel
+ * for, "[Perf][GLM-5.3-Flash] ..." description and commit messages):
+ *   dn = 256, dr = 0,  dv = 256 (NoPE): the key is k_nope itself, read in
+ *     place; k_pe is not read (it may be NULL);
+ *   dn = 192, dr = 64, dv = 256: the key is k_nope || k_pe, k_pe shared by
+ *     every head (the broadcast the pages' K concat builds); both are read in
+ *     place, no concatenated K is materialized.  k_pe must be non-NULL and
+ *     16-byte aligned.
+ * Anything else returns DSA_ERR_UNSUPPORTED.
  *
- *   q       bf16 [T, H, dn + dr];  k_nope bf16 [S, H, dn];  v bf16 [S, H, dv]
+ *   q       bf16 [T, H, dn + dr];  k_nope bf16 [S, H, dn];  k_pe bf16 [S, dr]
+ *   v       bf16 [S, H, dv]
  *   topk    int32 [T, ld] (cols used)
  *   mask_ws uint32 [T, ceil(S / 32)] caller-owned workspace of
  *           dsa_masked_mha_workspace_bytes(T, S) bytes; overwritten with the

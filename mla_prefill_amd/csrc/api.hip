@@ -108,21 +108,26 @@ int dsa_masked_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint
                            const uint16_t* v, const int32_t* topk, int64_t ld, int T, int S, int H,
                            int dn, int dr, int dv, int cols, int64_t q_pos_offset, float scale,
                            uint32_t* mask_ws, uint16_t* out, float* lse, void* stream) {
-  (void)k_pe;  // dr == 0: the key is k_nope itself
-  if (dn != 256 || dr != 0 || dv != 256 || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
+  // geometries: NoPE (256, 0, 256), the key is k_nope itself; (192, 64, 256), the key is
+  // k_nope || k_pe with k_pe shared by every head
+  const bool nope = dn == 256 && dr == 0 && dv == 256;
+  const bool rope = dn == 192 && dr == 64 && dv == 256;
+  if ((!nope && !rope) || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
   if (H < 1 || T < 0 || S < 1 || cols < 0 || ld < cols || q_pos_offset < 0) return DSA_ERR_SHAPE;
   if (T == 0) return DSA_OK;
-  if (!q || !k_nope || !v || (cols > 0 && !topk) || !mask_ws || !out || !lse) return DSA_ERR_NULL;
+  if (!q || !k_nope || !v || (cols > 0 && !topk) || !mask_ws || !out || !lse || (rope && !k_pe))
+    return DSA_ERR_NULL;
   if (!aligned_to(q, 16) || !aligned_to(k_nope, 16) || !aligned_to(v, 16) ||
       !aligned_to(out, 16) || !aligned_to(lse, 4) || !aligned_to(mask_ws, 4) ||
-      !aligned_to(topk, 4))
+      !aligned_to(topk, 4) || (rope && !aligned_to(k_pe, 16)))
     return DSA_ERR_ALIGN;
   const int words = (S + 31) / 32;
   hipError_t e = dsa::launch_scatter_topk_bits(topk, ld, T, cols, S, q_pos_offset, mask_ws, words,
                                                (hipStream_t)stream);
   if (e != hipSuccess) return DSA_ERR_LAUNCH;
-  return launch_status(dsa::launch_masked_mha(q, k_nope, v, mask_ws, words, T, S, H, q_pos_offset,
-                                              scale, out, lse, (hipStream_t)stream));
+  return launch_status(dsa::launch_masked_mha(q, k_nope, rope ? k_pe : nullptr, dn, v, mask_ws, words, T,
+                                              S, H, q_pos_offset, scale, out, lse,
+                                              (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -53,11 +53,16 @@ constexpr int kMQRegSteps = 12;                       // query k-steps kept in r
 constexpr int kMQLdsSteps = kMD / 16 - kMQRegSteps;   // the rest sit in LDS (lane-private)
 static_assert(kMStageBytes == 1024 * kMWaves * kMCopiesPerWave, "copies split evenly over waves");
 
+// kDN: the k_nope width (256: NoPE layout, K = k_nope; 192: K = k_nope || k_pe with the
+// 64-wide k_pe shared by all heads); the query/key width is 256 either way.
+template <int kDN>
 __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ kpe,
     const uint16_t* __restrict__ v, const uint32_t* __restrict__ bits, int words, int T, int S,
     int H, int64_t q_pos_offset, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse) {
+  constexpr int kDR = kMD - kDN;
+  static_assert(kDN % 64 == 0 && kDR >= 0, "k_nope covers whole 128-byte blocks of the key row");
   __shared__ __align__(16) uint8_t stage[kMStages][kMStageBytes];
   __shared__ __align__(16) uint32_t maskw[kMStages][kMWaves][64];
   __shared__ __align__(16) uint4 qlds[kMWaves][kMQLdsSteps][64];
@@ -114,21 +119,27 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
   const int cgrp = wave & 3;
   const int crow = 8 * cgrp + (lane >> 3);
   const int cchunk = (lane & 7) ^ swz8(lane >> 3) ^ cgrp;
-  const uint16_t* cbase = (wave < 4 ? k : v) + (size_t)h * kMD + 8 * cchunk;
-  const size_t key_stride = (size_t)H * kMD;
+  // (K rows: blocks 0 .. kDN / 64 - 1 from k_nope, the rest from k_pe)
+  const int kdim = wave < 4 ? kDN : kMD;
+  const uint16_t* cbase = (wave < 4 ? k : v) + (size_t)h * kdim + 8 * cchunk;
+  const size_t key_stride = (size_t)H * kdim;
+  // k_pe element e of a row sits at dim kDN + e of the key row
+  const uint16_t* pbase = kDR > 0 ? kpe + 8 * cchunk - kDN : cbase;
   const uint32_t cdst = (wave < 4 ? 0 : kMTileBytes) + cgrp * kMGroupBytes;
 
   auto issue = [&](int t) {
     int key = t * kMKeys + crow;
     key = key < kend ? key : kend - 1;
     const uint16_t* src = cbase + (size_t)key * key_stride;
+    const uint16_t* psrc = kDR > 0 ? pbase + (size_t)key * kDR : src;
     const uint32_t dst = lds_addr(stage[t % kMStages]) + cdst;
     // (the global address carries the block offset: an instruction offset would also
     // move the LDS destination of an LDS-DMA load)
-    dma16(src, dst);
-    dma16(src + 64, dst + 1024);
-    dma16(src + 128, dst + 2048);
-    dma16(src + 192, dst + 3072);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bool from_pe = kDR > 0 && wave < 4 && 64 * c >= kDN;
+      dma16((from_pe ? psrc : src) + 64 * c, dst + 1024 * c);
+    }
     dma4(bits + (size_t)mrow * words + ((t * kMKeys) >> 5), lds_addr(&maskw[t % kMStages][wave][0]));
   };
 
@@ -278,14 +289,18 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
     lse[(size_t)row * H + h] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
 }
 
-hipError_t launch_masked_mha(const uint16_t* q, const uint16_t* k_nope, const uint16_t* v,
-                             const uint32_t* bits, int words, int T, int S, int H,
+hipError_t launch_masked_mha(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_pe, int dn,
+                             const uint16_t* v, const uint32_t* bits, int words, int T, int S, int H,
                              int64_t q_pos_offset, float scale, uint16_t* out, float* lse,
                              hipStream_t stream) {
   const long long blocks = (long long)((T + kMQ - 1) / kMQ) * H;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(masked_mha_kernel, dim3((unsigned)blocks), dim3(kMThreads), 0, stream, q,
-                     k_nope, v, bits, words, T, S, H, q_pos_offset, scale * kLog2e, out, lse);
+  if (dn == 192)
+    hipLaunchKernelGGL(masked_mha_kernel<192>, dim3((unsigned)blocks), dim3(kMThreads), 0, stream, q,
+                       k_nope, k_pe, v, bits, words, T, S, H, q_pos_offset, scale * kLog2e, out, lse);
+  else
+    hipLaunchKernelGGL(masked_mha_kernel<256>, dim3((unsigned)blocks), dim3(kMThreads), 0, stream, q,
+                       k_nope, k_pe, v, bits, words, T, S, H, q_pos_offset, scale * kLog2e, out, lse);
   return hipGetLastError();
 }
 

@@ -195,6 +195,11 @@ CONFIGS = {
     "c4_masked_nope": Config("c4_masked_nope", T=16384, S=16384, H=16, k=2048, cols=2048,
                              G=8, scale=1.0 / 16.0, seed=3, kind="mha", d_qk=256, d_v=256,
                              dn=256, dr=0, dv=256),
+    # Masked dense MHA with a rope part (qk 256 = nope 192 + shared rope 64, v 256), the
+    # other layout the qk 256 / v 256 kernel serves; same shapes and top-k recipe as c4.
+    "c6_masked_rope": Config("c6_masked_rope", T=16384, S=16384, H=16, k=2048, cols=2048,
+                             G=8, scale=1.0 / 16.0, seed=5, kind="mha", d_qk=256, d_v=256,
+                             dn=192, dr=64, dv=256),
     # Long prompt: the last 21504 of 32768 positions are queries; 2176-wide top-k buffer.
     "c5_long": Config("c5_long", T=21504, S=32768, H=16, k=2048, cols=2176, G=8,
                       scale=1.0 / 16.0, seed=4, q_pos_offset=11264),

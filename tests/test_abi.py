@@ -135,7 +135,11 @@ def mha_call(lib, q=P, kn=P, kp=None, v=P, tk=P, ld=32, T=64, S=64, H=16, dn=256
 
 
 def test_masked_mha_validation(lib):
-    assert mha_call(lib, dn=192, dr=64) == UNSUP      # rope > 0: not in the first build
+    # (192, 64, 256) needs k_pe; (256, 64, 256) and other head dims are not supported
+    assert mha_call(lib, dn=192, dr=64) == NULL
+    assert mha_call(lib, dn=192, dr=64, kp=P + 2) == ALIGN
+    assert mha_call(lib, dn=192, dr=64, kp=P, T=0) == OK
+    assert mha_call(lib, dn=256, dr=64) == UNSUP and mha_call(lib, dn=192, dr=64, dv=128) == UNSUP
     assert mha_call(lib, dn=128) == UNSUP and mha_call(lib, dv=128) == UNSUP
     assert mha_call(lib, H=0) == SHAPE and mha_call(lib, ld=8) == SHAPE
     assert mha_call(lib, T=0) == OK

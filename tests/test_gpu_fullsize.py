@@ -80,19 +80,21 @@ def test_grouped_equals_pertoken_everywhere(full):
     assert (lg[fin] - lp[fin]).abs().max().item() <= 2e-3
 
 
-def test_masked_mha_full():
+@pytest.mark.parametrize("name", ["c4_masked_nope", "c6_masked_rope"])
+def test_masked_mha_full(name):
     from mla_prefill_amd import routings
-    c = make_case(CONFIGS["c4_masked_nope"])
+    c = make_case(CONFIGS[name])
     cfg = c.cfg
-    out, lse, ws = routings.masked_mha(dev_bf16(c.q), dev_bf16(c.k_nope), None, dev_bf16(c.v),
+    kp = None if c.k_pe is None else dev_bf16(c.k_pe)
+    out, lse, ws = routings.masked_mha(dev_bf16(c.q), dev_bf16(c.k_nope), kp, dev_bf16(c.v),
                                        dev_i32(c.topk), cfg.q_pos_offset, cfg.scale)
     torch.cuda.synchronize()
     toks = sample_tokens(cfg.T, cfg.G, n_random=16, seed=1)
-    print(f"[c4] dense-mask oracle on {len(toks)} sampled tokens", flush=True)
-    ref_out, ref_lse = oracle.masked_mha(c.q, c.k_nope, None, c.v, c.topk, cfg.S, cfg.q_pos_offset,
+    print(f"[{name}] dense-mask oracle on {len(toks)} sampled tokens", flush=True)
+    ref_out, ref_lse = oracle.masked_mha(c.q, c.k_nope, c.k_pe, c.v, c.topk, cfg.S, cfg.q_pos_offset,
                                          cfg.scale, tokens=toks)
     idx = torch.tensor(toks, device="cuda")
-    check_attention(out[idx], lse[idx], ref_out, ref_lse, "c4 masked MHA")
+    check_attention(out[idx], lse[idx], ref_out, ref_lse, f"{name} masked MHA")
     # bit-packed selection rows of the sampled tokens
     wsn = ws.cpu().numpy().view(np.uint32)
     for t in toks[:8]:

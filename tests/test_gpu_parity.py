@@ -202,26 +202,32 @@ def test_large_score_jump_and_negative_scale(R):
 # ---------------------------------------------------------------------------
 
 MHA_CASES = [
-    # (label, seed, T, S, H, k, cols, P0, mode)
-    ("causal_ragged", 20, 150, 150, 2, 40, 45, 0, "locality"),
-    ("chunked_ctx", 21, 100, 230, 3, 64, 70, 130, "uniform"),
-    ("all_selected", 22, 70, 70, 1, 70, 80, 0, "uniform"),
+    # (label, seed, T, S, H, k, cols, P0, mode, dn, dr)
+    ("causal_ragged", 20, 150, 150, 2, 40, 45, 0, "locality", 256, 0),
+    ("chunked_ctx", 21, 100, 230, 3, 64, 70, 130, "uniform", 256, 0),
+    ("all_selected", 22, 70, 70, 1, 70, 80, 0, "uniform", 256, 0),
+    # K = k_nope (192) || k_pe (64, shared by the heads)
+    ("rope_causal_ragged", 24, 150, 150, 2, 40, 45, 0, "locality", 192, 64),
+    ("rope_chunked_ctx", 25, 100, 230, 3, 64, 70, 130, "uniform", 192, 64),
+    ("rope_all_selected", 26, 300, 300, 2, 300, 300, 0, "uniform", 192, 64),
 ]
 
 
 @pytest.mark.parametrize("case", MHA_CASES, ids=[c[0] for c in MHA_CASES])
 def test_masked_mha_parity(R, case):
-    label, seed, T, S, H, k, cols, P0, mode = case
+    label, seed, T, S, H, k, cols, P0, mode, dn, dr = case
     rng = np.random.default_rng(seed)
-    q = normal_bf16(rng, (T, H, 256))
-    kn = normal_bf16(rng, (S, H, 256))
+    q = normal_bf16(rng, (T, H, dn + dr))
+    kn = normal_bf16(rng, (S, H, dn))
+    kp = normal_bf16(rng, (S, dr)) if dr else None
     v = normal_bf16(rng, (S, H, 256))
     topk = (topk_uniform(rng, T, S, k, cols, P0) if mode == "uniform"
             else topk_locality(rng, T, S, k, cols, 8, P0))
     topk = shuffle_rows(topk, seed)
     scale = 1.0 / 16.0
-    out, lse, ws = R.masked_mha(dev_bf16(q), dev_bf16(kn), None, dev_bf16(v), dev_i32(topk), P0, scale)
-    ref_out, ref_lse = oracle.masked_mha(q, kn, None, v, topk, S, P0, scale)
+    out, lse, ws = R.masked_mha(dev_bf16(q), dev_bf16(kn), None if kp is None else dev_bf16(kp),
+                                dev_bf16(v), dev_i32(topk), P0, scale)
+    ref_out, ref_lse = oracle.masked_mha(q, kn, kp, v, topk, S, P0, scale)
     check_attention(out, lse, ref_out, ref_lse, label)
     # the workspace holds exactly the bit-packed selection
     words = (S + 31) // 32
