@@ -7,11 +7,18 @@ and the ``cpu_baseline`` leg of ``bench.py``; never by the library.
 from .dsa_oracle import (  # noqa: F401
     UNION_BLOCK,
     bf16_to_f64,
+    convert_req_index_to_global,
     group_union_mask,
+    group_union_mask_varlen,
     grouped_sparse_mqa,
+    grouped_sparse_mqa_varlen,
     masked_mha,
     pertoken_sparse_mqa,
+    pertoken_sparse_mqa_varlen,
+    physical_row,
+    request_of_tokens,
     selected_positions,
     softmax_attention,
     union_pad,
+    varlen_groups,
 )

@@ -39,6 +39,15 @@ Readings where the pages are silent (each also listed in the design notes):
 * Union list: strictly ascending, -1 padded to union_pad = ceil(G*cols/64)*64.
 * head_group_mask: uint8 [NG, union_pad]; bit i of slot j is set iff token
   gG + i selects union position j; padding slots are 0.
+* Batches of requests over a paged KV cache ([GROUPED] "How": groups are
+  consecutive tokens of one request, and the union's request-local positions
+  become physical KV rows through the request's index conversion before the
+  attention): request r owns query tokens cu[r] .. cu[r+1] - 1; its token i sits
+  at position q_pos_start[r] + i; it may select positions 0 <= x < kv_len[r]
+  (and x <= its position); position x lives in physical row
+  block_table[r][x // page_size] * page_size + x % page_size of the cache.
+  Positions whose row falls outside the cache are ignored.  Groups are numbered
+  request by request (ceil(n_r / G) per request) and never cross a request.
 
 Pins: see ``tests/test_oracle_pins.py`` (library routines, closed forms,
 brute-force set arithmetic, invariants).  No function here is parity-unpinned.
@@ -229,4 +238,145 @@ def masked_mha(q: np.ndarray, k_nope: np.ndarray, k_pe: Optional[np.ndarray],
             total = e.sum()
             out[n, h] = (e @ vv[:, h, :]) / total
             lse[n, h] = m + math.log(total)
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# batches of requests over a paged KV cache  ([GROUPED] "How": groups of
+# consecutive tokens of a request; union positions mapped to physical rows)
+# ---------------------------------------------------------------------------
+
+def request_of_tokens(cu_seqlens: np.ndarray) -> np.ndarray:
+    """Request index of every query token (cu_seqlens [R + 1], ascending)."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    owner = np.zeros(int(cu[-1]), dtype=np.int64)
+    for r in range(cu.size - 1):
+        owner[cu[r]:cu[r + 1]] = r
+    return owner
+
+
+def physical_row(block_table: np.ndarray, r: int, x: int, page_size: int) -> int:
+    """Cache row of request r's position x."""
+    return int(block_table[r, x // page_size]) * page_size + x % page_size
+
+
+def token_position(cu_seqlens, q_pos_start, r: int, t: int) -> int:
+    return int(q_pos_start[r]) + (t - int(cu_seqlens[r]))
+
+
+def selected_local_positions(topk_row, kv_len: int, pos: int, block_table, r: int,
+                             page_size: int, num_slots: int) -> np.ndarray:
+    """Request-local positions a token selects whose physical row is in the cache."""
+    sel = selected_positions(topk_row, kv_len, pos)
+    keep = [x for x in sel if 0 <= physical_row(block_table, r, int(x), page_size) < num_slots]
+    return np.asarray(keep, dtype=np.int64)
+
+
+def convert_req_index_to_global(topk, cu_seqlens, kv_lens, q_pos_start, block_table,
+                                page_size: int, num_slots: int) -> np.ndarray:
+    """Each top-k entry as a physical cache row, -1 where it selects nothing.
+
+    topk int32 [T, cols] of request-local positions; returns int32 [T, cols].
+    """
+    T, cols = topk.shape
+    owner = request_of_tokens(cu_seqlens)
+    out = np.full((T, cols), -1, dtype=np.int32)
+    for t in range(T):
+        r = int(owner[t])
+        pos = token_position(cu_seqlens, q_pos_start, r, t)
+        for c in range(cols):
+            x = int(topk[t, c])
+            if 0 <= x < int(kv_lens[r]) and x <= pos:
+                row = physical_row(block_table, r, x, page_size)
+                if 0 <= row < num_slots:
+                    out[t, c] = row
+    return out
+
+
+def pertoken_sparse_mqa_varlen(q, kv_cache, topk, cu_seqlens, kv_lens, q_pos_start, block_table,
+                               page_size: int, scale: float, d_v: int = 512,
+                               tokens: Optional[Iterable[int]] = None):
+    """Per-token sparse MQA of a batch of requests over a paged cache [num_slots, d_qk]."""
+    T, H, _ = q.shape
+    scale = _as_scale(scale)
+    num_slots = kv_cache.shape[0]
+    owner = request_of_tokens(cu_seqlens)
+    toks = _tokens(T, tokens)
+    out = np.zeros((toks.size, H, d_v))
+    lse = np.full((toks.size, H), -np.inf)
+    for n, t in enumerate(toks):
+        r = int(owner[t])
+        pos = token_position(cu_seqlens, q_pos_start, r, int(t))
+        xs = selected_local_positions(topk[t], int(kv_lens[r]), pos, block_table, r, page_size,
+                                      num_slots)
+        rows = [physical_row(block_table, r, int(x), page_size) for x in xs]
+        keys = bf16_to_f64(kv_cache[np.asarray(rows, dtype=np.int64)]) if rows else np.zeros((0, q.shape[2]))
+        out[n], lse[n] = softmax_attention(bf16_to_f64(q[t]), keys, keys[:, :d_v], scale)
+    return out, lse
+
+
+def varlen_groups(cu_seqlens, G: int):
+    """(first token, token count) of every group, request by request."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    groups = []
+    for r in range(cu.size - 1):
+        for t0 in range(int(cu[r]), int(cu[r + 1]), G):
+            groups.append((t0, min(G, int(cu[r + 1]) - t0)))
+    return groups
+
+
+def group_union_mask_varlen(topk, cu_seqlens, kv_lens, q_pos_start, block_table, page_size: int,
+                            num_slots: int, G: int, max_groups: int, pad: Optional[int] = None):
+    """Union (as physical rows, ascending in request-local position) and membership mask of
+    every group of a batch.
+
+    Returns group_info int32 [max_groups, 2] (first token, token count; 0, 0 past the last
+    group), union_idx int32 [max_groups, pad], union_len int32 [max_groups],
+    mask uint8 [max_groups, pad].
+    """
+    T, cols = topk.shape
+    pad = union_pad(G, cols) if pad is None else pad
+    owner = request_of_tokens(cu_seqlens)
+    groups = varlen_groups(cu_seqlens, G)
+    if len(groups) > max_groups:
+        raise ValueError("max_groups is smaller than the batch's group count")
+    info = np.zeros((max_groups, 2), dtype=np.int32)
+    union_idx = np.full((max_groups, pad), -1, dtype=np.int32)
+    union_len = np.zeros(max_groups, dtype=np.int32)
+    mask = np.zeros((max_groups, pad), dtype=np.uint8)
+    for g, (t0, n) in enumerate(groups):
+        info[g] = (t0, n)
+        r = int(owner[t0])
+        members = [selected_local_positions(topk[t], int(kv_lens[r]),
+                                            token_position(cu_seqlens, q_pos_start, r, t),
+                                            block_table, r, page_size, num_slots)
+                   for t in range(t0, t0 + n)]
+        U = np.unique(np.concatenate(members)) if members else np.zeros(0, np.int64)
+        k = U.size
+        union_idx[g, :k] = [physical_row(block_table, r, int(x), page_size) for x in U]
+        union_len[g] = k
+        for i, sel in enumerate(members):
+            mask[g, :k] |= (np.isin(U, sel).astype(np.uint8) << np.uint8(i))
+    return info, union_idx, union_len, mask
+
+
+def grouped_sparse_mqa_varlen(q, kv_cache, group_info, union_idx, union_len, mask, scale: float,
+                              d_v: int = 512, groups: Optional[Iterable[int]] = None):
+    """Rows of group g (its tokens x H heads) over the union rows whose mask bit is set."""
+    T, H, _ = q.shape
+    scale = _as_scale(scale)
+    num_slots = kv_cache.shape[0]
+    out = np.zeros((T, H, d_v))
+    lse = np.full((T, H), -np.inf)
+    gs = range(group_info.shape[0]) if groups is None else groups
+    for g in gs:
+        t0, n = int(group_info[g, 0]), int(group_info[g, 1])
+        k = int(union_len[g])
+        rows = union_idx[g, :k].astype(np.int64)
+        bits = mask[g, :k]
+        if np.any((rows < 0) | (rows >= num_slots)):
+            raise ValueError("union list holds a row outside the cache")
+        for i in range(n):
+            keys = bf16_to_f64(kv_cache[rows[((bits >> i) & 1) == 1]])
+            out[t0 + i], lse[t0 + i] = softmax_attention(bf16_to_f64(q[t0 + i]), keys, keys[:, :d_v], scale)
     return out, lse

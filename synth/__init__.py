@@ -10,9 +10,11 @@ from .gen import (  # noqa: F401
     CONFIGS,
     Case,
     Config,
+    VarlenCase,
     bf16_bits_from_f32,
     bf16_bits_to_f32,
     make_case,
+    make_varlen_case,
     topk_locality,
     topk_uniform,
 )

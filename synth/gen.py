@@ -246,3 +246,77 @@ def make_case(cfg: Config, values: bool = True) -> Case:
     else:
         raise ValueError(cfg.kind)
     return case
+
+
+# ---------------------------------------------------------------------------
+# batches of requests over a paged KV cache
+# ---------------------------------------------------------------------------
+
+@dataclass
+class VarlenCase:
+    q: np.ndarray             # uint16 bf16 bits [T, H, d_qk], requests' tokens concatenated
+    kv_cache: np.ndarray      # uint16 bf16 bits [num_slots, d_qk] (pages of page_size rows)
+    topk: np.ndarray          # int32 [T, cols], request-local positions, -1 padded
+    cu_seqlens: np.ndarray    # int32 [R + 1]
+    kv_lens: np.ndarray       # int32 [R]
+    q_pos_start: np.ndarray   # int32 [R]: position of each request's first query token
+    block_table: np.ndarray   # int32 [R, max_pages]: physical page of each request page (-1 unused)
+    page_size: int
+    scale: float
+    G: int
+
+    @property
+    def num_slots(self) -> int:
+        return self.kv_cache.shape[0]
+
+    @property
+    def T(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    def max_groups(self) -> int:
+        return int(sum(-(-int(n) // self.G) for n in np.diff(self.cu_seqlens)))
+
+
+def make_varlen_case(seed: int, q_lens, ctx_lens, H: int = 16, k: int = 2048, cols: int = 0,
+                     page_size: int = 64, G: int = 8, mode: str = "locality", spare_pages: int = 3,
+                     d_qk: int = 576, scale: float = 1.0 / 16.0, values: bool = True) -> VarlenCase:
+    """A seeded batch: request r has q_lens[r] query tokens after ctx_lens[r] positions of
+    context (kv_len = ctx + q_len, first query position = ctx).  The cache holds every
+    request's pages plus ``spare_pages`` unused ones, in a random physical order; each
+    request's top-k rows come from the single-sequence generators over its own positions."""
+    q_lens = [int(n) for n in q_lens]
+    ctx_lens = [int(c) for c in ctx_lens]
+    R = len(q_lens)
+    cols = cols or k
+    ss = np.random.SeedSequence(seed).spawn(4)
+    rq, rkv, rtk, rpg = (np.random.Generator(np.random.PCG64(s)) for s in ss)
+    cu = np.zeros(R + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(q_lens)
+    kv_lens = np.asarray([c + n for c, n in zip(ctx_lens, q_lens)], dtype=np.int32)
+    q_pos_start = np.asarray(ctx_lens, dtype=np.int32)
+    pages = [-(-int(L) // page_size) for L in kv_lens]
+    total_pages = sum(pages) + spare_pages
+    perm = rpg.permutation(total_pages).astype(np.int32)
+    block_table = np.full((R, max(1, max(pages) if pages else 1)), -1, dtype=np.int32)
+    at = 0
+    for r in range(R):
+        block_table[r, :pages[r]] = perm[at:at + pages[r]]
+        at += pages[r]
+    parts = []
+    for r in range(R):
+        n, L, c = q_lens[r], int(kv_lens[r]), ctx_lens[r]
+        if mode == "uniform":
+            parts.append(topk_uniform(rtk, n, L, k, cols, c))
+        else:
+            parts.append(topk_locality(rtk, n, L, k, cols, G, c))
+    topk = np.concatenate(parts, axis=0) if parts else np.zeros((0, cols), np.int32)
+    T = int(cu[-1])
+    case = VarlenCase(q=None, kv_cache=None, topk=topk, cu_seqlens=cu, kv_lens=kv_lens,
+                      q_pos_start=q_pos_start, block_table=block_table, page_size=page_size,
+                      scale=scale, G=G)
+    if values:
+        case.q = normal_bf16(rq, (T, H, d_qk))
+        case.kv_cache = normal_bf16(rkv, (total_pages * page_size, d_qk))
+    else:
+        case.kv_cache = np.zeros((total_pages * page_size, 0), np.uint16)
+    return case

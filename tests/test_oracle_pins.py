@@ -327,3 +327,140 @@ def test_masked_mha_equals_pertoken_when_heads_share_kv():
     op, lp = oracle.pertoken_sparse_mqa(q, X, topk, S, P0, 0.3, d_v=d)
     np.testing.assert_allclose(om, op, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(lm, lp, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# batches of requests over a paged KV cache
+# ---------------------------------------------------------------------------
+
+def _varlen_args(c):
+    return (c.cu_seqlens, c.kv_lens, c.q_pos_start, c.block_table, c.page_size)
+
+
+def test_varlen_single_request_identity_pages_reduces_to_plain():
+    """One request whose page table is the identity: the paged functions equal the
+    single-sequence ones exactly (same rows in the same order)."""
+    rng = np.random.default_rng(40)
+    T, S, P0, H, d, page, G = 21, 44, 23, 2, 24, 4, 8
+    q = normal_bf16(rng, (T, H, d))
+    kv = normal_bf16(rng, (S, d))
+    topk = shuffle_rows(widen(topk_locality(rng, T, S, 9, 9, G, P0), 12), 40)
+    cu, kvl, p0 = np.array([0, T]), np.array([S]), np.array([P0])
+    bt = np.arange(S // page, dtype=np.int32)[None]
+    out_v, lse_v = oracle.pertoken_sparse_mqa_varlen(q, kv, topk, cu, kvl, p0, bt, page, 0.3, d_v=16)
+    out, lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, P0, 0.3, d_v=16)
+    np.testing.assert_array_equal(out_v, out)
+    np.testing.assert_array_equal(lse_v, lse)
+    ng = -(-T // G)
+    info, ui, ul, mk = oracle.group_union_mask_varlen(topk, cu, kvl, p0, bt, page, S, G, ng + 2)
+    ui0, ul0, mk0 = oracle.group_union_mask(topk, S, P0, G)
+    np.testing.assert_array_equal(ui[:ng], ui0)
+    np.testing.assert_array_equal(ul[:ng], ul0)
+    np.testing.assert_array_equal(mk[:ng], mk0)
+    assert (ul[ng:] == 0).all() and (ui[ng:] == -1).all() and (info[ng:] == 0).all()
+    np.testing.assert_array_equal(info[:ng], [(g * G, min(G, T - g * G)) for g in range(ng)])
+
+
+def _permute_pages(c, perm):
+    """The same batch with physical page p moved to perm[p]."""
+    ps = c.page_size
+    cache = np.empty_like(c.kv_cache)
+    for p in range(c.kv_cache.shape[0] // ps):
+        cache[perm[p] * ps:(perm[p] + 1) * ps] = c.kv_cache[p * ps:(p + 1) * ps]
+    bt = np.where(c.block_table >= 0, perm[np.maximum(c.block_table, 0)], -1).astype(np.int32)
+    return cache, bt
+
+
+def test_varlen_page_placement_does_not_matter():
+    from synth import make_varlen_case
+    c = make_varlen_case(41, [7, 19, 1, 12], [0, 30, 5, 17], H=2, k=10, cols=13, page_size=4,
+                         d_qk=24)
+    perm = np.random.default_rng(41).permutation(c.kv_cache.shape[0] // c.page_size)
+    cache2, bt2 = _permute_pages(c, perm)
+    a = oracle.pertoken_sparse_mqa_varlen(c.q, c.kv_cache, c.topk, *_varlen_args(c), 0.25, d_v=16)
+    b = oracle.pertoken_sparse_mqa_varlen(c.q, cache2, c.topk, c.cu_seqlens, c.kv_lens,
+                                          c.q_pos_start, bt2, c.page_size, 0.25, d_v=16)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+    mg = c.max_groups()
+    u1 = oracle.group_union_mask_varlen(c.topk, *_varlen_args(c), c.num_slots, c.G, mg)
+    u2 = oracle.group_union_mask_varlen(c.topk, c.cu_seqlens, c.kv_lens, c.q_pos_start, bt2,
+                                        c.page_size, c.num_slots, c.G, mg)
+    ps = c.page_size
+    moved = np.where(u1[1] >= 0, perm[np.maximum(u1[1], 0) // ps] * ps + np.maximum(u1[1], 0) % ps, -1)
+    np.testing.assert_array_equal(u2[1], moved)
+    for i in (0, 2, 3):
+        np.testing.assert_array_equal(u1[i], u2[i])
+
+
+def test_varlen_batch_equals_each_request_alone():
+    from synth import make_varlen_case
+    c = make_varlen_case(42, [9, 3, 14], [11, 0, 6], H=2, k=8, cols=8, page_size=8, d_qk=24)
+    out, lse = oracle.pertoken_sparse_mqa_varlen(c.q, c.kv_cache, c.topk, *_varlen_args(c), 0.2, d_v=16)
+    for r in range(c.cu_seqlens.size - 1):
+        a, b = int(c.cu_seqlens[r]), int(c.cu_seqlens[r + 1])
+        o1, l1 = oracle.pertoken_sparse_mqa_varlen(
+            c.q[a:b], c.kv_cache, c.topk[a:b], np.array([0, b - a]), c.kv_lens[r:r + 1],
+            c.q_pos_start[r:r + 1], c.block_table[r:r + 1], c.page_size, 0.2, d_v=16)
+        np.testing.assert_array_equal(o1, out[a:b])
+        np.testing.assert_array_equal(l1, lse[a:b])
+
+
+@pytest.mark.parametrize("mode", ["locality", "uniform"])
+def test_varlen_grouped_equals_pertoken(mode):
+    from synth import make_varlen_case
+    c = make_varlen_case(43, [13, 1, 8, 17], [20, 3, 0, 9], H=4, k=12, cols=15, page_size=4,
+                         G=4, mode=mode, d_qk=24)
+    mg = c.max_groups() + 3
+    info, ui, ul, mk = oracle.group_union_mask_varlen(c.topk, *_varlen_args(c), c.num_slots, c.G, mg)
+    og, lg = oracle.grouped_sparse_mqa_varlen(c.q, c.kv_cache, info, ui, ul, mk, 0.3, d_v=16)
+    op, lp = oracle.pertoken_sparse_mqa_varlen(c.q, c.kv_cache, c.topk, *_varlen_args(c), 0.3, d_v=16)
+    np.testing.assert_allclose(og, op, rtol=0, atol=1e-12)
+    fin = np.isfinite(lp)
+    np.testing.assert_array_equal(np.isfinite(lg), fin)
+    np.testing.assert_allclose(lg[fin], lp[fin], rtol=0, atol=1e-12)
+
+
+def test_varlen_convert_then_single_sequence_equals_varlen():
+    """Physical-row top-k (the index conversion) fed to the single-sequence per-token
+    function over the whole cache, with causality already applied, equals the paged one."""
+    from synth import make_varlen_case
+    c = make_varlen_case(44, [6, 11, 4], [9, 0, 30], H=2, k=7, cols=9, page_size=4, d_qk=24)
+    g = oracle.convert_req_index_to_global(c.topk, *_varlen_args(c), c.num_slots)
+    n = c.num_slots
+    a = oracle.pertoken_sparse_mqa(c.q, c.kv_cache, g, n, n - 1, 0.4, d_v=16)
+    b = oracle.pertoken_sparse_mqa_varlen(c.q, c.kv_cache, c.topk, *_varlen_args(c), 0.4, d_v=16)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+    # entries it drops: -1, beyond the request's KV, beyond the token's position
+    owner = oracle.request_of_tokens(c.cu_seqlens)
+    for t in range(g.shape[0]):
+        r = owner[t]
+        pos = c.q_pos_start[r] + t - c.cu_seqlens[r]
+        for col in range(g.shape[1]):
+            x = c.topk[t, col]
+            assert (g[t, col] >= 0) == (0 <= x < c.kv_lens[r] and x <= pos)
+
+
+def test_varlen_groups_stay_inside_requests():
+    cu = np.array([0, 3, 3, 20, 21, 37])
+    owner = oracle.request_of_tokens(cu)
+    groups = oracle.varlen_groups(cu, 8)
+    assert sum(n for _, n in groups) == 37
+    assert len(groups) == sum(-(-int(n) // 8) for n in np.diff(cu))
+    for t0, n in groups:
+        assert 1 <= n <= 8 and owner[t0] == owner[t0 + n - 1]
+        assert t0 == cu[owner[t0]] or (t0 - cu[owner[t0]]) % 8 == 0
+
+
+def test_varlen_rows_outside_the_cache_are_ignored():
+    from synth import make_varlen_case
+    c = make_varlen_case(45, [10], [12], H=2, k=9, cols=9, page_size=4, d_qk=24, spare_pages=0)
+    bt = c.block_table.copy()
+    bt[0, 1] = c.num_slots // c.page_size + 5     # page 1 of the request points past the cache
+    out, lse = oracle.pertoken_sparse_mqa_varlen(c.q, c.kv_cache, c.topk, c.cu_seqlens, c.kv_lens,
+                                                 c.q_pos_start, bt, c.page_size, 0.5, d_v=16)
+    topk2 = np.where((c.topk >= 4) & (c.topk < 8), -1, c.topk)  # the same positions dropped
+    o2, l2 = oracle.pertoken_sparse_mqa_varlen(c.q, c.kv_cache, topk2, *_varlen_args(c), 0.5, d_v=16)
+    np.testing.assert_array_equal(out, o2)
+    np.testing.assert_array_equal(lse, l2)
