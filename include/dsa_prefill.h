@@ -162,6 +162,81 @@ int dsa_masked_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint
                            int dn, int dr, int dv, int cols, int64_t q_pos_offset, float scale,
                            uint32_t* mask_ws, uint16_t* out, float* lse, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Batches of requests over a paged KV cache ("[Perf][DSA] Grouped sparse
+ * prefill ...", "How" section: groups are consecutive tokens of one request,
+ * and the union's request-local positions become physical rows through the
+ * request's index conversion before the attention).
+ *
+ * A batch of R >= 1 requests is described by device arrays:
+ *   cu_seqlens_q int32 [R + 1]  query tokens of request r are cu[r] .. cu[r+1]-1
+ *                               (ascending, cu[0] = 0, cu[R] = T)
+ *   kv_lens      int32 [R]      request r has positions 0 .. kv_lens[r] - 1
+ *   q_pos_start  int32 [R]      position of request r's first query token
+ *   block_table  int32 [R, bt_ld]  physical page of each request page: position
+ *                               x lives in cache row block_table[r][x / page_size]
+ *                               * page_size + x % page_size
+ *   page_size >= 1; the cache holds num_slots >= 1 rows of 576 bf16.
+ * Top-k rows hold request-local positions.  Token t of request r (local index
+ * i = t - cu[r], position p = q_pos_start[r] + i) selects x iff 0 <= x <
+ * kv_lens[r], x <= p and x maps to a row inside the cache (a page past bt_ld or
+ * a negative page id maps nowhere).  These contents are data, never errors: any
+ * values are memory-safe.  The host checks only sizes, pointers and alignment.
+ * ------------------------------------------------------------------------- */
+
+/* Upper bound on a batch's group count, min(T, ceil(T / G) + R): each request
+ * adds at most one partial group.  DSA_ERR_SHAPE for T < 0, R < 1 or G outside
+ * 1..8. */
+int dsa_varlen_group_bound(int T, int R, int G);
+
+/* The index conversion: topk_global int32 [T, cols] (contiguous) receives, for
+ * each top-k entry, the cache row it selects, or -1 where it selects nothing. */
+int dsa_convert_req_index_to_global(const int32_t* topk, int64_t ld, int T, int cols, int R,
+                                    const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                                    const int32_t* q_pos_start, const int32_t* block_table, int64_t bt_ld,
+                                    int page_size, int num_slots, int32_t* topk_global, void* stream);
+
+/* Union list and membership mask of every group of a batch.  Groups are
+ * numbered request by request, ceil(n_r / G) per request, each covering up to G
+ * consecutive tokens of one request; max_groups >= the batch's group count
+ * (dsa_varlen_group_bound is one such value), later groups are empty.
+ *   group_info      int32 [max_groups, 2] (8-byte aligned): first token and token
+ *                   count of each group (0, 0 for empty groups)
+ *   union_idx       int32 [max_groups, union_pad]: the union of the members'
+ *                   selections in ascending request-local position, each written
+ *                   as its cache row, then -1
+ *   union_len, head_group_mask: as for dsa_build_group_union (bit i <-> the
+ *                   group's i-th token)
+ * All outputs are fully overwritten.  Bit-exact and deterministic. */
+int dsa_build_group_union_varlen(const int32_t* topk, int64_t ld, int T, int cols, int R,
+                                 const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                                 const int32_t* q_pos_start, const int32_t* block_table, int64_t bt_ld,
+                                 int page_size, int num_slots, int G, int max_groups, int union_pad,
+                                 int32_t* group_info, int32_t* union_idx, int32_t* union_len,
+                                 uint8_t* head_group_mask, void* stream);
+
+/* Grouped sparse attention of a batch: as dsa_sparse_prefill_grouped, with
+ * group g's tokens taken from group_info (as written by
+ * dsa_build_group_union_varlen; entries are clamped into [0, T)) and the keys
+ * read from the cache rows union_idx names (rows outside [0, num_slots) are
+ * skipped).  Tokens covered by no group are not written. */
+int dsa_sparse_prefill_grouped_varlen(const uint16_t* q, const uint16_t* kv_cache, int num_slots,
+                                      const int32_t* group_info, int max_groups, const int32_t* union_idx,
+                                      const int32_t* union_len, const uint8_t* head_group_mask, int T,
+                                      int H, int union_pad, int d_qk, int d_v, float scale,
+                                      uint16_t* out, float* lse, void* stream);
+
+/* Per-token sparse MQA of a batch: the index conversion into the caller's
+ * workspace topk_ws int32 [T, cols], then dsa_sparse_prefill_pertoken over the
+ * whole cache with every row in every token's causal range.  Two kernels are
+ * enqueued. */
+int dsa_sparse_prefill_pertoken_varlen(const uint16_t* q, const uint16_t* kv_cache, int num_slots,
+                                       const int32_t* topk, int64_t ld, int T, int H, int cols, int R,
+                                       const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                                       const int32_t* q_pos_start, const int32_t* block_table,
+                                       int64_t bt_ld, int page_size, int d_qk, int d_v, float scale,
+                                       int32_t* topk_ws, uint16_t* out, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

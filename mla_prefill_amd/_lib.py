@@ -37,6 +37,16 @@ _SIGNATURES = {
                                      _vp, _vp, _vp], _i32),
     "dsa_masked_mha_prefill": ([_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                 _i64, _f32, _vp, _vp, _vp, _vp], _i32),
+    "dsa_varlen_group_bound": ([_i32, _i32, _i32], _i32),
+    "dsa_convert_req_index_to_global": ([_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
+                                         _vp, _vp], _i32),
+    "dsa_build_group_union_varlen": ([_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
+                                      _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], _i32),
+    "dsa_sparse_prefill_grouped_varlen": ([_vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32,
+                                           _i32, _i32, _f32, _vp, _vp, _vp], _i32),
+    "dsa_sparse_prefill_pertoken_varlen": ([_vp, _vp, _i32, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp,
+                                            _vp, _vp, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp],
+                                           _i32),
 }
 for _name, (_args, _ret) in _SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -149,3 +159,67 @@ def dsa_masked_mha_prefill(q, k_nope, k_pe, v, topk, q_pos_offset, scale, mask_w
         _ptr(_bits(q)), _ptr(_bits(k_nope)), _ptr(_bits(k_pe)), _ptr(_bits(v)), _ptr(topk),
         _topk_ld(topk), T, S, H, dn, dr, dv, cols, q_pos_offset, scale, _ptr(mask_ws),
         _ptr(_bits(out)), _ptr(lse), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# batches of requests over a paged KV cache.  A batch is passed as the tuple
+# (cu_seqlens_q, kv_lens, q_pos_start, block_table, page_size) of int32 device
+# tensors (block_table [R, bt_ld]) and the page size.
+# ---------------------------------------------------------------------------
+
+def _batch(batch):
+    cu, kv_lens, q_pos_start, block_table, page_size = batch
+    for t in (cu, kv_lens, q_pos_start, block_table):
+        if t.dtype != torch.int32:
+            raise TypeError("batch tensors must be int32")
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be [R, bt_ld] with unit column stride")
+    R = kv_lens.shape[0]
+    bt_ld = block_table.stride(0) if block_table.shape[0] > 1 else block_table.shape[1]
+    return R, _ptr(cu), _ptr(kv_lens), _ptr(q_pos_start), _ptr(block_table), bt_ld, page_size
+
+
+def dsa_varlen_group_bound(T: int, R: int, G: int) -> int:
+    v = lib.dsa_varlen_group_bound(T, R, G)
+    _check("dsa_varlen_group_bound", v if v < 0 else 0)
+    return v
+
+
+def dsa_convert_req_index_to_global(topk, batch, num_slots, topk_global, cols=None, stream=None):
+    T = topk.shape[0]
+    cols = topk.shape[1] if cols is None else cols
+    R, cu, kl, qs, bt, bt_ld, ps = _batch(batch)
+    _check("dsa_convert_req_index_to_global", lib.dsa_convert_req_index_to_global(
+        _ptr(topk), _topk_ld(topk), T, cols, R, cu, kl, qs, bt, bt_ld, ps, num_slots, _ptr(topk_global),
+        _stream(stream)))
+
+
+def dsa_build_group_union_varlen(topk, batch, num_slots, G, group_info, union_idx, union_len,
+                                 head_group_mask, cols=None, stream=None):
+    T = topk.shape[0]
+    cols = topk.shape[1] if cols is None else cols
+    R, cu, kl, qs, bt, bt_ld, ps = _batch(batch)
+    _check("dsa_build_group_union_varlen", lib.dsa_build_group_union_varlen(
+        _ptr(topk), _topk_ld(topk), T, cols, R, cu, kl, qs, bt, bt_ld, ps, num_slots, G,
+        group_info.shape[0], union_idx.shape[1], _ptr(group_info), _ptr(union_idx), _ptr(union_len),
+        _ptr(head_group_mask), _stream(stream)))
+
+
+def dsa_sparse_prefill_grouped_varlen(q, kv_cache, group_info, union_idx, union_len, head_group_mask,
+                                      scale, out, lse, stream=None):
+    T, H, d_qk = q.shape
+    _check("dsa_sparse_prefill_grouped_varlen", lib.dsa_sparse_prefill_grouped_varlen(
+        _ptr(_bits(q)), _ptr(_bits(kv_cache)), kv_cache.shape[0], _ptr(group_info), group_info.shape[0],
+        _ptr(union_idx), _ptr(union_len), _ptr(head_group_mask), T, H, union_idx.shape[1], d_qk,
+        out.shape[2], scale, _ptr(_bits(out)), _ptr(lse), _stream(stream)))
+
+
+def dsa_sparse_prefill_pertoken_varlen(q, kv_cache, topk, batch, scale, topk_ws, out, lse, cols=None,
+                                       stream=None):
+    T, H, d_qk = q.shape
+    cols = topk.shape[1] if cols is None else cols
+    R, cu, kl, qs, bt, bt_ld, ps = _batch(batch)
+    _check("dsa_sparse_prefill_pertoken_varlen", lib.dsa_sparse_prefill_pertoken_varlen(
+        _ptr(_bits(q)), _ptr(_bits(kv_cache)), kv_cache.shape[0], _ptr(topk), _topk_ld(topk), T, H, cols, R,
+        cu, kl, qs, bt, bt_ld, ps, d_qk, out.shape[2], scale, _ptr(topk_ws), _ptr(_bits(out)), _ptr(lse),
+        _stream(stream)))

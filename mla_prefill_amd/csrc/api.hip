@@ -18,6 +18,19 @@ inline bool scale_ok(float s) { return s == s && s != 0.f && s - s == 0.f; }
 constexpr int kLatentDim = 576;
 constexpr int kValueDim = 512;
 
+// host checks of a batch description (its device contents are never errors)
+inline bool batch_shape_ok(int T, int cols, int64_t ld, int R, int64_t bt_ld, int page_size, int num_slots) {
+  return T >= 0 && cols >= 0 && ld >= cols && R >= 1 && bt_ld >= 1 && page_size >= 1 && num_slots >= 1;
+}
+inline bool batch_ptrs_ok(const int32_t* cu, const int32_t* kv_lens, const int32_t* q_pos_start,
+                          const int32_t* block_table) {
+  return cu && kv_lens && q_pos_start && block_table;
+}
+inline bool batch_aligned(const int32_t* cu, const int32_t* kv_lens, const int32_t* q_pos_start,
+                          const int32_t* block_table) {
+  return aligned_to(cu, 4) && aligned_to(kv_lens, 4) && aligned_to(q_pos_start, 4) && aligned_to(block_table, 4);
+}
+
 }  // namespace
 
 extern "C" {
@@ -101,6 +114,104 @@ int dsa_sparse_prefill_pertoken(const uint16_t* q, const uint16_t* kv, const int
   else
     e = dsa::launch_pertoken_attn(q, kv, topk, ld, T, H, S, cols, q_pos_offset, scale, out, lse,
                                   (hipStream_t)stream);
+  return launch_status(e);
+}
+
+int dsa_varlen_group_bound(int T, int R, int G) {
+  if (T < 0 || R < 1 || G < 1 || G > 8) return DSA_ERR_SHAPE;
+  const long long v = ((long long)T + G - 1) / G + R;
+  return (int)(v < T ? v : T);
+}
+
+int dsa_convert_req_index_to_global(const int32_t* topk, int64_t ld, int T, int cols, int R,
+                                    const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                                    const int32_t* q_pos_start, const int32_t* block_table, int64_t bt_ld,
+                                    int page_size, int num_slots, int32_t* topk_global, void* stream) {
+  if (!batch_shape_ok(T, cols, ld, R, bt_ld, page_size, num_slots)) return DSA_ERR_SHAPE;
+  if (T == 0 || cols == 0) return DSA_OK;
+  if (!topk || !topk_global || !batch_ptrs_ok(cu_seqlens_q, kv_lens, q_pos_start, block_table))
+    return DSA_ERR_NULL;
+  if (!aligned_to(topk, 4) || !aligned_to(topk_global, 4) ||
+      !batch_aligned(cu_seqlens_q, kv_lens, q_pos_start, block_table))
+    return DSA_ERR_ALIGN;
+  return launch_status(dsa::launch_convert_req_index(topk, ld, T, cols, R, cu_seqlens_q, kv_lens,
+                                                     q_pos_start, block_table, bt_ld, page_size,
+                                                     num_slots, topk_global, (hipStream_t)stream));
+}
+
+int dsa_build_group_union_varlen(const int32_t* topk, int64_t ld, int T, int cols, int R,
+                                 const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                                 const int32_t* q_pos_start, const int32_t* block_table, int64_t bt_ld,
+                                 int page_size, int num_slots, int G, int max_groups, int union_pad,
+                                 int32_t* group_info, int32_t* union_idx, int32_t* union_len,
+                                 uint8_t* head_group_mask, void* stream) {
+  if (!batch_shape_ok(T, cols, ld, R, bt_ld, page_size, num_slots)) return DSA_ERR_SHAPE;
+  if (G < 1 || G > 8 || max_groups < 0) return DSA_ERR_SHAPE;
+  if (union_pad < 0 || union_pad % 64 != 0 || (long long)union_pad < (long long)G * cols)
+    return DSA_ERR_SHAPE;
+  if (max_groups == 0) return DSA_OK;
+  if ((T > 0 && cols > 0 && !topk) || !group_info || !union_idx || !union_len || !head_group_mask ||
+      !batch_ptrs_ok(cu_seqlens_q, kv_lens, q_pos_start, block_table))
+    return DSA_ERR_NULL;
+  if (!aligned_to(topk, 4) || !aligned_to(group_info, 8) || !aligned_to(union_idx, 4) ||
+      !aligned_to(union_len, 4) || !batch_aligned(cu_seqlens_q, kv_lens, q_pos_start, block_table))
+    return DSA_ERR_ALIGN;
+  return launch_status(dsa::launch_build_union_varlen(
+      topk, ld, T, cols, R, cu_seqlens_q, kv_lens, q_pos_start, block_table, bt_ld, page_size, num_slots,
+      G, max_groups, union_pad, group_info, union_idx, union_len, head_group_mask, (hipStream_t)stream));
+}
+
+int dsa_sparse_prefill_grouped_varlen(const uint16_t* q, const uint16_t* kv_cache, int num_slots,
+                                      const int32_t* group_info, int max_groups, const int32_t* union_idx,
+                                      const int32_t* union_len, const uint8_t* head_group_mask, int T,
+                                      int H, int union_pad, int d_qk, int d_v, float scale,
+                                      uint16_t* out, float* lse, void* stream) {
+  if (H != 16 && H != 32 && H != 64 && H != 128) return DSA_ERR_UNSUPPORTED;
+  if (d_qk != kLatentDim || d_v != kValueDim || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
+  if (T < 0 || num_slots < 1 || max_groups < 0 || union_pad < 0 || union_pad % 32 != 0)
+    return DSA_ERR_SHAPE;
+  if (T == 0 || max_groups == 0) return DSA_OK;
+  if (!q || !kv_cache || !group_info || !union_idx || !union_len || !head_group_mask || !out || !lse)
+    return DSA_ERR_NULL;
+  if (!aligned_to(q, 16) || !aligned_to(kv_cache, 16) || !aligned_to(out, 16) || !aligned_to(lse, 4) ||
+      !aligned_to(group_info, 8) || !aligned_to(union_idx, 4) || !aligned_to(union_len, 4) ||
+      !aligned_to(head_group_mask, 4))
+    return DSA_ERR_ALIGN;
+  return launch_status(dsa::launch_grouped_attn(q, kv_cache, union_idx, union_len, head_group_mask, T, H,
+                                                num_slots, union_pad, scale, out, lse, (hipStream_t)stream,
+                                                group_info, max_groups));
+}
+
+int dsa_sparse_prefill_pertoken_varlen(const uint16_t* q, const uint16_t* kv_cache, int num_slots,
+                                       const int32_t* topk, int64_t ld, int T, int H, int cols, int R,
+                                       const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                                       const int32_t* q_pos_start, const int32_t* block_table,
+                                       int64_t bt_ld, int page_size, int d_qk, int d_v, float scale,
+                                       int32_t* topk_ws, uint16_t* out, float* lse, void* stream) {
+  if (H < 16 || H > 128 || H % 16 != 0) return DSA_ERR_UNSUPPORTED;
+  if (d_qk != kLatentDim || d_v != kValueDim || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
+  if (!batch_shape_ok(T, cols, ld, R, bt_ld, page_size, num_slots)) return DSA_ERR_SHAPE;
+  if (T == 0) return DSA_OK;
+  if (!q || !kv_cache || !out || !lse || (cols > 0 && (!topk || !topk_ws)) ||
+      !batch_ptrs_ok(cu_seqlens_q, kv_lens, q_pos_start, block_table))
+    return DSA_ERR_NULL;
+  if (!aligned_to(q, 16) || !aligned_to(kv_cache, 16) || !aligned_to(out, 16) || !aligned_to(lse, 4) ||
+      !aligned_to(topk, 4) || !aligned_to(topk_ws, 4) ||
+      !batch_aligned(cu_seqlens_q, kv_lens, q_pos_start, block_table))
+    return DSA_ERR_ALIGN;
+  // physical-row top-k (causality applied), then the single-sequence kernel over the whole
+  // cache with every row in its causal range
+  hipError_t e = dsa::launch_convert_req_index(topk, ld, T, cols, R, cu_seqlens_q, kv_lens, q_pos_start,
+                                               block_table, bt_ld, page_size, num_slots, topk_ws,
+                                               (hipStream_t)stream);
+  if (e != hipSuccess) return DSA_ERR_LAUNCH;
+  const int64_t all_causal = (int64_t)num_slots - 1;
+  if (H == 128)
+    e = dsa::launch_pertoken_rows128(q, kv_cache, topk_ws, cols, T, num_slots, cols, all_causal, scale, out,
+                                     lse, (hipStream_t)stream);
+  else
+    e = dsa::launch_pertoken_attn(q, kv_cache, topk_ws, cols, T, H, num_slots, cols, all_causal, scale, out,
+                                  lse, (hipStream_t)stream);
   return launch_status(e);
 }
 

@@ -183,6 +183,15 @@ __device__ __forceinline__ LanePair pair_xor16(float v) {
 __device__ __forceinline__ float max_xor32(float v) { const LanePair p = pair_xor32(v); return fmaxf(p.a, p.b); }
 __device__ __forceinline__ float sum_xor32(float v) { const LanePair p = pair_xor32(v); return p.a + p.b; }
 
+// First token and token count of group grp of 128-row attention: G consecutive tokens
+// from grp * G, or the entry of a batch's group table [NG, 2] (clamped into [0, T)).
+__device__ __forceinline__ int2 group_span(const int32_t* ginfo, int grp, int G, int T) {
+  if (ginfo == nullptr) return int2{grp * G, min(G, T - grp * G)};
+  const int t0 = min(max(ginfo[2 * grp], 0), T);
+  const int n = min(max(ginfo[2 * grp + 1], 0), min(G, T - t0));
+  return int2{t0, n};
+}
+
 // max / sum over the 4 lanes l, l^16, l^32, l^48 (the 4 row groups of a 16x16 C tile)
 __device__ __forceinline__ float max_over_rowgroups(float v) {
   const LanePair p = pair_xor16(v);

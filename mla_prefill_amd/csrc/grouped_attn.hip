@@ -61,7 +61,8 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ keys, int64_t keys_ld, const int32_t* __restrict__ union_len,
     const uint8_t* __restrict__ hgmask, int T, int H, int S, int ncols, int64_t q_pos_offset,
-    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
+    const int32_t* __restrict__ ginfo) {
   __shared__ __align__(16) uint8_t stage[kRStages][kRStageBytes];
   // per tile and wave: lanes 0..7 = slot indices 8 w .. 8 w + 7, lanes 8, 9 = their membership bytes
   __shared__ __align__(16) uint32_t idxw[kRIdxBufs][kRWaves][64];
@@ -69,16 +70,17 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   __shared__ int over_any;
 
   const int G = 128 / H;
-  const int NG = (T + G - 1) / G;
+  const int NG = (int)gridDim.x;
   const int grp = NG - 1 - xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hi = lane >> 5, m = lane & 31;
-  const int t0 = grp * G;
+  const int2 span = group_span(ginfo, grp, G, T);  // (a batch's groups come from its table)
+  const int t0 = uniform(span.x), ntok = uniform(span.y);
   const int r = 32 * wave + m;  // this lane's row
   const int ri = r / H;
   const int rh = r - ri * H;
   const int tok = t0 + ri;
-  const bool live = tok < T;
+  const bool live = ri < ntok;
   if (tid == 0) over_any = 0;  // ordered before any use by the loop's (or the final) barrier
 
   // queries: row r, dims 16 s + 8 hi .. + 8; a negative scale is applied as |scale| on
@@ -333,17 +335,17 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
 hipError_t launch_grouped_attn(const uint16_t* q, const uint16_t* kv, const int32_t* union_idx,
                                const int32_t* union_len, const uint8_t* head_group_mask, int T,
                                int H, int S, int union_pad, float scale, uint16_t* out, float* lse,
-                               hipStream_t stream) {
+                               hipStream_t stream, const int32_t* group_info, int max_groups) {
   const int G = 128 / H;
-  const int NG = (T + G - 1) / G;
+  const int NG = group_info ? max_groups : (T + G - 1) / G;
   if (NG == 0) return hipSuccess;
   hipLaunchKernelGGL(rows128_attn_kernel<false>, dim3(NG), dim3(kRThreads), 0, stream, q, kv,
                      union_idx, (int64_t)union_pad, union_len, head_group_mask, T, H, S, union_pad,
-                     (int64_t)0, scale * kLog2e, out, lse);
+                     (int64_t)0, scale * kLog2e, out, lse, group_info);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_rows128_exact(q, kv, union_idx, (int64_t)union_pad, union_len, head_group_mask, T, H,
-                              S, union_pad, 0, scale, out, lse, stream);
+                              S, union_pad, 0, scale, out, lse, stream, group_info, NG);
 }
 
 hipError_t launch_pertoken_rows128(const uint16_t* q, const uint16_t* kv, const int32_t* topk,
@@ -352,11 +354,11 @@ hipError_t launch_pertoken_rows128(const uint16_t* q, const uint16_t* kv, const 
   if (T == 0) return hipSuccess;
   hipLaunchKernelGGL(rows128_attn_kernel<true>, dim3(T), dim3(kRThreads), 0, stream, q, kv, topk,
                      ld, (const int32_t*)nullptr, (const uint8_t*)nullptr, T, 128, S, cols,
-                     q_pos_offset, scale * kLog2e, out, lse);
+                     q_pos_offset, scale * kLog2e, out, lse, (const int32_t*)nullptr);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_rows128_exact(q, kv, topk, ld, nullptr, nullptr, T, 128, S, cols, q_pos_offset, scale,
-                              out, lse, stream);
+                              out, lse, stream, nullptr, T);
 }
 
 }  // namespace dsa

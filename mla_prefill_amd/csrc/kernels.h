@@ -12,6 +12,21 @@ hipError_t launch_build_union(const int32_t* topk, int64_t ld, int T, int cols, 
                               int64_t q_pos_offset, int G, int union_pad, int32_t* union_idx,
                               int32_t* union_len, uint8_t* head_group_mask, hipStream_t stream);
 
+// A batch of requests over a paged cache: union/mask per group of consecutive tokens of
+// one request (groups numbered request by request; group_info[g] = first token, count),
+// list entries written as physical rows.
+hipError_t launch_build_union_varlen(const int32_t* topk, int64_t ld, int T, int cols, int R,
+                                     const int32_t* cu_seqlens, const int32_t* kv_lens,
+                                     const int32_t* q_pos_start, const int32_t* block_table,
+                                     int64_t bt_ld, int page_size, int num_slots, int G, int max_groups,
+                                     int union_pad, int32_t* group_info, int32_t* union_idx,
+                                     int32_t* union_len, uint8_t* head_group_mask, hipStream_t stream);
+// request-local top-k entries -> physical rows (-1: selects nothing), out [T, cols]
+hipError_t launch_convert_req_index(const int32_t* topk, int64_t ld, int T, int cols, int R,
+                                    const int32_t* cu_seqlens, const int32_t* kv_lens,
+                                    const int32_t* q_pos_start, const int32_t* block_table, int64_t bt_ld,
+                                    int page_size, int num_slots, int32_t* out, hipStream_t stream);
+
 hipError_t launch_scatter_topk_bits(const int32_t* topk, int64_t ld, int T, int cols, int S,
                                     int64_t q_pos_offset, uint32_t* bits, int words,
                                     hipStream_t stream);
@@ -24,11 +39,13 @@ hipError_t launch_pertoken_attn(const uint16_t* q, const uint16_t* kv, const int
 // 128-row attention over a per-workgroup key list.  Grouped mode: rows are the
 // 128 pseudo-heads of a group, keys the group's union list, and each row is
 // restricted by its token's bit of head_group_mask.  Per-token mode (H = 128):
-// rows are the token's heads and keys its top-k row.
+// rows are the token's heads and keys its top-k row.  group_info (nullptr: group g is
+// tokens gG ..) gives each of max_groups groups' first token and token count.
 hipError_t launch_grouped_attn(const uint16_t* q, const uint16_t* kv, const int32_t* union_idx,
                                const int32_t* union_len, const uint8_t* head_group_mask, int T,
                                int H, int S, int union_pad, float scale, uint16_t* out, float* lse,
-                               hipStream_t stream);
+                               hipStream_t stream, const int32_t* group_info = nullptr,
+                               int max_groups = 0);
 hipError_t launch_pertoken_rows128(const uint16_t* q, const uint16_t* kv, const int32_t* topk,
                                    int64_t ld, int T, int S, int cols, int64_t q_pos_offset,
                                    float scale, uint16_t* out, float* lse, hipStream_t stream);
@@ -42,7 +59,8 @@ constexpr uint32_t kOverflowMark = 0x7fa5a5a5u;
 hipError_t launch_rows128_exact(const uint16_t* q, const uint16_t* kv, const int32_t* keys,
                                 int64_t keys_ld, const int32_t* union_len, const uint8_t* hgmask,
                                 int T, int H, int S, int ncols, int64_t q_pos_offset, float scale,
-                                uint16_t* out, float* lse, hipStream_t stream);
+                                uint16_t* out, float* lse, hipStream_t stream, const int32_t* group_info,
+                                int ngroups);
 
 // masked dense MHA, qk 256 = k_nope dn (256 or 192) + shared k_pe (0 or 64), v 256,
 // mask = causal AND top-k bit

@@ -45,7 +45,8 @@ __global__ __launch_bounds__(kGThreads) void rows128_exact_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ keys, int64_t keys_ld, const int32_t* __restrict__ union_len,
     const uint8_t* __restrict__ hgmask, int T, int H, int S, int ncols, int64_t q_pos_offset,
-    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
+    const int32_t* __restrict__ ginfo) {
   __shared__ __align__(16) uint8_t stage[kGStages][kGStageBytes];
   __shared__ __align__(16) uint16_t pbuf[128 * kGPStride];
   __shared__ float alpha_s[128];
@@ -53,21 +54,22 @@ __global__ __launch_bounds__(kGThreads) void rows128_exact_kernel(
   __shared__ __align__(16) uint8_t dummy[1024];
 
   const int G = 128 / H;
-  const int NG = (T + G - 1) / G;
+  const int NG = (int)gridDim.x;
   const int grp = NG - 1 - xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, n = lane & 15;
-  const int t0 = grp * G;
+  const int2 span = group_span(ginfo, grp, G, T);
+  const int t0 = uniform(span.x), ntok = uniform(span.y);
   // only groups the fast kernel marked are recomputed (the mark sits in the LSE of the
-  // group's first row, which always exists)
-  if (__float_as_uint(lse[(size_t)t0 * H]) != kOverflowMark) return;
+  // group's first row)
+  if (ntok <= 0 || __float_as_uint(lse[(size_t)t0 * H]) != kOverflowMark) return;
 
   // the row this lane's wave owns for QK^T / softmax
   const int r_own = 16 * wave + n;
   const int i_own = r_own / H;
   const int h_own = r_own - i_own * H;
   const int tok_own = t0 + i_own;
-  const bool row_live = tok_own < T;
+  const bool row_live = i_own < ntok;
 
   bf16x8 qreg[kGDqk / 32];
   if (row_live) {
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(kGThreads) void rows128_exact_kernel(
     const int i = row / H;
     const int h = row - i * H;
     const int tok = t0 + i;
-    if (tok >= T) continue;
+    if (i >= ntok) continue;
     const float inv = linv_s[row];
     uint16_t* orow = out + ((size_t)tok * H + h) * kGDv + 64 * wave + 4 * hi;
 #pragma unroll
@@ -314,18 +316,18 @@ __global__ __launch_bounds__(kGThreads) void rows128_exact_kernel(
 hipError_t launch_rows128_exact(const uint16_t* q, const uint16_t* kv, const int32_t* keys,
                                 int64_t keys_ld, const int32_t* union_len, const uint8_t* hgmask,
                                 int T, int H, int S, int ncols, int64_t q_pos_offset, float scale,
-                                uint16_t* out, float* lse, hipStream_t stream) {
-  const int G = 128 / H;
-  const int NG = (T + G - 1) / G;
+                                uint16_t* out, float* lse, hipStream_t stream, const int32_t* group_info,
+                                int ngroups) {
+  const int NG = ngroups;
   if (NG == 0) return hipSuccess;
   if (hgmask != nullptr)
     hipLaunchKernelGGL(rows128_exact_kernel<false>, dim3(NG), dim3(kGThreads), 0, stream, q, kv, keys,
                        keys_ld, union_len, hgmask, T, H, S, ncols, q_pos_offset, scale * kLog2e, out,
-                       lse);
+                       lse, group_info);
   else
     hipLaunchKernelGGL(rows128_exact_kernel<true>, dim3(NG), dim3(kGThreads), 0, stream, q, kv, keys,
                        keys_ld, union_len, hgmask, T, H, S, ncols, q_pos_offset, scale * kLog2e, out,
-                       lse);
+                       lse, group_info);
   return hipGetLastError();
 }
 

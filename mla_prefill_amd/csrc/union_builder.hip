@@ -7,6 +7,16 @@
 // selects, -1 padded, its length, and one byte per list slot whose bit i says
 // whether token gG + i selects that position.
 //
+// Batches of requests over a paged KV cache ("[Perf][DSA] Grouped sparse prefill
+// ...", "How" section: groups are consecutive tokens of one request, and the
+// union's request-local positions become physical rows through the request's
+// index conversion): groups are numbered request by request, each covers up to G
+// consecutive tokens of one request, the union is built over request-local
+// positions exactly as above, and each list entry is written as its physical row
+// (block_table[r][x / page_size] * page_size + x % page_size).  Positions whose
+// row falls outside the cache (or past the request's page table) are not
+// selected.  The group table (first token, token count) is written alongside.
+//
 // MI355X design: one workgroup per group.  A byte per KV position lives in LDS
 // (a 32 KiB window of positions per pass); member i ORs bit i into the byte of
 // each position it selects (LDS atomics commute, so the result does not depend
@@ -24,23 +34,107 @@ constexpr int kUnionThreads = 256;
 constexpr int kUnionWaves = kUnionThreads / 64;
 constexpr int kUnionWindow = 32768;  // positions per LDS pass (one byte each)
 
+// A batch of requests (device arrays; data contents are never errors, every index
+// is checked before use).
+struct ReqBatch {
+  int R;
+  const int32_t* cu_seqlens;   // [R + 1]: query tokens of request r are cu[r] .. cu[r + 1] - 1
+  const int32_t* kv_lens;      // [R]: positions 0 .. kv_len - 1 exist
+  const int32_t* q_pos_start;  // [R]: position of the request's first query token
+  const int32_t* block_table;  // [R, bt_ld]: physical page of each request page
+  int64_t bt_ld;
+  int page_size;
+  int num_slots;               // rows of the cache
+};
+
+// request of token t: the first r with cu[r + 1] > t (empty requests are skipped)
+__device__ __forceinline__ int request_of(const ReqBatch& b, int t) {
+  int lo = 0, hi = b.R - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (b.cu_seqlens[mid + 1] <= t) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// physical row of request r's position x, or -1 (past the page table or the cache)
+__device__ __forceinline__ int64_t physical_row(const ReqBatch& b, int r, int x) {
+  const int pg = x / b.page_size;
+  if ((int64_t)pg >= b.bt_ld) return -1;
+  const int32_t page = b.block_table[(int64_t)r * b.bt_ld + pg];
+  if (page < 0) return -1;
+  const int64_t row = (int64_t)page * b.page_size + (x - pg * b.page_size);
+  return row < b.num_slots ? row : -1;
+}
+
+// kVarlen = false: one sequence (group g = tokens gG ..), positions q_pos_offset + t,
+// rows = positions.  kVarlen = true: the batch `b` (S, q_pos_offset unused).
+template <bool kVarlen>
 __global__ __launch_bounds__(kUnionThreads) void build_union_kernel(
     const int32_t* __restrict__ topk, int64_t ld, int T, int cols, int S, int64_t q_pos_offset,
     int G, int union_pad, int32_t* __restrict__ union_idx, int32_t* __restrict__ union_len,
-    uint8_t* __restrict__ head_group_mask) {
+    uint8_t* __restrict__ head_group_mask, ReqBatch b, int32_t* __restrict__ group_info) {
   __shared__ uint32_t bytemap[kUnionWindow / 4];
   __shared__ int wave_count[kUnionWaves];
+  __shared__ int grp_req, grp_k, scan_tmp[kUnionThreads];
 
-  const int NG = (T + G - 1) / G;
+  const int NG = (int)gridDim.x;
   const int g = NG - 1 - (int)blockIdx.x;  // later groups scan more positions: start them first
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int t0 = g * G;
-  const int ntok = min(G, T - t0);
+  int t0, ntok, r = 0;
+  int64_t pos0;  // position of the group's first token
+  int S_eff;     // positions that exist
+  if (!kVarlen) {
+    t0 = g * G;
+    ntok = min(G, T - t0);
+    pos0 = q_pos_offset + t0;
+    S_eff = S;
+  } else {
+    // group g is group k of request r: a block-wide scan of ceil(n_r / G) over the requests
+    if (tid == 0) { grp_req = -1; grp_k = 0; }
+    __syncthreads();
+    int base = 0;
+    for (int r0 = 0; r0 < b.R; r0 += kUnionThreads) {
+      const int rr = r0 + tid;
+      int n = 0;
+      if (rr < b.R) n = max(0, min(b.cu_seqlens[rr + 1], T) - max(b.cu_seqlens[rr], 0));
+      const int cnt = (n + G - 1) / G;
+      scan_tmp[tid] = cnt;
+      __syncthreads();
+      for (int d = 1; d < kUnionThreads; d <<= 1) {  // inclusive scan (Hillis-Steele)
+        const int v = tid >= d ? scan_tmp[tid - d] : 0;
+        __syncthreads();
+        scan_tmp[tid] += v;
+        __syncthreads();
+      }
+      const int incl = base + scan_tmp[tid];
+      if (rr < b.R && cnt > 0 && g >= incl - cnt && g < incl) { grp_req = rr; grp_k = g - (incl - cnt); }
+      base += scan_tmp[kUnionThreads - 1];
+      __syncthreads();
+    }
+    r = grp_req;
+    if (r < 0) {  // past the batch's last group
+      t0 = 0;
+      ntok = 0;
+      pos0 = 0;
+      S_eff = 0;
+    } else {
+      const int c0 = max(b.cu_seqlens[r], 0);
+      t0 = c0 + grp_k * G;
+      ntok = min(G, min(b.cu_seqlens[r + 1], T) - t0);
+      pos0 = (int64_t)b.q_pos_start[r] + (t0 - b.cu_seqlens[r]);
+      S_eff = b.kv_lens[r];
+    }
+    if (tid == 0) {
+      group_info[2 * g] = t0;
+      group_info[2 * g + 1] = ntok;
+    }
+  }
 
   // positions a member can select: [0, pend)
-  int64_t pmax = q_pos_offset + t0 + ntok - 1;
-  if (pmax > (int64_t)S - 1) pmax = (int64_t)S - 1;
-  const int pend = pmax < 0 ? 0 : (int)(pmax + 1);
+  int64_t pmax = pos0 + ntok - 1;
+  if (pmax > (int64_t)S_eff - 1) pmax = (int64_t)S_eff - 1;
+  const int pend = (pmax < 0 || ntok <= 0) ? 0 : (int)(pmax + 1);
 
   int32_t* uout = union_idx + (size_t)g * union_pad;
   uint8_t* mout = head_group_mask + (size_t)g * union_pad;
@@ -58,7 +152,8 @@ __global__ __launch_bounds__(kUnionThreads) void build_union_kernel(
       const int t = t0 + i;
       const int32_t x = topk[(size_t)t * ld + c];
       // selection rule: 0 <= x < S and x <= position of token t; x >= w0 >= 0 covers x >= 0
-      if (x >= w0 && x - w0 < wlen && (int64_t)x <= q_pos_offset + t) {
+      // (a batch also drops positions without a physical row)
+      if (x >= w0 && x - w0 < wlen && (int64_t)x <= pos0 + i && (!kVarlen || physical_row(b, r, x) >= 0)) {
         const int p = x - w0;
         atomicOr(&bytemap[p >> 2], (1u << i) << (8 * (p & 3)));
       }
@@ -83,13 +178,13 @@ __global__ __launch_bounds__(kUnionThreads) void build_union_kernel(
     }
     for (int p = s0; p < s1; p += 64) {
       const int pp = p + lane;
-      const uint8_t b = pp < s1 ? bm[pp] : (uint8_t)0;
-      const uint64_t m = ballot(b != 0);
-      if (b != 0) {
+      const uint8_t mb = pp < s1 ? bm[pp] : (uint8_t)0;
+      const uint64_t m = ballot(mb != 0);
+      if (mb != 0) {
         const int o = base + lanes_below(m);
         if (o < union_pad) {  // always true when union_pad >= G * cols (checked on the host)
-          uout[o] = w0 + pp;
-          mout[o] = b;
+          uout[o] = kVarlen ? (int32_t)physical_row(b, r, w0 + pp) : w0 + pp;
+          mout[o] = mb;
         }
       }
       base += __popcll(m);
@@ -146,8 +241,54 @@ hipError_t launch_build_union(const int32_t* topk, int64_t ld, int T, int cols, 
                               int32_t* union_len, uint8_t* head_group_mask, hipStream_t stream) {
   const int NG = (T + G - 1) / G;
   if (NG == 0) return hipSuccess;
-  hipLaunchKernelGGL(build_union_kernel, dim3(NG), dim3(kUnionThreads), 0, stream, topk, ld, T,
-                     cols, S, q_pos_offset, G, union_pad, union_idx, union_len, head_group_mask);
+  hipLaunchKernelGGL(build_union_kernel<false>, dim3(NG), dim3(kUnionThreads), 0, stream, topk, ld, T,
+                     cols, S, q_pos_offset, G, union_pad, union_idx, union_len, head_group_mask,
+                     ReqBatch{}, (int32_t*)nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_union_varlen(const int32_t* topk, int64_t ld, int T, int cols, int R,
+                                     const int32_t* cu_seqlens, const int32_t* kv_lens,
+                                     const int32_t* q_pos_start, const int32_t* block_table,
+                                     int64_t bt_ld, int page_size, int num_slots, int G, int max_groups,
+                                     int union_pad, int32_t* group_info, int32_t* union_idx,
+                                     int32_t* union_len, uint8_t* head_group_mask, hipStream_t stream) {
+  if (max_groups == 0) return hipSuccess;
+  const ReqBatch b{R, cu_seqlens, kv_lens, q_pos_start, block_table, bt_ld, page_size, num_slots};
+  hipLaunchKernelGGL(build_union_kernel<true>, dim3(max_groups), dim3(kUnionThreads), 0, stream, topk,
+                     ld, T, cols, 0, (int64_t)0, G, union_pad, union_idx, union_len, head_group_mask, b,
+                     group_info);
+  return hipGetLastError();
+}
+
+// Request-local top-k entries as physical rows ("[Perf][DSA] Grouped sparse prefill ...",
+// "How" section: the index conversion to physical rows), -1 where the entry selects
+// nothing (negative, past the request's KV, beyond the token's position, or without a
+// physical row).  One workgroup per token.
+__global__ __launch_bounds__(256) void convert_req_index_kernel(const int32_t* __restrict__ topk,
+                                                                 int64_t ld, int T, int cols, ReqBatch b,
+                                                                 int32_t* __restrict__ out) {
+  const int t = blockIdx.x;
+  const int r = request_of(b, t);
+  const int64_t pos = (int64_t)b.q_pos_start[r] + (t - b.cu_seqlens[r]);
+  const int kvl = b.kv_lens[r];
+  const int32_t* trow = topk + (size_t)t * ld;
+  int32_t* orow = out + (size_t)t * cols;
+  for (int c = threadIdx.x; c < cols; c += 256) {
+    const int32_t x = trow[c];
+    int32_t row = -1;
+    if (x >= 0 && x < kvl && (int64_t)x <= pos) row = (int32_t)physical_row(b, r, x);
+    orow[c] = row;
+  }
+}
+
+hipError_t launch_convert_req_index(const int32_t* topk, int64_t ld, int T, int cols, int R,
+                                    const int32_t* cu_seqlens, const int32_t* kv_lens,
+                                    const int32_t* q_pos_start, const int32_t* block_table, int64_t bt_ld,
+                                    int page_size, int num_slots, int32_t* out, hipStream_t stream) {
+  if (T == 0 || cols == 0) return hipSuccess;
+  const ReqBatch b{R, cu_seqlens, kv_lens, q_pos_start, block_table, bt_ld, page_size, num_slots};
+  hipLaunchKernelGGL(convert_req_index_kernel, dim3(T), dim3(256), 0, stream, topk, ld, T, cols, b, out);
   return hipGetLastError();
 }
 

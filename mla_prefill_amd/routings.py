@@ -74,3 +74,58 @@ def masked_mha(q, k_nope, k_pe, v, topk, q_pos_offset: int, scale: float, mask_w
     _lib.dsa_masked_mha_prefill(q, k_nope, k_pe, v, topk, q_pos_offset, scale, mask_ws, out, lse,
                                 stream=stream)
     return out, lse, mask_ws
+
+
+# ---------------------------------------------------------------------------
+# batches of requests over a paged KV cache; `batch` = (cu_seqlens_q, kv_lens,
+# q_pos_start, block_table, page_size), int32 device tensors and an int
+# ---------------------------------------------------------------------------
+
+@dataclass
+class VarlenUnionBuffers:
+    group_info: torch.Tensor  # int32 [max_groups, 2]
+    union_idx: torch.Tensor   # int32 [max_groups, union_pad]
+    union_len: torch.Tensor   # int32 [max_groups]
+    mask: torch.Tensor        # uint8 [max_groups, union_pad]
+
+
+def alloc_union_varlen(max_groups: int, G: int, cols: int, device="cuda") -> VarlenUnionBuffers:
+    pad = _lib.dsa_union_pad(G, cols)
+    return VarlenUnionBuffers(torch.empty((max_groups, 2), dtype=torch.int32, device=device),
+                              torch.empty((max_groups, pad), dtype=torch.int32, device=device),
+                              torch.empty((max_groups,), dtype=torch.int32, device=device),
+                              torch.empty((max_groups, pad), dtype=torch.uint8, device=device))
+
+
+def build_group_union_varlen(topk, batch, num_slots: int, G: int, max_groups: int | None = None,
+                             bufs: VarlenUnionBuffers | None = None, stream=None) -> VarlenUnionBuffers:
+    T, cols = topk.shape
+    if bufs is None:
+        mg = max_groups if max_groups is not None else _lib.dsa_varlen_group_bound(T, batch[1].shape[0], G)
+        bufs = alloc_union_varlen(mg, G, cols, topk.device)
+    _lib.dsa_build_group_union_varlen(topk, batch, num_slots, G, bufs.group_info, bufs.union_idx,
+                                      bufs.union_len, bufs.mask, stream=stream)
+    return bufs
+
+
+def grouped_varlen(q, kv_cache, topk, batch, scale: float, max_groups: int | None = None,
+                   bufs: VarlenUnionBuffers | None = None, out=None, lse=None, stream=None):
+    """Union/mask build of a batch followed by its grouped attention (G = 128 / H)."""
+    T, H, _ = q.shape
+    G = 128 // H
+    bufs = build_group_union_varlen(topk, batch, kv_cache.shape[0], G, max_groups, bufs, stream)
+    if out is None:
+        out, lse = alloc_out(T, H, 512, q.device)
+    _lib.dsa_sparse_prefill_grouped_varlen(q, kv_cache, bufs.group_info, bufs.union_idx, bufs.union_len,
+                                           bufs.mask, scale, out, lse, stream=stream)
+    return out, lse, bufs
+
+
+def pertoken_varlen(q, kv_cache, topk, batch, scale: float, topk_ws=None, out=None, lse=None, stream=None):
+    T, H, _ = q.shape
+    if topk_ws is None:
+        topk_ws = torch.empty(topk.shape, dtype=torch.int32, device=q.device)
+    if out is None:
+        out, lse = alloc_out(T, H, 512, q.device)
+    _lib.dsa_sparse_prefill_pertoken_varlen(q, kv_cache, topk, batch, scale, topk_ws, out, lse, stream=stream)
+    return out, lse, topk_ws

@@ -163,3 +163,35 @@ def test_library_links_only_hip_runtime():
     out = subprocess.run(["ldd", LIB], capture_output=True, text=True).stdout
     assert "libamdhip64" in out
     assert "torch" not in out and "python" not in out
+
+
+def test_varlen_validation(lib):
+    assert lib.dsa_varlen_group_bound(37, 5, 8) == 10 and lib.dsa_varlen_group_bound(3, 5, 8) == 3
+    assert lib.dsa_varlen_group_bound(0, 1, 8) == 0
+    for args in ((-1, 1, 8), (5, 0, 8), (5, 1, 0), (5, 1, 9)):
+        assert lib.dsa_varlen_group_bound(*args) == SHAPE
+    def conv(tk=P, ld=16, T=8, cols=16, R_=2, cu=P, kl=P, qs=P, bt=P, bt_ld=4, ps=64, ns=256, out=P):
+        return lib.dsa_convert_req_index_to_global(tk, ld, T, cols, R_, cu, kl, qs, bt, bt_ld, ps, ns, out, None)
+    assert conv(R_=0) == SHAPE and conv(ps=0) == SHAPE and conv(ns=0) == SHAPE and conv(ld=8) == SHAPE
+    assert conv(T=0) == OK and conv(cols=0) == OK
+    for kw in ("tk", "cu", "kl", "qs", "bt", "out"):
+        assert conv(**{kw: None}) == NULL
+    assert conv(bt=P + 2) == ALIGN
+    def build(tk=P, T=8, cols=16, gi=P, ui=P, ul=P, mk=P, mg=3, pad=128, G=8, cu=P):
+        return lib.dsa_build_group_union_varlen(tk, 16, T, cols, 2, cu, P, P, P, 4, 64, 256, G, mg, pad,
+                                                gi, ui, ul, mk, None)
+    assert build(pad=100) == SHAPE and build(pad=64) == SHAPE and build(G=9) == SHAPE
+    assert build(mg=0) == OK
+    for kw in ("gi", "ui", "ul", "mk", "cu"):
+        assert build(**{kw: None}) == NULL
+    assert build(gi=P + 4) == ALIGN
+    def gv(H=16, dqk=576, ns=256, mg=3, pad=128, gi=P, T=8, scale=0.1):
+        return lib.dsa_sparse_prefill_grouped_varlen(P, P, ns, gi, mg, P, P, P, T, H, pad, dqk, 512, scale,
+                                                     P, P, None)
+    assert gv(H=24) == UNSUP and gv(dqk=512) == UNSUP and gv(scale=0.0) == UNSUP
+    assert gv(ns=0) == SHAPE and gv(pad=40) == SHAPE
+    assert gv(mg=0) == OK and gv(T=0) == OK and gv(gi=None) == NULL and gv(gi=P + 4) == ALIGN
+    def pv(H=16, ws=P, T=8, R_=2, cols=16):
+        return lib.dsa_sparse_prefill_pertoken_varlen(P, P, 256, P, 16, T, H, cols, R_, P, P, P, P, 4, 64,
+                                                      576, 512, 0.1, ws, P, P, None)
+    assert pv(H=8) == UNSUP and pv(R_=0) == SHAPE and pv(T=0) == OK and pv(ws=None) == NULL
