@@ -38,6 +38,9 @@ WORKLOADS = {
     # name: (MQA config, masked-MHA config or None)
     "glm16k": ("c3_glm16k", "c4_masked_nope"),
     "glm16k_rope": ("c3_glm16k", "c6_masked_rope"),
+    # a batch of 8 requests (2048 query tokens after 14336 positions of context each) over a
+    # paged cache (64-row pages in a random physical order): the two MQA routings
+    "glm16k_paged": (None, None),
     "glm16k_uniform": ("c3w_glm16k_uniform", None),
     "long32k": ("c5_long", None),
     "dsv32": ("c2_dsv32", None),
@@ -185,6 +188,9 @@ def main():
         calibrate_copy(a.calibrate_copy_mib)
         return
 
+    if a.workload == "glm16k_paged":
+        bench_paged(a)
+        return
     mqa_name, mha_name = WORKLOADS[a.workload]
     t_gen = time.perf_counter()
     case = make_case(CONFIGS[mqa_name])
@@ -305,6 +311,148 @@ def main():
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "routing_query_tokens_per_s": {k: round(v, 1) for k, v in routing_tps.items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
+PAGED = dict(seed=6, q_lens=[2048] * 8, ctx_lens=[14336] * 8, H=16, k=2048, cols=2048, page_size=64,
+             G=8, mode="locality", spare_pages=64)
+
+
+def cpu_baseline_paged(case, budget_s):
+    """The oracle on whole groups of the batch sampled across its requests."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    groups = oracle.varlen_groups(case.cu_seqlens, case.G)
+    args = (case.cu_seqlens, case.kv_lens, case.q_pos_start, case.block_table, case.page_size)
+    rng = np.random.default_rng(0)
+    done, spent, n = 0, 0.0, 0
+    for gi in rng.permutation(len(groups)):
+        t0, cnt = groups[gi]
+        toks = list(range(t0, t0 + cnt))
+        start = time.perf_counter()
+        r = int(np.searchsorted(case.cu_seqlens, t0, side="right") - 1)
+        sub_cu = np.array([0, cnt])
+        sub = (sub_cu, case.kv_lens[r:r + 1], case.q_pos_start[r:r + 1] + (t0 - case.cu_seqlens[r]),
+               case.block_table[r:r + 1], case.page_size)
+        info, ui, ul, mk = oracle.group_union_mask_varlen(case.topk[t0:t0 + cnt], *sub, case.num_slots,
+                                                          case.G, 1)
+        oracle.grouped_sparse_mqa_varlen(case.q[t0:t0 + cnt], case.kv_cache, info, ui, ul, mk, case.scale)
+        oracle.pertoken_sparse_mqa_varlen(case.q, case.kv_cache, case.topk, *args, case.scale, tokens=toks)
+        spent += time.perf_counter() - start
+        done += cnt
+        n += 1
+        if spent >= budget_s:
+            break
+    return {"value": done / spent, "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"{n} whole groups ({done} query tokens) drawn uniformly from the {len(groups)} groups "
+                       f"of the batch; union/mask, grouped and per-token on numpy float64; {spent:.1f} s")}
+
+
+def bench_paged(a):
+    """The two MQA routings on a batch of requests over a paged cache."""
+    import torch
+    from mla_prefill_amd import _lib, routings
+    from synth import make_varlen_case
+
+    t_gen = time.perf_counter()
+    c = make_varlen_case(**PAGED)
+    print(f"# inputs generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    def dbf(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+
+    def di(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
+
+    q, kv, tk = dbf(c.q), dbf(c.kv_cache), di(c.topk)
+    batch = (di(c.cu_seqlens), di(c.kv_lens), di(c.q_pos_start), di(c.block_table), c.page_size)
+    T, H = q.shape[0], q.shape[1]
+    mg = c.max_groups()
+    bufs = routings.alloc_union_varlen(mg, c.G, c.topk.shape[1])
+    out_g, lse_g = routings.alloc_out(T, H, 512)
+    out_p, lse_p = routings.alloc_out(T, H, 512)
+    ws = torch.empty_like(tk)
+    stream = torch.cuda.current_stream()
+    names = ["build_union", "grouped_attn", "pertoken_attn"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        _lib.dsa_build_group_union_varlen(tk, batch, c.num_slots, c.G, bufs.group_info, bufs.union_idx,
+                                          bufs.union_len, bufs.mask, stream=stream)
+        mark(1)
+        _lib.dsa_sparse_prefill_grouped_varlen(q, kv, bufs.group_info, bufs.union_idx, bufs.union_len,
+                                               bufs.mask, c.scale, out_g, lse_g, stream=stream)
+        mark(2)
+        _lib.dsa_sparse_prefill_pertoken_varlen(q, kv, tk, batch, c.scale, ws, out_p, lse_p, stream=stream)
+        mark(3)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_ in range(a.steps):
+        step(events[s_])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: float(np.mean([events[s_][i].elapsed_time(events[s_][i + 1]) for s_ in range(a.steps)]))
+           for i, n in enumerate(names)}
+    ms_step = wall * 1e3 / a.steps
+    if not (torch.isfinite(out_g.float()).all() and torch.isfinite(out_p.float()).all()):
+        print("non-finite output", file=sys.stderr)
+        sys.exit(3)
+
+    # algorithmic work: union over the groups' rows, selected rows of every token
+    info = bufs.group_info.cpu().numpy()
+    ul = bufs.union_len.cpu().numpy().astype(np.float64)
+    nsel = int((ws.cpu().numpy() >= 0).sum())
+    cols = c.topk.shape[1]
+    pad = bufs.union_idx.shape[1]
+    work = {
+        "build_union": ("hbm", T * cols * 4 + mg * pad * 5 + mg * 12),
+        "grouped_attn": ("mfma", float(np.sum(ul * info[:, 1] * H)) * 2 * (576 + 512)),
+        "pertoken_attn": ("hbm", nsel * 1152 + T * H * 576 * 2 + T * H * 512 * 2 + T * H * 4 + T * cols * 8),
+    }
+    kernels = {}
+    for n in names:
+        bound, amount = work[n]
+        ms = per[n]
+        if bound == "hbm":
+            ach = amount / (ms * 1e-3) / 1e9
+            kernels[n] = {"ms": ms, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": ach / HBM_PEAK_GBS, "algorithmic": amount}
+        else:
+            ach = amount / (ms * 1e-3) / 1e12
+            kernels[n] = {"ms": ms, "bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFS,
+                          "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFS, "algorithmic": amount}
+    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+    d = kernels[dom]
+    roofline = {"kernel": dom, "bound": d["bound"], "achieved": round(d["achieved"], 2), "peak": d["peak"],
+                "unit": d["unit"], "frac": round(d["frac"], 4), "traffic": None}
+    cpu = None if a.no_cpu else cpu_baseline_paged(c, a.cpu_seconds)
+    line = {
+        "metric": METRIC, "value": round(T / (ms_step * 1e-3), 1), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "glm16k_paged", "requests": len(PAGED["q_lens"]), "q_len": PAGED["q_lens"][0],
+                   "ctx": PAGED["ctx_lens"][0], "H": H, "k": PAGED["k"], "cols": cols, "G": c.G,
+                   "page_size": c.page_size, "num_slots": c.num_slots, "groups": mg, "selected_rows": nsel},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+        "routing_query_tokens_per_s": {
+            "grouped (union build + attention)": round(T / ((per["build_union"] + per["grouped_attn"]) * 1e-3), 1),
+            "per-token (index conversion + attention)": round(T / (per["pertoken_attn"] * 1e-3), 1)},
     }
     print(json.dumps(line), flush=True)
 

@@ -102,3 +102,47 @@ def test_masked_mha_full(name):
         for x in oracle.selected_positions(c.topk[t], cfg.S, cfg.q_pos_offset + t):
             row[x // 32] |= np.uint32(1) << np.uint32(x % 32)
         np.testing.assert_array_equal(wsn[t], row)
+
+
+def test_paged_batch_full():
+    """The benchmark's paged batch (8 requests x 2048 query tokens after 14336 positions of
+    context, 64-row pages shuffled over a 135168-row cache): union, mask and group table of
+    sampled groups bit-exact, both routings on sampled tokens, the index conversion on
+    sampled rows."""
+    import bench
+    from mla_prefill_amd import _lib, routings
+    from synth import make_varlen_case
+    c = make_varlen_case(**bench.PAGED)
+    q, kv, tk = dev_bf16(c.q), dev_bf16(c.kv_cache), dev_i32(c.topk)
+    batch = (dev_i32(c.cu_seqlens), dev_i32(c.kv_lens), dev_i32(c.q_pos_start), dev_i32(c.block_table),
+             c.page_size)
+    og, lg, bufs = routings.grouped_varlen(q, kv, tk, batch, c.scale, max_groups=c.max_groups())
+    op, lp, ws = routings.pertoken_varlen(q, kv, tk, batch, c.scale)
+    torch.cuda.synchronize()
+    args = (c.cu_seqlens, c.kv_lens, c.q_pos_start, c.block_table, c.page_size)
+    groups = oracle.varlen_groups(c.cu_seqlens, c.G)
+    rng = np.random.default_rng(3)
+    pick = sorted(set([0, 255, 256, len(groups) - 1]) | set(rng.choice(len(groups), 28, replace=False).tolist()))
+    print(f"[paged] union oracle on {len(pick)} groups, attention on their tokens", flush=True)
+    info, ui, ul, mk = (x.cpu().numpy() for x in (bufs.group_info, bufs.union_idx, bufs.union_len, bufs.mask))
+    toks = []
+    for g in pick:
+        t0, n = groups[g]
+        np.testing.assert_array_equal(info[g], (t0, n))
+        r = int(np.searchsorted(c.cu_seqlens, t0, side="right") - 1)
+        sub = (np.array([0, n]), c.kv_lens[r:r + 1], c.q_pos_start[r:r + 1] + (t0 - c.cu_seqlens[r]),
+               c.block_table[r:r + 1], c.page_size)
+        _, ui1, ul1, mk1 = oracle.group_union_mask_varlen(c.topk[t0:t0 + n], *sub, c.num_slots, c.G, 1,
+                                                          pad=ui.shape[1])
+        assert ul[g] == ul1[0]
+        np.testing.assert_array_equal(ui[g], ui1[0])
+        np.testing.assert_array_equal(mk[g], mk1[0])
+        toks.extend(range(t0, t0 + n))
+    # index conversion of request 0's first 64 tokens
+    ref_g = oracle.convert_req_index_to_global(c.topk[:64], np.array([0, 64]), c.kv_lens[:1],
+                                               c.q_pos_start[:1], c.block_table[:1], c.page_size, c.num_slots)
+    np.testing.assert_array_equal(ws[:64].cpu().numpy(), ref_g)
+    ref_out, ref_lse = oracle.pertoken_sparse_mqa_varlen(c.q, c.kv_cache, c.topk, *args, c.scale, tokens=toks)
+    idx = torch.tensor(toks, device="cuda")
+    check_attention(og[idx], lg[idx], ref_out, ref_lse, "paged grouped")
+    check_attention(op[idx], lp[idx], ref_out, ref_lse, "paged per-token")
