@@ -100,7 +100,7 @@ def algorithmic_work(case, union_len_sum, mha_case):
 
 
 KERNEL_SYMBOLS = {  # bench kernel name -> (device symbol, sources)
-    "build_union": ("dsa::build_union_kernel", ["union_builder.hip", "common.h"]),
+    "build_union": ("dsa::build_union_kernel<false>", ["union_builder.hip", "common.h"]),
     "grouped_attn": ("dsa::rows128_attn_kernel<false>", ["grouped_attn.hip", "common.h"]),
     "pertoken_attn": ("dsa::pertoken_sorted_kernel", ["pertoken_attn.hip", "common.h"]),
     "masked_mha_routing": ("dsa::masked_mha_kernel<256>", ["masked_mha.hip", "common.h"]),
