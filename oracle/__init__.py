@@ -8,6 +8,7 @@ from .dsa_oracle import (  # noqa: F401
     UNION_BLOCK,
     bf16_to_f64,
     convert_req_index_to_global,
+    dense_causal_mha,
     group_union_mask,
     group_union_mask_varlen,
     grouped_sparse_mqa,

@@ -11,7 +11,9 @@ bitmap tricks appear here.  Pages cited:
 
 * [MASKED] "[2/N][Attention] Enable masked MHA for sparse MLA prefills"
   (vllm-project/vllm PR #48770) -- Purpose section: below a length threshold a
-  masked MHA simulates DSA (mask = causal AND top-k membership).
+  masked MHA simulates DSA (mask = causal AND top-k membership); for chunks no
+  longer than the top-k every causal key is selected and a plain causal MHA
+  (the dense shortcut) gives the same result.
 * [NOPE] "[Perf][GLM-5.3-Flash] Dense/masked-MHA sparse prefill for the NoPE
   (256, 0, 256) layout + skip the NoPE K concat" (vllm-project/vllm PR #55738)
   -- commit messages (K is k_nope itself when the rope part is empty; K is
@@ -238,6 +240,34 @@ def masked_mha(q: np.ndarray, k_nope: np.ndarray, k_pe: Optional[np.ndarray],
             total = e.sum()
             out[n, h] = (e @ vv[:, h, :]) / total
             lse[n, h] = m + math.log(total)
+    return out, lse
+
+
+def dense_causal_mha(q: np.ndarray, k_nope: np.ndarray, k_pe: Optional[np.ndarray],
+                     v: np.ndarray, S: int, q_pos_offset: int, scale: float,
+                     tokens: Optional[Iterable[int]] = None):
+    """Plain causal MHA: token t attends over every key x <= q_pos_offset + t (x < S).
+
+    [MASKED] Purpose: the dense shortcut for chunks no longer than the top-k,
+    where every causal key is selected.  Layouts as ``masked_mha``.
+    """
+    T, H, _ = q.shape
+    scale = _as_scale(scale)
+    toks = _tokens(T, tokens)
+    kn = bf16_to_f64(k_nope[:S])
+    kp = bf16_to_f64(k_pe[:S]) if k_pe is not None and k_pe.shape[-1] > 0 else None
+    vv = bf16_to_f64(v[:S])
+    out = np.zeros((toks.size, H, v.shape[2]))
+    lse = np.full((toks.size, H), -np.inf)
+    for n, t in enumerate(toks):
+        last = min(q_pos_offset + int(t), S - 1)   # keys 0 .. last
+        qt = bf16_to_f64(q[t])
+        for h in range(H):
+            K = kn[: last + 1, h, :]
+            if kp is not None:
+                K = np.concatenate([K, kp[: last + 1]], axis=1)
+            o, l = softmax_attention(qt[h][None], K, vv[: last + 1, h, :], scale)
+            out[n, h], lse[n, h] = o[0], l[0]
     return out, lse
 
 

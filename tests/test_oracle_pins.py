@@ -330,6 +330,64 @@ def test_masked_mha_equals_pertoken_when_heads_share_kv():
 
 
 # ---------------------------------------------------------------------------
+# dense causal MHA (the shortcut for chunks no longer than the top-k)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dr,P0", [(0, 0), (5, 7), (5, 40)])
+def test_dense_mha_matches_torch_sdpa(dr, P0):
+    # causal mask with the chunk offset built from torch.tril; P0 = 40 puts the
+    # last positions past S - 1 (they see every key)
+    rng = np.random.default_rng(50 + dr + P0)
+    T, S, H, dn, dv = 21, 33, 3, 9, 6
+    q = normal_bf16(rng, (T, H, dn + dr))
+    kn = normal_bf16(rng, (S, H, dn))
+    kp = normal_bf16(rng, (S, dr)) if dr else None
+    v = normal_bf16(rng, (S, H, dv))
+    out, lse = oracle.dense_causal_mha(q, kn, kp, v, S, P0, 0.35)
+    qt = to_t64(q).transpose(0, 1)
+    K = to_t64(kn).transpose(0, 1)
+    if dr:
+        K = torch.cat([K, to_t64(kp)[None].expand(H, S, dr)], dim=-1)
+    V = to_t64(v).transpose(0, 1)
+    allow = torch.ones(T, S, dtype=torch.bool).tril(P0)
+    sc = float(np.float32(0.35))
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, K, V, attn_mask=allow[None], scale=sc)
+    logits = (qt @ K.transpose(1, 2) * sc).masked_fill(~allow[None], -math.inf)
+    np.testing.assert_allclose(out, ref.transpose(0, 1).numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(lse, torch.logsumexp(logits, -1).transpose(0, 1).numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("P0", [0, 6])
+def test_dense_mha_equals_masked_when_topk_covers_the_chunk(P0):
+    # the shortcut's premise: with q_pos_offset + T <= k every causal key is in the top-k
+    rng = np.random.default_rng(60 + P0)
+    T, H, d = 18, 2, 8
+    S = P0 + T
+    q = normal_bf16(rng, (T, H, d))
+    kn = normal_bf16(rng, (S, H, d))
+    v = normal_bf16(rng, (S, H, d))
+    topk = topk_uniform(rng, T, S, S, S + 3, P0)   # every causal position, shuffled, -1 padded
+    om, lm = oracle.masked_mha(q, kn, None, v, topk, S, P0, 0.5)
+    od, ld = oracle.dense_causal_mha(q, kn, None, v, S, P0, 0.5)
+    np.testing.assert_allclose(od, om, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ld, lm, rtol=1e-12, atol=1e-13)
+
+
+def test_dense_mha_first_position_sees_one_key():
+    rng = np.random.default_rng(63)
+    T = S = 5
+    H, d = 2, 4
+    q = normal_bf16(rng, (T, H, d))
+    kn = normal_bf16(rng, (S, H, d))
+    v = normal_bf16(rng, (S, H, d))
+    out, lse = oracle.dense_causal_mha(q, kn, None, v, S, 0, 0.25, tokens=[0])
+    qq, kk, vv = (oracle.bf16_to_f64(a) for a in (q, kn, v))
+    np.testing.assert_array_equal(out[0], vv[0])
+    sc = float(np.float32(0.25))
+    np.testing.assert_allclose(lse[0], sc * np.einsum("hd,hd->h", qq[0], kk[0]), rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
 # batches of requests over a paged KV cache
 # ---------------------------------------------------------------------------
 
