@@ -41,6 +41,7 @@ WORKLOADS = {
     # a batch of 8 requests (2048 query tokens after 14336 positions of context each) over a
     # paged cache (64-row pages in a random physical order): the two MQA routings
     "glm16k_paged": (None, None),
+    "crossover": (None, None),
     "glm16k_uniform": ("c3w_glm16k_uniform", None),
     "long32k": ("c5_long", None),
     "dsv32": ("c2_dsv32", None),
@@ -54,6 +55,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="glm16k", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
+    ap.add_argument("--heads", default="16,32,64,128", help="crossover: heads per GPU")
+    ap.add_argument("--lengths", default="1024,2048,4096,8192,16384,32768",
+                    help="crossover: chunk lengths (T = S, starting at position 0)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (calibrates HBM byte counters)")
@@ -103,7 +107,7 @@ KERNEL_SYMBOLS = {  # bench kernel name -> (device symbol, sources)
     "build_union": ("dsa::build_union_kernel<false>", ["union_builder.hip", "common.h"]),
     "grouped_attn": ("dsa::rows128_attn_kernel<false>", ["grouped_attn.hip", "common.h"]),
     "pertoken_attn": ("dsa::pertoken_sorted_kernel", ["pertoken_attn.hip", "common.h"]),
-    "masked_mha_routing": ("dsa::masked_mha_kernel<256>", ["masked_mha.hip", "common.h"]),
+    "masked_mha_routing": ("dsa::masked_mha_kernel<256, false>", ["masked_mha.hip", "common.h"]),
 }
 
 
@@ -190,6 +194,9 @@ def main():
 
     if a.workload == "glm16k_paged":
         bench_paged(a)
+        return
+    if a.workload == "crossover":
+        bench_crossover(a)
         return
     mqa_name, mha_name = WORKLOADS[a.workload]
     t_gen = time.perf_counter()
@@ -455,6 +462,92 @@ def bench_paged(a):
             "per-token (index conversion + attention)": round(T / (per["pertoken_attn"] * 1e-3), 1)},
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_crossover(a):
+    """Every routing of the same chunk across lengths and head counts (the routing decision).
+
+    For each chunk length L (T = S = L from position 0, top-2048 with 8-token locality, seed
+    10 + L) and each head count H (G = 128 / H): the grouped routing (union build + attention)
+    and the per-token routing over the 576-wide latent, the masked routing (bit scatter +
+    attention) over per-head NoPE K/V (qk 256, v 256), and for L <= k the dense shortcut.
+    Values are N(0, 1) bf16 drawn on the device from a seeded generator (timing only: parity of
+    every kernel is covered by the tests).  Median over --steps timed calls after --warmup.
+    One JSON line per (H, L), then a summary line with the fastest routing per point.
+    """
+    import torch
+    from mla_prefill_amd import _lib, routings
+    from synth.gen import topk_locality
+
+    heads = [int(x) for x in a.heads.split(",")]
+    lengths = [int(x) for x in a.lengths.split(",")]
+    k = cols = 2048
+    scale = 1.0 / 16.0
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device="cuda")
+
+    def randn_bf16(shape, seed):
+        gen.manual_seed(seed)
+        return torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+    def timed(fn):
+        for _ in range(a.warmup):
+            fn()
+        ms = []
+        for _ in range(a.steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms))
+
+    summary = {}
+    for L in lengths:
+        rng = np.random.default_rng(10 + L)
+        topk = torch.from_numpy(topk_locality(rng, L, L, k, cols, 8)).cuda()
+        for H in heads:
+            G = 128 // H
+            seed = 1000 * L + H
+            q, kv = randn_bf16((L, H, 576), seed), randn_bf16((L, 576), seed + 1)
+            bufs = routings.alloc_union(L, G, cols)
+            og, lg = routings.alloc_out(L, H, 512)
+            op, lp = routings.alloc_out(L, H, 512)
+
+            def grouped():
+                _lib.dsa_build_group_union(topk, L, 0, G, bufs.union_idx, bufs.union_len, bufs.mask,
+                                           stream=stream)
+                _lib.dsa_sparse_prefill_grouped(q, kv, bufs.union_idx, bufs.union_len, bufs.mask, scale,
+                                                og, lg, stream=stream)
+
+            def pertoken():
+                _lib.dsa_sparse_prefill_pertoken(q, kv, topk, 0, scale, op, lp, stream=stream)
+
+            ms = {"grouped": timed(grouped), "per-token": timed(pertoken)}
+            del q, kv, bufs, og, lg, op, lp
+            mq, mk, mv = (randn_bf16((L, H, 256), seed + 2 + i) for i in range(3))
+            ws = torch.empty((L, (L + 31) // 32), dtype=torch.int32, device="cuda")
+            om, lm = routings.alloc_out(L, H, 256)
+
+            def masked():
+                _lib.dsa_masked_mha_prefill(mq, mk, None, mv, topk, 0, scale, ws, om, lm, stream=stream)
+
+            def dense():
+                _lib.dsa_dense_mha_prefill(mq, mk, None, mv, 0, scale, om, lm, stream=stream)
+
+            ms["masked"] = timed(masked)
+            if L <= k:
+                ms["dense"] = timed(dense)
+            del mq, mk, mv, ws, om, lm
+            torch.cuda.empty_cache()
+            best = min(ms, key=ms.get)
+            summary[f"H{H}_L{L}"] = best
+            print(json.dumps({"workload": "crossover", "H": H, "G": G, "L": L, "k": k,
+                              "ms": {r: round(v, 4) for r, v in ms.items()}, "fastest": best,
+                              "query_tokens_per_s": {r: round(L / (v * 1e-3), 1) for r, v in ms.items()}}),
+                  flush=True)
+    print(json.dumps({"workload": "crossover", "fastest": summary}), flush=True)
 
 
 if __name__ == "__main__":

@@ -17,7 +17,9 @@
  *                 head-group-mask kernel", commit message and "How" section);
  *   masked MHA -- dsa_masked_mha_prefill: dense MHA with mask = causal AND
  *                 top-k membership ("[2/N][Attention] Enable masked MHA for
- *                 sparse MLA prefills", Purpose section).
+ *                 sparse MLA prefills", Purpose section); its mask-free
+ *                 special case for chunks no longer than the top-k is
+ *                 dsa_dense_mha_prefill.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -78,6 +80,38 @@ int dsa_union_pad(int G, int cols);
 /* Bytes of the bit-packed masked-MHA workspace: T * ceil(S / 32) * 4
  * (0 for negative sizes). */
 size_t dsa_masked_mha_workspace_bytes(int T, int S);
+
+/* Routing of one chunk on MI355X ("[2/N][Attention] Enable masked MHA for
+ * sparse MLA prefills", Purpose section and its heuristic commit: a masked
+ * MHA beats the sparse MQA kernels below some sequence length, and a chunk
+ * whose tokens' top-k hold every causal key is plain causal attention).
+ *   T, S, q_pos_offset  the chunk: T query tokens at positions
+ *                       q_pos_offset .. q_pos_offset + T - 1 over S keys
+ *   H                   query heads on this GPU
+ *   k                   the indexer's top-k size
+ *   mha_available       nonzero when the caller can run the MHA forms
+ *                       (per-head K/V of a geometry dsa_masked_mha_prefill
+ *                       accepts); zero restricts the choice to grouped and
+ *                       per-token
+ * Returns one of the DSA_ROUTING_* codes:
+ *   DENSE     mha_available and q_pos_offset + T <= k;
+ *   MASKED    mha_available and the mean over the chunk of the causal key
+ *             count min(S, p_t + 1) is at most c(H) * k, with c measured on
+ *             MI355X for this library's kernels: 3.0 / 2.4 / 2.2 for H = 16 /
+ *             32 / 64 (against grouped), 1.9 for H = 128 and 3.7 for other
+ *             multiples of 16 (against per-token); any H the MQA kernels do not
+ *             take (not a multiple of 16, or above 128) routes here as well;
+ *   GROUPED   H in {16, 32, 64} (128 / H consecutive tokens per group);
+ *   PERTOKEN  otherwise (H = 128 runs per-token: a group would be one token).
+ * DSA_ERR_SHAPE for T < 0, S < 1, q_pos_offset < 0, H < 1 or k < 1;
+ * DSA_ERR_UNSUPPORTED when no routing serves H (MQA kernels need H a
+ * multiple of 16 up to 128, and mha_available is zero).  Host-only: nothing
+ * is enqueued. */
+#define DSA_ROUTING_DENSE 1
+#define DSA_ROUTING_MASKED 2
+#define DSA_ROUTING_GROUPED 3
+#define DSA_ROUTING_PERTOKEN 4
+int dsa_select_routing(int T, int S, int64_t q_pos_offset, int H, int k, int mha_available);
 
 /* Union list and per-token membership mask of every group of G consecutive
  * tokens ("[Perf][DSA] Grouped sparse prefill ...", "How" section: sorted
@@ -161,6 +195,20 @@ int dsa_masked_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint
                            const uint16_t* v, const int32_t* topk, int64_t ld, int T, int S, int H,
                            int dn, int dr, int dv, int cols, int64_t q_pos_offset, float scale,
                            uint32_t* mask_ws, uint16_t* out, float* lse, void* stream);
+
+/* Dense causal MHA, the shortcut for chunks no longer than the top-k ("[2/N]
+ * [Attention] Enable masked MHA for sparse MLA prefills", Purpose section:
+ * when every causal key is among a token's top-k, the selection is the causal
+ * mask and sparse attention is plain causal attention).  Token t, head h
+ * attends over every key x <= q_pos_offset + t (x < S).  It equals
+ * dsa_masked_mha_prefill whenever each token's top-k row holds all of its
+ * causal positions, i.e. whenever q_pos_offset + T <= the top-k size; the
+ * caller decides when that holds -- no top-k is read here.  Geometries,
+ * layouts, alignment and errors as dsa_masked_mha_prefill (without topk and
+ * mask_ws).  One kernel is enqueued. */
+int dsa_dense_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_pe,
+                          const uint16_t* v, int T, int S, int H, int dn, int dr, int dv,
+                          int64_t q_pos_offset, float scale, uint16_t* out, float* lse, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Batches of requests over a paged KV cache ("[Perf][DSA] Grouped sparse

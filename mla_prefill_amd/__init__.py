@@ -12,7 +12,7 @@ not been built (``python -m mla_prefill_amd.build``).
 _BINDING_NAMES = (
     "dsa_abi_version", "dsa_status_string", "dsa_union_pad", "dsa_masked_mha_workspace_bytes",
     "dsa_build_group_union", "dsa_sparse_prefill_grouped", "dsa_sparse_prefill_pertoken",
-    "dsa_masked_mha_prefill", "DsaError",
+    "dsa_masked_mha_prefill", "dsa_dense_mha_prefill", "DsaError",
 )
 
 

@@ -30,6 +30,7 @@ _SIGNATURES = {
     "dsa_status_string": ([_i32], ctypes.c_char_p),
     "dsa_union_pad": ([_i32, _i32], _i32),
     "dsa_masked_mha_workspace_bytes": ([_i32, _i32], _sz),
+    "dsa_select_routing": ([_i32, _i32, _i64, _i32, _i32, _i32], _i32),
     "dsa_build_group_union": ([_vp, _i64, _i32, _i32, _i32, _i64, _i32, _i32, _vp, _vp, _vp, _vp], _i32),
     "dsa_sparse_prefill_grouped": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                     _vp, _vp, _vp], _i32),
@@ -37,6 +38,8 @@ _SIGNATURES = {
                                      _vp, _vp, _vp], _i32),
     "dsa_masked_mha_prefill": ([_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                 _i64, _f32, _vp, _vp, _vp, _vp], _i32),
+    "dsa_dense_mha_prefill": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32,
+                               _vp, _vp, _vp], _i32),
     "dsa_varlen_group_bound": ([_i32, _i32, _i32], _i32),
     "dsa_convert_req_index_to_global": ([_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
                                          _vp, _vp], _i32),
@@ -120,6 +123,17 @@ def dsa_masked_mha_workspace_bytes(T: int, S: int) -> int:
     return lib.dsa_masked_mha_workspace_bytes(T, S)
 
 
+ROUTING_NAMES = {1: "dense", 2: "masked", 3: "grouped", 4: "per-token"}
+
+
+def dsa_select_routing(T: int, S: int, q_pos_offset: int, H: int, k: int, mha_available: bool) -> str:
+    """Name of the routing the library picks for one chunk ("dense", "masked", "grouped" or
+    "per-token")."""
+    r = lib.dsa_select_routing(T, S, q_pos_offset, H, k, int(bool(mha_available)))
+    _check("dsa_select_routing", min(r, 0))
+    return ROUTING_NAMES[r]
+
+
 def dsa_build_group_union(topk, S, q_pos_offset, G, union_idx, union_len, head_group_mask,
                           cols=None, stream=None):
     T = topk.shape[0]
@@ -159,6 +173,16 @@ def dsa_masked_mha_prefill(q, k_nope, k_pe, v, topk, q_pos_offset, scale, mask_w
         _ptr(_bits(q)), _ptr(_bits(k_nope)), _ptr(_bits(k_pe)), _ptr(_bits(v)), _ptr(topk),
         _topk_ld(topk), T, S, H, dn, dr, dv, cols, q_pos_offset, scale, _ptr(mask_ws),
         _ptr(_bits(out)), _ptr(lse), _stream(stream)))
+
+
+def dsa_dense_mha_prefill(q, k_nope, k_pe, v, q_pos_offset, scale, out, lse, stream=None):
+    T, H, dqk = q.shape
+    S, _, dn = k_nope.shape
+    dr = 0 if k_pe is None else k_pe.shape[-1]
+    dv = v.shape[2]
+    _check("dsa_dense_mha_prefill", lib.dsa_dense_mha_prefill(
+        _ptr(_bits(q)), _ptr(_bits(k_nope)), _ptr(_bits(k_pe)), _ptr(_bits(v)), T, S, H, dn, dr, dv,
+        q_pos_offset, scale, _ptr(_bits(out)), _ptr(lse), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

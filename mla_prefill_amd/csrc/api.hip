@@ -1,6 +1,7 @@
 // C-ABI host layer of libdsa_prefill.so: argument checks, then kernel launches
 // on the caller's stream.  Nothing here allocates, frees or synchronizes.
 #include <limits.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "dsa_prefill.h"
@@ -54,6 +55,43 @@ int dsa_union_pad(int G, int cols) {
   const long long v = ((long long)G * cols + 63) / 64 * 64;
   if (v > INT_MAX) return DSA_ERR_SHAPE;
   return (int)v;
+}
+
+// Routing choice for one chunk ("[2/N][Attention] Enable masked MHA for sparse MLA prefills",
+// Purpose section and its heuristic commit: below some length the masked MHA beats the sparse
+// MQA kernels, and a chunk no longer than the top-k needs no mask at all).  The thresholds
+// are MI355X measurements of this library's kernels: chunks of L tokens from position 0 with
+// top-2048 (8-token locality), per-head NoPE K/V (qk 256, v 256) for the MHA forms and the
+// 576-wide latent for the MQA forms.  Masked and sparse times cross where the mean number of
+// causal keys per query token reaches c * k: with the grouped routing c = 3.0 (H 16), 2.4 (32),
+// 2.2 (64); against per-token c = 1.9 at H 128 (G = 1: per-token runs the 128-row kernel) and
+// about 3.7 for the other head counts, which have no grouped form.
+int dsa_select_routing(int T, int S, int64_t q_pos_offset, int H, int k, int mha_available) {
+  if (T < 0 || S < 1 || q_pos_offset < 0 || H < 1 || k < 1) return DSA_ERR_SHAPE;
+  const bool mqa_ok = H % 16 == 0 && H <= 128;
+  const bool grouped_ok = mqa_ok && 128 % H == 0 && H < 128;
+  if (!mqa_ok && !mha_available) return DSA_ERR_UNSUPPORTED;
+  if (mha_available && q_pos_offset + (int64_t)T <= k) return DSA_ROUTING_DENSE;
+  if (mha_available) {
+    if (!mqa_ok) return DSA_ROUTING_MASKED;
+    // mean over the chunk of min(S, p_t + 1), p_t = q_pos_offset + t
+    const double first = (double)q_pos_offset + 1.0;
+    double sum;
+    if (first >= (double)S) {
+      sum = (double)T * S;
+    } else {
+      const double n = fmin((double)T, (double)S - first + 1.0);  // tokens below the cap
+      sum = n * first + n * (n - 1.0) / 2.0 + ((double)T - n) * S;
+    }
+    const double mean = T > 0 ? sum / T : 0.0;
+    double c;
+    if (grouped_ok)
+      c = H == 16 ? 3.0 : (H == 32 ? 2.4 : 2.2);
+    else
+      c = H == 128 ? 1.9 : 3.7;
+    if (mean <= c * k) return DSA_ROUTING_MASKED;
+  }
+  return grouped_ok ? DSA_ROUTING_GROUPED : DSA_ROUTING_PERTOKEN;
 }
 
 size_t dsa_masked_mha_workspace_bytes(int T, int S) {
@@ -239,6 +277,22 @@ int dsa_masked_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint
   return launch_status(dsa::launch_masked_mha(q, k_nope, rope ? k_pe : nullptr, dn, v, mask_ws, words, T,
                                               S, H, q_pos_offset, scale, out, lse,
                                               (hipStream_t)stream));
+}
+
+int dsa_dense_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_pe,
+                          const uint16_t* v, int T, int S, int H, int dn, int dr, int dv,
+                          int64_t q_pos_offset, float scale, uint16_t* out, float* lse, void* stream) {
+  const bool nope = dn == 256 && dr == 0 && dv == 256;
+  const bool rope = dn == 192 && dr == 64 && dv == 256;
+  if ((!nope && !rope) || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
+  if (H < 1 || T < 0 || S < 1 || q_pos_offset < 0) return DSA_ERR_SHAPE;
+  if (T == 0) return DSA_OK;
+  if (!q || !k_nope || !v || !out || !lse || (rope && !k_pe)) return DSA_ERR_NULL;
+  if (!aligned_to(q, 16) || !aligned_to(k_nope, 16) || !aligned_to(v, 16) ||
+      !aligned_to(out, 16) || !aligned_to(lse, 4) || (rope && !aligned_to(k_pe, 16)))
+    return DSA_ERR_ALIGN;
+  return launch_status(dsa::launch_masked_mha(q, k_nope, rope ? k_pe : nullptr, dn, v, nullptr, 0, T, S,
+                                              H, q_pos_offset, scale, out, lse, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -55,7 +55,9 @@ static_assert(kMStageBytes == 1024 * kMWaves * kMCopiesPerWave, "copies split ev
 
 // kDN: the k_nope width (256: NoPE layout, K = k_nope; 192: K = k_nope || k_pe with the
 // 64-wide k_pe shared by all heads); the query/key width is 256 either way.
-template <int kDN>
+// kDense: plain causal attention (every causal key selected): no mask words are copied and
+// tiles below the diagonal of all of a wave's rows skip the select.
+template <int kDN, bool kDense>
 __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ kpe,
     const uint16_t* __restrict__ v, const uint32_t* __restrict__ bits, int words, int T, int S,
@@ -64,7 +66,8 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
   constexpr int kDR = kMD - kDN;
   static_assert(kDN % 64 == 0 && kDR >= 0, "k_nope covers whole 128-byte blocks of the key row");
   __shared__ __align__(16) uint8_t stage[kMStages][kMStageBytes];
-  __shared__ __align__(16) uint32_t maskw[kMStages][kMWaves][64];
+  __shared__ __align__(16) uint32_t maskw[kDense ? 1 : kMStages][kMWaves][64];
+  constexpr int kOps = kDense ? kMCopiesPerWave : kMOpsPerTile;  // copies per wave per tile
   __shared__ __align__(16) uint4 qlds[kMWaves][kMQLdsSteps][64];
 
   // longest query tiles first; consecutive blocks take consecutive heads, so the
@@ -140,7 +143,8 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
       const bool from_pe = kDR > 0 && wave < 4 && 64 * c >= kDN;
       dma16((from_pe ? psrc : src) + 64 * c, dst + 1024 * c);
     }
-    dma4(bits + (size_t)mrow * words + ((t * kMKeys) >> 5), lds_addr(&maskw[t % kMStages][wave][0]));
+    if constexpr (!kDense)
+      dma4(bits + (size_t)mrow * words + ((t * kMKeys) >> 5), lds_addr(&maskw[t % kMStages][wave][0]));
   };
 
   float m_run = kNegInf, l_run = 0.f;  // m_run: reference max of the exponents (log2 units)
@@ -163,7 +167,7 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
   if (ntiles > 1) issue(1);
   for (int t = 0; t < ntiles; ++t) {
     if (t + 1 < ntiles)
-      wait_vmcnt<kMOpsPerTile>();
+      wait_vmcnt<kOps>();
     else
       wait_vmcnt<0>();
     __syncthreads();  // tile t visible to all waves; stage (t + 2) % 3 free
@@ -206,23 +210,31 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
     // sacc[j] = raw score(key k0 + 8 (j / 4) + 4 hi + j % 4, row)
 
     // allowed keys: top-k bit AND key <= position; bit kk <-> key k0 + 4 hi + kk
-    uint32_t allowed = *reinterpret_cast<const uint32_t*>(
-                           reinterpret_cast<const uint8_t*>(&maskw[0][wave][m]) +
-                           loop_local((t % kMStages) * (int)sizeof(maskw[0]))) >> (4 * hi);
     const int lim = rpos - k0 - 4 * hi;
-    allowed &= lim >= 31 ? 0xffffffffu : (lim < 0 ? 0u : ((2u << lim) - 1u));
+    const uint32_t causal = lim >= 31 ? 0xffffffffu : (lim < 0 ? 0u : ((2u << lim) - 1u));
     float mt = kNegInf;
+    if (kDense && ballot(lim < 31) == 0) {
+      // every key of the tile is causal for every row of the wave
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int kk = 8 * (j >> 2) + (j & 3);
-      const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)allowed, kk, 1);  // all ones if allowed
-      // (the element goes through a scalar first: a bit cast applied directly to a
-      // vector element reads element 0 with this compiler)
-      const float raw = sacc[j];
-      const float val = __builtin_bit_cast(float, (sel & __builtin_bit_cast(uint32_t, raw)) |
-                                                      (~sel & 0xff800000u));
-      sacc[j] = val;
-      mt = fmaxf(mt, val);
+      for (int j = 0; j < 16; ++j) mt = fmaxf(mt, sacc[j]);
+    } else {
+      uint32_t allowed = causal;
+      if constexpr (!kDense)
+        allowed &= *reinterpret_cast<const uint32_t*>(
+                       reinterpret_cast<const uint8_t*>(&maskw[0][wave][m]) +
+                       loop_local((t % kMStages) * (int)sizeof(maskw[0]))) >> (4 * hi);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int kk = 8 * (j >> 2) + (j & 3);
+        const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)allowed, kk, 1);  // all ones if allowed
+        // (the element goes through a scalar first: a bit cast applied directly to a
+        // vector element reads element 0 with this compiler)
+        const float raw = sacc[j];
+        const float val = __builtin_bit_cast(float, (sel & __builtin_bit_cast(uint32_t, raw)) |
+                                                        (~sel & 0xff800000u));
+        sacc[j] = val;
+        mt = fmaxf(mt, val);
+      }
     }
     mt = max_xor32(mt) * sc;
     // lazy rescale: move the reference max only when this tile exceeds it by > 2^8
@@ -289,18 +301,33 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
     lse[(size_t)row * H + h] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
 }
 
+template <int kDN, bool kDense>
+static void launch_mha(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_pe,
+                       const uint16_t* v, const uint32_t* bits, int words, int T, int S, int H,
+                       int64_t q_pos_offset, float scale, uint16_t* out, float* lse, hipStream_t stream) {
+  const long long blocks = (long long)((T + kMQ - 1) / kMQ) * H;
+  hipLaunchKernelGGL((masked_mha_kernel<kDN, kDense>), dim3((unsigned)blocks), dim3(kMThreads), 0, stream,
+                     q, k_nope, k_pe, v, bits, words, T, S, H, q_pos_offset, scale * kLog2e, out, lse);
+}
+
 hipError_t launch_masked_mha(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_pe, int dn,
                              const uint16_t* v, const uint32_t* bits, int words, int T, int S, int H,
                              int64_t q_pos_offset, float scale, uint16_t* out, float* lse,
                              hipStream_t stream) {
-  const long long blocks = (long long)((T + kMQ - 1) / kMQ) * H;
-  if (blocks == 0) return hipSuccess;
-  if (dn == 192)
-    hipLaunchKernelGGL(masked_mha_kernel<192>, dim3((unsigned)blocks), dim3(kMThreads), 0, stream, q,
-                       k_nope, k_pe, v, bits, words, T, S, H, q_pos_offset, scale * kLog2e, out, lse);
-  else
-    hipLaunchKernelGGL(masked_mha_kernel<256>, dim3((unsigned)blocks), dim3(kMThreads), 0, stream, q,
-                       k_nope, k_pe, v, bits, words, T, S, H, q_pos_offset, scale * kLog2e, out, lse);
+  if (T <= 0 || H <= 0) return hipSuccess;
+  // no membership bits: every causal key is selected (plain causal attention)
+  const bool dense = bits == nullptr;
+  if (dn == 192) {
+    if (dense)
+      launch_mha<192, true>(q, k_nope, k_pe, v, bits, words, T, S, H, q_pos_offset, scale, out, lse, stream);
+    else
+      launch_mha<192, false>(q, k_nope, k_pe, v, bits, words, T, S, H, q_pos_offset, scale, out, lse, stream);
+  } else {
+    if (dense)
+      launch_mha<256, true>(q, k_nope, k_pe, v, bits, words, T, S, H, q_pos_offset, scale, out, lse, stream);
+    else
+      launch_mha<256, false>(q, k_nope, k_pe, v, bits, words, T, S, H, q_pos_offset, scale, out, lse, stream);
+  }
   return hipGetLastError();
 }
 

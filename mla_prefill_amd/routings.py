@@ -76,6 +76,14 @@ def masked_mha(q, k_nope, k_pe, v, topk, q_pos_offset: int, scale: float, mask_w
     return out, lse, mask_ws
 
 
+def dense_mha(q, k_nope, k_pe, v, q_pos_offset: int, scale: float, out=None, lse=None, stream=None):
+    T, H, _ = q.shape
+    if out is None:
+        out, lse = alloc_out(T, H, v.shape[2], q.device)
+    _lib.dsa_dense_mha_prefill(q, k_nope, k_pe, v, q_pos_offset, scale, out, lse, stream=stream)
+    return out, lse
+
+
 # ---------------------------------------------------------------------------
 # batches of requests over a paged KV cache; `batch` = (cu_seqlens_q, kv_lens,
 # q_pos_start, block_table, page_size), int32 device tensors and an int

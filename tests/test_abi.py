@@ -148,6 +148,25 @@ def test_masked_mha_validation(lib):
     assert mha_call(lib, kn=P + 2) == ALIGN and mha_call(lib, ws=P + 2) == ALIGN
 
 
+def dense_call(lib, q=P, kn=P, kp=None, v=P, T=4, S=8, H=2, dn=256, dr=0, dv=256, p0=0, scale=0.1,
+               out=P, lse=P):
+    return lib.dsa_dense_mha_prefill(q, kn, kp, v, T, S, H, dn, dr, dv, p0, scale, out, lse, None)
+
+
+def test_dense_mha_validation(lib):
+    assert dense_call(lib, dn=192, dr=64) == NULL
+    assert dense_call(lib, dn=192, dr=64, kp=P + 2) == ALIGN
+    assert dense_call(lib, dn=192, dr=64, kp=P, T=0) == OK
+    assert dense_call(lib, dn=256, dr=64) == UNSUP and dense_call(lib, dv=128) == UNSUP
+    assert dense_call(lib, H=0) == SHAPE and dense_call(lib, S=0) == SHAPE and dense_call(lib, p0=-1) == SHAPE
+    assert dense_call(lib, T=0) == OK
+    for kw in ("q", "kn", "v", "out", "lse"):
+        assert dense_call(lib, **{kw: None}) == NULL
+    assert dense_call(lib, q=P + 2) == ALIGN and dense_call(lib, lse=P + 2) == ALIGN
+    for bad in (0.0, float("nan")):
+        assert dense_call(lib, scale=bad) == UNSUP
+
+
 def test_scale_must_be_finite_and_nonzero(lib):
     for bad in (0.0, -0.0, float("inf"), float("-inf"), float("nan")):
         assert grouped_call(lib, scale=bad) == UNSUP

@@ -104,6 +104,29 @@ def test_masked_mha_full(name):
         np.testing.assert_array_equal(wsn[t], row)
 
 
+def test_dense_mha_full():
+    """The dense shortcut at its limit, a 2048-token chunk with k = 2048 (16 heads, NoPE
+    256): sampled tokens against the oracle, and every output bit-equal to the masked
+    kernel's with each token's top-k holding all of its causal keys."""
+    from mla_prefill_amd import routings
+    from synth.gen import normal_bf16, topk_uniform
+    T = S = 2048
+    H = 16
+    rng = np.random.default_rng(8)
+    qn, kn, vn = (normal_bf16(rng, (T, H, 256)) for _ in range(3))
+    topk = topk_uniform(rng, T, S, 2048, 2048)
+    q, k, v = dev_bf16(qn), dev_bf16(kn), dev_bf16(vn)
+    od, ld = routings.dense_mha(q, k, None, v, 0, 1.0 / 16.0)
+    om, lm, _ = routings.masked_mha(q, k, None, v, dev_i32(topk), 0, 1.0 / 16.0)
+    torch.cuda.synchronize()
+    assert torch.equal(od, om) and torch.equal(ld, lm)
+    toks = sample_tokens(T, 8, n_random=16, seed=2)
+    print(f"[dense 2048] causal oracle on {len(toks)} sampled tokens", flush=True)
+    ref_out, ref_lse = oracle.dense_causal_mha(qn, kn, None, vn, S, 0, 1.0 / 16.0, tokens=toks)
+    idx = torch.tensor(toks, device="cuda")
+    check_attention(od[idx], ld[idx], ref_out, ref_lse, "dense MHA 2048")
+
+
 def test_paged_batch_full():
     """The benchmark's paged batch (8 requests x 2048 query tokens after 14336 positions of
     context, 64-row pages shuffled over a 135168-row cache): union, mask and group table of

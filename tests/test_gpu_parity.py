@@ -238,6 +238,51 @@ def test_masked_mha_parity(R, case):
     np.testing.assert_array_equal(ws.cpu().numpy().view(np.uint32), bits)
 
 
+DENSE_CASES = [
+    # (label, seed, T, S, H, P0, dn, dr)
+    ("causal_two_tiles", 30, 300, 300, 2, 0, 256, 0),
+    ("chunked_ctx", 31, 100, 230, 3, 130, 256, 0),
+    ("positions_past_S", 32, 70, 90, 1, 60, 256, 0),
+    ("rope_causal", 33, 280, 280, 2, 0, 192, 64),
+    ("rope_chunked_ctx", 34, 90, 300, 2, 210, 192, 64),
+]
+
+
+@pytest.mark.parametrize("case", DENSE_CASES, ids=[c[0] for c in DENSE_CASES])
+def test_dense_mha_parity(R, case):
+    label, seed, T, S, H, P0, dn, dr = case
+    rng = np.random.default_rng(seed)
+    q = normal_bf16(rng, (T, H, dn + dr))
+    kn = normal_bf16(rng, (S, H, dn))
+    kp = normal_bf16(rng, (S, dr)) if dr else None
+    v = normal_bf16(rng, (S, H, 256))
+    scale = 1.0 / 16.0
+    out, lse = R.dense_mha(dev_bf16(q), dev_bf16(kn), None if kp is None else dev_bf16(kp), dev_bf16(v),
+                           P0, scale)
+    ref_out, ref_lse = oracle.dense_causal_mha(q, kn, kp, v, S, P0, scale)
+    check_attention(out, lse, ref_out, ref_lse, label)
+
+
+@pytest.mark.parametrize("dr", [0, 64])
+def test_dense_mha_equals_masked_when_topk_covers_the_chunk(R, dr):
+    """q_pos_offset + T <= k: both kernels do the same arithmetic on the same keys, so the
+    outputs agree bit for bit."""
+    rng = np.random.default_rng(35 + dr)
+    T, P0, H = 520, 40, 2
+    S = P0 + T
+    dn = 256 - dr
+    q = dev_bf16(normal_bf16(rng, (T, H, 256)))
+    kn = dev_bf16(normal_bf16(rng, (S, H, dn)))
+    kp = dev_bf16(normal_bf16(rng, (S, dr))) if dr else None
+    v = dev_bf16(normal_bf16(rng, (S, H, 256)))
+    topk = shuffle_rows(topk_uniform(rng, T, S, S, S, P0), 35)
+    om, lm, _ = R.masked_mha(q, kn, kp, v, dev_i32(topk), P0, 0.0625)
+    od, ld = R.dense_mha(q, kn, kp, v, P0, 0.0625)
+    torch.cuda.synchronize()
+    assert torch.equal(od, om)
+    assert torch.equal(ld, lm)
+
+
 def test_masked_mha_equals_pertoken_with_shared_heads(R):
     """Heads sharing K = V = X: masked MHA must equal per-token sparse attention over X."""
     rng = np.random.default_rng(23)

@@ -1,0 +1,92 @@
+"""Routing choice (host logic, CPU only): the rule's boundaries, and agreement with the
+committed MI355X crossover measurements of every routing."""
+
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def pick():
+    from mla_prefill_amd import _lib
+    return _lib.dsa_select_routing
+
+
+def test_dense_when_the_chunk_fits_in_the_top_k(pick):
+    assert pick(1024, 1024, 0, 16, 2048, True) == "dense"
+    assert pick(2048, 2048, 0, 128, 2048, True) == "dense"
+    assert pick(1000, 2000, 1000, 16, 2048, True) == "dense"      # q_pos_offset + T = k
+    assert pick(1049, 2049, 1000, 16, 2048, True) == "masked"     # one position more
+    assert pick(1024, 1024, 0, 16, 2048, False) == "grouped"      # no MHA inputs
+
+
+def test_masked_threshold_against_grouped(pick):
+    # H 16: c = 3.0, k = 2048 -> mean causal keys <= 6144; a chunk from 0 has mean (L + 1) / 2
+    assert pick(12287, 12287, 0, 16, 2048, True) == "masked"
+    assert pick(12289, 12289, 0, 16, 2048, True) == "grouped"
+    assert pick(8192, 8192, 0, 32, 2048, True) == "masked"
+    assert pick(10240, 10240, 0, 32, 2048, True) == "grouped"
+    assert pick(16384, 16384, 0, 64, 2048, True) == "grouped"
+
+
+def test_masked_threshold_against_pertoken(pick):
+    assert pick(6144, 6144, 0, 128, 2048, True) == "masked"
+    assert pick(8192, 8192, 0, 128, 2048, True) == "per-token"
+    assert pick(8192, 8192, 0, 128, 2048, False) == "per-token"
+    # H 48: no grouped form (128 % 48 != 0); c = 3.7
+    assert pick(14000, 14000, 0, 48, 2048, True) == "masked"
+    assert pick(16384, 16384, 0, 48, 2048, True) == "per-token"
+    assert pick(16384, 16384, 0, 48, 2048, False) == "per-token"
+
+
+def test_chunked_context_and_positions_past_S(pick):
+    # a long prefix: mean causal keys ~ q_pos_offset + T / 2
+    assert pick(512, 30512, 30000, 16, 2048, True) == "grouped"
+    assert pick(512, 5512, 5000, 16, 2048, True) == "masked"
+    # positions past S - 1 see S keys
+    assert pick(100, 3000, 5000, 16, 2048, True) == "masked"
+    assert pick(100, 9000, 9000, 16, 2048, True) == "grouped"
+
+
+def test_heads_only_the_mha_forms_take(pick):
+    from mla_prefill_amd import _lib
+    assert pick(8192, 8192, 0, 8, 2048, True) == "masked"
+    assert pick(1024, 1024, 0, 8, 2048, True) == "dense"
+    assert pick(8192, 8192, 0, 256, 2048, True) == "masked"
+    for H in (8, 24, 256):
+        assert _lib.lib.dsa_select_routing(8192, 8192, 0, H, 2048, 0) == -3
+
+
+def test_errors():
+    from mla_prefill_amd import _lib
+    f = _lib.lib.dsa_select_routing
+    for args in ((-1, 10, 0, 16, 2048, 1), (10, 0, 0, 16, 2048, 1), (10, 10, -1, 16, 2048, 1),
+                 (10, 10, 0, 0, 2048, 1), (10, 10, 0, 16, 0, 1)):
+        assert f(*args) == -2
+    assert f(0, 10, 0, 16, 2048, 0) == 3   # an empty chunk still names a routing (grouped)
+
+
+def measured_rows():
+    text = open(os.path.join(ROOT, "profiles", "crossover_mi355x.md")).read()
+    rows = []
+    for line in text.splitlines():
+        m = re.match(r"\|\s*(\d+)\s*\|\s*(\d+)\s*\|(.*)\|\s*([\w-]+)\s*\|$", line)
+        if m:
+            cells = [c.strip() for c in m.group(3).split("|")]
+            ms = {name: float(c) for name, c in zip(("dense", "masked", "grouped", "per-token"), cells)
+                  if c != "-"}
+            rows.append((int(m.group(1)), int(m.group(2)), ms))
+    return rows
+
+
+def test_choice_is_near_the_fastest_measured_routing(pick):
+    """At every measured point the chosen routing is the fastest or within 10 % of it."""
+    rows = measured_rows()
+    assert len(rows) >= 30
+    for H, L, ms in rows:
+        choice = pick(L, L, 0, H, 2048, True)
+        assert choice in ms, (H, L, choice)
+        assert ms[choice] <= 1.10 * min(ms.values()), (H, L, choice, ms)
