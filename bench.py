@@ -38,6 +38,7 @@ WORKLOADS = {
     # name: (MQA config, masked-MHA config or None)
     "glm16k": ("c3_glm16k", "c4_masked_nope"),
     "glm16k_rope": ("c3_glm16k", "c6_masked_rope"),
+    "glm16k_latent512": ("c7_glm16k_latent512", "c4_masked_nope"),
     # a batch of 8 requests (2048 query tokens after 14336 positions of context each) over a
     # paged cache (64-row pages in a random physical order): the two MQA routings
     "glm16k_paged": (None, None),
@@ -58,6 +59,8 @@ def parse():
     ap.add_argument("--heads", default="16,32,64,128", help="crossover: heads per GPU")
     ap.add_argument("--lengths", default="1024,2048,4096,8192,16384,32768",
                     help="crossover: chunk lengths (T = S, starting at position 0)")
+    ap.add_argument("--dqk", type=int, default=576, choices=(576, 512),
+                    help="crossover: latent width of the MQA routings")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (calibrates HBM byte counters)")
@@ -86,13 +89,14 @@ def algorithmic_work(case, union_len_sum, mha_case):
     NG = cfg.NG
     pad = -(-(cfg.G * cols) // 64) * 64
     rows_live = np.minimum(cfg.G, T - np.arange(NG) * cfg.G) * H   # live pseudo-head rows per group
+    d = cfg.d_qk   # latent width: 576 (with the rope part) or 512
     w = {
         "build_union": {"bound": "hbm", "bytes": T * cols * 4 + NG * pad * 5 + NG * 4},
         "grouped_attn": {"bound": "mfma", "flops": None},   # filled below from the union lengths
         "pertoken_attn": {"bound": "hbm",
-                          "bytes": nsel * 1152 + T * H * 576 * 2 + T * H * 512 * 2 + T * H * 4 + T * cols * 4},
+                          "bytes": nsel * 2 * d + T * H * d * 2 + T * H * 512 * 2 + T * H * 4 + T * cols * 4},
     }
-    w["grouped_attn"]["flops"] = float(np.sum(union_len_sum * rows_live)) * 2 * (576 + 512)
+    w["grouped_attn"]["flops"] = float(np.sum(union_len_sum * rows_live)) * 2 * (d + 512)
     if mha_case is not None:
         m = mha_case.cfg
         words = (m.S + 31) // 32
@@ -105,8 +109,8 @@ def algorithmic_work(case, union_len_sum, mha_case):
 
 KERNEL_SYMBOLS = {  # bench kernel name -> (device symbol, sources)
     "build_union": ("dsa::build_union_kernel<false>", ["union_builder.hip", "common.h"]),
-    "grouped_attn": ("dsa::rows128_attn_kernel<false>", ["grouped_attn.hip", "common.h"]),
-    "pertoken_attn": ("dsa::pertoken_sorted_kernel", ["pertoken_attn.hip", "common.h"]),
+    "grouped_attn": ("dsa::rows128_attn_kernel<576, false>", ["grouped_attn.hip", "common.h"]),
+    "pertoken_attn": ("dsa::pertoken_sorted_kernel<576>", ["pertoken_attn.hip", "common.h"]),
     "masked_mha_routing": ("dsa::masked_mha_kernel<256, false>", ["masked_mha.hip", "common.h"]),
 }
 
@@ -294,7 +298,8 @@ def main():
     if not a.no_cpu:
         cpu = cpu_baseline(case, mha_case, a.cpu_seconds)
 
-    config = {"workload": a.workload, "mqa": mqa_name, "T": cfg.T, "S": cfg.S, "H": cfg.H, "k": cfg.k,
+    config = {"workload": a.workload, "mqa": mqa_name, "d_qk": cfg.d_qk, "T": cfg.T, "S": cfg.S, "H": cfg.H,
+              "k": cfg.k,
               "cols": cfg.cols, "G": cfg.G, "q_pos_offset": cfg.q_pos_offset,
               "selected_rows": nsel}
     if mha_case is not None:
@@ -469,7 +474,7 @@ def bench_crossover(a):
 
     For each chunk length L (T = S = L from position 0, top-2048 with 8-token locality, seed
     10 + L) and each head count H (G = 128 / H): the grouped routing (union build + attention)
-    and the per-token routing over the 576-wide latent, the masked routing (bit scatter +
+    and the per-token routing over the latent (576 wide, or --dqk 512), the masked routing (bit scatter +
     attention) over per-head NoPE K/V (qk 256, v 256), and for L <= k the dense shortcut.
     Values are N(0, 1) bf16 drawn on the device from a seeded generator (timing only: parity of
     every kernel is covered by the tests).  Median over --steps timed calls after --warmup.
@@ -510,7 +515,7 @@ def bench_crossover(a):
         for H in heads:
             G = 128 // H
             seed = 1000 * L + H
-            q, kv = randn_bf16((L, H, 576), seed), randn_bf16((L, 576), seed + 1)
+            q, kv = randn_bf16((L, H, a.dqk), seed), randn_bf16((L, a.dqk), seed + 1)
             bufs = routings.alloc_union(L, G, cols)
             og, lg = routings.alloc_out(L, H, 512)
             op, lp = routings.alloc_out(L, H, 512)
@@ -543,7 +548,7 @@ def bench_crossover(a):
             torch.cuda.empty_cache()
             best = min(ms, key=ms.get)
             summary[f"H{H}_L{L}"] = best
-            print(json.dumps({"workload": "crossover", "H": H, "G": G, "L": L, "k": k,
+            print(json.dumps({"workload": "crossover", "H": H, "G": G, "L": L, "k": k, "d_qk": a.dqk,
                               "ms": {r: round(v, 4) for r, v in ms.items()}, "fastest": best,
                               "query_tokens_per_s": {r: round(L / (v * 1e-3), 1) for r, v in ms.items()}}),
                   flush=True)

@@ -16,8 +16,10 @@ inline int launch_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_E
 // the kernels fold the scale into exponent FMAs on raw scores: it must be finite and nonzero
 inline bool scale_ok(float s) { return s == s && s != 0.f && s - s == 0.f; }
 
-constexpr int kLatentDim = 576;
+// latent widths: 576 (512 + 64 rope dims) or 512 (no rope part); values are the first 512
+// dims of a row either way
 constexpr int kValueDim = 512;
+inline bool latent_ok(int d_qk, int d_v) { return (d_qk == 576 || d_qk == 512) && d_v == kValueDim; }
 
 // host checks of a batch description (its device contents are never errors)
 inline bool batch_shape_ok(int T, int cols, int64_t ld, int R, int64_t bt_ld, int page_size, int num_slots) {
@@ -120,7 +122,7 @@ int dsa_sparse_prefill_grouped(const uint16_t* q, const uint16_t* kv, const int3
                                int H, int S, int union_pad, int d_qk, int d_v, float scale,
                                uint16_t* out, float* lse, void* stream) {
   if (H != 16 && H != 32 && H != 64 && H != 128) return DSA_ERR_UNSUPPORTED;
-  if (d_qk != kLatentDim || d_v != kValueDim || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
+  if (!latent_ok(d_qk, d_v) || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
   if (T < 0 || S < 1 || union_pad < 0 || union_pad % 32 != 0) return DSA_ERR_SHAPE;
   if (T == 0) return DSA_OK;
   if (!q || !kv || !union_idx || !union_len || !head_group_mask || !out || !lse)
@@ -130,7 +132,7 @@ int dsa_sparse_prefill_grouped(const uint16_t* q, const uint16_t* kv, const int3
     return DSA_ERR_ALIGN;
   return launch_status(dsa::launch_grouped_attn(q, kv, union_idx, union_len, head_group_mask, T,
                                                 H, S, union_pad, scale, out, lse,
-                                                (hipStream_t)stream));
+                                                (hipStream_t)stream, nullptr, 0, d_qk));
 }
 
 int dsa_sparse_prefill_pertoken(const uint16_t* q, const uint16_t* kv, const int32_t* topk,
@@ -138,7 +140,7 @@ int dsa_sparse_prefill_pertoken(const uint16_t* q, const uint16_t* kv, const int
                                 int d_qk, int d_v, float scale, uint16_t* out, float* lse,
                                 void* stream) {
   if (H < 16 || H > 128 || H % 16 != 0) return DSA_ERR_UNSUPPORTED;
-  if (d_qk != kLatentDim || d_v != kValueDim || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
+  if (!latent_ok(d_qk, d_v) || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
   if (T < 0 || S < 1 || cols < 0 || ld < cols || q_pos_offset < 0) return DSA_ERR_SHAPE;
   if (T == 0) return DSA_OK;
   if (!q || !kv || (cols > 0 && !topk) || !out || !lse) return DSA_ERR_NULL;
@@ -148,10 +150,10 @@ int dsa_sparse_prefill_pertoken(const uint16_t* q, const uint16_t* kv, const int
   hipError_t e;
   if (H == 128)
     e = dsa::launch_pertoken_rows128(q, kv, topk, ld, T, S, cols, q_pos_offset, scale, out, lse,
-                                     (hipStream_t)stream);
+                                     (hipStream_t)stream, d_qk);
   else
     e = dsa::launch_pertoken_attn(q, kv, topk, ld, T, H, S, cols, q_pos_offset, scale, out, lse,
-                                  (hipStream_t)stream);
+                                  (hipStream_t)stream, d_qk);
   return launch_status(e);
 }
 
@@ -205,7 +207,7 @@ int dsa_sparse_prefill_grouped_varlen(const uint16_t* q, const uint16_t* kv_cach
                                       int H, int union_pad, int d_qk, int d_v, float scale,
                                       uint16_t* out, float* lse, void* stream) {
   if (H != 16 && H != 32 && H != 64 && H != 128) return DSA_ERR_UNSUPPORTED;
-  if (d_qk != kLatentDim || d_v != kValueDim || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
+  if (!latent_ok(d_qk, d_v) || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
   if (T < 0 || num_slots < 1 || max_groups < 0 || union_pad < 0 || union_pad % 32 != 0)
     return DSA_ERR_SHAPE;
   if (T == 0 || max_groups == 0) return DSA_OK;
@@ -217,7 +219,7 @@ int dsa_sparse_prefill_grouped_varlen(const uint16_t* q, const uint16_t* kv_cach
     return DSA_ERR_ALIGN;
   return launch_status(dsa::launch_grouped_attn(q, kv_cache, union_idx, union_len, head_group_mask, T, H,
                                                 num_slots, union_pad, scale, out, lse, (hipStream_t)stream,
-                                                group_info, max_groups));
+                                                group_info, max_groups, d_qk));
 }
 
 int dsa_sparse_prefill_pertoken_varlen(const uint16_t* q, const uint16_t* kv_cache, int num_slots,
@@ -227,7 +229,7 @@ int dsa_sparse_prefill_pertoken_varlen(const uint16_t* q, const uint16_t* kv_cac
                                        int64_t bt_ld, int page_size, int d_qk, int d_v, float scale,
                                        int32_t* topk_ws, uint16_t* out, float* lse, void* stream) {
   if (H < 16 || H > 128 || H % 16 != 0) return DSA_ERR_UNSUPPORTED;
-  if (d_qk != kLatentDim || d_v != kValueDim || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
+  if (!latent_ok(d_qk, d_v) || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
   if (!batch_shape_ok(T, cols, ld, R, bt_ld, page_size, num_slots)) return DSA_ERR_SHAPE;
   if (T == 0) return DSA_OK;
   if (!q || !kv_cache || !out || !lse || (cols > 0 && (!topk || !topk_ws)) ||
@@ -246,10 +248,10 @@ int dsa_sparse_prefill_pertoken_varlen(const uint16_t* q, const uint16_t* kv_cac
   const int64_t all_causal = (int64_t)num_slots - 1;
   if (H == 128)
     e = dsa::launch_pertoken_rows128(q, kv_cache, topk_ws, cols, T, num_slots, cols, all_causal, scale, out,
-                                     lse, (hipStream_t)stream);
+                                     lse, (hipStream_t)stream, d_qk);
   else
     e = dsa::launch_pertoken_attn(q, kv_cache, topk_ws, cols, T, H, num_slots, cols, all_causal, scale, out,
-                                  lse, (hipStream_t)stream);
+                                  lse, (hipStream_t)stream, d_qk);
   return launch_status(e);
 }
 

@@ -15,13 +15,14 @@
 //
 // MI355X design (one workgroup of 4 waves per group, one wave per SIMD):
 //  * wave w owns rows 32 w .. 32 w + 31 for the whole attention: their
-//    576-dim queries sit in registers as the B operand of S^T = K Q^T, and
+//    queries (576 or 512 dims: the latent with or without its 64 rope dims)
+//    sit in registers as the B operand of S^T = K Q^T, and
 //    O^T (512 columns x 32 rows) accumulates in registers, so no
 //    probabilities or rescale factors cross waves;
 //  * 32-slot tiles of latent rows stream through a 3-stage LDS ring by
 //    asynchronous global->LDS DMA, two tiles ahead of the compute, one
-//    barrier per tile.  Each wave copies one 8-row group of a tile (nine
-//    128-byte blocks per row) into the XOR-swizzled 8-row-group layout
+//    barrier per tile.  Each wave copies one 8-row group of a tile (nine or
+//    eight 128-byte blocks per row) into the XOR-swizzled 8-row-group layout
 //    (common.h), so the 16-byte K reads and the transposed V reads are free of
 //    bank conflicts.  The slot indices and membership bytes of a tile arrive
 //    by their own DMA one tile earlier; per-token membership masks then come
@@ -42,27 +43,28 @@
 
 namespace dsa {
 
-constexpr int kRDqk = 576;
 constexpr int kRDv = 512;
 constexpr int kRWaves = 4;
 constexpr int kRThreads = 64 * kRWaves;
 constexpr int kRKeys = 32;                          // slots per tile
 constexpr int kRStages = 3;
 constexpr int kRIdxBufs = 4;                        // index/membership buffers (one tile further ahead)
-constexpr int kRGroupBytes = 8 * kRDqk * 2;         // 9216: one 8-row group
-constexpr int kRStageBytes = 4 * kRGroupBytes;      // one 32-slot tile
-constexpr int kRCopies = kRGroupBytes / 1024;       // 9 row copies per wave per tile
 constexpr float kRSlack = 64.f;                     // log2 of the largest probability allowed
-constexpr int kRQRegSteps = 28;                     // query k-steps kept in registers (of 36)
-constexpr int kRQLdsSteps = kRDqk / 16 - kRQRegSteps;  // the rest sit in LDS (lane-private)
+constexpr int kRQRegSteps = 28;                     // query k-steps kept in registers
 
-template <bool kPerToken>
+// D: the latent width, 576 (512 + 64 rope dims) or 512 (no rope part)
+template <int D, bool kPerToken>
 __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ keys, int64_t keys_ld, const int32_t* __restrict__ union_len,
     const uint8_t* __restrict__ hgmask, int T, int H, int S, int ncols, int64_t q_pos_offset,
     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
     const int32_t* __restrict__ ginfo) {
+  static_assert(D == 576 || D == 512, "latent widths");
+  constexpr int kRGroupBytes = 8 * D * 2;           // one 8-row group (9216 / 8192)
+  constexpr int kRStageBytes = 4 * kRGroupBytes;    // one 32-slot tile
+  constexpr int kRCopies = kRGroupBytes / 1024;     // row copies per wave per tile (9 / 8)
+  constexpr int kRQLdsSteps = D / 16 - kRQRegSteps;  // query k-steps in LDS (lane-private)
   __shared__ __align__(16) uint8_t stage[kRStages][kRStageBytes];
   // per tile and wave: lanes 0..7 = slot indices 8 w .. 8 w + 7, lanes 8, 9 = their membership bytes
   __shared__ __align__(16) uint32_t idxw[kRIdxBufs][kRWaves][64];
@@ -91,9 +93,9 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   // operand reads in flight)
   bf16x8 qreg[kRQRegSteps];
   {
-    const uint16_t* qrow = q + ((size_t)tok * H + rh) * kRDqk + 8 * hi;
+    const uint16_t* qrow = q + ((size_t)tok * H + rh) * D + 8 * hi;
 #pragma unroll
-    for (int s = 0; s < kRDqk / 16; ++s) {
+    for (int s = 0; s < D / 16; ++s) {
       uint4 w = {0u, 0u, 0u, 0u};
       if (live) w = *reinterpret_cast<const uint4*>(qrow + 16 * s);
       w.x ^= qsign; w.y ^= qsign; w.z ^= qsign; w.w ^= qsign;
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   // membership bytes of slots 8 w .. + 3 and 8 w + 4 .. + 7 (the others repeat slot 8 w + l % 8;
   // in per-token mode the list is the top-k row, read no further than its last column).
   // Row copies of tile t: wave w fills tile rows 8 w .. 8 w + 7 (8-row group w), blocks
-  // 0..8; lane l takes row l / 8, position l % 8.
+  // 0 .. kRCopies - 1; lane l takes row l / 8, position l % 8.
   const int crow = lane >> 3;
   const int cchunk = (lane & 7) ^ swz8(crow) ^ wave;
   const uint16_t* cbase = kv + 8 * cchunk;
@@ -152,7 +154,7 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   auto issue_rows = [&](int t) {
     const int32_t x = (int32_t)idxw[t % kRIdxBufs][wave][crow];  // landed (own copy, waited for)
     const bool ok = slot_ok(x, t * kRKeys + 8 * wave + crow);
-    const uint16_t* src = cbase + (size_t)(ok ? x : 0) * kRDqk;  // invalid slots copy row 0 (masked)
+    const uint16_t* src = cbase + (size_t)(ok ? x : 0) * D;  // invalid slots copy row 0 (masked)
     const uint32_t dst = lds_addr(stage[t % kRStages]) + cdst;
     // (the global address carries the block offset: an instruction offset would also
     // move the LDS destination of an LDS-DMA load)
@@ -236,10 +238,10 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
     }
     f32x16 sacc = {};  // sacc[j] = raw score(slot 8 (j / 4) + 4 hi + j % 4, row r)
 #pragma unroll
-    for (int s = 0; s < kRDqk / 16; ++s) {
+    for (int s = 0; s < D / 16; ++s) {
       __builtin_amdgcn_sched_barrier(0);
       sacc = mfma32x32x16(kw[s % kRAhead], qw[s % kRAhead], sacc);
-      if (s + kRAhead < kRDqk / 16) {
+      if (s + kRAhead < D / 16) {
         kw[s % kRAhead] = kread(s + kRAhead);
         qw[s % kRAhead] = qread(s + kRAhead);
       }
@@ -335,30 +337,40 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
 hipError_t launch_grouped_attn(const uint16_t* q, const uint16_t* kv, const int32_t* union_idx,
                                const int32_t* union_len, const uint8_t* head_group_mask, int T,
                                int H, int S, int union_pad, float scale, uint16_t* out, float* lse,
-                               hipStream_t stream, const int32_t* group_info, int max_groups) {
+                               hipStream_t stream, const int32_t* group_info, int max_groups, int d_qk) {
   const int G = 128 / H;
   const int NG = group_info ? max_groups : (T + G - 1) / G;
   if (NG == 0) return hipSuccess;
-  hipLaunchKernelGGL(rows128_attn_kernel<false>, dim3(NG), dim3(kRThreads), 0, stream, q, kv,
-                     union_idx, (int64_t)union_pad, union_len, head_group_mask, T, H, S, union_pad,
-                     (int64_t)0, scale * kLog2e, out, lse, group_info);
+  if (d_qk == 512)
+    hipLaunchKernelGGL((rows128_attn_kernel<512, false>), dim3(NG), dim3(kRThreads), 0, stream, q, kv,
+                       union_idx, (int64_t)union_pad, union_len, head_group_mask, T, H, S, union_pad,
+                       (int64_t)0, scale * kLog2e, out, lse, group_info);
+  else
+    hipLaunchKernelGGL((rows128_attn_kernel<576, false>), dim3(NG), dim3(kRThreads), 0, stream, q, kv,
+                       union_idx, (int64_t)union_pad, union_len, head_group_mask, T, H, S, union_pad,
+                       (int64_t)0, scale * kLog2e, out, lse, group_info);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_rows128_exact(q, kv, union_idx, (int64_t)union_pad, union_len, head_group_mask, T, H,
-                              S, union_pad, 0, scale, out, lse, stream, group_info, NG);
+                              S, union_pad, 0, scale, out, lse, stream, group_info, NG, d_qk);
 }
 
 hipError_t launch_pertoken_rows128(const uint16_t* q, const uint16_t* kv, const int32_t* topk,
                                    int64_t ld, int T, int S, int cols, int64_t q_pos_offset,
-                                   float scale, uint16_t* out, float* lse, hipStream_t stream) {
+                                   float scale, uint16_t* out, float* lse, hipStream_t stream, int d_qk) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(rows128_attn_kernel<true>, dim3(T), dim3(kRThreads), 0, stream, q, kv, topk,
-                     ld, (const int32_t*)nullptr, (const uint8_t*)nullptr, T, 128, S, cols,
-                     q_pos_offset, scale * kLog2e, out, lse, (const int32_t*)nullptr);
+  if (d_qk == 512)
+    hipLaunchKernelGGL((rows128_attn_kernel<512, true>), dim3(T), dim3(kRThreads), 0, stream, q, kv, topk,
+                       ld, (const int32_t*)nullptr, (const uint8_t*)nullptr, T, 128, S, cols,
+                       q_pos_offset, scale * kLog2e, out, lse, (const int32_t*)nullptr);
+  else
+    hipLaunchKernelGGL((rows128_attn_kernel<576, true>), dim3(T), dim3(kRThreads), 0, stream, q, kv, topk,
+                       ld, (const int32_t*)nullptr, (const uint8_t*)nullptr, T, 128, S, cols,
+                       q_pos_offset, scale * kLog2e, out, lse, (const int32_t*)nullptr);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_rows128_exact(q, kv, topk, ld, nullptr, nullptr, T, 128, S, cols, q_pos_offset, scale,
-                              out, lse, stream, nullptr, T);
+                              out, lse, stream, nullptr, T, d_qk);
 }
 
 }  // namespace dsa

@@ -34,7 +34,7 @@ hipError_t launch_scatter_topk_bits(const int32_t* topk, int64_t ld, int T, int 
 // per-token sparse MQA for H % 16 == 0 (one workgroup per (token, 16-head block))
 hipError_t launch_pertoken_attn(const uint16_t* q, const uint16_t* kv, const int32_t* topk,
                                 int64_t ld, int T, int H, int S, int cols, int64_t q_pos_offset,
-                                float scale, uint16_t* out, float* lse, hipStream_t stream);
+                                float scale, uint16_t* out, float* lse, hipStream_t stream, int d_qk);
 
 // 128-row attention over a per-workgroup key list.  Grouped mode: rows are the
 // 128 pseudo-heads of a group, keys the group's union list, and each row is
@@ -44,11 +44,10 @@ hipError_t launch_pertoken_attn(const uint16_t* q, const uint16_t* kv, const int
 hipError_t launch_grouped_attn(const uint16_t* q, const uint16_t* kv, const int32_t* union_idx,
                                const int32_t* union_len, const uint8_t* head_group_mask, int T,
                                int H, int S, int union_pad, float scale, uint16_t* out, float* lse,
-                               hipStream_t stream, const int32_t* group_info = nullptr,
-                               int max_groups = 0);
+                               hipStream_t stream, const int32_t* group_info, int max_groups, int d_qk);
 hipError_t launch_pertoken_rows128(const uint16_t* q, const uint16_t* kv, const int32_t* topk,
                                    int64_t ld, int T, int S, int cols, int64_t q_pos_offset,
-                                   float scale, uint16_t* out, float* lse, hipStream_t stream);
+                                   float scale, uint16_t* out, float* lse, hipStream_t stream, int d_qk);
 
 // The fast 128-row kernel fixes each row's softmax reference at the row's first valid
 // scores.  A group in which a later score exceeds that reference by more than 2^64 gets
@@ -60,7 +59,7 @@ hipError_t launch_rows128_exact(const uint16_t* q, const uint16_t* kv, const int
                                 int64_t keys_ld, const int32_t* union_len, const uint8_t* hgmask,
                                 int T, int H, int S, int ncols, int64_t q_pos_offset, float scale,
                                 uint16_t* out, float* lse, hipStream_t stream, const int32_t* group_info,
-                                int ngroups);
+                                int ngroups, int d_qk);
 
 // masked dense MHA, qk 256 = k_nope dn (256 or 192) + shared k_pe (0 or 64), v 256,
 // mask = causal AND top-k bit; bits == nullptr: causal only (dense MHA)

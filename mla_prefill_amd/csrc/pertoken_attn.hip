@@ -1,12 +1,13 @@
-// Per-token sparse MQA prefill over the 576-wide bf16 latent.
+// Per-token sparse MQA prefill over a bf16 latent of 576 dims (512 + 64 rope) or
+// 512 dims (no rope part).
 //
 // Definition ("[Perf][GLM-5.3-Flash] Dense/masked-MHA sparse prefill for the
 // NoPE (256, 0, 256) layout ...", Purpose section; "[Perf][DSA] Grouped sparse
 // prefill ...", commit message): every query token attends, for each of its H
-// heads, over the latent rows of its own top-k selection; scores use all 576
-// dims, values are the first 512 dims of the same rows; the result is
-// out [T, H, 512] (bf16) and LSE [T, H] (fp32, natural log).  The pages find
-// this kernel bound by the KV gather (2048 rows x 1152 B per token).
+// heads, over the latent rows of its own top-k selection; scores use every dim
+// of the row, values are its first 512 dims; the result is out [T, H, 512]
+// (bf16) and LSE [T, H] (fp32, natural log).  The pages find this kernel bound
+// by the KV gather (2048 rows x 1152 B per token for the 576-wide latent).
 //
 // MI355X design: one wave per (token, 16-head block), one wave per workgroup
 // (no barriers), one wave per SIMD.  Two kernels share the arithmetic:
@@ -47,13 +48,20 @@
 
 namespace dsa {
 
-constexpr int kDqk = 576;
-constexpr int kDv = 512;
+constexpr int kDv = 512;                    // values: the first 512 dims of a latent row
 constexpr int kPKeys = 16;                  // keys per step
-constexpr int kPLoads = kDqk / 32;          // 16-byte chunks per lane per step (18)
-constexpr int kPLines = kDqk * 2 / 128;     // 128-byte lines per latent row (9)
-constexpr int kPRowBytes = kDqk * 2;        // 1152
 constexpr float kPSlack = 64.f;             // log2 of the largest probability allowed
+
+// Row geometry of latent width D: 576 (512 + 64 rope dims) or 512 (no rope part).
+template <int D>
+struct Lat {
+  static_assert(D == 576 || D == 512, "latent widths");
+  static constexpr int loads = D / 32;               // 16-byte chunks per lane per step (18 / 16)
+  static constexpr int lines = D * 2 / 128;          // 128-byte lines per latent row (9 / 8)
+  static constexpr int row_bytes = D * 2;            // 1152 / 1024
+  static constexpr int group_bytes = 8 * row_bytes;  // one 8-row group of a sorted-walk tile
+};
+constexpr int kDqkMax = 576;
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 // (a native vector: row chunks loaded into HIP's uint4 struct through a byte pointer
@@ -64,11 +72,12 @@ __device__ __forceinline__ f32x4 mfma16x16x16(s16x4_t a, s16x4_t b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-// LDS of the (single-wave) workgroup: the rows of the current step -- chunk c (16 B,
-// 0..71) of row r (0..15) at r * 1152 + 16 (c ^ tswz(r)); the XOR stays inside a
-// 128-byte line -- and the queries, lane-private: lane l's chunk s at pt_q[s][l].
-__shared__ __align__(16) uint8_t pt_tile[kPKeys * kPRowBytes];
-__shared__ __align__(16) uint4 pt_q[kPLoads][64];
+// LDS of the (single-wave) workgroup, sized for the wider latent: the rows of the current
+// step -- chunk c (16 B, 0..D/8-1) of row r (0..15) at r * 2D + 16 (c ^ tswz(r)); the XOR
+// stays inside a 128-byte line -- and the queries, lane-private: lane l's chunk s at
+// pt_q[s][l].
+__shared__ __align__(16) uint8_t pt_tile[kPKeys * Lat<kDqkMax>::row_bytes];
+__shared__ __align__(16) uint4 pt_q[Lat<kDqkMax>::loads][64];
 // sorted mode (positions < 65536, rows of at most kPSortMax columns): the token's valid
 // entries in ascending order
 constexpr int kPSortMax = 2048;
@@ -91,6 +100,7 @@ struct PtCtx {
 // The per-wave context for token `token` (built in registers; the exact routine rebuilds
 // it from the same scalars rather than taking it by reference, which would put it in
 // scratch memory for the whole kernel).
+template <int D>
 __device__ __forceinline__ PtCtx pt_context(const uint16_t* kv, const int32_t* topk, int64_t ld, int S,
                                             int cols, int64_t q_pos_offset, float scale_log2, int token) {
   PtCtx c;
@@ -114,14 +124,14 @@ __device__ __forceinline__ PtCtx pt_context(const uint16_t* kv, const int32_t* t
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int r = 8 * h + c.er;
-      c.wofs[h] = r * kPRowBytes + 16 * ((c.lane & 7) ^ tswz(r));
+      c.wofs[h] = r * Lat<D>::row_bytes + 16 * ((c.lane & 7) ^ tswz(r));
     }
 #pragma unroll
-    for (int p = 0; p < 2; ++p) c.kofs[p] = c.n * kPRowBytes + 16 * ((4 * p + c.g) ^ tswz(c.n));
+    for (int p = 0; p < 2; ++p) c.kofs[p] = c.n * Lat<D>::row_bytes + 16 * ((4 * p + c.g) ^ tswz(c.n));
     const int rr = 4 * c.g + (c.n >> 2);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      c.rofs[u] = rr * kPRowBytes + 8 * (c.n & 1) + 16 * ((2 * u + ((c.n & 3) >> 1)) ^ tswz(rr));
+      c.rofs[u] = rr * Lat<D>::row_bytes + 8 * (c.n & 1) + 16 * ((2 * u + ((c.n & 3) >> 1)) ^ tswz(rr));
   }
 
   return c;
@@ -138,15 +148,16 @@ __device__ __forceinline__ int2 pt_entries(const PtCtx& c, int j) {
 
 // start the loads of step j's rows into `buf` (buf[k]: line k of row er, buf[9 + k]: of row
 // 8 + er); returns the validity bits of the step's 16 keys (key r <-> bit r)
-__device__ __forceinline__ uint32_t pt_issue(const PtCtx& c, int2 e, int j, u32x4 (&buf)[kPLoads]) {
+template <int D>
+__device__ __forceinline__ uint32_t pt_issue(const PtCtx& c, int2 e, int j, u32x4 (&buf)[Lat<D>::loads]) {
   const bool ok0 = kPKeys * j + c.er < c.cols && e.x >= 0 && e.x <= c.pos;
   const bool ok1 = kPKeys * j + 8 + c.er < c.cols && e.y >= 0 && e.y <= c.pos;
-  const uint8_t* src0 = c.kvb + (size_t)(ok0 ? e.x : c.pos) * kPRowBytes;
-  const uint8_t* src1 = c.kvb + (size_t)(ok1 ? e.y : c.pos) * kPRowBytes;
+  const uint8_t* src0 = c.kvb + (size_t)(ok0 ? e.x : c.pos) * Lat<D>::row_bytes;
+  const uint8_t* src1 = c.kvb + (size_t)(ok1 ? e.y : c.pos) * Lat<D>::row_bytes;
 #pragma unroll
-  for (int k = 0; k < kPLines; ++k) {
+  for (int k = 0; k < Lat<D>::lines; ++k) {
     buf[k] = *reinterpret_cast<const u32x4*>(src0 + 128 * k);
-    buf[kPLines + k] = *reinterpret_cast<const u32x4*>(src1 + 128 * k);
+    buf[Lat<D>::lines + k] = *reinterpret_cast<const u32x4*>(src1 + 128 * k);
   }
   // key r's validity is that of lanes 8 (r % 8) .. + 7 (bits 8 (r % 8) of the ballots)
   const uint64_t b0 = ballot(ok0), b1 = ballot(ok1);
@@ -156,11 +167,12 @@ __device__ __forceinline__ uint32_t pt_issue(const PtCtx& c, int2 e, int j, u32x
   return v;
 }
 
-__device__ __forceinline__ void pt_store(const PtCtx& c, const u32x4 (&buf)[kPLoads]) {
+template <int D>
+__device__ __forceinline__ void pt_store(const PtCtx& c, const u32x4 (&buf)[Lat<D>::loads]) {
 #pragma unroll
-  for (int k = 0; k < kPLines; ++k) {
+  for (int k = 0; k < Lat<D>::lines; ++k) {
     *reinterpret_cast<u32x4*>(pt_tile + c.wofs[0] + 128 * k) = buf[k];
-    *reinterpret_cast<u32x4*>(pt_tile + c.wofs[1] + 128 * k) = buf[kPLines + k];
+    *reinterpret_cast<u32x4*>(pt_tile + c.wofs[1] + 128 * k) = buf[Lat<D>::lines + k];
   }
 }
 
@@ -168,6 +180,7 @@ __device__ __forceinline__ void pt_store(const PtCtx& c, const u32x4 (&buf)[kPLo
 // and query reads run kPQAhead MFMAs ahead (the order is pinned: left to itself the
 // scheduler puts every read right before its MFMA and waits out its latency).
 constexpr int kPQAhead = 4;
+template <int D>
 __device__ __forceinline__ f32x4 pt_qk(const PtCtx& c) {
   // (the query address is made opaque: hoisted out of a loop, the 18 reads would pin 72
   // registers for the whole token)
@@ -184,10 +197,10 @@ __device__ __forceinline__ f32x4 pt_qk(const PtCtx& c) {
   }
   f32x4 acc[3] = {};
 #pragma unroll
-  for (int s = 0; s < kPLoads; ++s) {
+  for (int s = 0; s < Lat<D>::loads; ++s) {
     __builtin_amdgcn_sched_barrier(0);
     acc[s % 3] = mfma16x16x32(kw[s % kPQAhead], qw[s % kPQAhead], acc[s % 3]);
-    if (s + kPQAhead < kPLoads) {
+    if (s + kPQAhead < Lat<D>::loads) {
       kw[s % kPQAhead] = kread(s + kPQAhead);
       qw[s % kPQAhead] = qread(s + kPQAhead);
     }
@@ -256,19 +269,19 @@ __device__ __forceinline__ void pt_write(int g, const f32x4 (&o)[kDv / 16], floa
 // Exact two-pass routine: head n's max over the whole row first, then the softmax
 // against it (no probability exceeds 1).  Both passes share pt_qk / pt_mask with the main
 // loop, so their scores are bit-identical.
-template <bool kSorted>
+template <int D, bool kSorted>
 __device__ __noinline__ void pt_exact(const uint16_t* kv, const int32_t* topk, int64_t ld, int S, int cols,
                                      int64_t q_pos_offset, float scale_log2, int token, uint16_t* orow,
                                      float* lse_at) {
-  const PtCtx c = pt_context(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token);
+  const PtCtx c = pt_context<D>(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token);
   const int nsteps = (c.cols + kPKeys - 1) / kPKeys;
   float m = kNegInf;
   for (int j = 0; j < nsteps; ++j) {
-    u32x4 buf[kPLoads];
-    const uint32_t vbits = pt_issue(c, pt_entries<kSorted>(c, j), j, buf);
-    pt_store(c, buf);
+    u32x4 buf[Lat<D>::loads];
+    const uint32_t vbits = pt_issue<D>(c, pt_entries<kSorted>(c, j), j, buf);
+    pt_store<D>(c, buf);
     float sv[4];
-    m = fmaxf(m, pt_mask(c, pt_qk(c), vbits, sv));
+    m = fmaxf(m, pt_mask(c, pt_qk<D>(c), vbits, sv));
   }
   m = max_over_rowgroups(m) * c.sc;
   float l = 0.f;
@@ -276,16 +289,17 @@ __device__ __noinline__ void pt_exact(const uint16_t* kv, const int32_t* topk, i
 #pragma unroll
   for (int cb = 0; cb < kDv / 16; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < nsteps; ++j) {
-    u32x4 buf[kPLoads];
-    const uint32_t vbits = pt_issue(c, pt_entries<kSorted>(c, j), j, buf);
-    pt_store(c, buf);
+    u32x4 buf[Lat<D>::loads];
+    const uint32_t vbits = pt_issue<D>(c, pt_entries<kSorted>(c, j), j, buf);
+    pt_store<D>(c, buf);
     float sv[4];
-    pt_mask(c, pt_qk(c), vbits, sv);
+    pt_mask(c, pt_qk<D>(c), vbits, sv);
     pt_pv(c, pt_probs(c, sv, m, l), o);
   }
   pt_write(c.g, o, l, m, orow, lse_at);
 }
 
+template <int D>
 __global__ __launch_bounds__(64) void pertoken_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ topk, int64_t ld, int T, int H, int S, int cols,
@@ -296,15 +310,15 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
   const int token = T - 1 - tq;
   const int hb = item - tq * nb;
 
-  const PtCtx c = pt_context(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token);
+  const PtCtx c = pt_context<D>(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token);
 
   // queries of head n, dims 32 s + 8 g .. + 8 (the B operand of S^T = K Q^T); a negative
   // scale is applied as |scale| on negated queries so the max can be taken on raw scores
   {
     const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
-    const uint16_t* qrow = q + ((size_t)token * H + hb * 16 + c.n) * kDqk + 8 * c.g;
+    const uint16_t* qrow = q + ((size_t)token * H + hb * 16 + c.n) * D + 8 * c.g;
 #pragma unroll
-    for (int s = 0; s < kPLoads; ++s) {
+    for (int s = 0; s < Lat<D>::loads; ++s) {
       uint4 w = *reinterpret_cast<const uint4*>(qrow + 32 * s);
       w.x ^= qsign; w.y ^= qsign; w.z ^= qsign; w.w ^= qsign;
       pt_q[s][c.lane] = w;
@@ -331,7 +345,7 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
   f32x4 o[kDv / 16];
 #pragma unroll
   for (int cb = 0; cb < kDv / 16; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  u32x4 ra[kPLoads], rb[kPLoads];
+  u32x4 ra[Lat<D>::loads], rb[Lat<D>::loads];
   uint32_t va = 0, vb = 0;
   int2 e_next = {0, 0};  // entries of the step whose loads start next
   {  // issue order as in the loop (entries, rows, entries, rows), pinned by scheduling
@@ -339,18 +353,18 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
     const int2 e0 = pt_entries<false>(c, 0);
     const int2 e1 = pt_entries<false>(c, 1);
     __builtin_amdgcn_sched_barrier(0);
-    va = pt_issue(c, e0, 0, ra);
+    va = pt_issue<D>(c, e0, 0, ra);
     __builtin_amdgcn_sched_barrier(0);
     e_next = pt_entries<false>(c, 2);
     __builtin_amdgcn_sched_barrier(0);
-    vb = pt_issue(c, e1, 1, rb);
+    vb = pt_issue<D>(c, e1, 1, rb);
     __builtin_amdgcn_sched_barrier(0);
   }
   // one step; `over` becomes true when a score exceeds the reference by more than the
   // slack (the loop still runs to its end, and its result is then discarded)
   bool over = false;
-  auto step = [&](int j, u32x4 (&buf)[kPLoads], uint32_t& vbuf) {
-    pt_store(c, buf);
+  auto step = [&](int j, u32x4 (&buf)[Lat<D>::loads], uint32_t& vbuf) {
+    pt_store<D>(c, buf);
     const uint32_t vbits = vbuf;
     // the refill must not be scheduled above the stores that read the buffer
     __builtin_amdgcn_sched_barrier(0);
@@ -359,11 +373,11 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
       const int2 e = e_next;
       e_next = pt_entries<false>(c, j + 3);
       __builtin_amdgcn_sched_barrier(0);
-      vbuf = pt_issue(c, e, j + 2, buf);
+      vbuf = pt_issue<D>(c, e, j + 2, buf);
     }
     __builtin_amdgcn_sched_barrier(0);
     float sv[4];
-    const float mt = pt_mask(c, pt_qk(c), vbits, sv) * c.sc;
+    const float mt = pt_mask(c, pt_qk<D>(c), vbits, sv) * c.sc;
     // a head's first valid scores set its reference (its O and l are still zero)
     if (ballot(m_ref == kNegInf && mt != kNegInf) != 0) {
       const float mh = max_over_rowgroups(mt);
@@ -377,7 +391,7 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
     step(j + 1, rb, vb);
   }
   if (over) {
-    pt_exact<false>(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token, orow, lse_at);
+    pt_exact<D, false>(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token, orow, lse_at);
     return;
   }
   pt_write(c.g, o, l_run, m_ref, orow, lse_at);
@@ -397,7 +411,6 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
 // The queries stay in registers.  The exact fallback reuses the register-ring
 // routines (the second tile is the query area there).
 // ---------------------------------------------------------------------------
-constexpr int kPGroupBytes = 8 * kPRowBytes;  // one 8-row group of a tile (9216)
 
 // returns the number of distinct valid entries of the token's row, sorted into pt_sorted
 __device__ __forceinline__ int pt_sort(const int32_t* trow, int cols, int pos, int lane) {
@@ -443,6 +456,7 @@ struct PdCtx {
   int rofs[4];  // transposed V read offsets (per column block cb % 4; + 1024 (cb / 4))
 };
 
+template <int D>
 __device__ __forceinline__ PdCtx pd_context(int pos, int cols, float scale_log2) {
   PdCtx c;
   c.lane = threadIdx.x;
@@ -459,28 +473,29 @@ __device__ __forceinline__ PdCtx pd_context(int pos, int cols, float scale_log2)
   // K reads: lane (g, n) reads row n, chunk 4 s + g
   const int kg = c.n >> 3, k8 = c.n & 7;
 #pragma unroll
-  for (int p = 0; p < 2; ++p) c.kofs[p] = kg * kPGroupBytes + 128 * k8 + 16 * ((4 * p + c.g) ^ swz8(k8) ^ kg);
+  for (int p = 0; p < 2; ++p) c.kofs[p] = kg * Lat<D>::group_bytes + 128 * k8 + 16 * ((4 * p + c.g) ^ swz8(k8) ^ kg);
   // transposed reads for block cb: lane (g, i) addresses row 4 g + i / 4, cols 16 cb + 4 (i % 4)
   // .. + 3 (chunk 2 cb + (i % 4) / 2, half i % 2): output lane (g, n) receives
   // V[key 4 g + jj][col 16 cb + n]
   const int rr = 4 * c.g + (c.n >> 2), rg = rr >> 3, r8 = rr & 7;
 #pragma unroll
   for (int u = 0; u < 4; ++u)
-    c.rofs[u] = rg * kPGroupBytes + 128 * r8 + 16 * ((2 * u + ((c.n & 3) >> 1)) ^ swz8(r8) ^ rg) + 8 * (c.n & 1);
+    c.rofs[u] = rg * Lat<D>::group_bytes + 128 * r8 + 16 * ((2 * u + ((c.n & 3) >> 1)) ^ swz8(r8) ^ rg) + 8 * (c.n & 1);
   return c;
 }
 
 // start the copies of step j's rows into the tile at LDS address `tile`; returns the
 // validity bits of the step's 16 keys (key r <-> bit r)
+template <int D>
 __device__ __forceinline__ uint32_t pd_issue(const PdCtx& c, const uint8_t* kvb, int2 e, int j, uint32_t tile) {
   const bool ok0 = kPKeys * j + c.er < c.cols && e.x >= 0 && e.x <= c.pos;
   const bool ok1 = kPKeys * j + 8 + c.er < c.cols && e.y >= 0 && e.y <= c.pos;
-  const uint8_t* src0 = kvb + (size_t)(ok0 ? e.x : c.pos) * kPRowBytes + c.dofs[0];
-  const uint8_t* src1 = kvb + (size_t)(ok1 ? e.y : c.pos) * kPRowBytes + c.dofs[1];
+  const uint8_t* src0 = kvb + (size_t)(ok0 ? e.x : c.pos) * Lat<D>::row_bytes + c.dofs[0];
+  const uint8_t* src1 = kvb + (size_t)(ok1 ? e.y : c.pos) * Lat<D>::row_bytes + c.dofs[1];
 #pragma unroll
-  for (int k = 0; k < kPLines; ++k) {
+  for (int k = 0; k < Lat<D>::lines; ++k) {
     dma16(src0 + 128 * k, tile + 1024 * k);
-    dma16(src1 + 128 * k, tile + kPGroupBytes + 1024 * k);
+    dma16(src1 + 128 * k, tile + Lat<D>::group_bytes + 1024 * k);
   }
   const uint64_t b0 = ballot(ok0), b1 = ballot(ok1);
   uint32_t v = 0;
@@ -495,12 +510,13 @@ struct PdSrc {
   const uint8_t* src1;  // ... of row 8 + er
   uint32_t vbits;
 };
+template <int D>
 __device__ __forceinline__ PdSrc pd_prep(const PdCtx& c, const uint8_t* kvb, int2 e, int j) {
   const bool ok0 = kPKeys * j + c.er < c.cols && e.x >= 0 && e.x <= c.pos;
   const bool ok1 = kPKeys * j + 8 + c.er < c.cols && e.y >= 0 && e.y <= c.pos;
   PdSrc p;
-  p.src0 = kvb + (size_t)(ok0 ? e.x : c.pos) * kPRowBytes + c.dofs[0];
-  p.src1 = kvb + (size_t)(ok1 ? e.y : c.pos) * kPRowBytes + c.dofs[1];
+  p.src0 = kvb + (size_t)(ok0 ? e.x : c.pos) * Lat<D>::row_bytes + c.dofs[0];
+  p.src1 = kvb + (size_t)(ok1 ? e.y : c.pos) * Lat<D>::row_bytes + c.dofs[1];
   const uint64_t b0 = ballot(ok0), b1 = ballot(ok1);
   uint32_t v = 0;
 #pragma unroll
@@ -509,9 +525,10 @@ __device__ __forceinline__ PdSrc pd_prep(const PdCtx& c, const uint8_t* kvb, int
   return p;
 }
 // the two copies (row groups 0 and 1) of line k
+template <int D>
 __device__ __forceinline__ void pd_copy_line(const PdSrc& p, uint32_t tile, int k) {
   dma16(p.src0 + 128 * k, tile + 1024 * k);
-  dma16(p.src1 + 128 * k, tile + kPGroupBytes + 1024 * k);
+  dma16(p.src1 + 128 * k, tile + Lat<D>::group_bytes + 1024 * k);
 }
 
 __device__ __forceinline__ int2 pd_entries(const PdCtx& c, int j) {
@@ -520,7 +537,8 @@ __device__ __forceinline__ int2 pd_entries(const PdCtx& c, int j) {
 }
 
 // S^T[key 4 g + jj][head n] (raw), three chains; K reads kPQAhead MFMAs ahead
-__device__ __forceinline__ f32x4 pd_qk(const PdCtx& c, const uint8_t* tile, const bf16x8 (&qreg)[kPLoads]) {
+template <int D>
+__device__ __forceinline__ f32x4 pd_qk(const PdCtx& c, const uint8_t* tile, const bf16x8 (&qreg)[Lat<D>::loads]) {
   auto kread = [&](int s) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(tile + c.kofs[s & 1] + 1024 * (s >> 1));
   };
@@ -529,19 +547,21 @@ __device__ __forceinline__ f32x4 pd_qk(const PdCtx& c, const uint8_t* tile, cons
   for (int s = 0; s < kPQAhead; ++s) kw[s] = kread(s);
   f32x4 acc[3] = {};
 #pragma unroll
-  for (int s = 0; s < kPLoads; ++s) {
+  for (int s = 0; s < Lat<D>::loads; ++s) {
     __builtin_amdgcn_sched_barrier(0);
     acc[s % 3] = mfma16x16x32(kw[s % kPQAhead], qreg[s], acc[s % 3]);
-    if (s + kPQAhead < kPLoads) kw[s % kPQAhead] = kread(s + kPQAhead);
+    if (s + kPQAhead < Lat<D>::loads) kw[s % kPQAhead] = kread(s + kPQAhead);
   }
   __builtin_amdgcn_sched_barrier(0);
   return acc[0] + acc[1] + acc[2];
 }
 
 // O^T += V^T P^T over the tile, which is refilled as it goes with the rows of a later step
-// (`next`): line 8 (dims 512..575, read only by S) first, then line k as soon as the MFMA of
-// column block 4 k + 3 has consumed the last read of that line.  Spread over the MFMAs,
+// (`next`): the lines past the values (dims 512..575 of a 576-wide row, read only by S)
+// first, then line k as soon as the MFMA of column block 4 k + 3 has consumed the last read
+// of that line.  Spread over the MFMAs,
 // the copies do not stall the wave on the CU's address path as a burst of 18 would.
+template <int D>
 __device__ __forceinline__ void pd_pv(const PdCtx& c, const uint8_t* tile, s16x4_t bop, f32x4 (&o)[kDv / 16],
                                       const PdSrc& next) {
   const uint32_t tl = lds_addr(tile);
@@ -550,7 +570,8 @@ __device__ __forceinline__ void pd_pv(const PdCtx& c, const uint8_t* tile, s16x4
 #pragma unroll
   for (int i = 0; i < kPVAhead; ++i) vw[i] = vread(i);
   __builtin_amdgcn_sched_barrier(0);
-  pd_copy_line(next, tl, kPLines - 1);
+#pragma unroll
+  for (int k = kDv / 64; k < Lat<D>::lines; ++k) pd_copy_line<D>(next, tl, k);
 #pragma unroll
   for (int cb = 0; cb < kDv / 16; ++cb) {
     __builtin_amdgcn_sched_barrier(0);
@@ -560,7 +581,7 @@ __device__ __forceinline__ void pd_pv(const PdCtx& c, const uint8_t* tile, s16x4
       // (after the MFMA: its wait for the operand read orders the copy behind the line's
       // last read)
       __builtin_amdgcn_sched_barrier(0);
-      pd_copy_line(next, tl, cb >> 2);
+      pd_copy_line<D>(next, tl, cb >> 2);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -592,6 +613,7 @@ __device__ __forceinline__ s16x4_t pd_probs(float sc, const float (&sv)[4], floa
   return __builtin_bit_cast(s16x4_t, pb);
 }
 
+template <int D>
 __global__ __launch_bounds__(64) void pertoken_sorted_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ topk, int64_t ld, int T, int H, int S, int cols,
@@ -608,12 +630,12 @@ __global__ __launch_bounds__(64) void pertoken_sorted_kernel(
 
   // queries of head n, dims 32 s + 8 g .. + 8 (the B operand of S^T = K Q^T), negated for a
   // negative scale; completed before any asynchronous copy is in flight
-  bf16x8 qreg[kPLoads];
+  bf16x8 qreg[Lat<D>::loads];
   {
     const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
-    const uint16_t* qrow = q + ((size_t)token * H + hb * 16 + n) * kDqk + 8 * g;
+    const uint16_t* qrow = q + ((size_t)token * H + hb * 16 + n) * D + 8 * g;
 #pragma unroll
-    for (int s = 0; s < kPLoads; ++s) {
+    for (int s = 0; s < Lat<D>::loads; ++s) {
       u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 32 * s);
       w ^= qsign;
       qreg[s] = __builtin_bit_cast(bf16x8, w);
@@ -623,13 +645,13 @@ __global__ __launch_bounds__(64) void pertoken_sorted_kernel(
   float* lse_at = lse + (size_t)token * H + hb * 16 + n;
   const int nsel = pt_sort(topk + (size_t)token * ld, cols, pos, lane);
 #pragma unroll
-  for (int s = 0; s < kPLoads; ++s) asm volatile("" : : "v"(qreg[s]));
+  for (int s = 0; s < Lat<D>::loads; ++s) asm volatile("" : : "v"(qreg[s]));
   if (nsel == 0) {  // nothing selected: zero output, LSE -inf
     const f32x4 z[kDv / 16] = {};
     pt_write(g, z, 0.f, kNegInf, orow, lse_at);
     return;
   }
-  const PdCtx c = pd_context(pos, nsel, scale_log2);
+  const PdCtx c = pd_context<D>(pos, nsel, scale_log2);
   const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv);
   uint8_t* const tile0 = pt_tile;
   uint8_t* const tile1 = reinterpret_cast<uint8_t*>(&pt_q[0][0]);
@@ -645,14 +667,14 @@ __global__ __launch_bounds__(64) void pertoken_sorted_kernel(
   f32x4 o[kDv / 16];
 #pragma unroll
   for (int cb = 0; cb < kDv / 16; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  uint32_t va = pd_issue(c, kvb, pd_entries(c, 0), 0, lds_addr(tile0));
-  uint32_t vb = pd_issue(c, kvb, pd_entries(c, 1), 1, lds_addr(tile1));
+  uint32_t va = pd_issue<D>(c, kvb, pd_entries(c, 0), 0, lds_addr(tile0));
+  uint32_t vb = pd_issue<D>(c, kvb, pd_entries(c, 1), 1, lds_addr(tile1));
   int2 e_next = pd_entries(c, 2);
   bool over = false;
   auto step = [&](int j, const uint8_t* tile, uint32_t& vbuf) {
-    wait_vmcnt<2 * kPLines>();  // step j's copies have landed (step j + 1's may be in flight)
+    wait_vmcnt<2 * Lat<D>::lines>();  // step j's copies have landed (step j + 1's may be in flight)
     float sv[4];
-    const float mt = pd_mask(g, pd_qk(c, tile, qreg), vbuf, sv) * c.sc;
+    const float mt = pd_mask(g, pd_qk<D>(c, tile, qreg), vbuf, sv) * c.sc;
     // a head's first valid scores set its reference (its O and l are still zero)
     if (ballot(m_ref == kNegInf && mt != kNegInf) != 0) {
       const float mh = max_over_rowgroups(mt);
@@ -660,9 +682,9 @@ __global__ __launch_bounds__(64) void pertoken_sorted_kernel(
     }
     over |= ballot(mt > m_ref + kPSlack) != 0;
     // the tile takes step j + 2's rows during its PV
-    const PdSrc next = pd_prep(c, kvb, e_next, j + 2);
+    const PdSrc next = pd_prep<D>(c, kvb, e_next, j + 2);
     e_next = pd_entries(c, j + 3);
-    pd_pv(c, tile, pd_probs(c.sc, sv, m_ref, l_run), o, next);
+    pd_pv<D>(c, tile, pd_probs(c.sc, sv, m_ref, l_run), o, next);
     vbuf = next.vbits;
   };
   for (int j = 0; j < nsteps2; j += 2) {
@@ -673,25 +695,35 @@ __global__ __launch_bounds__(64) void pertoken_sorted_kernel(
   if (over) {
     // the exact routine reads the queries from the second tile's area
 #pragma unroll
-    for (int s = 0; s < kPLoads; ++s) pt_q[s][lane] = __builtin_bit_cast(uint4, qreg[s]);
+    for (int s = 0; s < Lat<D>::loads; ++s) pt_q[s][lane] = __builtin_bit_cast(uint4, qreg[s]);
     __syncthreads();
-    pt_exact<true>(kv, topk, ld, S, nsel, q_pos_offset, scale_log2, token, orow, lse_at);
+    pt_exact<D, true>(kv, topk, ld, S, nsel, q_pos_offset, scale_log2, token, orow, lse_at);
     return;
   }
   pt_write(g, o, l_run, m_ref, orow, lse_at);
 }
 
-hipError_t launch_pertoken_attn(const uint16_t* q, const uint16_t* kv, const int32_t* topk,
-                                int64_t ld, int T, int H, int S, int cols, int64_t q_pos_offset,
-                                float scale, uint16_t* out, float* lse, hipStream_t stream) {
+template <int D>
+static void launch_pertoken(const uint16_t* q, const uint16_t* kv, const int32_t* topk, int64_t ld, int T,
+                            int H, int S, int cols, int64_t q_pos_offset, float scale, uint16_t* out,
+                            float* lse, hipStream_t stream) {
   const long long items = (long long)T * (H / 16);
-  if (items == 0) return hipSuccess;
   if (S <= 65536 && cols <= kPSortMax)
-    hipLaunchKernelGGL(pertoken_sorted_kernel, dim3((unsigned)items), dim3(64), 0, stream, q, kv, topk, ld,
+    hipLaunchKernelGGL(pertoken_sorted_kernel<D>, dim3((unsigned)items), dim3(64), 0, stream, q, kv, topk, ld,
                        T, H, S, cols, q_pos_offset, scale * kLog2e, out, lse);
   else
-    hipLaunchKernelGGL(pertoken_attn_kernel, dim3((unsigned)items), dim3(64), 0, stream, q, kv, topk, ld,
+    hipLaunchKernelGGL(pertoken_attn_kernel<D>, dim3((unsigned)items), dim3(64), 0, stream, q, kv, topk, ld,
                        T, H, S, cols, q_pos_offset, scale * kLog2e, out, lse);
+}
+
+hipError_t launch_pertoken_attn(const uint16_t* q, const uint16_t* kv, const int32_t* topk,
+                                int64_t ld, int T, int H, int S, int cols, int64_t q_pos_offset,
+                                float scale, uint16_t* out, float* lse, hipStream_t stream, int d_qk) {
+  if ((long long)T * (H / 16) == 0) return hipSuccess;
+  if (d_qk == 512)
+    launch_pertoken<512>(q, kv, topk, ld, T, H, S, cols, q_pos_offset, scale, out, lse, stream);
+  else
+    launch_pertoken<576>(q, kv, topk, ld, T, H, S, cols, q_pos_offset, scale, out, lse, stream);
   return hipGetLastError();
 }
 

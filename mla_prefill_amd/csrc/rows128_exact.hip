@@ -10,8 +10,8 @@
 // never exceed 2^8, so no input overflows it.
 //
 // Design (one workgroup of 8 waves per group, 2 waves per SIMD):
-//  * 32-slot tiles of latent rows (72 x 16 B chunks each, LDS rows padded to
-//    1168 B) stream through a 3-stage LDS ring by asynchronous global->LDS
+//  * 32-slot tiles of latent rows (D / 8 chunks of 16 B each, LDS rows padded
+//    by one chunk) stream through a 3-stage LDS ring by asynchronous global->LDS
 //    DMA, issued two tiles ahead; slot indices and membership bytes are
 //    wave-uniform and come through scalar loads;
 //  * QK^T is split by rows: wave w owns rows 16 w .. 16 w + 15, keeps their
@@ -26,27 +26,29 @@
 
 namespace dsa {
 
-constexpr int kGDqk = 576;
 constexpr int kGDv = 512;
 constexpr int kGWaves = 8;
 constexpr int kGThreads = 64 * kGWaves;
 constexpr int kGKeys = 32;                            // slots per tile
-constexpr int kGRowBytes = kGDqk * 2 + 16;            // 1168: 72 data chunks + 1 pad chunk
-constexpr int kGSlots = kGRowBytes / 16;              // 73
-constexpr int kGDma = (kGKeys * kGSlots + 63) / 64;   // 37 wave copies per tile
-constexpr int kGDmaPerWave = (kGDma + kGWaves - 1) / kGWaves;  // 5 (3 go to a dummy area)
-constexpr int kGStageBytes = kGDma * 1024;
 constexpr int kGStages = 3;
 constexpr int kGPStride = 40;                         // halves per probability row (32 + 8 pad)
 constexpr float kGSlack = 8.f;                        // lazy-rescale threshold (log2 units)
 
-template <bool kPerToken>
+// D: the latent width, 576 (512 + 64 rope dims) or 512 (no rope part)
+template <int D, bool kPerToken>
 __global__ __launch_bounds__(kGThreads) void rows128_exact_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ keys, int64_t keys_ld, const int32_t* __restrict__ union_len,
     const uint8_t* __restrict__ hgmask, int T, int H, int S, int ncols, int64_t q_pos_offset,
     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
     const int32_t* __restrict__ ginfo) {
+  static_assert(D == 576 || D == 512, "latent widths");
+  constexpr int kGRowBytes = D * 2 + 16;                          // D / 8 data chunks + 1 pad chunk
+  constexpr int kGSlots = kGRowBytes / 16;                        // 73 / 65
+  constexpr int kGDma = (kGKeys * kGSlots + 63) / 64;             // wave copies per tile (37 / 33)
+  constexpr int kGDmaPerWave = (kGDma + kGWaves - 1) / kGWaves;   // 5 (the rest go to a dummy area)
+  constexpr int kGStageBytes = kGDma * 1024;
+  static_assert(kGDmaPerWave == 5, "a wave's copies span at most 6 slot rows");
   __shared__ __align__(16) uint8_t stage[kGStages][kGStageBytes];
   __shared__ __align__(16) uint16_t pbuf[128 * kGPStride];
   __shared__ float alpha_s[128];
@@ -71,17 +73,17 @@ __global__ __launch_bounds__(kGThreads) void rows128_exact_kernel(
   const int tok_own = t0 + i_own;
   const bool row_live = i_own < ntok;
 
-  bf16x8 qreg[kGDqk / 32];
+  bf16x8 qreg[D / 32];
   if (row_live) {
-    const uint16_t* qrow = q + ((size_t)tok_own * H + h_own) * kGDqk + 8 * g;
+    const uint16_t* qrow = q + ((size_t)tok_own * H + h_own) * D + 8 * g;
 #pragma unroll
-    for (int s = 0; s < kGDqk / 32; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
+    for (int s = 0; s < D / 32; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
   } else {
 #pragma unroll
-    for (int s = 0; s < kGDqk / 32; ++s) qreg[s] = bf16x8{};
+    for (int s = 0; s < D / 32; ++s) qreg[s] = bf16x8{};
   }
 #pragma unroll
-  for (int s = 0; s < kGDqk / 32; ++s) asm volatile("" : : "v"(qreg[s]));  // loads done before any copy
+  for (int s = 0; s < D / 32; ++s) asm volatile("" : : "v"(qreg[s]));  // loads done before any copy
 
   int nkeys;
   if (kPerToken) {
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(kGThreads) void rows128_exact_kernel(
         }
         int32_t xr = up ? x1 : x0;
         if (r >= kGKeys) xr = 0;
-        dma16(kv + (size_t)xr * kGDqk + (c < 72 ? c : 0) * 8, lds_addr(st + 1024 * i));
+        dma16(kv + (size_t)xr * D + (c < D / 8 ? c : 0) * 8, lds_addr(st + 1024 * i));
       } else {
         dma16(kv, lds_addr(dummy));  // keeps every wave's copy count per tile equal
       }
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(kGThreads) void rows128_exact_kernel(
     // ---- scores of this wave's 16 rows over the 32 slots
     f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int s = 0; s < kGDqk / 32; ++s)
+    for (int s = 0; s < D / 32; ++s)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         sacc[kb] = mfma16x16x32(*reinterpret_cast<const bf16x8*>(tile + koff + kb * 16 * kGRowBytes + 64 * s),
@@ -317,17 +319,29 @@ hipError_t launch_rows128_exact(const uint16_t* q, const uint16_t* kv, const int
                                 int64_t keys_ld, const int32_t* union_len, const uint8_t* hgmask,
                                 int T, int H, int S, int ncols, int64_t q_pos_offset, float scale,
                                 uint16_t* out, float* lse, hipStream_t stream, const int32_t* group_info,
-                                int ngroups) {
+                                int ngroups, int d_qk) {
   const int NG = ngroups;
   if (NG == 0) return hipSuccess;
-  if (hgmask != nullptr)
-    hipLaunchKernelGGL(rows128_exact_kernel<false>, dim3(NG), dim3(kGThreads), 0, stream, q, kv, keys,
-                       keys_ld, union_len, hgmask, T, H, S, ncols, q_pos_offset, scale * kLog2e, out,
-                       lse, group_info);
-  else
-    hipLaunchKernelGGL(rows128_exact_kernel<true>, dim3(NG), dim3(kGThreads), 0, stream, q, kv, keys,
-                       keys_ld, union_len, hgmask, T, H, S, ncols, q_pos_offset, scale * kLog2e, out,
-                       lse, group_info);
+  const float sl = scale * kLog2e;
+  if (d_qk == 512) {
+    if (hgmask != nullptr)
+      hipLaunchKernelGGL((rows128_exact_kernel<512, false>), dim3(NG), dim3(kGThreads), 0, stream, q, kv,
+                         keys, keys_ld, union_len, hgmask, T, H, S, ncols, q_pos_offset, sl, out, lse,
+                         group_info);
+    else
+      hipLaunchKernelGGL((rows128_exact_kernel<512, true>), dim3(NG), dim3(kGThreads), 0, stream, q, kv,
+                         keys, keys_ld, union_len, hgmask, T, H, S, ncols, q_pos_offset, sl, out, lse,
+                         group_info);
+  } else {
+    if (hgmask != nullptr)
+      hipLaunchKernelGGL((rows128_exact_kernel<576, false>), dim3(NG), dim3(kGThreads), 0, stream, q, kv,
+                         keys, keys_ld, union_len, hgmask, T, H, S, ncols, q_pos_offset, sl, out, lse,
+                         group_info);
+    else
+      hipLaunchKernelGGL((rows128_exact_kernel<576, true>), dim3(NG), dim3(kGThreads), 0, stream, q, kv,
+                         keys, keys_ld, union_len, hgmask, T, H, S, ncols, q_pos_offset, sl, out, lse,
+                         group_info);
+  }
   return hipGetLastError();
 }
 

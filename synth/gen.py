@@ -200,6 +200,10 @@ CONFIGS = {
     "c6_masked_rope": Config("c6_masked_rope", T=16384, S=16384, H=16, k=2048, cols=2048,
                              G=8, scale=1.0 / 16.0, seed=5, kind="mha", d_qk=256, d_v=256,
                              dn=192, dr=64, dv=256),
+    # The 512-wide latent (no rope part; K = V = the whole row), the MQA form of the NoPE
+    # (256, 0, 256) model; otherwise the shapes and top-k recipe of c3.
+    "c7_glm16k_latent512": Config("c7_glm16k_latent512", T=16384, S=16384, H=16, k=2048,
+                                  cols=2048, G=8, scale=1.0 / 16.0, seed=7, d_qk=512),
     # Long prompt: the last 21504 of 32768 positions are queries; 2176-wide top-k buffer.
     "c5_long": Config("c5_long", T=21504, S=32768, H=16, k=2048, cols=2176, G=8,
                       scale=1.0 / 16.0, seed=4, q_pos_offset=11264),

@@ -98,7 +98,9 @@ def grouped_call(lib, q=P, kv=P, ui=P, ul=P, mk=P, T=64, H=16, S=64, pad=256, dq
 def test_grouped_validation(lib):
     for H in (8, 24, 48, 256):
         assert grouped_call(lib, H=H) == UNSUP
-    assert grouped_call(lib, dqk=512) == UNSUP and grouped_call(lib, dv=256) == UNSUP
+    assert grouped_call(lib, dqk=448) == UNSUP and grouped_call(lib, dv=256) == UNSUP
+    assert grouped_call(lib, dqk=512, dv=576) == UNSUP
+    assert grouped_call(lib, dqk=512, T=0) == OK       # the 512-wide latent (no rope part)
     assert grouped_call(lib, T=-3) == SHAPE and grouped_call(lib, S=0) == SHAPE
     assert grouped_call(lib, pad=48) == SHAPE          # union rows must hold whole 32-slot tiles
     assert grouped_call(lib, T=0) == OK
@@ -119,7 +121,8 @@ def pertoken_call(lib, q=P, kv=P, tk=P, ld=32, T=64, H=16, S=64, cols=32, P0=0, 
 def test_pertoken_validation(lib):
     for H in (8, 24, 136, 0):
         assert pertoken_call(lib, H=H) == UNSUP
-    assert pertoken_call(lib, dqk=192) == UNSUP
+    assert pertoken_call(lib, dqk=192) == UNSUP and pertoken_call(lib, dqk=512, dv=256) == UNSUP
+    assert pertoken_call(lib, dqk=512, T=0) == OK
     assert pertoken_call(lib, ld=16) == SHAPE and pertoken_call(lib, cols=-1) == SHAPE
     assert pertoken_call(lib, P0=-5) == SHAPE
     assert pertoken_call(lib, T=0) == OK
@@ -207,7 +210,8 @@ def test_varlen_validation(lib):
     def gv(H=16, dqk=576, ns=256, mg=3, pad=128, gi=P, T=8, scale=0.1):
         return lib.dsa_sparse_prefill_grouped_varlen(P, P, ns, gi, mg, P, P, P, T, H, pad, dqk, 512, scale,
                                                      P, P, None)
-    assert gv(H=24) == UNSUP and gv(dqk=512) == UNSUP and gv(scale=0.0) == UNSUP
+    assert gv(H=24) == UNSUP and gv(dqk=448) == UNSUP and gv(scale=0.0) == UNSUP
+    assert gv(dqk=512, T=0) == OK
     assert gv(ns=0) == SHAPE and gv(pad=40) == SHAPE
     assert gv(mg=0) == OK and gv(T=0) == OK and gv(gi=None) == NULL and gv(gi=P + 4) == ALIGN
     def pv(H=16, ws=P, T=8, R_=2, cols=16):

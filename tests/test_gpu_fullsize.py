@@ -17,7 +17,7 @@ from tests.gpu_helpers import OUT_RTOL, check_attention, dev_bf16, dev_i32
 
 pytestmark = pytest.mark.gpu
 
-MQA = ["c2_dsv32", "c3_glm16k", "c3w_glm16k_uniform", "c5_long"]
+MQA = ["c2_dsv32", "c3_glm16k", "c3w_glm16k_uniform", "c5_long", "c7_glm16k_latent512"]
 
 
 @pytest.fixture(scope="module", params=MQA)

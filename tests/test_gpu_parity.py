@@ -24,10 +24,10 @@ def R():
     return routings
 
 
-def small_mqa(seed, T, S, H, k, cols, G, P0, mode="locality", shuffle=False):
+def small_mqa(seed, T, S, H, k, cols, G, P0, mode="locality", shuffle=False, d=576):
     rng = np.random.default_rng(seed)
-    q = normal_bf16(rng, (T, H, 576))
-    kv = normal_bf16(rng, (S, 576))
+    q = normal_bf16(rng, (T, H, d))
+    kv = normal_bf16(rng, (S, d))
     if mode == "uniform":
         topk = topk_uniform(rng, T, S, k, cols, P0)
     else:
@@ -195,6 +195,64 @@ def test_large_score_jump_and_negative_scale(R):
         check_attention(out, lse, ref_out, ref_lse, f"per-token score jump, scale {scale}")
         out, lse, _ = R.grouped(qd, kvd, tkd, P0, scale)
         check_attention(out, lse, ref_out, ref_lse, f"grouped score jump, scale {scale}")
+
+
+# ---------------------------------------------------------------------------
+# the 512-wide latent (no rope part: K = V = the whole row)
+# ---------------------------------------------------------------------------
+
+D512_CASES = [c for c in MQA_CASES if c[0] != "h16_uniform"]
+
+
+@pytest.mark.parametrize("case", D512_CASES, ids=[c[0] for c in D512_CASES])
+def test_latent512_parity(R, case):
+    label, seed, T, S, H, k, cols, P0, mode, shuffle = case
+    G = 128 // H
+    q, kv, topk = small_mqa(seed + 40, T, S, H, k, cols, G, P0, mode, shuffle, d=512)
+    scale = 1.0 / 16.0
+    ref_out, ref_lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, P0, scale)
+    qd, kvd, tkd = dev_bf16(q), dev_bf16(kv), dev_i32(topk)
+    out, lse = R.pertoken(qd, kvd, tkd, P0, scale)
+    check_attention(out, lse, ref_out, ref_lse, f"{label} d512 per-token")
+    out, lse, _ = R.grouped(qd, kvd, tkd, P0, scale)
+    check_attention(out, lse, ref_out, ref_lse, f"{label} d512 grouped")
+
+
+def test_latent512_far_positions_and_wide_rows(R):
+    """The register-ring per-token kernel at 512 dims (positions past 65535, rows wider than
+    the sorted walk takes)."""
+    rng = np.random.default_rng(44)
+    H = 16
+    for T, S, k, cols, P0 in ((12, 70000, 300, 320, 70000 - 12), (10, 4000, 3000, 3100, 4000 - 10)):
+        q = normal_bf16(rng, (T, H, 512))
+        kv = normal_bf16(rng, (S, 512))
+        topk = topk_uniform(rng, T, S, k, cols, P0)
+        ref_out, ref_lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, P0, 0.0625)
+        out, lse = R.pertoken(dev_bf16(q), dev_bf16(kv), dev_i32(topk), P0, 0.0625)
+        check_attention(out, lse, ref_out, ref_lse, f"d512 per-token S={S} cols={cols}")
+
+
+@pytest.mark.parametrize("H", [16, 128])
+def test_latent512_score_jump(R, H):
+    """The exact fallbacks at 512 dims: one late key per affected token scores far above the
+    rest (as in test_large_score_jump_and_negative_scale)."""
+    rng = np.random.default_rng(45 + H)
+    T, S, P0 = 24, 200, 176
+    q = normal_bf16(rng, (T, H, 512))
+    kv = normal_bf16(rng, (S, 512))
+    topk = topk_uniform(rng, T, S, 120, 128, P0)
+    for t in range(0, T, 3):
+        r = t
+        kv[r] = np.where(q[t, 0] & 0x8000, 0xC000, 0x4000).astype(np.uint16)
+        topk[t][topk[t] == r] = -1
+        topk[t, 120] = r
+    for scale in (0.0625, -0.0625):
+        ref_out, ref_lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, P0, scale)
+        qd, kvd, tkd = dev_bf16(q), dev_bf16(kv), dev_i32(topk)
+        out, lse = R.pertoken(qd, kvd, tkd, P0, scale)
+        check_attention(out, lse, ref_out, ref_lse, f"d512 H={H} per-token score jump, scale {scale}")
+        out, lse, _ = R.grouped(qd, kvd, tkd, P0, scale)
+        check_attention(out, lse, ref_out, ref_lse, f"d512 H={H} grouped score jump, scale {scale}")
 
 
 # ---------------------------------------------------------------------------

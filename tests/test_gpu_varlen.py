@@ -109,3 +109,17 @@ def test_varlen_single_request_matches_single_sequence(R):
     o1, l1, _ = R.grouped_varlen(q, kv[:S].contiguous(), tk, b, 0.1)
     o2, l2, _ = R.grouped(q, kv[:S].contiguous(), tk, P0, 0.1)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("H", [16, 128])
+def test_varlen_latent512(R, H):
+    """A batch over a paged cache of 512-wide latent rows (no rope part): both routings."""
+    c = make_varlen_case(56 + H, [11, 30, 4], [40, 0, 90], H=H, k=24, cols=28, page_size=8, G=128 // H,
+                         mode="locality", d_qk=512)
+    q, kv, tk, b = dev_bf16(c.q), dev_bf16(c.kv_cache), dev_i32(c.topk), device_batch(c)
+    scale = 1.0 / 16.0
+    ref_out, ref_lse = oracle.pertoken_sparse_mqa_varlen(c.q, c.kv_cache, c.topk, *oracle_args(c), scale)
+    out_g, lse_g, _ = R.grouped_varlen(q, kv, tk, b, scale, max_groups=c.max_groups())
+    check_attention(out_g, lse_g, ref_out, ref_lse, f"d512 H={H} grouped batch")
+    out_p, lse_p, _ = R.pertoken_varlen(q, kv, tk, b, scale)
+    check_attention(out_p, lse_p, ref_out, ref_lse, f"d512 H={H} per-token batch")

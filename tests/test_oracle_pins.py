@@ -83,6 +83,17 @@ def test_pertoken_matches_torch_sdpa(seed):
     np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
 
 
+def test_pertoken_without_rope_part_matches_torch_sdpa():
+    # the 512-wide latent: scores and values over the same whole row (d_qk = d_v)
+    S, T, d = 40, 33, 16
+    q, kv, topk, P0 = rand_case(3, T=T, S=S, d=d)
+    out, lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, P0, 0.29, d_v=d)
+    ref_out, ref_lse, nonempty = sdpa_reference(q, kv, topk, S, P0, float(np.float32(0.29)), d)
+    assert nonempty.all()
+    np.testing.assert_allclose(out, ref_out, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+
+
 def test_all_causal_selected_is_causal_attention():
     rng = np.random.default_rng(5)
     T = S = 33

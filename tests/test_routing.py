@@ -83,9 +83,10 @@ def measured_rows():
 
 
 def test_choice_is_near_the_fastest_measured_routing(pick):
-    """At every measured point the chosen routing is the fastest or within 10 % of it."""
+    """At every measured point (both latent widths) the chosen routing is the fastest or within
+    10 % of it."""
     rows = measured_rows()
-    assert len(rows) >= 30
+    assert len(rows) >= 70
     for H, L, ms in rows:
         choice = pick(L, L, 0, H, 2048, True)
         assert choice in ms, (H, L, choice)
