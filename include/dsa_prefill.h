@@ -7,7 +7,7 @@
  * describe three routings of this one function, each exposed here:
  *
  *   per-token  -- dsa_sparse_prefill_pertoken: each token gathers its own rows
- *                 of the 576-wide bf16 latent ("[Perf][GLM-5.3-Flash]
+ *                 of the bf16 latent ("[Perf][GLM-5.3-Flash]
  *                 Dense/masked-MHA sparse prefill for the NoPE (256, 0, 256)
  *                 layout + skip the NoPE K concat", Purpose section);
  *   grouped    -- dsa_build_group_union + dsa_sparse_prefill_grouped: 128/H
@@ -140,15 +140,17 @@ int dsa_build_group_union(const int32_t* topk, int64_t ld, int T, int cols, int 
  * (token gG + i, head h) attends over the slots j < union_len[g] of
  * union_idx[g] whose mask bit i is set; this equals per-token attention.
  *
- *   q         bf16 [T, H, 576] absorbed MLA queries (free view [NG, 128, 576])
- *   kv        bf16 [S, 576] latent rows; V = the first 512 dims of a row
+ *   q         bf16 [T, H, d_qk] absorbed MLA queries (free view [NG, 128, d_qk])
+ *   kv        bf16 [S, d_qk] latent rows; V = the first 512 dims of a row
  *   union_idx, union_len, head_group_mask: as written by dsa_build_group_union
  *             (union_len is clamped to [0, union_pad]; slots holding a
  *             position outside [0, S) are skipped); union_pad must be a
  *             multiple of 32 (dsa_union_pad gives a multiple of 64) and
  *             head_group_mask 4-byte aligned
  *   H         16, 32, 64 or 128 (128 % H == 0 and G = 128 / H <= 8)
- *   d_qk, d_v must be 576 and 512
+ *   d_qk      576 (512 latent dims + 64 rope dims) or 512 (the GLM-5.3-Flash
+ *             latent with no rope part, "[Perf][GLM-5.3-Flash] ...": scores
+ *             and values then use the same 512 dims); d_v must be 512
  *   scale     softmax scale applied to q.k
  *   out       bf16 [T, H, 512];  lse  fp32 [T, H]
  * Rows of the partial last group beyond T are neither read nor written. */
@@ -161,8 +163,9 @@ int dsa_sparse_prefill_grouped(const uint16_t* q, const uint16_t* kv, const int3
  * attends, for each head, over the latent rows it selects from its own top-k
  * row (selection rule above), gathering them itself.
  *
- *   q [T, H, 576], kv [S, 576], topk int32 [T, ld] (cols used), H a multiple of
- *   16 up to 128, d_qk = 576, d_v = 512, q_pos_offset >= 0;
+ *   q [T, H, d_qk], kv [S, d_qk], topk int32 [T, ld] (cols used), H a multiple
+ *   of 16 up to 128, d_qk = 576 or 512 (as for the grouped form), d_v = 512,
+ *   q_pos_offset >= 0;
  *   out bf16 [T, H, 512], lse fp32 [T, H]. */
 int dsa_sparse_prefill_pertoken(const uint16_t* q, const uint16_t* kv, const int32_t* topk,
                                 int64_t ld, int T, int H, int S, int cols, int64_t q_pos_offset,
@@ -224,7 +227,8 @@ int dsa_dense_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint1
  *   block_table  int32 [R, bt_ld]  physical page of each request page: position
  *                               x lives in cache row block_table[r][x / page_size]
  *                               * page_size + x % page_size
- *   page_size >= 1; the cache holds num_slots >= 1 rows of 576 bf16.
+ *   page_size >= 1; the cache holds num_slots >= 1 rows of d_qk bf16 (576 or
+ *   512, as for the single-sequence forms).
  * Top-k rows hold request-local positions.  Token t of request r (local index
  * i = t - cu[r], position p = q_pos_start[r] + i) selects x iff 0 <= x <
  * kv_lens[r], x <= p and x maps to a row inside the cache (a page past bt_ld or
