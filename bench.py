@@ -45,7 +45,7 @@ WORKLOADS = {
     "crossover": (None, None),
     "glm16k_uniform": ("c3w_glm16k_uniform", None),
     "long32k": ("c5_long", None),
-    "dsv32": ("c2_dsv32", None),
+    "dsv32": ("c2_dsv32", "c8_masked_dsv32"),
 }
 
 
@@ -61,6 +61,8 @@ def parse():
                     help="crossover: chunk lengths (T = S, starting at position 0)")
     ap.add_argument("--dqk", type=int, default=576, choices=(576, 512),
                     help="crossover: latent width of the MQA routings")
+    ap.add_argument("--mha", default="256,0,256", choices=("256,0,256", "192,64,256", "128,64,128"),
+                    help="crossover: (qk_nope, qk_rope, v) of the MHA routings")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (calibrates HBM byte counters)")
@@ -111,7 +113,7 @@ KERNEL_SYMBOLS = {  # bench kernel name -> (device symbol, sources)
     "build_union": ("dsa::build_union_kernel<false>", ["union_builder.hip", "common.h"]),
     "grouped_attn": ("dsa::rows128_attn_kernel<576, false>", ["grouped_attn.hip", "common.h"]),
     "pertoken_attn": ("dsa::pertoken_sorted_kernel<576>", ["pertoken_attn.hip", "common.h"]),
-    "masked_mha_routing": ("dsa::masked_mha_kernel<256, false>", ["masked_mha.hip", "common.h"]),
+    "masked_mha_routing": ("dsa::masked_mha_kernel<256, 0, 256, false>", ["masked_mha.hip", "common.h"]),
 }
 
 
@@ -475,7 +477,8 @@ def bench_crossover(a):
     For each chunk length L (T = S = L from position 0, top-2048 with 8-token locality, seed
     10 + L) and each head count H (G = 128 / H): the grouped routing (union build + attention)
     and the per-token routing over the latent (576 wide, or --dqk 512), the masked routing (bit scatter +
-    attention) over per-head NoPE K/V (qk 256, v 256), and for L <= k the dense shortcut.
+    attention) over per-head K/V (--mha: NoPE (256, 0, 256) by default), and for L <= k the
+    dense shortcut.
     Values are N(0, 1) bf16 drawn on the device from a seeded generator (timing only: parity of
     every kernel is covered by the tests).  Median over --steps timed calls after --warmup.
     One JSON line per (H, L), then a summary line with the fastest routing per point.
@@ -531,24 +534,29 @@ def bench_crossover(a):
 
             ms = {"grouped": timed(grouped), "per-token": timed(pertoken)}
             del q, kv, bufs, og, lg, op, lp
-            mq, mk, mv = (randn_bf16((L, H, 256), seed + 2 + i) for i in range(3))
+            dn, dr, dv = (int(x) for x in a.mha.split(","))
+            mq = randn_bf16((L, H, dn + dr), seed + 2)
+            mk = randn_bf16((L, H, dn), seed + 3)
+            mv = randn_bf16((L, H, dv), seed + 4)
+            mkp = randn_bf16((L, dr), seed + 5) if dr else None
             ws = torch.empty((L, (L + 31) // 32), dtype=torch.int32, device="cuda")
-            om, lm = routings.alloc_out(L, H, 256)
+            om, lm = routings.alloc_out(L, H, dv)
 
             def masked():
-                _lib.dsa_masked_mha_prefill(mq, mk, None, mv, topk, 0, scale, ws, om, lm, stream=stream)
+                _lib.dsa_masked_mha_prefill(mq, mk, mkp, mv, topk, 0, scale, ws, om, lm, stream=stream)
 
             def dense():
-                _lib.dsa_dense_mha_prefill(mq, mk, None, mv, 0, scale, om, lm, stream=stream)
+                _lib.dsa_dense_mha_prefill(mq, mk, mkp, mv, 0, scale, om, lm, stream=stream)
 
             ms["masked"] = timed(masked)
             if L <= k:
                 ms["dense"] = timed(dense)
-            del mq, mk, mv, ws, om, lm
+            del mq, mk, mv, mkp, ws, om, lm
             torch.cuda.empty_cache()
             best = min(ms, key=ms.get)
             summary[f"H{H}_L{L}"] = best
             print(json.dumps({"workload": "crossover", "H": H, "G": G, "L": L, "k": k, "d_qk": a.dqk,
+                              "mha": a.mha,
                               "ms": {r: round(v, 4) for r, v in ms.items()}, "fastest": best,
                               "query_tokens_per_s": {r: round(L / (v * 1e-3), 1) for r, v in ms.items()}}),
                   flush=True)

@@ -89,29 +89,32 @@ size_t dsa_masked_mha_workspace_bytes(int T, int S);
  *                       q_pos_offset .. q_pos_offset + T - 1 over S keys
  *   H                   query heads on this GPU
  *   k                   the indexer's top-k size
- *   mha_available       nonzero when the caller can run the MHA forms
- *                       (per-head K/V of a geometry dsa_masked_mha_prefill
- *                       accepts); zero restricts the choice to grouped and
- *                       per-token
+ *   mha_dv              the value width of the caller's per-head MHA geometry
+ *                       when it can run the MHA forms: 256 for (256, 0, 256)
+ *                       and (192, 64, 256), 128 for (128, 64, 128); 0 when it
+ *                       cannot (the choice is then grouped or per-token)
  * Returns one of the DSA_ROUTING_* codes:
- *   DENSE     mha_available and q_pos_offset + T <= k;
- *   MASKED    mha_available and the mean over the chunk of the causal key
- *             count min(S, p_t + 1) is at most c(H) * k, with c measured on
- *             MI355X for this library's kernels: 3.0 / 2.4 / 2.2 for H = 16 /
- *             32 / 64 (against grouped), 1.9 for H = 128 and 3.7 for other
- *             multiples of 16 (against per-token); any H the MQA kernels do not
- *             take (not a multiple of 16, or above 128) routes here as well;
+ *   DENSE     mha_dv != 0 and q_pos_offset + T <= k;
+ *   MASKED    mha_dv != 0 and the mean over the chunk of the causal key count
+ *             min(S, p_t + 1) is at most c * k, with c measured on MI355X for
+ *             this library's kernels (against the 576-wide latent):
+ *                         H = 16   32   64  | 128 | other multiples of 16
+ *               mha_dv 256:  3.0  2.4  2.2  | 1.9 | 3.7
+ *               mha_dv 128:  4.3  3.4  3.1  | 2.8 | 5.5
+ *             (first three against grouped, the rest against per-token); any
+ *             H the MQA kernels do not take (not a multiple of 16, or above
+ *             128) routes here as well;
  *   GROUPED   H in {16, 32, 64} (128 / H consecutive tokens per group);
  *   PERTOKEN  otherwise (H = 128 runs per-token: a group would be one token).
  * DSA_ERR_SHAPE for T < 0, S < 1, q_pos_offset < 0, H < 1 or k < 1;
- * DSA_ERR_UNSUPPORTED when no routing serves H (MQA kernels need H a
- * multiple of 16 up to 128, and mha_available is zero).  Host-only: nothing
- * is enqueued. */
+ * DSA_ERR_UNSUPPORTED for another mha_dv, or when no routing serves H (MQA
+ * kernels need H a multiple of 16 up to 128, and mha_dv is 0).  Host-only:
+ * nothing is enqueued. */
 #define DSA_ROUTING_DENSE 1
 #define DSA_ROUTING_MASKED 2
 #define DSA_ROUTING_GROUPED 3
 #define DSA_ROUTING_PERTOKEN 4
-int dsa_select_routing(int T, int S, int64_t q_pos_offset, int H, int k, int mha_available);
+int dsa_select_routing(int T, int S, int64_t q_pos_offset, int H, int k, int mha_dv);
 
 /* Union list and per-token membership mask of every group of G consecutive
  * tokens ("[Perf][DSA] Grouped sparse prefill ...", "How" section: sorted
@@ -176,14 +179,15 @@ int dsa_sparse_prefill_pertoken(const uint16_t* q, const uint16_t* kv, const int
  * prefills", Purpose section; "[Perf][GLM-5.3-Flash] ...", commit messages):
  * token t, head h attends over every key x with x <= q_pos_offset + t and
  * x in sel(t), using per-head keys and values.  Supported geometries (the
- * qk 256 / v 256 layouts the pages' masked-MHA allow-list shares one kernel
- * for, "[Perf][GLM-5.3-Flash] ..." description and commit messages):
+ * three (qk_nope, qk_rope, v) tuples of the pages' masked-MHA allow-list,
+ * "[Perf][GLM-5.3-Flash] ..." description and commit messages):
  *   dn = 256, dr = 0,  dv = 256 (NoPE): the key is k_nope itself, read in
  *     place; k_pe is not read (it may be NULL);
- *   dn = 192, dr = 64, dv = 256: the key is k_nope || k_pe, k_pe shared by
- *     every head (the broadcast the pages' K concat builds); both are read in
- *     place, no concatenated K is materialized.  k_pe must be non-NULL and
- *     16-byte aligned.
+ *   dn = 192, dr = 64, dv = 256 (GLM-5) and dn = 128, dr = 64, dv = 128
+ *   (DeepSeek-V3.2): the key is k_nope || k_pe, k_pe shared by every head (the
+ *   broadcast the pages' K concat builds); both are read in place, no
+ *   concatenated K is materialized.  k_pe must be non-NULL and 16-byte
+ *   aligned.
  * Anything else returns DSA_ERR_UNSUPPORTED.
  *
  *   q       bf16 [T, H, dn + dr];  k_nope bf16 [S, H, dn];  k_pe bf16 [S, dr]

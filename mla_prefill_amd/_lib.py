@@ -126,10 +126,11 @@ def dsa_masked_mha_workspace_bytes(T: int, S: int) -> int:
 ROUTING_NAMES = {1: "dense", 2: "masked", 3: "grouped", 4: "per-token"}
 
 
-def dsa_select_routing(T: int, S: int, q_pos_offset: int, H: int, k: int, mha_available: bool) -> str:
+def dsa_select_routing(T: int, S: int, q_pos_offset: int, H: int, k: int, mha_dv: int) -> str:
     """Name of the routing the library picks for one chunk ("dense", "masked", "grouped" or
-    "per-token")."""
-    r = lib.dsa_select_routing(T, S, q_pos_offset, H, k, int(bool(mha_available)))
+    "per-token"); mha_dv is the value width of the caller's MHA geometry (256 or 128), or 0
+    when it cannot run the MHA forms."""
+    r = lib.dsa_select_routing(T, S, q_pos_offset, H, k, int(mha_dv))
     _check("dsa_select_routing", min(r, 0))
     return ROUTING_NAMES[r]
 

@@ -21,6 +21,12 @@ inline bool scale_ok(float s) { return s == s && s != 0.f && s - s == 0.f; }
 constexpr int kValueDim = 512;
 inline bool latent_ok(int d_qk, int d_v) { return (d_qk == 576 || d_qk == 512) && d_v == kValueDim; }
 
+// MHA geometries (qk_nope, qk_rope, v) of the masked and dense forms
+inline bool mha_nope(int dn, int dr, int dv) { return dn == 256 && dr == 0 && dv == 256; }
+inline bool mha_rope(int dn, int dr, int dv) {
+  return (dn == 192 && dr == 64 && dv == 256) || (dn == 128 && dr == 64 && dv == 128);
+}
+
 // host checks of a batch description (its device contents are never errors)
 inline bool batch_shape_ok(int T, int cols, int64_t ld, int R, int64_t bt_ld, int page_size, int num_slots) {
   return T >= 0 && cols >= 0 && ld >= cols && R >= 1 && bt_ld >= 1 && page_size >= 1 && num_slots >= 1;
@@ -63,18 +69,29 @@ int dsa_union_pad(int G, int cols) {
 // Purpose section and its heuristic commit: below some length the masked MHA beats the sparse
 // MQA kernels, and a chunk no longer than the top-k needs no mask at all).  The thresholds
 // are MI355X measurements of this library's kernels: chunks of L tokens from position 0 with
-// top-2048 (8-token locality), per-head NoPE K/V (qk 256, v 256) for the MHA forms and the
-// 576-wide latent for the MQA forms.  Masked and sparse times cross where the mean number of
-// causal keys per query token reaches c * k: with the grouped routing c = 3.0 (H 16), 2.4 (32),
-// 2.2 (64); against per-token c = 1.9 at H 128 (G = 1: per-token runs the 128-row kernel) and
-// about 3.7 for the other head counts, which have no grouped form.
-int dsa_select_routing(int T, int S, int64_t q_pos_offset, int H, int k, int mha_available) {
+// top-2048 (8-token locality), the 576-wide latent for the MQA forms.  Masked and sparse times
+// cross where the mean number of causal keys per query token reaches c * k (masked time grows
+// with the causal pairs, sparse time with the selected ones).
+namespace {
+double masked_threshold(int H, int mha_dv, bool grouped) {
+  // {H 16, 32, 64 against grouped; 128 against per-token (G = 1); other H against per-token}
+  static const double kQk256[5] = {3.0, 2.4, 2.2, 1.9, 3.7};  // (256, 0, 256), (192, 64, 256)
+  static const double kDsv[5] = {4.3, 3.4, 3.1, 2.8, 5.5};    // (128, 64, 128)
+  const double* c = mha_dv == 128 ? kDsv : kQk256;
+  if (!grouped) return H == 128 ? c[3] : c[4];
+  return H == 16 ? c[0] : (H == 32 ? c[1] : c[2]);
+}
+}  // namespace
+
+int dsa_select_routing(int T, int S, int64_t q_pos_offset, int H, int k, int mha_dv) {
   if (T < 0 || S < 1 || q_pos_offset < 0 || H < 1 || k < 1) return DSA_ERR_SHAPE;
+  if (mha_dv != 0 && mha_dv != 256 && mha_dv != 128) return DSA_ERR_UNSUPPORTED;
+  const bool mha = mha_dv != 0;
   const bool mqa_ok = H % 16 == 0 && H <= 128;
   const bool grouped_ok = mqa_ok && 128 % H == 0 && H < 128;
-  if (!mqa_ok && !mha_available) return DSA_ERR_UNSUPPORTED;
-  if (mha_available && q_pos_offset + (int64_t)T <= k) return DSA_ROUTING_DENSE;
-  if (mha_available) {
+  if (!mqa_ok && !mha) return DSA_ERR_UNSUPPORTED;
+  if (mha && q_pos_offset + (int64_t)T <= k) return DSA_ROUTING_DENSE;
+  if (mha) {
     if (!mqa_ok) return DSA_ROUTING_MASKED;
     // mean over the chunk of min(S, p_t + 1), p_t = q_pos_offset + t
     const double first = (double)q_pos_offset + 1.0;
@@ -86,12 +103,7 @@ int dsa_select_routing(int T, int S, int64_t q_pos_offset, int H, int k, int mha
       sum = n * first + n * (n - 1.0) / 2.0 + ((double)T - n) * S;
     }
     const double mean = T > 0 ? sum / T : 0.0;
-    double c;
-    if (grouped_ok)
-      c = H == 16 ? 3.0 : (H == 32 ? 2.4 : 2.2);
-    else
-      c = H == 128 ? 1.9 : 3.7;
-    if (mean <= c * k) return DSA_ROUTING_MASKED;
+    if (mean <= masked_threshold(H, mha_dv, grouped_ok) * k) return DSA_ROUTING_MASKED;
   }
   return grouped_ok ? DSA_ROUTING_GROUPED : DSA_ROUTING_PERTOKEN;
 }
@@ -259,10 +271,9 @@ int dsa_masked_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint
                            const uint16_t* v, const int32_t* topk, int64_t ld, int T, int S, int H,
                            int dn, int dr, int dv, int cols, int64_t q_pos_offset, float scale,
                            uint32_t* mask_ws, uint16_t* out, float* lse, void* stream) {
-  // geometries: NoPE (256, 0, 256), the key is k_nope itself; (192, 64, 256), the key is
-  // k_nope || k_pe with k_pe shared by every head
-  const bool nope = dn == 256 && dr == 0 && dv == 256;
-  const bool rope = dn == 192 && dr == 64 && dv == 256;
+  // geometries: NoPE (256, 0, 256), the key is k_nope itself; (192, 64, 256) and
+  // (128, 64, 128), the key is k_nope || k_pe with k_pe shared by every head
+  const bool nope = mha_nope(dn, dr, dv), rope = mha_rope(dn, dr, dv);
   if ((!nope && !rope) || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
   if (H < 1 || T < 0 || S < 1 || cols < 0 || ld < cols || q_pos_offset < 0) return DSA_ERR_SHAPE;
   if (T == 0) return DSA_OK;
@@ -276,16 +287,15 @@ int dsa_masked_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint
   hipError_t e = dsa::launch_scatter_topk_bits(topk, ld, T, cols, S, q_pos_offset, mask_ws, words,
                                                (hipStream_t)stream);
   if (e != hipSuccess) return DSA_ERR_LAUNCH;
-  return launch_status(dsa::launch_masked_mha(q, k_nope, rope ? k_pe : nullptr, dn, v, mask_ws, words, T,
-                                              S, H, q_pos_offset, scale, out, lse,
+  return launch_status(dsa::launch_masked_mha(q, k_nope, rope ? k_pe : nullptr, dn, dr, dv, v, mask_ws,
+                                              words, T, S, H, q_pos_offset, scale, out, lse,
                                               (hipStream_t)stream));
 }
 
 int dsa_dense_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_pe,
                           const uint16_t* v, int T, int S, int H, int dn, int dr, int dv,
                           int64_t q_pos_offset, float scale, uint16_t* out, float* lse, void* stream) {
-  const bool nope = dn == 256 && dr == 0 && dv == 256;
-  const bool rope = dn == 192 && dr == 64 && dv == 256;
+  const bool nope = mha_nope(dn, dr, dv), rope = mha_rope(dn, dr, dv);
   if ((!nope && !rope) || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
   if (H < 1 || T < 0 || S < 1 || q_pos_offset < 0) return DSA_ERR_SHAPE;
   if (T == 0) return DSA_OK;
@@ -293,8 +303,8 @@ int dsa_dense_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint1
   if (!aligned_to(q, 16) || !aligned_to(k_nope, 16) || !aligned_to(v, 16) ||
       !aligned_to(out, 16) || !aligned_to(lse, 4) || (rope && !aligned_to(k_pe, 16)))
     return DSA_ERR_ALIGN;
-  return launch_status(dsa::launch_masked_mha(q, k_nope, rope ? k_pe : nullptr, dn, v, nullptr, 0, T, S,
-                                              H, q_pos_offset, scale, out, lse, (hipStream_t)stream));
+  return launch_status(dsa::launch_masked_mha(q, k_nope, rope ? k_pe : nullptr, dn, dr, dv, v, nullptr, 0,
+                                              T, S, H, q_pos_offset, scale, out, lse, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -61,11 +61,12 @@ hipError_t launch_rows128_exact(const uint16_t* q, const uint16_t* kv, const int
                                 uint16_t* out, float* lse, hipStream_t stream, const int32_t* group_info,
                                 int ngroups, int d_qk);
 
-// masked dense MHA, qk 256 = k_nope dn (256 or 192) + shared k_pe (0 or 64), v 256,
-// mask = causal AND top-k bit; bits == nullptr: causal only (dense MHA)
+// masked dense MHA, key = k_nope (dn) + shared k_pe (dr), value dv: (256, 0, 256),
+// (192, 64, 256) or (128, 64, 128); mask = causal AND top-k bit; bits == nullptr: causal
+// only (dense MHA)
 hipError_t launch_masked_mha(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_pe, int dn,
-                             const uint16_t* v, const uint32_t* bits, int words, int T, int S, int H,
-                             int64_t q_pos_offset, float scale, uint16_t* out, float* lse,
+                             int dr, int dv, const uint16_t* v, const uint32_t* bits, int words, int T,
+                             int S, int H, int64_t q_pos_offset, float scale, uint16_t* out, float* lse,
                              hipStream_t stream);
 
 }  // namespace dsa

@@ -1,28 +1,31 @@
-// Masked dense MHA for sparse-MLA prefill, NoPE layout (qk 256 = nope 256 +
-// rope 0, v 256).
+// Masked dense MHA for sparse-MLA prefill, and its mask-free special case (dense
+// causal MHA), for the per-head geometries (qk_nope, qk_rope, v) = (256, 0, 256),
+// (192, 64, 256) and (128, 64, 128).
 //
 // Definition ("[2/N][Attention] Enable masked MHA for sparse MLA prefills",
 // Purpose section; "[Perf][GLM-5.3-Flash] Dense/masked-MHA sparse prefill for
-// the NoPE (256, 0, 256) layout + skip the NoPE K concat", commit messages):
-// below a length threshold, full-head attention over the up-projected per-head
-// K and V with mask = causal AND top-k membership simulates DSA; with no rope
-// part the key is k_nope itself, so no K concat is built -- this kernel reads
-// k_nope in place.  Token t sits at position q_pos_offset + t (chunked
-// context); the membership bits come from the bit-packed [T, ceil(S/32)] mask
-// that scatter_topk_bits_kernel writes.
+// the NoPE (256, 0, 256) layout + skip the NoPE K concat", commit messages and
+// the masked-MHA allow-list of its description): below a length threshold,
+// full-head attention over the up-projected per-head K and V with mask =
+// causal AND top-k membership simulates DSA.  The key of a head is k_nope
+// followed by the k_pe shared by all heads; with no rope part it is k_nope
+// itself, and either way this kernel reads both in place (no K concat is
+// built).  Token t sits at position q_pos_offset + t (chunked context); the
+// membership bits come from the bit-packed [T, ceil(S/32)] mask that
+// scatter_topk_bits_kernel writes.
 //
 // MI355X design (one workgroup of 8 waves per (256-query tile, head); 2 waves
 // per SIMD):
-//  * each wave owns 32 query rows; their 256-dim queries sit in registers as
-//    the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16, the full-rate
-//    shape on gfx950);
-//  * 32-key tiles of K and V (512 B per key row of one head) and the matching
-//    mask words stream through a 3-stage LDS ring by asynchronous global->LDS
-//    DMA, two tiles ahead of the compute; one barrier per tile.  Each wave
-//    copy moves 128 B of 8 consecutive key rows into the swizzled 8-row-group
-//    layout (common.h), so a lane's source address is its row plus an
-//    immediate, and every operand read is a per-lane base plus an immediate
-//    with no LDS bank conflicts;
+//  * each wave owns 32 query rows; their queries (up to 12 k-steps in
+//    registers, the rest in a lane-private LDS area) are the B operand of
+//    S^T = K Q^T (v_mfma_f32_32x32x16_bf16, the full-rate shape on gfx950);
+//  * 32-key tiles of K and V (one head's rows) and the matching mask words
+//    stream through a 3-stage LDS ring by asynchronous global->LDS DMA, two
+//    tiles ahead of the compute; one barrier per tile.  Each wave copy moves
+//    128 B of 8 consecutive key rows into the swizzled 8-row-group layout
+//    (common.h), so a lane's source address is its row plus an immediate, and
+//    every operand read is a per-lane base plus an immediate with no LDS bank
+//    conflicts;
 //  * the causal test and the top-k bit select scores in registers (bit-field
 //    insert of -inf); the running max is taken on raw scores and the softmax
 //    scale is folded into one fused multiply-add before the base-2
@@ -37,38 +40,40 @@
 
 namespace dsa {
 
-constexpr int kMD = 256;                              // qk and v head dim
 constexpr int kMWaves = 8;
 constexpr int kMThreads = 64 * kMWaves;
 constexpr int kMQ = 32 * kMWaves;                     // query rows per workgroup
 constexpr int kMKeys = 32;                            // keys per tile
 constexpr int kMStages = 3;
-constexpr int kMGroupBytes = 8 * kMD * 2;             // 8 key rows of 512 B
-constexpr int kMTileBytes = kMKeys * kMD * 2;         // K (or V) tile: 16 KiB
-constexpr int kMStageBytes = 2 * kMTileBytes;
-constexpr int kMCopiesPerWave = kMStageBytes / 1024 / kMWaves;  // 4
-constexpr int kMOpsPerTile = kMCopiesPerWave + 1;     // + the mask-word copy
 constexpr float kRescaleSlack = 8.f;                  // rescale O only when the max grows by > 2^8
-constexpr int kMQRegSteps = 12;                       // query k-steps kept in registers (of 16)
-constexpr int kMQLdsSteps = kMD / 16 - kMQRegSteps;   // the rest sit in LDS (lane-private)
-static_assert(kMStageBytes == 1024 * kMWaves * kMCopiesPerWave, "copies split evenly over waves");
+constexpr int kMQRegMax = 12;                         // query k-steps kept in registers (at most)
 
-// kDN: the k_nope width (256: NoPE layout, K = k_nope; 192: K = k_nope || k_pe with the
-// 64-wide k_pe shared by all heads); the query/key width is 256 either way.
+// Geometry (kDN, kDR, kDV): the key is k_nope (kDN dims, per head) followed by k_pe (kDR
+// dims, shared by every head), the value kDV dims per head: (256, 0, 256) NoPE -- K is
+// k_nope itself; (192, 64, 256); (128, 64, 128).
 // kDense: plain causal attention (every causal key selected): no mask words are copied and
 // tiles below the diagonal of all of a wave's rows skip the select.
-template <int kDN, bool kDense>
+template <int kDN, int kDR, int kDV, bool kDense>
 __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ kpe,
     const uint16_t* __restrict__ v, const uint32_t* __restrict__ bits, int words, int T, int S,
     int H, int64_t q_pos_offset, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse) {
-  constexpr int kDR = kMD - kDN;
-  static_assert(kDN % 64 == 0 && kDR >= 0, "k_nope covers whole 128-byte blocks of the key row");
-  __shared__ __align__(16) uint8_t stage[kMStages][kMStageBytes];
+  constexpr int kDQK = kDN + kDR;
+  static_assert(kDN % 64 == 0 && kDR % 64 == 0 && kDV % 64 == 0, "whole 128-byte blocks per row");
+  constexpr int kKBlocks = kDQK / 64, kVBlocks = kDV / 64;  // 1 KiB blocks per 8-row group
+  constexpr int kKGroupBytes = 1024 * kKBlocks, kVGroupBytes = 1024 * kVBlocks;
+  constexpr int kKTileBytes = 4 * kKGroupBytes;         // 32 keys of K
+  constexpr int kStageBytes = kKTileBytes + 4 * kVGroupBytes;
+  constexpr int kQSteps = kDQK / 16;                    // k-steps of S^T = K Q^T
+  constexpr int kQRegSteps = kQSteps < kMQRegMax ? kQSteps : kMQRegMax;
+  constexpr int kQLdsSteps = kQSteps - kQRegSteps;      // the rest sit in LDS (lane-private)
+  constexpr int kCB = kDV / 32;                         // O^T column blocks
+  // copies per wave per tile (K waves 0..3, V waves 4..7), + the mask-word copy
+  constexpr int kOpsK = kKBlocks + (kDense ? 0 : 1), kOpsV = kVBlocks + (kDense ? 0 : 1);
+  __shared__ __align__(16) uint8_t stage[kMStages][kStageBytes];
   __shared__ __align__(16) uint32_t maskw[kDense ? 1 : kMStages][kMWaves][64];
-  constexpr int kOps = kDense ? kMCopiesPerWave : kMOpsPerTile;  // copies per wave per tile
-  __shared__ __align__(16) uint4 qlds[kMWaves][kMQLdsSteps][64];
+  __shared__ __align__(16) uint4 qlds[kMWaves][kQLdsSteps > 0 ? kQLdsSteps : 1][64];
 
   // longest query tiles first; consecutive blocks take consecutive heads, so the
   // round-robin XCD dispatch keeps each head on one XCD and balances the work
@@ -90,25 +95,25 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
   // running max can be taken on raw scores
   const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
   const float sc = fabsf(scale_log2);
-  // (steps kMQRegSteps.. go to a lane-private LDS area: the registers are needed to keep
+  // (steps kQRegSteps.. go to a lane-private LDS area: the registers are needed to keep
   // operand reads in flight)
-  bf16x8 qreg[kMQRegSteps];
+  bf16x8 qreg[kQRegSteps];
   {
-    const uint16_t* qrow = q + ((size_t)row * H + h) * kMD + 8 * hi;
+    const uint16_t* qrow = q + ((size_t)row * H + h) * kDQK + 8 * hi;
 #pragma unroll
-    for (int s = 0; s < kMD / 16; ++s) {
+    for (int s = 0; s < kQSteps; ++s) {
       uint4 w = {0u, 0u, 0u, 0u};
       if (live) w = *reinterpret_cast<const uint4*>(qrow + 16 * s);
       w.x ^= qsign; w.y ^= qsign; w.z ^= qsign; w.w ^= qsign;
-      if (s < kMQRegSteps)
+      if (s < kQRegSteps)
         qreg[s] = __builtin_bit_cast(bf16x8, w);
       else
-        qlds[wave][s - kMQRegSteps][lane] = w;
+        qlds[wave][s - kQRegSteps][lane] = w;
     }
   }
   // complete the query loads now, before any asynchronous copy is in flight
 #pragma unroll
-  for (int s = 0; s < kMQRegSteps; ++s) asm volatile("" : : "v"(qreg[s]));
+  for (int s = 0; s < kQRegSteps; ++s) asm volatile("" : : "v"(qreg[s]));
 
   const int last = min(T, q0 + kMQ) - 1;
   int64_t kend64 = q_pos_offset + last + 1;
@@ -117,18 +122,20 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
   const int ntiles = (kend + kMKeys - 1) / kMKeys;
   const int mrow = min(row, T - 1);
 
-  // copies: wave w fills K (w < 4) or V (w >= 4) rows 8 (w % 4) .. + 7, blocks 0..3;
-  // lane l takes row l / 8 of the group, position l % 8 (chunk 8 c + pos ^ swizzle)
+  // copies: wave w fills K (w < 4, kKBlocks blocks) or V (w >= 4, kVBlocks blocks) rows
+  // 8 (w % 4) .. + 7; lane l takes row l / 8 of the group, position l % 8 (chunk 8 c + pos
+  // ^ swizzle)
+  const bool kwave = wave < 4;
   const int cgrp = wave & 3;
   const int crow = 8 * cgrp + (lane >> 3);
   const int cchunk = (lane & 7) ^ swz8(lane >> 3) ^ cgrp;
   // (K rows: blocks 0 .. kDN / 64 - 1 from k_nope, the rest from k_pe)
-  const int kdim = wave < 4 ? kDN : kMD;
-  const uint16_t* cbase = (wave < 4 ? k : v) + (size_t)h * kdim + 8 * cchunk;
+  const int kdim = kwave ? kDN : kDV;
+  const uint16_t* cbase = (kwave ? k : v) + (size_t)h * kdim + 8 * cchunk;
   const size_t key_stride = (size_t)H * kdim;
   // k_pe element e of a row sits at dim kDN + e of the key row
   const uint16_t* pbase = kDR > 0 ? kpe + 8 * cchunk - kDN : cbase;
-  const uint32_t cdst = (wave < 4 ? 0 : kMTileBytes) + cgrp * kMGroupBytes;
+  const uint32_t cdst = kwave ? cgrp * kKGroupBytes : kKTileBytes + cgrp * kVGroupBytes;
 
   auto issue = [&](int t) {
     int key = t * kMKeys + crow;
@@ -138,25 +145,27 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
     const uint32_t dst = lds_addr(stage[t % kMStages]) + cdst;
     // (the global address carries the block offset: an instruction offset would also
     // move the LDS destination of an LDS-DMA load)
+    if (kwave) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const bool from_pe = kDR > 0 && wave < 4 && 64 * c >= kDN;
-      dma16((from_pe ? psrc : src) + 64 * c, dst + 1024 * c);
+      for (int c = 0; c < kKBlocks; ++c) dma16((kDR > 0 && 64 * c >= kDN ? psrc : src) + 64 * c, dst + 1024 * c);
+    } else {
+#pragma unroll
+      for (int c = 0; c < kVBlocks; ++c) dma16(src + 64 * c, dst + 1024 * c);
     }
     if constexpr (!kDense)
       dma4(bits + (size_t)mrow * words + ((t * kMKeys) >> 5), lds_addr(&maskw[t % kMStages][wave][0]));
   };
 
   float m_run = kNegInf, l_run = 0.f;  // m_run: reference max of the exponents (log2 units)
-  f32x16 o[kMD / 32];
+  f32x16 o[kCB];
 #pragma unroll
-  for (int cb = 0; cb < kMD / 32; ++cb) o[cb] = f32x16{};
+  for (int cb = 0; cb < kCB; ++cb) o[cb] = f32x16{};
 
   // K reads (A of S^T): row m, chunk 2 s + hi -> 4 bases, one per s % 4, plus (s / 4) KiB
   const int kx = swz8(m & 7) ^ (m >> 3) ^ hi;
   int kofs[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) kofs[u] = (m >> 3) * kMGroupBytes + (m & 7) * 128 + 16 * ((2 * u) ^ kx);
+  for (int u = 0; u < 4; ++u) kofs[u] = (m >> 3) * kKGroupBytes + (m & 7) * 128 + 16 * ((2 * u) ^ kx);
   // transposed V reads: row 16 st + 8 uu + 4 hi + s16 / 4, columns 32 cb + 16 (g16 % 2) + 4 (s16 % 4)
   const int g16 = lane >> 4, s16 = lane & 15;
   const int vr8 = 4 * hi + (s16 >> 2);
@@ -166,17 +175,19 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
   if (ntiles > 0) issue(0);
   if (ntiles > 1) issue(1);
   for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles)
-      wait_vmcnt<kOps>();
-    else
+    if (t + 1 >= ntiles)
       wait_vmcnt<0>();
+    else if (kwave)
+      wait_vmcnt<kOpsK>();
+    else
+      wait_vmcnt<kOpsV>();
     __syncthreads();  // tile t visible to all waves; stage (t + 2) % 3 free
     if (t + 2 < ntiles) issue(t + 2);
 
     // one stage offset per iteration (kept opaque so no per-stage address sets are hoisted)
-    const int sofs = loop_local((t % kMStages) * kMStageBytes);
+    const int sofs = loop_local((t % kMStages) * kStageBytes);
     const uint8_t* kt = &stage[0][0] + sofs;
-    const uint8_t* vt = kt + kMTileBytes;
+    const uint8_t* vt = kt + kKTileBytes;
     const int k0 = t * kMKeys;
 
     // K operand reads run kMAhead steps ahead of the MFMAs (the order is pinned: left to
@@ -186,8 +197,8 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
       return *reinterpret_cast<const bf16x8*>(kt + kofs[s & 3] + 1024 * (s >> 2));
     };
     auto qread = [&](int s) -> bf16x8 {
-      return s < kMQRegSteps ? qreg[s < kMQRegSteps ? s : 0]
-                             : *reinterpret_cast<const bf16x8*>(qb + 1024 * (s - kMQRegSteps));
+      return s < kQRegSteps ? qreg[s < kQRegSteps ? s : 0]
+                            : *reinterpret_cast<const bf16x8*>(qb + 1024 * (s - kQRegSteps));
     };
     constexpr int kMAhead = 4;
     bf16x8 kw[kMAhead], qw[kMAhead];
@@ -198,10 +209,10 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
     }
     f32x16 sacc = {};
 #pragma unroll
-    for (int s = 0; s < kMD / 16; ++s) {
+    for (int s = 0; s < kQSteps; ++s) {
       __builtin_amdgcn_sched_barrier(0);
       sacc = mfma32x32x16(kw[s % kMAhead], qw[s % kMAhead], sacc);
-      if (s + kMAhead < kMD / 16) {
+      if (s + kMAhead < kQSteps) {
         kw[s % kMAhead] = kread(s + kMAhead);
         qw[s % kMAhead] = qread(s + kMAhead);
       }
@@ -244,7 +255,7 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
       const float alpha = need ? fast_exp2(m_run - mt) : 1.f;  // 0 when m_run = -inf
       l_run *= alpha;
 #pragma unroll
-      for (int cb = 0; cb < kMD / 32; ++cb) o[cb] *= alpha;
+      for (int cb = 0; cb < kCB; ++cb) o[cb] *= alpha;
       m_run = need ? mt : m_run;
     }
     const float nm = m_run == kNegInf ? 0.f : -m_run;
@@ -260,15 +271,15 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
 
     // O^T += V^T P^T: step st covers keys 16 st .. 16 st + 15 with k-slot (hi, i) <->
     // key 16 st + 8 (i / 4) + 4 hi + i % 4, i.e. accumulator registers 8 st .. 8 st + 7
-    // MFMA i (0..15) is step i / 8, column block i % 8; its V^T operand is read kMVAhead
-    // MFMAs ahead (order pinned as for QK)
+    // MFMA i (0 .. 2 kCB - 1) is step i / kCB, column block i % kCB; its V^T operand is read
+    // kMVAhead MFMAs ahead (order pinned as for QK)
     auto vread = [&](int i) -> bf16x8 {
-      const int st = i >> 3, cb = i & 7;
+      const int st = i / kCB, cb = i % kCB;
       // rows 16 st + 8 uu + vr8 are in group 2 st + uu; chunk 4 cb + c2 is in block cb / 2
       const int p0 = 16 * (vx ^ (4 * (cb & 1)) ^ (2 * st));
       const int p1 = 16 * (vx ^ (4 * (cb & 1)) ^ (2 * st + 1));
-      const u16x4 lo = lds_read_tr16(vt + (2 * st) * kMGroupBytes + 1024 * (cb >> 1) + vbase + p0);
-      const u16x4 up = lds_read_tr16(vt + (2 * st + 1) * kMGroupBytes + 1024 * (cb >> 1) + vbase + p1);
+      const u16x4 lo = lds_read_tr16(vt + (2 * st) * kVGroupBytes + 1024 * (cb >> 1) + vbase + p0);
+      const u16x4 up = lds_read_tr16(vt + (2 * st + 1) * kVGroupBytes + 1024 * (cb >> 1) + vbase + p1);
       return __builtin_bit_cast(bf16x8, u16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
     };
     constexpr int kMVAhead = 3;
@@ -276,10 +287,10 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
 #pragma unroll
     for (int i = 0; i < kMVAhead; ++i) vw[i] = vread(i);
 #pragma unroll
-    for (int i = 0; i < 2 * (kMD / 32); ++i) {
+    for (int i = 0; i < 2 * kCB; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-      o[i & 7] = mfma32x32x16(vw[i % kMVAhead], bop[i >> 3], o[i & 7]);
-      if (i + kMVAhead < 2 * (kMD / 32)) vw[i % kMVAhead] = vread(i + kMVAhead);
+      o[i % kCB] = mfma32x32x16(vw[i % kMVAhead], bop[i / kCB], o[i % kCB]);
+      if (i + kMVAhead < 2 * kCB) vw[i % kMVAhead] = vread(i + kMVAhead);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -288,9 +299,9 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
   if (!live) return;
   // o[cb][j] = O^T[col 32 cb + 8 (j / 4) + 4 hi + j % 4][row]
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  uint16_t* orow = out + ((size_t)row * H + h) * kMD + 4 * hi;
+  uint16_t* orow = out + ((size_t)row * H + h) * kDV + 4 * hi;
 #pragma unroll
-  for (int cb = 0; cb < kMD / 32; ++cb)
+  for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const bf16x4 w = {(__bf16)(o[cb][4 * jj + 0] * inv), (__bf16)(o[cb][4 * jj + 1] * inv),
@@ -301,33 +312,33 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
     lse[(size_t)row * H + h] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
 }
 
-template <int kDN, bool kDense>
+template <int kDN, int kDR, int kDV>
 static void launch_mha(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_pe,
                        const uint16_t* v, const uint32_t* bits, int words, int T, int S, int H,
                        int64_t q_pos_offset, float scale, uint16_t* out, float* lse, hipStream_t stream) {
   const long long blocks = (long long)((T + kMQ - 1) / kMQ) * H;
-  hipLaunchKernelGGL((masked_mha_kernel<kDN, kDense>), dim3((unsigned)blocks), dim3(kMThreads), 0, stream,
-                     q, k_nope, k_pe, v, bits, words, T, S, H, q_pos_offset, scale * kLog2e, out, lse);
+  // no membership bits: every causal key is selected (plain causal attention)
+  if (bits == nullptr)
+    hipLaunchKernelGGL((masked_mha_kernel<kDN, kDR, kDV, true>), dim3((unsigned)blocks), dim3(kMThreads), 0,
+                       stream, q, k_nope, k_pe, v, bits, words, T, S, H, q_pos_offset, scale * kLog2e, out,
+                       lse);
+  else
+    hipLaunchKernelGGL((masked_mha_kernel<kDN, kDR, kDV, false>), dim3((unsigned)blocks), dim3(kMThreads), 0,
+                       stream, q, k_nope, k_pe, v, bits, words, T, S, H, q_pos_offset, scale * kLog2e, out,
+                       lse);
 }
 
 hipError_t launch_masked_mha(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_pe, int dn,
-                             const uint16_t* v, const uint32_t* bits, int words, int T, int S, int H,
-                             int64_t q_pos_offset, float scale, uint16_t* out, float* lse,
+                             int dr, int dv, const uint16_t* v, const uint32_t* bits, int words, int T,
+                             int S, int H, int64_t q_pos_offset, float scale, uint16_t* out, float* lse,
                              hipStream_t stream) {
   if (T <= 0 || H <= 0) return hipSuccess;
-  // no membership bits: every causal key is selected (plain causal attention)
-  const bool dense = bits == nullptr;
-  if (dn == 192) {
-    if (dense)
-      launch_mha<192, true>(q, k_nope, k_pe, v, bits, words, T, S, H, q_pos_offset, scale, out, lse, stream);
-    else
-      launch_mha<192, false>(q, k_nope, k_pe, v, bits, words, T, S, H, q_pos_offset, scale, out, lse, stream);
-  } else {
-    if (dense)
-      launch_mha<256, true>(q, k_nope, k_pe, v, bits, words, T, S, H, q_pos_offset, scale, out, lse, stream);
-    else
-      launch_mha<256, false>(q, k_nope, k_pe, v, bits, words, T, S, H, q_pos_offset, scale, out, lse, stream);
-  }
+  if (dn == 128 && dr == 64 && dv == 128)
+    launch_mha<128, 64, 128>(q, k_nope, k_pe, v, bits, words, T, S, H, q_pos_offset, scale, out, lse, stream);
+  else if (dn == 192 && dr == 64 && dv == 256)
+    launch_mha<192, 64, 256>(q, k_nope, k_pe, v, bits, words, T, S, H, q_pos_offset, scale, out, lse, stream);
+  else
+    launch_mha<256, 0, 256>(q, k_nope, k_pe, v, bits, words, T, S, H, q_pos_offset, scale, out, lse, stream);
   return hipGetLastError();
 }
 

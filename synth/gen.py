@@ -204,6 +204,11 @@ CONFIGS = {
     # (256, 0, 256) model; otherwise the shapes and top-k recipe of c3.
     "c7_glm16k_latent512": Config("c7_glm16k_latent512", T=16384, S=16384, H=16, k=2048,
                                   cols=2048, G=8, scale=1.0 / 16.0, seed=7, d_qk=512),
+    # Masked dense MHA in the DeepSeek-V3.2 geometry (qk 192 = nope 128 + shared rope 64,
+    # v 128) at 128 heads, over the chunk and top-k recipe of c2.
+    "c8_masked_dsv32": Config("c8_masked_dsv32", T=4096, S=4096, H=128, k=2048, cols=2048, G=1,
+                              scale=1.0 / math.sqrt(192.0), seed=8, kind="mha", d_qk=192, d_v=128,
+                              dn=128, dr=64, dv=128),
     # Long prompt: the last 21504 of 32768 positions are queries; 2176-wide top-k buffer.
     "c5_long": Config("c5_long", T=21504, S=32768, H=16, k=2048, cols=2176, G=8,
                       scale=1.0 / 16.0, seed=4, q_pos_offset=11264),

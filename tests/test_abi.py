@@ -143,6 +143,10 @@ def test_masked_mha_validation(lib):
     assert mha_call(lib, dn=192, dr=64, kp=P + 2) == ALIGN
     assert mha_call(lib, dn=192, dr=64, kp=P, T=0) == OK
     assert mha_call(lib, dn=256, dr=64) == UNSUP and mha_call(lib, dn=192, dr=64, dv=128) == UNSUP
+    # (128, 64, 128): the DeepSeek-V3.2 geometry
+    assert mha_call(lib, dn=128, dr=64, dv=128) == NULL
+    assert mha_call(lib, dn=128, dr=64, dv=128, kp=P, T=0) == OK
+    assert mha_call(lib, dn=128, dr=0, dv=128) == UNSUP and mha_call(lib, dn=128, dr=64, dv=256) == UNSUP
     assert mha_call(lib, dn=128) == UNSUP and mha_call(lib, dv=128) == UNSUP
     assert mha_call(lib, H=0) == SHAPE and mha_call(lib, ld=8) == SHAPE
     assert mha_call(lib, T=0) == OK

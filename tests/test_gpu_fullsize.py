@@ -80,7 +80,7 @@ def test_grouped_equals_pertoken_everywhere(full):
     assert (lg[fin] - lp[fin]).abs().max().item() <= 2e-3
 
 
-@pytest.mark.parametrize("name", ["c4_masked_nope", "c6_masked_rope"])
+@pytest.mark.parametrize("name", ["c4_masked_nope", "c6_masked_rope", "c8_masked_dsv32"])
 def test_masked_mha_full(name):
     from mla_prefill_amd import routings
     c = make_case(CONFIGS[name])

@@ -268,7 +268,15 @@ MHA_CASES = [
     ("rope_causal_ragged", 24, 150, 150, 2, 40, 45, 0, "locality", 192, 64),
     ("rope_chunked_ctx", 25, 100, 230, 3, 64, 70, 130, "uniform", 192, 64),
     ("rope_all_selected", 26, 300, 300, 2, 300, 300, 0, "uniform", 192, 64),
+    # (128, 64, 128): K = k_nope (128) || k_pe (64), v 128
+    ("dsv_causal_ragged", 27, 150, 150, 3, 40, 45, 0, "locality", 128, 64),
+    ("dsv_chunked_ctx", 28, 100, 230, 2, 64, 70, 130, "uniform", 128, 64),
+    ("dsv_all_selected", 29, 280, 280, 1, 280, 290, 0, "uniform", 128, 64),
 ]
+
+
+def mha_dv(dn):
+    return 128 if dn == 128 else 256
 
 
 @pytest.mark.parametrize("case", MHA_CASES, ids=[c[0] for c in MHA_CASES])
@@ -278,7 +286,7 @@ def test_masked_mha_parity(R, case):
     q = normal_bf16(rng, (T, H, dn + dr))
     kn = normal_bf16(rng, (S, H, dn))
     kp = normal_bf16(rng, (S, dr)) if dr else None
-    v = normal_bf16(rng, (S, H, 256))
+    v = normal_bf16(rng, (S, H, mha_dv(dn)))
     topk = (topk_uniform(rng, T, S, k, cols, P0) if mode == "uniform"
             else topk_locality(rng, T, S, k, cols, 8, P0))
     topk = shuffle_rows(topk, seed)
@@ -303,6 +311,8 @@ DENSE_CASES = [
     ("positions_past_S", 32, 70, 90, 1, 60, 256, 0),
     ("rope_causal", 33, 280, 280, 2, 0, 192, 64),
     ("rope_chunked_ctx", 34, 90, 300, 2, 210, 192, 64),
+    ("dsv_causal", 36, 270, 270, 2, 0, 128, 64),
+    ("dsv_chunked_ctx", 37, 80, 300, 3, 220, 128, 64),
 ]
 
 
@@ -313,7 +323,7 @@ def test_dense_mha_parity(R, case):
     q = normal_bf16(rng, (T, H, dn + dr))
     kn = normal_bf16(rng, (S, H, dn))
     kp = normal_bf16(rng, (S, dr)) if dr else None
-    v = normal_bf16(rng, (S, H, 256))
+    v = normal_bf16(rng, (S, H, mha_dv(dn)))
     scale = 1.0 / 16.0
     out, lse = R.dense_mha(dev_bf16(q), dev_bf16(kn), None if kp is None else dev_bf16(kp), dev_bf16(v),
                            P0, scale)
@@ -321,18 +331,17 @@ def test_dense_mha_parity(R, case):
     check_attention(out, lse, ref_out, ref_lse, label)
 
 
-@pytest.mark.parametrize("dr", [0, 64])
-def test_dense_mha_equals_masked_when_topk_covers_the_chunk(R, dr):
+@pytest.mark.parametrize("dn,dr", [(256, 0), (192, 64), (128, 64)])
+def test_dense_mha_equals_masked_when_topk_covers_the_chunk(R, dn, dr):
     """q_pos_offset + T <= k: both kernels do the same arithmetic on the same keys, so the
     outputs agree bit for bit."""
-    rng = np.random.default_rng(35 + dr)
+    rng = np.random.default_rng(35 + dr + dn)
     T, P0, H = 520, 40, 2
     S = P0 + T
-    dn = 256 - dr
-    q = dev_bf16(normal_bf16(rng, (T, H, 256)))
+    q = dev_bf16(normal_bf16(rng, (T, H, dn + dr)))
     kn = dev_bf16(normal_bf16(rng, (S, H, dn)))
     kp = dev_bf16(normal_bf16(rng, (S, dr))) if dr else None
-    v = dev_bf16(normal_bf16(rng, (S, H, 256)))
+    v = dev_bf16(normal_bf16(rng, (S, H, mha_dv(dn))))
     topk = shuffle_rows(topk_uniform(rng, T, S, S, S, P0), 35)
     om, lm, _ = R.masked_mha(q, kn, kp, v, dev_i32(topk), P0, 0.0625)
     od, ld = R.dense_mha(q, kn, kp, v, P0, 0.0625)

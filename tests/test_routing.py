@@ -16,48 +16,60 @@ def pick():
 
 
 def test_dense_when_the_chunk_fits_in_the_top_k(pick):
-    assert pick(1024, 1024, 0, 16, 2048, True) == "dense"
-    assert pick(2048, 2048, 0, 128, 2048, True) == "dense"
-    assert pick(1000, 2000, 1000, 16, 2048, True) == "dense"      # q_pos_offset + T = k
-    assert pick(1049, 2049, 1000, 16, 2048, True) == "masked"     # one position more
-    assert pick(1024, 1024, 0, 16, 2048, False) == "grouped"      # no MHA inputs
+    assert pick(1024, 1024, 0, 16, 2048, 256) == "dense"
+    assert pick(2048, 2048, 0, 128, 2048, 256) == "dense"
+    assert pick(1000, 2000, 1000, 16, 2048, 256) == "dense"      # q_pos_offset + T = k
+    assert pick(1049, 2049, 1000, 16, 2048, 256) == "masked"     # one position more
+    assert pick(1024, 1024, 0, 16, 2048, 0) == "grouped"      # no MHA inputs
 
 
 def test_masked_threshold_against_grouped(pick):
     # H 16: c = 3.0, k = 2048 -> mean causal keys <= 6144; a chunk from 0 has mean (L + 1) / 2
-    assert pick(12287, 12287, 0, 16, 2048, True) == "masked"
-    assert pick(12289, 12289, 0, 16, 2048, True) == "grouped"
-    assert pick(8192, 8192, 0, 32, 2048, True) == "masked"
-    assert pick(10240, 10240, 0, 32, 2048, True) == "grouped"
-    assert pick(16384, 16384, 0, 64, 2048, True) == "grouped"
+    assert pick(12287, 12287, 0, 16, 2048, 256) == "masked"
+    assert pick(12289, 12289, 0, 16, 2048, 256) == "grouped"
+    assert pick(8192, 8192, 0, 32, 2048, 256) == "masked"
+    assert pick(10240, 10240, 0, 32, 2048, 256) == "grouped"
+    assert pick(16384, 16384, 0, 64, 2048, 256) == "grouped"
 
 
 def test_masked_threshold_against_pertoken(pick):
-    assert pick(6144, 6144, 0, 128, 2048, True) == "masked"
-    assert pick(8192, 8192, 0, 128, 2048, True) == "per-token"
-    assert pick(8192, 8192, 0, 128, 2048, False) == "per-token"
+    assert pick(6144, 6144, 0, 128, 2048, 256) == "masked"
+    assert pick(8192, 8192, 0, 128, 2048, 256) == "per-token"
+    assert pick(8192, 8192, 0, 128, 2048, 0) == "per-token"
     # H 48: no grouped form (128 % 48 != 0); c = 3.7
-    assert pick(14000, 14000, 0, 48, 2048, True) == "masked"
-    assert pick(16384, 16384, 0, 48, 2048, True) == "per-token"
-    assert pick(16384, 16384, 0, 48, 2048, False) == "per-token"
+    assert pick(14000, 14000, 0, 48, 2048, 256) == "masked"
+    assert pick(16384, 16384, 0, 48, 2048, 256) == "per-token"
+    assert pick(16384, 16384, 0, 48, 2048, 0) == "per-token"
+
+
+def test_thresholds_of_the_dsv32_geometry(pick):
+    # (128, 64, 128): c = 4.3 / 3.4 / 3.1 against grouped, 2.8 at H 128
+    assert pick(17000, 17000, 0, 16, 2048, 128) == "masked"
+    assert pick(18000, 18000, 0, 16, 2048, 128) == "grouped"
+    assert pick(11000, 11000, 0, 128, 2048, 128) == "masked"
+    assert pick(12000, 12000, 0, 128, 2048, 128) == "per-token"
+    assert pick(22000, 22000, 0, 48, 2048, 128) == "masked"
+    from mla_prefill_amd import _lib
+    assert _lib.lib.dsa_select_routing(8192, 8192, 0, 16, 2048, 192) == -3
 
 
 def test_chunked_context_and_positions_past_S(pick):
     # a long prefix: mean causal keys ~ q_pos_offset + T / 2
-    assert pick(512, 30512, 30000, 16, 2048, True) == "grouped"
-    assert pick(512, 5512, 5000, 16, 2048, True) == "masked"
+    assert pick(512, 30512, 30000, 16, 2048, 256) == "grouped"
+    assert pick(512, 5512, 5000, 16, 2048, 256) == "masked"
     # positions past S - 1 see S keys
-    assert pick(100, 3000, 5000, 16, 2048, True) == "masked"
-    assert pick(100, 9000, 9000, 16, 2048, True) == "grouped"
+    assert pick(100, 3000, 5000, 16, 2048, 256) == "masked"
+    assert pick(100, 9000, 9000, 16, 2048, 256) == "grouped"
 
 
 def test_heads_only_the_mha_forms_take(pick):
     from mla_prefill_amd import _lib
-    assert pick(8192, 8192, 0, 8, 2048, True) == "masked"
-    assert pick(1024, 1024, 0, 8, 2048, True) == "dense"
-    assert pick(8192, 8192, 0, 256, 2048, True) == "masked"
+    assert pick(8192, 8192, 0, 8, 2048, 256) == "masked"
+    assert pick(1024, 1024, 0, 8, 2048, 256) == "dense"
+    assert pick(8192, 8192, 0, 256, 2048, 256) == "masked"
     for H in (8, 24, 256):
         assert _lib.lib.dsa_select_routing(8192, 8192, 0, H, 2048, 0) == -3
+    assert pick(8192, 8192, 0, 8, 2048, 128) == "masked"
 
 
 def test_errors():
@@ -70,24 +82,29 @@ def test_errors():
 
 
 def measured_rows():
+    """(mha_dv, H, L, {routing: ms}) of every measured point; mha_dv from the section headers."""
     text = open(os.path.join(ROOT, "profiles", "crossover_mi355x.md")).read()
     rows = []
+    mha_dv = None
     for line in text.splitlines():
+        h = re.match(r"##.*\(mha_dv = (\d+)\)", line)
+        if h:
+            mha_dv = int(h.group(1))
         m = re.match(r"\|\s*(\d+)\s*\|\s*(\d+)\s*\|(.*)\|\s*([\w-]+)\s*\|$", line)
         if m:
             cells = [c.strip() for c in m.group(3).split("|")]
             ms = {name: float(c) for name, c in zip(("dense", "masked", "grouped", "per-token"), cells)
                   if c != "-"}
-            rows.append((int(m.group(1)), int(m.group(2)), ms))
+            rows.append((mha_dv, int(m.group(1)), int(m.group(2)), ms))
     return rows
 
 
 def test_choice_is_near_the_fastest_measured_routing(pick):
-    """At every measured point (both latent widths) the chosen routing is the fastest or within
-    10 % of it."""
+    """At every measured point (both latent widths, both MHA value widths) the chosen routing is
+    the fastest or within 10 % of it."""
     rows = measured_rows()
-    assert len(rows) >= 70
-    for H, L, ms in rows:
-        choice = pick(L, L, 0, H, 2048, True)
-        assert choice in ms, (H, L, choice)
-        assert ms[choice] <= 1.10 * min(ms.values()), (H, L, choice, ms)
+    assert len(rows) >= 110 and {r[0] for r in rows} == {256, 128}
+    for mha_dv, H, L, ms in rows:
+        choice = pick(L, L, 0, H, 2048, mha_dv)
+        assert choice in ms, (mha_dv, H, L, choice)
+        assert ms[choice] <= 1.10 * min(ms.values()), (mha_dv, H, L, choice, ms)
