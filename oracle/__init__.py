@@ -9,12 +9,17 @@ from .dsa_oracle import (  # noqa: F401
     bf16_to_f64,
     convert_req_index_to_global,
     dense_causal_mha,
+    dequant_latent_fp8,
+    dequant_latent_fp8_bf16,
+    f64_to_bf16_bits,
+    fp8_e4m3_to_f64,
     group_union_mask,
     group_union_mask_varlen,
     grouped_sparse_mqa,
     grouped_sparse_mqa_varlen,
     masked_mha,
     pertoken_sparse_mqa,
+    pertoken_sparse_mqa_fp8,
     pertoken_sparse_mqa_varlen,
     physical_row,
     request_of_tokens,

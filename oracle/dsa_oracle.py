@@ -41,6 +41,12 @@ Readings where the pages are silent (each also listed in the design notes):
 * Union list: strictly ascending, -1 padded to union_pad = ceil(G*cols/64)*64.
 * head_group_mask: uint8 [NG, union_pad]; bit i of slot j is set iff token
   gG + i selects union position j; padding slots are 0.
+* FP8 KV latent (the pages only gate quantized caches off the grouped path and
+  define no format): OCP E4M3 codes (uint8) with a float32 scale per row or one
+  for the whole cache; element (x, i) = e4m3(kv8[x, i]) * scale.  The attention
+  is the per-token definition on those exact values.  The GPU path converts each
+  row once to bf16 (float32 product, rounded to nearest even), which
+  ``dequant_latent_fp8_bf16`` states bit for bit.
 * Batches of requests over a paged KV cache ([GROUPED] "How": groups are
   consecutive tokens of one request, and the union's request-local positions
   become physical KV rows through the request's index conversion before the
@@ -268,6 +274,70 @@ def dense_causal_mha(q: np.ndarray, k_nope: np.ndarray, k_pe: Optional[np.ndarra
                 K = np.concatenate([K, kp[: last + 1]], axis=1)
             o, l = softmax_attention(qt[h][None], K, vv[: last + 1, h, :], scale)
             out[n, h], lse[n, h] = o[0], l[0]
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# FP8 KV latent  ([GROUPED] "How": the grouped path is gated off for quantized
+# KV caches; the pages give no FP8 format -- see the module docstring)
+# ---------------------------------------------------------------------------
+
+def fp8_e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Value of OCP FP8 E4M3 codes (uint8): sign bit, 4 exponent bits (bias 7), 3 mantissa
+    bits; exponent 0 holds the subnormals m * 2^-9; S.1111.111 is NaN; no infinities."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def dequant_latent_fp8(kv8: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Latent rows of an FP8 cache: element (x, i) = e4m3(kv8[x, i]) * scale[x] (float64).
+
+    scale: float32 [S] per row, or a single float32 for the whole cache."""
+    v = fp8_e4m3_to_f64(kv8)
+    sc = np.asarray(scale, dtype=np.float32).astype(np.float64)
+    return v * (sc.reshape(-1, 1) if sc.ndim == 1 else sc)
+
+
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of float64 values (round to nearest even through float32)."""
+    f = np.asarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    nan = np.isnan(f)
+    out = rounded.astype(np.uint16)
+    out[nan] = 0x7FC0
+    return out
+
+
+def dequant_latent_fp8_bf16(kv8: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """The bf16 latent the dequantizing pass writes: the float32 product e4m3 * scale,
+    rounded to bf16 (nearest even).  uint16 bit patterns."""
+    v = fp8_e4m3_to_f64(kv8).astype(np.float32)   # exact: every E4M3 value is a float32
+    sc = np.asarray(scale, dtype=np.float32)
+    prod = v * (sc.reshape(-1, 1) if sc.ndim == 1 else sc)  # one float32 rounding
+    return f64_to_bf16_bits(prod)
+
+
+def pertoken_sparse_mqa_fp8(q: np.ndarray, kv8: np.ndarray, scale_kv: np.ndarray, topk: np.ndarray,
+                            S: int, q_pos_offset: int, scale: float, d_v: int = 512,
+                            tokens: Optional[Iterable[int]] = None):
+    """Per-token sparse MQA over an FP8 latent: as ``pertoken_sparse_mqa`` with every latent
+    element e4m3(kv8) * scale_kv taken exactly (float64)."""
+    T, H, _ = q.shape
+    scale = _as_scale(scale)
+    toks = _tokens(T, tokens)
+    kv64 = dequant_latent_fp8(kv8[:S], np.asarray(scale_kv)[:S] if np.ndim(scale_kv) else scale_kv)
+    out = np.zeros((toks.size, H, d_v))
+    lse = np.full((toks.size, H), -np.inf)
+    for n, t in enumerate(toks):
+        sel = selected_positions(topk[t], S, q_pos_offset + int(t))
+        keys = kv64[sel]
+        out[n], lse[n] = softmax_attention(bf16_to_f64(q[t]), keys, keys[:, :d_v], scale)
     return out, lse
 
 

@@ -399,6 +399,92 @@ def test_dense_mha_first_position_sees_one_key():
 
 
 # ---------------------------------------------------------------------------
+# FP8 KV latent
+# ---------------------------------------------------------------------------
+
+def test_fp8_decode_matches_torch_float8_e4m3fn():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = oracle.fp8_e4m3_to_f64(codes)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+    np.testing.assert_array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
+def test_fp8_decode_closed_forms():
+    v = oracle.fp8_e4m3_to_f64(np.array([0x00, 0x01, 0x07, 0x08, 0x38, 0x3C, 0x7E, 0xB8, 0x7F, 0xFF],
+                                        np.uint8))
+    assert v[0] == 0 and v[1] == 2.0 ** -9 and v[2] == 7 * 2.0 ** -9 and v[3] == 2.0 ** -6
+    assert v[4] == 1.0 and v[5] == 1.5 and v[6] == 448.0 and v[7] == -1.0
+    assert np.isnan(v[8]) and np.isnan(v[9])
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(70)
+    x = np.concatenate([rng.standard_normal(5000).astype(np.float32),
+                        # exact ties between two bf16 values, both parities, and specials
+                        np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 0.0, -0.0,
+                                  np.inf, -np.inf, 3.0e38], np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.f64_to_bf16_bits(x), ref)
+
+
+@pytest.mark.parametrize("per_row", [False, True])
+def test_fp8_dequant_bits_match_torch(per_row):
+    rng = np.random.default_rng(71 + per_row)
+    S, d = 37, 40
+    kv8 = rng.integers(0, 256, (S, d)).astype(np.uint8)
+    kv8[(kv8 & 0x7F) == 0x7F] = 0x3A   # no NaN codes in a cache
+    scale = (rng.uniform(0.01, 3.0, S) if per_row else np.float32(0.0371)).astype(np.float32)
+    got = oracle.dequant_latent_fp8_bf16(kv8, scale)
+    f = torch.from_numpy(kv8).view(torch.float8_e4m3fn).float()
+    sc = torch.from_numpy(np.atleast_1d(scale)).float()
+    prod = f * (sc[:, None] if per_row else sc[0])
+    ref = prod.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, ref)
+    np.testing.assert_allclose(oracle.dequant_latent_fp8(kv8, scale), prod.double().numpy(), rtol=1e-7)
+
+
+def test_fp8_attention_equals_bf16_attention_on_exact_values():
+    """A power-of-two scale keeps every dequantized value a bf16 number, so the FP8 definition
+    must equal the (pinned) bf16 one on those bits; per-row scales all equal to it as well."""
+    rng = np.random.default_rng(73)
+    T, S, H, d, dv = 20, 30, 2, 24, 16
+    kv8 = rng.integers(0, 256, (S, d)).astype(np.uint8)
+    kv8[(kv8 & 0x7F) == 0x7F] = 0x41
+    q = normal_bf16(rng, (T, H, d))
+    topk = topk_uniform(rng, T, S, 8, 10, S - T)
+    sc = np.float32(0.125)
+    kv_bits = oracle.dequant_latent_fp8_bf16(kv8, sc)
+    np.testing.assert_array_equal(oracle.bf16_to_f64(kv_bits), oracle.dequant_latent_fp8(kv8, sc))
+    ref = oracle.pertoken_sparse_mqa(q, kv_bits, topk, S, S - T, 0.3, d_v=dv)
+    for scale_kv in (sc, np.full(S, sc, np.float32)):
+        got = oracle.pertoken_sparse_mqa_fp8(q, kv8, scale_kv, topk, S, S - T, 0.3, d_v=dv)
+        np.testing.assert_array_equal(got[0], ref[0])
+        np.testing.assert_array_equal(got[1], ref[1])
+
+
+def test_fp8_per_row_scale_scales_values_only():
+    """Doubling one row's scale doubles that row's value vector and its dot products: with the
+    row as the only selection, out doubles and LSE moves by scale * q.k."""
+    rng = np.random.default_rng(74)
+    S, d = 6, 16
+    kv8 = rng.integers(0, 0x70, (S, d)).astype(np.uint8)
+    q = normal_bf16(rng, (1, 1, d))
+    topk = np.array([[4, -1]], np.int32)
+    s1 = np.full(S, 0.5, np.float32)
+    s2 = s1.copy()
+    s2[4] = 1.0
+    o1, l1 = oracle.pertoken_sparse_mqa_fp8(q, kv8, s1, topk, S, S - 1, 0.2, d_v=8)
+    o2, l2 = oracle.pertoken_sparse_mqa_fp8(q, kv8, s2, topk, S, S - 1, 0.2, d_v=8)
+    np.testing.assert_allclose(o2, 2 * o1, rtol=1e-14)
+    qk = oracle.bf16_to_f64(q[0, 0]) @ oracle.fp8_e4m3_to_f64(kv8[4])
+    np.testing.assert_allclose(l1[0, 0], float(np.float32(0.2)) * 0.5 * qk, rtol=1e-12)
+    np.testing.assert_allclose(l2[0, 0], float(np.float32(0.2)) * 1.0 * qk, rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
 # batches of requests over a paged KV cache
 # ---------------------------------------------------------------------------
 
