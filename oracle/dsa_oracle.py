@@ -43,10 +43,10 @@ Readings where the pages are silent (each also listed in the design notes):
   gG + i selects union position j; padding slots are 0.
 * FP8 KV latent (the pages only gate quantized caches off the grouped path and
   define no format): OCP E4M3 codes (uint8) with a float32 scale per row or one
-  for the whole cache; element (x, i) = e4m3(kv8[x, i]) * scale.  The attention
-  is the per-token definition on those exact values.  The GPU path converts each
-  row once to bf16 (float32 product, rounded to nearest even), which
-  ``dequant_latent_fp8_bf16`` states bit for bit.
+  for the whole cache; element (x, i) = e4m3(kv8[x, i]) * scale.  Attention
+  over such a cache dequantizes it to the bf16 latent the bf16 definition takes
+  -- the float32 product rounded to nearest even, ``dequant_latent_fp8_bf16`` --
+  and is then the per-token definition on those values.
 * Batches of requests over a paged KV cache ([GROUPED] "How": groups are
   consecutive tokens of one request, and the union's request-local positions
   become physical KV rows through the request's index conversion before the
@@ -326,12 +326,13 @@ def dequant_latent_fp8_bf16(kv8: np.ndarray, scale: np.ndarray) -> np.ndarray:
 def pertoken_sparse_mqa_fp8(q: np.ndarray, kv8: np.ndarray, scale_kv: np.ndarray, topk: np.ndarray,
                             S: int, q_pos_offset: int, scale: float, d_v: int = 512,
                             tokens: Optional[Iterable[int]] = None):
-    """Per-token sparse MQA over an FP8 latent: as ``pertoken_sparse_mqa`` with every latent
-    element e4m3(kv8) * scale_kv taken exactly (float64)."""
+    """Per-token sparse MQA over an FP8 latent: the latent dequantized to bf16
+    (``dequant_latent_fp8_bf16``), then ``pertoken_sparse_mqa``'s definition on it."""
     T, H, _ = q.shape
     scale = _as_scale(scale)
     toks = _tokens(T, tokens)
-    kv64 = dequant_latent_fp8(kv8[:S], np.asarray(scale_kv)[:S] if np.ndim(scale_kv) else scale_kv)
+    sc = np.asarray(scale_kv, dtype=np.float32)
+    kv64 = bf16_to_f64(dequant_latent_fp8_bf16(kv8[:S], sc[:S] if sc.ndim else sc))
     out = np.zeros((toks.size, H, d_v))
     lse = np.full((toks.size, H), -np.inf)
     for n, t in enumerate(toks):
