@@ -43,6 +43,8 @@ WORKLOADS = {
     # paged cache (64-row pages in a random physical order): the two MQA routings
     "glm16k_paged": (None, None),
     "crossover": (None, None),
+    # the glm16k chunk over an FP8 (E4M3, per-row scale) latent: conversion + the MQA routings
+    "glm16k_fp8": (None, None),
     "glm16k_uniform": ("c3w_glm16k_uniform", None),
     "long32k": ("c5_long", None),
     "dsv32": ("c2_dsv32", "c8_masked_dsv32"),
@@ -203,6 +205,9 @@ def main():
         return
     if a.workload == "crossover":
         bench_crossover(a)
+        return
+    if a.workload == "glm16k_fp8":
+        bench_fp8(a)
         return
     mqa_name, mha_name = WORKLOADS[a.workload]
     t_gen = time.perf_counter()
@@ -469,6 +474,88 @@ def bench_paged(a):
             "per-token (index conversion + attention)": round(T / (per["pertoken_attn"] * 1e-3), 1)},
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_fp8(a):
+    """The glm16k chunk (c3 shapes and top-k) over an FP8 latent: the conversion pass into the
+    bf16 workspace, then union + grouped attention and per-token attention on it."""
+    import torch
+    from mla_prefill_amd import _lib, routings
+    from synth import CONFIGS, make_case, normal_fp8
+
+    cfg = CONFIGS["c3_glm16k"]
+    t_gen = time.perf_counter()
+    case = make_case(cfg)
+    codes, kscale = normal_fp8(np.random.default_rng(9), cfg.S, cfg.d_qk, per_row=True)
+    print(f"# inputs generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    q = torch.from_numpy(case.q.view(np.int16)).cuda().view(torch.bfloat16)
+    topk = torch.from_numpy(case.topk).cuda()
+    kv8 = torch.from_numpy(codes).cuda()
+    ksc = torch.from_numpy(kscale).cuda()
+    T, H, G, S = cfg.T, cfg.H, cfg.G, cfg.S
+    ws = routings.alloc_latent_ws(S, cfg.d_qk)
+    bufs = routings.alloc_union(T, G, cfg.cols)
+    out_g, lse_g = routings.alloc_out(T, H, 512)
+    out_p, lse_p = routings.alloc_out(T, H, 512)
+    stream = torch.cuda.current_stream()
+    names = ["dequant_fp8", "build_union", "grouped_attn", "pertoken_attn"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        _lib.dsa_dequant_latent_fp8(kv8, ksc, ws, stream=stream)
+        mark(1)
+        _lib.dsa_build_group_union(topk, S, 0, G, bufs.union_idx, bufs.union_len, bufs.mask, stream=stream)
+        mark(2)
+        _lib.dsa_sparse_prefill_grouped(q, ws, bufs.union_idx, bufs.union_len, bufs.mask, cfg.scale, out_g,
+                                        lse_g, stream=stream)
+        mark(3)
+        _lib.dsa_sparse_prefill_pertoken(q, ws, topk, 0, cfg.scale, out_p, lse_p, stream=stream)
+        mark(4)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
+    t0 = time.perf_counter()
+    for s_ in range(a.steps):
+        step(events[s_])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: float(np.mean([events[s_][i].elapsed_time(events[s_][i + 1]) for s_ in range(a.steps)]))
+           for i, n in enumerate(names)}
+    ms_step = wall * 1e3 / a.steps
+    work, nsel = algorithmic_work(case, bufs.union_len.cpu().numpy().astype(np.float64), None)
+    work["dequant_fp8"] = {"bound": "hbm", "bytes": S * cfg.d_qk * 3 + S * 4}
+    kernels = {}
+    for n in names:
+        wk, ms = work[n], per[n]
+        if wk["bound"] == "hbm":
+            ach = wk["bytes"] / (ms * 1e-3) / 1e9
+            kernels[n] = {"ms": ms, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": ach / HBM_PEAK_GBS, "algorithmic": wk["bytes"]}
+        else:
+            ach = wk["flops"] / (ms * 1e-3) / 1e12
+            kernels[n] = {"ms": ms, "bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFS,
+                          "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFS, "algorithmic": wk["flops"]}
+    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+    d = kernels[dom]
+    line = {
+        "metric": METRIC, "value": round(T / (ms_step * 1e-3), 1), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8 latent, bf16 compute", "data": "synthetic",
+        "config": {"workload": "glm16k_fp8", "T": T, "S": S, "H": H, "k": cfg.k, "G": G, "d_qk": cfg.d_qk,
+                   "fp8": "E4M3, per-row float32 scale", "selected_rows": nsel},
+        "roofline": {"kernel": dom, "bound": d["bound"], "achieved": round(d["achieved"], 2), "peak": d["peak"],
+                     "unit": d["unit"], "frac": round(d["frac"], 4), "traffic": None},
+        "cpu_baseline": None,
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+    }
+    print(json.dumps(line), flush=True)
+
 
 
 def bench_crossover(a):

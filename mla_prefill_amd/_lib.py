@@ -40,6 +40,13 @@ _SIGNATURES = {
                                 _i64, _f32, _vp, _vp, _vp, _vp], _i32),
     "dsa_dense_mha_prefill": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32,
                                _vp, _vp, _vp], _i32),
+    "dsa_dequant_latent_fp8": ([_vp, _vp, _i32, _i32, _i32, _vp, _vp], _i32),
+    "dsa_sparse_prefill_grouped_fp8": ([_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                        _f32, _vp, _vp, _vp, _vp], _i32),
+    "dsa_sparse_prefill_pertoken_fp8": ([_vp, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _i32, _i32, _i64, _i32, _i32,
+                                         _f32, _vp, _vp, _vp, _vp], _i32),
+    "dsa_dequant_paged_fp8": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp],
+                              _i32),
     "dsa_varlen_group_bound": ([_i32, _i32, _i32], _i32),
     "dsa_convert_req_index_to_global": ([_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
                                          _vp, _vp], _i32),
@@ -187,6 +194,48 @@ def dsa_dense_mha_prefill(q, k_nope, k_pe, v, q_pos_offset, scale, out, lse, str
 
 
 # ---------------------------------------------------------------------------
+# FP8 latent: kv8 uint8 [S, d] OCP E4M3 codes, kv_scale float32 [S] (per row) or [1]
+# ---------------------------------------------------------------------------
+
+def _fp8(kv8, kv_scale):
+    if kv8.dtype != torch.uint8:
+        raise TypeError("FP8 codes travel as uint8")
+    if kv_scale.dtype != torch.float32:
+        raise TypeError("kv_scale must be float32")
+    per_row = int(kv_scale.numel() != 1)
+    if per_row and kv_scale.numel() < kv8.shape[0]:
+        raise ValueError("kv_scale needs one value per row (or a single value)")
+    return per_row
+
+
+def dsa_dequant_latent_fp8(kv8, kv_scale, out, stream=None):
+    S, d = kv8.shape
+    _check("dsa_dequant_latent_fp8", lib.dsa_dequant_latent_fp8(
+        _ptr(kv8), _ptr(kv_scale), _fp8(kv8, kv_scale), S, d, _ptr(_bits(out)), _stream(stream)))
+
+
+def dsa_sparse_prefill_grouped_fp8(q, kv8, kv_scale, union_idx, union_len, head_group_mask, scale, kv_ws,
+                                   out, lse, stream=None):
+    T, H, d_qk = q.shape
+    S = kv8.shape[0]
+    _check("dsa_sparse_prefill_grouped_fp8", lib.dsa_sparse_prefill_grouped_fp8(
+        _ptr(_bits(q)), _ptr(kv8), _ptr(kv_scale), _fp8(kv8, kv_scale), _ptr(union_idx), _ptr(union_len),
+        _ptr(head_group_mask), T, H, S, union_idx.shape[1], d_qk, out.shape[2], scale, _ptr(_bits(kv_ws)),
+        _ptr(_bits(out)), _ptr(lse), _stream(stream)))
+
+
+def dsa_sparse_prefill_pertoken_fp8(q, kv8, kv_scale, topk, q_pos_offset, scale, kv_ws, out, lse, cols=None,
+                                    stream=None):
+    T, H, d_qk = q.shape
+    S = kv8.shape[0]
+    cols = topk.shape[1] if cols is None else cols
+    _check("dsa_sparse_prefill_pertoken_fp8", lib.dsa_sparse_prefill_pertoken_fp8(
+        _ptr(_bits(q)), _ptr(kv8), _ptr(kv_scale), _fp8(kv8, kv_scale), _ptr(topk), _topk_ld(topk), T, H, S,
+        cols, q_pos_offset, d_qk, out.shape[2], scale, _ptr(_bits(kv_ws)), _ptr(_bits(out)), _ptr(lse),
+        _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
 # batches of requests over a paged KV cache.  A batch is passed as the tuple
 # (cu_seqlens_q, kv_lens, q_pos_start, block_table, page_size) of int32 device
 # tensors (block_table [R, bt_ld]) and the page size.
@@ -248,3 +297,18 @@ def dsa_sparse_prefill_pertoken_varlen(q, kv_cache, topk, batch, scale, topk_ws,
         _ptr(_bits(q)), _ptr(_bits(kv_cache)), kv_cache.shape[0], _ptr(topk), _topk_ld(topk), T, H, cols, R,
         cu, kl, qs, bt, bt_ld, ps, d_qk, out.shape[2], scale, _ptr(topk_ws), _ptr(_bits(out)), _ptr(lse),
         _stream(stream)))
+
+
+def dsa_dequant_paged_fp8(cache8, kv_scale, batch, ws_cache, ws_block_table, stream=None):
+    """Convert the pages a batch can reach into ws_cache [ws_pages * page_size, d] and write
+    ws_block_table [R, bt_ld] over it."""
+    _, kv_lens, _, block_table, page_size = batch
+    b = _batch(batch)
+    R, bt_ld = b[0], b[5]
+    num_slots, d = cache8.shape
+    if ws_block_table.dtype != torch.int32 or ws_block_table.shape != block_table.shape:
+        raise ValueError("ws_block_table must be int32 shaped like block_table")
+    ws_pages = ws_cache.shape[0] // page_size
+    _check("dsa_dequant_paged_fp8", lib.dsa_dequant_paged_fp8(
+        _ptr(cache8), _ptr(kv_scale), _fp8(cache8, kv_scale), num_slots, d, R, _ptr(kv_lens), _ptr(block_table),
+        bt_ld, page_size, ws_pages, _ptr(_bits(ws_cache)), _ptr(ws_block_table), _stream(stream)))

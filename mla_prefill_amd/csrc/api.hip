@@ -129,19 +129,65 @@ int dsa_build_group_union(const int32_t* topk, int64_t ld, int T, int cols, int 
                                                (hipStream_t)stream));
 }
 
-int dsa_sparse_prefill_grouped(const uint16_t* q, const uint16_t* kv, const int32_t* union_idx,
-                               const int32_t* union_len, const uint8_t* head_group_mask, int T,
-                               int H, int S, int union_pad, int d_qk, int d_v, float scale,
-                               uint16_t* out, float* lse, void* stream) {
+// Host checks of the grouped and per-token calls: DSA_OK when the call has work to enqueue,
+// kNothingToDo for an empty one, else the (negative) status.
+constexpr int kNothingToDo = 1;
+
+static int grouped_check(const uint16_t* q, const uint16_t* kv, const int32_t* union_idx,
+                         const int32_t* union_len, const uint8_t* head_group_mask, int T, int H, int S,
+                         int union_pad, int d_qk, int d_v, float scale, const uint16_t* out,
+                         const float* lse) {
   if (H != 16 && H != 32 && H != 64 && H != 128) return DSA_ERR_UNSUPPORTED;
   if (!latent_ok(d_qk, d_v) || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
   if (T < 0 || S < 1 || union_pad < 0 || union_pad % 32 != 0) return DSA_ERR_SHAPE;
-  if (T == 0) return DSA_OK;
+  if (T == 0) return kNothingToDo;
   if (!q || !kv || !union_idx || !union_len || !head_group_mask || !out || !lse)
     return DSA_ERR_NULL;
   if (!aligned_to(q, 16) || !aligned_to(kv, 16) || !aligned_to(out, 16) || !aligned_to(lse, 4) ||
       !aligned_to(union_idx, 4) || !aligned_to(union_len, 4) || !aligned_to(head_group_mask, 4))
     return DSA_ERR_ALIGN;
+  return DSA_OK;
+}
+
+static int pertoken_check(const uint16_t* q, const uint16_t* kv, const int32_t* topk, int64_t ld, int T,
+                          int H, int S, int cols, int64_t q_pos_offset, int d_qk, int d_v, float scale,
+                          const uint16_t* out, const float* lse) {
+  if (H < 16 || H > 128 || H % 16 != 0) return DSA_ERR_UNSUPPORTED;
+  if (!latent_ok(d_qk, d_v) || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
+  if (T < 0 || S < 1 || cols < 0 || ld < cols || q_pos_offset < 0) return DSA_ERR_SHAPE;
+  if (T == 0) return kNothingToDo;
+  if (!q || !kv || (cols > 0 && !topk) || !out || !lse) return DSA_ERR_NULL;
+  if (!aligned_to(q, 16) || !aligned_to(kv, 16) || !aligned_to(out, 16) || !aligned_to(lse, 4) ||
+      !aligned_to(topk, 4))
+    return DSA_ERR_ALIGN;
+  return DSA_OK;
+}
+
+static hipError_t pertoken_launch(const uint16_t* q, const uint16_t* kv, const int32_t* topk, int64_t ld,
+                                  int T, int H, int S, int cols, int64_t q_pos_offset, int d_qk, float scale,
+                                  uint16_t* out, float* lse, hipStream_t stream) {
+  if (H == 128)
+    return dsa::launch_pertoken_rows128(q, kv, topk, ld, T, S, cols, q_pos_offset, scale, out, lse, stream,
+                                        d_qk);
+  return dsa::launch_pertoken_attn(q, kv, topk, ld, T, H, S, cols, q_pos_offset, scale, out, lse, stream,
+                                   d_qk);
+}
+
+// the FP8 latent arguments (kv8 [S, d_qk] codes, kv_scale, the bf16 workspace)
+static int fp8_check(const uint8_t* kv8, const float* kv_scale, int scale_per_row, const uint16_t* kv_ws) {
+  if (scale_per_row != 0 && scale_per_row != 1) return DSA_ERR_SHAPE;
+  if (!kv8 || !kv_scale || !kv_ws) return DSA_ERR_NULL;
+  if (!aligned_to(kv8, 16) || !aligned_to(kv_scale, 4) || !aligned_to(kv_ws, 16)) return DSA_ERR_ALIGN;
+  return DSA_OK;
+}
+
+int dsa_sparse_prefill_grouped(const uint16_t* q, const uint16_t* kv, const int32_t* union_idx,
+                               const int32_t* union_len, const uint8_t* head_group_mask, int T,
+                               int H, int S, int union_pad, int d_qk, int d_v, float scale,
+                               uint16_t* out, float* lse, void* stream) {
+  const int st = grouped_check(q, kv, union_idx, union_len, head_group_mask, T, H, S, union_pad, d_qk, d_v,
+                               scale, out, lse);
+  if (st != DSA_OK) return st == kNothingToDo ? DSA_OK : st;
   return launch_status(dsa::launch_grouped_attn(q, kv, union_idx, union_len, head_group_mask, T,
                                                 H, S, union_pad, scale, out, lse,
                                                 (hipStream_t)stream, nullptr, 0, d_qk));
@@ -151,22 +197,50 @@ int dsa_sparse_prefill_pertoken(const uint16_t* q, const uint16_t* kv, const int
                                 int64_t ld, int T, int H, int S, int cols, int64_t q_pos_offset,
                                 int d_qk, int d_v, float scale, uint16_t* out, float* lse,
                                 void* stream) {
-  if (H < 16 || H > 128 || H % 16 != 0) return DSA_ERR_UNSUPPORTED;
-  if (!latent_ok(d_qk, d_v) || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
-  if (T < 0 || S < 1 || cols < 0 || ld < cols || q_pos_offset < 0) return DSA_ERR_SHAPE;
-  if (T == 0) return DSA_OK;
-  if (!q || !kv || (cols > 0 && !topk) || !out || !lse) return DSA_ERR_NULL;
-  if (!aligned_to(q, 16) || !aligned_to(kv, 16) || !aligned_to(out, 16) || !aligned_to(lse, 4) ||
-      !aligned_to(topk, 4))
-    return DSA_ERR_ALIGN;
-  hipError_t e;
-  if (H == 128)
-    e = dsa::launch_pertoken_rows128(q, kv, topk, ld, T, S, cols, q_pos_offset, scale, out, lse,
-                                     (hipStream_t)stream, d_qk);
-  else
-    e = dsa::launch_pertoken_attn(q, kv, topk, ld, T, H, S, cols, q_pos_offset, scale, out, lse,
-                                  (hipStream_t)stream, d_qk);
-  return launch_status(e);
+  const int st = pertoken_check(q, kv, topk, ld, T, H, S, cols, q_pos_offset, d_qk, d_v, scale, out, lse);
+  if (st != DSA_OK) return st == kNothingToDo ? DSA_OK : st;
+  return launch_status(pertoken_launch(q, kv, topk, ld, T, H, S, cols, q_pos_offset, d_qk, scale, out, lse,
+                                       (hipStream_t)stream));
+}
+
+int dsa_dequant_latent_fp8(const uint8_t* kv8, const float* kv_scale, int scale_per_row, int S, int d,
+                           uint16_t* out, void* stream) {
+  if (d != 576 && d != 512) return DSA_ERR_UNSUPPORTED;
+  if (S < 0) return DSA_ERR_SHAPE;
+  if (S == 0) return DSA_OK;
+  const int st = fp8_check(kv8, kv_scale, scale_per_row, out);
+  if (st != DSA_OK) return st;
+  return launch_status(dsa::launch_dequant_fp8(kv8, kv_scale, scale_per_row, S, d, out, (hipStream_t)stream));
+}
+
+int dsa_sparse_prefill_grouped_fp8(const uint16_t* q, const uint8_t* kv8, const float* kv_scale,
+                                   int scale_per_row, const int32_t* union_idx, const int32_t* union_len,
+                                   const uint8_t* head_group_mask, int T, int H, int S, int union_pad,
+                                   int d_qk, int d_v, float scale, uint16_t* kv_ws, uint16_t* out, float* lse,
+                                   void* stream) {
+  // (the bf16 checks see the workspace as the latent)
+  int st = grouped_check(q, kv_ws, union_idx, union_len, head_group_mask, T, H, S, union_pad, d_qk, d_v,
+                         scale, out, lse);
+  if (st != DSA_OK) return st == kNothingToDo ? DSA_OK : st;
+  if ((st = fp8_check(kv8, kv_scale, scale_per_row, kv_ws)) != DSA_OK) return st;
+  const hipError_t e = dsa::launch_dequant_fp8(kv8, kv_scale, scale_per_row, S, d_qk, kv_ws, (hipStream_t)stream);
+  if (e != hipSuccess) return DSA_ERR_LAUNCH;
+  return launch_status(dsa::launch_grouped_attn(q, kv_ws, union_idx, union_len, head_group_mask, T, H, S,
+                                                union_pad, scale, out, lse, (hipStream_t)stream, nullptr, 0,
+                                                d_qk));
+}
+
+int dsa_sparse_prefill_pertoken_fp8(const uint16_t* q, const uint8_t* kv8, const float* kv_scale,
+                                    int scale_per_row, const int32_t* topk, int64_t ld, int T, int H, int S,
+                                    int cols, int64_t q_pos_offset, int d_qk, int d_v, float scale,
+                                    uint16_t* kv_ws, uint16_t* out, float* lse, void* stream) {
+  int st = pertoken_check(q, kv_ws, topk, ld, T, H, S, cols, q_pos_offset, d_qk, d_v, scale, out, lse);
+  if (st != DSA_OK) return st == kNothingToDo ? DSA_OK : st;
+  if ((st = fp8_check(kv8, kv_scale, scale_per_row, kv_ws)) != DSA_OK) return st;
+  const hipError_t e = dsa::launch_dequant_fp8(kv8, kv_scale, scale_per_row, S, d_qk, kv_ws, (hipStream_t)stream);
+  if (e != hipSuccess) return DSA_ERR_LAUNCH;
+  return launch_status(pertoken_launch(q, kv_ws, topk, ld, T, H, S, cols, q_pos_offset, d_qk, scale, out, lse,
+                                       (hipStream_t)stream));
 }
 
 int dsa_varlen_group_bound(int T, int R, int G) {
@@ -265,6 +339,24 @@ int dsa_sparse_prefill_pertoken_varlen(const uint16_t* q, const uint16_t* kv_cac
     e = dsa::launch_pertoken_attn(q, kv_cache, topk_ws, cols, T, H, num_slots, cols, all_causal, scale, out,
                                   lse, (hipStream_t)stream, d_qk);
   return launch_status(e);
+}
+
+int dsa_dequant_paged_fp8(const uint8_t* cache8, const float* kv_scale, int scale_per_row, int num_slots,
+                          int d, int R, const int32_t* kv_lens, const int32_t* block_table, int64_t bt_ld,
+                          int page_size, int ws_pages, uint16_t* ws_cache, int32_t* ws_block_table,
+                          void* stream) {
+  if (d != 576 && d != 512) return DSA_ERR_UNSUPPORTED;
+  if (num_slots < 1 || R < 1 || bt_ld < 1 || page_size < 1 || num_slots % page_size != 0 || ws_pages < 0 ||
+      bt_ld > 65535 || R > 65535)
+    return DSA_ERR_SHAPE;
+  if (!kv_lens || !block_table || !ws_block_table) return DSA_ERR_NULL;
+  if (!aligned_to(kv_lens, 4) || !aligned_to(block_table, 4) || !aligned_to(ws_block_table, 4))
+    return DSA_ERR_ALIGN;
+  const int st = fp8_check(cache8, kv_scale, scale_per_row, ws_cache);
+  if (st != DSA_OK) return st;
+  return launch_status(dsa::launch_dequant_paged_fp8(cache8, kv_scale, scale_per_row, num_slots, d, R, kv_lens,
+                                                     block_table, bt_ld, page_size, ws_pages, ws_cache,
+                                                     ws_block_table, (hipStream_t)stream));
 }
 
 int dsa_masked_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_pe,

@@ -61,6 +61,17 @@ hipError_t launch_rows128_exact(const uint16_t* q, const uint16_t* kv, const int
                                 uint16_t* out, float* lse, hipStream_t stream, const int32_t* group_info,
                                 int ngroups, int d_qk);
 
+// FP8 (OCP E4M3) latent -> bf16 rows: e4m3 * scale[per_row ? row : 0] (float32 product,
+// nearest even); rows x d codes, d a multiple of 16
+hipError_t launch_dequant_fp8(const uint8_t* kv8, const float* scale, int per_row, int64_t rows, int d,
+                              uint16_t* out, hipStream_t stream);
+// a batch over a paged FP8 cache: each request's reachable pages into a compact bf16 workspace
+// of ws_pages pages, and the block table over it (-1 where nothing maps)
+hipError_t launch_dequant_paged_fp8(const uint8_t* cache8, const float* scale, int per_row, int num_slots,
+                                    int d, int R, const int32_t* kv_lens, const int32_t* block_table,
+                                    int64_t bt_ld, int page_size, int ws_pages, uint16_t* out_cache,
+                                    int32_t* out_bt, hipStream_t stream);
+
 // masked dense MHA, key = k_nope (dn) + shared k_pe (dr), value dv: (256, 0, 256),
 // (192, 64, 256) or (128, 64, 128); mask = causal AND top-k bit; bits == nullptr: causal
 // only (dense MHA)

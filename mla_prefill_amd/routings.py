@@ -85,6 +85,51 @@ def dense_mha(q, k_nope, k_pe, v, q_pos_offset: int, scale: float, out=None, lse
 
 
 # ---------------------------------------------------------------------------
+# FP8 latent (kv8 uint8 OCP E4M3 codes, kv_scale float32 per row or single)
+# ---------------------------------------------------------------------------
+
+def alloc_latent_ws(S: int, d: int, device="cuda"):
+    """bf16 workspace for a converted latent."""
+    return torch.empty((S, d), dtype=torch.bfloat16, device=device)
+
+
+def grouped_fp8(q, kv8, kv_scale, topk, q_pos_offset: int, scale: float, bufs: UnionBuffers | None = None,
+                kv_ws=None, out=None, lse=None, stream=None):
+    T, H, _ = q.shape
+    G = 128 // H
+    bufs = build_group_union(topk, kv8.shape[0], q_pos_offset, G, bufs, stream)
+    if kv_ws is None:
+        kv_ws = alloc_latent_ws(*kv8.shape, q.device)
+    if out is None:
+        out, lse = alloc_out(T, H, 512, q.device)
+    _lib.dsa_sparse_prefill_grouped_fp8(q, kv8, kv_scale, bufs.union_idx, bufs.union_len, bufs.mask, scale,
+                                        kv_ws, out, lse, stream=stream)
+    return out, lse, bufs
+
+
+def pertoken_fp8(q, kv8, kv_scale, topk, q_pos_offset: int, scale: float, kv_ws=None, out=None, lse=None,
+                 stream=None):
+    T, H, _ = q.shape
+    if kv_ws is None:
+        kv_ws = alloc_latent_ws(*kv8.shape, q.device)
+    if out is None:
+        out, lse = alloc_out(T, H, 512, q.device)
+    _lib.dsa_sparse_prefill_pertoken_fp8(q, kv8, kv_scale, topk, q_pos_offset, scale, kv_ws, out, lse,
+                                         stream=stream)
+    return out, lse
+
+
+def dequant_paged_fp8(cache8, kv_scale, batch, ws_pages: int, stream=None):
+    """(ws_cache, batch over it): the batch's reachable pages converted to bf16, and the same
+    batch with the block table over the workspace."""
+    cu, kv_lens, q_pos_start, block_table, page_size = batch
+    ws_cache = torch.empty((ws_pages * page_size, cache8.shape[1]), dtype=torch.bfloat16, device=cache8.device)
+    ws_bt = torch.empty_like(block_table)
+    _lib.dsa_dequant_paged_fp8(cache8, kv_scale, batch, ws_cache, ws_bt, stream=stream)
+    return ws_cache, (cu, kv_lens, q_pos_start, ws_bt, page_size)
+
+
+# ---------------------------------------------------------------------------
 # batches of requests over a paged KV cache; `batch` = (cu_seqlens_q, kv_lens,
 # q_pos_start, block_table, page_size), int32 device tensors and an int
 # ---------------------------------------------------------------------------

@@ -63,6 +63,20 @@ def normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
     return out.reshape(shape)
 
 
+def normal_fp8(rng: np.random.Generator, rows: int, d: int, per_row: bool = True):
+    """An FP8 latent: N(0, 1) float32 draws stored as OCP E4M3 codes (uint8 [rows, d]) with
+    float32 scales (per row: the row's largest magnitude / 448, else one for the whole
+    tensor), encoded by torch's float8_e4m3fn conversion (nearest even).  Returns
+    (codes, scales [rows] or [1])."""
+    import torch
+    v = rng.standard_normal((rows, d), dtype=np.float32)
+    amax = np.abs(v).max(axis=1) if per_row else np.array([np.abs(v).max()], np.float32)
+    scale = (np.maximum(amax, 1e-30) / np.float32(448.0)).astype(np.float32)
+    x = v / (scale[:, None] if per_row else scale[0])
+    codes = torch.from_numpy(np.clip(x, -448.0, 448.0)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, scale
+
+
 # ---------------------------------------------------------------------------
 # top-k index buffers
 # ---------------------------------------------------------------------------

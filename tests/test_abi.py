@@ -222,3 +222,33 @@ def test_varlen_validation(lib):
         return lib.dsa_sparse_prefill_pertoken_varlen(P, P, 256, P, 16, T, H, cols, R_, P, P, P, P, 4, 64,
                                                       576, 512, 0.1, ws, P, P, None)
     assert pv(H=8) == UNSUP and pv(R_=0) == SHAPE and pv(T=0) == OK and pv(ws=None) == NULL
+
+
+def test_fp8_validation(lib):
+    # conversion pass
+    def dq(kv=P, sc=P, per_row=1, S=64, d=576, out=P):
+        return lib.dsa_dequant_latent_fp8(kv, sc, per_row, S, d, out, None)
+    assert dq(d=500) == UNSUP and dq(S=-1) == SHAPE and dq(S=0) == OK and dq(per_row=2) == SHAPE
+    for kw in ("kv", "sc", "out"):
+        assert dq(**{kw: None}) == NULL
+    assert dq(kv=P + 8) == ALIGN and dq(sc=P + 2) == ALIGN and dq(out=P + 2) == ALIGN
+    # attention over an FP8 latent: the bf16 checks first (T = 0 enqueues nothing)
+    def gf(q=P, kv=P, sc=P, per_row=0, T=64, H=16, dqk=576, ws=P, pad=256):
+        return lib.dsa_sparse_prefill_grouped_fp8(q, kv, sc, per_row, P, P, P, T, H, 64, pad, dqk, 512, 0.1,
+                                                  ws, P, P, None)
+    assert gf(H=24) == UNSUP and gf(dqk=448) == UNSUP and gf(pad=48) == SHAPE and gf(T=0) == OK
+    assert gf(kv=None) == NULL and gf(sc=None) == NULL and gf(ws=None) == NULL and gf(q=None) == NULL
+    assert gf(kv=P + 4) == ALIGN and gf(ws=P + 2) == ALIGN and gf(per_row=3) == SHAPE
+    def pf(q=P, kv=P, sc=P, T=64, H=16, ld=32, cols=32, ws=P):
+        return lib.dsa_sparse_prefill_pertoken_fp8(q, kv, sc, 1, P, ld, T, H, 64, cols, 0, 576, 512, 0.1, ws,
+                                                   P, P, None)
+    assert pf(H=8) == UNSUP and pf(ld=16) == SHAPE and pf(T=0) == OK
+    assert pf(kv=None) == NULL and pf(ws=None) == NULL and pf(sc=P + 1) == ALIGN
+    # paged conversion
+    def pg(kv=P, sc=P, ns=256, d=576, R_=2, kl=P, bt=P, bt_ld=4, ps=64, wsp=4, ws=P, wbt=P):
+        return lib.dsa_dequant_paged_fp8(kv, sc, 1, ns, d, R_, kl, bt, bt_ld, ps, wsp, ws, wbt, None)
+    assert pg(d=192) == UNSUP and pg(ns=100) == SHAPE and pg(R_=0) == SHAPE and pg(ps=0) == SHAPE
+    assert pg(wsp=-1) == SHAPE and pg(bt_ld=0) == SHAPE
+    for kw in ("kv", "sc", "kl", "bt", "ws", "wbt"):
+        assert pg(**{kw: None}) == NULL
+    assert pg(wbt=P + 2) == ALIGN and pg(kv=P + 4) == ALIGN
