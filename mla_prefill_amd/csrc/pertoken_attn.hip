@@ -484,12 +484,19 @@ __device__ __forceinline__ PdCtx pd_context(int pos, int cols, float scale_log2)
   return c;
 }
 
+// validity bits of step j's 16 keys (key r <-> bit r): the sorted list holds only valid
+// entries, so key r is valid iff 16 j + r < n (list length n)
+__device__ __forceinline__ uint32_t pd_valid(const PdCtx& c, int j) {
+  const int left = c.cols - kPKeys * j;
+  return left >= kPKeys ? 0xffffu : (left <= 0 ? 0u : (1u << left) - 1u);
+}
+
 // start the copies of step j's rows into the tile at LDS address `tile`; returns the
-// validity bits of the step's 16 keys (key r <-> bit r)
+// validity bits of the step's 16 keys (past the list the copies fetch the token's own row)
 template <int D>
 __device__ __forceinline__ uint32_t pd_issue(const PdCtx& c, const uint8_t* kvb, int2 e, int j, uint32_t tile) {
-  const bool ok0 = kPKeys * j + c.er < c.cols && e.x >= 0 && e.x <= c.pos;
-  const bool ok1 = kPKeys * j + 8 + c.er < c.cols && e.y >= 0 && e.y <= c.pos;
+  const bool ok0 = kPKeys * j + c.er < c.cols;
+  const bool ok1 = kPKeys * j + 8 + c.er < c.cols;
   const uint8_t* src0 = kvb + (size_t)(ok0 ? e.x : c.pos) * Lat<D>::row_bytes + c.dofs[0];
   const uint8_t* src1 = kvb + (size_t)(ok1 ? e.y : c.pos) * Lat<D>::row_bytes + c.dofs[1];
 #pragma unroll
@@ -497,11 +504,7 @@ __device__ __forceinline__ uint32_t pd_issue(const PdCtx& c, const uint8_t* kvb,
     dma16(src0 + 128 * k, tile + 1024 * k);
     dma16(src1 + 128 * k, tile + Lat<D>::group_bytes + 1024 * k);
   }
-  const uint64_t b0 = ballot(ok0), b1 = ballot(ok1);
-  uint32_t v = 0;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) v |= (uint32_t)((b0 >> (8 * r)) & 1u) << r | (uint32_t)((b1 >> (8 * r)) & 1u) << (8 + r);
-  return v;
+  return pd_valid(c, j);
 }
 
 // the sources of step j's copies and the validity bits of its 16 keys (key r <-> bit r)
@@ -512,16 +515,12 @@ struct PdSrc {
 };
 template <int D>
 __device__ __forceinline__ PdSrc pd_prep(const PdCtx& c, const uint8_t* kvb, int2 e, int j) {
-  const bool ok0 = kPKeys * j + c.er < c.cols && e.x >= 0 && e.x <= c.pos;
-  const bool ok1 = kPKeys * j + 8 + c.er < c.cols && e.y >= 0 && e.y <= c.pos;
+  const bool ok0 = kPKeys * j + c.er < c.cols;
+  const bool ok1 = kPKeys * j + 8 + c.er < c.cols;
   PdSrc p;
   p.src0 = kvb + (size_t)(ok0 ? e.x : c.pos) * Lat<D>::row_bytes + c.dofs[0];
   p.src1 = kvb + (size_t)(ok1 ? e.y : c.pos) * Lat<D>::row_bytes + c.dofs[1];
-  const uint64_t b0 = ballot(ok0), b1 = ballot(ok1);
-  uint32_t v = 0;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) v |= (uint32_t)((b0 >> (8 * r)) & 1u) << r | (uint32_t)((b1 >> (8 * r)) & 1u) << (8 + r);
-  p.vbits = v;
+  p.vbits = pd_valid(c, j);
   return p;
 }
 // the two copies (row groups 0 and 1) of line k
