@@ -535,7 +535,8 @@ __device__ __forceinline__ int2 pd_entries(const PdCtx& c, int j) {
   return int2{(int)pt_sorted[i0], (int)pt_sorted[i1]};
 }
 
-// S^T[key 4 g + jj][head n] (raw), three chains; K reads kPQAhead MFMAs ahead
+// S^T[key 4 g + jj][head n] (raw), one accumulation chain (dependent 16x16x32 MFMAs issue at
+// full rate); K reads kPQAhead MFMAs ahead
 template <int D>
 __device__ __forceinline__ f32x4 pd_qk(const PdCtx& c, const uint8_t* tile, const bf16x8 (&qreg)[Lat<D>::loads]) {
   auto kread = [&](int s) -> bf16x8 {
@@ -544,15 +545,15 @@ __device__ __forceinline__ f32x4 pd_qk(const PdCtx& c, const uint8_t* tile, cons
   bf16x8 kw[kPQAhead];
 #pragma unroll
   for (int s = 0; s < kPQAhead; ++s) kw[s] = kread(s);
-  f32x4 acc[3] = {};
+  f32x4 acc = {};
 #pragma unroll
   for (int s = 0; s < Lat<D>::loads; ++s) {
     __builtin_amdgcn_sched_barrier(0);
-    acc[s % 3] = mfma16x16x32(kw[s % kPQAhead], qreg[s], acc[s % 3]);
+    acc = mfma16x16x32(kw[s % kPQAhead], qreg[s], acc);
     if (s + kPQAhead < Lat<D>::loads) kw[s % kPQAhead] = kread(s + kPQAhead);
   }
   __builtin_amdgcn_sched_barrier(0);
-  return acc[0] + acc[1] + acc[2];
+  return acc;
 }
 
 // O^T += V^T P^T over the tile, which is refilled as it goes with the rows of a later step
