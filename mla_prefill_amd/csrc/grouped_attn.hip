@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   const int G = 128 / H;
   const int NG = (int)gridDim.x;
   const int grp = NG - 1 - xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;  // (wave: a scalar)
   const int hi = lane >> 5, m = lane & 31;
   const int2 span = group_span(ginfo, grp, G, T);  // (a batch's groups come from its table)
   const int t0 = uniform(span.x), ntok = uniform(span.y);

@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
   const int qt = nqt - 1 - lb / H;
   const int h = lb - (lb / H) * H;
   const int q0 = qt * kMQ;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;  // (wave: a scalar)
   const int hi = lane >> 5, m = lane & 31;
   const int row = q0 + 32 * wave + m;  // query token of this lane's row
   const bool live = row < T;
