@@ -174,6 +174,27 @@ def test_pertoken_far_positions_and_wide_rows(R):
         check_attention(out, lse, ref_out, ref_lse, f"per-token S={S} cols={cols}")
 
 
+@pytest.mark.parametrize("H", [48, 112])
+def test_pertoken_head_counts_without_grouped_form(R, H):
+    """Head counts the per-token kernel takes (multiples of 16) but 128 / H is no group size."""
+    q, kv, topk = small_mqa(15 + H, 33, 150, H, 60, 64, 1, 117, "uniform", True)
+    ref_out, ref_lse = oracle.pertoken_sparse_mqa(q, kv, topk, 150, 117, 0.0625)
+    out, lse = R.pertoken(dev_bf16(q), dev_bf16(kv), dev_i32(topk), 117, 0.0625)
+    check_attention(out, lse, ref_out, ref_lse, f"per-token H={H}")
+
+
+def test_grouped_far_positions(R):
+    """The union builder's position windows past 65535 (a 70000-row latent, chunk at its end)."""
+    q, kv, topk = small_mqa(16, 24, 70000, 16, 300, 320, 8, 70000 - 24, "uniform", True)
+    ui, ul, mk = oracle.group_union_mask(topk, 70000, 70000 - 24, 8)
+    out, lse, bufs = R.grouped(dev_bf16(q), dev_bf16(kv), dev_i32(topk), 70000 - 24, 0.0625)
+    np.testing.assert_array_equal(bufs.union_len.cpu().numpy(), ul)
+    np.testing.assert_array_equal(bufs.union_idx.cpu().numpy(), ui)
+    np.testing.assert_array_equal(bufs.mask.cpu().numpy(), mk)
+    ref_out, ref_lse = oracle.pertoken_sparse_mqa(q, kv, topk, 70000, 70000 - 24, 0.0625)
+    check_attention(out, lse, ref_out, ref_lse, "grouped S=70000")
+
+
 def test_large_score_jump_and_negative_scale(R):
     """Scores that jump far above everything earlier in the row (one key per affected token
     scores ~900 raw units on head 0, ~80 in base-2 softmax units, placed late in the row),
@@ -348,6 +369,23 @@ def test_dense_mha_equals_masked_when_topk_covers_the_chunk(R, dn, dr):
     torch.cuda.synchronize()
     assert torch.equal(od, om)
     assert torch.equal(ld, lm)
+
+
+def test_masked_and_dense_mha_long_context(R):
+    """Keys past position 65535 (a 70000-key context, 20 query tokens at its end)."""
+    rng = np.random.default_rng(38)
+    T, S, H = 20, 70000, 2
+    P0 = S - T
+    q = normal_bf16(rng, (T, H, 256))
+    kn = normal_bf16(rng, (S, H, 256))
+    v = normal_bf16(rng, (S, H, 256))
+    topk = topk_uniform(rng, T, S, 2048, 2100, P0)
+    out, lse, _ = R.masked_mha(dev_bf16(q), dev_bf16(kn), None, dev_bf16(v), dev_i32(topk), P0, 0.0625)
+    ref_out, ref_lse = oracle.masked_mha(q, kn, None, v, topk, S, P0, 0.0625)
+    check_attention(out, lse, ref_out, ref_lse, "masked S=70000")
+    out, lse = R.dense_mha(dev_bf16(q), dev_bf16(kn), None, dev_bf16(v), P0, 0.0625)
+    ref_out, ref_lse = oracle.dense_causal_mha(q, kn, None, v, S, P0, 0.0625)
+    check_attention(out, lse, ref_out, ref_lse, "dense S=70000")
 
 
 def test_masked_mha_equals_pertoken_with_shared_heads(R):
