@@ -15,7 +15,10 @@ NoPE masked-MHA layer of the same chunk (qk 256, rope 0, v 256, H = 16, scale
 HBM before the timed region starts.
 
 value = query tokens per second of the whole step (T / step time).  Per-kernel
-times come from HIP events recorded on the launch stream over the timed region.
+times come from HIP events recorded on the launch stream over the timed region
+(mean, median and min over the timed steps); after it, each call is also timed
+"cold", right after a 1 GiB write that evicts L2 and the Infinity Cache (median
+of 5, outside the timed region).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 """
@@ -140,6 +143,24 @@ def measured_traffic(kernel: str, workload: str):
     return (k["fetch_kib"] * rec["fetch_scale"] + k["write_kib"] * rec["write_scale"]) * 1024.0
 
 
+def cold_times(calls, names, stream, reps=5):
+    """Median time of each call after a 1 GiB write that evicts L2 and the Infinity Cache."""
+    import torch
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    got = {n: [] for n in names}
+    for r in range(reps):
+        for n, call in zip(names, calls):
+            flush.fill_(float(r))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            e1.synchronize()
+            got[n].append(e0.elapsed_time(e1))
+    del flush
+    return {n: float(np.median(v)) for n, v in got.items()}
+
+
 def cpu_baseline(case, mha_case, budget_s):
     """The oracle, as it stands, on whole groups sampled across the sequence."""
     import oracle
@@ -237,24 +258,25 @@ def main():
 
     names = ["build_union", "grouped_attn", "pertoken_attn"] + (["masked_mha_routing"] if mha_case else [])
 
+    calls = [
+        lambda: _lib.dsa_build_group_union(topk, cfg.S, cfg.q_pos_offset, G, bufs.union_idx, bufs.union_len,
+                                           bufs.mask, stream=stream),
+        lambda: _lib.dsa_sparse_prefill_grouped(q, kv, bufs.union_idx, bufs.union_len, bufs.mask, cfg.scale,
+                                                out_g, lse_g, stream=stream),
+        lambda: _lib.dsa_sparse_prefill_pertoken(q, kv, topk, cfg.q_pos_offset, cfg.scale, out_p, lse_p,
+                                                 stream=stream),
+    ]
+    if mha_case is not None:
+        calls.append(lambda: _lib.dsa_masked_mha_prefill(mq, mk, mkp, mv, mtopk, m.q_pos_offset, m.scale, ws,
+                                                         out_m, lse_m, stream=stream))
+
     def step(ev=None):
-        def mark(i):
+        for i, call in enumerate(calls):
             if ev is not None:
                 ev[i].record(stream)
-        mark(0)
-        _lib.dsa_build_group_union(topk, cfg.S, cfg.q_pos_offset, G, bufs.union_idx, bufs.union_len,
-                                   bufs.mask, stream=stream)
-        mark(1)
-        _lib.dsa_sparse_prefill_grouped(q, kv, bufs.union_idx, bufs.union_len, bufs.mask, cfg.scale,
-                                        out_g, lse_g, stream=stream)
-        mark(2)
-        _lib.dsa_sparse_prefill_pertoken(q, kv, topk, cfg.q_pos_offset, cfg.scale, out_p, lse_p,
-                                         stream=stream)
-        mark(3)
-        if mha_case is not None:
-            _lib.dsa_masked_mha_prefill(mq, mk, mkp, mv, mtopk, m.q_pos_offset, m.scale, ws, out_m,
-                                        lse_m, stream=stream)
-            mark(4)
+            call()
+        if ev is not None:
+            ev[len(calls)].record(stream)
 
     for _ in range(a.warmup):
         step()
@@ -267,9 +289,11 @@ def main():
         step(events[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = {n: float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(a.steps)]))
-           for i, n in enumerate(names)}
+    samples = {n: [events[s][i].elapsed_time(events[s][i + 1]) for s in range(a.steps)]
+               for i, n in enumerate(names)}
+    per = {n: float(np.mean(v)) for n, v in samples.items()}
     ms_step = wall * 1e3 / a.steps
+    cold = cold_times(calls, names, stream)
     if not (torch.isfinite(out_g.float()).all() and torch.isfinite(out_p.float()).all()):
         print("non-finite output", file=sys.stderr)
         sys.exit(3)
@@ -288,6 +312,8 @@ def main():
             ach = wk["flops"] / (ms * 1e-3) / 1e12
             kernels[n] = {"ms": ms, "bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFS,
                           "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFS, "algorithmic": wk["flops"]}
+        kernels[n].update({"median_ms": float(np.median(samples[n])), "min_ms": float(np.min(samples[n])),
+                           "cold_ms": cold[n]})
     dom = max(kernels, key=lambda k: kernels[k]["ms"])
     d = kernels[dom]
     traffic = measured_traffic(dom, a.workload)
