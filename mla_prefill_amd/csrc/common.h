@@ -103,6 +103,15 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
                : "m0");
 }
 
+// The same copy addressed as a uniform base plus this lane's 32-bit byte offset (below 2^31):
+// line offsets can live in the base, so the lanes need no address arithmetic per line.
+__device__ __forceinline__ void dma16_sbase(uint32_t lane_ofs, const void* base, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(lane_ofs), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "m0");
+}
+
 __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
                :

@@ -493,24 +493,27 @@ __device__ __forceinline__ uint32_t pd_valid(const PdCtx& c, int j) {
 
 // start the copies of step j's rows into the tile at LDS address `tile`; returns the
 // validity bits of the step's 16 keys (past the list the copies fetch the token's own row)
+// (positions are below 65536 here, so a row's byte offset fits 31 bits; line k's copies take
+// the base kvb + 128 k and the lane's row offset)
 template <int D>
 __device__ __forceinline__ uint32_t pd_issue(const PdCtx& c, const uint8_t* kvb, int2 e, int j, uint32_t tile) {
   const bool ok0 = kPKeys * j + c.er < c.cols;
   const bool ok1 = kPKeys * j + 8 + c.er < c.cols;
-  const uint8_t* src0 = kvb + (size_t)(ok0 ? e.x : c.pos) * Lat<D>::row_bytes + c.dofs[0];
-  const uint8_t* src1 = kvb + (size_t)(ok1 ? e.y : c.pos) * Lat<D>::row_bytes + c.dofs[1];
+  const uint32_t off0 = (uint32_t)(ok0 ? e.x : c.pos) * Lat<D>::row_bytes + c.dofs[0];
+  const uint32_t off1 = (uint32_t)(ok1 ? e.y : c.pos) * Lat<D>::row_bytes + c.dofs[1];
 #pragma unroll
   for (int k = 0; k < Lat<D>::lines; ++k) {
-    dma16(src0 + 128 * k, tile + 1024 * k);
-    dma16(src1 + 128 * k, tile + Lat<D>::group_bytes + 1024 * k);
+    dma16_sbase(off0, kvb + 128 * k, tile + 1024 * k);
+    dma16_sbase(off1, kvb + 128 * k, tile + Lat<D>::group_bytes + 1024 * k);
   }
   return pd_valid(c, j);
 }
 
 // the sources of step j's copies and the validity bits of its 16 keys (key r <-> bit r)
 struct PdSrc {
-  const uint8_t* src0;  // this lane's 16 bytes of row er's first line
-  const uint8_t* src1;  // ... of row 8 + er
+  const uint8_t* base;  // the latent (uniform)
+  uint32_t off0;        // byte offset of this lane's 16 bytes of row er's first line
+  uint32_t off1;        // ... of row 8 + er
   uint32_t vbits;
 };
 template <int D>
@@ -518,16 +521,17 @@ __device__ __forceinline__ PdSrc pd_prep(const PdCtx& c, const uint8_t* kvb, int
   const bool ok0 = kPKeys * j + c.er < c.cols;
   const bool ok1 = kPKeys * j + 8 + c.er < c.cols;
   PdSrc p;
-  p.src0 = kvb + (size_t)(ok0 ? e.x : c.pos) * Lat<D>::row_bytes + c.dofs[0];
-  p.src1 = kvb + (size_t)(ok1 ? e.y : c.pos) * Lat<D>::row_bytes + c.dofs[1];
+  p.base = kvb;
+  p.off0 = (uint32_t)(ok0 ? e.x : c.pos) * Lat<D>::row_bytes + c.dofs[0];
+  p.off1 = (uint32_t)(ok1 ? e.y : c.pos) * Lat<D>::row_bytes + c.dofs[1];
   p.vbits = pd_valid(c, j);
   return p;
 }
 // the two copies (row groups 0 and 1) of line k
 template <int D>
 __device__ __forceinline__ void pd_copy_line(const PdSrc& p, uint32_t tile, int k) {
-  dma16(p.src0 + 128 * k, tile + 1024 * k);
-  dma16(p.src1 + 128 * k, tile + Lat<D>::group_bytes + 1024 * k);
+  dma16_sbase(p.off0, p.base + 128 * k, tile + 1024 * k);
+  dma16_sbase(p.off1, p.base + 128 * k, tile + Lat<D>::group_bytes + 1024 * k);
 }
 
 __device__ __forceinline__ int2 pd_entries(const PdCtx& c, int j) {
