@@ -61,6 +61,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="glm16k", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold (cache-flushed) timings")
     ap.add_argument("--heads", default="16,32,64,128", help="crossover: heads per GPU")
     ap.add_argument("--lengths", default="1024,2048,4096,8192,16384,32768",
                     help="crossover: chunk lengths (T = S, starting at position 0)")
@@ -293,7 +294,7 @@ def main():
                for i, n in enumerate(names)}
     per = {n: float(np.mean(v)) for n, v in samples.items()}
     ms_step = wall * 1e3 / a.steps
-    cold = cold_times(calls, names, stream)
+    cold = {n: None for n in names} if a.no_cold else cold_times(calls, names, stream)
     if not (torch.isfinite(out_g.float()).all() and torch.isfinite(out_p.float()).all()):
         print("non-finite output", file=sys.stderr)
         sys.exit(3)
