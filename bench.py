@@ -123,10 +123,23 @@ KERNEL_SYMBOLS = {  # bench kernel name -> (device symbol, sources)
 }
 
 
+def source_digest(files) -> str:
+    """Digest of the kernel sources' code: comments and blank lines are dropped, so an edit
+    of the comments alone keeps a counter record valid."""
+    import hashlib
+    import re
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for f in files:
+        text = open(os.path.join(root, "mla_prefill_amd", "csrc", f)).read()
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(l.rstrip() for l in text.splitlines() if l.strip()).encode())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(kernel: str, workload: str):
     """L2-to-memory bytes per launch from the committed rocprofv3 counter record, or None when
-    there is no record for this workload or the kernel's source has changed since."""
-    import hashlib
+    there is no record for this workload or the kernel's code has changed since."""
     root = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(root, "profiles", f"hbm_traffic_{workload}.json")
     if not os.path.exists(path) or kernel not in KERNEL_SYMBOLS:
@@ -136,10 +149,7 @@ def measured_traffic(kernel: str, workload: str):
     k = rec["kernels"].get(sym)
     if k is None:
         return None
-    h = hashlib.sha256()
-    for f in files:
-        h.update(open(os.path.join(root, "mla_prefill_amd", "csrc", f), "rb").read())
-    if h.hexdigest()[:16] != k["source_sha256_16"]:
+    if source_digest(files) != k.get("source_code_sha256_16"):
         return None
     return (k["fetch_kib"] * rec["fetch_scale"] + k["write_kib"] * rec["write_scale"]) * 1024.0
 

@@ -15,19 +15,20 @@
 //    covers the pages' workloads): the wave first sorts its token's valid
 //    entries in LDS, so that the concurrent tokens of a range, which select
 //    nearly the same rows, walk them in the same order and find them in L2.
-//    Rows then stream 16 at a time into two 18 KiB LDS tiles by asynchronous
+//    Rows then stream 16 at a time into two LDS tiles (18 KiB at 576 dims) by asynchronous
 //    global->LDS copies, one step ahead of the compute (each copy instruction
 //    covers one 128-byte line of 8 rows, so a quarter-wave touches two cache
 //    lines); the 16 heads' queries stay in registers;
 //  * register ring (any size): rows are loaded with the same coalesced pattern
 //    into two register buffers, each refilled two steps ahead as soon as it
-//    has been written to an 18 KiB LDS tile; the queries sit in a lane-private
+//    has been written to an LDS tile of 16 rows; the queries sit in a lane-private
 //    LDS area;
 //  * both: invalid entries (-1, past the row, beyond the token's position)
 //    fetch the token's own row and are masked.  The tiles are XOR-swizzled,
 //    free of bank conflicts for the writes, the 16-byte K reads and the
-//    transposed V reads.  S^T = K Q^T runs on v_mfma_f32_16x16x32_bf16 in
-//    three independent accumulation chains; O^T = V^T P^T runs on
+//    transposed V reads.  S^T = K Q^T runs on v_mfma_f32_16x16x32_bf16 (one
+//    accumulation chain in the sorted walk, three in the ring kernel, whose
+//    exact routine the sorted walk shares); O^T = V^T P^T runs on
 //    v_mfma_f32_16x16x16_bf16 with V^T from ds_read_b64_tr_b16 and the
 //    probabilities straight from the score accumulators as the B operand.
 //    Operand reads run several MFMAs ahead (the order is pinned: left to
@@ -404,10 +405,10 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
 // a bitmap of the positions in the LDS tile, a prefix count over the lanes, and
 // compaction.  Tokens of a range select nearly the same rows, so walking them in the
 // same order lets concurrent tokens find each other's rows in L2.  (Repeated entries
-// collapse to one.)  Rows then stream into two 18 KiB LDS tiles by asynchronous
-// global->LDS copies (one step ahead; no register ring and no LDS store instructions),
-// in the 8-row-group layout of common.h: 16-byte chunk k of tile row r at
-// 9216 (r / 8) + 1024 (k / 8) + 128 (r % 8) + 16 ((k % 8) ^ swz8(r % 8) ^ (r / 8)).
+// collapse to one.)  Rows then stream into two LDS tiles of 16 rows (18 KiB at D = 576)
+// by asynchronous global->LDS copies (one step ahead; no register ring and no LDS store
+// instructions), in the 8-row-group layout of common.h: 16-byte chunk k of tile row r at
+// 16 D (r / 8) + 1024 (k / 8) + 128 (r % 8) + 16 ((k % 8) ^ swz8(r % 8) ^ (r / 8)).
 // The queries stay in registers.  The exact fallback reuses the register-ring
 // routines (the second tile is the query area there).
 // ---------------------------------------------------------------------------

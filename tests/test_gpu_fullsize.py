@@ -127,6 +127,31 @@ def test_dense_mha_full():
     check_attention(od[idx], ld[idx], ref_out, ref_lse, "dense MHA 2048")
 
 
+def test_fp8_latent_full():
+    """The benchmark's FP8 workload: the c3 chunk over an E4M3 latent with per-row scales.
+    Sampled tokens of both routings against the oracle, grouped == per-token everywhere."""
+    from mla_prefill_amd import routings
+    from synth import normal_fp8
+    c = make_case(CONFIGS["c3_glm16k"])
+    cfg = c.cfg
+    codes, kscale = normal_fp8(np.random.default_rng(9), cfg.S, cfg.d_qk, per_row=True)
+    q, tk = dev_bf16(c.q), dev_i32(c.topk)
+    c8 = torch.from_numpy(codes).cuda()
+    s8 = torch.from_numpy(kscale).cuda()
+    op, lp = routings.pertoken_fp8(q, c8, s8, tk, 0, cfg.scale)
+    og, lg, _ = routings.grouped_fp8(q, c8, s8, tk, 0, cfg.scale)
+    torch.cuda.synchronize()
+    toks = sample_tokens(cfg.T, cfg.G, n_random=16, seed=4)
+    print(f"[fp8] oracle on {len(toks)} sampled tokens", flush=True)
+    ref_out, ref_lse = oracle.pertoken_sparse_mqa_fp8(c.q, codes, kscale, c.topk, cfg.S, 0, cfg.scale,
+                                                      tokens=toks)
+    idx = torch.tensor(toks, device="cuda")
+    check_attention(op[idx], lp[idx], ref_out, ref_lse, "fp8 per-token")
+    check_attention(og[idx], lg[idx], ref_out, ref_lse, "fp8 grouped")
+    rel = (torch.linalg.vector_norm(og.float() - op.float()) / torch.linalg.vector_norm(op.float())).item()
+    assert rel <= OUT_RTOL, rel
+
+
 def test_paged_batch_full():
     """The benchmark's paged batch (8 requests x 2048 query tokens after 14336 positions of
     context, 64-row pages shuffled over a 135168-row cache): union, mask and group table of
