@@ -151,15 +151,25 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
       src = klist + min(j0 + (lane & 7), ncols - 1);
     dma4(src, lds_addr(&idxw[t % kRIdxBufs][wave][0]));
   };
+  // (a latent below 2 GiB: every row offset fits 31 bits, and block c's copies take the
+  // uniform base kv + 128 c plus the lane's offset, with no 64-bit address arithmetic)
+  const bool small_kv = (int64_t)S * (2 * D) < ((int64_t)1 << 31);
+  const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv);
   auto issue_rows = [&](int t) {
     const int32_t x = (int32_t)idxw[t % kRIdxBufs][wave][crow];  // landed (own copy, waited for)
     const bool ok = slot_ok(x, t * kRKeys + 8 * wave + crow);
-    const uint16_t* src = cbase + (size_t)(ok ? x : 0) * D;  // invalid slots copy row 0 (masked)
     const uint32_t dst = lds_addr(stage[t % kRStages]) + cdst;
     // (the global address carries the block offset: an instruction offset would also
     // move the LDS destination of an LDS-DMA load)
+    if (small_kv) {
+      const uint32_t ofs = (uint32_t)(ok ? x : 0) * (2 * D) + 16 * cchunk;  // invalid slots copy row 0
 #pragma unroll
-    for (int c = 0; c < kRCopies; ++c) dma16(src + 64 * c, dst + 1024 * c);
+      for (int c = 0; c < kRCopies; ++c) dma16_sbase(ofs, kvb + 128 * c, dst + 1024 * c);
+    } else {
+      const uint16_t* src = cbase + (size_t)(ok ? x : 0) * D;  // invalid slots copy row 0 (masked)
+#pragma unroll
+      for (int c = 0; c < kRCopies; ++c) dma16(src + 64 * c, dst + 1024 * c);
+    }
   };
 
   // K reads (A of S^T): key m, dims 16 s + 8 hi -> chunk 2 s + hi: 4 bases (s % 4) + (s / 4) KiB
