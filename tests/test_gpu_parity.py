@@ -371,6 +371,34 @@ def test_dense_mha_equals_masked_when_topk_covers_the_chunk(R, dn, dr):
     assert torch.equal(ld, lm)
 
 
+@pytest.mark.parametrize("dn,dr", [(256, 0), (192, 64), (128, 64)])
+def test_masked_and_dense_mha_score_jump(R, dn, dr):
+    """A few keys score far above everything earlier in their token's row (key rows set to
+    +-8 along the token's query on head 0: ~140 units of the base-2 exponent above the
+    first tile's maximum, beyond the fast kernel's 2^64 reference range), so those rows go
+    through the exact path; the other rows and head 1 stay on the fast path."""
+    rng = np.random.default_rng(41 + dn)
+    T, S, H, P0 = 300, 300, 2, 0
+    q = normal_bf16(rng, (T, H, dn + dr))
+    kn = normal_bf16(rng, (S, H, dn))
+    kp = normal_bf16(rng, (S, dr)) if dr else None
+    v = normal_bf16(rng, (S, H, mha_dv(dn)))
+    topk = topk_uniform(rng, T, S, 64, 70, P0)
+    for t, x in ((250, 200), (263, 131), (299, 298), (40, 33)):
+        kn[x, 0] = np.where(q[t, 0, :dn] & 0x8000, 0xC100, 0x4100).astype(np.uint16)  # bf16 -8 / +8
+        topk[t][topk[t] == x] = -1
+        topk[t, 3] = x
+    topk = shuffle_rows(topk, 41)
+    qd, knd, vd = dev_bf16(q), dev_bf16(kn), dev_bf16(v)
+    kpd = None if kp is None else dev_bf16(kp)
+    out, lse, _ = R.masked_mha(qd, knd, kpd, vd, dev_i32(topk), P0, 0.0625)
+    ref_out, ref_lse = oracle.masked_mha(q, kn, kp, v, topk, S, P0, 0.0625)
+    check_attention(out, lse, ref_out, ref_lse, f"masked score jump ({dn}, {dr})")
+    out, lse = R.dense_mha(qd, knd, kpd, vd, P0, 0.0625)
+    ref_out, ref_lse = oracle.dense_causal_mha(q, kn, kp, v, S, P0, 0.0625)
+    check_attention(out, lse, ref_out, ref_lse, f"dense score jump ({dn}, {dr})")
+
+
 def test_masked_and_dense_mha_long_context(R):
     """Keys past position 65535 (a 70000-key context, 20 query tokens at its end)."""
     rng = np.random.default_rng(38)
