@@ -29,9 +29,10 @@
 //    conflicts;
 //  * the PV runs one tile behind the QK, and the softmax work sits between the
 //    MFMAs of the same wave, so the vector ALU works while the matrix cores
-//    do: block 0's QK MFMAs of tile t take block 1's exponentials of tile
-//    t-1, then block 1's QK follows; tile t-1's PV MFMAs take tile t's
-//    masking and maxima and block 0's exponentials (one S^T buffer per block);
+//    do: the QK MFMAs of tile t take block 1's exponentials of tile
+//    t-1 (block 1's new scores go to a second buffer, so each K operand read
+//    feeds both blocks); tile t-1's PV MFMAs take tile t's masking and maxima
+//    and block 0's exponentials;
 //  * the causal test and the top-k bit select scores in registers (bit-field
 //    insert of -inf); the softmax scale is folded into one fused multiply-add
 //    before the base-2 exponential; the bf16 probabilities go straight from
@@ -267,15 +268,17 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
       expo(sa, nma, lsa, pan, id - 34);
   };
 
-  // Phase 1 of tile t: block 0's S^T (kS) interleaved with block 1's exponentials of the
-  // previous tile (kE; its masked scores are still in sb), then block 1's S^T.
+  // Phase 1 of tile t: S^T of both blocks (kS; one K operand read feeds both MFMAs of a
+  // k-step), block 1's into a second buffer, interleaved with block 1's exponentials of the
+  // previous tile (kE; its masked scores are in sb); then sb takes the new scores.
+  f32x16 sbn;
   auto phase1 = [&](auto do_s, auto do_exp, int t) {
     constexpr bool kS = decltype(do_s)::value, kE = decltype(do_exp)::value;
     const uint8_t* kt = &stage[0][0] + loop_local((t % kMStages) * kStageBytes);
     auto kread = [&](int s) -> bf16x8 {
       return *reinterpret_cast<const bf16x8*>(kt + kofs[s & 3] + 1024 * (s >> 2));
     };
-    constexpr int kAhead = 4;
+    constexpr int kAhead = 2;
     bf16x8 kw[kAhead];
     if constexpr (kS) {
 #pragma unroll
@@ -286,25 +289,20 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (kS) {
-        sa = s == 0 ? mfma_qk_first(kw[s % kAhead], qa[s]) : mfma_qk(kw[s % kAhead], qa[s], sa);
-        kw[s % kAhead] = kread(s + kAhead < kQSteps ? s + kAhead : s + kAhead - kQSteps);
-      }
+      if constexpr (kS) sa = s == 0 ? mfma_qk_first(kw[s % kAhead], qa[s]) : mfma_qk(kw[s % kAhead], qa[s], sa);
       if constexpr (kE) {
 #pragma unroll
         for (int j = s * 16 / kSteps; j < (s + 1) * 16 / kSteps; ++j) expo(sb, nmb, lsb, pb, j);
       }
-    }
-    if constexpr (kE) lb_ += lsb;  // this half's keys; the halves are summed at the end
-    if constexpr (kS) {
-#pragma unroll
-      for (int s = 0; s < kQSteps; ++s) {
-        __builtin_amdgcn_sched_barrier(0);
-        sb = s == 0 ? mfma_qk_first(kw[s % kAhead], qb[s]) : mfma_qk(kw[s % kAhead], qb[s], sb);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kS) {
+        sbn = s == 0 ? mfma_qk_first(kw[s % kAhead], qb[s]) : mfma_qk(kw[s % kAhead], qb[s], sbn);
         if (s + kAhead < kQSteps) kw[s % kAhead] = kread(s + kAhead);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kE) lb_ += lsb;  // this half's keys; the halves are summed at the end
+    if constexpr (kS) sb = sbn;
   };
 
   // Phase 2: O^T += V^T P^T for tile tv (kP; one V^T operand read per MFMA pair)
@@ -324,7 +322,7 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
       const u16x4 up = lds_read_tr16(vt + (2 * st + 1) * kVGroupBytes + 1024 * (cbk >> 1) + vbase + p1);
       return __builtin_bit_cast(bf16x8, u16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
     };
-    constexpr int kVAhead = 3;
+    constexpr int kVAhead = 2;
     bf16x8 vw[kVAhead];
     if constexpr (kP) {
 #pragma unroll
