@@ -75,8 +75,8 @@ int dsa_union_pad(int G, int cols) {
 namespace {
 double masked_threshold(int H, int mha_dv, bool grouped) {
   // {H 16, 32, 64 against grouped; 128 against per-token (G = 1); other H against per-token}
-  static const double kQk256[5] = {3.0, 2.4, 2.2, 1.9, 3.7};  // (256, 0, 256), (192, 64, 256)
-  static const double kDsv[5] = {4.3, 3.4, 3.1, 2.8, 5.5};    // (128, 64, 128)
+  static const double kQk256[5] = {3.0, 2.4, 2.2, 2.1, 3.4};  // (256, 0, 256), (192, 64, 256)
+  static const double kDsv[5] = {4.6, 3.6, 3.3, 3.1, 5.5};    // (128, 64, 128)
   const double* c = mha_dv == 128 ? kDsv : kQk256;
   if (!grouped) return H == 128 ? c[3] : c[4];
   return H == 16 ? c[0] : (H == 32 ? c[1] : c[2]);

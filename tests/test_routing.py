@@ -33,21 +33,22 @@ def test_masked_threshold_against_grouped(pick):
 
 
 def test_masked_threshold_against_pertoken(pick):
-    assert pick(6144, 6144, 0, 128, 2048, 256) == "masked"
-    assert pick(8192, 8192, 0, 128, 2048, 256) == "per-token"
+    # H 128: c = 2.1 -> mean causal keys <= 4300.8
+    assert pick(8192, 8192, 0, 128, 2048, 256) == "masked"
+    assert pick(9216, 9216, 0, 128, 2048, 256) == "per-token"
     assert pick(8192, 8192, 0, 128, 2048, 0) == "per-token"
-    # H 48: no grouped form (128 % 48 != 0); c = 3.7
-    assert pick(14000, 14000, 0, 48, 2048, 256) == "masked"
+    # H 48: no grouped form (128 % 48 != 0); c = 3.4
+    assert pick(13000, 13000, 0, 48, 2048, 256) == "masked"
     assert pick(16384, 16384, 0, 48, 2048, 256) == "per-token"
     assert pick(16384, 16384, 0, 48, 2048, 0) == "per-token"
 
 
 def test_thresholds_of_the_dsv32_geometry(pick):
-    # (128, 64, 128): c = 4.3 / 3.4 / 3.1 against grouped, 2.8 at H 128
-    assert pick(17000, 17000, 0, 16, 2048, 128) == "masked"
-    assert pick(18000, 18000, 0, 16, 2048, 128) == "grouped"
-    assert pick(11000, 11000, 0, 128, 2048, 128) == "masked"
-    assert pick(12000, 12000, 0, 128, 2048, 128) == "per-token"
+    # (128, 64, 128): c = 4.6 / 3.6 / 3.3 against grouped, 3.1 at H 128
+    assert pick(18000, 18000, 0, 16, 2048, 128) == "masked"
+    assert pick(19500, 19500, 0, 16, 2048, 128) == "grouped"
+    assert pick(12000, 12000, 0, 128, 2048, 128) == "masked"
+    assert pick(13000, 13000, 0, 128, 2048, 128) == "per-token"
     assert pick(22000, 22000, 0, 48, 2048, 128) == "masked"
     from mla_prefill_amd import _lib
     assert _lib.lib.dsa_select_routing(8192, 8192, 0, 16, 2048, 192) == -3
