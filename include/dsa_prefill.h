@@ -197,7 +197,11 @@ int dsa_sparse_prefill_pertoken(const uint16_t* q, const uint16_t* kv, const int
  *           dsa_masked_mha_workspace_bytes(T, S) bytes; overwritten with the
  *           bit-packed top-k membership (bit x % 32 of word x / 32 of row t)
  *   out     bf16 [T, H, dv];  lse fp32 [T, H]
- * Two kernels are enqueued: the mask scatter, then the attention. */
+ *   H       1 .. 65536, and ceil(T / 256) * H < 2^31 (else DSA_ERR_SHAPE)
+ * Three kernels are enqueued: the mask scatter, the attention, and an exact
+ * pass that returns at once unless a row's scores rose more than 2^64 above
+ * the attention kernel's fixed softmax reference (it then recomputes that
+ * row's 256-token tile with a running max). */
 int dsa_masked_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_pe,
                            const uint16_t* v, const int32_t* topk, int64_t ld, int T, int S, int H,
                            int dn, int dr, int dv, int cols, int64_t q_pos_offset, float scale,
@@ -212,7 +216,8 @@ int dsa_masked_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint
  * causal positions, i.e. whenever q_pos_offset + T <= the top-k size; the
  * caller decides when that holds -- no top-k is read here.  Geometries,
  * layouts, alignment and errors as dsa_masked_mha_prefill (without topk and
- * mask_ws).  One kernel is enqueued. */
+ * mask_ws).  Two kernels are enqueued: the attention and the exact pass
+ * described there. */
 int dsa_dense_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_pe,
                           const uint16_t* v, int T, int S, int H, int dn, int dr, int dv,
                           int64_t q_pos_offset, float scale, uint16_t* out, float* lse, void* stream);

@@ -367,7 +367,9 @@ int dsa_masked_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint
   // (128, 64, 128), the key is k_nope || k_pe with k_pe shared by every head
   const bool nope = mha_nope(dn, dr, dv), rope = mha_rope(dn, dr, dv);
   if ((!nope && !rope) || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
-  if (H < 1 || T < 0 || S < 1 || cols < 0 || ld < cols || q_pos_offset < 0) return DSA_ERR_SHAPE;
+  // (H <= 65536 keeps the kernels' 32-bit per-lane key-row offsets and the grid in range)
+  if (H < 1 || H > 65536 || T < 0 || S < 1 || cols < 0 || ld < cols || q_pos_offset < 0) return DSA_ERR_SHAPE;
+  if (((int64_t)T + 255) / 256 * H > 0x7fffffff) return DSA_ERR_SHAPE;  // one workgroup per (256 tokens, head)
   if (T == 0) return DSA_OK;
   if (!q || !k_nope || !v || (cols > 0 && !topk) || !mask_ws || !out || !lse || (rope && !k_pe))
     return DSA_ERR_NULL;
@@ -389,7 +391,8 @@ int dsa_dense_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint1
                           int64_t q_pos_offset, float scale, uint16_t* out, float* lse, void* stream) {
   const bool nope = mha_nope(dn, dr, dv), rope = mha_rope(dn, dr, dv);
   if ((!nope && !rope) || !scale_ok(scale)) return DSA_ERR_UNSUPPORTED;
-  if (H < 1 || T < 0 || S < 1 || q_pos_offset < 0) return DSA_ERR_SHAPE;
+  if (H < 1 || H > 65536 || T < 0 || S < 1 || q_pos_offset < 0) return DSA_ERR_SHAPE;
+  if (((int64_t)T + 255) / 256 * H > 0x7fffffff) return DSA_ERR_SHAPE;  // one workgroup per (256 tokens, head)
   if (T == 0) return DSA_OK;
   if (!q || !k_nope || !v || !out || !lse || (rope && !k_pe)) return DSA_ERR_NULL;
   if (!aligned_to(q, 16) || !aligned_to(k_nope, 16) || !aligned_to(v, 16) ||

@@ -149,6 +149,7 @@ def test_masked_mha_validation(lib):
     assert mha_call(lib, dn=128, dr=0, dv=128) == UNSUP and mha_call(lib, dn=128, dr=64, dv=256) == UNSUP
     assert mha_call(lib, dn=128) == UNSUP and mha_call(lib, dv=128) == UNSUP
     assert mha_call(lib, H=0) == SHAPE and mha_call(lib, ld=8) == SHAPE
+    assert mha_call(lib, H=65537) == SHAPE and mha_call(lib, T=2**31 - 1, H=65536) == SHAPE
     assert mha_call(lib, T=0) == OK
     for kw in ("q", "kn", "v", "tk", "ws", "out", "lse"):
         assert mha_call(lib, **{kw: None}) == NULL
@@ -166,6 +167,7 @@ def test_dense_mha_validation(lib):
     assert dense_call(lib, dn=192, dr=64, kp=P, T=0) == OK
     assert dense_call(lib, dn=256, dr=64) == UNSUP and dense_call(lib, dv=128) == UNSUP
     assert dense_call(lib, H=0) == SHAPE and dense_call(lib, S=0) == SHAPE and dense_call(lib, p0=-1) == SHAPE
+    assert dense_call(lib, H=65537) == SHAPE and dense_call(lib, T=2**31 - 1, H=65536) == SHAPE
     assert dense_call(lib, T=0) == OK
     for kw in ("q", "kn", "v", "out", "lse"):
         assert dense_call(lib, **{kw: None}) == NULL
