@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kUnionThreads) void build_union_kernel(
 // per token row; the row's words are built in LDS and written out coalesced,
 // so every word (including the zero ones) is overwritten by each call.
 constexpr int kBitsThreads = 256;
-constexpr int kBitsWindowWords = 8192;  // 32 KiB of LDS: 262144 positions per pass
+constexpr int kBitsWindowWords = 4096;  // 16 KiB of LDS: 131072 positions per pass
 
 __global__ __launch_bounds__(kBitsThreads) void scatter_topk_bits_kernel(
     const int32_t* __restrict__ topk, int64_t ld, int T, int cols, int S, int64_t q_pos_offset,
@@ -223,11 +223,22 @@ __global__ __launch_bounds__(kBitsThreads) void scatter_topk_bits_kernel(
     for (int i = tid; i < nw; i += kBitsThreads) row[i] = 0u;
     __syncthreads();
     const int64_t lo = (int64_t)wb * 32, hi = lo + (int64_t)nw * 32;
-    for (int c = tid; c < cols; c += kBitsThreads) {
-      const int32_t x = trow[c];
-      if (x >= 0 && x < S && (int64_t)x <= pos && x >= lo && x < hi) {
-        const int p = (int)(x - lo);
-        atomicOr(&row[p >> 5], 1u << (p & 31));
+    // (eight independent loads per thread before their LDS updates: one memory latency per
+    // eight entries instead of one per entry)
+    for (int c0 = tid; c0 < cols; c0 += 8 * kBitsThreads) {
+      int32_t xs[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = c0 + u * kBitsThreads;
+        xs[u] = c < cols ? trow[c] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int32_t x = xs[u];
+        if (x >= 0 && x < S && (int64_t)x <= pos && x >= lo && x < hi) {
+          const int p = (int)(x - lo);
+          atomicOr(&row[p >> 5], 1u << (p & 31));
+        }
       }
     }
     __syncthreads();
