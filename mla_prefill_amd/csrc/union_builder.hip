@@ -146,16 +146,32 @@ __global__ __launch_bounds__(kUnionThreads) void build_union_kernel(
     for (int i = tid; i < (wlen + 3) / 4; i += kUnionThreads) bytemap[i] = 0u;
     __syncthreads();
 
-    for (int e = tid; e < ntok * cols; e += kUnionThreads) {
-      const int i = e / cols;
-      const int c = e - i * cols;
-      const int t = t0 + i;
-      const int32_t x = topk[(size_t)t * ld + c];
-      // selection rule: 0 <= x < S and x <= position of token t; x >= w0 >= 0 covers x >= 0
-      // (a batch also drops positions without a physical row)
-      if (x >= w0 && x - w0 < wlen && (int64_t)x <= pos0 + i && (!kVarlen || physical_row(b, r, x) >= 0)) {
-        const int p = x - w0;
-        atomicOr(&bytemap[p >> 2], (1u << i) << (8 * (p & 3)));
+    // (eight independent loads per thread before their LDS updates: one memory latency per
+    // eight entries instead of one per entry)
+    const int nent = ntok * cols;
+    for (int e0 = tid; e0 < nent; e0 += 8 * kUnionThreads) {
+      int32_t xs[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * kUnionThreads;
+        xs[u] = -1;
+        if (e < nent) {
+          const int i = e / cols;
+          xs[u] = topk[(size_t)(t0 + i) * ld + (e - i * cols)];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * kUnionThreads;
+        const int i = e / cols;
+        const int32_t x = xs[u];
+        // selection rule: 0 <= x < S and x <= position of token t; x >= w0 >= 0 covers x >= 0
+        // (a batch also drops positions without a physical row); entries past the group
+        // hold -1
+        if (x >= w0 && x - w0 < wlen && (int64_t)x <= pos0 + i && (!kVarlen || physical_row(b, r, x) >= 0)) {
+          const int p = x - w0;
+          atomicOr(&bytemap[p >> 2], (1u << i) << (8 * (p & 3)));
+        }
       }
     }
     __syncthreads();
