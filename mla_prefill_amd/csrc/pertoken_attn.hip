@@ -419,9 +419,15 @@ __device__ __forceinline__ int pt_sort(const int32_t* trow, int cols, int pos, i
   const int nw = (pos >> 5) + 1;  // words covering positions 0..pos (pos < 65536)
   for (int w = lane; w < nw; w += 64) bm[w] = 0u;
   __syncthreads();  // (one wave: orders the LDS accesses for the compiler)
-  for (int col = lane; col < cols; col += 64) {
-    const int32_t x = trow[col];
-    if (x >= 0 && x <= pos) atomicOr(&bm[x >> 5], 1u << (x & 31));
+  // (eight independent loads per lane before their LDS updates: one memory latency per
+  // eight entries instead of one per entry)
+  for (int c0 = lane; c0 < cols; c0 += 8 * 64) {
+    int32_t xs[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) xs[u] = c0 + 64 * u < cols ? trow[c0 + 64 * u] : -1;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (xs[u] >= 0 && xs[u] <= pos) atomicOr(&bm[xs[u] >> 5], 1u << (xs[u] & 31));
   }
   __syncthreads();
   const int wpl = (nw + 63) >> 6;  // lane l owns words l * wpl .. + wpl - 1
