@@ -11,15 +11,17 @@
 //
 // MI355X design: one wave per (token, 16-head block), one wave per workgroup
 // (no barriers), one wave per SIMD.  Two kernels share the arithmetic:
-//  * sorted walk (positions below 65536, rows of at most 2048 columns, which
-//    covers the pages' workloads): the wave first sorts its token's valid
-//    entries in LDS, so that the concurrent tokens of a range, which select
-//    nearly the same rows, walk them in the same order and find them in L2.
+//  * sorted walk (caches of up to 2^20 rows, rows of any width with at most
+//    2048 valid entries): the wave first sorts its token's valid entries in
+//    LDS, so that the concurrent tokens of a range, which select nearly the
+//    same rows, walk them in the same order and find them in L2.
 //    Rows then stream 16 at a time into two LDS tiles (18 KiB at 576 dims) by asynchronous
 //    global->LDS copies, one step ahead of the compute (each copy instruction
 //    covers one 128-byte line of 8 rows, so a quarter-wave touches two cache
 //    lines); the 16 heads' queries stay in registers;
-//  * register ring (any size): rows are loaded with the same coalesced pattern
+//  * register ring (any size; also taken inside the sorted kernel when a
+//    token has more than 2048 valid entries): rows are loaded with the same
+//    coalesced pattern
 //    into two register buffers, each refilled two steps ahead as soon as it
 //    has been written to an LDS tile of 16 rows; the queries sit in a lane-private
 //    LDS area;
@@ -79,10 +81,19 @@ __device__ __forceinline__ f32x4 mfma16x16x16(s16x4_t a, s16x4_t b, f32x4 c) {
 // pt_q[s][l].
 __shared__ __align__(16) uint8_t pt_tile[kPKeys * Lat<kDqkMax>::row_bytes];
 __shared__ __align__(16) uint4 pt_q[Lat<kDqkMax>::loads][64];
-// sorted mode (positions < 65536, rows of at most kPSortMax columns): the token's valid
-// entries in ascending order
+// sorted mode: the token's valid entries in ascending order, each as its low 16 bits (the
+// 65536-row window of list index i is the number of window starts at or below i; the starts
+// travel in a register, one window per lane)
 constexpr int kPSortMax = 2048;
+constexpr int kPSortRows = 1 << 20;  // caches up to this many rows (16 windows; row offsets below 2^31)
 __shared__ __align__(16) uint16_t pt_sorted[kPSortMax];
+
+// the list entry at index i (below the list length), with its window restored
+__device__ __forceinline__ int pt_list_entry(int i, int wstart) {
+  int w = 0;
+  for (int u = 1; u < 16; ++u) w += __builtin_amdgcn_readlane(wstart, u) <= i ? 1 : 0;
+  return (int)pt_sorted[i] | (w << 16);
+}
 
 __device__ __forceinline__ int tswz(int r) { return (2 * (r >> 1) + (r >> 3)) & 7; }
 
@@ -141,9 +152,9 @@ __device__ __forceinline__ PtCtx pt_context(const uint16_t* kv, const int32_t* t
 // this lane's entries of step j: rows er and 8 + er (clamped into the list: the top-k row,
 // or in sorted mode the sorted valid entries, c.cols of them)
 template <bool kSorted>
-__device__ __forceinline__ int2 pt_entries(const PtCtx& c, int j) {
+__device__ __forceinline__ int2 pt_entries(const PtCtx& c, int j, int wstart = 0) {
   const int i0 = min(kPKeys * j + c.er, c.cols - 1), i1 = min(kPKeys * j + 8 + c.er, c.cols - 1);
-  if (kSorted) return int2{(int)pt_sorted[i0], (int)pt_sorted[i1]};
+  if (kSorted) return int2{pt_list_entry(i0, wstart), pt_list_entry(i1, wstart)};
   return int2{c.trow[i0], c.trow[i1]};
 }
 
@@ -273,13 +284,13 @@ __device__ __forceinline__ void pt_write(int g, const f32x4 (&o)[kDv / 16], floa
 template <int D, bool kSorted>
 __device__ __noinline__ void pt_exact(const uint16_t* kv, const int32_t* topk, int64_t ld, int S, int cols,
                                      int64_t q_pos_offset, float scale_log2, int token, uint16_t* orow,
-                                     float* lse_at) {
+                                     float* lse_at, int wstart) {
   const PtCtx c = pt_context<D>(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token);
   const int nsteps = (c.cols + kPKeys - 1) / kPKeys;
   float m = kNegInf;
   for (int j = 0; j < nsteps; ++j) {
     u32x4 buf[Lat<D>::loads];
-    const uint32_t vbits = pt_issue<D>(c, pt_entries<kSorted>(c, j), j, buf);
+    const uint32_t vbits = pt_issue<D>(c, pt_entries<kSorted>(c, j, wstart), j, buf);
     pt_store<D>(c, buf);
     float sv[4];
     m = fmaxf(m, pt_mask(c, pt_qk<D>(c), vbits, sv));
@@ -291,7 +302,7 @@ __device__ __noinline__ void pt_exact(const uint16_t* kv, const int32_t* topk, i
   for (int cb = 0; cb < kDv / 16; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < nsteps; ++j) {
     u32x4 buf[Lat<D>::loads];
-    const uint32_t vbits = pt_issue<D>(c, pt_entries<kSorted>(c, j), j, buf);
+    const uint32_t vbits = pt_issue<D>(c, pt_entries<kSorted>(c, j, wstart), j, buf);
     pt_store<D>(c, buf);
     float sv[4];
     pt_mask(c, pt_qk<D>(c), vbits, sv);
@@ -300,17 +311,15 @@ __device__ __noinline__ void pt_exact(const uint16_t* kv, const int32_t* topk, i
   pt_write(c.g, o, l, m, orow, lse_at);
 }
 
+// The register-ring walk of one (token, 16-head block): the whole work of the ring kernel,
+// and the sorted kernel's path for a token with more valid entries than its list holds.
+// (Scalars only in the signature: a struct passed to a non-inlined function would live in
+// scratch memory.)
 template <int D>
-__global__ __launch_bounds__(64) void pertoken_attn_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
-    const int32_t* __restrict__ topk, int64_t ld, int T, int H, int S, int cols,
-    int64_t q_pos_offset, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  const int nb = H >> 4;
-  const int item = xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
-  const int tq = item / nb;
-  const int token = T - 1 - tq;
-  const int hb = item - tq * nb;
-
+__device__ __noinline__ void pt_ring_token(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                                           const int32_t* __restrict__ topk, int64_t ld, int H, int S, int cols,
+                                           int64_t q_pos_offset, float scale_log2, uint16_t* __restrict__ out,
+                                           float* __restrict__ lse, int token, int hb) {
   const PtCtx c = pt_context<D>(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token);
 
   // queries of head n, dims 32 s + 8 g .. + 8 (the B operand of S^T = K Q^T); a negative
@@ -392,18 +401,30 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
     step(j + 1, rb, vb);
   }
   if (over) {
-    pt_exact<D, false>(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token, orow, lse_at);
+    pt_exact<D, false>(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token, orow, lse_at, 0);
     return;
   }
   pt_write(c.g, o, l_run, m_ref, orow, lse_at);
 }
 
+template <int D>
+__global__ __launch_bounds__(64) void pertoken_attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+    const int32_t* __restrict__ topk, int64_t ld, int T, int H, int S, int cols,
+    int64_t q_pos_offset, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  const int nb = H >> 4;
+  const int item = xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
+  const int tq = item / nb;
+  pt_ring_token<D>(q, kv, topk, ld, H, S, cols, q_pos_offset, scale_log2, out, lse, T - 1 - tq, item - tq * nb);
+}
+
 // ---------------------------------------------------------------------------
-// Sorted-walk kernel (positions below 65536, rows of at most kPSortMax columns).
+// Sorted-walk kernel (caches of up to kPSortRows rows; a token with more than kPSortMax
+// valid entries takes the register-ring walk instead).
 //
 // The wave first sorts its token's valid entries (0 <= x <= position) into pt_sorted:
 // a bitmap of the positions in the LDS tile, a prefix count over the lanes, and
-// compaction.  Tokens of a range select nearly the same rows, so walking them in the
+// compaction, one 131072-position chunk at a time.  Tokens of a range select nearly the same rows, so walking them in the
 // same order lets concurrent tokens find each other's rows in L2.  (Repeated entries
 // collapse to one.)  Rows then stream into two LDS tiles of 16 rows (18 KiB at D = 576)
 // by asynchronous global->LDS copies (one step ahead; no register ring and no LDS store
@@ -413,50 +434,70 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
 // routines (the second tile is the query area there).
 // ---------------------------------------------------------------------------
 
-// returns the number of distinct valid entries of the token's row, sorted into pt_sorted
-__device__ __forceinline__ int pt_sort(const int32_t* trow, int cols, int pos, int lane) {
+// Sorts the token's valid entries (0 <= x <= pos) into pt_sorted and returns how many there
+// are (repeated entries collapse to one; past kPSortMax the count goes on but nothing more is
+// stored).  Positions are taken in chunks of 131072 (a 16 KiB bitmap in the tile, one pass
+// over the row per chunk); each 65536-position window's first list index goes to lane w of
+// `wstart` (lanes of windows past the last position hold the count).
+__device__ __forceinline__ int pt_sort(const int32_t* trow, int cols, int pos, int lane, int& wstart) {
   uint32_t* bm = reinterpret_cast<uint32_t*>(pt_tile);
-  const int nw = (pos >> 5) + 1;  // words covering positions 0..pos (pos < 65536)
-  for (int w = lane; w < nw; w += 64) bm[w] = 0u;
-  __syncthreads();  // (one wave: orders the LDS accesses for the compiler)
-  // (eight independent loads per lane before their LDS updates: one memory latency per
-  // eight entries instead of one per entry)
-  for (int c0 = lane; c0 < cols; c0 += 8 * 64) {
-    int32_t xs[8];
+  int total = 0;
+  wstart = 0;
+  const int nchunks = uniform((pos >> 17) + 1);
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int lo = ch << 17;
+    const int hi = min(pos, lo + (1 << 17) - 1);  // inclusive
+    const int nw = ((hi - lo) >> 5) + 1;          // bitmap words of the chunk
+    for (int w = lane; w < nw; w += 64) bm[w] = 0u;
+    __syncthreads();  // (one wave: orders the LDS accesses for the compiler)
+    // (eight independent loads per lane before their LDS updates: one memory latency per
+    // eight entries instead of one per entry)
+    for (int c0 = lane; c0 < cols; c0 += 8 * 64) {
+      int32_t xs[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) xs[u] = c0 + 64 * u < cols ? trow[c0 + 64 * u] : -1;
+      for (int u = 0; u < 8; ++u) xs[u] = c0 + 64 * u < cols ? trow[c0 + 64 * u] : -1;
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (xs[u] >= 0 && xs[u] <= pos) atomicOr(&bm[xs[u] >> 5], 1u << (xs[u] & 31));
-  }
-  __syncthreads();
-  const int wpl = (nw + 63) >> 6;  // lane l owns words l * wpl .. + wpl - 1
-  const int w0 = lane * wpl;
-  int cnt = 0;
-  for (int k = 0; k < wpl; ++k)
-    if (w0 + k < nw) cnt += __popc(bm[w0 + k]);
-  int incl = cnt;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int v = __shfl_up(incl, d);
-    if (lane >= d) incl += v;
-  }
-  int at = incl - cnt;
-  for (int k = 0; k < wpl; ++k) {
-    if (w0 + k >= nw) break;
-    uint32_t bits = bm[w0 + k];
-    while (bits != 0u) {
-      pt_sorted[at++] = (uint16_t)(32 * (w0 + k) + __ffs(bits) - 1);
-      bits &= bits - 1u;
+      for (int u = 0; u < 8; ++u)
+        if (xs[u] >= lo && xs[u] <= hi) atomicOr(&bm[(xs[u] - lo) >> 5], 1u << (xs[u] & 31));
     }
+    __syncthreads();
+    // lane l owns words l * wpl .. + wpl - 1; past 2048 words a lane owns 64 words, so that
+    // the chunk's second window (words 2048..) starts exactly at lane 32
+    const int wpl = nw > 2048 ? 64 : (nw + 63) >> 6;
+    const int w0 = lane * wpl;
+    int cnt = 0;
+    for (int k = 0; k < wpl; ++k)
+      if (w0 + k < nw) cnt += __popc(bm[w0 + k]);
+    int incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d);
+      if (lane >= d) incl += v;
+    }
+    int at = total + incl - cnt;
+    for (int k = 0; k < wpl; ++k) {
+      if (w0 + k >= nw) break;
+      uint32_t bits = bm[w0 + k];
+      while (bits != 0u) {
+        if (at < kPSortMax) pt_sorted[at] = (uint16_t)(32 * (w0 + k) + __ffs(bits) - 1);  // (lo % 65536 = 0)
+        ++at;
+        bits &= bits - 1u;
+      }
+    }
+    const int below_half = uniform(__shfl(incl, nw > 2048 ? 31 : 63));
+    if (lane == 2 * ch) wstart = total;
+    if (lane == 2 * ch + 1) wstart = total + below_half;
+    total += uniform(__shfl(incl, 63));
+    __syncthreads();  // the bitmap is cleared again, or the tile rewritten, from here on
   }
-  const int n = uniform(__shfl(incl, 63));
-  __syncthreads();  // the sorted list is read, and the tile rewritten, from here on
-  return n;
+  if (lane >= 2 * nchunks) wstart = total;
+  return total;
 }
 
 struct PdCtx {
   int cols, pos, lane, g, n, er;
+  int wstart;   // lane w: list index of window w's first entry (windows of 65536 positions)
+  bool multi;   // the list spans more than one window
   float sc;
   int dofs[2];  // this lane's 16 bytes of each 128-byte line, for rows er (h = 0) and 8 + er (h = 1)
   int kofs[2];  // K read offsets (row n, chunk 4 s + g: per s % 2; + 1024 (s / 2))
@@ -464,8 +505,10 @@ struct PdCtx {
 };
 
 template <int D>
-__device__ __forceinline__ PdCtx pd_context(int pos, int cols, float scale_log2) {
+__device__ __forceinline__ PdCtx pd_context(int pos, int cols, float scale_log2, int wstart) {
   PdCtx c;
+  c.wstart = wstart;
+  c.multi = pos >= 65536;
   c.lane = threadIdx.x;
   c.g = c.lane >> 4;
   c.n = c.lane & 15;
@@ -500,7 +543,7 @@ __device__ __forceinline__ uint32_t pd_valid(const PdCtx& c, int j) {
 
 // start the copies of step j's rows into the tile at LDS address `tile`; returns the
 // validity bits of the step's 16 keys (past the list the copies fetch the token's own row)
-// (positions are below 65536 here, so a row's byte offset fits 31 bits; line k's copies take
+// (positions are below 2^20 here, so a row's byte offset fits 31 bits; line k's copies take
 // the base kvb + 128 k and the lane's row offset)
 template <int D>
 __device__ __forceinline__ uint32_t pd_issue(const PdCtx& c, const uint8_t* kvb, int2 e, int j, uint32_t tile) {
@@ -543,7 +586,23 @@ __device__ __forceinline__ void pd_copy_line(const PdSrc& p, uint32_t tile, int 
 
 __device__ __forceinline__ int2 pd_entries(const PdCtx& c, int j) {
   const int i0 = min(kPKeys * j + c.er, c.cols - 1), i1 = min(kPKeys * j + 8 + c.er, c.cols - 1);
-  return int2{(int)pt_sorted[i0], (int)pt_sorted[i1]};
+  int x0 = (int)pt_sorted[i0], x1 = (int)pt_sorted[i1];
+  if (c.multi) {
+    // the windows of the step's first and last entries (uniform); entries of a step that
+    // crosses a window start count the starts below them one by one
+    const int first = kPKeys * j, last = min(first + kPKeys - 1, c.cols - 1);
+    const int wa = __popcll(ballot(c.lane >= 1 && c.wstart <= first));
+    const int wb = __popcll(ballot(c.lane >= 1 && c.wstart <= last));
+    int h0 = wa, h1 = wa;
+    for (int w = wa + 1; w <= wb; ++w) {
+      const int st = __builtin_amdgcn_readlane(c.wstart, w);
+      h0 += i0 >= st ? 1 : 0;
+      h1 += i1 >= st ? 1 : 0;
+    }
+    x0 |= h0 << 16;
+    x1 |= h1 << 16;
+  }
+  return int2{x0, x1};
 }
 
 // S^T[key 4 g + jj][head n] (raw), one accumulation chain (dependent 16x16x32 MFMAs issue at
@@ -654,7 +713,8 @@ __global__ __launch_bounds__(64) void pertoken_sorted_kernel(
   }
   uint16_t* orow = out + ((size_t)token * H + hb * 16 + n) * kDv + 4 * g;
   float* lse_at = lse + (size_t)token * H + hb * 16 + n;
-  const int nsel = pt_sort(topk + (size_t)token * ld, cols, pos, lane);
+  int wstart;
+  const int nsel = pt_sort(topk + (size_t)token * ld, cols, pos, lane, wstart);
 #pragma unroll
   for (int s = 0; s < Lat<D>::loads; ++s) asm volatile("" : : "v"(qreg[s]));
   if (nsel == 0) {  // nothing selected: zero output, LSE -inf
@@ -662,7 +722,11 @@ __global__ __launch_bounds__(64) void pertoken_sorted_kernel(
     pt_write(g, z, 0.f, kNegInf, orow, lse_at);
     return;
   }
-  const PdCtx c = pd_context<D>(pos, nsel, scale_log2);
+  if (nsel > kPSortMax) {  // more valid entries than the list holds: the register-ring walk
+    pt_ring_token<D>(q, kv, topk, ld, H, S, cols, q_pos_offset, scale_log2, out, lse, token, hb);
+    return;
+  }
+  const PdCtx c = pd_context<D>(pos, nsel, scale_log2, wstart);
   const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv);
   uint8_t* const tile0 = pt_tile;
   uint8_t* const tile1 = reinterpret_cast<uint8_t*>(&pt_q[0][0]);
@@ -708,7 +772,7 @@ __global__ __launch_bounds__(64) void pertoken_sorted_kernel(
 #pragma unroll
     for (int s = 0; s < Lat<D>::loads; ++s) pt_q[s][lane] = __builtin_bit_cast(uint4, qreg[s]);
     __syncthreads();
-    pt_exact<D, true>(kv, topk, ld, S, nsel, q_pos_offset, scale_log2, token, orow, lse_at);
+    pt_exact<D, true>(kv, topk, ld, S, nsel, q_pos_offset, scale_log2, token, orow, lse_at, wstart);
     return;
   }
   pt_write(g, o, l_run, m_ref, orow, lse_at);
@@ -719,7 +783,7 @@ static void launch_pertoken(const uint16_t* q, const uint16_t* kv, const int32_t
                             int H, int S, int cols, int64_t q_pos_offset, float scale, uint16_t* out,
                             float* lse, hipStream_t stream) {
   const long long items = (long long)T * (H / 16);
-  if (S <= 65536 && cols <= kPSortMax)
+  if (S <= kPSortRows)
     hipLaunchKernelGGL(pertoken_sorted_kernel<D>, dim3((unsigned)items), dim3(64), 0, stream, q, kv, topk, ld,
                        T, H, S, cols, q_pos_offset, scale * kLog2e, out, lse);
   else

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from synth import CONFIGS, make_case
-from tests.gpu_helpers import OUT_RTOL, check_attention, dev_bf16, dev_i32
+from tests.gpu_helpers import check_attention, check_rows_equal, dev_bf16, dev_i32
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +40,7 @@ def _run(name):
     return c, (og, lg), (op, lp), bufs
 
 
-def sample_tokens(T, G, n_random=24, seed=0):
+def sample_tokens(T, G, n_random=48, seed=0):
     rng = np.random.default_rng(seed)
     last_group = ((T - 1) // G) * G
     toks = set(range(0, min(T, 4))) | set(range(max(0, T - 4), T)) | set(range(last_group, T))
@@ -72,9 +72,7 @@ def test_attention_sampled(full):
 
 def test_grouped_equals_pertoken_everywhere(full):
     name, (_, (og, lg), (op, lp), _) = full
-    a, b = og.float(), op.float()
-    rel = (torch.linalg.vector_norm(a - b) / torch.linalg.vector_norm(b)).item()
-    assert rel <= OUT_RTOL, rel
+    check_rows_equal(og, op, f"{name} grouped vs per-token")
     fin = torch.isfinite(lp)
     assert torch.equal(fin, torch.isfinite(lg))
     assert (lg[fin] - lp[fin]).abs().max().item() <= 2e-3
@@ -89,7 +87,7 @@ def test_masked_mha_full(name):
     out, lse, ws = routings.masked_mha(dev_bf16(c.q), dev_bf16(c.k_nope), kp, dev_bf16(c.v),
                                        dev_i32(c.topk), cfg.q_pos_offset, cfg.scale)
     torch.cuda.synchronize()
-    toks = sample_tokens(cfg.T, cfg.G, n_random=16, seed=1)
+    toks = sample_tokens(cfg.T, cfg.G, n_random=32, seed=1)
     print(f"[{name}] dense-mask oracle on {len(toks)} sampled tokens", flush=True)
     ref_out, ref_lse = oracle.masked_mha(c.q, c.k_nope, c.k_pe, c.v, c.topk, cfg.S, cfg.q_pos_offset,
                                          cfg.scale, tokens=toks)
@@ -148,8 +146,7 @@ def test_fp8_latent_full():
     idx = torch.tensor(toks, device="cuda")
     check_attention(op[idx], lp[idx], ref_out, ref_lse, "fp8 per-token")
     check_attention(og[idx], lg[idx], ref_out, ref_lse, "fp8 grouped")
-    rel = (torch.linalg.vector_norm(og.float() - op.float()) / torch.linalg.vector_norm(op.float())).item()
-    assert rel <= OUT_RTOL, rel
+    check_rows_equal(og, op, "fp8 grouped vs per-token")
 
 
 def test_paged_batch_full():

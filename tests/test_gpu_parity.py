@@ -162,7 +162,9 @@ def test_deterministic(R):
 
 
 def test_pertoken_far_positions_and_wide_rows(R):
-    """Per-token rows with positions beyond 65535 and rows wider than 3072 columns."""
+    """Per-token rows with positions beyond 65535 (two windows of the sorted list), and rows
+    with up to 3000 valid entries (more than the sorted list holds: the register-ring walk
+    inside the sorted kernel)."""
     rng = np.random.default_rng(14)
     H = 16
     for T, S, k, cols, P0 in ((12, 70000, 300, 320, 70000 - 12), (10, 4000, 3000, 3100, 4000 - 10)):
@@ -172,6 +174,33 @@ def test_pertoken_far_positions_and_wide_rows(R):
         ref_out, ref_lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, P0, 0.0625)
         out, lse = R.pertoken(dev_bf16(q), dev_bf16(kv), dev_i32(topk), P0, 0.0625)
         check_attention(out, lse, ref_out, ref_lse, f"per-token S={S} cols={cols}")
+
+
+def test_pertoken_sorted_windows(R):
+    """The sorted walk over a 300000-row latent: three 131072-position sort chunks, five
+    65536-row windows of the sorted list, rows at every window edge, a window holding a single
+    row (steps that cross several window starts), -1, out-of-range and non-causal entries."""
+    rng = np.random.default_rng(31)
+    T, S, H, cols = 6, 300000, 16, 300
+    P0 = S - T
+    q = normal_bf16(rng, (T, H, 576))
+    kv = normal_bf16(rng, (S, 576))
+    topk = np.full((T, cols), -1, np.int32)
+    for t in range(T):
+        pos = P0 + t
+        sel = {0, 65535, 65536, 131071, 131072, 196607, 196608, 262143, 262144, pos}
+        for lo, hi, n in ((1, 65534, 40), (65537, 131070, 3), (131073, 196606, 150), (196609, 262142, 1),
+                          (262145, pos - 1, 17)):
+            while sum(lo <= x <= hi for x in sel) < n:
+                sel.add(int(rng.integers(lo, hi + 1)))
+        row = sorted(sel) + [S, S + 7, -5]                       # out of range: ignored
+        if t < T - 1:
+            row += [int(rng.integers(pos + 1, S))]                 # not causal: ignored
+        row = [row[i] for i in rng.permutation(len(row))]
+        topk[t, :len(row)] = row
+    ref_out, ref_lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, P0, 0.0625)
+    out, lse = R.pertoken(dev_bf16(q), dev_bf16(kv), dev_i32(topk), P0, 0.0625)
+    check_attention(out, lse, ref_out, ref_lse, "per-token S=300000 windows")
 
 
 @pytest.mark.parametrize("H", [48, 112])
