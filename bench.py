@@ -695,8 +695,9 @@ def bench_paged(a):
 
 
 def bench_fp8(a):
-    """The glm16k chunk (c3 shapes and top-k) over an FP8 latent: the conversion pass into the
-    bf16 workspace, then union + grouped attention and per-token attention on it."""
+    """The glm16k chunk (c3 shapes and top-k) over an FP8 latent with per-row scales: each
+    routing's FP8 entry point (the exact decode into the bf16 workspace, then the attention
+    with the row scales) timed as a whole, plus the decode pass alone."""
     import torch
     from mla_prefill_amd import _lib, routings
     from synth import CONFIGS, make_case, normal_fp8
@@ -716,61 +717,42 @@ def bench_fp8(a):
     out_g, lse_g = routings.alloc_out(T, H, 512)
     out_p, lse_p = routings.alloc_out(T, H, 512)
     stream = torch.cuda.current_stream()
-    names = ["dequant_fp8", "build_union", "grouped_attn", "pertoken_attn"]
-
-    def step(ev=None):
-        def mark(i):
-            if ev is not None:
-                ev[i].record(stream)
-        mark(0)
-        _lib.dsa_dequant_latent_fp8(kv8, ksc, ws, stream=stream)
-        mark(1)
-        _lib.dsa_build_group_union(topk, S, 0, G, bufs.union_idx, bufs.union_len, bufs.mask, stream=stream)
-        mark(2)
-        _lib.dsa_sparse_prefill_grouped(q, ws, bufs.union_idx, bufs.union_len, bufs.mask, cfg.scale, out_g,
-                                        lse_g, stream=stream)
-        mark(3)
-        _lib.dsa_sparse_prefill_pertoken(q, ws, topk, 0, cfg.scale, out_p, lse_p, stream=stream)
-        mark(4)
-
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
-    t0 = time.perf_counter()
-    for s_ in range(a.steps):
-        step(events[s_])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = {n: float(np.mean([events[s_][i].elapsed_time(events[s_][i + 1]) for s_ in range(a.steps)]))
-           for i, n in enumerate(names)}
-    ms_step = wall * 1e3 / a.steps
-    work, nsel = algorithmic_work(case, bufs.union_len.cpu().numpy().astype(np.float64), None)
-    work["dequant_fp8"] = {"bound": "hbm", "bytes": S * cfg.d_qk * 3 + S * 4}
-    kernels = {}
-    for n in names:
-        wk, ms = work[n], per[n]
-        if wk["bound"] == "hbm":
-            ach = wk["bytes"] / (ms * 1e-3) / 1e9
-            kernels[n] = {"ms": ms, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": ach / HBM_PEAK_GBS, "algorithmic": wk["bytes"]}
-        else:
-            ach = wk["flops"] / (ms * 1e-3) / 1e12
-            kernels[n] = {"ms": ms, "bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFS,
-                          "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFS, "algorithmic": wk["flops"]}
-    dom = max(kernels, key=lambda k: kernels[k]["ms"])
-    d = kernels[dom]
+    calls = {
+        "decode": [("decode_fp8", lambda: _lib.dsa_decode_latent_fp8(kv8, ws, stream=stream))],
+        "grouped": [
+            ("build_union", lambda: _lib.dsa_build_group_union(topk, S, 0, G, bufs.union_idx, bufs.union_len,
+                                                               bufs.mask, stream=stream)),
+            ("grouped_fp8", lambda: _lib.dsa_sparse_prefill_grouped_fp8(q, kv8, ksc, bufs.union_idx, bufs.union_len,
+                                                                        bufs.mask, cfg.scale, ws, out_g, lse_g,
+                                                                        stream=stream))],
+        "per-token": [("pertoken_fp8", lambda: _lib.dsa_sparse_prefill_pertoken_fp8(q, kv8, ksc, topk, 0, cfg.scale,
+                                                                                   ws, out_p, lse_p,
+                                                                                   stream=stream))],
+    }
+    samples = {}
+    for cl in calls.values():
+        smp, _ = time_calls(cl, stream, a.steps, a.warmup)
+        samples.update(smp)
+    work, nsel = mqa_work(cfg, case.topk, bufs.union_len.cpu().numpy())
+    work["decode_fp8"] = ("hbm", S * cfg.d_qk * 3)
+    work["grouped_fp8"] = work["grouped_attn"]
+    work["pertoken_fp8"] = work["pertoken_attn"]
+    routings_out = {}
+    for r, cl in calls.items():
+        ks = {k: kernel_record(samples[k], *work[k]) for k, _ in cl}
+        routings_out[r] = routing_summary(T, ks)
+    ms_step = routings_out["grouped"]["ms"]
+    d = routings_out["grouped"]["kernels"]["grouped_fp8"]
     line = {
         "metric": METRIC, "value": round(T / (ms_step * 1e-3), 1), "unit": "query-tokens/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8 latent, bf16 compute", "data": "synthetic",
-        "config": {"workload": "glm16k_fp8", "T": T, "S": S, "H": H, "k": cfg.k, "G": G, "d_qk": cfg.d_qk,
-                   "fp8": "E4M3, per-row float32 scale", "selected_rows": nsel},
-        "roofline": {"kernel": dom, "bound": d["bound"], "achieved": round(d["achieved"], 2), "peak": d["peak"],
-                     "unit": d["unit"], "frac": round(d["frac"], 4), "traffic": None},
+        "config": {"workload": "glm16k_fp8", "routing": "grouped", "T": T, "S": S, "H": H, "k": cfg.k, "G": G,
+                   "d_qk": cfg.d_qk, "fp8": "E4M3, per-row float32 scale", "selected_rows": nsel},
+        "roofline": {"kernel": "grouped_fp8", "bound": d["bound"], "achieved": round(d["achieved"], 2),
+                     "peak": d["peak"], "unit": d["unit"], "frac": round(d["frac"], 4), "traffic": None},
         "cpu_baseline": None,
-        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-                    for k, v in kernels.items()},
+        "routings": rounded(routings_out),
     }
     print(json.dumps(line), flush=True)
 

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 
 /* status codes */
 #define DSA_OK 0
@@ -227,32 +227,36 @@ int dsa_dense_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint1
  * ("[Perf][DSA] Grouped sparse prefill ...", "How" section) and give no FP8
  * format; this library takes OCP E4M3 codes (uint8; sign, 4 exponent bits with
  * bias 7, 3 mantissa bits, subnormals, S.1111.111 = NaN) and float32 scales:
- * element (x, i) = e4m3(kv8[x, i]) * kv_scale[scale_per_row ? x : 0].
- * Each latent row is converted once per call into a caller workspace of bf16
- * rows (the float32 product rounded to nearest even), which the bf16 kernels
- * then gather: a row is gathered about T * k / S times per chunk, so one
- * conversion per row is far cheaper than one per use.
+ * element (x, i) = e4m3(kv8[x, i]) * kv_scale[scale_per_row ? x : 0], and the
+ * attention is the bf16 definition above on those exact values.
+ * Every E4M3 value is a bf16 number, so each latent row is decoded once per
+ * call, without rounding, into a caller workspace of bf16 rows (no scale
+ * applied); the attention kernels then multiply each key's score and each
+ * probability by the key row's scale (finite scales; l and the LSE use the
+ * unscaled probabilities).  A row is gathered about T * k / S times per chunk,
+ * so one decode per row is far cheaper than one per use.
  *   kv8       uint8 [S, d] codes, 16-byte aligned;  kv_scale float32 [S] or [1]
  *   scale_per_row  1: kv_scale[x] for row x;  0: kv_scale[0] for every row
  *   kv_ws     bf16 [S, d] workspace (16-byte aligned), overwritten
  * --------------------------------------------------------------------------- */
 
-/* Convert an FP8 latent (d = 576 or 512) to bf16 rows: out[x, i] = bf16(e4m3(
- * kv8[x, i]) * scale).  One kernel is enqueued. */
-int dsa_dequant_latent_fp8(const uint8_t* kv8, const float* kv_scale, int scale_per_row, int S, int d,
-                           uint16_t* out, void* stream);
+/* Decode FP8 codes (d = 576 or 512 per row) to the bf16 numbers they encode:
+ * out[x, i] = e4m3(kv8[x, i]), exactly; no scale is applied.  One kernel is
+ * enqueued. */
+int dsa_decode_latent_fp8(const uint8_t* kv8, int S, int d, uint16_t* out, void* stream);
 
-/* dsa_sparse_prefill_grouped over an FP8 latent: the conversion into kv_ws,
- * then grouped attention over kv_ws.  Arguments and errors as the bf16 form
- * plus the FP8 ones above; every check precedes the first enqueue. */
+/* dsa_sparse_prefill_grouped over an FP8 latent: the decode into kv_ws, then
+ * grouped attention over kv_ws with the row scales.  Arguments and errors as
+ * the bf16 form plus the FP8 ones above; every check precedes the first
+ * enqueue. */
 int dsa_sparse_prefill_grouped_fp8(const uint16_t* q, const uint8_t* kv8, const float* kv_scale,
                                    int scale_per_row, const int32_t* union_idx, const int32_t* union_len,
                                    const uint8_t* head_group_mask, int T, int H, int S, int union_pad,
                                    int d_qk, int d_v, float scale, uint16_t* kv_ws, uint16_t* out, float* lse,
                                    void* stream);
 
-/* dsa_sparse_prefill_pertoken over an FP8 latent (conversion, then the bf16
- * per-token path), as dsa_sparse_prefill_grouped_fp8. */
+/* dsa_sparse_prefill_pertoken over an FP8 latent (decode, then the per-token
+ * path with the row scales), as dsa_sparse_prefill_grouped_fp8. */
 int dsa_sparse_prefill_pertoken_fp8(const uint16_t* q, const uint8_t* kv8, const float* kv_scale,
                                     int scale_per_row, const int32_t* topk, int64_t ld, int T, int H, int S,
                                     int cols, int64_t q_pos_offset, int d_qk, int d_v, float scale,
@@ -316,8 +320,13 @@ int dsa_build_group_union_varlen(const int32_t* topk, int64_t ld, int T, int col
  * group g's tokens taken from group_info (as written by
  * dsa_build_group_union_varlen; entries are clamped into [0, T)) and the keys
  * read from the cache rows union_idx names (rows outside [0, num_slots) are
- * skipped).  Tokens covered by no group are not written. */
-int dsa_sparse_prefill_grouped_varlen(const uint16_t* q, const uint16_t* kv_cache, int num_slots,
+ * skipped).  Tokens covered by no group are not written.
+ *   kv_row_scale  NULL for a bf16 cache; else float32 [num_slots] (4-byte
+ *                 aligned), the scale of each cache row, which then holds
+ *                 decoded FP8 codes (the workspace dsa_decode_paged_fp8 writes):
+ *                 row x's elements are its values times kv_row_scale[x]. */
+int dsa_sparse_prefill_grouped_varlen(const uint16_t* q, const uint16_t* kv_cache, const float* kv_row_scale,
+                                      int num_slots,
                                       const int32_t* group_info, int max_groups, const int32_t* union_idx,
                                       const int32_t* union_len, const uint8_t* head_group_mask, int T,
                                       int H, int union_pad, int d_qk, int d_v, float scale,
@@ -326,8 +335,9 @@ int dsa_sparse_prefill_grouped_varlen(const uint16_t* q, const uint16_t* kv_cach
 /* Per-token sparse MQA of a batch: the index conversion into the caller's
  * workspace topk_ws int32 [T, cols], then dsa_sparse_prefill_pertoken over the
  * whole cache with every row in every token's causal range.  Two kernels are
- * enqueued. */
-int dsa_sparse_prefill_pertoken_varlen(const uint16_t* q, const uint16_t* kv_cache, int num_slots,
+ * enqueued.  kv_row_scale as for dsa_sparse_prefill_grouped_varlen. */
+int dsa_sparse_prefill_pertoken_varlen(const uint16_t* q, const uint16_t* kv_cache, const float* kv_row_scale,
+                                       int num_slots,
                                        const int32_t* topk, int64_t ld, int T, int H, int cols, int R,
                                        const int32_t* cu_seqlens_q, const int32_t* kv_lens,
                                        const int32_t* q_pos_start, const int32_t* block_table,
@@ -335,26 +345,29 @@ int dsa_sparse_prefill_pertoken_varlen(const uint16_t* q, const uint16_t* kv_cac
                                        int32_t* topk_ws, uint16_t* out, float* lse, void* stream);
 
 /* A batch over a paged FP8 cache (kv_scale indexed by cache row when
- * scale_per_row is 1): converts the pages each request can reach (positions
+ * scale_per_row is 1): decodes the pages each request can reach (positions
  * below kv_lens[r], pages 0 .. ceil(kv_lens[r] / page_size) - 1 of its block
  * table row) into ws_cache, request after request -- request r's pages start
- * at compact page off(r) = the reachable pages of requests 0 .. r - 1 -- and
- * writes ws_block_table [R, bt_ld] over ws_cache: off(r) + p for a reachable
- * page p whose page id is valid (0 <= id < num_slots / page_size) and fits
- * the workspace, -1 elsewhere.  The batch entry points above then run on
- * (ws_cache, ws_pages * page_size rows, ws_block_table) with the same
- * cu_seqlens_q / kv_lens / q_pos_start.  Pages shared by several requests are
- * converted once per request.
- *   ws_pages   workspace capacity in pages; it must hold the sum over requests
- *              of ceil(kv_lens[r] / page_size), or the pages past it map
- *              nowhere (their positions are not selected)
- *   ws_cache   bf16 [ws_pages * page_size, d];  ws_block_table int32 [R, bt_ld]
+ * at compact page off(r) = the reachable pages of requests 0 .. r - 1 --
+ * writes each decoded row's scale to ws_row_scale, and writes ws_block_table
+ * [R, bt_ld] over ws_cache: off(r) + p for a reachable page p whose page id is
+ * valid (0 <= id < num_slots / page_size) and fits the workspace, -1 elsewhere.
+ * The batch entry points above then run on (ws_cache, ws_row_scale, ws_pages *
+ * page_size rows, ws_block_table) with the same cu_seqlens_q / kv_lens /
+ * q_pos_start.  Pages shared by several requests are decoded once per request.
+ *   ws_pages      workspace capacity in pages; it must hold the sum over
+ *                 requests of ceil(kv_lens[r] / page_size), or the pages past
+ *                 it map nowhere (their positions are not selected)
+ *   ws_cache      bf16 [ws_pages * page_size, d] (decoded codes, exact)
+ *   ws_row_scale  float32 [ws_pages * page_size] (rows of pages that map
+ *                 nowhere are not written)
+ *   ws_block_table int32 [R, bt_ld]
  * num_slots must be a multiple of page_size; d = 576 or 512.  One kernel is
  * enqueued. */
-int dsa_dequant_paged_fp8(const uint8_t* cache8, const float* kv_scale, int scale_per_row, int num_slots,
-                          int d, int R, const int32_t* kv_lens, const int32_t* block_table, int64_t bt_ld,
-                          int page_size, int ws_pages, uint16_t* ws_cache, int32_t* ws_block_table,
-                          void* stream);
+int dsa_decode_paged_fp8(const uint8_t* cache8, const float* kv_scale, int scale_per_row, int num_slots,
+                         int d, int R, const int32_t* kv_lens, const int32_t* block_table, int64_t bt_ld,
+                         int page_size, int ws_pages, uint16_t* ws_cache, float* ws_row_scale,
+                         int32_t* ws_block_table, void* stream);
 
 #ifdef __cplusplus
 }

@@ -40,21 +40,21 @@ _SIGNATURES = {
                                 _i64, _f32, _vp, _vp, _vp, _vp], _i32),
     "dsa_dense_mha_prefill": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32,
                                _vp, _vp, _vp], _i32),
-    "dsa_dequant_latent_fp8": ([_vp, _vp, _i32, _i32, _i32, _vp, _vp], _i32),
+    "dsa_decode_latent_fp8": ([_vp, _i32, _i32, _vp, _vp], _i32),
     "dsa_sparse_prefill_grouped_fp8": ([_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                         _f32, _vp, _vp, _vp, _vp], _i32),
     "dsa_sparse_prefill_pertoken_fp8": ([_vp, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _i32, _i32, _i64, _i32, _i32,
                                          _f32, _vp, _vp, _vp, _vp], _i32),
-    "dsa_dequant_paged_fp8": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp],
-                              _i32),
+    "dsa_decode_paged_fp8": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp],
+                             _i32),
     "dsa_varlen_group_bound": ([_i32, _i32, _i32], _i32),
     "dsa_convert_req_index_to_global": ([_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
                                          _vp, _vp], _i32),
     "dsa_build_group_union_varlen": ([_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
                                       _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], _i32),
-    "dsa_sparse_prefill_grouped_varlen": ([_vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32,
+    "dsa_sparse_prefill_grouped_varlen": ([_vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32,
                                            _i32, _i32, _f32, _vp, _vp, _vp], _i32),
-    "dsa_sparse_prefill_pertoken_varlen": ([_vp, _vp, _i32, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp,
+    "dsa_sparse_prefill_pertoken_varlen": ([_vp, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp,
                                             _vp, _vp, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp],
                                            _i32),
 }
@@ -208,10 +208,11 @@ def _fp8(kv8, kv_scale):
     return per_row
 
 
-def dsa_dequant_latent_fp8(kv8, kv_scale, out, stream=None):
+def dsa_decode_latent_fp8(kv8, out, stream=None):
+    if kv8.dtype != torch.uint8:
+        raise TypeError("FP8 codes travel as uint8")
     S, d = kv8.shape
-    _check("dsa_dequant_latent_fp8", lib.dsa_dequant_latent_fp8(
-        _ptr(kv8), _ptr(kv_scale), _fp8(kv8, kv_scale), S, d, _ptr(_bits(out)), _stream(stream)))
+    _check("dsa_decode_latent_fp8", lib.dsa_decode_latent_fp8(_ptr(kv8), S, d, _ptr(_bits(out)), _stream(stream)))
 
 
 def dsa_sparse_prefill_grouped_fp8(q, kv8, kv_scale, union_idx, union_len, head_group_mask, scale, kv_ws,
@@ -279,29 +280,38 @@ def dsa_build_group_union_varlen(topk, batch, num_slots, G, group_info, union_id
         _ptr(head_group_mask), _stream(stream)))
 
 
+def _row_scale(kv_cache, kv_row_scale):
+    if kv_row_scale is None:
+        return None
+    if kv_row_scale.dtype != torch.float32 or kv_row_scale.numel() < kv_cache.shape[0]:
+        raise ValueError("kv_row_scale must be float32 with one value per cache row")
+    return _ptr(kv_row_scale)
+
+
 def dsa_sparse_prefill_grouped_varlen(q, kv_cache, group_info, union_idx, union_len, head_group_mask,
-                                      scale, out, lse, stream=None):
+                                      scale, out, lse, kv_row_scale=None, stream=None):
     T, H, d_qk = q.shape
     _check("dsa_sparse_prefill_grouped_varlen", lib.dsa_sparse_prefill_grouped_varlen(
-        _ptr(_bits(q)), _ptr(_bits(kv_cache)), kv_cache.shape[0], _ptr(group_info), group_info.shape[0],
+        _ptr(_bits(q)), _ptr(_bits(kv_cache)), _row_scale(kv_cache, kv_row_scale), kv_cache.shape[0],
+        _ptr(group_info), group_info.shape[0],
         _ptr(union_idx), _ptr(union_len), _ptr(head_group_mask), T, H, union_idx.shape[1], d_qk,
         out.shape[2], scale, _ptr(_bits(out)), _ptr(lse), _stream(stream)))
 
 
 def dsa_sparse_prefill_pertoken_varlen(q, kv_cache, topk, batch, scale, topk_ws, out, lse, cols=None,
-                                       stream=None):
+                                       kv_row_scale=None, stream=None):
     T, H, d_qk = q.shape
     cols = topk.shape[1] if cols is None else cols
     R, cu, kl, qs, bt, bt_ld, ps = _batch(batch)
     _check("dsa_sparse_prefill_pertoken_varlen", lib.dsa_sparse_prefill_pertoken_varlen(
-        _ptr(_bits(q)), _ptr(_bits(kv_cache)), kv_cache.shape[0], _ptr(topk), _topk_ld(topk), T, H, cols, R,
+        _ptr(_bits(q)), _ptr(_bits(kv_cache)), _row_scale(kv_cache, kv_row_scale), kv_cache.shape[0], _ptr(topk), _topk_ld(topk), T, H, cols, R,
         cu, kl, qs, bt, bt_ld, ps, d_qk, out.shape[2], scale, _ptr(topk_ws), _ptr(_bits(out)), _ptr(lse),
         _stream(stream)))
 
 
-def dsa_dequant_paged_fp8(cache8, kv_scale, batch, ws_cache, ws_block_table, stream=None):
-    """Convert the pages a batch can reach into ws_cache [ws_pages * page_size, d] and write
-    ws_block_table [R, bt_ld] over it."""
+def dsa_decode_paged_fp8(cache8, kv_scale, batch, ws_cache, ws_row_scale, ws_block_table, stream=None):
+    """Decode the pages a batch can reach into ws_cache [ws_pages * page_size, d], their rows'
+    scales into ws_row_scale, and write ws_block_table [R, bt_ld] over the workspace."""
     _, kv_lens, _, block_table, page_size = batch
     b = _batch(batch)
     R, bt_ld = b[0], b[5]
@@ -309,6 +319,9 @@ def dsa_dequant_paged_fp8(cache8, kv_scale, batch, ws_cache, ws_block_table, str
     if ws_block_table.dtype != torch.int32 or ws_block_table.shape != block_table.shape:
         raise ValueError("ws_block_table must be int32 shaped like block_table")
     ws_pages = ws_cache.shape[0] // page_size
-    _check("dsa_dequant_paged_fp8", lib.dsa_dequant_paged_fp8(
+    if ws_row_scale.dtype != torch.float32 or ws_row_scale.numel() < ws_pages * page_size:
+        raise ValueError("ws_row_scale must be float32 with one value per workspace row")
+    _check("dsa_decode_paged_fp8", lib.dsa_decode_paged_fp8(
         _ptr(cache8), _ptr(kv_scale), _fp8(cache8, kv_scale), num_slots, d, R, _ptr(kv_lens), _ptr(block_table),
-        bt_ld, page_size, ws_pages, _ptr(_bits(ws_cache)), _ptr(ws_block_table), _stream(stream)))
+        bt_ld, page_size, ws_pages, _ptr(_bits(ws_cache)), _ptr(ws_row_scale), _ptr(ws_block_table),
+        _stream(stream)))

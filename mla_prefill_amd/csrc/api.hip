@@ -165,12 +165,13 @@ static int pertoken_check(const uint16_t* q, const uint16_t* kv, const int32_t* 
 
 static hipError_t pertoken_launch(const uint16_t* q, const uint16_t* kv, const int32_t* topk, int64_t ld,
                                   int T, int H, int S, int cols, int64_t q_pos_offset, int d_qk, float scale,
-                                  uint16_t* out, float* lse, hipStream_t stream) {
+                                  uint16_t* out, float* lse, hipStream_t stream, const float* kscale = nullptr,
+                                  int scale_per_row = 0) {
   if (H == 128)
     return dsa::launch_pertoken_rows128(q, kv, topk, ld, T, S, cols, q_pos_offset, scale, out, lse, stream,
-                                        d_qk);
+                                        d_qk, kscale, scale_per_row);
   return dsa::launch_pertoken_attn(q, kv, topk, ld, T, H, S, cols, q_pos_offset, scale, out, lse, stream,
-                                   d_qk);
+                                   d_qk, kscale, scale_per_row);
 }
 
 // the FP8 latent arguments (kv8 [S, d_qk] codes, kv_scale, the bf16 workspace)
@@ -203,14 +204,13 @@ int dsa_sparse_prefill_pertoken(const uint16_t* q, const uint16_t* kv, const int
                                        (hipStream_t)stream));
 }
 
-int dsa_dequant_latent_fp8(const uint8_t* kv8, const float* kv_scale, int scale_per_row, int S, int d,
-                           uint16_t* out, void* stream) {
+int dsa_decode_latent_fp8(const uint8_t* kv8, int S, int d, uint16_t* out, void* stream) {
   if (d != 576 && d != 512) return DSA_ERR_UNSUPPORTED;
   if (S < 0) return DSA_ERR_SHAPE;
   if (S == 0) return DSA_OK;
-  const int st = fp8_check(kv8, kv_scale, scale_per_row, out);
-  if (st != DSA_OK) return st;
-  return launch_status(dsa::launch_dequant_fp8(kv8, kv_scale, scale_per_row, S, d, out, (hipStream_t)stream));
+  if (!kv8 || !out) return DSA_ERR_NULL;
+  if (!aligned_to(kv8, 16) || !aligned_to(out, 16)) return DSA_ERR_ALIGN;
+  return launch_status(dsa::launch_decode_fp8(kv8, S, d, out, (hipStream_t)stream));
 }
 
 int dsa_sparse_prefill_grouped_fp8(const uint16_t* q, const uint8_t* kv8, const float* kv_scale,
@@ -223,11 +223,11 @@ int dsa_sparse_prefill_grouped_fp8(const uint16_t* q, const uint8_t* kv8, const 
                          scale, out, lse);
   if (st != DSA_OK) return st == kNothingToDo ? DSA_OK : st;
   if ((st = fp8_check(kv8, kv_scale, scale_per_row, kv_ws)) != DSA_OK) return st;
-  const hipError_t e = dsa::launch_dequant_fp8(kv8, kv_scale, scale_per_row, S, d_qk, kv_ws, (hipStream_t)stream);
+  const hipError_t e = dsa::launch_decode_fp8(kv8, S, d_qk, kv_ws, (hipStream_t)stream);
   if (e != hipSuccess) return DSA_ERR_LAUNCH;
   return launch_status(dsa::launch_grouped_attn(q, kv_ws, union_idx, union_len, head_group_mask, T, H, S,
                                                 union_pad, scale, out, lse, (hipStream_t)stream, nullptr, 0,
-                                                d_qk));
+                                                d_qk, kv_scale, scale_per_row));
 }
 
 int dsa_sparse_prefill_pertoken_fp8(const uint16_t* q, const uint8_t* kv8, const float* kv_scale,
@@ -237,10 +237,10 @@ int dsa_sparse_prefill_pertoken_fp8(const uint16_t* q, const uint8_t* kv8, const
   int st = pertoken_check(q, kv_ws, topk, ld, T, H, S, cols, q_pos_offset, d_qk, d_v, scale, out, lse);
   if (st != DSA_OK) return st == kNothingToDo ? DSA_OK : st;
   if ((st = fp8_check(kv8, kv_scale, scale_per_row, kv_ws)) != DSA_OK) return st;
-  const hipError_t e = dsa::launch_dequant_fp8(kv8, kv_scale, scale_per_row, S, d_qk, kv_ws, (hipStream_t)stream);
+  const hipError_t e = dsa::launch_decode_fp8(kv8, S, d_qk, kv_ws, (hipStream_t)stream);
   if (e != hipSuccess) return DSA_ERR_LAUNCH;
   return launch_status(pertoken_launch(q, kv_ws, topk, ld, T, H, S, cols, q_pos_offset, d_qk, scale, out, lse,
-                                       (hipStream_t)stream));
+                                       (hipStream_t)stream, kv_scale, scale_per_row));
 }
 
 int dsa_varlen_group_bound(int T, int R, int G) {
@@ -287,7 +287,8 @@ int dsa_build_group_union_varlen(const int32_t* topk, int64_t ld, int T, int col
       G, max_groups, union_pad, group_info, union_idx, union_len, head_group_mask, (hipStream_t)stream));
 }
 
-int dsa_sparse_prefill_grouped_varlen(const uint16_t* q, const uint16_t* kv_cache, int num_slots,
+int dsa_sparse_prefill_grouped_varlen(const uint16_t* q, const uint16_t* kv_cache, const float* kv_row_scale,
+                                      int num_slots,
                                       const int32_t* group_info, int max_groups, const int32_t* union_idx,
                                       const int32_t* union_len, const uint8_t* head_group_mask, int T,
                                       int H, int union_pad, int d_qk, int d_v, float scale,
@@ -301,14 +302,15 @@ int dsa_sparse_prefill_grouped_varlen(const uint16_t* q, const uint16_t* kv_cach
     return DSA_ERR_NULL;
   if (!aligned_to(q, 16) || !aligned_to(kv_cache, 16) || !aligned_to(out, 16) || !aligned_to(lse, 4) ||
       !aligned_to(group_info, 8) || !aligned_to(union_idx, 4) || !aligned_to(union_len, 4) ||
-      !aligned_to(head_group_mask, 4))
+      !aligned_to(head_group_mask, 4) || !aligned_to(kv_row_scale, 4))
     return DSA_ERR_ALIGN;
   return launch_status(dsa::launch_grouped_attn(q, kv_cache, union_idx, union_len, head_group_mask, T, H,
                                                 num_slots, union_pad, scale, out, lse, (hipStream_t)stream,
-                                                group_info, max_groups, d_qk));
+                                                group_info, max_groups, d_qk, kv_row_scale, 1));
 }
 
-int dsa_sparse_prefill_pertoken_varlen(const uint16_t* q, const uint16_t* kv_cache, int num_slots,
+int dsa_sparse_prefill_pertoken_varlen(const uint16_t* q, const uint16_t* kv_cache, const float* kv_row_scale,
+                                       int num_slots,
                                        const int32_t* topk, int64_t ld, int T, int H, int cols, int R,
                                        const int32_t* cu_seqlens_q, const int32_t* kv_lens,
                                        const int32_t* q_pos_start, const int32_t* block_table,
@@ -322,7 +324,7 @@ int dsa_sparse_prefill_pertoken_varlen(const uint16_t* q, const uint16_t* kv_cac
       !batch_ptrs_ok(cu_seqlens_q, kv_lens, q_pos_start, block_table))
     return DSA_ERR_NULL;
   if (!aligned_to(q, 16) || !aligned_to(kv_cache, 16) || !aligned_to(out, 16) || !aligned_to(lse, 4) ||
-      !aligned_to(topk, 4) || !aligned_to(topk_ws, 4) ||
+      !aligned_to(topk, 4) || !aligned_to(topk_ws, 4) || !aligned_to(kv_row_scale, 4) ||
       !batch_aligned(cu_seqlens_q, kv_lens, q_pos_start, block_table))
     return DSA_ERR_ALIGN;
   // physical-row top-k (causality applied), then the single-sequence kernel over the whole
@@ -334,29 +336,30 @@ int dsa_sparse_prefill_pertoken_varlen(const uint16_t* q, const uint16_t* kv_cac
   const int64_t all_causal = (int64_t)num_slots - 1;
   if (H == 128)
     e = dsa::launch_pertoken_rows128(q, kv_cache, topk_ws, cols, T, num_slots, cols, all_causal, scale, out,
-                                     lse, (hipStream_t)stream, d_qk);
+                                     lse, (hipStream_t)stream, d_qk, kv_row_scale, 1);
   else
     e = dsa::launch_pertoken_attn(q, kv_cache, topk_ws, cols, T, H, num_slots, cols, all_causal, scale, out,
-                                  lse, (hipStream_t)stream, d_qk);
+                                  lse, (hipStream_t)stream, d_qk, kv_row_scale, 1);
   return launch_status(e);
 }
 
-int dsa_dequant_paged_fp8(const uint8_t* cache8, const float* kv_scale, int scale_per_row, int num_slots,
-                          int d, int R, const int32_t* kv_lens, const int32_t* block_table, int64_t bt_ld,
-                          int page_size, int ws_pages, uint16_t* ws_cache, int32_t* ws_block_table,
-                          void* stream) {
+int dsa_decode_paged_fp8(const uint8_t* cache8, const float* kv_scale, int scale_per_row, int num_slots,
+                         int d, int R, const int32_t* kv_lens, const int32_t* block_table, int64_t bt_ld,
+                         int page_size, int ws_pages, uint16_t* ws_cache, float* ws_row_scale,
+                         int32_t* ws_block_table, void* stream) {
   if (d != 576 && d != 512) return DSA_ERR_UNSUPPORTED;
   if (num_slots < 1 || R < 1 || bt_ld < 1 || page_size < 1 || num_slots % page_size != 0 || ws_pages < 0 ||
       bt_ld > 65535 || R > 65535)
     return DSA_ERR_SHAPE;
-  if (!kv_lens || !block_table || !ws_block_table) return DSA_ERR_NULL;
-  if (!aligned_to(kv_lens, 4) || !aligned_to(block_table, 4) || !aligned_to(ws_block_table, 4))
+  if (!kv_lens || !block_table || !ws_block_table || !ws_row_scale) return DSA_ERR_NULL;
+  if (!aligned_to(kv_lens, 4) || !aligned_to(block_table, 4) || !aligned_to(ws_block_table, 4) ||
+      !aligned_to(ws_row_scale, 4))
     return DSA_ERR_ALIGN;
   const int st = fp8_check(cache8, kv_scale, scale_per_row, ws_cache);
   if (st != DSA_OK) return st;
-  return launch_status(dsa::launch_dequant_paged_fp8(cache8, kv_scale, scale_per_row, num_slots, d, R, kv_lens,
-                                                     block_table, bt_ld, page_size, ws_pages, ws_cache,
-                                                     ws_block_table, (hipStream_t)stream));
+  return launch_status(dsa::launch_decode_paged_fp8(cache8, kv_scale, scale_per_row, num_slots, d, R, kv_lens,
+                                                    block_table, bt_ld, page_size, ws_pages, ws_cache,
+                                                    ws_row_scale, ws_block_table, (hipStream_t)stream));
 }
 
 int dsa_masked_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_pe,

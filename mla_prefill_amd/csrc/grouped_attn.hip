@@ -37,6 +37,10 @@
 //    Probabilities may exceed 1 by up to 2^64 (safe for bf16 P and fp32 O and
 //    l); a group with a score beyond that is marked and recomputed by the
 //    exact kernel (rows128_exact.hip), which ordinary inputs never reach;
+//  * an FP8 latent (decoded exactly to bf16) carries a float32 scale per row:
+//    the scales of a tile's slots arrive by DMA with its rows, each raw score
+//    is multiplied by its row's scale before the softmax and each probability
+//    by it before the PV product (l sums the unscaled probabilities);
 //  * longest groups (most union slots) are launched first.
 #include "common.h"
 #include "kernels.h"
@@ -52,23 +56,27 @@ constexpr int kRIdxBufs = 4;                        // index/membership buffers 
 constexpr float kRSlack = 64.f;                     // log2 of the largest probability allowed
 constexpr int kRQRegSteps = 28;                     // query k-steps kept in registers
 
-// D: the latent width, 576 (512 + 64 rope dims) or 512 (no rope part)
-template <int D, bool kPerToken>
+// D: the latent width, 576 (512 + 64 rope dims) or 512 (no rope part); kScaled: the latent
+// rows carry scales (kscale[scale_per_row ? x : 0] for row x)
+template <int D, bool kPerToken, bool kScaled>
 __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ keys, int64_t keys_ld, const int32_t* __restrict__ union_len,
     const uint8_t* __restrict__ hgmask, int T, int H, int S, int ncols, int64_t q_pos_offset,
     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
-    const int32_t* __restrict__ ginfo) {
+    const int32_t* __restrict__ ginfo, const float* __restrict__ kscale, int scale_per_row) {
   static_assert(D == 576 || D == 512, "latent widths");
   constexpr int kRGroupBytes = 8 * D * 2;           // one 8-row group (9216 / 8192)
   constexpr int kRStageBytes = 4 * kRGroupBytes;    // one 32-slot tile
   constexpr int kRCopies = kRGroupBytes / 1024;     // row copies per wave per tile (9 / 8)
+  constexpr int kRRowOps = kRCopies + (kScaled ? 1 : 0);  // + the tile's scale copy
   constexpr int kRQLdsSteps = D / 16 - kRQRegSteps;  // query k-steps in LDS (lane-private)
   __shared__ __align__(16) uint8_t stage[kRStages][kRStageBytes];
   // per tile and wave: lanes 0..7 = slot indices 8 w .. 8 w + 7, lanes 8, 9 = their membership bytes
   __shared__ __align__(16) uint32_t idxw[kRIdxBufs][kRWaves][64];
   __shared__ __align__(16) uint4 qlds[kRWaves][kRQLdsSteps][64];
+  // kScaled: per tile and wave, lane l holds the scale of slot 8 w + l % 8
+  __shared__ __align__(16) float sbuf[kScaled ? kRStages : 1][kRWaves][64];
   __shared__ int over_any;
 
   const int G = 128 / H;
@@ -122,12 +130,25 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   int64_t pos64 = q_pos_offset + t0;  // per-token mode: the token's position
   if (pos64 > S - 1) pos64 = S - 1;
   const int pos = uniform((int)pos64);
-  const int ntiles = (nkeys + kRKeys - 1) / kRKeys;
   // validity of slot j holding latent row x (grouped: a union entry inside [0, S);
   // per-token: the selection rule)
   auto slot_ok = [&](int32_t x, int j) -> bool {
     return j < nkeys && x >= 0 && (kPerToken ? x <= pos : x < S);  // pos <= S - 1
   };
+  // the row invalid slots copy (their P is 0): the list's first valid entry, a row the group
+  // selects -- an unselected row (an unused slot of a paged cache) may hold anything, and 0
+  // times a NaN is NaN.  With no valid entry there is nothing to attend over.
+  int dummy_row = -1;
+  for (int c0 = 0; c0 < nkeys; c0 += 64) {
+    const int32_t x = c0 + lane < nkeys ? klist[c0 + lane] : -1;
+    const uint64_t b = ballot(slot_ok(x, c0 + lane));
+    if (b != 0) {
+      dummy_row = __builtin_amdgcn_readlane(x, __builtin_ctzll(b));
+      break;
+    }
+  }
+  dummy_row = uniform(dummy_row);
+  const int ntiles = dummy_row < 0 ? 0 : (nkeys + kRKeys - 1) / kRKeys;
 
   // the tokens of this wave's rows: 32 w / H and (32 w + 31) / H (two only for H = 16)
   const int ti0 = (32 * wave) / H, ti1 = (32 * wave + 31) / H;
@@ -162,13 +183,18 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
     // (the global address carries the block offset: an instruction offset would also
     // move the LDS destination of an LDS-DMA load)
     if (small_kv) {
-      const uint32_t ofs = (uint32_t)(ok ? x : 0) * (2 * D) + 16 * cchunk;  // invalid slots copy row 0
+      const uint32_t ofs = (uint32_t)(ok ? x : dummy_row) * (2 * D) + 16 * cchunk;
 #pragma unroll
       for (int c = 0; c < kRCopies; ++c) dma16_sbase(ofs, kvb + 128 * c, dst + 1024 * c);
     } else {
-      const uint16_t* src = cbase + (size_t)(ok ? x : 0) * D;  // invalid slots copy row 0 (masked)
+      const uint16_t* src = cbase + (size_t)(ok ? x : dummy_row) * D;
 #pragma unroll
       for (int c = 0; c < kRCopies; ++c) dma16(src + 64 * c, dst + 1024 * c);
+    }
+    if (kScaled) {  // the scales of slots 8 w .. 8 w + 7 (lane l: slot 8 w + l % 8)
+      const int32_t xs = (int32_t)idxw[t % kRIdxBufs][wave][lane & 7];
+      const bool oks = slot_ok(xs, t * kRKeys + 8 * wave + (lane & 7));
+      dma4(kscale + (scale_per_row && oks ? xs : 0), lds_addr(&sbuf[kScaled ? t % kRStages : 0][wave][0]));
     }
   };
 
@@ -201,7 +227,7 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   for (int t = 0; t < ntiles; ++t) {
     // tile t and the indices of tile t + 2 (copied before tile t + 1's rows) have landed
     if (t + 1 < ntiles)
-      wait_vmcnt<kRCopies>();
+      wait_vmcnt<kRRowOps>();
     else
       wait_vmcnt<0>();
     __syncthreads();  // tile t visible to all waves; stage (t + 2) % 3 and index buffer (t + 3) % 4 free
@@ -280,12 +306,20 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
     for (int i = 0; i < kRVAhead; ++i) vw[i] = vread(i);
     __builtin_amdgcn_sched_barrier(0);
 
+    // kScaled: the scales of slots 8 u + 4 hi .. + 3 (score registers 4 u .. 4 u + 3)
+    f32x4 ks[4];
+    if (kScaled) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        ks[u] = *reinterpret_cast<const f32x4*>(&sbuf[kScaled ? t % kRStages : 0][u][4 * hi]);
+    }
     float ml = kNegInf;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int kk = 8 * (j >> 2) + (j & 3);
       const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)allowed, kk, 1);  // all ones if allowed
-      const float raw = sacc[j];  // (a scalar copy: bit casts of vector elements misread)
+      // (a scalar copy: bit casts of vector elements misread)
+      const float raw = kScaled ? sacc[j] * ks[j >> 2][j & 3] : sacc[j];
       const float val = __builtin_bit_cast(float, (sel & __builtin_bit_cast(uint32_t, raw)) | (~sel & 0xff800000u));
       sacc[j] = val;
       ml = fmaxf(ml, val);
@@ -305,7 +339,7 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
     auto prob = [&](int j, float& l) {
       const float p = fast_exp2(__builtin_fmaf(sacc[j], sc, nm));
       l += p;
-      bop[j >> 3][j & 7] = (__bf16)p;
+      bop[j >> 3][j & 7] = (__bf16)(kScaled ? p * ks[j >> 2][j & 3] : p);
     };
 #pragma unroll
     for (int j = 0; j < 8; ++j) prob(j, l0);
@@ -344,43 +378,67 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   if (hi == 0) lse[(size_t)tok * H + rh] = l > 0.f ? (m_ref + fast_log2(l)) * kLn2 : kNegInf;
 }
 
+template <int D, bool kPerToken, bool kScaled>
+static void launch_rows128(int blocks, hipStream_t stream, const uint16_t* q, const uint16_t* kv,
+                           const int32_t* keys, int64_t keys_ld, const int32_t* union_len, const uint8_t* hgmask,
+                           int T, int H, int S, int ncols, int64_t q_pos_offset, float scale, uint16_t* out,
+                           float* lse, const int32_t* ginfo, const float* kscale, int scale_per_row) {
+  hipLaunchKernelGGL((rows128_attn_kernel<D, kPerToken, kScaled>), dim3(blocks), dim3(kRThreads), 0, stream, q,
+                     kv, keys, keys_ld, union_len, hgmask, T, H, S, ncols, q_pos_offset, scale * kLog2e, out, lse,
+                     ginfo, kscale, scale_per_row);
+}
+
+template <bool kPerToken>
+static void launch_rows128_any(int d_qk, int blocks, hipStream_t stream, const uint16_t* q, const uint16_t* kv,
+                               const int32_t* keys, int64_t keys_ld, const int32_t* union_len,
+                               const uint8_t* hgmask, int T, int H, int S, int ncols, int64_t q_pos_offset,
+                               float scale, uint16_t* out, float* lse, const int32_t* ginfo, const float* kscale,
+                               int scale_per_row) {
+  if (d_qk == 512) {
+    if (kscale)
+      launch_rows128<512, kPerToken, true>(blocks, stream, q, kv, keys, keys_ld, union_len, hgmask, T, H, S, ncols,
+                                           q_pos_offset, scale, out, lse, ginfo, kscale, scale_per_row);
+    else
+      launch_rows128<512, kPerToken, false>(blocks, stream, q, kv, keys, keys_ld, union_len, hgmask, T, H, S,
+                                            ncols, q_pos_offset, scale, out, lse, ginfo, kscale, scale_per_row);
+  } else {
+    if (kscale)
+      launch_rows128<576, kPerToken, true>(blocks, stream, q, kv, keys, keys_ld, union_len, hgmask, T, H, S, ncols,
+                                           q_pos_offset, scale, out, lse, ginfo, kscale, scale_per_row);
+    else
+      launch_rows128<576, kPerToken, false>(blocks, stream, q, kv, keys, keys_ld, union_len, hgmask, T, H, S,
+                                            ncols, q_pos_offset, scale, out, lse, ginfo, kscale, scale_per_row);
+  }
+}
+
 hipError_t launch_grouped_attn(const uint16_t* q, const uint16_t* kv, const int32_t* union_idx,
                                const int32_t* union_len, const uint8_t* head_group_mask, int T,
                                int H, int S, int union_pad, float scale, uint16_t* out, float* lse,
-                               hipStream_t stream, const int32_t* group_info, int max_groups, int d_qk) {
+                               hipStream_t stream, const int32_t* group_info, int max_groups, int d_qk,
+                               const float* kscale, int scale_per_row) {
   const int G = 128 / H;
   const int NG = group_info ? max_groups : (T + G - 1) / G;
   if (NG == 0) return hipSuccess;
-  if (d_qk == 512)
-    hipLaunchKernelGGL((rows128_attn_kernel<512, false>), dim3(NG), dim3(kRThreads), 0, stream, q, kv,
-                       union_idx, (int64_t)union_pad, union_len, head_group_mask, T, H, S, union_pad,
-                       (int64_t)0, scale * kLog2e, out, lse, group_info);
-  else
-    hipLaunchKernelGGL((rows128_attn_kernel<576, false>), dim3(NG), dim3(kRThreads), 0, stream, q, kv,
-                       union_idx, (int64_t)union_pad, union_len, head_group_mask, T, H, S, union_pad,
-                       (int64_t)0, scale * kLog2e, out, lse, group_info);
+  launch_rows128_any<false>(d_qk, NG, stream, q, kv, union_idx, (int64_t)union_pad, union_len, head_group_mask,
+                            T, H, S, union_pad, 0, scale, out, lse, group_info, kscale, scale_per_row);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_rows128_exact(q, kv, union_idx, (int64_t)union_pad, union_len, head_group_mask, T, H,
-                              S, union_pad, 0, scale, out, lse, stream, group_info, NG, d_qk);
+                              S, union_pad, 0, scale, out, lse, stream, group_info, NG, d_qk, kscale,
+                              scale_per_row);
 }
 
 hipError_t launch_pertoken_rows128(const uint16_t* q, const uint16_t* kv, const int32_t* topk,
                                    int64_t ld, int T, int S, int cols, int64_t q_pos_offset,
-                                   float scale, uint16_t* out, float* lse, hipStream_t stream, int d_qk) {
+                                   float scale, uint16_t* out, float* lse, hipStream_t stream, int d_qk,
+                                   const float* kscale, int scale_per_row) {
   if (T == 0) return hipSuccess;
-  if (d_qk == 512)
-    hipLaunchKernelGGL((rows128_attn_kernel<512, true>), dim3(T), dim3(kRThreads), 0, stream, q, kv, topk,
-                       ld, (const int32_t*)nullptr, (const uint8_t*)nullptr, T, 128, S, cols,
-                       q_pos_offset, scale * kLog2e, out, lse, (const int32_t*)nullptr);
-  else
-    hipLaunchKernelGGL((rows128_attn_kernel<576, true>), dim3(T), dim3(kRThreads), 0, stream, q, kv, topk,
-                       ld, (const int32_t*)nullptr, (const uint8_t*)nullptr, T, 128, S, cols,
-                       q_pos_offset, scale * kLog2e, out, lse, (const int32_t*)nullptr);
+  launch_rows128_any<true>(d_qk, T, stream, q, kv, topk, ld, nullptr, nullptr, T, 128, S, cols, q_pos_offset,
+                           scale, out, lse, nullptr, kscale, scale_per_row);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_rows128_exact(q, kv, topk, ld, nullptr, nullptr, T, 128, S, cols, q_pos_offset, scale,
-                              out, lse, stream, nullptr, T, d_qk);
+                              out, lse, stream, nullptr, T, d_qk, kscale, scale_per_row);
 }
 
 }  // namespace dsa

@@ -31,10 +31,16 @@ hipError_t launch_scatter_topk_bits(const int32_t* topk, int64_t ld, int T, int 
                                     int64_t q_pos_offset, uint32_t* bits, int words,
                                     hipStream_t stream);
 
+// Row scales of the latent (every MQA launcher): kscale == nullptr for a plain bf16 latent;
+// otherwise row x's elements are its bf16 values times kscale[scale_per_row ? x : 0] (an FP8
+// latent decoded exactly to bf16): the kernels scale each key's raw score and each
+// probability before the PV product by it.
+
 // per-token sparse MQA for H % 16 == 0 (one workgroup per (token, 16-head block))
 hipError_t launch_pertoken_attn(const uint16_t* q, const uint16_t* kv, const int32_t* topk,
                                 int64_t ld, int T, int H, int S, int cols, int64_t q_pos_offset,
-                                float scale, uint16_t* out, float* lse, hipStream_t stream, int d_qk);
+                                float scale, uint16_t* out, float* lse, hipStream_t stream, int d_qk,
+                                const float* kscale = nullptr, int scale_per_row = 0);
 
 // 128-row attention over a per-workgroup key list.  Grouped mode: rows are the
 // 128 pseudo-heads of a group, keys the group's union list, and each row is
@@ -44,10 +50,12 @@ hipError_t launch_pertoken_attn(const uint16_t* q, const uint16_t* kv, const int
 hipError_t launch_grouped_attn(const uint16_t* q, const uint16_t* kv, const int32_t* union_idx,
                                const int32_t* union_len, const uint8_t* head_group_mask, int T,
                                int H, int S, int union_pad, float scale, uint16_t* out, float* lse,
-                               hipStream_t stream, const int32_t* group_info, int max_groups, int d_qk);
+                               hipStream_t stream, const int32_t* group_info, int max_groups, int d_qk,
+                               const float* kscale = nullptr, int scale_per_row = 0);
 hipError_t launch_pertoken_rows128(const uint16_t* q, const uint16_t* kv, const int32_t* topk,
                                    int64_t ld, int T, int S, int cols, int64_t q_pos_offset,
-                                   float scale, uint16_t* out, float* lse, hipStream_t stream, int d_qk);
+                                   float scale, uint16_t* out, float* lse, hipStream_t stream, int d_qk,
+                                   const float* kscale = nullptr, int scale_per_row = 0);
 
 // The fast 128-row kernel fixes each row's softmax reference at the row's first valid
 // scores.  A group in which a later score exceeds that reference by more than 2^64 gets
@@ -59,18 +67,18 @@ hipError_t launch_rows128_exact(const uint16_t* q, const uint16_t* kv, const int
                                 int64_t keys_ld, const int32_t* union_len, const uint8_t* hgmask,
                                 int T, int H, int S, int ncols, int64_t q_pos_offset, float scale,
                                 uint16_t* out, float* lse, hipStream_t stream, const int32_t* group_info,
-                                int ngroups, int d_qk);
+                                int ngroups, int d_qk, const float* kscale, int scale_per_row);
 
-// FP8 (OCP E4M3) latent -> bf16 rows: e4m3 * scale[per_row ? row : 0] (float32 product,
-// nearest even); rows x d codes, d a multiple of 16
-hipError_t launch_dequant_fp8(const uint8_t* kv8, const float* scale, int per_row, int64_t rows, int d,
-                              uint16_t* out, hipStream_t stream);
-// a batch over a paged FP8 cache: each request's reachable pages into a compact bf16 workspace
-// of ws_pages pages, and the block table over it (-1 where nothing maps)
-hipError_t launch_dequant_paged_fp8(const uint8_t* cache8, const float* scale, int per_row, int num_slots,
-                                    int d, int R, const int32_t* kv_lens, const int32_t* block_table,
-                                    int64_t bt_ld, int page_size, int ws_pages, uint16_t* out_cache,
-                                    int32_t* out_bt, hipStream_t stream);
+// FP8 (OCP E4M3) codes -> the bf16 numbers they encode (exact; no scale applied); rows x d
+// codes, d a multiple of 16
+hipError_t launch_decode_fp8(const uint8_t* kv8, int64_t rows, int d, uint16_t* out, hipStream_t stream);
+// a batch over a paged FP8 cache: each request's reachable pages decoded into a compact bf16
+// workspace of ws_pages pages, each workspace row's scale, and the block table over it (-1
+// where nothing maps)
+hipError_t launch_decode_paged_fp8(const uint8_t* cache8, const float* scale, int per_row, int num_slots, int d,
+                                   int R, const int32_t* kv_lens, const int32_t* block_table, int64_t bt_ld,
+                                   int page_size, int ws_pages, uint16_t* out_cache, float* out_scale,
+                                   int32_t* out_bt, hipStream_t stream);
 
 // masked dense MHA, key = k_nope (dn) + shared k_pe (dr), value dv: (256, 0, 256),
 // (192, 64, 256) or (128, 64, 128); mask = causal AND top-k bit; bits == nullptr: causal

@@ -26,7 +26,10 @@
 //    has been written to an LDS tile of 16 rows; the queries sit in a lane-private
 //    LDS area;
 //  * both: invalid entries (-1, past the row, beyond the token's position)
-//    fetch the token's own row and are masked.  The tiles are XOR-swizzled,
+//    fetch the token's first valid row and are masked (P = 0); a row the
+//    token selects holds real data, where an unselected one (an unused slot
+//    of a paged cache) may hold anything, and 0 times a NaN would be NaN.  A
+//    token with no valid entry writes zeros and -inf at once.  The tiles are XOR-swizzled,
 //    free of bank conflicts for the writes, the 16-byte K reads and the
 //    transposed V reads.  S^T = K Q^T runs on v_mfma_f32_16x16x32_bf16 (one
 //    accumulation chain in the sorted walk, three in the ring kernel, whose
@@ -43,6 +46,12 @@
 //    Probabilities may exceed 1 by up to 2^64 (safe for bf16 P and fp32 O and
 //    l); a token with a score beyond that is recomputed by an exact two-pass
 //    routine (max first), which is not met with ordinary inputs;
+//  * an FP8 latent (decoded exactly to bf16) carries a float32 scale per row:
+//    each raw score is multiplied by its row's scale before the softmax and
+//    each probability by it before the PV product (l sums the unscaled
+//    probabilities).  The LDS is fully used by the tiles and the sorted list,
+//    so the scales of a step's 16 rows come by scalar loads (their row indices
+//    read out of the lanes), issued a step ahead of their use;
 //  * token order is reversed (long causal rows first) and block ids are
 //    remapped so each XCD runs a contiguous token range: neighbouring tokens,
 //    which share most of their rows, then hit the same L2.
@@ -97,17 +106,54 @@ __device__ __forceinline__ int pt_list_entry(int i, int wstart) {
 
 __device__ __forceinline__ int tswz(int r) { return (2 * (r >> 1) + (r >> 3)) & 7; }
 
+// Row scales of a step's 16 keys.  Lane l holds the row indices of keys l / 8 (rows.x) and
+// 8 + l / 8 (rows.y); the scales come by uniform scalar loads (no LDS, no vector-memory
+// count), and each lane then keeps those of its keys 4 g .. 4 g + 3.
+struct StepScales {
+  float v[16];
+};
+__device__ __forceinline__ StepScales step_scales_load(const float* kscale, int per_row, int2 rows) {
+  StepScales st;
+  const_i32* sp = uniform_const(reinterpret_cast<const int32_t*>(kscale));
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int x0 = __builtin_amdgcn_readlane(rows.x, 8 * r);
+    const int x1 = __builtin_amdgcn_readlane(rows.y, 8 * r);
+    st.v[r] = __int_as_float(sp[per_row ? x0 : 0]);
+    st.v[8 + r] = __int_as_float(sp[per_row ? x1 : 0]);
+  }
+  return st;
+}
+__device__ __forceinline__ f32x4 step_scales_mine(const StepScales& st, int g) {
+  f32x4 r;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj)
+    r[jj] = g == 0 ? st.v[jj] : g == 1 ? st.v[4 + jj] : g == 2 ? st.v[8 + jj] : st.v[12 + jj];
+  return r;
+}
+
 // What one wave needs to walk its token's row.
 struct PtCtx {
   const int32_t* trow;  // the token's top-k row
   const uint8_t* kvb;   // latent base + 16 (lane % 8): this lane's 16 bytes of each line
   int cols, pos, lane, g, n;
+  int dummy;            // the row invalid entries fetch: the token's first valid entry
   int er;               // the rows this lane loads: er and 8 + er of each step
   float sc;             // |scale| * log2(e)
   int wofs[2];          // tile store offsets (rows er, 8 + er; + 128 per line)
   int kofs[2];          // K read offsets (row n, chunk 4 s + g: per s % 2; + 128 (s / 2))
   int rofs[4];          // transposed V read offsets (per column block cb % 4; + 128 (cb / 4))
 };
+
+// The first entry x of a top-k row with 0 <= x <= pos (pos <= S - 1), or -1 (uniform).
+__device__ __forceinline__ int pt_first_valid(const int32_t* trow, int cols, int pos, int lane) {
+  for (int c0 = 0; c0 < cols; c0 += 64) {
+    const int x = c0 + lane < cols ? trow[c0 + lane] : -1;
+    const uint64_t b = ballot(x >= 0 && x <= pos);
+    if (b != 0) return uniform(__builtin_amdgcn_readlane(x, __builtin_ctzll(b)));
+  }
+  return -1;
+}
 
 // The per-wave context for token `token` (built in registers; the exact routine rebuilds
 // it from the same scalars rather than taking it by reference, which would put it in
@@ -161,11 +207,13 @@ __device__ __forceinline__ int2 pt_entries(const PtCtx& c, int j, int wstart = 0
 // start the loads of step j's rows into `buf` (buf[k]: line k of row er, buf[9 + k]: of row
 // 8 + er); returns the validity bits of the step's 16 keys (key r <-> bit r)
 template <int D>
-__device__ __forceinline__ uint32_t pt_issue(const PtCtx& c, int2 e, int j, u32x4 (&buf)[Lat<D>::loads]) {
+__device__ __forceinline__ uint32_t pt_issue(const PtCtx& c, int2 e, int j, u32x4 (&buf)[Lat<D>::loads],
+                                             int2& rows) {
   const bool ok0 = kPKeys * j + c.er < c.cols && e.x >= 0 && e.x <= c.pos;
   const bool ok1 = kPKeys * j + 8 + c.er < c.cols && e.y >= 0 && e.y <= c.pos;
-  const uint8_t* src0 = c.kvb + (size_t)(ok0 ? e.x : c.pos) * Lat<D>::row_bytes;
-  const uint8_t* src1 = c.kvb + (size_t)(ok1 ? e.y : c.pos) * Lat<D>::row_bytes;
+  rows = int2{ok0 ? e.x : c.dummy, ok1 ? e.y : c.dummy};  // (the rows the loads fetch)
+  const uint8_t* src0 = c.kvb + (size_t)rows.x * Lat<D>::row_bytes;
+  const uint8_t* src1 = c.kvb + (size_t)rows.y * Lat<D>::row_bytes;
 #pragma unroll
   for (int k = 0; k < Lat<D>::lines; ++k) {
     buf[k] = *reinterpret_cast<const u32x4*>(src0 + 128 * k);
@@ -221,29 +269,35 @@ __device__ __forceinline__ f32x4 pt_qk(const PtCtx& c) {
   return acc[0] + acc[1] + acc[2];
 }
 
-// invalid keys -> -inf; returns the max of this lane's 4 scores
-__device__ __forceinline__ float pt_mask(const PtCtx& c, const f32x4& sacc, uint32_t vbits, float (&sv)[4]) {
+// invalid keys -> -inf (kScaled: valid scores times their row scales ks); returns the max of
+// this lane's 4 scores
+template <bool kScaled>
+__device__ __forceinline__ float pt_mask(const PtCtx& c, const f32x4& sacc, uint32_t vbits, float (&sv)[4],
+                                         f32x4 ks) {
   const uint32_t mine = vbits >> (4 * c.g);
   float mt = kNegInf;
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)mine, jj, 1);  // all ones if valid
-    const float raw = sacc[jj];  // (a scalar copy: bit casts of vector elements misread)
+    // (a scalar copy: bit casts of vector elements misread)
+    const float raw = kScaled ? sacc[jj] * ks[jj] : sacc[jj];
     sv[jj] = __builtin_bit_cast(float, (sel & __builtin_bit_cast(uint32_t, raw)) | (~sel & 0xff800000u));
     mt = fmaxf(mt, sv[jj]);
   }
   return mt;
 }
 
-// P = 2^(s sc - m) (bf16, as the B operand P^T[key 4 g + jj][head n]); adds to l
-__device__ __forceinline__ s16x4_t pt_probs(const PtCtx& c, const float (&sv)[4], float m, float& l) {
+// P = 2^(s sc - m) (bf16, as the B operand P^T[key 4 g + jj][head n]; kScaled: times the
+// key's row scale); adds the unscaled P to l
+template <bool kScaled>
+__device__ __forceinline__ s16x4_t pt_probs(const PtCtx& c, const float (&sv)[4], float m, float& l, f32x4 ks) {
   const float nm = m == kNegInf ? 0.f : -m;
   bf16x4 pb;
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const float p = fast_exp2(__builtin_fmaf(sv[jj], c.sc, nm));
     l += p;
-    pb[jj] = (__bf16)p;
+    pb[jj] = (__bf16)(kScaled ? p * ks[jj] : p);
   }
   return __builtin_bit_cast(s16x4_t, pb);
 }
@@ -281,19 +335,23 @@ __device__ __forceinline__ void pt_write(int g, const f32x4 (&o)[kDv / 16], floa
 // Exact two-pass routine: head n's max over the whole row first, then the softmax
 // against it (no probability exceeds 1).  Both passes share pt_qk / pt_mask with the main
 // loop, so their scores are bit-identical.
-template <int D, bool kSorted>
+template <int D, bool kSorted, bool kScaled>
 __device__ __noinline__ void pt_exact(const uint16_t* kv, const int32_t* topk, int64_t ld, int S, int cols,
                                      int64_t q_pos_offset, float scale_log2, int token, uint16_t* orow,
-                                     float* lse_at, int wstart) {
-  const PtCtx c = pt_context<D>(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token);
+                                     float* lse_at, int wstart, const float* kscale, int per_row, int dummy) {
+  PtCtx c = pt_context<D>(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token);
+  c.dummy = dummy;
   const int nsteps = (c.cols + kPKeys - 1) / kPKeys;
   float m = kNegInf;
   for (int j = 0; j < nsteps; ++j) {
     u32x4 buf[Lat<D>::loads];
-    const uint32_t vbits = pt_issue<D>(c, pt_entries<kSorted>(c, j, wstart), j, buf);
+    int2 rows;
+    const uint32_t vbits = pt_issue<D>(c, pt_entries<kSorted>(c, j, wstart), j, buf, rows);
+    f32x4 ks = {1.f, 1.f, 1.f, 1.f};
+    if (kScaled) ks = step_scales_mine(step_scales_load(kscale, per_row, rows), c.g);
     pt_store<D>(c, buf);
     float sv[4];
-    m = fmaxf(m, pt_mask(c, pt_qk<D>(c), vbits, sv));
+    m = fmaxf(m, pt_mask<kScaled>(c, pt_qk<D>(c), vbits, sv, ks));
   }
   m = max_over_rowgroups(m) * c.sc;
   float l = 0.f;
@@ -302,11 +360,14 @@ __device__ __noinline__ void pt_exact(const uint16_t* kv, const int32_t* topk, i
   for (int cb = 0; cb < kDv / 16; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < nsteps; ++j) {
     u32x4 buf[Lat<D>::loads];
-    const uint32_t vbits = pt_issue<D>(c, pt_entries<kSorted>(c, j, wstart), j, buf);
+    int2 rows;
+    const uint32_t vbits = pt_issue<D>(c, pt_entries<kSorted>(c, j, wstart), j, buf, rows);
+    f32x4 ks = {1.f, 1.f, 1.f, 1.f};
+    if (kScaled) ks = step_scales_mine(step_scales_load(kscale, per_row, rows), c.g);
     pt_store<D>(c, buf);
     float sv[4];
-    pt_mask(c, pt_qk<D>(c), vbits, sv);
-    pt_pv(c, pt_probs(c, sv, m, l), o);
+    pt_mask<kScaled>(c, pt_qk<D>(c), vbits, sv, ks);
+    pt_pv(c, pt_probs<kScaled>(c, sv, m, l, ks), o);
   }
   pt_write(c.g, o, l, m, orow, lse_at);
 }
@@ -315,12 +376,14 @@ __device__ __noinline__ void pt_exact(const uint16_t* kv, const int32_t* topk, i
 // and the sorted kernel's path for a token with more valid entries than its list holds.
 // (Scalars only in the signature: a struct passed to a non-inlined function would live in
 // scratch memory.)
-template <int D>
+template <int D, bool kScaled>
 __device__ __noinline__ void pt_ring_token(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                                            const int32_t* __restrict__ topk, int64_t ld, int H, int S, int cols,
                                            int64_t q_pos_offset, float scale_log2, uint16_t* __restrict__ out,
-                                           float* __restrict__ lse, int token, int hb) {
-  const PtCtx c = pt_context<D>(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token);
+                                           float* __restrict__ lse, int token, int hb, const float* kscale,
+                                           int per_row) {
+  PtCtx c = pt_context<D>(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token);
+  c.dummy = pt_first_valid(c.trow, c.cols, c.pos, c.lane);
 
   // queries of head n, dims 32 s + 8 g .. + 8 (the B operand of S^T = K Q^T); a negative
   // scale is applied as |scale| on negated queries so the max can be taken on raw scores
@@ -336,7 +399,7 @@ __device__ __noinline__ void pt_ring_token(const uint16_t* __restrict__ q, const
   }
   uint16_t* orow = out + ((size_t)token * H + hb * 16 + c.n) * kDv + 4 * c.g;
   float* lse_at = lse + (size_t)token * H + hb * 16 + c.n;
-  if (c.cols == 0) {  // nothing selected: zero output, LSE -inf
+  if (c.dummy < 0) {  // nothing selected: zero output, LSE -inf
     const f32x4 z[kDv / 16] = {};
     pt_write(c.g, z, 0.f, kNegInf, orow, lse_at);
     return;
@@ -357,25 +420,33 @@ __device__ __noinline__ void pt_ring_token(const uint16_t* __restrict__ q, const
   for (int cb = 0; cb < kDv / 16; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   u32x4 ra[Lat<D>::loads], rb[Lat<D>::loads];
   uint32_t va = 0, vb = 0;
+  f32x4 sa = {1.f, 1.f, 1.f, 1.f}, sb = sa;  // kScaled: this lane's row scales of the buffered steps
   int2 e_next = {0, 0};  // entries of the step whose loads start next
   {  // issue order as in the loop (entries, rows, entries, rows), pinned by scheduling
      // barriers: the wait counts at the loop head merge this order with the loop's
     const int2 e0 = pt_entries<false>(c, 0);
     const int2 e1 = pt_entries<false>(c, 1);
+    int2 rows0, rows1;
     __builtin_amdgcn_sched_barrier(0);
-    va = pt_issue<D>(c, e0, 0, ra);
+    va = pt_issue<D>(c, e0, 0, ra, rows0);
     __builtin_amdgcn_sched_barrier(0);
     e_next = pt_entries<false>(c, 2);
     __builtin_amdgcn_sched_barrier(0);
-    vb = pt_issue<D>(c, e1, 1, rb);
+    vb = pt_issue<D>(c, e1, 1, rb, rows1);
     __builtin_amdgcn_sched_barrier(0);
+    if (kScaled) {
+      sa = step_scales_mine(step_scales_load(kscale, per_row, rows0), c.g);
+      sb = step_scales_mine(step_scales_load(kscale, per_row, rows1), c.g);
+    }
   }
   // one step; `over` becomes true when a score exceeds the reference by more than the
   // slack (the loop still runs to its end, and its result is then discarded)
   bool over = false;
-  auto step = [&](int j, u32x4 (&buf)[Lat<D>::loads], uint32_t& vbuf) {
+  auto step = [&](int j, u32x4 (&buf)[Lat<D>::loads], uint32_t& vbuf, f32x4& sbuf) {
     pt_store<D>(c, buf);
     const uint32_t vbits = vbuf;
+    const f32x4 ks = sbuf;
+    int2 rows;
     // the refill must not be scheduled above the stores that read the buffer
     __builtin_amdgcn_sched_barrier(0);
     {  // (unconditional: past the row the loads are masked dummies, and the wait
@@ -383,39 +454,47 @@ __device__ __noinline__ void pt_ring_token(const uint16_t* __restrict__ q, const
       const int2 e = e_next;
       e_next = pt_entries<false>(c, j + 3);
       __builtin_amdgcn_sched_barrier(0);
-      vbuf = pt_issue<D>(c, e, j + 2, buf);
+      vbuf = pt_issue<D>(c, e, j + 2, buf, rows);
     }
     __builtin_amdgcn_sched_barrier(0);
+    const f32x4 sacc = pt_qk<D>(c);
+    // kScaled: step j + 2's scales, loaded under this step's softmax and selected after its PV
+    StepScales st;
+    if (kScaled) st = step_scales_load(kscale, per_row, rows);
     float sv[4];
-    const float mt = pt_mask(c, pt_qk<D>(c), vbits, sv) * c.sc;
+    const float mt = pt_mask<kScaled>(c, sacc, vbits, sv, ks) * c.sc;
     // a head's first valid scores set its reference (its O and l are still zero)
     if (ballot(m_ref == kNegInf && mt != kNegInf) != 0) {
       const float mh = max_over_rowgroups(mt);
       m_ref = m_ref == kNegInf ? mh : m_ref;
     }
     over |= ballot(mt > m_ref + kPSlack) != 0;
-    pt_pv(c, pt_probs(c, sv, m_ref, l_run), o);
+    pt_pv(c, pt_probs<kScaled>(c, sv, m_ref, l_run, ks), o);
+    if (kScaled) sbuf = step_scales_mine(st, c.g);
   };
   for (int j = 0; j < nsteps2; j += 2) {
-    step(j, ra, va);
-    step(j + 1, rb, vb);
+    step(j, ra, va, sa);
+    step(j + 1, rb, vb, sb);
   }
   if (over) {
-    pt_exact<D, false>(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token, orow, lse_at, 0);
+    pt_exact<D, false, kScaled>(kv, topk, ld, S, cols, q_pos_offset, scale_log2, token, orow, lse_at, 0, kscale,
+                                per_row, c.dummy);
     return;
   }
   pt_write(c.g, o, l_run, m_ref, orow, lse_at);
 }
 
-template <int D>
+template <int D, bool kScaled>
 __global__ __launch_bounds__(64) void pertoken_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ topk, int64_t ld, int T, int H, int S, int cols,
-    int64_t q_pos_offset, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    int64_t q_pos_offset, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
+    const float* __restrict__ kscale, int per_row) {
   const int nb = H >> 4;
   const int item = xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
   const int tq = item / nb;
-  pt_ring_token<D>(q, kv, topk, ld, H, S, cols, q_pos_offset, scale_log2, out, lse, T - 1 - tq, item - tq * nb);
+  pt_ring_token<D, kScaled>(q, kv, topk, ld, H, S, cols, q_pos_offset, scale_log2, out, lse, T - 1 - tq,
+                            item - tq * nb, kscale, per_row);
 }
 
 // ---------------------------------------------------------------------------
@@ -496,6 +575,7 @@ __device__ __forceinline__ int pt_sort(const int32_t* trow, int cols, int pos, i
 
 struct PdCtx {
   int cols, pos, lane, g, n, er;
+  int dummy;    // the row copies past the list fetch: the list's first entry
   int wstart;   // lane w: list index of window w's first entry (windows of 65536 positions)
   bool multi;   // the list spans more than one window
   float sc;
@@ -508,6 +588,7 @@ template <int D>
 __device__ __forceinline__ PdCtx pd_context(int pos, int cols, float scale_log2, int wstart) {
   PdCtx c;
   c.wstart = wstart;
+  c.dummy = uniform(pt_list_entry(0, wstart));
   c.multi = pos >= 65536;
   c.lane = threadIdx.x;
   c.g = c.lane >> 4;
@@ -549,8 +630,8 @@ template <int D>
 __device__ __forceinline__ uint32_t pd_issue(const PdCtx& c, const uint8_t* kvb, int2 e, int j, uint32_t tile) {
   const bool ok0 = kPKeys * j + c.er < c.cols;
   const bool ok1 = kPKeys * j + 8 + c.er < c.cols;
-  const uint32_t off0 = (uint32_t)(ok0 ? e.x : c.pos) * Lat<D>::row_bytes + c.dofs[0];
-  const uint32_t off1 = (uint32_t)(ok1 ? e.y : c.pos) * Lat<D>::row_bytes + c.dofs[1];
+  const uint32_t off0 = (uint32_t)(ok0 ? e.x : c.dummy) * Lat<D>::row_bytes + c.dofs[0];
+  const uint32_t off1 = (uint32_t)(ok1 ? e.y : c.dummy) * Lat<D>::row_bytes + c.dofs[1];
 #pragma unroll
   for (int k = 0; k < Lat<D>::lines; ++k) {
     dma16_sbase(off0, kvb + 128 * k, tile + 1024 * k);
@@ -565,6 +646,7 @@ struct PdSrc {
   uint32_t off0;        // byte offset of this lane's 16 bytes of row er's first line
   uint32_t off1;        // ... of row 8 + er
   uint32_t vbits;
+  int2 rows;            // the rows copied for keys er and 8 + er
 };
 template <int D>
 __device__ __forceinline__ PdSrc pd_prep(const PdCtx& c, const uint8_t* kvb, int2 e, int j) {
@@ -572,8 +654,9 @@ __device__ __forceinline__ PdSrc pd_prep(const PdCtx& c, const uint8_t* kvb, int
   const bool ok1 = kPKeys * j + 8 + c.er < c.cols;
   PdSrc p;
   p.base = kvb;
-  p.off0 = (uint32_t)(ok0 ? e.x : c.pos) * Lat<D>::row_bytes + c.dofs[0];
-  p.off1 = (uint32_t)(ok1 ? e.y : c.pos) * Lat<D>::row_bytes + c.dofs[1];
+  p.rows = int2{ok0 ? e.x : c.dummy, ok1 ? e.y : c.dummy};
+  p.off0 = (uint32_t)p.rows.x * Lat<D>::row_bytes + c.dofs[0];
+  p.off1 = (uint32_t)p.rows.y * Lat<D>::row_bytes + c.dofs[1];
   p.vbits = pd_valid(c, j);
   return p;
 }
@@ -657,37 +740,42 @@ __device__ __forceinline__ void pd_pv(const PdCtx& c, const uint8_t* tile, s16x4
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// invalid keys -> -inf; returns the max of this lane's 4 scores
-__device__ __forceinline__ float pd_mask(int g, const f32x4& sacc, uint32_t vbits, float (&sv)[4]) {
+// invalid keys -> -inf (kScaled: valid scores times their row scales ks); returns the max of
+// this lane's 4 scores
+template <bool kScaled>
+__device__ __forceinline__ float pd_mask(int g, const f32x4& sacc, uint32_t vbits, float (&sv)[4], f32x4 ks) {
   const uint32_t mine = vbits >> (4 * g);
   float mt = kNegInf;
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)mine, jj, 1);  // all ones if valid
-    const float raw = sacc[jj];  // (a scalar copy: bit casts of vector elements misread)
+    // (a scalar copy: bit casts of vector elements misread)
+    const float raw = kScaled ? sacc[jj] * ks[jj] : sacc[jj];
     sv[jj] = __builtin_bit_cast(float, (sel & __builtin_bit_cast(uint32_t, raw)) | (~sel & 0xff800000u));
     mt = fmaxf(mt, sv[jj]);
   }
   return mt;
 }
 
-__device__ __forceinline__ s16x4_t pd_probs(float sc, const float (&sv)[4], float m, float& l) {
+template <bool kScaled>
+__device__ __forceinline__ s16x4_t pd_probs(float sc, const float (&sv)[4], float m, float& l, f32x4 ks) {
   const float nm = m == kNegInf ? 0.f : -m;
   bf16x4 pb;
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const float p = fast_exp2(__builtin_fmaf(sv[jj], sc, nm));
     l += p;
-    pb[jj] = (__bf16)p;
+    pb[jj] = (__bf16)(kScaled ? p * ks[jj] : p);
   }
   return __builtin_bit_cast(s16x4_t, pb);
 }
 
-template <int D>
+template <int D, bool kScaled>
 __global__ __launch_bounds__(64) void pertoken_sorted_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ topk, int64_t ld, int T, int H, int S, int cols,
-    int64_t q_pos_offset, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    int64_t q_pos_offset, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
+    const float* __restrict__ kscale, int per_row) {
   const int nb = H >> 4;
   const int item = xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
   const int tq = item / nb;
@@ -723,7 +811,8 @@ __global__ __launch_bounds__(64) void pertoken_sorted_kernel(
     return;
   }
   if (nsel > kPSortMax) {  // more valid entries than the list holds: the register-ring walk
-    pt_ring_token<D>(q, kv, topk, ld, H, S, cols, q_pos_offset, scale_log2, out, lse, token, hb);
+    pt_ring_token<D, kScaled>(q, kv, topk, ld, H, S, cols, q_pos_offset, scale_log2, out, lse, token, hb, kscale,
+                              per_row);
     return;
   }
   const PdCtx c = pd_context<D>(pos, nsel, scale_log2, wstart);
@@ -742,29 +831,41 @@ __global__ __launch_bounds__(64) void pertoken_sorted_kernel(
   f32x4 o[kDv / 16];
 #pragma unroll
   for (int cb = 0; cb < kDv / 16; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 sa = {1.f, 1.f, 1.f, 1.f}, sb = sa;  // kScaled: this lane's row scales of the tiles' steps
+  const PdSrc s0 = pd_prep<D>(c, kvb, pd_entries(c, 0), 0);
+  const PdSrc s1 = pd_prep<D>(c, kvb, pd_entries(c, 1), 1);
   uint32_t va = pd_issue<D>(c, kvb, pd_entries(c, 0), 0, lds_addr(tile0));
   uint32_t vb = pd_issue<D>(c, kvb, pd_entries(c, 1), 1, lds_addr(tile1));
+  if (kScaled) {
+    sa = step_scales_mine(step_scales_load(kscale, per_row, s0.rows), g);
+    sb = step_scales_mine(step_scales_load(kscale, per_row, s1.rows), g);
+  }
   int2 e_next = pd_entries(c, 2);
   bool over = false;
-  auto step = [&](int j, const uint8_t* tile, uint32_t& vbuf) {
+  auto step = [&](int j, const uint8_t* tile, uint32_t& vbuf, f32x4& sbuf) {
     wait_vmcnt<2 * Lat<D>::lines>();  // step j's copies have landed (step j + 1's may be in flight)
+    const f32x4 sacc = pd_qk<D>(c, tile, qreg);
+    // the tile takes step j + 2's rows during its PV; kScaled: their scales are loaded under
+    // this step's softmax and selected after its PV
+    const PdSrc next = pd_prep<D>(c, kvb, e_next, j + 2);
+    StepScales st;
+    if (kScaled) st = step_scales_load(kscale, per_row, next.rows);
     float sv[4];
-    const float mt = pd_mask(g, pd_qk<D>(c, tile, qreg), vbuf, sv) * c.sc;
+    const float mt = pd_mask<kScaled>(g, sacc, vbuf, sv, sbuf) * c.sc;
     // a head's first valid scores set its reference (its O and l are still zero)
     if (ballot(m_ref == kNegInf && mt != kNegInf) != 0) {
       const float mh = max_over_rowgroups(mt);
       m_ref = m_ref == kNegInf ? mh : m_ref;
     }
     over |= ballot(mt > m_ref + kPSlack) != 0;
-    // the tile takes step j + 2's rows during its PV
-    const PdSrc next = pd_prep<D>(c, kvb, e_next, j + 2);
     e_next = pd_entries(c, j + 3);
-    pd_pv<D>(c, tile, pd_probs(c.sc, sv, m_ref, l_run), o, next);
+    pd_pv<D>(c, tile, pd_probs<kScaled>(c.sc, sv, m_ref, l_run, sbuf), o, next);
     vbuf = next.vbits;
+    if (kScaled) sbuf = step_scales_mine(st, g);
   };
   for (int j = 0; j < nsteps2; j += 2) {
-    step(j, tile0, va);
-    step(j + 1, tile1, vb);
+    step(j, tile0, va, sa);
+    step(j + 1, tile1, vb, sb);
   }
   wait_vmcnt<0>();  // the copies issued past the list
   if (over) {
@@ -772,33 +873,46 @@ __global__ __launch_bounds__(64) void pertoken_sorted_kernel(
 #pragma unroll
     for (int s = 0; s < Lat<D>::loads; ++s) pt_q[s][lane] = __builtin_bit_cast(uint4, qreg[s]);
     __syncthreads();
-    pt_exact<D, true>(kv, topk, ld, S, nsel, q_pos_offset, scale_log2, token, orow, lse_at, wstart);
+    pt_exact<D, true, kScaled>(kv, topk, ld, S, nsel, q_pos_offset, scale_log2, token, orow, lse_at, wstart,
+                               kscale, per_row, c.dummy);
     return;
   }
   pt_write(g, o, l_run, m_ref, orow, lse_at);
 }
 
-template <int D>
+template <int D, bool kScaled>
 static void launch_pertoken(const uint16_t* q, const uint16_t* kv, const int32_t* topk, int64_t ld, int T,
                             int H, int S, int cols, int64_t q_pos_offset, float scale, uint16_t* out,
-                            float* lse, hipStream_t stream) {
+                            float* lse, hipStream_t stream, const float* kscale, int per_row) {
   const long long items = (long long)T * (H / 16);
   if (S <= kPSortRows)
-    hipLaunchKernelGGL(pertoken_sorted_kernel<D>, dim3((unsigned)items), dim3(64), 0, stream, q, kv, topk, ld,
-                       T, H, S, cols, q_pos_offset, scale * kLog2e, out, lse);
+    hipLaunchKernelGGL((pertoken_sorted_kernel<D, kScaled>), dim3((unsigned)items), dim3(64), 0, stream, q, kv,
+                       topk, ld, T, H, S, cols, q_pos_offset, scale * kLog2e, out, lse, kscale, per_row);
   else
-    hipLaunchKernelGGL(pertoken_attn_kernel<D>, dim3((unsigned)items), dim3(64), 0, stream, q, kv, topk, ld,
-                       T, H, S, cols, q_pos_offset, scale * kLog2e, out, lse);
+    hipLaunchKernelGGL((pertoken_attn_kernel<D, kScaled>), dim3((unsigned)items), dim3(64), 0, stream, q, kv,
+                       topk, ld, T, H, S, cols, q_pos_offset, scale * kLog2e, out, lse, kscale, per_row);
 }
 
 hipError_t launch_pertoken_attn(const uint16_t* q, const uint16_t* kv, const int32_t* topk,
                                 int64_t ld, int T, int H, int S, int cols, int64_t q_pos_offset,
-                                float scale, uint16_t* out, float* lse, hipStream_t stream, int d_qk) {
+                                float scale, uint16_t* out, float* lse, hipStream_t stream, int d_qk,
+                                const float* kscale, int per_row) {
   if ((long long)T * (H / 16) == 0) return hipSuccess;
-  if (d_qk == 512)
-    launch_pertoken<512>(q, kv, topk, ld, T, H, S, cols, q_pos_offset, scale, out, lse, stream);
-  else
-    launch_pertoken<576>(q, kv, topk, ld, T, H, S, cols, q_pos_offset, scale, out, lse, stream);
+  if (d_qk == 512) {
+    if (kscale)
+      launch_pertoken<512, true>(q, kv, topk, ld, T, H, S, cols, q_pos_offset, scale, out, lse, stream, kscale,
+                                 per_row);
+    else
+      launch_pertoken<512, false>(q, kv, topk, ld, T, H, S, cols, q_pos_offset, scale, out, lse, stream, kscale,
+                                  per_row);
+  } else {
+    if (kscale)
+      launch_pertoken<576, true>(q, kv, topk, ld, T, H, S, cols, q_pos_offset, scale, out, lse, stream, kscale,
+                                 per_row);
+    else
+      launch_pertoken<576, false>(q, kv, topk, ld, T, H, S, cols, q_pos_offset, scale, out, lse, stream, kscale,
+                                  per_row);
+  }
   return hipGetLastError();
 }
 

@@ -20,7 +20,9 @@
 //    registers; the bf16 probabilities and per-row rescale factors go to LDS;
 //  * PV is split by value columns: wave w owns columns 64 w .. 64 w + 63 of all
 //    128 rows and computes O^T = V^T P^T with v_mfma_f32_32x32x16_bf16, V^T
-//    from ds_read_b64_tr_b16, P^T from 16-byte reads.
+//    from ds_read_b64_tr_b16, P^T from 16-byte reads;
+//  * rows with scales (an FP8 latent decoded exactly to bf16): each raw score
+//    and each probability is multiplied by its row's scale (scalar loads).
 #include "common.h"
 #include "kernels.h"
 
@@ -34,14 +36,15 @@ constexpr int kGStages = 3;
 constexpr int kGPStride = 40;                         // halves per probability row (32 + 8 pad)
 constexpr float kGSlack = 8.f;                        // lazy-rescale threshold (log2 units)
 
-// D: the latent width, 576 (512 + 64 rope dims) or 512 (no rope part)
-template <int D, bool kPerToken>
+// D: the latent width, 576 (512 + 64 rope dims) or 512 (no rope part); kScaled: rows carry
+// scales (kscale[scale_per_row ? x : 0] for row x)
+template <int D, bool kPerToken, bool kScaled>
 __global__ __launch_bounds__(kGThreads) void rows128_exact_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ keys, int64_t keys_ld, const int32_t* __restrict__ union_len,
     const uint8_t* __restrict__ hgmask, int T, int H, int S, int ncols, int64_t q_pos_offset,
     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
-    const int32_t* __restrict__ ginfo) {
+    const int32_t* __restrict__ ginfo, const float* __restrict__ kscale, int scale_per_row) {
   static_assert(D == 576 || D == 512, "latent widths");
   constexpr int kGRowBytes = D * 2 + 16;                          // D / 8 data chunks + 1 pad chunk
   constexpr int kGSlots = kGRowBytes / 16;                        // 73 / 65
@@ -98,13 +101,24 @@ __global__ __launch_bounds__(kGThreads) void rows128_exact_kernel(
   int64_t pos64 = q_pos_offset + t0;  // per-token mode: the token's position
   if (pos64 > S - 1) pos64 = S - 1;
   const int pos = uniform((int)pos64);
-  const int ntiles = (nkeys + kGKeys - 1) / kGKeys;
-
   // validity of slot j0 + r as a latent-row index (grouped: a union entry inside [0, S);
   // per-token: the selection rule) -- wave-uniform, scalar loads
   auto slot_ok = [&](int32_t x, int j) -> bool {
     return j < nkeys && x >= 0 && (kPerToken ? x <= pos : x < S);  // pos <= S - 1
   };
+  // the row invalid slots copy (their P is 0): the list's first valid entry (an unselected
+  // row may hold anything, and 0 times a NaN is NaN); none: nothing to attend over
+  int dummy_row = -1;
+  for (int c0 = 0; c0 < nkeys; c0 += 64) {
+    const int32_t xv = c0 + lane < nkeys ? klist[c0 + lane] : -1;
+    const uint64_t b = ballot(slot_ok(xv, c0 + lane));
+    if (b != 0) {
+      dummy_row = __builtin_amdgcn_readlane(xv, __builtin_ctzll(b));
+      break;
+    }
+  }
+  dummy_row = uniform(dummy_row);
+  const int ntiles = dummy_row < 0 ? 0 : (nkeys + kGKeys - 1) / kGKeys;
 
   // this wave's copies of a tile are 5 w .. 5 w + 4: slots 320 w .. 320 w + 319, i.e. at
   // most 6 consecutive slot rows starting at r_lo
@@ -122,7 +136,7 @@ __global__ __launch_bounds__(kGThreads) void rows128_exact_kernel(
       for (int e = 0; e < 6; ++e) x[e] = e < avail ? ip[e] : -1;
     }
 #pragma unroll
-    for (int e = 0; e < 6; ++e) x[e] = slot_ok(x[e], j0 + r_lo + e) ? x[e] : 0;
+    for (int e = 0; e < 6; ++e) x[e] = slot_ok(x[e], j0 + r_lo + e) ? x[e] : dummy_row;
     uint8_t* st = stage[t % kGStages];
 #pragma unroll
     for (int u = 0; u < kGDmaPerWave; ++u) {
@@ -149,8 +163,9 @@ __global__ __launch_bounds__(kGThreads) void rows128_exact_kernel(
     }
   };
 
-  // for the row this lane owns: bit 4 kb + jj <-> slot 16 kb + 4 g + jj of tile t is allowed
-  auto allowed_bits = [&](int t) -> uint32_t {
+  // for the row this lane owns: bit 4 kb + jj <-> slot 16 kb + 4 g + jj of tile t is allowed;
+  // kScaled: ksc[kb][jj] = that slot's row scale
+  auto allowed_bits = [&](int t, f32x4 (&ksc)[2]) -> uint32_t {
     const int j0 = t * kGKeys;
     uint32_t bits = 0;
 #pragma unroll
@@ -168,6 +183,14 @@ __global__ __launch_bounds__(kGThreads) void rows128_exact_kernel(
       uint32_t vbits = 0;  // validity of the 16 slots
 #pragma unroll
       for (int r = 0; r < 16; ++r) vbits |= slot_ok(e[r], jb + r) ? (1u << r) : 0u;
+      if (kScaled) {  // (uniform indices: scalar loads)
+        const_i32* sp = uniform_const(reinterpret_cast<const int32_t*>(kscale));
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = __int_as_float(sp[scale_per_row && ((vbits >> r) & 1u) ? e[r] : 0]);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) ksc[kb][jj] = g == 0 ? v[jj] : g == 1 ? v[4 + jj] : g == 2 ? v[8 + jj] : v[12 + jj];
+      }
       const uint32_t vb = (vbits >> (4 * g)) & 0xfu;
       if (kPerToken) {
         bits |= vb << (4 * kb);
@@ -209,7 +232,8 @@ __global__ __launch_bounds__(kGThreads) void rows128_exact_kernel(
       wait_vmcnt<0>();
     __syncthreads();  // tile t visible; every wave is done with tile t - 1 (stage and P)
     if (t + 2 < ntiles) issue(t + 2);
-    const uint32_t abits = allowed_bits(t);
+    f32x4 ksc[2] = {{1.f, 1.f, 1.f, 1.f}, {1.f, 1.f, 1.f, 1.f}};
+    const uint32_t abits = allowed_bits(t, ksc);
 
     const uint8_t* tile = stage[t % kGStages];
     // ---- scores of this wave's 16 rows over the 32 slots
@@ -228,7 +252,8 @@ __global__ __launch_bounds__(kGThreads) void rows128_exact_kernel(
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const bool ok = ((abits >> (4 * kb + jj)) & 1u) != 0u;
-        const float val = ok ? sacc[kb][jj] * scale_log2 : kNegInf;
+        const float raw = kScaled ? sacc[kb][jj] * ksc[kb][jj] : sacc[kb][jj];
+        const float val = ok ? raw * scale_log2 : kNegInf;
         sacc[kb][jj] = val;
         mt = fmaxf(mt, val);
       }
@@ -251,7 +276,7 @@ __global__ __launch_bounds__(kGThreads) void rows128_exact_kernel(
       for (int jj = 0; jj < 4; ++jj) {
         const float p = fast_exp2(sacc[kb][jj] - msafe);
         ls += p;
-        pw[jj] = (__bf16)p;
+        pw[jj] = (__bf16)(kScaled ? p * ksc[kb][jj] : p);
       }
       *reinterpret_cast<bf16x4*>(pbuf + r_own * kGPStride + 16 * kb + 4 * g) = pw;
     }
@@ -315,32 +340,52 @@ __global__ __launch_bounds__(kGThreads) void rows128_exact_kernel(
   }
 }
 
+template <int D, bool kPerToken, bool kScaled>
+static void launch_exact(int blocks, hipStream_t stream, const uint16_t* q, const uint16_t* kv, const int32_t* keys,
+                         int64_t keys_ld, const int32_t* union_len, const uint8_t* hgmask, int T, int H, int S,
+                         int ncols, int64_t q_pos_offset, float sl, uint16_t* out, float* lse,
+                         const int32_t* ginfo, const float* kscale, int scale_per_row) {
+  hipLaunchKernelGGL((rows128_exact_kernel<D, kPerToken, kScaled>), dim3(blocks), dim3(kGThreads), 0, stream, q, kv,
+                     keys, keys_ld, union_len, hgmask, T, H, S, ncols, q_pos_offset, sl, out, lse, ginfo, kscale,
+                     scale_per_row);
+}
+
+template <int D, bool kPerToken>
+static void launch_exact_scaled(int blocks, hipStream_t stream, const uint16_t* q, const uint16_t* kv,
+                                const int32_t* keys, int64_t keys_ld, const int32_t* union_len,
+                                const uint8_t* hgmask, int T, int H, int S, int ncols, int64_t q_pos_offset,
+                                float sl, uint16_t* out, float* lse, const int32_t* ginfo, const float* kscale,
+                                int scale_per_row) {
+  if (kscale)
+    launch_exact<D, kPerToken, true>(blocks, stream, q, kv, keys, keys_ld, union_len, hgmask, T, H, S, ncols,
+                                     q_pos_offset, sl, out, lse, ginfo, kscale, scale_per_row);
+  else
+    launch_exact<D, kPerToken, false>(blocks, stream, q, kv, keys, keys_ld, union_len, hgmask, T, H, S, ncols,
+                                      q_pos_offset, sl, out, lse, ginfo, kscale, scale_per_row);
+}
+
 hipError_t launch_rows128_exact(const uint16_t* q, const uint16_t* kv, const int32_t* keys,
                                 int64_t keys_ld, const int32_t* union_len, const uint8_t* hgmask,
                                 int T, int H, int S, int ncols, int64_t q_pos_offset, float scale,
                                 uint16_t* out, float* lse, hipStream_t stream, const int32_t* group_info,
-                                int ngroups, int d_qk) {
+                                int ngroups, int d_qk, const float* kscale, int scale_per_row) {
   const int NG = ngroups;
   if (NG == 0) return hipSuccess;
   const float sl = scale * kLog2e;
   if (d_qk == 512) {
     if (hgmask != nullptr)
-      hipLaunchKernelGGL((rows128_exact_kernel<512, false>), dim3(NG), dim3(kGThreads), 0, stream, q, kv,
-                         keys, keys_ld, union_len, hgmask, T, H, S, ncols, q_pos_offset, sl, out, lse,
-                         group_info);
+      launch_exact_scaled<512, false>(NG, stream, q, kv, keys, keys_ld, union_len, hgmask, T, H, S, ncols,
+                                      q_pos_offset, sl, out, lse, group_info, kscale, scale_per_row);
     else
-      hipLaunchKernelGGL((rows128_exact_kernel<512, true>), dim3(NG), dim3(kGThreads), 0, stream, q, kv,
-                         keys, keys_ld, union_len, hgmask, T, H, S, ncols, q_pos_offset, sl, out, lse,
-                         group_info);
+      launch_exact_scaled<512, true>(NG, stream, q, kv, keys, keys_ld, union_len, hgmask, T, H, S, ncols,
+                                     q_pos_offset, sl, out, lse, group_info, kscale, scale_per_row);
   } else {
     if (hgmask != nullptr)
-      hipLaunchKernelGGL((rows128_exact_kernel<576, false>), dim3(NG), dim3(kGThreads), 0, stream, q, kv,
-                         keys, keys_ld, union_len, hgmask, T, H, S, ncols, q_pos_offset, sl, out, lse,
-                         group_info);
+      launch_exact_scaled<576, false>(NG, stream, q, kv, keys, keys_ld, union_len, hgmask, T, H, S, ncols,
+                                      q_pos_offset, sl, out, lse, group_info, kscale, scale_per_row);
     else
-      hipLaunchKernelGGL((rows128_exact_kernel<576, true>), dim3(NG), dim3(kGThreads), 0, stream, q, kv,
-                         keys, keys_ld, union_len, hgmask, T, H, S, ncols, q_pos_offset, sl, out, lse,
-                         group_info);
+      launch_exact_scaled<576, true>(NG, stream, q, kv, keys, keys_ld, union_len, hgmask, T, H, S, ncols,
+                                     q_pos_offset, sl, out, lse, group_info, kscale, scale_per_row);
   }
   return hipGetLastError();
 }

@@ -89,7 +89,7 @@ def dense_mha(q, k_nope, k_pe, v, q_pos_offset: int, scale: float, out=None, lse
 # ---------------------------------------------------------------------------
 
 def alloc_latent_ws(S: int, d: int, device="cuda"):
-    """bf16 workspace for a converted latent."""
+    """bf16 workspace for a decoded latent."""
     return torch.empty((S, d), dtype=torch.bfloat16, device=device)
 
 
@@ -119,14 +119,16 @@ def pertoken_fp8(q, kv8, kv_scale, topk, q_pos_offset: int, scale: float, kv_ws=
     return out, lse
 
 
-def dequant_paged_fp8(cache8, kv_scale, batch, ws_pages: int, stream=None):
-    """(ws_cache, batch over it): the batch's reachable pages converted to bf16, and the same
-    batch with the block table over the workspace."""
+def decode_paged_fp8(cache8, kv_scale, batch, ws_pages: int, stream=None):
+    """(ws_cache, ws_row_scale, batch over it): the batch's reachable pages decoded to bf16
+    (exactly), each workspace row's scale, and the same batch with the block table over the
+    workspace."""
     cu, kv_lens, q_pos_start, block_table, page_size = batch
     ws_cache = torch.empty((ws_pages * page_size, cache8.shape[1]), dtype=torch.bfloat16, device=cache8.device)
+    ws_scale = torch.empty((ws_pages * page_size,), dtype=torch.float32, device=cache8.device)
     ws_bt = torch.empty_like(block_table)
-    _lib.dsa_dequant_paged_fp8(cache8, kv_scale, batch, ws_cache, ws_bt, stream=stream)
-    return ws_cache, (cu, kv_lens, q_pos_start, ws_bt, page_size)
+    _lib.dsa_decode_paged_fp8(cache8, kv_scale, batch, ws_cache, ws_scale, ws_bt, stream=stream)
+    return ws_cache, ws_scale, (cu, kv_lens, q_pos_start, ws_bt, page_size)
 
 
 # ---------------------------------------------------------------------------
@@ -162,23 +164,26 @@ def build_group_union_varlen(topk, batch, num_slots: int, G: int, max_groups: in
 
 
 def grouped_varlen(q, kv_cache, topk, batch, scale: float, max_groups: int | None = None,
-                   bufs: VarlenUnionBuffers | None = None, out=None, lse=None, stream=None):
-    """Union/mask build of a batch followed by its grouped attention (G = 128 / H)."""
+                   bufs: VarlenUnionBuffers | None = None, out=None, lse=None, kv_row_scale=None, stream=None):
+    """Union/mask build of a batch followed by its grouped attention (G = 128 / H); kv_row_scale:
+    the cache rows' scales (a decoded FP8 cache) or None."""
     T, H, _ = q.shape
     G = 128 // H
     bufs = build_group_union_varlen(topk, batch, kv_cache.shape[0], G, max_groups, bufs, stream)
     if out is None:
         out, lse = alloc_out(T, H, 512, q.device)
     _lib.dsa_sparse_prefill_grouped_varlen(q, kv_cache, bufs.group_info, bufs.union_idx, bufs.union_len,
-                                           bufs.mask, scale, out, lse, stream=stream)
+                                           bufs.mask, scale, out, lse, kv_row_scale=kv_row_scale, stream=stream)
     return out, lse, bufs
 
 
-def pertoken_varlen(q, kv_cache, topk, batch, scale: float, topk_ws=None, out=None, lse=None, stream=None):
+def pertoken_varlen(q, kv_cache, topk, batch, scale: float, topk_ws=None, out=None, lse=None, kv_row_scale=None,
+                    stream=None):
     T, H, _ = q.shape
     if topk_ws is None:
         topk_ws = torch.empty(topk.shape, dtype=torch.int32, device=q.device)
     if out is None:
         out, lse = alloc_out(T, H, 512, q.device)
-    _lib.dsa_sparse_prefill_pertoken_varlen(q, kv_cache, topk, batch, scale, topk_ws, out, lse, stream=stream)
+    _lib.dsa_sparse_prefill_pertoken_varlen(q, kv_cache, topk, batch, scale, topk_ws, out, lse,
+                                            kv_row_scale=kv_row_scale, stream=stream)
     return out, lse, topk_ws

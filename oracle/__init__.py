@@ -10,8 +10,6 @@ from .dsa_oracle import (  # noqa: F401
     convert_req_index_to_global,
     dense_causal_mha,
     dequant_latent_fp8,
-    dequant_latent_fp8_bf16,
-    f64_to_bf16_bits,
     fp8_e4m3_to_f64,
     group_union_mask,
     group_union_mask_varlen,
@@ -21,6 +19,7 @@ from .dsa_oracle import (  # noqa: F401
     pertoken_sparse_mqa,
     pertoken_sparse_mqa_fp8,
     pertoken_sparse_mqa_varlen,
+    pertoken_sparse_mqa_varlen_fp8,
     physical_row,
     request_of_tokens,
     selected_positions,

@@ -43,10 +43,9 @@ Readings where the pages are silent (each also listed in the design notes):
   gG + i selects union position j; padding slots are 0.
 * FP8 KV latent (the pages only gate quantized caches off the grouped path and
   define no format): OCP E4M3 codes (uint8) with a float32 scale per row or one
-  for the whole cache; element (x, i) = e4m3(kv8[x, i]) * scale.  Attention
-  over such a cache dequantizes it to the bf16 latent the bf16 definition takes
-  -- the float32 product rounded to nearest even, ``dequant_latent_fp8_bf16`` --
-  and is then the per-token definition on those values.
+  for the whole cache; element (x, i) = e4m3(kv8[x, i]) * scale, exactly (in
+  float64).  Attention over such a cache is the per-token definition on those
+  exact values (scores and values both use the scaled elements).
 * Batches of requests over a paged KV cache ([GROUPED] "How": groups are
   consecutive tokens of one request, and the union's request-local positions
   become physical KV rows through the request's index conversion before the
@@ -303,36 +302,16 @@ def dequant_latent_fp8(kv8: np.ndarray, scale: np.ndarray) -> np.ndarray:
     return v * (sc.reshape(-1, 1) if sc.ndim == 1 else sc)
 
 
-def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """bf16 bit patterns of float64 values (round to nearest even through float32)."""
-    f = np.asarray(x, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    nan = np.isnan(f)
-    out = rounded.astype(np.uint16)
-    out[nan] = 0x7FC0
-    return out
-
-
-def dequant_latent_fp8_bf16(kv8: np.ndarray, scale: np.ndarray) -> np.ndarray:
-    """The bf16 latent the dequantizing pass writes: the float32 product e4m3 * scale,
-    rounded to bf16 (nearest even).  uint16 bit patterns."""
-    v = fp8_e4m3_to_f64(kv8).astype(np.float32)   # exact: every E4M3 value is a float32
-    sc = np.asarray(scale, dtype=np.float32)
-    prod = v * (sc.reshape(-1, 1) if sc.ndim == 1 else sc)  # one float32 rounding
-    return f64_to_bf16_bits(prod)
-
-
 def pertoken_sparse_mqa_fp8(q: np.ndarray, kv8: np.ndarray, scale_kv: np.ndarray, topk: np.ndarray,
                             S: int, q_pos_offset: int, scale: float, d_v: int = 512,
                             tokens: Optional[Iterable[int]] = None):
-    """Per-token sparse MQA over an FP8 latent: the latent dequantized to bf16
-    (``dequant_latent_fp8_bf16``), then ``pertoken_sparse_mqa``'s definition on it."""
+    """Per-token sparse MQA over an FP8 latent: ``pertoken_sparse_mqa``'s definition on the
+    exact element values e4m3 * scale (``dequant_latent_fp8``)."""
     T, H, _ = q.shape
     scale = _as_scale(scale)
     toks = _tokens(T, tokens)
     sc = np.asarray(scale_kv, dtype=np.float32)
-    kv64 = bf16_to_f64(dequant_latent_fp8_bf16(kv8[:S], sc[:S] if sc.ndim else sc))
+    kv64 = dequant_latent_fp8(kv8[:S], sc[:S] if sc.ndim else sc)
     out = np.zeros((toks.size, H, d_v))
     lse = np.full((toks.size, H), -np.inf)
     for n, t in enumerate(toks):
@@ -397,10 +376,30 @@ def convert_req_index_to_global(topk, cu_seqlens, kv_lens, q_pos_start, block_ta
 def pertoken_sparse_mqa_varlen(q, kv_cache, topk, cu_seqlens, kv_lens, q_pos_start, block_table,
                                page_size: int, scale: float, d_v: int = 512,
                                tokens: Optional[Iterable[int]] = None):
-    """Per-token sparse MQA of a batch of requests over a paged cache [num_slots, d_qk]."""
+    """Per-token sparse MQA of a batch of requests over a paged cache [num_slots, d_qk]
+    (bf16 bit patterns)."""
+    return _pertoken_varlen(q, lambda rows: bf16_to_f64(kv_cache[rows]), kv_cache.shape[0], topk, cu_seqlens,
+                            kv_lens, q_pos_start, block_table, page_size, scale, d_v, tokens)
+
+
+def pertoken_sparse_mqa_varlen_fp8(q, cache8, scale_kv, topk, cu_seqlens, kv_lens, q_pos_start, block_table,
+                                   page_size: int, scale: float, d_v: int = 512,
+                                   tokens: Optional[Iterable[int]] = None):
+    """Per-token sparse MQA of a batch over a paged FP8 cache (codes [num_slots, d_qk], scale
+    per cache row or one for the cache): the exact element values e4m3 * scale."""
+    sc = np.asarray(scale_kv, dtype=np.float32)
+
+    def rows_of(rows):
+        return dequant_latent_fp8(cache8[rows], sc[rows] if sc.ndim else sc)
+
+    return _pertoken_varlen(q, rows_of, cache8.shape[0], topk, cu_seqlens, kv_lens, q_pos_start, block_table,
+                            page_size, scale, d_v, tokens)
+
+
+def _pertoken_varlen(q, rows_of, num_slots, topk, cu_seqlens, kv_lens, q_pos_start, block_table,
+                     page_size: int, scale: float, d_v: int, tokens):
     T, H, _ = q.shape
     scale = _as_scale(scale)
-    num_slots = kv_cache.shape[0]
     owner = request_of_tokens(cu_seqlens)
     toks = _tokens(T, tokens)
     out = np.zeros((toks.size, H, d_v))
@@ -411,7 +410,7 @@ def pertoken_sparse_mqa_varlen(q, kv_cache, topk, cu_seqlens, kv_lens, q_pos_sta
         xs = selected_local_positions(topk[t], int(kv_lens[r]), pos, block_table, r, page_size,
                                       num_slots)
         rows = [physical_row(block_table, r, int(x), page_size) for x in xs]
-        keys = bf16_to_f64(kv_cache[np.asarray(rows, dtype=np.int64)]) if rows else np.zeros((0, q.shape[2]))
+        keys = rows_of(np.asarray(rows, dtype=np.int64)) if rows else np.zeros((0, q.shape[2]))
         out[n], lse[n] = softmax_attention(bf16_to_f64(q[t]), keys, keys[:, :d_v], scale)
     return out, lse
 

@@ -54,7 +54,7 @@ def test_binding_covers_every_declared_symbol():
 
 def test_helpers(lib):
     from mla_prefill_amd import _lib
-    assert _lib.dsa_abi_version() == 1
+    assert _lib.dsa_abi_version() == 2
     assert _lib.dsa_union_pad(8, 2048) == 16384
     assert _lib.dsa_union_pad(8, 2176) == 17408
     assert _lib.dsa_union_pad(1, 1) == 64
@@ -213,27 +213,29 @@ def test_varlen_validation(lib):
     for kw in ("gi", "ui", "ul", "mk", "cu"):
         assert build(**{kw: None}) == NULL
     assert build(gi=P + 4) == ALIGN
-    def gv(H=16, dqk=576, ns=256, mg=3, pad=128, gi=P, T=8, scale=0.1):
-        return lib.dsa_sparse_prefill_grouped_varlen(P, P, ns, gi, mg, P, P, P, T, H, pad, dqk, 512, scale,
+    def gv(H=16, dqk=576, ns=256, mg=3, pad=128, gi=P, T=8, scale=0.1, rs=None):
+        return lib.dsa_sparse_prefill_grouped_varlen(P, P, rs, ns, gi, mg, P, P, P, T, H, pad, dqk, 512, scale,
                                                      P, P, None)
     assert gv(H=24) == UNSUP and gv(dqk=448) == UNSUP and gv(scale=0.0) == UNSUP
     assert gv(dqk=512, T=0) == OK
     assert gv(ns=0) == SHAPE and gv(pad=40) == SHAPE
     assert gv(mg=0) == OK and gv(T=0) == OK and gv(gi=None) == NULL and gv(gi=P + 4) == ALIGN
-    def pv(H=16, ws=P, T=8, R_=2, cols=16):
-        return lib.dsa_sparse_prefill_pertoken_varlen(P, P, 256, P, 16, T, H, cols, R_, P, P, P, P, 4, 64,
+    assert gv(rs=P + 2) == ALIGN
+    def pv(H=16, ws=P, T=8, R_=2, cols=16, rs=None):
+        return lib.dsa_sparse_prefill_pertoken_varlen(P, P, rs, 256, P, 16, T, H, cols, R_, P, P, P, P, 4, 64,
                                                       576, 512, 0.1, ws, P, P, None)
     assert pv(H=8) == UNSUP and pv(R_=0) == SHAPE and pv(T=0) == OK and pv(ws=None) == NULL
+    assert pv(rs=P + 1) == ALIGN
 
 
 def test_fp8_validation(lib):
-    # conversion pass
-    def dq(kv=P, sc=P, per_row=1, S=64, d=576, out=P):
-        return lib.dsa_dequant_latent_fp8(kv, sc, per_row, S, d, out, None)
-    assert dq(d=500) == UNSUP and dq(S=-1) == SHAPE and dq(S=0) == OK and dq(per_row=2) == SHAPE
-    for kw in ("kv", "sc", "out"):
+    # decode pass
+    def dq(kv=P, S=64, d=576, out=P):
+        return lib.dsa_decode_latent_fp8(kv, S, d, out, None)
+    assert dq(d=500) == UNSUP and dq(S=-1) == SHAPE and dq(S=0) == OK
+    for kw in ("kv", "out"):
         assert dq(**{kw: None}) == NULL
-    assert dq(kv=P + 8) == ALIGN and dq(sc=P + 2) == ALIGN and dq(out=P + 2) == ALIGN
+    assert dq(kv=P + 8) == ALIGN and dq(out=P + 2) == ALIGN
     # attention over an FP8 latent: the bf16 checks first (T = 0 enqueues nothing)
     def gf(q=P, kv=P, sc=P, per_row=0, T=64, H=16, dqk=576, ws=P, pad=256):
         return lib.dsa_sparse_prefill_grouped_fp8(q, kv, sc, per_row, P, P, P, T, H, 64, pad, dqk, 512, 0.1,
@@ -246,11 +248,11 @@ def test_fp8_validation(lib):
                                                    P, P, None)
     assert pf(H=8) == UNSUP and pf(ld=16) == SHAPE and pf(T=0) == OK
     assert pf(kv=None) == NULL and pf(ws=None) == NULL and pf(sc=P + 1) == ALIGN
-    # paged conversion
-    def pg(kv=P, sc=P, ns=256, d=576, R_=2, kl=P, bt=P, bt_ld=4, ps=64, wsp=4, ws=P, wbt=P):
-        return lib.dsa_dequant_paged_fp8(kv, sc, 1, ns, d, R_, kl, bt, bt_ld, ps, wsp, ws, wbt, None)
+    # paged decode
+    def pg(kv=P, sc=P, ns=256, d=576, R_=2, kl=P, bt=P, bt_ld=4, ps=64, wsp=4, ws=P, wsc=P, wbt=P):
+        return lib.dsa_decode_paged_fp8(kv, sc, 1, ns, d, R_, kl, bt, bt_ld, ps, wsp, ws, wsc, wbt, None)
     assert pg(d=192) == UNSUP and pg(ns=100) == SHAPE and pg(R_=0) == SHAPE and pg(ps=0) == SHAPE
     assert pg(wsp=-1) == SHAPE and pg(bt_ld=0) == SHAPE
-    for kw in ("kv", "sc", "kl", "bt", "ws", "wbt"):
+    for kw in ("kv", "sc", "kl", "bt", "ws", "wsc", "wbt"):
         assert pg(**{kw: None}) == NULL
-    assert pg(wbt=P + 2) == ALIGN and pg(kv=P + 4) == ALIGN
+    assert pg(wbt=P + 2) == ALIGN and pg(kv=P + 4) == ALIGN and pg(wsc=P + 2) == ALIGN

@@ -420,35 +420,51 @@ def test_fp8_decode_closed_forms():
     assert np.isnan(v[8]) and np.isnan(v[9])
 
 
-def test_bf16_rounding_matches_torch():
-    rng = np.random.default_rng(70)
-    x = np.concatenate([rng.standard_normal(5000).astype(np.float32),
-                        # exact ties between two bf16 values, both parities, and specials
-                        np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 0.0, -0.0,
-                                  np.inf, -np.inf, 3.0e38], np.float32)])
-    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    np.testing.assert_array_equal(oracle.f64_to_bf16_bits(x), ref)
-
-
 @pytest.mark.parametrize("per_row", [False, True])
-def test_fp8_dequant_bits_match_torch(per_row):
+def test_fp8_dequant_is_the_exact_product(per_row):
+    """e4m3 * scale in float64 is exact (4 significant bits times 24): it equals torch's
+    float8_e4m3fn decode times the float32 scale computed in float64, bit for bit."""
     rng = np.random.default_rng(71 + per_row)
     S, d = 37, 40
     kv8 = rng.integers(0, 256, (S, d)).astype(np.uint8)
     kv8[(kv8 & 0x7F) == 0x7F] = 0x3A   # no NaN codes in a cache
     scale = (rng.uniform(0.01, 3.0, S) if per_row else np.float32(0.0371)).astype(np.float32)
-    got = oracle.dequant_latent_fp8_bf16(kv8, scale)
-    f = torch.from_numpy(kv8).view(torch.float8_e4m3fn).float()
-    sc = torch.from_numpy(np.atleast_1d(scale)).float()
+    f = torch.from_numpy(kv8).view(torch.float8_e4m3fn).double()
+    sc = torch.from_numpy(np.atleast_1d(scale)).double()
     prod = f * (sc[:, None] if per_row else sc[0])
-    ref = prod.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    np.testing.assert_array_equal(got, ref)
-    np.testing.assert_allclose(oracle.dequant_latent_fp8(kv8, scale), prod.double().numpy(), rtol=1e-7)
+    np.testing.assert_array_equal(oracle.dequant_latent_fp8(kv8, scale), prod.numpy())
+
+
+def test_fp8_attention_matches_torch_sdpa_on_scaled_rows():
+    """Per-row scales that are not powers of two (the scaled elements are not bf16 numbers):
+    the oracle equals torch SDPA / logsumexp in float64 over torch's own decode of the codes
+    times the scales, under the selection mask built with torch scatter."""
+    rng = np.random.default_rng(75)
+    T, S, H, d, dv = 30, 41, 3, 24, 16
+    kv8 = rng.integers(0, 256, (S, d)).astype(np.uint8)
+    kv8[(kv8 & 0x7F) == 0x7F] = 0x33
+    scale_kv = rng.uniform(0.003, 0.9, S).astype(np.float32)
+    q = normal_bf16(rng, (T, H, d))
+    topk = topk_uniform(rng, T, S, 9, 11, S - T)
+    topk[3, -1] = S + 4          # out of range: ignored
+    sc = float(np.float32(0.31))
+    out, lse = oracle.pertoken_sparse_mqa_fp8(q, kv8, scale_kv, topk, S, S - T, 0.31, d_v=dv)
+    kv = torch.from_numpy(kv8).view(torch.float8_e4m3fn).double() * torch.from_numpy(scale_kv).double()[:, None]
+    qt = to_t64(q)
+    allow = allowed_mask(topk, S, S - T)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qt.transpose(0, 1), kv[None].expand(H, S, -1), kv[None, :, :dv].expand(H, S, -1),
+        attn_mask=allow[None], scale=sc).transpose(0, 1)
+    logits = torch.einsum("thd,sd->ths", qt, kv) * sc
+    ref_lse = torch.logsumexp(logits.masked_fill(~allow[:, None, :], -math.inf), dim=-1)
+    np.testing.assert_allclose(out, ref.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse.numpy(), rtol=1e-12, atol=1e-12)
 
 
 def test_fp8_attention_equals_bf16_attention_on_exact_values():
-    """A power-of-two scale keeps every dequantized value a bf16 number, so the FP8 definition
+    """A power-of-two scale keeps every scaled element a bf16 number, so the FP8 definition
     must equal the (pinned) bf16 one on those bits; per-row scales all equal to it as well."""
+    from synth.gen import bf16_bits_from_f32
     rng = np.random.default_rng(73)
     T, S, H, d, dv = 20, 30, 2, 24, 16
     kv8 = rng.integers(0, 256, (S, d)).astype(np.uint8)
@@ -456,13 +472,36 @@ def test_fp8_attention_equals_bf16_attention_on_exact_values():
     q = normal_bf16(rng, (T, H, d))
     topk = topk_uniform(rng, T, S, 8, 10, S - T)
     sc = np.float32(0.125)
-    kv_bits = oracle.dequant_latent_fp8_bf16(kv8, sc)
-    np.testing.assert_array_equal(oracle.bf16_to_f64(kv_bits), oracle.dequant_latent_fp8(kv8, sc))
+    vals = torch.from_numpy(kv8).view(torch.float8_e4m3fn).float().numpy() * sc
+    kv_bits = bf16_bits_from_f32(vals)
+    np.testing.assert_array_equal(oracle.bf16_to_f64(kv_bits), vals.astype(np.float64))   # exact in bf16
     ref = oracle.pertoken_sparse_mqa(q, kv_bits, topk, S, S - T, 0.3, d_v=dv)
     for scale_kv in (sc, np.full(S, sc, np.float32)):
         got = oracle.pertoken_sparse_mqa_fp8(q, kv8, scale_kv, topk, S, S - T, 0.3, d_v=dv)
         np.testing.assert_array_equal(got[0], ref[0])
         np.testing.assert_array_equal(got[1], ref[1])
+
+
+def test_fp8_paged_equals_single_sequence_on_gathered_rows():
+    """A paged FP8 batch of one request equals the single-sequence FP8 definition over the
+    request's rows gathered in position order (codes and scales moved together)."""
+    rng = np.random.default_rng(76)
+    T, P0, H, d, page = 9, 14, 2, 24, 4
+    L = P0 + T
+    pages = -(-L // page)
+    perm = rng.permutation(pages + 2).astype(np.int32)
+    bt = perm[:pages][None]
+    ns = (pages + 2) * page
+    cache8 = rng.integers(0, 0x7E, (ns, d)).astype(np.uint8)
+    sck = rng.uniform(0.01, 2.0, ns).astype(np.float32)
+    q = normal_bf16(rng, (T, H, d))
+    topk = topk_uniform(rng, T, L, 6, 7, P0)
+    got = oracle.pertoken_sparse_mqa_varlen_fp8(q, cache8, sck, topk, np.array([0, T]), np.array([L]),
+                                                np.array([P0]), bt, page, 0.2, d_v=16)
+    rows = np.array([oracle.physical_row(bt, 0, x, page) for x in range(L)])
+    ref = oracle.pertoken_sparse_mqa_fp8(q, cache8[rows], sck[rows], topk, L, P0, 0.2, d_v=16)
+    np.testing.assert_array_equal(got[0], ref[0])
+    np.testing.assert_array_equal(got[1], ref[1])
 
 
 def test_fp8_per_row_scale_scales_values_only():
