@@ -65,6 +65,7 @@ extern "C" {
 #define DSA_ERR_UNSUPPORTED (-3) /* head count / head dims / scale outside the supported set */
 #define DSA_ERR_ALIGN (-4)       /* a pointer is not aligned as required */
 #define DSA_ERR_LAUNCH (-5)      /* the HIP runtime rejected a kernel launch */
+#define DSA_ERR_CAPACITY (-6)    /* the work needs more than the library's static scratch */
 
 /* Version of this ABI (DSA_ABI_VERSION). */
 int dsa_abi_version(void);
@@ -206,6 +207,25 @@ int dsa_masked_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint
                            const uint16_t* v, const int32_t* topk, int64_t ld, int T, int S, int H,
                            int dn, int dr, int dv, int cols, int64_t q_pos_offset, float scale,
                            uint32_t* mask_ws, uint16_t* out, float* lse, void* stream);
+
+/* For callers that cannot allocate (code under graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): dsa_masked_mha_prefill without the
+ * mask_ws argument.  The bit-packed top-k mask lives in a static device array
+ * of the library, DSA_SCRATCH_BYTES on each GPU it runs on, held until the
+ * process ends; the call allocates nothing (no hipMalloc / hipFree, no
+ * allocating library routine) and does not synchronize.  Every call on a GPU
+ * shares that GPU's array, and each call rewrites the T * ceil(S / 32) words
+ * it uses before reading them, so calls that overlap on one GPU (on other
+ * streams or threads) race and must be ordered by the caller.
+ * DSA_ERR_CAPACITY when dsa_masked_mha_workspace_bytes(T, S) exceeds
+ * DSA_SCRATCH_BYTES (e.g. T = S = 16384 fits; T = 16384, S = 32800 does not);
+ * DSA_ERR_LAUNCH also when the array's device address cannot be obtained.
+ * Every other argument, check and result as dsa_masked_mha_prefill. */
+#define DSA_SCRATCH_BYTES ((size_t)32 << 20)
+int dsa_masked_mha_prefill_noalloc(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_pe,
+                                   const uint16_t* v, const int32_t* topk, int64_t ld, int T, int S, int H,
+                                   int dn, int dr, int dv, int cols, int64_t q_pos_offset, float scale,
+                                   uint16_t* out, float* lse, void* stream);
 
 /* Dense causal MHA, the shortcut for chunks no longer than the top-k ("[2/N]
  * [Attention] Enable masked MHA for sparse MLA prefills", Purpose section:

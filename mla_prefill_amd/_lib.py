@@ -38,6 +38,8 @@ _SIGNATURES = {
                                      _vp, _vp, _vp], _i32),
     "dsa_masked_mha_prefill": ([_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                 _i64, _f32, _vp, _vp, _vp, _vp], _i32),
+    "dsa_masked_mha_prefill_noalloc": ([_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                        _i64, _f32, _vp, _vp, _vp], _i32),
     "dsa_dense_mha_prefill": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32,
                                _vp, _vp, _vp], _i32),
     "dsa_decode_latent_fp8": ([_vp, _i32, _i32, _vp, _vp], _i32),
@@ -181,6 +183,20 @@ def dsa_masked_mha_prefill(q, k_nope, k_pe, v, topk, q_pos_offset, scale, mask_w
         _ptr(_bits(q)), _ptr(_bits(k_nope)), _ptr(_bits(k_pe)), _ptr(_bits(v)), _ptr(topk),
         _topk_ld(topk), T, S, H, dn, dr, dv, cols, q_pos_offset, scale, _ptr(mask_ws),
         _ptr(_bits(out)), _ptr(lse), _stream(stream)))
+
+
+def dsa_masked_mha_prefill_noalloc(q, k_nope, k_pe, v, topk, q_pos_offset, scale, out, lse, cols=None,
+                                   stream=None):
+    """dsa_masked_mha_prefill with the mask in the library's static scratch (no workspace)."""
+    T, H, dqk = q.shape
+    S, _, dn = k_nope.shape
+    dr = 0 if k_pe is None else k_pe.shape[-1]
+    dv = v.shape[2]
+    cols = topk.shape[1] if cols is None else cols
+    _check("dsa_masked_mha_prefill_noalloc", lib.dsa_masked_mha_prefill_noalloc(
+        _ptr(_bits(q)), _ptr(_bits(k_nope)), _ptr(_bits(k_pe)), _ptr(_bits(v)), _ptr(topk),
+        _topk_ld(topk), T, S, H, dn, dr, dv, cols, q_pos_offset, scale, _ptr(_bits(out)), _ptr(lse),
+        _stream(stream)))
 
 
 def dsa_dense_mha_prefill(q, k_nope, k_pe, v, q_pos_offset, scale, out, lse, stream=None):

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "dsa_prefill.h"
 #include "kernels.h"
 
@@ -54,6 +56,7 @@ const char* dsa_status_string(int status) {
     case DSA_ERR_UNSUPPORTED: return "unsupported head count, head dimensions or scale";
     case DSA_ERR_ALIGN: return "a pointer is not aligned as required";
     case DSA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case DSA_ERR_CAPACITY: return "the work needs more than the library's static scratch (DSA_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -362,10 +365,12 @@ int dsa_decode_paged_fp8(const uint8_t* cache8, const float* kv_scale, int scale
                                                     ws_row_scale, ws_block_table, (hipStream_t)stream));
 }
 
-int dsa_masked_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_pe,
-                           const uint16_t* v, const int32_t* topk, int64_t ld, int T, int S, int H,
-                           int dn, int dr, int dv, int cols, int64_t q_pos_offset, float scale,
-                           uint32_t* mask_ws, uint16_t* out, float* lse, void* stream) {
+// Host checks of the masked MHA calls (mask_ws is checked only when `with_ws`): DSA_OK when
+// the call has work to enqueue, kNothingToDo for an empty one, else the status.
+static int masked_check(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_pe, const uint16_t* v,
+                        const int32_t* topk, int64_t ld, int T, int S, int H, int dn, int dr, int dv, int cols,
+                        int64_t q_pos_offset, float scale, bool with_ws, const uint32_t* mask_ws,
+                        const uint16_t* out, const float* lse) {
   // geometries: NoPE (256, 0, 256), the key is k_nope itself; (192, 64, 256) and
   // (128, 64, 128), the key is k_nope || k_pe with k_pe shared by every head
   const bool nope = mha_nope(dn, dr, dv), rope = mha_rope(dn, dr, dv);
@@ -373,13 +378,21 @@ int dsa_masked_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint
   // (H <= 65536 keeps the kernels' 32-bit per-lane key-row offsets and the grid in range)
   if (H < 1 || H > 65536 || T < 0 || S < 1 || cols < 0 || ld < cols || q_pos_offset < 0) return DSA_ERR_SHAPE;
   if (((int64_t)T + 255) / 256 * H > 0x7fffffff) return DSA_ERR_SHAPE;  // one workgroup per (256 tokens, head)
-  if (T == 0) return DSA_OK;
-  if (!q || !k_nope || !v || (cols > 0 && !topk) || !mask_ws || !out || !lse || (rope && !k_pe))
+  if (T == 0) return kNothingToDo;
+  if (!q || !k_nope || !v || (cols > 0 && !topk) || (with_ws && !mask_ws) || !out || !lse || (rope && !k_pe))
     return DSA_ERR_NULL;
   if (!aligned_to(q, 16) || !aligned_to(k_nope, 16) || !aligned_to(v, 16) ||
-      !aligned_to(out, 16) || !aligned_to(lse, 4) || !aligned_to(mask_ws, 4) ||
+      !aligned_to(out, 16) || !aligned_to(lse, 4) || (with_ws && !aligned_to(mask_ws, 4)) ||
       !aligned_to(topk, 4) || (rope && !aligned_to(k_pe, 16)))
     return DSA_ERR_ALIGN;
+  return DSA_OK;
+}
+
+static int masked_launch(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_pe, const uint16_t* v,
+                         const int32_t* topk, int64_t ld, int T, int S, int H, int dn, int dr, int dv, int cols,
+                         int64_t q_pos_offset, float scale, uint32_t* mask_ws, uint16_t* out, float* lse,
+                         void* stream) {
+  const bool rope = dr > 0;
   const int words = (S + 31) / 32;
   hipError_t e = dsa::launch_scatter_topk_bits(topk, ld, T, cols, S, q_pos_offset, mask_ws, words,
                                                (hipStream_t)stream);
@@ -387,6 +400,17 @@ int dsa_masked_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint
   return launch_status(dsa::launch_masked_mha(q, k_nope, rope ? k_pe : nullptr, dn, dr, dv, v, mask_ws,
                                               words, T, S, H, q_pos_offset, scale, out, lse,
                                               (hipStream_t)stream));
+}
+
+int dsa_masked_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_pe,
+                           const uint16_t* v, const int32_t* topk, int64_t ld, int T, int S, int H,
+                           int dn, int dr, int dv, int cols, int64_t q_pos_offset, float scale,
+                           uint32_t* mask_ws, uint16_t* out, float* lse, void* stream) {
+  const int st = masked_check(q, k_nope, k_pe, v, topk, ld, T, S, H, dn, dr, dv, cols, q_pos_offset, scale, true,
+                              mask_ws, out, lse);
+  if (st != DSA_OK) return st == kNothingToDo ? DSA_OK : st;
+  return masked_launch(q, k_nope, k_pe, v, topk, ld, T, S, H, dn, dr, dv, cols, q_pos_offset, scale, mask_ws, out,
+                       lse, stream);
 }
 
 int dsa_dense_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_pe,
@@ -406,3 +430,46 @@ int dsa_dense_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint1
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The entry point that allocates nothing: the masked-MHA bit mask in a static device array.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kScratchWords = DSA_SCRATCH_BYTES / sizeof(uint32_t);
+constexpr int kMaxDevices = 64;
+// this array's device address on each GPU, taken once per device with that device current
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+}  // namespace
+
+// Per GPU, held until the process ends.  In host code `scratch` names a host-side stand-in,
+// never the device memory: kernels get the address hipGetSymbolAddress returns.
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+
+// the device address of `scratch` on the current device (DSA_OK), or DSA_ERR_LAUNCH
+static int scratch_address(uint32_t** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DSA_ERR_LAUNCH;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // (two threads may both get here first: they store the same address)
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return DSA_ERR_LAUNCH;
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *addr = static_cast<uint32_t*>(p);
+  return DSA_OK;
+}
+
+extern "C" int dsa_masked_mha_prefill_noalloc(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_pe,
+                                              const uint16_t* v, const int32_t* topk, int64_t ld, int T, int S,
+                                              int H, int dn, int dr, int dv, int cols, int64_t q_pos_offset,
+                                              float scale, uint16_t* out, float* lse, void* stream) {
+  const int st = masked_check(q, k_nope, k_pe, v, topk, ld, T, S, H, dn, dr, dv, cols, q_pos_offset, scale, false,
+                              nullptr, out, lse);
+  if (st != DSA_OK) return st == kNothingToDo ? DSA_OK : st;
+  if (dsa_masked_mha_workspace_bytes(T, S) > DSA_SCRATCH_BYTES) return DSA_ERR_CAPACITY;
+  uint32_t* mask_ws = nullptr;
+  const int sa = scratch_address(&mask_ws);
+  if (sa != DSA_OK) return sa;
+  return masked_launch(q, k_nope, k_pe, v, topk, ld, T, S, H, dn, dr, dv, cols, q_pos_offset, scale, mask_ws, out,
+                       lse, stream);
+}

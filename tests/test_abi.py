@@ -156,6 +156,25 @@ def test_masked_mha_validation(lib):
     assert mha_call(lib, kn=P + 2) == ALIGN and mha_call(lib, ws=P + 2) == ALIGN
 
 
+def test_masked_mha_noalloc_validation(lib):
+    """The no-allocation form: the same host checks without a workspace argument, and
+    DSA_ERR_CAPACITY (checked before any HIP call) past the static scratch."""
+    CAPACITY = -6
+    def call(q=P, kn=P, kp=None, v=P, tk=P, ld=16, T=4, S=8, H=2, dn=256, dr=0, dv=256, cols=16, P0=0,
+             scale=0.1, out=P, lse=P):
+        return lib.dsa_masked_mha_prefill_noalloc(q, kn, kp, v, tk, ld, T, S, H, dn, dr, dv, cols, P0, scale,
+                                                  out, lse, None)
+    assert call(dn=192, dr=64) == NULL and call(dn=256, dr=64) == UNSUP and call(scale=0.0) == UNSUP
+    assert call(H=0) == SHAPE and call(ld=8) == SHAPE and call(T=0) == OK
+    for kw in ("q", "kn", "v", "tk", "out", "lse"):
+        assert call(**{kw: None}) == NULL
+    assert call(kn=P + 2) == ALIGN
+    # 16384 x ceil(32800 / 32) words = 67 MB > 32 MiB; 16384 x 16384 fits exactly
+    assert lib.dsa_masked_mha_workspace_bytes(16384, 16384) == 32 << 20
+    assert call(T=16384, S=32800) == CAPACITY
+    assert lib.dsa_status_string(CAPACITY).decode().startswith("the work needs more than")
+
+
 def dense_call(lib, q=P, kn=P, kp=None, v=P, T=4, S=8, H=2, dn=256, dr=0, dv=256, p0=0, scale=0.1,
                out=P, lse=P):
     return lib.dsa_dense_mha_prefill(q, kn, kp, v, T, S, H, dn, dr, dv, p0, scale, out, lse, None)
