@@ -72,6 +72,20 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// The same 32x32x16 MFMA written out, with its accumulator in VGPRs: score accumulators that
+// the softmax reads and masks in place stay out of the accumulation registers, which the O^T
+// accumulators fill.  The compiler sees no latency for these, so a VALU read of the result
+// must come several MFMAs later (the kernels keep at least four between them).
+__device__ __forceinline__ f32x16 mfma_qk_first(bf16x8 a, bf16x8 b) {
+  f32x16 d;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ f32x16 mfma_qk(bf16x8 a, bf16x8 b, f32x16 c) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  return c;
+}
+
 // ---------------------------------------------------------------------------
 // Asynchronous global -> LDS copies (gfx950 LDS DMA).
 //

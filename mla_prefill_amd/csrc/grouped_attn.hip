@@ -42,6 +42,8 @@
 //    is multiplied by its row's scale before the softmax and each probability
 //    by it before the PV product (l sums the unscaled probabilities);
 //  * longest groups (most union slots) are launched first.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -54,7 +56,7 @@ constexpr int kRKeys = 32;                          // slots per tile
 constexpr int kRStages = 3;
 constexpr int kRIdxBufs = 4;                        // index/membership buffers (one tile further ahead)
 constexpr float kRSlack = 64.f;                     // log2 of the largest probability allowed
-constexpr int kRQRegSteps = 28;                     // query k-steps kept in registers
+constexpr int kRQRegSteps = 32;                     // query k-steps kept in registers
 
 // D: the latent width, 576 (512 + 64 rope dims) or 512 (no rope part); kScaled: the latent
 // rows carry scales (kscale[scale_per_row ? x : 0] for row x)
@@ -69,12 +71,15 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   constexpr int kRGroupBytes = 8 * D * 2;           // one 8-row group (9216 / 8192)
   constexpr int kRStageBytes = 4 * kRGroupBytes;    // one 32-slot tile
   constexpr int kRCopies = kRGroupBytes / 1024;     // row copies per wave per tile (9 / 8)
-  constexpr int kRRowOps = kRCopies + (kScaled ? 1 : 0);  // + the tile's scale copy
   constexpr int kRQLdsSteps = D / 16 - kRQRegSteps;  // query k-steps in LDS (lane-private)
   __shared__ __align__(16) uint8_t stage[kRStages][kRStageBytes];
   // per tile and wave: lanes 0..7 = slot indices 8 w .. 8 w + 7, lanes 8, 9 = their membership bytes
   __shared__ __align__(16) uint32_t idxw[kRIdxBufs][kRWaves][64];
-  __shared__ __align__(16) uint4 qlds[kRWaves][kRQLdsSteps][64];
+  __shared__ __align__(16) uint4 qlds[kRWaves][kRQLdsSteps > 0 ? kRQLdsSteps : 1][64];
+  // probabilities of a tile (two buffers): wave w's lane l stores the B operand of slot step st
+  // for its row block at pbuf[b][w][st][l]; every wave reads it back for row block w
+  __shared__ __align__(16) bf16x8 pbuf[2][kRWaves][2][64];
+  __shared__ float lsum[128];
   // kScaled: per tile and wave, lane l holds the scale of slot 8 w + l % 8
   __shared__ __align__(16) float sbuf[kScaled ? kRStages : 1][kRWaves][64];
   __shared__ int over_any;
@@ -176,26 +181,50 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   // uniform base kv + 128 c plus the lane's offset, with no 64-bit address arithmetic)
   const bool small_kv = (int64_t)S * (2 * D) < ((int64_t)1 << 31);
   const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv);
-  auto issue_rows = [&](int t) {
-    const int32_t x = (int32_t)idxw[t % kRIdxBufs][wave][crow];  // landed (own copy, waited for)
+  // A tile's row copies: the source row of this lane's slot, resolved once (rows_make, which
+  // also copies the slots' scales), its source and LDS destination (rows_src), then one
+  // 128-byte block per copy instruction (rows_copy), so that a tile's copies can be spread
+  // between MFMAs.
+  struct RowSrc {
+    uint32_t ofs;          // small latent: byte offset of this lane's 16 bytes of the row
+    const uint16_t* src;   // otherwise: their address
+    uint32_t dst;          // LDS address of the wave's 8-row group in the stage
+  };
+  // (the slot indices of a tile's copies: this lane's copy row, and for the scales slot
+  // 8 w + l % 8 -- read from this wave's own landed words first, used later, so the LDS
+  // latency can pass under MFMAs)
+  auto rows_read = [&](int t) -> int2 {
+    return int2{(int)idxw[t % kRIdxBufs][wave][crow], kScaled ? (int)idxw[t % kRIdxBufs][wave][lane & 7] : 0};
+  };
+  auto rows_src = [&](int t, uint32_t row) -> RowSrc {
+    RowSrc r;
+    r.dst = lds_addr(stage[t % kRStages]) + cdst;
+    r.ofs = row * (2 * D) + 16 * cchunk;
+    r.src = cbase + (size_t)row * D;
+    return r;
+  };
+  auto rows_make = [&](int t, int2 xr) -> uint32_t {
+    const int32_t x = xr.x;
     const bool ok = slot_ok(x, t * kRKeys + 8 * wave + crow);
-    const uint32_t dst = lds_addr(stage[t % kRStages]) + cdst;
-    // (the global address carries the block offset: an instruction offset would also
-    // move the LDS destination of an LDS-DMA load)
-    if (small_kv) {
-      const uint32_t ofs = (uint32_t)(ok ? x : dummy_row) * (2 * D) + 16 * cchunk;
-#pragma unroll
-      for (int c = 0; c < kRCopies; ++c) dma16_sbase(ofs, kvb + 128 * c, dst + 1024 * c);
-    } else {
-      const uint16_t* src = cbase + (size_t)(ok ? x : dummy_row) * D;
-#pragma unroll
-      for (int c = 0; c < kRCopies; ++c) dma16(src + 64 * c, dst + 1024 * c);
-    }
     if (kScaled) {  // the scales of slots 8 w .. 8 w + 7 (lane l: slot 8 w + l % 8)
-      const int32_t xs = (int32_t)idxw[t % kRIdxBufs][wave][lane & 7];
+      const int32_t xs = xr.y;
       const bool oks = slot_ok(xs, t * kRKeys + 8 * wave + (lane & 7));
       dma4(kscale + (scale_per_row && oks ? xs : 0), lds_addr(&sbuf[kScaled ? t % kRStages : 0][wave][0]));
     }
+    return (uint32_t)(ok ? x : dummy_row);
+  };
+  // (the global address carries the block offset: an instruction offset would also move the
+  // LDS destination of an LDS-DMA load)
+  auto rows_copy = [&](const RowSrc& r, int c) {
+    if (small_kv)
+      dma16_sbase(r.ofs, kvb + 128 * c, r.dst + 1024 * c);
+    else
+      dma16(r.src + 64 * c, r.dst + 1024 * c);
+  };
+  auto issue_rows = [&](int t) {
+    const RowSrc r = rows_src(t, rows_make(t, rows_read(t)));
+#pragma unroll
+    for (int c = 0; c < kRCopies; ++c) rows_copy(r, c);
   };
 
   // K reads (A of S^T): key m, dims 16 s + 8 hi -> chunk 2 s + hi: 4 bases (s % 4) + (s / 4) KiB
@@ -209,173 +238,263 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   const int vx = (2 * (g16 & 1) + ((s16 & 3) >> 1)) ^ swz8(vr8);
   const int vbase = vr8 * 128 + 8 * (s16 & 1);
 
-  float m_ref = kNegInf;  // row r's reference (log2 units), equal in both halves
-  float l_run = 0.f;      // this lane's partial sum (its 16 keys of every tile)
-  bool over = false;
-  f32x16 o[kRDv / 32];
-#pragma unroll
-  for (int cb = 0; cb < kRDv / 32; ++cb) o[cb] = f32x16{};
-
-  if (ntiles > 0) {
-    issue_idx(0);
-    if (ntiles > 1) issue_idx(1);
-    wait_vmcnt<0>();
-    issue_rows(0);
-    if (ntiles > 2) issue_idx(2);
-    if (ntiles > 1) issue_rows(1);
-  }
-  for (int t = 0; t < ntiles; ++t) {
-    // tile t and the indices of tile t + 2 (copied before tile t + 1's rows) have landed
-    if (t + 1 < ntiles)
-      wait_vmcnt<kRRowOps>();
-    else
-      wait_vmcnt<0>();
-    __syncthreads();  // tile t visible to all waves; stage (t + 2) % 3 and index buffer (t + 3) % 4 free
-    if (t + 3 < ntiles) issue_idx(t + 3);
-    if (t + 2 < ntiles) issue_rows(t + 2);
-
-    // membership masks of this tile for the wave's two tokens (bit j <-> slot j)
+  // ---- per-tile pieces ------------------------------------------------------------------
+  // membership of tile t's slots for this lane's row: bit kk <-> slot 4 hi + kk (kk = 8 u + jj)
+  // (read: lane l takes slot l % 32's index and membership word, written by every wave's
+  // copies, so after a barrier; make: the ballots)
+  auto allowed_read = [&](int t) -> uint2 {
+    const int sl = lane & 31;
+    const uint32_t* iw = &idxw[t % kRIdxBufs][sl >> 3][0];
+    return uint2{iw[sl & 7], kPerToken ? 0u : iw[8 + ((sl & 7) >> 2)]};
+  };
+  auto allowed_make = [&](int t, uint2 w) -> uint32_t {
+    const int sl = lane & 31;
+    const bool ok = slot_ok((int32_t)w.x, t * kRKeys + sl);
     uint32_t mk0, mk1;
-    {
-      const int sl = lane & 31;
-      const uint32_t* iw = &idxw[t % kRIdxBufs][sl >> 3][0];
-      const bool ok = slot_ok((int32_t)iw[sl & 7], t * kRKeys + sl);
-      if (kPerToken) {
-        mk0 = mk1 = (uint32_t)ballot(ok);
-      } else {
-        const uint32_t byte = iw[8 + ((sl & 7) >> 2)] >> (8 * (sl & 3));
-        mk0 = (uint32_t)ballot(ok && ((byte >> ti0) & 1u));
-        mk1 = (uint32_t)ballot(ok && ((byte >> ti1) & 1u));
-      }
+    if (kPerToken) {
+      mk0 = mk1 = (uint32_t)ballot(ok);
+    } else {
+      const uint32_t byte = w.y >> (8 * (sl & 3));
+      mk0 = (uint32_t)ballot(ok && ((byte >> ti0) & 1u));
+      mk1 = (uint32_t)ballot(ok && ((byte >> ti1) & 1u));
     }
-    // bit kk <-> slot 4 hi + kk
-    const uint32_t allowed = (second ? mk1 : mk0) >> (4 * hi);
+    return (second ? mk1 : mk0) >> (4 * hi);
+  };
+  auto tile_allowed = [&](int t) -> uint32_t { return allowed_make(t, allowed_read(t)); };
+  // kScaled: row scales of tile t's slots 8 u + 4 hi .. + 3 (score registers 4 u .. 4 u + 3)
+  auto tile_scales = [&](int t, f32x4 (&ks)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      ks[u] = kScaled ? *reinterpret_cast<const f32x4*>(&sbuf[kScaled ? t % kRStages : 0][u][4 * hi])
+                      : f32x4{1.f, 1.f, 1.f, 1.f};
+  };
 
-    // one stage offset per iteration (kept opaque so no per-stage address sets are hoisted)
-    const int sofs = loop_local((t % kRStages) * kRStageBytes);
-    const uint8_t* kt = &stage[0][0] + sofs;
+  // S^T = K Q^T of tile t: sacc[j] = raw score(slot 8 (j / 4) + 4 hi + j % 4, row r).  The K
+  // reads run kRAhead MFMAs ahead (the order is pinned: left to itself the scheduler puts
+  // every read right before its MFMA and waits out its latency).  With `copy`, block c of a
+  // later tile's row copies (`next`) goes out after MFMA 4 c + 1: spread over the MFMAs, the
+  // copies do not hold the wave at their issue as a burst does.
+  auto qk = [&](int t, auto copy_tag, uint32_t next_row) -> f32x16 {
+    constexpr bool copy = decltype(copy_tag)::value;
+    const RowSrc next = rows_src(t + 1, next_row);
+    const uint8_t* kt = &stage[0][0] + loop_local((t % kRStages) * kRStageBytes);
     // (the LDS query address is made opaque per tile, so that its reads are not hoisted)
     const uint8_t* qb = reinterpret_cast<const uint8_t*>(&qlds[wave][0][0]) + loop_local(16 * lane);
-    // K operand reads run kRAhead steps ahead of the MFMAs (the order is pinned: left to
-    // itself the scheduler puts every read right before its MFMA and waits out its latency)
-    auto kread = [&](int s) -> bf16x8 {
-      return *reinterpret_cast<const bf16x8*>(kt + kofs[s & 3] + 1024 * (s >> 2));
+    auto kread = [&](int st) -> bf16x8 {
+      return *reinterpret_cast<const bf16x8*>(kt + kofs[st & 3] + 1024 * (st >> 2));
     };
-    auto qread = [&](int s) -> bf16x8 {
-      return s < kRQRegSteps ? qreg[s < kRQRegSteps ? s : 0]
-                             : *reinterpret_cast<const bf16x8*>(qb + 1024 * (s - kRQRegSteps));
+    auto qread = [&](int st) -> bf16x8 {
+      return st < kRQRegSteps ? qreg[st < kRQRegSteps ? st : 0]
+                              : *reinterpret_cast<const bf16x8*>(qb + 1024 * (st - kRQRegSteps));
     };
     constexpr int kRAhead = 4;
     bf16x8 kw[kRAhead], qw[kRAhead];
 #pragma unroll
-    for (int s = 0; s < kRAhead; ++s) {
-      kw[s] = kread(s);
-      qw[s] = qread(s);
+    for (int st = 0; st < kRAhead; ++st) {
+      kw[st] = kread(st);
+      qw[st] = qread(st);
     }
-    f32x16 sacc = {};  // sacc[j] = raw score(slot 8 (j / 4) + 4 hi + j % 4, row r)
+    f32x16 acc;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
+    for (int st = 0; st < D / 16; ++st) {
       __builtin_amdgcn_sched_barrier(0);
-      sacc = mfma32x32x16(kw[s % kRAhead], qw[s % kRAhead], sacc);
-      if (s + kRAhead < D / 16) {
-        kw[s % kRAhead] = kread(s + kRAhead);
-        qw[s % kRAhead] = qread(s + kRAhead);
+      acc = st == 0 ? mfma_qk_first(kw[0], qw[0]) : mfma_qk(kw[st % kRAhead], qw[st % kRAhead], acc);
+      if (st + kRAhead < D / 16) {
+        kw[st % kRAhead] = kread(st + kRAhead);
+        qw[st % kRAhead] = qread(st + kRAhead);
       }
+      if (copy && (st & 3) == 1 && (st >> 2) < kRCopies) rows_copy(next, st >> 2);
     }
     __builtin_amdgcn_sched_barrier(0);
+    return acc;
+  };
 
-    // O^T += V^T P^T: step st covers slots 16 st .. 16 st + 15 with k-slot (hi, i) <->
-    // slot 16 st + 8 (i / 4) + 4 hi + i % 4, i.e. score registers 8 st .. 8 st + 7.  MFMA i
-    // (0..31) is step i / 16, column block i % 16; its V^T operand is read kRVAhead MFMAs
-    // ahead (order pinned as for QK).
-    const uint8_t* vt = kt;  // V = the first 512 dims of the same rows
-    auto vread = [&](int i) -> bf16x8 {
-      const int st = i >> 4, cb = i & 15;
-      // rows 16 st + 8 uu + vr8 are in group 2 st + uu; chunk 4 cb + c2 is in block cb / 2
-      const int p0 = 16 * (vx ^ (4 * (cb & 1)) ^ (2 * st));
-      const int p1 = 16 * (vx ^ (4 * (cb & 1)) ^ (2 * st + 1));
-      const u16x4 lo = lds_read_tr16(vt + (2 * st) * kRGroupBytes + 1024 * (cb >> 1) + vbase + p0);
-      const u16x4 up = lds_read_tr16(vt + (2 * st + 1) * kRGroupBytes + 1024 * (cb >> 1) + vbase + p1);
-      return __builtin_bit_cast(bf16x8, u16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
-    };
-    constexpr int kRVAhead = 3;
-    // (the first V^T reads do not depend on the probabilities: issued before the softmax,
-    // they complete under it)
-    bf16x8 vw[kRVAhead];
-#pragma unroll
-    for (int i = 0; i < kRVAhead; ++i) vw[i] = vread(i);
-    __builtin_amdgcn_sched_barrier(0);
+  // O^T[cols 128 w + 32 cb ..][rows 32 rb ..] += V^T P^T of tile t, slot step st (slots
+  // 16 st .. 16 st + 15, k-slot (hi, i) <-> slot 16 st + 8 (i / 4) + 4 hi + i % 4): the V^T
+  // operand of this wave's column block cb, and the P^T operand of row block rb written by
+  // wave rb (its lanes' probabilities of those slots)
+  const int vcol0 = 4 * wave;  // this wave's first 32-column block
+  auto vread = [&](const uint8_t* vt, int st, int cb) -> bf16x8 {
+    const int cg = vcol0 + cb;
+    // rows 16 st + 8 uu + vr8 are in group 2 st + uu; chunk 4 cg + c2 is in block cg / 2
+    const int p0 = 16 * (vx ^ (4 * (cg & 1)) ^ (2 * st));
+    const int p1 = 16 * (vx ^ (4 * (cg & 1)) ^ (2 * st + 1));
+    const u16x4 lo = lds_read_tr16(vt + (2 * st) * kRGroupBytes + 1024 * (cg >> 1) + vbase + p0);
+    const u16x4 up = lds_read_tr16(vt + (2 * st + 1) * kRGroupBytes + 1024 * (cg >> 1) + vbase + p1);
+    return __builtin_bit_cast(bf16x8, u16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
+  };
 
-    // kScaled: the scales of slots 8 u + 4 hi .. + 3 (score registers 4 u .. 4 u + 3)
-    f32x4 ks[4];
-    if (kScaled) {
+  float m_ref = kNegInf;  // row r's reference (log2 units), equal in both halves
+  float l_run = 0.f;      // this lane's partial sum (its 16 slots of every tile)
+  bool over = false;
+  f32x16 o[4][4];         // o[cb][rb][j] = O^T[col 128 w + 32 cb + 8 (j / 4) + 4 hi + j % 4][row 32 rb + m]
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        ks[u] = *reinterpret_cast<const f32x4*>(&sbuf[kScaled ? t % kRStages : 0][u][4 * hi]);
-    }
-    float ml = kNegInf;
+  for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int kk = 8 * (j >> 2) + (j & 3);
-      const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)allowed, kk, 1);  // all ones if allowed
-      // (a scalar copy: bit casts of vector elements misread)
-      const float raw = kScaled ? sacc[j] * ks[j >> 2][j & 3] : sacc[j];
-      const float val = __builtin_bit_cast(float, (sel & __builtin_bit_cast(uint32_t, raw)) | (~sel & 0xff800000u));
-      sacc[j] = val;
-      ml = fmaxf(ml, val);
-    }
-    ml *= sc;
-    // a row's first valid scores set its reference (its O and l are still zero)
-    if (ballot(m_ref == kNegInf && ml != kNegInf) != 0) {
+    for (int rb = 0; rb < 4; ++rb) o[cb][rb] = f32x16{};
+
+  // The softmax of tile tn on its scores sacc, in pieces k = 0..kSmPieces - 1 that the PV
+  // MFMAs of the previous tile carry: masking (and the row scales), the reference, the
+  // probabilities, and their store to pbuf[tn % 2] for every wave.
+  constexpr int kSmPieces = 24;
+  constexpr int kSmLag = 4;
+  float sm_ml = kNegInf, sm_nm = 0.f;
+  bf16x8 bop[2];
+  auto sm_piece = [&](int k, int tn, f32x16& sacc, uint32_t allowed, const f32x4 (&ks)[4]) {
+    if (k < 4) {  // masking of scores 4 k .. 4 k + 3; the row max (raw units)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = 4 * k + jj;
+        const int kk = 8 * (j >> 2) + (j & 3);
+        const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)allowed, kk, 1);  // all ones if allowed
+        // (a scalar copy: bit casts of vector elements misread)
+        const float raw = kScaled ? sacc[j] * ks[j >> 2][j & 3] : sacc[j];
+        const float val = __builtin_bit_cast(float, (sel & __builtin_bit_cast(uint32_t, raw)) | (~sel & 0xff800000u));
+        sacc[j] = val;
+        sm_ml = fmaxf(sm_ml, val);
+      }
+    } else if (k == 4) {
+      // a row's first valid scores set its reference (its O and l are still zero); both halves
+      // of the row agree on it
+      const float ml = sm_ml * sc;
       const float mr = max_xor32(ml);
       m_ref = m_ref == kNegInf ? mr : m_ref;
-    }
-    over |= ballot(ml > m_ref + kRSlack) != 0;
-    const float nm = m_ref == kNegInf ? 0.f : -m_ref;
-    // probabilities of the first 16 slots (step 0); those of step 1 are computed between
-    // step 0's MFMAs, which do not need them
-    bf16x8 bop[2];
-    float l0 = 0.f, l1 = 0.f;
-    auto prob = [&](int j, float& l) {
-      const float p = fast_exp2(__builtin_fmaf(sacc[j], sc, nm));
-      l += p;
+      over |= ml > m_ref + kRSlack;
+      sm_nm = m_ref == kNegInf ? 0.f : -m_ref;
+      sm_ml = kNegInf;
+    } else if (k < 21) {  // probability of score k - 5 (times its row scale: the PV operand)
+      const int j = k - 5;
+      const float p = fast_exp2(__builtin_fmaf(sacc[j], sc, sm_nm));
+      l_run += p;
       bop[j >> 3][j & 7] = (__bf16)(kScaled ? p * ks[j >> 2][j & 3] : p);
-    };
-#pragma unroll
-    for (int j = 0; j < 8; ++j) prob(j, l0);
+    } else if (k < 23) {
+      pbuf[tn & 1][wave][k - 21][lane] = bop[k - 21];
+    }
+  };
 
+  // PV of tile t (V^T from stage t % 3, P^T from pbuf[t % 2]) carrying the softmax of tile
+  // t + 1, whose pieces start kSmLag MFMAs in (the scores come from written-out MFMAs whose
+  // latency the compiler does not see).  MFMA i: slot step st = i / 16, row block
+  // rb = (i / 4) % 4, column block cb = i % 4; the 4 V^T operands of a step are held through
+  // it (the next step's are read as these retire), P^T operands are read two row blocks ahead.
+  auto pv_sm = [&](int t, f32x16& sacc_n, uint32_t allowed_n, const f32x4 (&ks_n)[4], uint32_t& al_next,
+                   uint32_t& row_next) {
+    uint2 aw;
+    int2 rw;
+    const uint8_t* vt = &stage[0][0] + loop_local((t % kRStages) * kRStageBytes);
+    const bf16x8* pt = &pbuf[t & 1][0][0][0] + loop_local(lane);
+    auto pread = [&](int st, int rb) -> bf16x8 { return pt[(2 * rb + st) * 64]; };
+    bf16x8 va[4], pw[2];
 #pragma unroll
-    for (int i = 0; i < 2 * (kRDv / 32); ++i) {
+    for (int cb = 0; cb < 4; ++cb) va[cb] = vread(vt, 0, cb);
+    pw[0] = pread(0, 0);
+    pw[1] = pread(0, 1);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-      o[i & 15] = mfma32x32x16(vw[i % kRVAhead], bop[i >> 4], o[i & 15]);
-      if (i + kRVAhead < 2 * (kRDv / 32)) vw[i % kRVAhead] = vread(i + kRVAhead);
-      if (i < 8) prob(8 + i, l1);
+      const int st = i >> 4, rb = (i >> 2) & 3, cb = i & 3;
+      o[cb][rb] = mfma32x32x16(va[cb], pw[(i >> 2) & 1], o[cb][rb]);
+      if (st == 0 && rb == 3) va[cb] = vread(vt, 1, cb);          // this operand's last use in step 0
+      if (cb == 3 && i + 8 < 32) {                               // the P^T operand two row blocks on
+        const int ni = i + 5;
+        pw[(i >> 2) & 1] = pread(ni >> 4, (ni >> 2) & 3);
+      }
+      if (i == kSmLag) asm volatile("" : "+v"(sacc_n));  // (no read of the scores above this point)
+      // the next iteration's membership (tile t + 2) and copy sources (tile t + 3): their index
+      // words are read here and used 20 MFMAs later
+      if (i == 8) {
+        aw = allowed_read(t + 2);
+        rw = rows_read(t + 3);
+      }
+      if (i == 28) {
+        al_next = t + 2 < ntiles ? allowed_make(t + 2, aw) : 0u;  // (past the last tile: all masked)
+        if (t + 3 < ntiles) row_next = rows_make(t + 3, rw);
+      }
+      if (i >= kSmLag && i < kSmLag + kSmPieces) sm_piece(i - kSmLag, t + 1, sacc_n, allowed_n, ks_n);
     }
     __builtin_amdgcn_sched_barrier(0);
-    l_run += l0 + l1;
+  };
+
+  // ---- the pipeline ---------------------------------------------------------------------
+  // Iteration t: (wait + barrier) tile t + 1 and the probabilities of tile t are in LDS;
+  // copy tile t + 2 into the stage of tile t - 1; QK of tile t + 1; PV of tile t carrying the
+  // softmax of tile t + 1.  Stages in use: t (V), t + 1 (K), t + 2 (in flight).  A tile's
+  // index words arrive four tiles ahead of its QK (issued in iteration t - 4); the membership
+  // of tile t + 1 and the copy sources of tile t + 2 are made during the PV of iteration
+  // t - 1, so after the barrier only the copies go out before the QK.
+  uint32_t al_next = 0u;
+  uint32_t row_next = 0;
+  if (ntiles > 0) {
+    issue_idx(0);
+    if (ntiles > 1) issue_idx(1);
+    if (ntiles > 2) issue_idx(2);
+    if (ntiles > 3) issue_idx(3);
+    wait_vmcnt<0>();
+    issue_rows(0);
+    if (ntiles > 1) issue_rows(1);
+    if (ntiles > 2) row_next = rows_make(2, rows_read(2));
+    wait_vmcnt<0>();
+    __syncthreads();  // tile 0 and the index words of tiles 0 .. 3 visible to all waves
+    f32x4 ks0[4];
+    tile_scales(0, ks0);
+    const uint32_t al0 = tile_allowed(0);
+    if (ntiles > 1) al_next = tile_allowed(1);
+    f32x16 s0 = qk(0, std::false_type{}, 0u);
+    // wait states before the VALU reads the last score MFMA's results (the scores pass
+    // through the statement, so no read of them can be placed above it)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0));
+#pragma unroll
+    for (int k = 0; k < kSmPieces; ++k) sm_piece(k, 0, s0, al0, ks0);
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    wait_vmcnt<0>();  // tile t + 1, the scales of tile t + 2 and the indices of tile t + 3
+    __syncthreads();  // P(t) of every wave visible; stage (t + 2) % 3, pbuf (t + 1) % 2 and index
+                      // buffer t % 4 free
+    if (t + 4 < ntiles) issue_idx(t + 4);
+    const bool copy = t + 2 < ntiles;
+    const uint32_t next = row_next;  // tile t + 2's copy row (its blocks go out during the QK below)
+    const bool more = t + 1 < ntiles;
+    f32x4 ks[4];
+    tile_scales(more ? t + 1 : t, ks);
+    const uint32_t al = al_next;   // tile t + 1's membership (0 past the last tile: all masked)
+    f32x16 sn = {};
+    if (copy)
+      sn = qk(t + 1, std::true_type{}, next);
+    else if (more)
+      sn = qk(t + 1, std::false_type{}, next);
+    // (a VGPR-resident value for the softmax even past the last tile)
+    pv_sm(t, sn, al, ks, al_next, row_next);
   }
 
-  if (over && lane == 0) over_any = 1;
+  if (ballot(over) != 0 && lane == 0) over_any = 1;
+  const float l = sum_xor32(l_run);
+  if (hi == 0) lsum[r] = l;
   __syncthreads();
   const bool marked = over_any != 0;
-  const float l = sum_xor32(l_run);
-  if (!live) return;
   if (marked) {  // recomputed by the exact kernel
-    if (hi == 0) lse[(size_t)tok * H + rh] = __uint_as_float(kOverflowMark);
+    if (live && hi == 0) lse[(size_t)tok * H + rh] = __uint_as_float(kOverflowMark);
     return;
   }
-  // o[cb][j] = O^T[col 32 cb + 8 (j / 4) + 4 hi + j % 4][row r]
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  uint16_t* orow = out + ((size_t)tok * H + rh) * kRDv + 4 * hi;
+  if (live && hi == 0) lse[(size_t)tok * H + rh] = l > 0.f ? (m_ref + fast_log2(l)) * kLn2 : kNegInf;
+  // o[cb][rb][j] = O^T[col 128 w + 32 cb + 8 (j / 4) + 4 hi + j % 4][row 32 rb + m]
 #pragma unroll
-  for (int cb = 0; cb < kRDv / 32; ++cb)
+  for (int rb = 0; rb < 4; ++rb) {
+    const int row = 32 * rb + m;
+    const int i = row / H;
+    if (i >= ntok) continue;
+    const int h = row - i * H;
+    const float lr = lsum[row];
+    const float inv = lr > 0.f ? 1.f / lr : 0.f;
+    uint16_t* orow = out + ((size_t)(t0 + i) * H + h) * kRDv + 128 * wave + 4 * hi;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const bf16x4 w = {(__bf16)(o[cb][4 * jj + 0] * inv), (__bf16)(o[cb][4 * jj + 1] * inv),
-                        (__bf16)(o[cb][4 * jj + 2] * inv), (__bf16)(o[cb][4 * jj + 3] * inv)};
-      *reinterpret_cast<bf16x4*>(orow + 32 * cb + 8 * jj) = w;
-    }
-  if (hi == 0) lse[(size_t)tok * H + rh] = l > 0.f ? (m_ref + fast_log2(l)) * kLn2 : kNegInf;
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const bf16x4 w = {(__bf16)(o[cb][rb][4 * jj + 0] * inv), (__bf16)(o[cb][rb][4 * jj + 1] * inv),
+                          (__bf16)(o[cb][rb][4 * jj + 2] * inv), (__bf16)(o[cb][rb][4 * jj + 3] * inv)};
+        *reinterpret_cast<bf16x4*>(orow + 32 * cb + 8 * jj) = w;
+      }
+  }
 }
 
 template <int D, bool kPerToken, bool kScaled>

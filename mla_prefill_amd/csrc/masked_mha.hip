@@ -60,19 +60,9 @@ constexpr int kMKeys = 32;                            // keys per tile
 constexpr int kMStages = 4;
 constexpr float kMRefSlack = 64.f;                    // reference range: exponents up to 2^64
 
-// S^T accumulators stay in VGPRs (the softmax reads and masks them in place) while the
-// O^T accumulators take the accumulation registers: the QK MFMAs are written out so that
-// the compiler does not place their results in accumulation registers too.  Every VALU
-// access to their results comes at least one 16-MFMA chain later.
-__device__ __forceinline__ f32x16 mfma_qk_first(bf16x8 a, bf16x8 b) {
-  f32x16 d;
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
-  return d;
-}
-__device__ __forceinline__ f32x16 mfma_qk(bf16x8 a, bf16x8 b, f32x16 c) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
-  return c;
-}
+// (The QK MFMAs are written out -- mfma_qk_first / mfma_qk, common.h -- so that their S^T
+// accumulators stay in VGPRs while O^T takes the accumulation registers.  Every VALU access
+// to their results comes at least one 16-MFMA chain later.)
 
 // Geometry (kDN, kDR, kDV): the key is k_nope (kDN dims, per head) followed by k_pe (kDR
 // dims, shared by every head), the value kDV dims per head: (256, 0, 256) NoPE -- K is
