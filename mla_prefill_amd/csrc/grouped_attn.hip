@@ -91,6 +91,7 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   const int hi = lane >> 5, m = lane & 31;
   const int2 span = group_span(ginfo, grp, G, T);  // (a batch's groups come from its table)
   const int t0 = uniform(span.x), ntok = uniform(span.y);
+  if (ntok <= 0) return;  // (an empty group of a batch: nothing to write)
   const int r = 32 * wave + m;  // this lane's row
   const int ri = r / H;
   const int rh = r - ri * H;
@@ -98,29 +99,10 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   const bool live = ri < ntok;
   if (tid == 0) over_any = 0;  // ordered before any use by the loop's (or the final) barrier
 
-  // queries: row r, dims 16 s + 8 hi .. + 8; a negative scale is applied as |scale| on
-  // negated queries so that the reference can be taken on raw scores
+  // a negative scale is applied as |scale| on negated queries so that the reference can be
+  // taken on raw scores
   const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
   const float sc = fabsf(scale_log2);
-  // (steps kRQRegSteps.. go to a lane-private LDS area: the registers are needed to keep
-  // operand reads in flight)
-  bf16x8 qreg[kRQRegSteps];
-  {
-    const uint16_t* qrow = q + ((size_t)tok * H + rh) * D + 8 * hi;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      uint4 w = {0u, 0u, 0u, 0u};
-      if (live) w = *reinterpret_cast<const uint4*>(qrow + 16 * s);
-      w.x ^= qsign; w.y ^= qsign; w.z ^= qsign; w.w ^= qsign;
-      if (s < kRQRegSteps)
-        qreg[s] = __builtin_bit_cast(bf16x8, w);
-      else
-        qlds[wave][s - kRQRegSteps][lane] = w;
-    }
-  }
-  // complete the query loads now, before any asynchronous copy is in flight
-#pragma unroll
-  for (int s = 0; s < kRQRegSteps; ++s) asm volatile("" : : "v"(qreg[s]));
 
   int nkeys;
   if (kPerToken) {
@@ -142,18 +124,12 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   };
   // the row invalid slots copy (their P is 0): the list's first valid entry, a row the group
   // selects -- an unselected row (an unused slot of a paged cache) may hold anything, and 0
-  // times a NaN is NaN.  With no valid entry there is nothing to attend over.
+  // times a NaN is NaN.  With no valid entry there is nothing to attend over.  (The first
+  // 64 entries are loaded here, before the queries, and looked at after them.)
+  const int32_t x_first = lane < nkeys ? klist[lane] : -1;
   int dummy_row = -1;
-  for (int c0 = 0; c0 < nkeys; c0 += 64) {
-    const int32_t x = c0 + lane < nkeys ? klist[c0 + lane] : -1;
-    const uint64_t b = ballot(slot_ok(x, c0 + lane));
-    if (b != 0) {
-      dummy_row = __builtin_amdgcn_readlane(x, __builtin_ctzll(b));
-      break;
-    }
-  }
-  dummy_row = uniform(dummy_row);
-  const int ntiles = dummy_row < 0 ? 0 : (nkeys + kRKeys - 1) / kRKeys;
+  int ntiles = 0;  // (both set in the prologue below)
+  bf16x8 qreg[kRQRegSteps];  // the queries' register steps (loaded in the prologue)
 
   // the tokens of this wave's rows: 32 w / H and (32 w + 31) / H (two only for H = 16)
   const int ti0 = (32 * wave) / H, ti1 = (32 * wave + 31) / H;
@@ -415,6 +391,51 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // ---- the prologue ---------------------------------------------------------------------
+  // The index words of tiles 0 .. 3 travel with the list's first entries; once they have
+  // landed, the row copies of tiles 0 and 1 and the queries travel together.
+#pragma unroll
+  for (int t = 0; t < kRIdxBufs; ++t)
+    if (t * kRKeys < nkeys) issue_idx(t);
+  wait_vmcnt<0>();
+  {
+    const uint64_t b = ballot(slot_ok(x_first, lane));
+    if (b != 0) dummy_row = __builtin_amdgcn_readlane(x_first, __builtin_ctzll(b));
+  }
+  for (int c0 = 64; dummy_row < 0 && c0 < nkeys; c0 += 64) {
+    const int32_t x = c0 + lane < nkeys ? klist[c0 + lane] : -1;
+    const uint64_t b = ballot(slot_ok(x, c0 + lane));
+    if (b != 0) dummy_row = __builtin_amdgcn_readlane(x, __builtin_ctzll(b));
+  }
+  dummy_row = uniform(dummy_row);
+  ntiles = uniform(dummy_row < 0 ? 0 : (nkeys + kRKeys - 1) / kRKeys);
+  uint32_t al_next = 0u;
+  uint32_t row_next = 0;
+  if (ntiles > 0) {
+    issue_rows(0);
+    if (ntiles > 1) issue_rows(1);
+    if (ntiles > 2) row_next = rows_make(2, rows_read(2));
+  }
+  asm volatile("" ::: "memory");  // (the query loads below go out after the copies)
+  // queries: row r, dims 16 s + 8 hi .. + 8 (steps kRQRegSteps.. go to a lane-private LDS
+  // area: the registers are needed to keep operand reads in flight); a row past the group's
+  // tokens is zero
+  {
+    const uint16_t* qrow = q + ((size_t)tok * H + rh) * D + 8 * hi;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      uint4 w = {0u, 0u, 0u, 0u};
+      if (live) w = *reinterpret_cast<const uint4*>(qrow + 16 * s);
+      w.x ^= qsign; w.y ^= qsign; w.z ^= qsign; w.w ^= qsign;
+      if (s < kRQRegSteps)
+        qreg[s] = __builtin_bit_cast(bf16x8, w);
+      else
+        qlds[wave][s - kRQRegSteps][lane] = w;
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();  // tile 0 and the index words of tiles 0 .. 3 visible to all waves
+
   // ---- the pipeline ---------------------------------------------------------------------
   // Iteration t: (wait + barrier) tile t + 1 and the probabilities of tile t are in LDS;
   // copy tile t + 2 into the stage of tile t - 1; QK of tile t + 1; PV of tile t carrying the
@@ -422,19 +443,7 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   // index words arrive four tiles ahead of its QK (issued in iteration t - 4); the membership
   // of tile t + 1 and the copy sources of tile t + 2 are made during the PV of iteration
   // t - 1, so after the barrier only the copies go out before the QK.
-  uint32_t al_next = 0u;
-  uint32_t row_next = 0;
   if (ntiles > 0) {
-    issue_idx(0);
-    if (ntiles > 1) issue_idx(1);
-    if (ntiles > 2) issue_idx(2);
-    if (ntiles > 3) issue_idx(3);
-    wait_vmcnt<0>();
-    issue_rows(0);
-    if (ntiles > 1) issue_rows(1);
-    if (ntiles > 2) row_next = rows_make(2, rows_read(2));
-    wait_vmcnt<0>();
-    __syncthreads();  // tile 0 and the index words of tiles 0 .. 3 visible to all waves
     f32x4 ks0[4];
     tile_scales(0, ks0);
     const uint32_t al0 = tile_allowed(0);
@@ -476,24 +485,42 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
     return;
   }
   if (live && hi == 0) lse[(size_t)tok * H + rh] = l > 0.f ? (m_ref + fast_log2(l)) * kLn2 : kNegInf;
-  // o[cb][rb][j] = O^T[col 128 w + 32 cb + 8 (j / 4) + 4 hi + j % 4][row 32 rb + m]
+  // The output goes out through LDS (the stages are free after the barrier above): wave w
+  // turns its 128 columns of 64 rows at a time into rows of 256 contiguous bytes, so that each
+  // store instruction writes four such segments.  o[cb][rb][j] = O^T[col 128 w + 32 cb +
+  // 8 (j / 4) + 4 hi + j % 4][row 32 rb + m].
+  constexpr int kOPitch = 272;  // bytes per staged row (256 + 16: rows start on other banks)
+  static_assert(4 * 64 * kOPitch <= kRStages * kRStageBytes, "output staging fits the stages");
+  uint8_t* ost = &stage[0][0] + wave * 64 * kOPitch;
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const int row = 32 * rb + m;
-    const int i = row / H;
-    if (i >= ntok) continue;
-    const int h = row - i * H;
-    const float lr = lsum[row];
-    const float inv = lr > 0.f ? 1.f / lr : 0.f;
-    uint16_t* orow = out + ((size_t)(t0 + i) * H + h) * kRDv + 128 * wave + 4 * hi;
+  for (int half = 0; half < 2; ++half) {
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int rbl = 0; rbl < 2; ++rbl) {
+      const int rb = 2 * half + rbl;
+      const float lr = lsum[32 * rb + m];
+      const float inv = lr > 0.f ? 1.f / lr : 0.f;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const bf16x4 w = {(__bf16)(o[cb][rb][4 * jj + 0] * inv), (__bf16)(o[cb][rb][4 * jj + 1] * inv),
-                          (__bf16)(o[cb][rb][4 * jj + 2] * inv), (__bf16)(o[cb][rb][4 * jj + 3] * inv)};
-        *reinterpret_cast<bf16x4*>(orow + 32 * cb + 8 * jj) = w;
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const bf16x4 w = {(__bf16)(o[cb][rb][4 * jj + 0] * inv), (__bf16)(o[cb][rb][4 * jj + 1] * inv),
+                            (__bf16)(o[cb][rb][4 * jj + 2] * inv), (__bf16)(o[cb][rb][4 * jj + 3] * inv)};
+          *reinterpret_cast<bf16x4*>(ost + (32 * rbl + m) * kOPitch + 64 * cb + 16 * jj + 8 * hi) = w;
+        }
+    }
+    // (a wave's LDS accesses complete in order: these reads see the writes above, and the next
+    // half's writes come after these reads have returned their data to the stores)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int lr = 4 * k + (lane >> 4);
+      const int row = 64 * half + lr;
+      const int i = row / H;
+      const uint4 v = *reinterpret_cast<const uint4*>(ost + lr * kOPitch + 16 * (lane & 15));
+      if (i < ntok) {
+        const int h = row - i * H;
+        *reinterpret_cast<uint4*>(out + ((size_t)(t0 + i) * H + h) * kRDv + 128 * wave + 8 * (lane & 15)) = v;
       }
+    }
   }
 }
 
