@@ -173,7 +173,7 @@ def rounded(d):
 
 KERNEL_SYMBOLS = {  # bench kernel name -> (device symbol, sources)
     "build_union": ("dsa::build_union_kernel<false>", ["union_builder.hip", "common.h"]),
-    "grouped_attn": ("dsa::rows128_attn_kernel<576, false, false>", ["grouped_attn.hip", "common.h"]),
+    "grouped_attn": ("dsa::rows128_attn_kernel<576, false, false, true>", ["grouped_attn.hip", "common.h"]),
     "pertoken_attn": ("dsa::pertoken_sorted_kernel<576, false>", ["pertoken_attn.hip", "common.h"]),
     "masked_mha": ("dsa::masked_mha_kernel<256, 0, 256, false>", ["masked_mha.hip", "common.h"]),
 }

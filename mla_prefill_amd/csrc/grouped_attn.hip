@@ -60,7 +60,7 @@ constexpr int kRQRegSteps = 32;                     // query k-steps kept in reg
 
 // D: the latent width, 576 (512 + 64 rope dims) or 512 (no rope part); kScaled: the latent
 // rows carry scales (kscale[scale_per_row ? x : 0] for row x)
-template <int D, bool kPerToken, bool kScaled>
+template <int D, bool kPerToken, bool kScaled, bool kSmallKv>
 __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ keys, int64_t keys_ld, const int32_t* __restrict__ union_len,
@@ -153,9 +153,8 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
       src = klist + min(j0 + (lane & 7), ncols - 1);
     dma4(src, lds_addr(&idxw[t % kRIdxBufs][wave][0]));
   };
-  // (a latent below 2 GiB: every row offset fits 31 bits, and block c's copies take the
-  // uniform base kv + 128 c plus the lane's offset, with no 64-bit address arithmetic)
-  const bool small_kv = (int64_t)S * (2 * D) < ((int64_t)1 << 31);
+  // (kSmallKv, a latent below 2 GiB: every row offset fits 31 bits, and block c's copies take
+  // the uniform base kv + 128 c plus the lane's offset, with no 64-bit address arithmetic)
   const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv);
   // A tile's row copies: the source row of this lane's slot, resolved once (rows_make, which
   // also copies the slots' scales), its source and LDS destination (rows_src), then one
@@ -192,7 +191,7 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   // (the global address carries the block offset: an instruction offset would also move the
   // LDS destination of an LDS-DMA load)
   auto rows_copy = [&](const RowSrc& r, int c) {
-    if (small_kv)
+    if (kSmallKv)
       dma16_sbase(r.ofs, kvb + 128 * c, r.dst + 1024 * c);
     else
       dma16(r.src + 64 * c, r.dst + 1024 * c);
@@ -529,9 +528,14 @@ static void launch_rows128(int blocks, hipStream_t stream, const uint16_t* q, co
                            const int32_t* keys, int64_t keys_ld, const int32_t* union_len, const uint8_t* hgmask,
                            int T, int H, int S, int ncols, int64_t q_pos_offset, float scale, uint16_t* out,
                            float* lse, const int32_t* ginfo, const float* kscale, int scale_per_row) {
-  hipLaunchKernelGGL((rows128_attn_kernel<D, kPerToken, kScaled>), dim3(blocks), dim3(kRThreads), 0, stream, q,
-                     kv, keys, keys_ld, union_len, hgmask, T, H, S, ncols, q_pos_offset, scale * kLog2e, out, lse,
-                     ginfo, kscale, scale_per_row);
+  if ((int64_t)S * (2 * D) < ((int64_t)1 << 31))
+    hipLaunchKernelGGL((rows128_attn_kernel<D, kPerToken, kScaled, true>), dim3(blocks), dim3(kRThreads), 0, stream,
+                       q, kv, keys, keys_ld, union_len, hgmask, T, H, S, ncols, q_pos_offset, scale * kLog2e, out,
+                       lse, ginfo, kscale, scale_per_row);
+  else
+    hipLaunchKernelGGL((rows128_attn_kernel<D, kPerToken, kScaled, false>), dim3(blocks), dim3(kRThreads), 0,
+                       stream, q, kv, keys, keys_ld, union_len, hgmask, T, H, S, ncols, q_pos_offset,
+                       scale * kLog2e, out, lse, ginfo, kscale, scale_per_row);
 }
 
 template <bool kPerToken>

@@ -203,6 +203,37 @@ def test_pertoken_sorted_windows(R):
     check_attention(out, lse, ref_out, ref_lse, "per-token S=300000 windows")
 
 
+def test_latent_past_2gib(R):
+    """Both routings over a latent of 1.9 M rows (2.19 GB): row offsets past 2^31 bytes, where
+    the grouped kernel's copies take full 64-bit addresses.  Only the selected rows hold values
+    (the rest stay zero on the device); the oracle runs on those rows alone, renumbered in
+    order, which leaves every token's selection and therefore its attention unchanged."""
+    rng = np.random.default_rng(35)
+    T, S, H, k = 24, 1_900_000, 16, 96
+    P0 = S - T
+    limit = (1 << 31) // (576 * 2)                                  # first row past 2 GiB
+    topk = np.full((T, k + 4), -1, np.int32)
+    for t in range(T):
+        far = rng.choice(np.arange(limit, P0), 40, replace=False)
+        near = rng.choice(np.arange(0, limit), k - 40, replace=False)
+        row = np.concatenate([far, near])
+        topk[t, :k] = row[rng.permutation(k)]
+    rows = np.unique(topk[topk >= 0])
+    vals = normal_bf16(rng, (rows.size, 576))
+    q = normal_bf16(rng, (T, H, 576))
+    kv = torch.zeros((S, 576), dtype=torch.bfloat16, device="cuda")
+    kv[torch.from_numpy(rows.astype(np.int64)).cuda()] = dev_bf16(vals)
+    topk_c = np.where(topk >= 0, np.searchsorted(rows, topk), -1).astype(np.int32)
+    ref_out, ref_lse = oracle.pertoken_sparse_mqa(q, vals, topk_c, rows.size, rows.size, 0.0625)
+    qd, tk = dev_bf16(q), dev_i32(topk)
+    out, lse, _ = R.grouped(qd, kv, tk, P0, 0.0625)
+    check_attention(out, lse, ref_out, ref_lse, "grouped, latent past 2 GiB")
+    out, lse = R.pertoken(qd, kv, tk, P0, 0.0625)
+    check_attention(out, lse, ref_out, ref_lse, "per-token, latent past 2 GiB")
+    del kv
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("H", [48, 112])
 def test_pertoken_head_counts_without_grouped_form(R, H):
     """Head counts the per-token kernel takes (multiples of 16) but 128 / H is no group size."""
