@@ -341,6 +341,8 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
       const int j = k - 5;
       const float p = fast_exp2(__builtin_fmaf(sacc[j], sc, sm_nm));
       l_run += p;
+      asm volatile("" : "+v"(l_run));  // (the sum stays in its piece: sunk to the loop's end, the
+                                       // 16 dependent adds would stall the MFMAs there)
       bop[j >> 3][j & 7] = (__bf16)(kScaled ? p * ks[j >> 2][j & 3] : p);
     } else if (k < 23) {
       pbuf[tn & 1][wave][k - 21][lane] = bop[k - 21];
