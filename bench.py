@@ -376,7 +376,29 @@ def mqa_routings(case, stream):
                                                                    lse_p, stream=stream)),
     ]
     keep = (q, kv, topk, bufs, out_g, lse_g, out_p, lse_p)
-    return calls, bufs, keep
+    route = None
+    if cfg.H in (16, 32, 64):
+        # the library's union-size routing: union build, the decision, and the chosen form, in one call
+        bufs_a = routings.alloc_union(cfg.T, cfg.G, cfg.cols)
+        out_a, lse_a = routings.alloc_out(cfg.T, cfg.H, 512)
+        route = torch.zeros(4, dtype=torch.int32, device="cuda")
+        calls["auto"] = [
+            ("auto", lambda: _lib.dsa_sparse_prefill_auto(q, kv, topk, cfg.q_pos_offset, cfg.scale, bufs_a.union_idx,
+                                                          bufs_a.union_len, bufs_a.mask, route, out_a, lse_a,
+                                                          stream=stream)),
+        ]
+        keep = keep + (bufs_a, out_a, lse_a, route)
+    return calls, bufs, keep, route
+
+
+def auto_summary(samples, cfg_T, route, routings):
+    """The union-size routing of one configuration: its time per call and the form it ran."""
+    r = route.cpu().numpy()
+    ran = "per-token" if r[0] else "grouped"
+    ms = float(np.mean(samples))
+    return {"ms": ms, "median_ms": float(np.median(samples)), "min_ms": float(np.min(samples)),
+            "query_tokens_per_s": cfg_T / (ms * 1e-3), "ran": ran, "union_tiles": int(r[2]),
+            "overhead_ms": ms - routings[ran]["ms"]}
 
 
 def mha_routing(mcase, stream):
@@ -413,7 +435,9 @@ def measure_config(name, a, stream, want_cold=False):
     print(f"# [{name}] inputs generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
     mha_dv = mcase.cfg.dv if mcase is not None else 0
     chosen = _lib.dsa_select_routing(cfg.T, cfg.S, cfg.q_pos_offset, cfg.H, cfg.k, mha_dv)
-    calls, bufs, keep = mqa_routings(case, stream)
+    calls, bufs, keep, route = mqa_routings(case, stream)
+    if chosen == "grouped" and "auto" in calls:
+        chosen = "auto"  # the grouped form where the union is compact, else per-token (decided on the device)
     if mcase is not None:
         mcalls, mkeep = mha_routing(mcase, stream)
         calls["masked"] = mcalls
@@ -427,9 +451,12 @@ def measure_config(name, a, stream, want_cold=False):
     work, nsel = mqa_work(cfg, case.topk, union_len if union_len is not None else np.zeros(cfg.NG))
     if mcase is not None:
         work.update(mha_work(mcase.cfg))
-    cold = cold_times([c for cl in calls.values() for c in cl], stream) if want_cold and not a.no_cold else {}
+    cold = (cold_times([c for r, cl in calls.items() if r != "auto" for c in cl], stream)
+            if want_cold and not a.no_cold else {})
     routings = {}
     for r, cl in calls.items():
+        if r == "auto":
+            continue
         ks = {}
         for kname, _ in cl:
             bound, amount = work[kname]
@@ -438,6 +465,8 @@ def measure_config(name, a, stream, want_cold=False):
                 # the gathered rows per second: mostly served by L2 (see `traffic`), not an HBM figure
                 ks[kname]["gathered_gbs"] = work["pertoken_gather_bytes"] / (ks[kname]["ms"] * 1e-3) / 1e9
         routings[r] = routing_summary(mcase.cfg.T if r == "masked" else cfg.T, ks)
+    if "auto" in calls:
+        routings["auto"] = auto_summary(samples["auto"], cfg.T, route, routings)
     summary = {
         "config": {"name": name, "T": cfg.T, "S": cfg.S, "H": cfg.H, "k": cfg.k, "cols": cfg.cols, "G": cfg.G,
                    "q_pos_offset": cfg.q_pos_offset, "d_qk": cfg.d_qk, "topk": cfg.topk_mode,
@@ -450,7 +479,7 @@ def measure_config(name, a, stream, want_cold=False):
     if union_len is not None:
         summary["config"]["union_len_mean"] = float(np.mean(union_len))
         summary["config"]["union_len_max"] = int(np.max(union_len))
-    return summary, chosen, calls, keep, case
+    return summary, chosen, calls, keep, case, route
 
 
 def main():
@@ -494,23 +523,30 @@ def main():
         sys.exit(1)
     stream = torch.cuda.current_stream()
 
-    summary, chosen, calls, keep, case = measure_config(mqa_name, a, stream, want_cold=True)
+    summary, chosen, calls, keep, case, route = measure_config(mqa_name, a, stream, want_cold=True)
     cfg = case.cfg
-    step_calls = calls["grouped" if chosen == "grouped" else ("per-token" if chosen == "per-token" else "masked")]
+    step_calls = calls[chosen]
     # the timed steps: one layer by the chosen routing
     samples, ms_step = time_calls(step_calls, stream, a.steps, a.warmup)
     kernels = {}
-    step_routing = summary["routings"]["grouped" if chosen == "grouped" else
-                                       ("per-token" if chosen == "per-token" else "masked")]
-    for kname, _ in step_calls:
-        rec = dict(step_routing["kernels"][kname])
-        fresh = kernel_record(samples[kname], rec["bound"], rec["algorithmic"], rec.get("cold_ms"))
-        if "gathered_gbs" in rec:
-            fresh["gathered_gbs"] = rec["gathered_gbs"] * rec["ms"] / fresh["ms"]
-        kernels[kname] = fresh
+    if chosen == "auto":
+        # one call enqueues every kernel of the step: its per-kernel records are those of the
+        # form it ran, timed kernel by kernel above
+        ran = summary["routings"]["auto"]["ran"]
+        kernels = {k: dict(v) for k, v in summary["routings"][ran]["kernels"].items()}
+        kernels["auto"] = {"ms": float(np.mean(samples["auto"])), "median_ms": float(np.median(samples["auto"])),
+                           "min_ms": float(np.min(samples["auto"])), "ran": ran}
+    else:
+        step_routing = summary["routings"][chosen]
+        for kname, _ in step_calls:
+            rec = dict(step_routing["kernels"][kname])
+            fresh = kernel_record(samples[kname], rec["bound"], rec["algorithmic"], rec.get("cold_ms"))
+            if "gathered_gbs" in rec:
+                fresh["gathered_gbs"] = rec["gathered_gbs"] * rec["ms"] / fresh["ms"]
+            kernels[kname] = fresh
     del keep
     torch.cuda.empty_cache()
-    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+    dom = max((k for k in kernels if k != "auto"), key=lambda k: kernels[k]["ms"])
     d = kernels[dom]
     traffic = measured_traffic(dom, a.workload)
     roofline = {"kernel": dom, "bound": d["bound"], "achieved": round(d["achieved"], 2), "peak": d["peak"],

@@ -163,6 +163,31 @@ int dsa_sparse_prefill_grouped(const uint16_t* q, const uint16_t* kv, const int3
                                int H, int S, int union_pad, int d_qk, int d_v, float scale,
                                uint16_t* out, float* lse, void* stream);
 
+/* Sparse MQA prefill with the routing chosen on the device from the union's
+ * size (grouped and per-token forms as above; both compute per-token attention,
+ * "[Perf][DSA] Grouped sparse prefill ...", "How" section).  The union and
+ * membership mask of every group of G = 128 / H tokens are built; then one
+ * workgroup sums the grouped form's tiles, ceil(union_len / 32) over the groups,
+ * and compares them with the per-token form's cost in the same unit,
+ * rho(H) * sum_t min(cols, S, q_pos_offset + t + 1) / 32 with rho = 0.20, 0.41,
+ * 0.88 for H = 16, 32, 64 (measured on MI355X for this library's kernels).
+ * Both attention launches are enqueued; the one not chosen returns at once.
+ *
+ *   q, kv, topk, ld, T, H, S, cols, q_pos_offset, d_qk, d_v, scale, out, lse:
+ *             as for dsa_sparse_prefill_pertoken; H must be 16, 32 or 64
+ *   union_pad, union_idx, union_len, head_group_mask: the union workspace, as
+ *             for dsa_build_group_union with G = 128 / H (overwritten)
+ *   route     int32 [4] device workspace (overwritten, 4-byte aligned): after
+ *             the call route[0] = 1 if the per-token form ran (grouped
+ *             skipped), route[1] = 1 if the grouped form ran, route[2] = the
+ *             union's tile count (saturated at 2^31 - 1); route[3] is unused
+ * Errors as for the grouped and per-token calls; DSA_ERR_UNSUPPORTED for another H.
+ * The result equals either form's (within its rounding). */
+int dsa_sparse_prefill_auto(const uint16_t* q, const uint16_t* kv, const int32_t* topk, int64_t ld, int T,
+                            int H, int S, int cols, int64_t q_pos_offset, int d_qk, int d_v, float scale,
+                            int union_pad, int32_t* union_idx, int32_t* union_len, uint8_t* head_group_mask,
+                            int32_t* route, uint16_t* out, float* lse, void* stream);
+
 /* Per-token sparse MQA ("[Perf][GLM-5.3-Flash] ...", Purpose section): token t
  * attends, for each head, over the latent rows it selects from its own top-k
  * row (selection rule above), gathering them itself.

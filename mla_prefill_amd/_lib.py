@@ -36,6 +36,8 @@ _SIGNATURES = {
                                     _vp, _vp, _vp], _i32),
     "dsa_sparse_prefill_pertoken": ([_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _f32,
                                      _vp, _vp, _vp], _i32),
+    "dsa_sparse_prefill_auto": ([_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _f32, _i32,
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
     "dsa_masked_mha_prefill": ([_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                 _i64, _f32, _vp, _vp, _vp, _vp], _i32),
     "dsa_masked_mha_prefill_noalloc": ([_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -170,6 +172,17 @@ def dsa_sparse_prefill_pertoken(q, kv, topk, q_pos_offset, scale, out, lse, cols
     _check("dsa_sparse_prefill_pertoken", lib.dsa_sparse_prefill_pertoken(
         _ptr(_bits(q)), _ptr(_bits(kv)), _ptr(topk), _topk_ld(topk), T, H, S, cols, q_pos_offset,
         d_qk, out.shape[2], scale, _ptr(_bits(out)), _ptr(lse), _stream(stream)))
+
+
+def dsa_sparse_prefill_auto(q, kv, topk, q_pos_offset, scale, union_idx, union_len, head_group_mask, route, out,
+                            lse, cols=None, stream=None):
+    T, H, d_qk = q.shape
+    S = kv.shape[0]
+    cols = topk.shape[1] if cols is None else cols
+    _check("dsa_sparse_prefill_auto", lib.dsa_sparse_prefill_auto(
+        _ptr(_bits(q)), _ptr(_bits(kv)), _ptr(topk), _topk_ld(topk), T, H, S, cols, q_pos_offset, d_qk,
+        out.shape[2], scale, union_idx.shape[1], _ptr(union_idx), _ptr(union_len), _ptr(head_group_mask),
+        _ptr(route), _ptr(_bits(out)), _ptr(lse), _stream(stream)))
 
 
 def dsa_masked_mha_prefill(q, k_nope, k_pe, v, topk, q_pos_offset, scale, mask_ws, out, lse,

@@ -207,6 +207,48 @@ int dsa_sparse_prefill_pertoken(const uint16_t* q, const uint16_t* kv, const int
                                        (hipStream_t)stream));
 }
 
+// per-token cost of the grouped form's 128-row tiles, per 32 selections (measured on MI355X
+// with this library's kernels, 576-wide latent, 16k-token chunks, locality and uniform top-k)
+static double route_rho(int H) { return H == 16 ? 0.20 : (H == 32 ? 0.41 : 0.88); }
+
+// sum over the chunk of min(cols, S, p_t + 1), p_t = q_pos_offset + t: the selections a
+// token can make (an upper bound when rows hold -1 or out-of-range entries)
+static double selections_bound(int T, int S, int64_t q_pos_offset, int cols) {
+  const double c = (double)(cols < S ? cols : S);
+  const double p1 = (double)q_pos_offset + 1.0;                  // p_0 + 1
+  const double n1 = fmin((double)T, fmax(0.0, c - p1));           // tokens below the cap
+  return n1 * p1 + n1 * (n1 - 1.0) / 2.0 + ((double)T - n1) * c;
+}
+
+int dsa_sparse_prefill_auto(const uint16_t* q, const uint16_t* kv, const int32_t* topk, int64_t ld, int T,
+                            int H, int S, int cols, int64_t q_pos_offset, int d_qk, int d_v, float scale,
+                            int union_pad, int32_t* union_idx, int32_t* union_len, uint8_t* head_group_mask,
+                            int32_t* route, uint16_t* out, float* lse, void* stream) {
+  if (H != 16 && H != 32 && H != 64) return DSA_ERR_UNSUPPORTED;
+  const int G = 128 / H;
+  int st = pertoken_check(q, kv, topk, ld, T, H, S, cols, q_pos_offset, d_qk, d_v, scale, out, lse);
+  if (st != DSA_OK) return st == kNothingToDo ? DSA_OK : st;
+  st = grouped_check(q, kv, union_idx, union_len, head_group_mask, T, H, S, union_pad, d_qk, d_v, scale, out,
+                     lse);
+  if (st != DSA_OK) return st;
+  if (union_pad % 64 != 0 || (long long)union_pad < (long long)G * cols) return DSA_ERR_SHAPE;
+  if (!route) return DSA_ERR_NULL;
+  if (!aligned_to(route, 4)) return DSA_ERR_ALIGN;
+  const hipStream_t s = (hipStream_t)stream;
+  const int NG = (T + G - 1) / G;
+  const double limit = route_rho(H) * selections_bound(T, S, q_pos_offset, cols) / 32.0;
+  hipError_t e = dsa::launch_build_union(topk, ld, T, cols, S, q_pos_offset, G, union_pad, union_idx, union_len,
+                                         head_group_mask, s);
+  if (e == hipSuccess) e = dsa::launch_route_by_union(union_len, NG, union_pad, limit, route, s);
+  if (e == hipSuccess)
+    e = dsa::launch_grouped_attn(q, kv, union_idx, union_len, head_group_mask, T, H, S, union_pad, scale, out,
+                                 lse, s, nullptr, 0, d_qk, nullptr, 0, route);
+  if (e == hipSuccess)
+    e = dsa::launch_pertoken_attn(q, kv, topk, ld, T, H, S, cols, q_pos_offset, scale, out, lse, s, d_qk, nullptr,
+                                  0, route + 1);
+  return launch_status(e);
+}
+
 int dsa_decode_latent_fp8(const uint8_t* kv8, int S, int d, uint16_t* out, void* stream) {
   if (d != 576 && d != 512) return DSA_ERR_UNSUPPORTED;
   if (S < 0) return DSA_ERR_SHAPE;

@@ -66,8 +66,10 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
     const int32_t* __restrict__ keys, int64_t keys_ld, const int32_t* __restrict__ union_len,
     const uint8_t* __restrict__ hgmask, int T, int H, int S, int ncols, int64_t q_pos_offset,
     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
-    const int32_t* __restrict__ ginfo, const float* __restrict__ kscale, int scale_per_row) {
+    const int32_t* __restrict__ ginfo, const float* __restrict__ kscale, int scale_per_row,
+    const int32_t* __restrict__ skip) {
   static_assert(D == 576 || D == 512, "latent widths");
+  if (skip != nullptr && uniform(*skip) != 0) return;  // (another routing was chosen on the device)
   constexpr int kRGroupBytes = 8 * D * 2;           // one 8-row group (9216 / 8192)
   constexpr int kRStageBytes = 4 * kRGroupBytes;    // one 32-slot tile
   constexpr int kRCopies = kRGroupBytes / 1024;     // row copies per wave per tile (9 / 8)
@@ -529,15 +531,16 @@ template <int D, bool kPerToken, bool kScaled>
 static void launch_rows128(int blocks, hipStream_t stream, const uint16_t* q, const uint16_t* kv,
                            const int32_t* keys, int64_t keys_ld, const int32_t* union_len, const uint8_t* hgmask,
                            int T, int H, int S, int ncols, int64_t q_pos_offset, float scale, uint16_t* out,
-                           float* lse, const int32_t* ginfo, const float* kscale, int scale_per_row) {
+                           float* lse, const int32_t* ginfo, const float* kscale, int scale_per_row,
+                           const int32_t* skip) {
   if ((int64_t)S * (2 * D) < ((int64_t)1 << 31))
     hipLaunchKernelGGL((rows128_attn_kernel<D, kPerToken, kScaled, true>), dim3(blocks), dim3(kRThreads), 0, stream,
                        q, kv, keys, keys_ld, union_len, hgmask, T, H, S, ncols, q_pos_offset, scale * kLog2e, out,
-                       lse, ginfo, kscale, scale_per_row);
+                       lse, ginfo, kscale, scale_per_row, skip);
   else
     hipLaunchKernelGGL((rows128_attn_kernel<D, kPerToken, kScaled, false>), dim3(blocks), dim3(kRThreads), 0,
                        stream, q, kv, keys, keys_ld, union_len, hgmask, T, H, S, ncols, q_pos_offset,
-                       scale * kLog2e, out, lse, ginfo, kscale, scale_per_row);
+                       scale * kLog2e, out, lse, ginfo, kscale, scale_per_row, skip);
 }
 
 template <bool kPerToken>
@@ -545,21 +548,21 @@ static void launch_rows128_any(int d_qk, int blocks, hipStream_t stream, const u
                                const int32_t* keys, int64_t keys_ld, const int32_t* union_len,
                                const uint8_t* hgmask, int T, int H, int S, int ncols, int64_t q_pos_offset,
                                float scale, uint16_t* out, float* lse, const int32_t* ginfo, const float* kscale,
-                               int scale_per_row) {
+                               int scale_per_row, const int32_t* skip = nullptr) {
   if (d_qk == 512) {
     if (kscale)
       launch_rows128<512, kPerToken, true>(blocks, stream, q, kv, keys, keys_ld, union_len, hgmask, T, H, S, ncols,
-                                           q_pos_offset, scale, out, lse, ginfo, kscale, scale_per_row);
+                                           q_pos_offset, scale, out, lse, ginfo, kscale, scale_per_row, skip);
     else
       launch_rows128<512, kPerToken, false>(blocks, stream, q, kv, keys, keys_ld, union_len, hgmask, T, H, S,
-                                            ncols, q_pos_offset, scale, out, lse, ginfo, kscale, scale_per_row);
+                                            ncols, q_pos_offset, scale, out, lse, ginfo, kscale, scale_per_row, skip);
   } else {
     if (kscale)
       launch_rows128<576, kPerToken, true>(blocks, stream, q, kv, keys, keys_ld, union_len, hgmask, T, H, S, ncols,
-                                           q_pos_offset, scale, out, lse, ginfo, kscale, scale_per_row);
+                                           q_pos_offset, scale, out, lse, ginfo, kscale, scale_per_row, skip);
     else
       launch_rows128<576, kPerToken, false>(blocks, stream, q, kv, keys, keys_ld, union_len, hgmask, T, H, S,
-                                            ncols, q_pos_offset, scale, out, lse, ginfo, kscale, scale_per_row);
+                                            ncols, q_pos_offset, scale, out, lse, ginfo, kscale, scale_per_row, skip);
   }
 }
 
@@ -567,17 +570,17 @@ hipError_t launch_grouped_attn(const uint16_t* q, const uint16_t* kv, const int3
                                const int32_t* union_len, const uint8_t* head_group_mask, int T,
                                int H, int S, int union_pad, float scale, uint16_t* out, float* lse,
                                hipStream_t stream, const int32_t* group_info, int max_groups, int d_qk,
-                               const float* kscale, int scale_per_row) {
+                               const float* kscale, int scale_per_row, const int32_t* skip) {
   const int G = 128 / H;
   const int NG = group_info ? max_groups : (T + G - 1) / G;
   if (NG == 0) return hipSuccess;
   launch_rows128_any<false>(d_qk, NG, stream, q, kv, union_idx, (int64_t)union_pad, union_len, head_group_mask,
-                            T, H, S, union_pad, 0, scale, out, lse, group_info, kscale, scale_per_row);
+                            T, H, S, union_pad, 0, scale, out, lse, group_info, kscale, scale_per_row, skip);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_rows128_exact(q, kv, union_idx, (int64_t)union_pad, union_len, head_group_mask, T, H,
                               S, union_pad, 0, scale, out, lse, stream, group_info, NG, d_qk, kscale,
-                              scale_per_row);
+                              scale_per_row, skip);
 }
 
 hipError_t launch_pertoken_rows128(const uint16_t* q, const uint16_t* kv, const int32_t* topk,

@@ -36,11 +36,18 @@ hipError_t launch_scatter_topk_bits(const int32_t* topk, int64_t ld, int T, int 
 // latent decoded exactly to bf16): the kernels scale each key's raw score and each
 // probability before the PV product by it.
 
+// `skip` (optional, device): when *skip != 0 at run time the attention kernels return at
+// once -- the routing chosen on the device by launch_route_by_union (route[0] gates the
+// grouped kernels, route[1] the per-token kernel).
+hipError_t launch_route_by_union(const int32_t* union_len, int NG, int union_pad, double limit, int32_t* route,
+                                 hipStream_t stream);
+
 // per-token sparse MQA for H % 16 == 0 (one workgroup per (token, 16-head block))
 hipError_t launch_pertoken_attn(const uint16_t* q, const uint16_t* kv, const int32_t* topk,
                                 int64_t ld, int T, int H, int S, int cols, int64_t q_pos_offset,
                                 float scale, uint16_t* out, float* lse, hipStream_t stream, int d_qk,
-                                const float* kscale = nullptr, int scale_per_row = 0);
+                                const float* kscale = nullptr, int scale_per_row = 0,
+                                const int32_t* skip = nullptr);
 
 // 128-row attention over a per-workgroup key list.  Grouped mode: rows are the
 // 128 pseudo-heads of a group, keys the group's union list, and each row is
@@ -51,7 +58,8 @@ hipError_t launch_grouped_attn(const uint16_t* q, const uint16_t* kv, const int3
                                const int32_t* union_len, const uint8_t* head_group_mask, int T,
                                int H, int S, int union_pad, float scale, uint16_t* out, float* lse,
                                hipStream_t stream, const int32_t* group_info, int max_groups, int d_qk,
-                               const float* kscale = nullptr, int scale_per_row = 0);
+                               const float* kscale = nullptr, int scale_per_row = 0,
+                               const int32_t* skip = nullptr);
 hipError_t launch_pertoken_rows128(const uint16_t* q, const uint16_t* kv, const int32_t* topk,
                                    int64_t ld, int T, int S, int cols, int64_t q_pos_offset,
                                    float scale, uint16_t* out, float* lse, hipStream_t stream, int d_qk,
@@ -67,7 +75,8 @@ hipError_t launch_rows128_exact(const uint16_t* q, const uint16_t* kv, const int
                                 int64_t keys_ld, const int32_t* union_len, const uint8_t* hgmask,
                                 int T, int H, int S, int ncols, int64_t q_pos_offset, float scale,
                                 uint16_t* out, float* lse, hipStream_t stream, const int32_t* group_info,
-                                int ngroups, int d_qk, const float* kscale, int scale_per_row);
+                                int ngroups, int d_qk, const float* kscale, int scale_per_row,
+                                const int32_t* skip = nullptr);
 
 // FP8 (OCP E4M3) codes -> the bf16 numbers they encode (exact; no scale applied); rows x d
 // codes, d a multiple of 16

@@ -489,7 +489,8 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ topk, int64_t ld, int T, int H, int S, int cols,
     int64_t q_pos_offset, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
-    const float* __restrict__ kscale, int per_row) {
+    const float* __restrict__ kscale, int per_row, const int32_t* __restrict__ skip) {
+  if (skip != nullptr && uniform(*skip) != 0) return;  // (another routing was chosen on the device)
   const int nb = H >> 4;
   const int item = xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
   const int tq = item / nb;
@@ -775,7 +776,8 @@ __global__ __launch_bounds__(64) void pertoken_sorted_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ topk, int64_t ld, int T, int H, int S, int cols,
     int64_t q_pos_offset, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
-    const float* __restrict__ kscale, int per_row) {
+    const float* __restrict__ kscale, int per_row, const int32_t* __restrict__ skip) {
+  if (skip != nullptr && uniform(*skip) != 0) return;  // (another routing was chosen on the device)
   const int nb = H >> 4;
   const int item = xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
   const int tq = item / nb;
@@ -883,35 +885,36 @@ __global__ __launch_bounds__(64) void pertoken_sorted_kernel(
 template <int D, bool kScaled>
 static void launch_pertoken(const uint16_t* q, const uint16_t* kv, const int32_t* topk, int64_t ld, int T,
                             int H, int S, int cols, int64_t q_pos_offset, float scale, uint16_t* out,
-                            float* lse, hipStream_t stream, const float* kscale, int per_row) {
+                            float* lse, hipStream_t stream, const float* kscale, int per_row,
+                            const int32_t* skip) {
   const long long items = (long long)T * (H / 16);
   if (S <= kPSortRows)
     hipLaunchKernelGGL((pertoken_sorted_kernel<D, kScaled>), dim3((unsigned)items), dim3(64), 0, stream, q, kv,
-                       topk, ld, T, H, S, cols, q_pos_offset, scale * kLog2e, out, lse, kscale, per_row);
+                       topk, ld, T, H, S, cols, q_pos_offset, scale * kLog2e, out, lse, kscale, per_row, skip);
   else
     hipLaunchKernelGGL((pertoken_attn_kernel<D, kScaled>), dim3((unsigned)items), dim3(64), 0, stream, q, kv,
-                       topk, ld, T, H, S, cols, q_pos_offset, scale * kLog2e, out, lse, kscale, per_row);
+                       topk, ld, T, H, S, cols, q_pos_offset, scale * kLog2e, out, lse, kscale, per_row, skip);
 }
 
 hipError_t launch_pertoken_attn(const uint16_t* q, const uint16_t* kv, const int32_t* topk,
                                 int64_t ld, int T, int H, int S, int cols, int64_t q_pos_offset,
                                 float scale, uint16_t* out, float* lse, hipStream_t stream, int d_qk,
-                                const float* kscale, int per_row) {
+                                const float* kscale, int per_row, const int32_t* skip) {
   if ((long long)T * (H / 16) == 0) return hipSuccess;
   if (d_qk == 512) {
     if (kscale)
       launch_pertoken<512, true>(q, kv, topk, ld, T, H, S, cols, q_pos_offset, scale, out, lse, stream, kscale,
-                                 per_row);
+                                 per_row, skip);
     else
       launch_pertoken<512, false>(q, kv, topk, ld, T, H, S, cols, q_pos_offset, scale, out, lse, stream, kscale,
-                                  per_row);
+                                  per_row, skip);
   } else {
     if (kscale)
       launch_pertoken<576, true>(q, kv, topk, ld, T, H, S, cols, q_pos_offset, scale, out, lse, stream, kscale,
-                                 per_row);
+                                 per_row, skip);
     else
       launch_pertoken<576, false>(q, kv, topk, ld, T, H, S, cols, q_pos_offset, scale, out, lse, stream, kscale,
-                                  per_row);
+                                  per_row, skip);
   }
   return hipGetLastError();
 }

@@ -44,7 +44,8 @@ __global__ __launch_bounds__(kGThreads) void rows128_exact_kernel(
     const int32_t* __restrict__ keys, int64_t keys_ld, const int32_t* __restrict__ union_len,
     const uint8_t* __restrict__ hgmask, int T, int H, int S, int ncols, int64_t q_pos_offset,
     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
-    const int32_t* __restrict__ ginfo, const float* __restrict__ kscale, int scale_per_row) {
+    const int32_t* __restrict__ ginfo, const float* __restrict__ kscale, int scale_per_row,
+    const int32_t* __restrict__ skip) {
   static_assert(D == 576 || D == 512, "latent widths");
   constexpr int kGRowBytes = D * 2 + 16;                          // D / 8 data chunks + 1 pad chunk
   constexpr int kGSlots = kGRowBytes / 16;                        // 73 / 65
@@ -67,7 +68,9 @@ __global__ __launch_bounds__(kGThreads) void rows128_exact_kernel(
   const int t0 = uniform(span.x), ntok = uniform(span.y);
   // only groups the fast kernel marked are recomputed (the mark sits in the LSE of the
   // group's first row)
-  if (ntok <= 0 || __float_as_uint(lse[(size_t)t0 * H]) != kOverflowMark) return;
+  if (ntok <= 0 || (skip != nullptr && uniform(*skip) != 0) ||
+      __float_as_uint(lse[(size_t)t0 * H]) != kOverflowMark)
+    return;
 
   // the row this lane's wave owns for QK^T / softmax
   const int r_own = 16 * wave + n;
@@ -344,10 +347,10 @@ template <int D, bool kPerToken, bool kScaled>
 static void launch_exact(int blocks, hipStream_t stream, const uint16_t* q, const uint16_t* kv, const int32_t* keys,
                          int64_t keys_ld, const int32_t* union_len, const uint8_t* hgmask, int T, int H, int S,
                          int ncols, int64_t q_pos_offset, float sl, uint16_t* out, float* lse,
-                         const int32_t* ginfo, const float* kscale, int scale_per_row) {
+                         const int32_t* ginfo, const float* kscale, int scale_per_row, const int32_t* skip) {
   hipLaunchKernelGGL((rows128_exact_kernel<D, kPerToken, kScaled>), dim3(blocks), dim3(kGThreads), 0, stream, q, kv,
                      keys, keys_ld, union_len, hgmask, T, H, S, ncols, q_pos_offset, sl, out, lse, ginfo, kscale,
-                     scale_per_row);
+                     scale_per_row, skip);
 }
 
 template <int D, bool kPerToken>
@@ -355,37 +358,38 @@ static void launch_exact_scaled(int blocks, hipStream_t stream, const uint16_t* 
                                 const int32_t* keys, int64_t keys_ld, const int32_t* union_len,
                                 const uint8_t* hgmask, int T, int H, int S, int ncols, int64_t q_pos_offset,
                                 float sl, uint16_t* out, float* lse, const int32_t* ginfo, const float* kscale,
-                                int scale_per_row) {
+                                int scale_per_row, const int32_t* skip) {
   if (kscale)
     launch_exact<D, kPerToken, true>(blocks, stream, q, kv, keys, keys_ld, union_len, hgmask, T, H, S, ncols,
-                                     q_pos_offset, sl, out, lse, ginfo, kscale, scale_per_row);
+                                     q_pos_offset, sl, out, lse, ginfo, kscale, scale_per_row, skip);
   else
     launch_exact<D, kPerToken, false>(blocks, stream, q, kv, keys, keys_ld, union_len, hgmask, T, H, S, ncols,
-                                      q_pos_offset, sl, out, lse, ginfo, kscale, scale_per_row);
+                                      q_pos_offset, sl, out, lse, ginfo, kscale, scale_per_row, skip);
 }
 
 hipError_t launch_rows128_exact(const uint16_t* q, const uint16_t* kv, const int32_t* keys,
                                 int64_t keys_ld, const int32_t* union_len, const uint8_t* hgmask,
                                 int T, int H, int S, int ncols, int64_t q_pos_offset, float scale,
                                 uint16_t* out, float* lse, hipStream_t stream, const int32_t* group_info,
-                                int ngroups, int d_qk, const float* kscale, int scale_per_row) {
+                                int ngroups, int d_qk, const float* kscale, int scale_per_row,
+                                const int32_t* skip) {
   const int NG = ngroups;
   if (NG == 0) return hipSuccess;
   const float sl = scale * kLog2e;
   if (d_qk == 512) {
     if (hgmask != nullptr)
       launch_exact_scaled<512, false>(NG, stream, q, kv, keys, keys_ld, union_len, hgmask, T, H, S, ncols,
-                                      q_pos_offset, sl, out, lse, group_info, kscale, scale_per_row);
+                                      q_pos_offset, sl, out, lse, group_info, kscale, scale_per_row, skip);
     else
       launch_exact_scaled<512, true>(NG, stream, q, kv, keys, keys_ld, union_len, hgmask, T, H, S, ncols,
-                                     q_pos_offset, sl, out, lse, group_info, kscale, scale_per_row);
+                                     q_pos_offset, sl, out, lse, group_info, kscale, scale_per_row, skip);
   } else {
     if (hgmask != nullptr)
       launch_exact_scaled<576, false>(NG, stream, q, kv, keys, keys_ld, union_len, hgmask, T, H, S, ncols,
-                                      q_pos_offset, sl, out, lse, group_info, kscale, scale_per_row);
+                                      q_pos_offset, sl, out, lse, group_info, kscale, scale_per_row, skip);
     else
       launch_exact_scaled<576, true>(NG, stream, q, kv, keys, keys_ld, union_len, hgmask, T, H, S, ncols,
-                                     q_pos_offset, sl, out, lse, group_info, kscale, scale_per_row);
+                                     q_pos_offset, sl, out, lse, group_info, kscale, scale_per_row, skip);
   }
   return hipGetLastError();
 }

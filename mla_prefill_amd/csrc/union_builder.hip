@@ -319,6 +319,43 @@ hipError_t launch_convert_req_index(const int32_t* topk, int64_t ld, int T, int 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Routing by the union's size.  The grouped form costs about one 128-row tile per 32 union
+// slots of a group; the per-token form about rho(H) such tiles per 32 selections of a
+// token.  With the union built, one workgroup sums ceil(union_len / 32) over the groups and
+// writes route[0] = 1 (skip the grouped kernels) when the sum exceeds `limit` (the per-token
+// cost in the same tiles), else route[1] = 1 (skip the per-token kernel); route[2] = the
+// union tiles (saturated at 2^31 - 1).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void route_by_union_kernel(const int32_t* __restrict__ union_len, int NG,
+                                                             int union_pad, double limit, int32_t* route) {
+  __shared__ long long part[256];
+  long long s = 0;
+  for (int g = threadIdx.x; g < NG; g += 256) {
+    const int u = min(max(union_len[g], 0), union_pad);
+    s += (u + 31) / 32;
+  }
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const long long tiles = part[0];
+    const bool grouped = (double)tiles <= limit;
+    route[0] = grouped ? 0 : 1;
+    route[1] = grouped ? 1 : 0;
+    route[2] = (int32_t)min(tiles, (long long)INT32_MAX);
+  }
+}
+
+hipError_t launch_route_by_union(const int32_t* union_len, int NG, int union_pad, double limit, int32_t* route,
+                                 hipStream_t stream) {
+  hipLaunchKernelGGL(route_by_union_kernel, dim3(1), dim3(256), 0, stream, union_len, NG, union_pad, limit, route);
+  return hipGetLastError();
+}
+
 hipError_t launch_scatter_topk_bits(const int32_t* topk, int64_t ld, int T, int cols, int S,
                                     int64_t q_pos_offset, uint32_t* bits, int words,
                                     hipStream_t stream) {

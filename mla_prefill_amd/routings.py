@@ -55,6 +55,21 @@ def grouped(q, kv, topk, q_pos_offset: int, scale: float, bufs: UnionBuffers | N
     return out, lse, bufs
 
 
+def auto(q, kv, topk, q_pos_offset: int, scale: float, bufs: UnionBuffers | None = None, route=None,
+         out=None, lse=None, stream=None):
+    """Union build, then grouped or per-token attention as chosen on the device from the
+    union's size; route[0] == 1 afterwards when the per-token form ran."""
+    T, H, _ = q.shape
+    bufs = bufs or alloc_union(T, 128 // H, topk.shape[1], q.device)
+    if route is None:
+        route = torch.zeros(4, dtype=torch.int32, device=q.device)
+    if out is None:
+        out, lse = alloc_out(T, H, 512, q.device)
+    _lib.dsa_sparse_prefill_auto(q, kv, topk, q_pos_offset, scale, bufs.union_idx, bufs.union_len, bufs.mask,
+                                 route, out, lse, stream=stream)
+    return out, lse, bufs, route
+
+
 def pertoken(q, kv, topk, q_pos_offset: int, scale: float, out=None, lse=None, stream=None):
     T, H, _ = q.shape
     if out is None:

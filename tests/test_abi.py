@@ -131,6 +131,25 @@ def test_pertoken_validation(lib):
     assert pertoken_call(lib, q=P + 2) == ALIGN and pertoken_call(lib, tk=P + 1) == ALIGN
 
 
+def auto_call(lib, q=P, kv=P, tk=P, ld=32, T=64, H=16, S=64, cols=32, P0=0, dqk=576, dv=512, scale=0.0625,
+              pad=256, ui=P, ul=P, mk=P, route=P, out=P, lse=P):
+    return lib.dsa_sparse_prefill_auto(q, kv, tk, ld, T, H, S, cols, P0, dqk, dv, scale, pad, ui, ul, mk, route,
+                                       out, lse, None)
+
+
+def test_auto_validation(lib):
+    for H in (128, 48, 8, 0):                       # only the head counts with a grouped form
+        assert auto_call(lib, H=H) == UNSUP
+    assert auto_call(lib, dqk=192) == UNSUP and auto_call(lib, scale=0.0) == UNSUP
+    assert auto_call(lib, T=0) == OK
+    assert auto_call(lib, ld=16) == SHAPE and auto_call(lib, P0=-1) == SHAPE
+    assert auto_call(lib, pad=192) == SHAPE         # below G * cols = 256
+    assert auto_call(lib, pad=288) == SHAPE         # not a multiple of 64
+    for kw in ("q", "kv", "tk", "ui", "ul", "mk", "route", "out", "lse"):
+        assert auto_call(lib, **{kw: None}) == NULL
+    assert auto_call(lib, route=P + 2) == ALIGN and auto_call(lib, ul=P + 1) == ALIGN
+
+
 def mha_call(lib, q=P, kn=P, kp=None, v=P, tk=P, ld=32, T=64, S=64, H=16, dn=256, dr=0, dv=256,
              cols=32, P0=0, ws=P, out=P, lse=P, scale=0.0625):
     return lib.dsa_masked_mha_prefill(q, kn, kp, v, tk, ld, T, S, H, dn, dr, dv, cols, P0, scale, ws,

@@ -203,6 +203,33 @@ def test_pertoken_sorted_windows(R):
     check_attention(out, lse, ref_out, ref_lse, "per-token S=300000 windows")
 
 
+AUTO_CASES = [
+    # (label, seed, T, S, H, k, P0, mode, the form expected to run: 0 grouped, 1 per-token)
+    ("h16_locality", 41, 400, 1200, 16, 256, 800, "locality", 0),
+    ("h16_uniform", 42, 400, 2400, 16, 256, 2000, "uniform", 1),
+    ("h32_uniform", 43, 240, 3000, 32, 200, 2760, "uniform", 1),
+    ("h64_locality", 44, 130, 900, 64, 300, 770, "locality", 0),
+    ("h16_short_rows", 45, 70, 70, 16, 64, 0, "uniform", None),  # early tokens: few keys each
+]
+
+
+@pytest.mark.parametrize("case", AUTO_CASES, ids=[c[0] for c in AUTO_CASES])
+def test_auto_routing(R, case):
+    """The routing chosen on the device from the union's size: the chosen form runs (route
+    words), its result matches the oracle, and the union tiles it counted are the union's."""
+    label, seed, T, S, H, k, P0, mode, expect = case
+    q, kv, topk = small_mqa(seed, T, S, H, k, k, 128 // H, P0, mode, True)
+    ref_out, ref_lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, P0, 0.0625)
+    out, lse, bufs, route = R.auto(dev_bf16(q), dev_bf16(kv), dev_i32(topk), P0, 0.0625)
+    check_attention(out, lse, ref_out, ref_lse, f"auto {label}")
+    rt = route.cpu().numpy()
+    _, ul, _ = oracle.group_union_mask(topk, S, P0, 128 // H)
+    assert rt[2] == int(np.sum((np.asarray(ul) + 31) // 32))
+    assert rt[0] + rt[1] == 1
+    if expect is not None:
+        assert rt[0] == expect, (label, rt)
+
+
 def test_latent_past_2gib(R):
     """Both routings over a latent of 1.9 M rows (2.19 GB): row offsets past 2^31 bytes, where
     the grouped kernel's copies take full 64-bit addresses.  Only the selected rows hold values
