@@ -126,12 +126,12 @@ def mqa_work(cfg, topk, union_len):
     for the attention kernels (bf16 MFMA), and the per-token kernel's gathered bytes."""
     T, S, H, cols, G = cfg.T, cfg.S, cfg.H, cfg.cols, cfg.G
     NG = cfg.NG
-    pad = -(-(G * cols) // 64) * 64
     d = cfg.d_qk
     nsel = selected_rows(cfg, topk)
     rows_live = np.minimum(G, T - np.arange(NG) * G) * H   # live pseudo-head rows per group
     return {
-        "build_union": ("hbm", T * cols * 4 + NG * pad * 5 + NG * 4),
+        # the top-k rows read, the union entries and their mask bytes written, union_len
+        "build_union": ("hbm", T * cols * 4 + int(np.sum(union_len)) * 5 + NG * 4),
         "grouped_attn": ("mfma", float(np.sum(np.asarray(union_len, np.float64) * rows_live)) * 2 * (d + 512)),
         "pertoken_attn": ("mfma", float(nsel) * H * 2 * (d + 512)),
         "pertoken_gather_bytes": nsel * 2 * d,

@@ -129,12 +129,14 @@ int dsa_select_routing(int T, int S, int64_t q_pos_offset, int H, int k, int mha
  *                   (dsa_union_pad(G, cols) is the smallest such value)
  * Outputs, NG = ceil(T / G) groups, group g = tokens gG .. min(T, gG + G) - 1:
  *   union_idx       int32 [NG, union_pad]: the strictly ascending union of the
- *                   members' selections, then -1 up to union_pad
+ *                   members' selections, then -1 up to the next multiple of 64
+ *                   (entries past that are not written)
  *   union_len       int32 [NG]: number of union entries
  *   head_group_mask uint8 [NG, union_pad]: bit i of slot j is set iff token
- *                   gG + i selects union_idx[g, j]; 0 in padding slots and for
- *                   absent members of the last group.
- * All three outputs are fully overwritten.  Bit-exact and deterministic. */
+ *                   gG + i selects union_idx[g, j]; 0 in the written padding
+ *                   slots and for absent members of the last group.
+ * union_len and each row's slots up to the next multiple of 64 past its union are
+ * written (the attention kernels read no further).  Bit-exact and deterministic. */
 int dsa_build_group_union(const int32_t* topk, int64_t ld, int T, int cols, int S,
                           int64_t q_pos_offset, int G, int union_pad, int32_t* union_idx,
                           int32_t* union_len, uint8_t* head_group_mask, void* stream);
@@ -350,10 +352,11 @@ int dsa_convert_req_index_to_global(const int32_t* topk, int64_t ld, int T, int 
  *                   count of each group (0, 0 for empty groups)
  *   union_idx       int32 [max_groups, union_pad]: the union of the members'
  *                   selections in ascending request-local position, each written
- *                   as its cache row, then -1
+ *                   as its cache row, then -1 up to the next multiple of 64
  *   union_len, head_group_mask: as for dsa_build_group_union (bit i <-> the
  *                   group's i-th token)
- * All outputs are fully overwritten.  Bit-exact and deterministic. */
+ * group_info and union_len are fully overwritten, union rows as for
+ * dsa_build_group_union.  Bit-exact and deterministic. */
 int dsa_build_group_union_varlen(const int32_t* topk, int64_t ld, int T, int cols, int R,
                                  const int32_t* cu_seqlens_q, const int32_t* kv_lens,
                                  const int32_t* q_pos_start, const int32_t* block_table, int64_t bt_ld,

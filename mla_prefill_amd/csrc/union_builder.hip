@@ -210,7 +210,10 @@ __global__ __launch_bounds__(kUnionThreads) void build_union_kernel(
   }
 
   if (total > union_pad) total = union_pad;
-  for (int j = total + tid; j < union_pad; j += kUnionThreads) {
+  // padding up to a whole number of 64-slot blocks only: readers stop at the tile holding the
+  // last entry, and the rest of the row (most of it for compact unions) is not written
+  const int pad_end = min(union_pad, (total + 63) & ~63);
+  for (int j = total + tid; j < pad_end; j += kUnionThreads) {
     uout[j] = -1;
     mout[j] = 0;
   }

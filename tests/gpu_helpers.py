@@ -83,3 +83,17 @@ def check_rows_equal(a: torch.Tensor, b: torch.Tensor, label=""):
     assert worst <= ROW_RTOL, (f"{label}: worst (token, head) row rel diff {worst:.3e} at "
                                f"{divmod(int(rows.argmax().item()), rows.shape[1])}")
     return rel, worst
+
+
+def check_union_rows(union_idx, mask, ref_idx, ref_len, ref_mask, label=""):
+    """The union buffers against the oracle's: union_len equal, and each row's slots up to the
+    next multiple of 64 past its union (the written part) bit-exact; the rest of the row is
+    not written by the builder and not compared."""
+    ui = union_idx.cpu().numpy() if hasattr(union_idx, "cpu") else np.asarray(union_idx)
+    mk = mask.cpu().numpy() if hasattr(mask, "cpu") else np.asarray(mask)
+    ref_idx, ref_mask, ref_len = np.asarray(ref_idx), np.asarray(ref_mask), np.asarray(ref_len)
+    assert ui.shape == ref_idx.shape and mk.shape == ref_mask.shape, label
+    for g in range(ui.shape[0]):
+        end = min(ui.shape[1], (int(ref_len[g]) + 63) // 64 * 64)
+        np.testing.assert_array_equal(ui[g, :end], ref_idx[g, :end], err_msg=f"{label} union_idx row {g}")
+        np.testing.assert_array_equal(mk[g, :end], ref_mask[g, :end], err_msg=f"{label} mask row {g}")
