@@ -127,8 +127,7 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   // the row invalid slots copy (their P is 0): the list's first valid entry, a row the group
   // selects -- an unselected row (an unused slot of a paged cache) may hold anything, and 0
   // times a NaN is NaN.  With no valid entry there is nothing to attend over.  (The first
-  // 64 entries are loaded here, before the queries, and looked at after them.)
-  const int32_t x_first = lane < nkeys ? klist[lane] : -1;
+  // 64 entries are loaded in the prologue, with the queries.)
   int dummy_row = -1;
   int ntiles = 0;  // (both set in the prologue below)
   bf16x8 qreg[kRQRegSteps];  // the queries' register steps (loaded in the prologue)
@@ -395,12 +394,43 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   };
 
   // ---- the prologue ---------------------------------------------------------------------
-  // The index words of tiles 0 .. 3 travel with the list's first entries; once they have
-  // landed, the row copies of tiles 0 and 1 and the queries travel together.
+  // One round trip brings the queries, the index words of tiles 0 .. 3, the list's first
+  // entries and the union length (none of them needs another); a second brings the row
+  // copies of tiles 0 and 1.  (Index words are copied for the tiles the list's padded length
+  // allows; past the union they are not looked at.)
+  uint4 qtail[kRQLdsSteps > 0 ? kRQLdsSteps : 1];
+  {
+    // queries: row r, dims 16 s + 8 hi .. + 8 (steps kRQRegSteps.. go to a lane-private LDS
+    // area: the registers are needed to keep operand reads in flight).  A row past the group's
+    // tokens loads the first token's row and is zeroed below: unconditional loads go out back
+    // to back (a load under a branch is waited for inside it).
+    const uint16_t* qrow = q + ((size_t)(live ? tok : t0) * H + rh) * D + 8 * hi;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const uint4 w = *reinterpret_cast<const uint4*>(qrow + 16 * s);
+      if (s < kRQRegSteps)
+        qreg[s] = __builtin_bit_cast(bf16x8, w);
+      else
+        qtail[s - kRQRegSteps] = w;
+    }
+  }
+  asm volatile("" ::: "memory");  // (the copies below go out after the query loads)
 #pragma unroll
   for (int t = 0; t < kRIdxBufs; ++t)
-    if (t * kRKeys < nkeys) issue_idx(t);
+    if (t * kRKeys < ncols) issue_idx(t);
+  const int32_t x_first = lane < ncols ? klist[lane] : -1;
   wait_vmcnt<0>();
+  // (the queries' sign and the rows past the group's tokens, once they have landed: the
+  // statement orders the reads after the wait)
+  auto qfix = [&](uint4 w) -> uint4 {
+    asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+    w.x ^= qsign; w.y ^= qsign; w.z ^= qsign; w.w ^= qsign;
+    return live ? w : uint4{0u, 0u, 0u, 0u};
+  };
+#pragma unroll
+  for (int s = 0; s < kRQLdsSteps; ++s) qlds[wave][s][lane] = qfix(qtail[s]);
+#pragma unroll
+  for (int s = 0; s < kRQRegSteps; ++s) qreg[s] = __builtin_bit_cast(bf16x8, qfix(__builtin_bit_cast(uint4, qreg[s])));
   {
     const uint64_t b = ballot(slot_ok(x_first, lane));
     if (b != 0) dummy_row = __builtin_amdgcn_readlane(x_first, __builtin_ctzll(b));
@@ -418,23 +448,6 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
     issue_rows(0);
     if (ntiles > 1) issue_rows(1);
     if (ntiles > 2) row_next = rows_make(2, rows_read(2));
-  }
-  asm volatile("" ::: "memory");  // (the query loads below go out after the copies)
-  // queries: row r, dims 16 s + 8 hi .. + 8 (steps kRQRegSteps.. go to a lane-private LDS
-  // area: the registers are needed to keep operand reads in flight); a row past the group's
-  // tokens is zero
-  {
-    const uint16_t* qrow = q + ((size_t)tok * H + rh) * D + 8 * hi;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      uint4 w = {0u, 0u, 0u, 0u};
-      if (live) w = *reinterpret_cast<const uint4*>(qrow + 16 * s);
-      w.x ^= qsign; w.y ^= qsign; w.z ^= qsign; w.w ^= qsign;
-      if (s < kRQRegSteps)
-        qreg[s] = __builtin_bit_cast(bf16x8, w);
-      else
-        qlds[wave][s - kRQRegSteps][lane] = w;
-    }
   }
   wait_vmcnt<0>();
   __syncthreads();  // tile 0 and the index words of tiles 0 .. 3 visible to all waves
