@@ -114,15 +114,22 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
   const float sc = fabsf(scale_log2);
   bf16x8 qa[kQSteps], qb[kQSteps];
   {
-    const uint16_t* qra = q + ((size_t)ra * H + h) * kDQK + 8 * hi;
-    const uint16_t* qrb = q + ((size_t)rb * H + h) * kDQK + 8 * hi;
+    // (rows past T load row T - 1 and are zeroed after: unconditional loads go out back to
+    // back, where a load under a branch is waited for inside it)
+    const uint16_t* qra = q + ((size_t)min(ra, T - 1) * H + h) * kDQK + 8 * hi;
+    const uint16_t* qrb = q + ((size_t)min(rb, T - 1) * H + h) * kDQK + 8 * hi;
+    uint4 la[kQSteps], lb[kQSteps];
 #pragma unroll
     for (int s = 0; s < kQSteps; ++s) {
-      uint4 wa = {0u, 0u, 0u, 0u}, wb = {0u, 0u, 0u, 0u};
-      if (ra < T) wa = *reinterpret_cast<const uint4*>(qra + 16 * s);
-      if (rb < T) wb = *reinterpret_cast<const uint4*>(qrb + 16 * s);
-      wa.x ^= qsign; wa.y ^= qsign; wa.z ^= qsign; wa.w ^= qsign;
-      wb.x ^= qsign; wb.y ^= qsign; wb.z ^= qsign; wb.w ^= qsign;
+      la[s] = *reinterpret_cast<const uint4*>(qra + 16 * s);
+      lb[s] = *reinterpret_cast<const uint4*>(qrb + 16 * s);
+    }
+    const uint32_t ka = ra < T ? 0xffffffffu : 0u, kb = rb < T ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int s = 0; s < kQSteps; ++s) {
+      uint4 wa = la[s], wb = lb[s];
+      wa.x = (wa.x ^ qsign) & ka; wa.y = (wa.y ^ qsign) & ka; wa.z = (wa.z ^ qsign) & ka; wa.w = (wa.w ^ qsign) & ka;
+      wb.x = (wb.x ^ qsign) & kb; wb.y = (wb.y ^ qsign) & kb; wb.z = (wb.z ^ qsign) & kb; wb.w = (wb.w ^ qsign) & kb;
       qa[s] = __builtin_bit_cast(bf16x8, wa);
       qb[s] = __builtin_bit_cast(bf16x8, wb);
     }

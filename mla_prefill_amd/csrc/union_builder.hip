@@ -30,6 +30,8 @@
 
 namespace dsa {
 
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kUnionThreads = 256;
 constexpr int kUnionWaves = kUnionThreads / 64;
 constexpr int kUnionWindow = 32768;  // positions per LDS pass (one byte each)
@@ -149,7 +151,34 @@ __global__ __launch_bounds__(kUnionThreads) void build_union_kernel(
     // (eight independent loads per thread before their LDS updates: one memory latency per
     // eight entries instead of one per entry)
     const int nent = ntok * cols;
-    for (int e0 = tid; e0 < nent; e0 += 8 * kUnionThreads) {
+    // rows of whole 16-byte vectors (the usual top-k widths): each thread loads 16 vectors
+    // (64 entries) back to back -- unconditionally, at a clamped index, so that no load waits
+    // under a branch -- and a group's 8 x 2048 entries arrive in one memory round trip
+    const bool vec = !kVarlen && (cols & 3) == 0 && (ld & 3) == 0 && ((uintptr_t)topk & 15) == 0;
+    const int nvec = vec ? nent >> 2 : 0;
+    for (int v0 = tid; v0 < nvec; v0 += 16 * kUnionThreads) {
+      i32x4 xs[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int e = 4 * min(v0 + u * kUnionThreads, nvec - 1);
+        const int i = e / cols;
+        xs[u] = *reinterpret_cast<const i32x4*>(topk + (size_t)(t0 + i) * ld + (e - i * cols));
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int v = v0 + u * kUnionThreads;
+        const int i = (4 * v) / cols;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int32_t x = xs[u][c];
+          if (v < nvec && x >= w0 && x - w0 < wlen && (int64_t)x <= pos0 + i) {
+            const int p = x - w0;
+            atomicOr(&bytemap[p >> 2], (1u << i) << (8 * (p & 3)));
+          }
+        }
+      }
+    }
+    for (int e0 = vec ? nent : tid; e0 < nent; e0 += 8 * kUnionThreads) {
       int32_t xs[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
