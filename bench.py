@@ -2,18 +2,24 @@
 """Throughput of DSA sparse-MLA prefill attention on one MI355X.
 
 One step is one layer of sparse prefill attention over one chunk of synthetic
-input, computed by the routing the library itself picks for the chunk
-(``dsa_select_routing``).  The default workload "glm16k" is the GLM-style per-GPU
-share of a 16k-token prefill chunk (T = S = 16384, H = 16, top-2048, groups of 8
-tokens, 576-wide bf16 latent, scale 1/16; locality top-k, seed 2).  There the
-library picks the grouped routing, so a step is the union + membership-mask
-build followed by grouped attention, and
+input, computed by the routing the library itself picks for the chunk.  The
+choice has two stages: ``dsa_select_routing`` weighs the MHA forms against the
+sparse MQA forms from the chunk's lengths (host side), and where it picks the
+grouped form (H = 16, 32, 64) the step is one ``dsa_sparse_prefill_auto`` call:
+union + membership-mask build, then one workgroup that compares the union's
+32-slot tiles with the per-token cost and lets only the cheaper of grouped and
+per-token attention run (the other returns at once).  The default workload
+"glm16k" is the GLM-style per-GPU share of a 16k-token prefill chunk
+(T = S = 16384, H = 16, top-2048, groups of 8 tokens, 576-wide bf16 latent,
+scale 1/16; locality top-k, seed 2), where the grouped form runs, and
 
     value = query tokens per second of one layer (T / step time).
 
 Inputs are resident in HBM before the timed region starts.  Per-kernel times
-come from HIP events recorded on the launch stream over the timed steps (mean,
-median and min); after the timed region each kernel is also timed "cold", right
+come from HIP events recorded on the launch stream around each kernel's own
+calls (mean, median and min over --steps calls after --warmup, the form the
+union-size routing ran timed kernel by kernel, since one ``auto`` call enqueues
+all of them); after the timed region each kernel is also timed "cold", right
 after a 1 GiB write that evicts L2 and the Infinity Cache.
 
 Extra keys of the same JSON line (not part of ``value``):
@@ -24,9 +30,11 @@ Extra keys of the same JSON line (not part of ``value``):
   same chunk (c4 shapes, seed 3);
 * ``configs``: the other single-GPU configurations -- the long prompt (32k KV,
   the last 21504 positions as queries, 2176-column top-k buffer), the
-  worst-case uniform top-k over the 16k chunk, and the DeepSeek-V3.2-style
-  layer (H = 128, T = S = 4096) -- with the routing the library picks for each,
-  and every MQA routing timed with its roofline fraction.
+  worst-case uniform top-k over the 16k chunk (unions up to 10.8k rows, where
+  the union-size routing runs per-token), and the DeepSeek-V3.2-style layer
+  (H = 128, T = S = 4096) -- with the routing the library picks for each, every
+  routing timed with its roofline fraction, and the ``auto`` call's own time,
+  the form it ran and its overhead over that form.
 
 Roofline bounds (algorithmic work per launch over its mean launch time):
 grouped, per-token and masked attention against dense bf16 MFMA

@@ -100,8 +100,8 @@ size_t dsa_masked_mha_workspace_bytes(int T, int S);
  *             min(S, p_t + 1) is at most c * k, with c measured on MI355X for
  *             this library's kernels (against the 576-wide latent):
  *                         H = 16   32   64  | 128 | other multiples of 16
- *               mha_dv 256:  3.0  2.4  2.2  | 2.1 | 3.4
- *               mha_dv 128:  4.6  3.6  3.3  | 3.1 | 5.5
+ *               mha_dv 256:  2.5  2.1  1.85 | 1.8 | 3.4
+ *               mha_dv 128:  3.9  3.3  3.0  | 2.7 | 5.5
  *             (first three against grouped, the rest against per-token); any
  *             H the MQA kernels do not take (not a multiple of 16, or above
  *             128) routes here as well;

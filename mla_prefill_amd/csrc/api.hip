@@ -72,14 +72,15 @@ int dsa_union_pad(int G, int cols) {
 // Purpose section and its heuristic commit: below some length the masked MHA beats the sparse
 // MQA kernels, and a chunk no longer than the top-k needs no mask at all).  The thresholds
 // are MI355X measurements of this library's kernels: chunks of L tokens from position 0 with
-// top-2048 (8-token locality), the 576-wide latent for the MQA forms.  Masked and sparse times
+// top-2048 (8-token locality), the MQA forms over the 576- and the 512-wide latent (c lies
+// between the two widths' crossovers, nearer the 576-wide one).  Masked and sparse times
 // cross where the mean number of causal keys per query token reaches c * k (masked time grows
 // with the causal pairs, sparse time with the selected ones).
 namespace {
 double masked_threshold(int H, int mha_dv, bool grouped) {
   // {H 16, 32, 64 against grouped; 128 against per-token (G = 1); other H against per-token}
-  static const double kQk256[5] = {3.0, 2.4, 2.2, 2.1, 3.4};  // (256, 0, 256), (192, 64, 256)
-  static const double kDsv[5] = {4.6, 3.6, 3.3, 3.1, 5.5};    // (128, 64, 128)
+  static const double kQk256[5] = {2.5, 2.1, 1.85, 1.8, 3.4};  // (256, 0, 256), (192, 64, 256)
+  static const double kDsv[5] = {3.9, 3.3, 3.0, 2.7, 5.5};      // (128, 64, 128)
   const double* c = mha_dv == 128 ? kDsv : kQk256;
   if (!grouped) return H == 128 ? c[3] : c[4];
   return H == 16 ? c[0] : (H == 32 ? c[1] : c[2]);

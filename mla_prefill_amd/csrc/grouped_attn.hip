@@ -14,23 +14,31 @@
 // selection rule (0 <= x < S, x <= position) instead of a membership byte.
 //
 // MI355X design (one workgroup of 4 waves per group, one wave per SIMD):
-//  * wave w owns rows 32 w .. 32 w + 31 for the whole attention: their
-//    queries (576 or 512 dims: the latent with or without its 64 rope dims)
-//    sit in registers as the B operand of S^T = K Q^T, and
-//    O^T (512 columns x 32 rows) accumulates in registers, so no
-//    probabilities or rescale factors cross waves;
+//  * S^T = K Q^T is split by rows, O^T = V^T P^T by columns: wave w scores rows
+//    32 w .. 32 w + 31 (their queries, 576 or 512 dims, sit in registers as
+//    the B operand, 32 k-steps, the rest in a lane-private LDS area), runs
+//    their softmax and writes their bf16 probabilities to LDS; after the
+//    tile's barrier every wave multiplies all 128 rows' probabilities by its
+//    own 128 value columns, so O^T (128 columns x 128 rows) fills the wave's
+//    256 accumulation registers and each wave reads only a quarter of V^T.
+//    The per-row softmax reference is fixed (below), so only P crosses waves;
+//    the row sums meet once, at the end;
+//  * iteration t runs the QK of tile t + 1 and then the PV of tile t, whose
+//    MFMAs carry the softmax of tile t + 1 in pieces (masking, reference,
+//    exponentials, P stores), so MFMA and VALU work overlap inside the wave;
 //  * 32-slot tiles of latent rows stream through a 3-stage LDS ring by
 //    asynchronous global->LDS DMA, two tiles ahead of the compute, one
 //    barrier per tile.  Each wave copies one 8-row group of a tile (nine or
 //    eight 128-byte blocks per row) into the XOR-swizzled 8-row-group layout
 //    (common.h), so the 16-byte K reads and the transposed V reads are free of
-//    bank conflicts.  The slot indices and membership bytes of a tile arrive
-//    by their own DMA one tile earlier; per-token membership masks then come
-//    from ballots;
+//    bank conflicts; the copy instructions are spread between the QK MFMAs.
+//    The slot indices and membership bytes of a tile arrive by their own DMA
+//    four tiles ahead; per-token membership masks then come from ballots,
+//    made (with the next copies' source rows) during the previous tile's PV;
 //  * S^T = K Q^T and O^T = V^T P^T both run on v_mfma_f32_32x32x16_bf16 (the
 //    full-rate shape); V^T comes from ds_read_b64_tr_b16, and the bf16
-//    probabilities go straight from the score accumulators into the B
-//    operand (keys relabelled consistently);
+//    probabilities are stored in the score accumulators' own layout, which is
+//    the PV B operand's (keys relabelled consistently);
 //  * softmax in base 2 on raw scores (the scale folded into the exponent's
 //    FMA; a negative scale negates the queries) against a per-row reference
 //    fixed at the row's first valid scores, so O is written only by MFMAs.
@@ -41,6 +49,8 @@
 //    the scales of a tile's slots arrive by DMA with its rows, each raw score
 //    is multiplied by its row's scale before the softmax and each probability
 //    by it before the PV product (l sums the unscaled probabilities);
+//  * the output is staged through LDS, so that each store instruction
+//    writes 256-byte row segments;
 //  * longest groups (most union slots) are launched first.
 #include <type_traits>
 

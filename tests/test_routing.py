@@ -24,18 +24,18 @@ def test_dense_when_the_chunk_fits_in_the_top_k(pick):
 
 
 def test_masked_threshold_against_grouped(pick):
-    # H 16: c = 3.0, k = 2048 -> mean causal keys <= 6144; a chunk from 0 has mean (L + 1) / 2
-    assert pick(12287, 12287, 0, 16, 2048, 256) == "masked"
-    assert pick(12289, 12289, 0, 16, 2048, 256) == "grouped"
+    # H 16: c = 2.5, k = 2048 -> mean causal keys <= 5120; a chunk from 0 has mean (L + 1) / 2
+    assert pick(10239, 10239, 0, 16, 2048, 256) == "masked"
+    assert pick(10241, 10241, 0, 16, 2048, 256) == "grouped"
     assert pick(8192, 8192, 0, 32, 2048, 256) == "masked"
     assert pick(10240, 10240, 0, 32, 2048, 256) == "grouped"
     assert pick(16384, 16384, 0, 64, 2048, 256) == "grouped"
 
 
 def test_masked_threshold_against_pertoken(pick):
-    # H 128: c = 2.1 -> mean causal keys <= 4300.8
-    assert pick(8192, 8192, 0, 128, 2048, 256) == "masked"
-    assert pick(9216, 9216, 0, 128, 2048, 256) == "per-token"
+    # H 128: c = 1.8 -> mean causal keys <= 3686.4
+    assert pick(7168, 7168, 0, 128, 2048, 256) == "masked"
+    assert pick(8192, 8192, 0, 128, 2048, 256) == "per-token"
     assert pick(8192, 8192, 0, 128, 2048, 0) == "per-token"
     # H 48: no grouped form (128 % 48 != 0); c = 3.4
     assert pick(13000, 13000, 0, 48, 2048, 256) == "masked"
@@ -44,11 +44,11 @@ def test_masked_threshold_against_pertoken(pick):
 
 
 def test_thresholds_of_the_dsv32_geometry(pick):
-    # (128, 64, 128): c = 4.6 / 3.6 / 3.3 against grouped, 3.1 at H 128
-    assert pick(18000, 18000, 0, 16, 2048, 128) == "masked"
-    assert pick(19500, 19500, 0, 16, 2048, 128) == "grouped"
-    assert pick(12000, 12000, 0, 128, 2048, 128) == "masked"
-    assert pick(13000, 13000, 0, 128, 2048, 128) == "per-token"
+    # (128, 64, 128): c = 3.9 / 3.3 / 3.0 against grouped, 2.7 at H 128
+    assert pick(15500, 15500, 0, 16, 2048, 128) == "masked"
+    assert pick(16500, 16500, 0, 16, 2048, 128) == "grouped"
+    assert pick(10500, 10500, 0, 128, 2048, 128) == "masked"
+    assert pick(11500, 11500, 0, 128, 2048, 128) == "per-token"
     assert pick(22000, 22000, 0, 48, 2048, 128) == "masked"
     from mla_prefill_amd import _lib
     assert _lib.lib.dsa_select_routing(8192, 8192, 0, 16, 2048, 192) == -3
@@ -57,7 +57,8 @@ def test_thresholds_of_the_dsv32_geometry(pick):
 def test_chunked_context_and_positions_past_S(pick):
     # a long prefix: mean causal keys ~ q_pos_offset + T / 2
     assert pick(512, 30512, 30000, 16, 2048, 256) == "grouped"
-    assert pick(512, 5512, 5000, 16, 2048, 256) == "masked"
+    assert pick(512, 4512, 4000, 16, 2048, 256) == "masked"
+    assert pick(512, 5512, 5000, 16, 2048, 256) == "grouped"
     # positions past S - 1 see S keys
     assert pick(100, 3000, 5000, 16, 2048, 256) == "masked"
     assert pick(100, 9000, 9000, 16, 2048, 256) == "grouped"
