@@ -246,7 +246,6 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
     }
     return (second ? mk1 : mk0) >> (4 * hi);
   };
-  auto tile_allowed = [&](int t) -> uint32_t { return allowed_make(t, allowed_read(t)); };
   // kScaled: row scales of tile t's slots 8 u + 4 hi .. + 3 (score registers 4 u .. 4 u + 3)
   auto tile_scales = [&](int t, f32x4 (&ks)[4]) {
 #pragma unroll
@@ -255,14 +254,46 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
                       : f32x4{1.f, 1.f, 1.f, 1.f};
   };
 
+  // O^T[cols 128 w + 32 cb ..][rows 32 rb ..] += V^T P^T of tile t, slot step st (slots
+  // 16 st .. 16 st + 15, k-slot (hi, i) <-> slot 16 st + 8 (i / 4) + 4 hi + i % 4): the V^T
+  // operand of this wave's column block cb, and the P^T operand of row block rb written by
+  // wave rb (its lanes' probabilities of those slots)
+  const int vcol0 = 4 * wave;  // this wave's first 32-column block
+  auto vread = [&](const uint8_t* vt, int st, int cb) -> bf16x8 {
+    const int cg = vcol0 + cb;
+    // rows 16 st + 8 uu + vr8 are in group 2 st + uu; chunk 4 cg + c2 is in block cg / 2
+    const int p0 = 16 * (vx ^ (4 * (cg & 1)) ^ (2 * st));
+    const int p1 = 16 * (vx ^ (4 * (cg & 1)) ^ (2 * st + 1));
+    const u16x4 lo = lds_read_tr16(vt + (2 * st) * kRGroupBytes + 1024 * (cg >> 1) + vbase + p0);
+    const u16x4 up = lds_read_tr16(vt + (2 * st + 1) * kRGroupBytes + 1024 * (cg >> 1) + vbase + p1);
+    return __builtin_bit_cast(bf16x8, u16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
+  };
+
+  // The first operands of tile t's PV (the V^T operands of column blocks 0 and 1 and the
+  // four P^T operands of slot step 0), read during the tail of the QK before it, whose
+  // last MFMAs no longer read the LDS: the PV then starts without waiting.
+  bf16x8 pv_va[2], pv_pw[4];
+  auto pv_pre = [&](int t) {
+    const uint8_t* vt = &stage[0][0] + loop_local((t % kRStages) * kRStageBytes);
+    const bf16x8* pt = &pbuf[t & 1][0][0][0] + loop_local(lane);
+    pv_va[0] = vread(vt, 0, 0);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) pv_pw[rb] = pt[2 * rb * 64];
+    pv_va[1] = vread(vt, 0, 1);
+  };
+
   // S^T = K Q^T of tile t: sacc[j] = raw score(slot 8 (j / 4) + 4 hi + j % 4, row r).  The K
   // reads run kRAhead MFMAs ahead (the order is pinned: left to itself the scheduler puts
-  // every read right before its MFMA and waits out its latency).  With `copy`, block c of a
-  // later tile's row copies (`next`) goes out after MFMA 4 c + 1: spread over the MFMAs, the
-  // copies do not hold the wave at their issue as a burst does.
-  auto qk = [&](int t, auto copy_tag, uint32_t next_row) -> f32x16 {
+  // every read right before its MFMA and waits out its latency).  With `copy`, block c of
+  // tile t + 1's row copies goes out after MFMA 4 c + 1: spread over the MFMAs, the copies do
+  // not hold the wave at their issue as a burst does.  The VALU work of the next steps rides
+  // here, where the MFMAs have no other company: the copy source rows of tile t + 1 (from
+  // its index words `rw`, read earlier) and the membership of tile t (from `aw`) for its
+  // softmax.
+  auto qk = [&](int t, auto copy_tag, int2 rw, uint2 aw, uint32_t& al, int pv_t) -> f32x16 {
     constexpr bool copy = decltype(copy_tag)::value;
-    const RowSrc next = rows_src(t + 1, next_row);
+    RowSrc next{};
+    if (copy) next = rows_src(t + 1, rows_make(t + 1, rw));
     const uint8_t* kt = &stage[0][0] + loop_local((t % kRStages) * kRStageBytes);
     // (the LDS query address is made opaque per tile, so that its reads are not hoisted)
     const uint8_t* qb = reinterpret_cast<const uint8_t*>(&qlds[wave][0][0]) + loop_local(16 * lane);
@@ -290,24 +321,11 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
         qw[st % kRAhead] = qread(st + kRAhead);
       }
       if (copy && (st & 3) == 1 && (st >> 2) < kRCopies) rows_copy(next, st >> 2);
+      if (st == 10) al = allowed_make(t, aw);  // (past the last tile: no valid slot, all masked)
+      if (st == D / 16 - 4 && pv_t >= 0) pv_pre(pv_t);
     }
     __builtin_amdgcn_sched_barrier(0);
     return acc;
-  };
-
-  // O^T[cols 128 w + 32 cb ..][rows 32 rb ..] += V^T P^T of tile t, slot step st (slots
-  // 16 st .. 16 st + 15, k-slot (hi, i) <-> slot 16 st + 8 (i / 4) + 4 hi + i % 4): the V^T
-  // operand of this wave's column block cb, and the P^T operand of row block rb written by
-  // wave rb (its lanes' probabilities of those slots)
-  const int vcol0 = 4 * wave;  // this wave's first 32-column block
-  auto vread = [&](const uint8_t* vt, int st, int cb) -> bf16x8 {
-    const int cg = vcol0 + cb;
-    // rows 16 st + 8 uu + vr8 are in group 2 st + uu; chunk 4 cg + c2 is in block cg / 2
-    const int p0 = 16 * (vx ^ (4 * (cg & 1)) ^ (2 * st));
-    const int p1 = 16 * (vx ^ (4 * (cg & 1)) ^ (2 * st + 1));
-    const u16x4 lo = lds_read_tr16(vt + (2 * st) * kRGroupBytes + 1024 * (cg >> 1) + vbase + p0);
-    const u16x4 up = lds_read_tr16(vt + (2 * st + 1) * kRGroupBytes + 1024 * (cg >> 1) + vbase + p1);
-    return __builtin_bit_cast(bf16x8, u16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
   };
 
   float m_ref = kNegInf;  // row r's reference (log2 units), equal in both halves
@@ -321,84 +339,83 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
 
   // The softmax of tile tn on its scores sacc, in pieces k = 0..kSmPieces - 1 that the PV
   // MFMAs of the previous tile carry: masking (and the row scales), the reference, the
-  // probabilities, and their store to pbuf[tn % 2] for every wave.
-  constexpr int kSmPieces = 24;
+  // probabilities, and their store to pbuf[tn % 2] for every wave.  The row max is needed only
+  // until every row of the wave has its reference (kRef: the first tiles); after that a score
+  // far above the reference shows in the probabilities' sum, which is checked at the end.
+  constexpr int kSmPieces = 28;
   constexpr int kSmLag = 4;
-  float sm_ml = kNegInf, sm_nm = 0.f;
+  float sm_ml = kNegInf, sm_mr = kNegInf, sm_nm = 0.f;
   bf16x8 bop[2];
-  auto sm_piece = [&](int k, int tn, f32x16& sacc, uint32_t allowed, const f32x4 (&ks)[4]) {
-    if (k < 4) {  // masking of scores 4 k .. 4 k + 3; the row max (raw units)
+  auto sm_piece = [&](int k, int tn, f32x16& sacc, uint32_t allowed, const f32x4 (&ks)[4], auto ref_tag) {
+    constexpr bool kRef = decltype(ref_tag)::value;
+    if (k < 8) {  // masking of scores 2 k, 2 k + 1; the row max (raw units)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int j = 4 * k + jj;
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * k + jj;
         const int kk = 8 * (j >> 2) + (j & 3);
         const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)allowed, kk, 1);  // all ones if allowed
         // (a scalar copy: bit casts of vector elements misread)
         const float raw = kScaled ? sacc[j] * ks[j >> 2][j & 3] : sacc[j];
         const float val = __builtin_bit_cast(float, (sel & __builtin_bit_cast(uint32_t, raw)) | (~sel & 0xff800000u));
         sacc[j] = val;
-        sm_ml = fmaxf(sm_ml, val);
+        if (kRef) sm_ml = fmaxf(sm_ml, val);
       }
-    } else if (k == 4) {
+    } else if (k == 8) {  // the row max over both halves of the row
+      if (!kRef) return;
+      sm_ml *= sc;
+      sm_mr = max_xor32(sm_ml);
+    } else if (k == 9) {
       // a row's first valid scores set its reference (its O and l are still zero); both halves
       // of the row agree on it
-      const float ml = sm_ml * sc;
-      const float mr = max_xor32(ml);
-      m_ref = m_ref == kNegInf ? mr : m_ref;
-      over |= ml > m_ref + kRSlack;
+      if (!kRef) return;
+      m_ref = m_ref == kNegInf ? sm_mr : m_ref;
+      over |= sm_ml > m_ref + kRSlack;
       sm_nm = m_ref == kNegInf ? 0.f : -m_ref;
       sm_ml = kNegInf;
-    } else if (k < 21) {  // probability of score k - 5 (times its row scale: the PV operand)
-      const int j = k - 5;
+    } else if (k < 26) {  // probability of score k - 10 (times its row scale: the PV operand)
+      const int j = k - 10;
       const float p = fast_exp2(__builtin_fmaf(sacc[j], sc, sm_nm));
       l_run += p;
       asm volatile("" : "+v"(l_run));  // (the sum stays in its piece: sunk to the loop's end, the
                                        // 16 dependent adds would stall the MFMAs there)
       bop[j >> 3][j & 7] = (__bf16)(kScaled ? p * ks[j >> 2][j & 3] : p);
-    } else if (k < 23) {
-      pbuf[tn & 1][wave][k - 21][lane] = bop[k - 21];
+    } else {
+      pbuf[tn & 1][wave][k - 26][lane] = bop[k - 26];
     }
   };
 
   // PV of tile t (V^T from stage t % 3, P^T from pbuf[t % 2]) carrying the softmax of tile
   // t + 1, whose pieces start kSmLag MFMAs in (the scores come from written-out MFMAs whose
-  // latency the compiler does not see).  MFMA i: slot step st = i / 16, row block
-  // rb = (i / 4) % 4, column block cb = i % 4; the 4 V^T operands of a step are held through
-  // it (the next step's are read as these retire), P^T operands are read two row blocks ahead.
-  auto pv_sm = [&](int t, f32x16& sacc_n, uint32_t allowed_n, const f32x4 (&ks_n)[4], uint32_t& al_next,
-                   uint32_t& row_next) {
-    uint2 aw;
-    int2 rw;
+  // latency the compiler does not see).  MFMA i: slot step st = i / 16, column block
+  // cb = (i / 4) % 4, row block rb = i % 4.  A V^T operand serves four MFMAs in a row; the
+  // one two column blocks on is read as it retires (two buffers, reads about five MFMAs
+  // ahead, evenly spread), and the four P^T operands of a step are held through it (the next
+  // step's are read as these retire).
+  auto pv_sm = [&](int t, f32x16& sacc_n, uint32_t allowed_n, const f32x4 (&ks_n)[4], uint2& aw, int2& rw,
+                   auto ref_tag) {
     const uint8_t* vt = &stage[0][0] + loop_local((t % kRStages) * kRStageBytes);
     const bf16x8* pt = &pbuf[t & 1][0][0][0] + loop_local(lane);
     auto pread = [&](int st, int rb) -> bf16x8 { return pt[(2 * rb + st) * 64]; };
-    bf16x8 va[4], pw[2];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) va[cb] = vread(vt, 0, cb);
-    pw[0] = pread(0, 0);
-    pw[1] = pread(0, 1);
+    bf16x8 va[2] = {pv_va[0], pv_va[1]}, pw[4] = {pv_pw[0], pv_pw[1], pv_pw[2], pv_pw[3]};  // (pv_pre)
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-      const int st = i >> 4, rb = (i >> 2) & 3, cb = i & 3;
-      o[cb][rb] = mfma32x32x16(va[cb], pw[(i >> 2) & 1], o[cb][rb]);
-      if (st == 0 && rb == 3) va[cb] = vread(vt, 1, cb);          // this operand's last use in step 0
-      if (cb == 3 && i + 8 < 32) {                               // the P^T operand two row blocks on
-        const int ni = i + 5;
-        pw[(i >> 2) & 1] = pread(ni >> 4, (ni >> 2) & 3);
+      const int st = i >> 4, cb = (i >> 2) & 3, rb = i & 3;
+      o[cb][rb] = mfma32x32x16(va[cb & 1], pw[rb], o[cb][rb]);
+      // (the P^T read first: it is needed sooner, and LDS reads retire in order)
+      if (st == 0 && cb == 3) pw[rb] = pread(1, rb);  // this P^T operand's last use in step 0
+      if (rb == 3 && (i >> 2) + 2 < 8) {  // this V^T operand's last use: the one two blocks on
+        const int nb = (i >> 2) + 2;
+        va[cb & 1] = vread(vt, nb >> 2, nb & 3);
       }
       if (i == kSmLag) asm volatile("" : "+v"(sacc_n));  // (no read of the scores above this point)
-      // the next iteration's membership (tile t + 2) and copy sources (tile t + 3): their index
-      // words are read here and used 20 MFMAs later
+      // the index words of the next iteration's membership (tile t + 2) and copy sources
+      // (tile t + 3), made during its QK
       if (i == 8) {
         aw = allowed_read(t + 2);
         rw = rows_read(t + 3);
       }
-      if (i == 28) {
-        al_next = t + 2 < ntiles ? allowed_make(t + 2, aw) : 0u;  // (past the last tile: all masked)
-        if (t + 3 < ntiles) row_next = rows_make(t + 3, rw);
-      }
-      if (i >= kSmLag && i < kSmLag + kSmPieces) sm_piece(i - kSmLag, t + 1, sacc_n, allowed_n, ks_n);
+      if (i >= kSmLag && i < kSmLag + kSmPieces) sm_piece(i - kSmLag, t + 1, sacc_n, allowed_n, ks_n, ref_tag);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -452,12 +469,9 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   }
   dummy_row = uniform(dummy_row);
   ntiles = uniform(dummy_row < 0 ? 0 : (nkeys + kRKeys - 1) / kRKeys);
-  uint32_t al_next = 0u;
-  uint32_t row_next = 0;
   if (ntiles > 0) {
     issue_rows(0);
     if (ntiles > 1) issue_rows(1);
-    if (ntiles > 2) row_next = rows_make(2, rows_read(2));
   }
   wait_vmcnt<0>();
   __syncthreads();  // tile 0 and the index words of tiles 0 .. 3 visible to all waves
@@ -466,40 +480,50 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   // Iteration t: (wait + barrier) tile t + 1 and the probabilities of tile t are in LDS;
   // copy tile t + 2 into the stage of tile t - 1; QK of tile t + 1; PV of tile t carrying the
   // softmax of tile t + 1.  Stages in use: t (V), t + 1 (K), t + 2 (in flight).  A tile's
-  // index words arrive four tiles ahead of its QK (issued in iteration t - 4); the membership
-  // of tile t + 1 and the copy sources of tile t + 2 are made during the PV of iteration
-  // t - 1, so after the barrier only the copies go out before the QK.
+  // index words arrive four tiles ahead of its QK (issued in iteration t - 4); the words of
+  // tile t + 1's membership and tile t + 2's copy sources are read during the PV of
+  // iteration t - 1 and turned into masks and rows during the QK of tile t + 1.
   if (ntiles > 0) {
     f32x4 ks0[4];
     tile_scales(0, ks0);
-    const uint32_t al0 = tile_allowed(0);
-    if (ntiles > 1) al_next = tile_allowed(1);
-    f32x16 s0 = qk(0, std::false_type{}, 0u);
+    uint32_t al0 = 0u;
+    f32x16 s0 = qk(0, std::false_type{}, int2{0, 0}, allowed_read(0), al0, -1);
     // wait states before the VALU reads the last score MFMA's results (the scores pass
     // through the statement, so no read of them can be placed above it)
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0));
 #pragma unroll
-    for (int k = 0; k < kSmPieces; ++k) sm_piece(k, 0, s0, al0, ks0);
+    for (int k = 0; k < kSmPieces; ++k) sm_piece(k, 0, s0, al0, ks0, std::true_type{});
   }
-  for (int t = 0; t < ntiles; ++t) {
+  uint2 aw = allowed_read(1);  // (words of tiles past the last are never used: no slot is valid)
+  int2 rw = rows_read(2);
+  auto iteration = [&](int t, auto ref_tag) {
     wait_vmcnt<0>();  // tile t + 1, the scales of tile t + 2 and the indices of tile t + 3
     __syncthreads();  // P(t) of every wave visible; stage (t + 2) % 3, pbuf (t + 1) % 2 and index
                       // buffer t % 4 free
     if (t + 4 < ntiles) issue_idx(t + 4);
-    const bool copy = t + 2 < ntiles;
-    const uint32_t next = row_next;  // tile t + 2's copy row (its blocks go out during the QK below)
+    const bool copy = t + 2 < ntiles;  // (tile t + 2's blocks go out during the QK below)
     const bool more = t + 1 < ntiles;
     f32x4 ks[4];
     tile_scales(more ? t + 1 : t, ks);
-    const uint32_t al = al_next;   // tile t + 1's membership (0 past the last tile: all masked)
+    uint32_t al = 0u;  // tile t + 1's membership (0 past the last tile: all masked)
     f32x16 sn = {};
     if (copy)
-      sn = qk(t + 1, std::true_type{}, next);
+      sn = qk(t + 1, std::true_type{}, rw, aw, al, t);
     else if (more)
-      sn = qk(t + 1, std::false_type{}, next);
+      sn = qk(t + 1, std::false_type{}, rw, aw, al, t);
+    else
+      pv_pre(t);
     // (a VGPR-resident value for the softmax even past the last tile)
-    pv_sm(t, sn, al, ks, al_next, row_next);
-  }
+    pv_sm(t, sn, al, ks, aw, rw, ref_tag);
+  };
+  // while a row of this wave has no reference yet (normally not past tile 0), the softmax
+  // takes row maxima; then the loop without them
+  int t = 0;
+  for (; t < ntiles && ballot(m_ref == kNegInf) != 0; ++t) iteration(t, std::true_type{});
+  for (; t < ntiles; ++t) iteration(t, std::false_type{});
+  // every probability is at most 2^kRSlack unless a score rose that far above its reference:
+  // then this lane's sum shows it (an infinite or NaN sum as well)
+  over |= !(l_run <= __builtin_ldexpf(1.f, (int)kRSlack));
 
   if (ballot(over) != 0 && lane == 0) over_any = 1;
   const float l = sum_xor32(l_run);
