@@ -155,13 +155,12 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   const int cchunk = (lane & 7) ^ swz8(crow) ^ wave;
   const uint16_t* cbase = kv + 8 * cchunk;
   const uint32_t cdst = wave * kRGroupBytes;
+  const bool idx_mask_lane = !kPerToken && lane >= 8 && lane < 10;
   auto issue_idx = [&](int t) {
     const int j0 = t * kRKeys + 8 * wave;
-    const int32_t* src;
-    if (!kPerToken && lane >= 8 && lane < 10)
-      src = reinterpret_cast<const int32_t*>(mlist + j0) + (lane - 8);
-    else
-      src = klist + min(j0 + (lane & 7), ncols - 1);
+    const int32_t* src = klist + min(j0 + (lane & 7), ncols - 1);
+    if (!kPerToken)  // (a select, not a branch)
+      src = idx_mask_lane ? reinterpret_cast<const int32_t*>(mlist + j0) + (lane - 8) : src;
     dma4(src, lds_addr(&idxw[t % kRIdxBufs][wave][0]));
   };
   // (kSmallKv, a latent below 2 GiB: every row offset fits 31 bits, and block c's copies take
@@ -447,17 +446,22 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
     if (t * kRKeys < ncols) issue_idx(t);
   const int32_t x_first = lane < ncols ? klist[lane] : -1;
   wait_vmcnt<0>();
-  // (the queries' sign and the rows past the group's tokens, once they have landed: the
-  // statement orders the reads after the wait)
-  auto qfix = [&](uint4 w) -> uint4 {
-    asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
-    w.x ^= qsign; w.y ^= qsign; w.z ^= qsign; w.w ^= qsign;
-    return live ? w : uint4{0u, 0u, 0u, 0u};
-  };
+  // (the queries' sign, once they have landed: the statement orders the reads after the
+  // wait.  A row past the group's tokens keeps the first token's query: its token selects
+  // nothing, so every score of the row is masked, and the row is never stored.)
+  if (qsign != 0) {
+    auto qfix = [&](uint4 w) -> uint4 {
+      asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+      w.x ^= qsign; w.y ^= qsign; w.z ^= qsign; w.w ^= qsign;
+      return w;
+    };
 #pragma unroll
-  for (int s = 0; s < kRQLdsSteps; ++s) qlds[wave][s][lane] = qfix(qtail[s]);
+    for (int s = 0; s < kRQLdsSteps; ++s) qtail[s] = qfix(qtail[s]);
 #pragma unroll
-  for (int s = 0; s < kRQRegSteps; ++s) qreg[s] = __builtin_bit_cast(bf16x8, qfix(__builtin_bit_cast(uint4, qreg[s])));
+    for (int s = 0; s < kRQRegSteps; ++s) qreg[s] = __builtin_bit_cast(bf16x8, qfix(__builtin_bit_cast(uint4, qreg[s])));
+  }
+#pragma unroll
+  for (int s = 0; s < kRQLdsSteps; ++s) qlds[wave][s][lane] = qtail[s];
   {
     const uint64_t b = ballot(slot_ok(x_first, lane));
     if (b != 0) dummy_row = __builtin_amdgcn_readlane(x_first, __builtin_ctzll(b));
@@ -559,17 +563,22 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
         }
     }
     // (a wave's LDS accesses complete in order: these reads see the writes above, and the next
-    // half's writes come after these reads have returned their data to the stores)
+    // half's writes come after the stores have taken these reads' data.)  Row r of the group
+    // is token t0 + r / H, head r % H: its output row is t0 * H + r.  All 16 reads go out
+    // before the first store; the rows past the group's tokens are not stored.
+    uint4 v[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int lr = 4 * k + (lane >> 4);
-      const int row = 64 * half + lr;
-      const int i = row / H;
-      const uint4 v = *reinterpret_cast<const uint4*>(ost + lr * kOPitch + 16 * (lane & 15));
-      if (i < ntok) {
-        const int h = row - i * H;
-        *reinterpret_cast<uint4*>(out + ((size_t)(t0 + i) * H + h) * kRDv + 128 * wave + 8 * (lane & 15)) = v;
-      }
+    for (int k = 0; k < 16; ++k)
+      v[k] = *reinterpret_cast<const uint4*>(ost + (4 * k + (lane >> 4)) * kOPitch + 16 * (lane & 15));
+    uint16_t* orow = out + ((size_t)t0 * H + 64 * half + (lane >> 4)) * kRDv + 128 * wave + 8 * (lane & 15);
+    const int rows_live = ntok * H - 64 * half;  // rows of this half that are stored (uniform)
+    if (rows_live >= 64) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) *reinterpret_cast<uint4*>(orow + (size_t)(4 * k) * kRDv) = v[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (4 * k + (lane >> 4) < rows_live) *reinterpret_cast<uint4*>(orow + (size_t)(4 * k) * kRDv) = v[k];
     }
   }
 }

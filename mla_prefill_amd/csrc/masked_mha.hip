@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
   // ---- softmax pieces (VALU), placed between MFMAs below ----
   // scores: sacc[j] = raw score(key k0 + 8 (j / 4) + 4 hi + j % 4, row)
   uint32_t alla = 0u, allb = 0u;
-  float mta = kNegInf, mtb = kNegInf, lsa = 0.f, lsb = 0.f;
+  float lsa = 0.f, lsb = 0.f;
   // allowed keys of tile t: top-k bit AND key <= position; bit kk <-> key k0 + 4 hi + kk
   auto mask_setup = [&](int t) {
     const int k0 = t * kMKeys;
@@ -222,10 +222,8 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
       alla &= *reinterpret_cast<const uint32_t*>(mw) >> (4 * hi);
       allb &= *reinterpret_cast<const uint32_t*>(mw + 128) >> (4 * hi);
     }
-    mta = kNegInf;
-    mtb = kNegInf;
   };
-  auto select = [&](f32x16& c, uint32_t allowed, float& mt, int j) {
+  auto select = [&](f32x16& c, uint32_t allowed, int j) {
     const int kk = 8 * (j >> 2) + (j & 3);
     const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)allowed, kk, 1);  // all ones if allowed
     // (the element goes through a scalar first: a bit cast applied directly to a
@@ -234,12 +232,18 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
     const float val =
         __builtin_bit_cast(float, (sel & __builtin_bit_cast(uint32_t, raw)) | (~sel & 0xff800000u));
     c[j] = val;
-    mt = fmaxf(mt, val);
   };
   // fixed reference: a row's reference is the max of its first tile with a selected key
   // (O^T and l are still zero then) and never moves, so O^T is never rescaled; a later max
-  // beyond reference + 2^kMRefSlack marks the row for the exact path
-  auto reduce = [&](float mt, float& mref, float& nm, bool& fb) {
+  // beyond reference + 2^kMRefSlack marks the row for the exact path.  Maxima are taken only
+  // while a row of the wave has no reference (need_ref, normally the first tiles); after that
+  // a score that far above the reference shows in the row's sum, which is checked at the end.
+  bool need_ref = true;
+  auto reduce = [&](const f32x16& c, float& mref, float& nm, bool& fb) {
+    if (!need_ref) return;  // (a uniform branch around the whole reduction)
+    float mt = c[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) mt = fmaxf(mt, c[j]);
     mt = max_xor32(mt) * sc;
     fb = fb | ((mref != kNegInf) & (mt > mref + kMRefSlack));  // (no short circuit: no branch)
     mref = mref == kNegInf ? mt : mref;
@@ -254,13 +258,13 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
   constexpr int kTasks = 16 + 1 + 16 + 1 + 16;
   auto task = [&](int id) {
     if (id < 16)
-      select(sa, alla, mta, id);
+      select(sa, alla, id);
     else if (id == 16)
-      reduce(mta, ma, nma, fba);
+      reduce(sa, ma, nma, fba);
     else if (id < 33)
-      select(sb, allb, mtb, id - 17);
+      select(sb, allb, id - 17);
     else if (id == 33)
-      reduce(mtb, mb, nmb, fbb);
+      reduce(sb, mb, nmb, fbb);
     else
       expo(sa, nma, lsa, pan, id - 34);
   };
@@ -375,6 +379,7 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
   }
   // steady state: tile t's QK, tile t - 1's PV, tile t's softmax around them
   for (int t = 1; t < ntiles; ++t) {
+    need_ref = need_ref && ballot(ma == kNegInf || mb == kNegInf) != 0;
     arrive(t);
     phase1(yes{}, yes{}, t);
     phase2(yes{}, yes{}, t - 1, t);
@@ -389,6 +394,9 @@ __global__ __launch_bounds__(kMThreads) void masked_mha_kernel(
   // (rows marked for the exact path get LSE = +inf, which no finite softmax produces)
   auto store = [&](int row, float l, float mref, bool fb, const f32x16* o) {
     const float l_tot = sum_xor32(l);  // (every lane takes part)
+    // every probability is at most 2^kMRefSlack unless a score rose that far above the
+    // row's reference: then its sum shows it (an infinite or NaN sum as well)
+    fb = fb || !(l_tot <= __builtin_ldexpf(1.f, (int)kMRefSlack));
     if (row >= T) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* orow = out + ((size_t)row * H + h) * kDV + 4 * hi;
