@@ -206,11 +206,6 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
     else
       dma16(r.src + 64 * c, r.dst + 1024 * c);
   };
-  auto issue_rows = [&](int t) {
-    const RowSrc r = rows_src(t, rows_make(t, rows_read(t)));
-#pragma unroll
-    for (int c = 0; c < kRCopies; ++c) rows_copy(r, c);
-  };
 
   // K reads (A of S^T): key m, dims 16 s + 8 hi -> chunk 2 s + hi: 4 bases (s % 4) + (s / 4) KiB
   const int kx = swz8(m & 7) ^ (m >> 3) ^ hi;
@@ -420,10 +415,23 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   };
 
   // ---- the prologue ---------------------------------------------------------------------
-  // One round trip brings the queries, the index words of tiles 0 .. 3, the list's first
-  // entries and the union length (none of them needs another); a second brings the row
-  // copies of tiles 0 and 1.  (Index words are copied for the tiles the list's padded length
-  // allows; past the union they are not looked at.)
+  // The list's first entries and the slots of this lane's row copies in tiles 0 and 1 go out
+  // first, then the index words of tiles 0 .. 3 and the queries; the row copies of tiles 0 and
+  // 1 follow as soon as the list's head has landed, while the queries still stream in (their
+  // loads, 16 rows under every quarter-wave, are limited by the address path).  (Index words
+  // are copied for the tiles the list's padded length allows; past the union they are not
+  // looked at.)
+  const int32_t x_first = lane < ncols ? klist[lane] : -1;
+  int2 xr0 = {-1, -1}, xr1 = {-1, -1};  // (rows_read's words of tiles 0 and 1, from the list)
+  if (ncols > 0) {
+    const int last = ncols - 1;
+    xr0 = int2{klist[min(8 * wave + crow, last)], kScaled ? klist[min(8 * wave + (lane & 7), last)] : 0};
+    xr1 = int2{klist[min(kRKeys + 8 * wave + crow, last)], kScaled ? klist[min(kRKeys + 8 * wave + (lane & 7), last)] : 0};
+  }
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int t = 0; t < kRIdxBufs; ++t)
+    if (t * kRKeys < ncols) issue_idx(t);
   uint4 qtail[kRQLdsSteps > 0 ? kRQLdsSteps : 1];
   {
     // queries: row r, dims 16 s + 8 hi .. + 8 (steps kRQRegSteps.. go to a lane-private LDS
@@ -441,10 +449,27 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
     }
   }
   asm volatile("" ::: "memory");  // (the copies below go out after the query loads)
+  {
+    const uint64_t b = ballot(slot_ok(x_first, lane));
+    if (b != 0) dummy_row = __builtin_amdgcn_readlane(x_first, __builtin_ctzll(b));
+  }
+  for (int c0 = 64; dummy_row < 0 && c0 < nkeys; c0 += 64) {
+    const int32_t x = c0 + lane < nkeys ? klist[c0 + lane] : -1;
+    const uint64_t b = ballot(slot_ok(x, c0 + lane));
+    if (b != 0) dummy_row = __builtin_amdgcn_readlane(x, __builtin_ctzll(b));
+  }
+  dummy_row = uniform(dummy_row);
+  ntiles = uniform(dummy_row < 0 ? 0 : (nkeys + kRKeys - 1) / kRKeys);
+  if (ntiles > 0) {
+    const RowSrc r0 = rows_src(0, rows_make(0, xr0));
 #pragma unroll
-  for (int t = 0; t < kRIdxBufs; ++t)
-    if (t * kRKeys < ncols) issue_idx(t);
-  const int32_t x_first = lane < ncols ? klist[lane] : -1;
+    for (int c = 0; c < kRCopies; ++c) rows_copy(r0, c);
+    if (ntiles > 1) {
+      const RowSrc r1 = rows_src(1, rows_make(1, xr1));
+#pragma unroll
+      for (int c = 0; c < kRCopies; ++c) rows_copy(r1, c);
+    }
+  }
   wait_vmcnt<0>();
   // (the queries' sign, once they have landed: the statement orders the reads after the
   // wait.  A row past the group's tokens keeps the first token's query: its token selects
@@ -462,22 +487,6 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   }
 #pragma unroll
   for (int s = 0; s < kRQLdsSteps; ++s) qlds[wave][s][lane] = qtail[s];
-  {
-    const uint64_t b = ballot(slot_ok(x_first, lane));
-    if (b != 0) dummy_row = __builtin_amdgcn_readlane(x_first, __builtin_ctzll(b));
-  }
-  for (int c0 = 64; dummy_row < 0 && c0 < nkeys; c0 += 64) {
-    const int32_t x = c0 + lane < nkeys ? klist[c0 + lane] : -1;
-    const uint64_t b = ballot(slot_ok(x, c0 + lane));
-    if (b != 0) dummy_row = __builtin_amdgcn_readlane(x, __builtin_ctzll(b));
-  }
-  dummy_row = uniform(dummy_row);
-  ntiles = uniform(dummy_row < 0 ? 0 : (nkeys + kRKeys - 1) / kRKeys);
-  if (ntiles > 0) {
-    issue_rows(0);
-    if (ntiles > 1) issue_rows(1);
-  }
-  wait_vmcnt<0>();
   __syncthreads();  // tile 0 and the index words of tiles 0 .. 3 visible to all waves
 
   // ---- the pipeline ---------------------------------------------------------------------
