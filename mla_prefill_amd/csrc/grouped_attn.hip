@@ -471,6 +471,14 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
     }
   }
   wait_vmcnt<0>();
+  // (the list words and the queries are consumed here, after the wait, so the compiler counts
+  // their loads as done: a load it still took for pending at the loop would put vector-memory
+  // waits, which also wait for the row copies in flight, into every iteration)
+  asm volatile("" : : "v"(x_first), "v"(xr0.x), "v"(xr0.y), "v"(xr1.x), "v"(xr1.y));
+  if constexpr (kRQLdsSteps <= 0) {  // (else the stores of the LDS steps below consume the last loads)
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) asm volatile("" : : "v"(qreg[s]));
+  }
   // (the queries' sign, once they have landed: the statement orders the reads after the
   // wait.  A row past the group's tokens keeps the first token's query: its token selects
   // nothing, so every score of the row is masked, and the row is never stored.)

@@ -836,12 +836,16 @@ __global__ __launch_bounds__(64) void pertoken_sorted_kernel(
   f32x4 sa = {1.f, 1.f, 1.f, 1.f}, sb = sa;  // kScaled: this lane's row scales of the tiles' steps
   const PdSrc s0 = pd_prep<D>(c, kvb, pd_entries(c, 0), 0);
   const PdSrc s1 = pd_prep<D>(c, kvb, pd_entries(c, 1), 1);
-  uint32_t va = pd_issue<D>(c, kvb, pd_entries(c, 0), 0, lds_addr(tile0));
-  uint32_t vb = pd_issue<D>(c, kvb, pd_entries(c, 1), 1, lds_addr(tile1));
   if (kScaled) {
     sa = step_scales_mine(step_scales_load(kscale, per_row, s0.rows), g);
     sb = step_scales_mine(step_scales_load(kscale, per_row, s1.rows), g);
+    // (consumed here, before any copy is in flight: the compiler may fetch these scales with
+    // a vector load, and one it still took for pending at the loop would put vector-memory
+    // waits, which also wait for the copies in flight, into every step)
+    asm volatile("" : "+v"(sa), "+v"(sb));
   }
+  uint32_t va = pd_issue<D>(c, kvb, pd_entries(c, 0), 0, lds_addr(tile0));
+  uint32_t vb = pd_issue<D>(c, kvb, pd_entries(c, 1), 1, lds_addr(tile1));
   int2 e_next = pd_entries(c, 2);
   bool over = false;
   auto step = [&](int j, const uint8_t* tile, uint32_t& vbuf, f32x4& sbuf) {
