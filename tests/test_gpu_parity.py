@@ -301,6 +301,82 @@ def test_large_score_jump_and_negative_scale(R):
         check_attention(out, lse, ref_out, ref_lse, f"grouped score jump, scale {scale}")
 
 
+def _late_topk(rng, T, G, P0, cols, first_keys, late_from):
+    """The first token of every group selects keys 0 .. first_keys - 1 and some late ones; the
+    other tokens select only keys at or after late_from (so, sorted, their first selected union
+    entry sits first_keys slots in).  Every row keeps 8 slots of -1 padding."""
+    topk = np.full((T, cols), -1, np.int32)
+    for t in range(T):
+        late = rng.choice(np.arange(late_from, P0 + t + 1), cols - first_keys - 8, replace=False)
+        sel = np.concatenate([np.arange(first_keys), late]) if t % G == 0 else late
+        topk[t, :len(sel)] = rng.permutation(sel)
+    return topk
+
+
+def _add_jumps(q, kv_rows, topk, tokens, keys, head=0, dims=None, mag=(0xC000, 0x4000)):
+    """Key row x (one per token, selected by that token alone) set to +-2 (or mag) along the
+    token's query on one head: its score lies far above every earlier score of the row."""
+    for t, x in zip(tokens, keys):
+        for u in range(topk.shape[0]):
+            topk[u][topk[u] == x] = -1
+        slot = int(np.flatnonzero(topk[t] == -1)[0])
+        topk[t, slot] = x
+        qrow = q[t, head] if dims is None else q[t, head, :dims]
+        kv_rows[x] = np.where(qrow & 0x8000, mag[0], mag[1]).astype(np.uint16)
+
+
+@pytest.mark.parametrize("H", [16, 32, 64])
+@pytest.mark.parametrize("jump", [False, True], ids=["plain", "jump"])
+def test_grouped_late_reference(R, H, jump):
+    """Rows whose first selected key sits several union tiles in (their token selects nothing
+    among the group's first 100 union entries): the grouped kernel takes row maxima until
+    every row of a wave has its reference.  With `jump`, a key near the end of the union
+    scores far above the references (~330 base-2 units: its probability would overflow) after
+    the maxima are no longer taken, which the probability sum catches (the group goes through
+    the exact kernel)."""
+    rng = np.random.default_rng(17 + H + jump)
+    G = 128 // H
+    T, S = 2 * G, 700
+    P0 = S - T
+    q = normal_bf16(rng, (T, H, 576))
+    kv = normal_bf16(rng, (S, 576))
+    topk = _late_topk(rng, T, G, P0, 160, 100, 300)
+    if jump:
+        toks = list(range(1, T, 3))
+        _add_jumps(q, kv, topk, toks, [650 + i for i in range(len(toks))], mag=(0xC100, 0x4100))  # +-8
+    scale = 0.0625
+    ref_out, ref_lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, P0, scale)
+    qd, kvd, tkd = dev_bf16(q), dev_bf16(kv), dev_i32(topk)
+    out, lse, _ = R.grouped(qd, kvd, tkd, P0, scale)
+    check_attention(out, lse, ref_out, ref_lse, f"grouped late reference H={H} jump={jump}")
+    out, lse = R.pertoken(qd, kvd, tkd, P0, scale)
+    check_attention(out, lse, ref_out, ref_lse, f"per-token late reference H={H} jump={jump}")
+
+
+@pytest.mark.parametrize("jump", [False, True], ids=["plain", "jump"])
+def test_masked_mha_late_reference(R, jump):
+    """Masked MHA rows whose selected keys all lie past key 200 (their first six 32-key tiles
+    hold nothing for them): maxima until every row of a wave has its reference; with `jump`,
+    a late key scores far above the reference afterwards (~150 base-2 units: its probability
+    would overflow), which the row's sum catches (the tile goes through the exact kernel)."""
+    rng = np.random.default_rng(53 + jump)
+    T, S, H, P0 = 300, 300, 2, 0
+    q = normal_bf16(rng, (T, H, 256))
+    kn = normal_bf16(rng, (S, H, 256))
+    v = normal_bf16(rng, (S, H, 256))
+    topk = np.full((T, 70), -1, np.int32)
+    for t in range(T):
+        lo = 200 if t >= 260 else 0
+        sel = rng.choice(np.arange(lo, t + 1), min(60, t + 1 - lo), replace=False)
+        topk[t, :len(sel)] = sel
+    if jump:
+        toks = [270, 281, 299]
+        _add_jumps(q, kn[:, 0], topk, toks, [262, 275, 290], mag=(0xC100, 0x4100))  # +-8
+    out, lse, _ = R.masked_mha(dev_bf16(q), dev_bf16(kn), None, dev_bf16(v), dev_i32(topk), P0, 0.0625)
+    ref_out, ref_lse = oracle.masked_mha(q, kn, None, v, topk, S, P0, 0.0625)
+    check_attention(out, lse, ref_out, ref_lse, f"masked late reference jump={jump}")
+
+
 # ---------------------------------------------------------------------------
 # the 512-wide latent (no rope part: K = V = the whole row)
 # ---------------------------------------------------------------------------
