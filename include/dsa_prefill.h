@@ -171,8 +171,8 @@ int dsa_sparse_prefill_grouped(const uint16_t* q, const uint16_t* kv, const int3
  * membership mask of every group of G = 128 / H tokens are built; then one
  * workgroup sums the grouped form's tiles, ceil(union_len / 32) over the groups,
  * and compares them with the per-token form's cost in the same unit,
- * rho(H) * sum_t min(cols, S, q_pos_offset + t + 1) / 32 with rho = 0.20, 0.41,
- * 0.88 for H = 16, 32, 64 (measured on MI355X for this library's kernels).
+ * rho(H) * sum_t min(cols, S, q_pos_offset + t + 1) / 32 with rho = 0.20, 0.43,
+ * 0.92 for H = 16, 32, 64 (measured on MI355X for this library's kernels).
  * Both attention launches are enqueued; the one not chosen returns at once.
  *
  *   q, kv, topk, ld, T, H, S, cols, q_pos_offset, d_qk, d_v, scale, out, lse:

@@ -210,7 +210,7 @@ int dsa_sparse_prefill_pertoken(const uint16_t* q, const uint16_t* kv, const int
 
 // per-token cost of the grouped form's 128-row tiles, per 32 selections (measured on MI355X
 // with this library's kernels, 576-wide latent, 16k-token chunks, locality and uniform top-k)
-static double route_rho(int H) { return H == 16 ? 0.20 : (H == 32 ? 0.41 : 0.88); }
+static double route_rho(int H) { return H == 16 ? 0.20 : (H == 32 ? 0.43 : 0.92); }
 
 // sum over the chunk of min(cols, S, p_t + 1), p_t = q_pos_offset + t: the selections a
 // token can make (an upper bound when rows hold -1 or out-of-range entries)
