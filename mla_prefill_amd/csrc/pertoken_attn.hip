@@ -503,12 +503,13 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
 // valid entries takes the register-ring walk instead).
 //
 // The wave first sorts its token's valid entries (0 <= x <= position) into pt_sorted:
-// a bitmap of the positions in the LDS tile, a prefix count over the lanes, and
-// compaction, one 131072-position chunk at a time.  Tokens of a range select nearly the same rows, so walking them in the
-// same order lets concurrent tokens find each other's rows in L2.  (Repeated entries
-// collapse to one.)  Rows then stream into two LDS tiles of 16 rows (18 KiB at D = 576)
-// by asynchronous global->LDS copies (one step ahead; no register ring and no LDS store
-// instructions), in the 8-row-group layout of common.h: 16-byte chunk k of tile row r at
+// a bitmap of the positions in the LDS tile, the count of set bits below each bitmap word,
+// and each entry stored at its rank, one 131072-position chunk at a time.  Tokens of a range
+// select nearly the same rows, so walking them in the same order lets concurrent tokens find
+// each other's rows in L2.  (Repeated entries collapse to one.)  Rows then stream into two
+// LDS tiles of 16 rows (18 KiB at D = 576) by asynchronous global->LDS copies (one step
+// ahead; no register ring and no LDS store instructions), in the 8-row-group layout of
+// common.h: 16-byte chunk k of tile row r at
 // 16 D (r / 8) + 1024 (k / 8) + 128 (r % 8) + 16 ((k % 8) ^ swz8(r % 8) ^ (r / 8)).
 // The queries stay in registers.  The exact fallback reuses the register-ring
 // routines (the second tile is the query area there).
@@ -516,11 +517,20 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
 
 // Sorts the token's valid entries (0 <= x <= pos) into pt_sorted and returns how many there
 // are (repeated entries collapse to one; past kPSortMax the count goes on but nothing more is
-// stored).  Positions are taken in chunks of 131072 (a 16 KiB bitmap in the tile, one pass
-// over the row per chunk); each 65536-position window's first list index goes to lane w of
-// `wstart` (lanes of windows past the last position hold the count).
+// stored).  Positions are taken in chunks of 131072.  For each chunk: a bitmap of its positions
+// in the tile (16 KiB at most); for every bitmap word, the number of set bits below it (in the
+// query area); then every entry writes itself at its rank, the set bits below it.  The work
+// follows the entries, wherever in [0, pos] they lie.  Each 65536-position window's first list
+// index goes to lane w of `wstart` (lanes of windows past the last position hold the count).
+constexpr int kPSortRegs = 5;  // 8-entry batches of the row held in registers (2560 columns)
+
 __device__ __forceinline__ int pt_sort(const int32_t* trow, int cols, int pos, int lane, int& wstart) {
   uint32_t* bm = reinterpret_cast<uint32_t*>(pt_tile);
+  uint32_t* below = reinterpret_cast<uint32_t*>(&pt_q[0][0]);  // per word: list index of its first bit
+  // the row's first 2560 entries in one round trip (columns past them are read once per pass)
+  int32_t xr[kPSortRegs * 8];
+#pragma unroll
+  for (int u = 0; u < kPSortRegs * 8; ++u) xr[u] = lane + 64 * u < cols ? trow[lane + 64 * u] : -1;
   int total = 0;
   wstart = 0;
   const int nchunks = uniform((pos >> 17) + 1);
@@ -530,44 +540,45 @@ __device__ __forceinline__ int pt_sort(const int32_t* trow, int cols, int pos, i
     const int nw = ((hi - lo) >> 5) + 1;          // bitmap words of the chunk
     for (int w = lane; w < nw; w += 64) bm[w] = 0u;
     __syncthreads();  // (one wave: orders the LDS accesses for the compiler)
-    // (eight independent loads per lane before their LDS updates: one memory latency per
-    // eight entries instead of one per entry)
-    for (int c0 = lane; c0 < cols; c0 += 8 * 64) {
-      int32_t xs[8];
+    auto mark = [&](int x) {
+      if (x >= lo && x <= hi) atomicOr(&bm[(x - lo) >> 5], 1u << (x & 31));
+    };
 #pragma unroll
-      for (int u = 0; u < 8; ++u) xs[u] = c0 + 64 * u < cols ? trow[c0 + 64 * u] : -1;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (xs[u] >= lo && xs[u] <= hi) atomicOr(&bm[(xs[u] - lo) >> 5], 1u << (xs[u] & 31));
-    }
+    for (int u = 0; u < kPSortRegs * 8; ++u) mark(xr[u]);
+    for (int c = kPSortRegs * 512 + lane; c < cols; c += 64) mark(trow[c]);
     __syncthreads();
-    // lane l owns words l * wpl .. + wpl - 1; past 2048 words a lane owns 64 words, so that
-    // the chunk's second window (words 2048..) starts exactly at lane 32
-    const int wpl = nw > 2048 ? 64 : (nw + 63) >> 6;
-    const int w0 = lane * wpl;
+    // lane l owns words l * wpl .. + wpl - 1; the odd stride puts the 64 lanes of each read
+    // in 64 different banks
+    const int wpl = ((nw + 63) >> 6) | 1;
+    const int w0 = lane * wpl, w1 = min(nw, w0 + wpl);
     int cnt = 0;
-    for (int k = 0; k < wpl; ++k)
-      if (w0 + k < nw) cnt += __popc(bm[w0 + k]);
+    for (int w = w0; w < w1; ++w) cnt += __popc(bm[w]);
     int incl = cnt;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const int v = __shfl_up(incl, d);
       if (lane >= d) incl += v;
     }
-    int at = total + incl - cnt;
-    for (int k = 0; k < wpl; ++k) {
-      if (w0 + k >= nw) break;
-      uint32_t bits = bm[w0 + k];
-      while (bits != 0u) {
-        if (at < kPSortMax) pt_sorted[at] = (uint16_t)(32 * (w0 + k) + __ffs(bits) - 1);  // (lo % 65536 = 0)
-        ++at;
-        bits &= bits - 1u;
-      }
+    int run = total + incl - cnt;
+    for (int w = w0; w < w1; ++w) {
+      below[w] = (uint32_t)run;
+      run += __popc(bm[w]);
     }
-    const int below_half = uniform(__shfl(incl, nw > 2048 ? 31 : 63));
+    __syncthreads();
+    auto place = [&](int x) {
+      if (x >= lo && x <= hi) {
+        const int w = (x - lo) >> 5;
+        const int at = (int)below[w] + __popc(bm[w] & ((1u << (x & 31)) - 1u));
+        if (at < kPSortMax) pt_sorted[at] = (uint16_t)x;  // the low 16 bits (lo % 65536 = 0)
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < kPSortRegs * 8; ++u) place(xr[u]);
+    for (int c = kPSortRegs * 512 + lane; c < cols; c += 64) place(trow[c]);
+    const int ctot = uniform(__shfl(incl, 63));
     if (lane == 2 * ch) wstart = total;
-    if (lane == 2 * ch + 1) wstart = total + below_half;
-    total += uniform(__shfl(incl, 63));
+    if (lane == 2 * ch + 1) wstart = nw > 2048 ? (int)below[2048] : total + ctot;
+    total += ctot;
     __syncthreads();  // the bitmap is cleared again, or the tile rewritten, from here on
   }
   if (lane >= 2 * nchunks) wstart = total;

@@ -200,6 +200,31 @@ def test_pertoken_sorted_windows(R):
     check_attention(out, lse, ref_out, ref_lse, "per-token S=300000 windows")
 
 
+def test_pertoken_sort_crowded_entries(R):
+    """Entries packed into a few bitmap words far from 0: each token's 2048 entries lie among
+    the 2100 positions up to its own (positions past 131072, so in the second sort chunk and in
+    the third 65536-row window), one token takes every position of a 2048-wide range, and the
+    rows arrive in a shuffled order.  The rank of an entry is the set bits below it, so
+    nearly full words test the within-word count; the list must come out sorted."""
+    rng = np.random.default_rng(37)
+    T, H, k, cols = 5, 16, 2048, 2176
+    S = 140000
+    P0 = S - T
+    q = normal_bf16(rng, (T, H, 576))
+    kv = normal_bf16(rng, (S, 576))
+    topk = np.full((T, cols), -1, np.int32)
+    for t in range(T):
+        pos = P0 + t
+        if t == 0:
+            sel = np.arange(pos - k + 1, pos + 1)                   # every position of the range
+        else:
+            sel = pos - rng.choice(2100, size=k, replace=False)
+        topk[t, :k] = rng.permutation(sel)
+    ref_out, ref_lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, P0, 0.0625)
+    out, lse = R.pertoken(dev_bf16(q), dev_bf16(kv), dev_i32(topk), P0, 0.0625)
+    check_attention(out, lse, ref_out, ref_lse, "per-token crowded entries")
+
+
 AUTO_CASES = [
     # (label, seed, T, S, H, k, P0, mode, the form expected to run: 0 grouped, 1 per-token)
     ("h16_locality", 41, 400, 1200, 16, 256, 800, "locality", 0),
