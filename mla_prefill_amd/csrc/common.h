@@ -206,6 +206,25 @@ __device__ __forceinline__ LanePair pair_xor16(float v) {
 __device__ __forceinline__ float max_xor32(float v) { const LanePair p = pair_xor32(v); return fmaxf(p.a, p.b); }
 __device__ __forceinline__ float sum_xor32(float v) { const LanePair p = pair_xor32(v); return p.a + p.b; }
 
+// Inclusive prefix sum of v over the wave's lanes, and the wave's total (uniform), by DPP
+// row shifts inside each 16-lane row (a source lane outside the row contributes 0) and the
+// four row totals read from lanes 15, 31, 47 and 63: no LDS round trip.
+__device__ __forceinline__ int wave_incl_scan(int v, int& total) {
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) {
+    const int sh = d == 1 ? __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false)
+                 : d == 2 ? __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false)
+                 : d == 4 ? __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false)
+                          : __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:d
+    v += sh;
+  }
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47), r3 = __builtin_amdgcn_readlane(v, 63);
+  total = r0 + r1 + r2 + r3;
+  const int row = (int)(threadIdx.x & 63) >> 4;
+  return v + (row == 0 ? 0 : row == 1 ? r0 : row == 2 ? r0 + r1 : r0 + r1 + r2);
+}
+
 // First token and token count of group grp of 128-row attention: G consecutive tokens
 // from grp * G, or the entry of a batch's group table [NG, 2] (clamped into [0, T)).
 __device__ __forceinline__ int2 group_span(const int32_t* ginfo, int grp, int G, int T) {

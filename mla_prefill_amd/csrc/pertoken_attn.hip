@@ -553,13 +553,8 @@ __device__ __forceinline__ int pt_sort(const int32_t* trow, int cols, int pos, i
     const int w0 = lane * wpl, w1 = min(nw, w0 + wpl);
     int cnt = 0;
     for (int w = w0; w < w1; ++w) cnt += __popc(bm[w]);
-    int incl = cnt;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int v = __shfl_up(incl, d);
-      if (lane >= d) incl += v;
-    }
-    int run = total + incl - cnt;
+    int ctot;
+    int run = total + wave_incl_scan(cnt, ctot) - cnt;
     for (int w = w0; w < w1; ++w) {
       below[w] = (uint32_t)run;
       run += __popc(bm[w]);
@@ -575,7 +570,7 @@ __device__ __forceinline__ int pt_sort(const int32_t* trow, int cols, int pos, i
 #pragma unroll
     for (int u = 0; u < kPSortRegs * 8; ++u) place(xr[u]);
     for (int c = kPSortRegs * 512 + lane; c < cols; c += 64) place(trow[c]);
-    const int ctot = uniform(__shfl(incl, 63));
+    ctot = uniform(ctot);
     if (lane == 2 * ch) wstart = total;
     if (lane == 2 * ch + 1) wstart = nw > 2048 ? (int)below[2048] : total + ctot;
     total += ctot;

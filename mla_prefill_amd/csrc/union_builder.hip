@@ -22,9 +22,9 @@
 // each position it selects (LDS atomics commute, so the result does not depend
 // on their order).  Each byte is then both "in the union" (non-zero) and the
 // mask byte itself.  Compaction is ordered: every wave counts the non-zero
-// bytes of its contiguous segment with ballot/popcount, the four counts are
-// scanned, and a second pass writes each non-zero position at
-// base + mbcnt(ballot) -- coalesced stores of consecutive slots.
+// bytes of its contiguous segment, 16 bytes per lane per read, the four counts
+// are scanned, and a second pass scans the lanes' counts and writes each
+// non-zero position at base + its rank, consecutive slots in order.
 #include "common.h"
 #include "kernels.h"
 
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kUnionThreads) void build_union_kernel(
     const int32_t* __restrict__ topk, int64_t ld, int T, int cols, int S, int64_t q_pos_offset,
     int G, int union_pad, int32_t* __restrict__ union_idx, int32_t* __restrict__ union_len,
     uint8_t* __restrict__ head_group_mask, ReqBatch b, int32_t* __restrict__ group_info) {
-  __shared__ uint32_t bytemap[kUnionWindow / 4];
+  __shared__ __align__(16) uint32_t bytemap[kUnionWindow / 4];
   __shared__ int wave_count[kUnionWaves];
   __shared__ int grp_req, grp_k, scan_tmp[kUnionThreads];
 
@@ -205,34 +205,77 @@ __global__ __launch_bounds__(kUnionThreads) void build_union_kernel(
     }
     __syncthreads();
 
-    // ordered compaction: wave w owns positions [s0, s1) of this window
-    const int seg = ((wlen + 64 * kUnionWaves - 1) / (64 * kUnionWaves)) * 64;
+    // ordered compaction: wave w owns positions [s0, s1) of this window.  A lane counts the
+    // non-zero bytes of 16 at a time; the four wave totals are scanned; then a sparse segment
+    // goes 1024 positions at a time (the lanes' counts scanned, each lane writing its entries
+    // in order from base + its exclusive prefix) and a dense one 64 positions at a time
+    // (ballot ranks, one slot per lane)
+    const int seg = ((wlen + 1024 * kUnionWaves - 1) / (1024 * kUnionWaves)) * 1024;
     const int s0 = wave * seg;
     const int s1 = min(wlen, s0 + seg);
+    // bit k: byte p + k of the map is non-zero (p % 16 == 0; bytes at or past wlen count as zero)
+    auto nonzero16 = [&](int p, uint4& w) -> uint32_t {
+      w = *reinterpret_cast<const uint4*>(bm + p);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+      uint32_t m = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t hi = (((ws[j] & 0x7f7f7f7fu) + 0x7f7f7f7fu) | ws[j]) & 0x80808080u;  // bit 8 i + 7: byte i
+        m |= (((hi >> 7) * 0x00204081u) >> 21 & 0xfu) << (4 * j);                         // gathered to bits 0..3
+      }
+      const int valid = wlen - p;
+      return valid >= 16 ? m : (m & ((1u << valid) - 1u));
+    };
     int cnt = 0;
-    for (int p = s0; p < s1; p += 64) {
-      const int pp = p + lane;
-      cnt += __popcll(ballot(pp < s1 && bm[pp] != 0));
+    for (int p = s0 + 16 * lane; p < s1; p += 1024) {
+      uint4 w;
+      cnt += __popc(nonzero16(p, w));
     }
-    if (lane == 0) wave_count[wave] = cnt;
+    int wsum;
+    (void)wave_incl_scan(cnt, wsum);
+    if (lane == 0) wave_count[wave] = wsum;
     __syncthreads();
     int base = total, wtotal = 0;
     for (int w = 0; w < kUnionWaves; ++w) {
       if (w < wave) base += wave_count[w];
       wtotal += wave_count[w];
     }
-    for (int p = s0; p < s1; p += 64) {
-      const int pp = p + lane;
-      const uint8_t mb = pp < s1 ? bm[pp] : (uint8_t)0;
-      const uint64_t m = ballot(mb != 0);
-      if (mb != 0) {
-        const int o = base + lanes_below(m);
-        if (o < union_pad) {  // always true when union_pad >= G * cols (checked on the host)
-          uout[o] = kVarlen ? (int32_t)physical_row(b, r, w0 + pp) : w0 + pp;
-          mout[o] = mb;
+    if (4 * wsum > s1 - s0) {
+      // a dense segment (more than one position in four): 64 consecutive positions per step,
+      // one slot per lane (coalesced stores)
+      for (int q = s0; q < s1; q += 64) {
+        const int pp = q + lane;
+        const uint8_t mb = pp < s1 ? bm[pp] : (uint8_t)0;
+        const uint64_t bal = ballot(mb != 0);
+        if (mb != 0) {
+          const int o = base + lanes_below(bal);
+          if (o < union_pad) {  // always true when union_pad >= G * cols (checked on the host)
+            uout[o] = kVarlen ? (int32_t)physical_row(b, r, w0 + pp) : w0 + pp;
+            mout[o] = mb;
+          }
         }
+        base += __popcll(bal);
       }
-      base += __popcll(m);
+    } else {
+      for (int c0 = s0; c0 < s1; c0 += 1024) {
+        const int p = c0 + 16 * lane;
+        uint4 w = {0u, 0u, 0u, 0u};
+        uint32_t m = p < s1 ? nonzero16(p, w) : 0u;
+        const int c = __popc(m);
+        int n;
+        int o = base + wave_incl_scan(c, n) - c;
+        while (m != 0u) {
+          const int k = __ffs(m) - 1;
+          if (o < union_pad) {
+            const uint32_t wk = (k & 8) ? ((k & 4) ? w.w : w.z) : ((k & 4) ? w.y : w.x);
+            uout[o] = kVarlen ? (int32_t)physical_row(b, r, w0 + p + k) : w0 + p + k;
+            mout[o] = (uint8_t)(wk >> (8 * (k & 3)));
+          }
+          ++o;
+          m &= m - 1u;
+        }
+        base += n;
+      }
     }
     total += wtotal;
     __syncthreads();  // the next window reuses bytemap and wave_count
