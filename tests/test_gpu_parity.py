@@ -60,6 +60,35 @@ def test_union_bit_exact(R, case):
     check_union_rows(bufs.union_idx, bufs.mask, ui, ul, mk)
 
 
+def test_union_dense_and_sparse_segments(R):
+    """The builder's compaction: each group mixes a dense run (most positions of a
+    1500-wide range selected by some member) with sparse picks far away, entries at the
+    window edge (32767, 32768), at the first and the last position a member may select,
+    and rows of 16-entry vectors and of odd width; group lengths are not multiples of 16.
+    Over 40000 positions (two windows, sparse segments) and 5000 (segments of 2048
+    positions: the dense run makes one wave's segment dense, its neighbour's mixed).
+    Union, lengths and masks bit-exact."""
+    rng = np.random.default_rng(43)
+    for cols, G, T, S in ((768, 8, 19, 40000), (771, 4, 9, 40000), (768, 8, 19, 5000)):
+        P0 = S - T
+        topk = np.full((T, cols), -1, np.int32)
+        for t in range(T):
+            pos = P0 + t
+            base = 1000 + 13 * (t // G)
+            dense = base + rng.permutation(1500)[: 500 + 100 * (t % G)]   # members cover the run
+            far = rng.choice(np.arange(3000, pos + 1), size=120, replace=False)
+            edge = np.array([0, 32767, 32768, pos, pos - 1, 31999, 32000])
+            sel = np.unique(np.concatenate([dense, far, edge]))
+            sel = sel[sel <= pos][: cols - 3]
+            row = np.concatenate([rng.permutation(sel), [S + 5, -3, pos + 1]])   # ignored entries
+            topk[t, : len(row)] = row[:cols]
+        ui, ul, mk = oracle.group_union_mask(topk, S, P0, G)
+        bufs = R.build_group_union(dev_i32(topk), S, P0, G)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bufs.union_len.cpu().numpy(), ul)
+        check_union_rows(bufs.union_idx, bufs.mask, ui, ul, mk, f"cols {cols} G {G}")
+
+
 @pytest.mark.parametrize("case", MQA_CASES, ids=[c[0] for c in MQA_CASES])
 def test_pertoken_parity(R, case):
     label, seed, T, S, H, k, cols, P0, mode, shuffle = case
