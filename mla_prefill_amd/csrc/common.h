@@ -191,6 +191,17 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nblocks) {
   return start + k;
 }
 
+// Remap so that every XCD receives chunks of c consecutive logical block ids, the XCDs taking
+// the chunks in turn (XCD x: chunks x, x + 8, ..): neighbouring work items still share an L2,
+// while work that grows or shrinks along the ids is spread evenly over the XCDs.  Each XCD
+// walks its chunks in order; a last partial round of 8 c ids keeps the identity.
+__device__ __forceinline__ int xcd_chunked_block(int b, int nblocks, int c) {
+  const int full = (nblocks / (8 * c)) * (8 * c);
+  if (b >= full) return b;
+  const int x = b % 8, k = b / 8;
+  return ((k / c) * 8 + x) * c + (k % c);
+}
+
 // The values of lanes l and l ^ 32 (or l ^ 16), as a pair (own half first or second does not
 // matter to the symmetric reductions below).  v_permlane32_swap / v_permlane16_swap are
 // VALU operations: no LDS round trip, unlike a general lane shuffle.

@@ -95,10 +95,14 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   // kScaled: per tile and wave, lane l holds the scale of slot 8 w + l % 8
   __shared__ __align__(16) float sbuf[kScaled ? kRStages : 1][kRWaves][64];
   __shared__ int over_any;
+  __shared__ int last_slot[kRWaves];  // per-token mode: each wave's last slot with a valid entry
 
   const int G = 128 / H;
   const int NG = (int)gridDim.x;
-  const int grp = NG - 1 - xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
+  // (a group's work is its union's length -- a token's, its valid slots -- which grows along
+  // a causal chunk: the XCDs take chunks of 32 groups in turn, so that each gets its share of
+  // the short early groups instead of one XCD getting all of them)
+  const int grp = NG - 1 - xcd_chunked_block((int)blockIdx.x, NG, 32);
   const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;  // (wave: a scalar)
   const int hi = lane >> 5, m = lane & 31;
   const int2 span = group_span(ginfo, grp, G, T);  // (a batch's groups come from its table)
@@ -428,6 +432,18 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
     xr0 = int2{klist[min(8 * wave + crow, last)], kScaled ? klist[min(8 * wave + (lane & 7), last)] : 0};
     xr1 = int2{klist[min(kRKeys + 8 * wave + crow, last)], kScaled ? klist[min(kRKeys + 8 * wave + (lane & 7), last)] : 0};
   }
+  // per-token mode: the row's entries, for its last valid slot (rows end in -1 padding when a
+  // token selects fewer rows than the buffer holds; the loop then stops at the last tile with
+  // a valid slot).  One load per thread and 256 slots, all in flight with the queries.
+  constexpr int kRScan = kPerToken ? 8 : 1;
+  int32_t xs[kRScan];
+  if constexpr (kPerToken) {
+#pragma unroll
+    for (int u = 0; u < kRScan; ++u) {
+      const int j = tid + u * kRThreads;
+      xs[u] = j < ncols ? klist[j] : -1;
+    }
+  }
   asm volatile("" ::: "memory");
 #pragma unroll
   for (int t = 0; t < kRIdxBufs; ++t)
@@ -495,7 +511,22 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   }
 #pragma unroll
   for (int s = 0; s < kRQLdsSteps; ++s) qlds[wave][s][lane] = qtail[s];
+  if constexpr (kPerToken) {
+    int last_ok = -1;
+#pragma unroll
+    for (int u = 0; u < kRScan; ++u)
+      if (slot_ok(xs[u], tid + u * kRThreads)) last_ok = tid + u * kRThreads;
+    for (int c0 = kRScan * kRThreads; c0 < ncols; c0 += kRThreads)  // (rows past 2048 columns)
+      if (c0 + tid < ncols && slot_ok(klist[c0 + tid], c0 + tid)) last_ok = c0 + tid;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) last_ok = max(last_ok, __shfl_xor(last_ok, d));
+    if (lane == 0) last_slot[wave] = last_ok;
+  }
   __syncthreads();  // tile 0 and the index words of tiles 0 .. 3 visible to all waves
+  if constexpr (kPerToken) {
+    const int last = max(max(last_slot[0], last_slot[1]), max(last_slot[2], last_slot[3]));
+    ntiles = uniform(min(ntiles, (last + kRKeys) / kRKeys));  // (tiles 0 and 1 already went out)
+  }
 
   // ---- the pipeline ---------------------------------------------------------------------
   // Iteration t: (wait + barrier) tile t + 1 and the probabilities of tile t are in LDS;

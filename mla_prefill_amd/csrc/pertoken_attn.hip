@@ -53,8 +53,9 @@
 //    so the scales of a step's 16 rows come by scalar loads (their row indices
 //    read out of the lanes), issued a step ahead of their use;
 //  * token order is reversed (long causal rows first) and block ids are
-//    remapped so each XCD runs a contiguous token range: neighbouring tokens,
-//    which share most of their rows, then hit the same L2.
+//    remapped so each XCD runs chunks of 16 consecutive tokens, the XCDs taking
+//    the chunks in turn: neighbouring tokens, which share most of their rows,
+//    hit the same L2, and every XCD gets its share of the short early rows.
 #include "common.h"
 #include "kernels.h"
 
@@ -492,7 +493,7 @@ __global__ __launch_bounds__(64) void pertoken_attn_kernel(
     const float* __restrict__ kscale, int per_row, const int32_t* __restrict__ skip) {
   if (skip != nullptr && uniform(*skip) != 0) return;  // (another routing was chosen on the device)
   const int nb = H >> 4;
-  const int item = xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
+  const int item = xcd_chunked_block((int)blockIdx.x, (int)gridDim.x, 16 * (H >> 4));  // (16 tokens)
   const int tq = item / nb;
   pt_ring_token<D, kScaled>(q, kv, topk, ld, H, S, cols, q_pos_offset, scale_log2, out, lse, T - 1 - tq,
                             item - tq * nb, kscale, per_row);
@@ -785,7 +786,7 @@ __global__ __launch_bounds__(64) void pertoken_sorted_kernel(
     const float* __restrict__ kscale, int per_row, const int32_t* __restrict__ skip) {
   if (skip != nullptr && uniform(*skip) != 0) return;  // (another routing was chosen on the device)
   const int nb = H >> 4;
-  const int item = xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
+  const int item = xcd_chunked_block((int)blockIdx.x, (int)gridDim.x, 16 * (H >> 4));  // (16 tokens)
   const int tq = item / nb;
   const int token = T - 1 - tq;
   const int hb = item - tq * nb;
