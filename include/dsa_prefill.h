@@ -100,8 +100,8 @@ size_t dsa_masked_mha_workspace_bytes(int T, int S);
  *             min(S, p_t + 1) is at most c * k, with c measured on MI355X for
  *             this library's kernels (against the 576-wide latent):
  *                         H = 16   32   64  | 128 | other multiples of 16
- *               mha_dv 256:  2.5  2.1  1.85 | 1.8 | 3.4
- *               mha_dv 128:  3.9  3.3  3.0  | 2.7 | 5.5
+ *               mha_dv 256:  2.4  1.95 1.7  | 1.4 | 3.4
+ *               mha_dv 128:  3.6  3.05 2.75 | 2.4 | 5.5
  *             (first three against grouped, the rest against per-token); any
  *             H the MQA kernels do not take (not a multiple of 16, or above
  *             128) routes here as well;
@@ -171,8 +171,8 @@ int dsa_sparse_prefill_grouped(const uint16_t* q, const uint16_t* kv, const int3
  * membership mask of every group of G = 128 / H tokens are built; then one
  * workgroup sums the grouped form's tiles, ceil(union_len / 32) over the groups,
  * and compares them with the per-token form's cost in the same unit,
- * rho(H) * sum_t min(cols, S, q_pos_offset + t + 1) / 32 with rho = 0.20, 0.43,
- * 0.92 for H = 16, 32, 64 (measured on MI355X for this library's kernels).
+ * rho(H) * sum_t min(cols, S, q_pos_offset + t + 1) / 32 with rho = 0.22, 0.46,
+ * 0.94 for H = 16, 32, 64 (measured on MI355X for this library's kernels).
  * Both attention launches are enqueued; the one not chosen returns at once.
  *
  *   q, kv, topk, ld, T, H, S, cols, q_pos_offset, d_qk, d_v, scale, out, lse:

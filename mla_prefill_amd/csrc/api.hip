@@ -79,8 +79,8 @@ int dsa_union_pad(int G, int cols) {
 namespace {
 double masked_threshold(int H, int mha_dv, bool grouped) {
   // {H 16, 32, 64 against grouped; 128 against per-token (G = 1); other H against per-token}
-  static const double kQk256[5] = {2.5, 2.1, 1.85, 1.8, 3.4};  // (256, 0, 256), (192, 64, 256)
-  static const double kDsv[5] = {3.9, 3.3, 3.0, 2.7, 5.5};      // (128, 64, 128)
+  static const double kQk256[5] = {2.4, 1.95, 1.7, 1.4, 3.4};  // (256, 0, 256), (192, 64, 256)
+  static const double kDsv[5] = {3.6, 3.05, 2.75, 2.4, 5.5};     // (128, 64, 128)
   const double* c = mha_dv == 128 ? kDsv : kQk256;
   if (!grouped) return H == 128 ? c[3] : c[4];
   return H == 16 ? c[0] : (H == 32 ? c[1] : c[2]);
@@ -210,7 +210,7 @@ int dsa_sparse_prefill_pertoken(const uint16_t* q, const uint16_t* kv, const int
 
 // per-token cost of the grouped form's 128-row tiles, per 32 selections (measured on MI355X
 // with this library's kernels, 576-wide latent, 16k-token chunks, locality and uniform top-k)
-static double route_rho(int H) { return H == 16 ? 0.20 : (H == 32 ? 0.43 : 0.92); }
+static double route_rho(int H) { return H == 16 ? 0.22 : (H == 32 ? 0.46 : 0.94); }
 
 // sum over the chunk of min(cols, S, p_t + 1), p_t = q_pos_offset + t: the selections a
 // token can make (an upper bound when rows hold -1 or out-of-range entries)

@@ -24,18 +24,19 @@ def test_dense_when_the_chunk_fits_in_the_top_k(pick):
 
 
 def test_masked_threshold_against_grouped(pick):
-    # H 16: c = 2.5, k = 2048 -> mean causal keys <= 5120; a chunk from 0 has mean (L + 1) / 2
-    assert pick(10239, 10239, 0, 16, 2048, 256) == "masked"
-    assert pick(10241, 10241, 0, 16, 2048, 256) == "grouped"
-    assert pick(8192, 8192, 0, 32, 2048, 256) == "masked"
-    assert pick(10240, 10240, 0, 32, 2048, 256) == "grouped"
+    # H 16: c = 2.4, k = 2048 -> mean causal keys <= 4915.2; a chunk from 0 has mean (L + 1) / 2
+    assert pick(9829, 9829, 0, 16, 2048, 256) == "masked"
+    assert pick(9831, 9831, 0, 16, 2048, 256) == "grouped"
+    # H 32: c = 1.95 -> mean <= 3993.6
+    assert pick(7986, 7986, 0, 32, 2048, 256) == "masked"
+    assert pick(7988, 7988, 0, 32, 2048, 256) == "grouped"
     assert pick(16384, 16384, 0, 64, 2048, 256) == "grouped"
 
 
 def test_masked_threshold_against_pertoken(pick):
-    # H 128: c = 1.8 -> mean causal keys <= 3686.4
-    assert pick(7168, 7168, 0, 128, 2048, 256) == "masked"
-    assert pick(8192, 8192, 0, 128, 2048, 256) == "per-token"
+    # H 128: c = 1.4 -> mean causal keys <= 2867.2
+    assert pick(5733, 5733, 0, 128, 2048, 256) == "masked"
+    assert pick(5735, 5735, 0, 128, 2048, 256) == "per-token"
     assert pick(8192, 8192, 0, 128, 2048, 0) == "per-token"
     # H 48: no grouped form (128 % 48 != 0); c = 3.4
     assert pick(13000, 13000, 0, 48, 2048, 256) == "masked"
@@ -44,11 +45,11 @@ def test_masked_threshold_against_pertoken(pick):
 
 
 def test_thresholds_of_the_dsv32_geometry(pick):
-    # (128, 64, 128): c = 3.9 / 3.3 / 3.0 against grouped, 2.7 at H 128
-    assert pick(15500, 15500, 0, 16, 2048, 128) == "masked"
-    assert pick(16500, 16500, 0, 16, 2048, 128) == "grouped"
-    assert pick(10500, 10500, 0, 128, 2048, 128) == "masked"
-    assert pick(11500, 11500, 0, 128, 2048, 128) == "per-token"
+    # (128, 64, 128): c = 3.6 / 3.05 / 2.75 against grouped, 2.4 at H 128
+    assert pick(14744, 14744, 0, 16, 2048, 128) == "masked"
+    assert pick(14746, 14746, 0, 16, 2048, 128) == "grouped"
+    assert pick(9829, 9829, 0, 128, 2048, 128) == "masked"
+    assert pick(9831, 9831, 0, 128, 2048, 128) == "per-token"
     assert pick(22000, 22000, 0, 48, 2048, 128) == "masked"
     from mla_prefill_amd import _lib
     assert _lib.lib.dsa_select_routing(8192, 8192, 0, 16, 2048, 192) == -3
