@@ -51,7 +51,11 @@
 //    by it before the PV product (l sums the unscaled probabilities);
 //  * the output is staged through LDS, so that each store instruction
 //    writes 256-byte row segments;
-//  * longest groups (most union slots) are launched first.
+//  * longest groups (most union slots) are launched first, and the XCDs take
+//    chunks of 32 consecutive groups in turn, so each gets its share of the
+//    short groups at the start of a causal chunk;
+//  * per-token mode (H = 128, one token per "group"): the loop ends at the
+//    tile of the row's last valid slot (rows that end in -1 padding).
 #include <type_traits>
 
 #include "common.h"

@@ -23,8 +23,9 @@
 // on their order).  Each byte is then both "in the union" (non-zero) and the
 // mask byte itself.  Compaction is ordered: every wave counts the non-zero
 // bytes of its contiguous segment, 16 bytes per lane per read, the four counts
-// are scanned, and a second pass scans the lanes' counts and writes each
-// non-zero position at base + its rank, consecutive slots in order.
+// are scanned, and a second pass writes each non-zero position at base + its
+// rank, consecutive slots in order (a sparse segment from each lane's prefix of
+// the lanes' counts, a dense one 64 positions at a time by ballot ranks).
 #include "common.h"
 #include "kernels.h"
 
