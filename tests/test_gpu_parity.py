@@ -321,6 +321,35 @@ def test_pertoken_head_counts_without_grouped_form(R, H):
     check_attention(out, lse, ref_out, ref_lse, f"per-token H={H}")
 
 
+def test_pertoken_h128_trailing_slots(R):
+    """The 128-row kernel in per-token mode stops at the tile of the row's last valid slot.
+    Rows here end in -1 padding, in non-causal or out-of-range entries (not valid either),
+    hold their last valid entry past column 2048 (the prologue's second scan), in the very
+    last column, in the first tile only, or hold none at all; a 2300-column buffer."""
+    rng = np.random.default_rng(47)
+    T, S, H, cols = 9, 3000, 128, 2300
+    P0 = S - T
+    q = normal_bf16(rng, (T, H, 576))
+    kv = normal_bf16(rng, (S, 576))
+    topk = np.full((T, cols), -1, np.int32)
+    for t in range(T):
+        pos = P0 + t
+        if t == 8:
+            continue                                                  # nothing valid
+        n = (40, 700, 1500, 2000, 2100, 2299, 5, 300)[t]
+        topk[t, :n] = rng.choice(pos + 1, size=n, replace=False)
+    topk[0, 40:60] = P0 + 5                                           # non-causal for token 0
+    topk[1, 700:720] = S + 3                                          # out of range
+    topk[4, 2100:2105] = -7
+    unused = lambda t: int(np.setdiff1d(np.arange(P0), topk[t])[0])
+    topk[4, 2150] = unused(4)                                         # last valid slot past 2048
+    topk[5, cols - 1] = unused(5)                                     # the very last column
+    topk[7, 300:] = P0 + 8                                            # non-causal for all of them
+    ref_out, ref_lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, P0, 0.0625)
+    out, lse = R.pertoken(dev_bf16(q), dev_bf16(kv), dev_i32(topk), P0, 0.0625)
+    check_attention(out, lse, ref_out, ref_lse, "per-token H=128 trailing slots")
+
+
 def test_grouped_far_positions(R):
     """The union builder's position windows past 65535 (a 70000-row latent, chunk at its end)."""
     q, kv, topk = small_mqa(16, 24, 70000, 16, 300, 320, 8, 70000 - 24, "uniform", True)
