@@ -52,7 +52,7 @@
 //  * the output is staged through LDS, so that each store instruction
 //    writes 256-byte row segments;
 //  * longest groups (most union slots) are launched first, and the XCDs take
-//    chunks of 32 consecutive groups in turn, so each gets its share of the
+//    chunks of 8 consecutive groups in turn, so each gets its share of the
 //    short groups at the start of a causal chunk;
 //  * per-token mode (H = 128, one token per "group"): the loop ends at the
 //    tile of the row's last valid slot (rows that end in -1 padding).
@@ -104,9 +104,9 @@ __global__ __launch_bounds__(kRThreads) void rows128_attn_kernel(
   const int G = 128 / H;
   const int NG = (int)gridDim.x;
   // (a group's work is its union's length -- a token's, its valid slots -- which grows along
-  // a causal chunk: the XCDs take chunks of 32 groups in turn, so that each gets its share of
+  // a causal chunk: the XCDs take chunks of 8 groups in turn, so that each gets its share of
   // the short early groups instead of one XCD getting all of them)
-  const int grp = NG - 1 - xcd_chunked_block((int)blockIdx.x, NG, 32);
+  const int grp = NG - 1 - xcd_chunked_block((int)blockIdx.x, NG, 8);
   const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;  // (wave: a scalar)
   const int hi = lane >> 5, m = lane & 31;
   const int2 span = group_span(ginfo, grp, G, T);  // (a batch's groups come from its table)
