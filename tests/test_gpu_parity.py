@@ -321,6 +321,21 @@ def test_pertoken_head_counts_without_grouped_form(R, H):
     check_attention(out, lse, ref_out, ref_lse, f"per-token H={H}")
 
 
+def test_grouped_chunked_block_order_with_a_ragged_tail(R):
+    """Enough groups (100 at H = 16, 157 at H = 32) that the launch maps most blocks to XCD
+    chunks and the rest (a partial round of chunks) one to one: every group must be computed
+    exactly once.  Every token is compared with the per-token oracle; also the 128-row kernel
+    in per-token mode over 150 tokens at H = 128."""
+    for seed, T, S, H, k in ((48, 800, 900, 16, 96), (49, 628, 700, 32, 80), (50, 150, 400, 128, 64)):
+        q, kv, topk = small_mqa(seed, T, S, H, k, k, max(1, 128 // H), S - T, "locality", True)
+        ref_out, ref_lse = oracle.pertoken_sparse_mqa(q, kv, topk, S, S - T, 0.0625)
+        if H < 128:
+            out, lse, _ = R.grouped(dev_bf16(q), dev_bf16(kv), dev_i32(topk), S - T, 0.0625)
+        else:
+            out, lse = R.pertoken(dev_bf16(q), dev_bf16(kv), dev_i32(topk), S - T, 0.0625)
+        check_attention(out, lse, ref_out, ref_lse, f"T={T} H={H} chunked block order")
+
+
 def test_pertoken_h128_trailing_slots(R):
     """The 128-row kernel in per-token mode stops at the tile of the row's last valid slot.
     Rows here end in -1 padding, in non-causal or out-of-range entries (not valid either),
